@@ -1,0 +1,179 @@
+"""Seeded synthetic inputs for the quantized-base + low-rank-adapter linear layer.
+
+This module is shared by the CPU oracle, the tests and the benchmark.  It holds
+no arithmetic of the method itself: it only draws random numbers and rounds
+them to the storage dtypes (fp16 by numpy's IEEE cast, bf16 by round-to-nearest-
+even from fp32).  bf16 arrays are returned as ``uint16`` bit patterns because
+numpy has no bf16 type.
+
+Recipe (every tensor): ``numpy.random.default_rng(SeedSequence([seed, cfg,
+tensor_id, *extra]))`` (PCG64), standard normals drawn in float32 and scaled by
+the stated sigma in float32, then cast to the storage dtype.
+
+The shapes follow the layer sizes the pages talk about (a 7B-class model's
+attention and MLP projections, and a 65B-class MLP projection: QLoRA page,
+section on the memory decomposition and the 65B example); the pretrained
+weights are replaced by N(0, sigma^2) draws, which is the distribution the
+QLoRA page gives as the premise of the NormalFloat codebook.
+"""
+from __future__ import annotations
+
+import dataclasses
+from typing import List, Optional, Tuple
+
+import numpy as np
+
+# tensor ids inside one config
+T_W, T_A, T_B, T_X, T_OUTLIER, T_DRAW = 0, 1, 2, 3, 4, 5
+
+BITS_CHOICES = (2, 3, 4, 8)
+RANK_CHOICES = (4, 8, 16, 32, 64)
+
+
+def rng_for(cfg: int, *ids: int, seed: int = 0) -> np.random.Generator:
+    return np.random.default_rng(np.random.SeedSequence([seed, cfg, *ids]))
+
+
+def normal(shape, sigma: float, cfg: int, *ids: int, seed: int = 0) -> np.ndarray:
+    g = rng_for(cfg, *ids, seed=seed)
+    z = g.standard_normal(size=shape, dtype=np.float32)
+    return z * np.float32(sigma)
+
+
+def to_bf16_bits(a32: np.ndarray) -> np.ndarray:
+    """Round float32 to bf16 (nearest, ties to even); returns uint16 bit patterns."""
+    u = np.ascontiguousarray(a32, dtype=np.float32).view(np.uint32)
+    bias = np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    return ((u + bias) >> np.uint32(16)).astype(np.uint16)
+
+
+def store(a32: np.ndarray, dtype: str) -> np.ndarray:
+    if dtype == "f32":
+        return np.ascontiguousarray(a32, dtype=np.float32)
+    if dtype == "f16":
+        return a32.astype(np.float16)
+    if dtype == "bf16":
+        return to_bf16_bits(a32)
+    raise ValueError(dtype)
+
+
+@dataclasses.dataclass
+class Linear:
+    """One linear layer's synthetic inputs (all host numpy arrays).
+
+    W: (N, K) in ``wdtype``; A: (r, K); B: (N, r) in ``abdtype``;
+    x: (M, K) in ``xdtype``; scale = alpha / r.
+    """
+    name: str
+    W: np.ndarray
+    wdtype: str
+    bits: int
+    r: int
+    alpha: float
+    A: Optional[np.ndarray]
+    B: Optional[np.ndarray]
+    abdtype: str
+    x: np.ndarray
+    xdtype: str
+
+    @property
+    def N(self) -> int:
+        return self.W.shape[0]
+
+    @property
+    def K(self) -> int:
+        return self.W.shape[1]
+
+    @property
+    def M(self) -> int:
+        return self.x.shape[0]
+
+    @property
+    def scale(self) -> float:
+        return float(np.float32(self.alpha) / np.float32(self.r)) if self.r > 0 else 0.0
+
+
+def make_weight(cfg: int, N: int, K: int, sigma: float, wdtype: str, sub: int = 0,
+                outlier_frac: float = 0.0, outlier_mult: float = 20.0, seed: int = 0) -> np.ndarray:
+    w = normal((N, K), sigma, cfg, T_W, sub, seed=seed)
+    if outlier_frac > 0.0:
+        cnt = int(round(outlier_frac * N * K))
+        pos = rng_for(cfg, T_OUTLIER, sub, seed=seed).choice(N * K, size=cnt, replace=False)
+        flat = w.reshape(-1)
+        flat[pos] = flat[pos] * np.float32(outlier_mult)
+    return store(w, wdtype)
+
+
+def make_linear(name: str, cfg: int, N: int, K: int, M: int, *, sigma: float, wdtype: str,
+                bits: int, r: int, alpha: float, abdtype: str, xdtype: str,
+                a_sigma: Optional[float] = None, b_sigma: float = 0.01, sub: int = 0,
+                outlier_frac: float = 0.0, seed: int = 0, W: Optional[np.ndarray] = None) -> Linear:
+    if W is None:
+        W = make_weight(cfg, N, K, sigma, wdtype, sub=sub, outlier_frac=outlier_frac, seed=seed)
+    if a_sigma is None:
+        a_sigma = float(np.sqrt(1.0 / K))
+    A = store(normal((r, K), a_sigma, cfg, T_A, sub, seed=seed), abdtype) if r > 0 else None
+    B = store(normal((N, r), b_sigma, cfg, T_B, sub, seed=seed), abdtype) if r > 0 else None
+    x = store(normal((M, K), 1.0, cfg, T_X, sub, M, seed=seed), xdtype)
+    return Linear(name, W, wdtype, bits, r, alpha, A, B, abdtype, x, xdtype)
+
+
+# ---------------------------------------------------------------- the five workloads
+
+def tiny(seed: int = 0) -> Linear:
+    """256x256 fp32 weights, 4-bit, rank 4 (alpha 8) fp32 adapters, 8x256 fp32 x."""
+    return make_linear("tiny", 1, 256, 256, 8, sigma=0.02, wdtype="f32", bits=4, r=4,
+                       alpha=8.0, abdtype="f32", xdtype="f32", a_sigma=float(np.sqrt(1 / 256)),
+                       seed=seed)
+
+
+def attn(M: int, seed: int = 0, W: Optional[np.ndarray] = None) -> Linear:
+    """7B-class attention projection 4096x4096 fp16 with 0.1% x20 outliers, 4-bit, r16 a16."""
+    return make_linear(f"attn_M{M}", 2, 4096, 4096, M, sigma=0.02, wdtype="f16", bits=4, r=16,
+                       alpha=16.0, abdtype="bf16", xdtype="bf16", outlier_frac=0.001,
+                       seed=seed, W=W)
+
+
+def mlp(which: str, M: int, seed: int = 0, W: Optional[np.ndarray] = None) -> Linear:
+    """7B-class MLP projection: 'up' 11008x4096 or 'down' 4096x11008, fp16, 4-bit, r64 a16."""
+    N, K, sub = (11008, 4096, 0) if which == "up" else (4096, 11008, 1)
+    return make_linear(f"mlp_{which}_M{M}", 3, N, K, M, sigma=0.02, wdtype="f16", bits=4, r=64,
+                       alpha=16.0, abdtype="bf16", xdtype="bf16", sub=sub, seed=seed, W=W)
+
+
+def big65(M: int, seed: int = 0, W: Optional[np.ndarray] = None) -> Linear:
+    """65B-class MLP projection 22016x8192 fp16 (sigma 0.015), 4-bit, r64 a16."""
+    return make_linear(f"big65_M{M}", 5, 22016, 8192, M, sigma=0.015, wdtype="f16", bits=4,
+                       r=64, alpha=16.0, abdtype="bf16", xdtype="bf16", seed=seed, W=W)
+
+
+MIXED_SHAPES: Tuple[Tuple[int, int], ...] = ((4096, 4096),) * 4 + ((11008, 4096),) * 2 + ((4096, 11008),)
+MIXED_LAYERS = 32
+
+
+def mixed_plan(seed: int = 0, layers: int = MIXED_LAYERS) -> List[Tuple[int, int, int, int]]:
+    """(N, K, bits, rank) for every linear of the mixed stack, layer-major."""
+    g = rng_for(4, T_DRAW, seed=seed)
+    n = layers * len(MIXED_SHAPES)
+    bits = g.choice(np.array(BITS_CHOICES), size=n)
+    ranks = g.choice(np.array(RANK_CHOICES), size=n)
+    plan = []
+    for i in range(n):
+        N, K = MIXED_SHAPES[i % len(MIXED_SHAPES)]
+        plan.append((N, K, int(bits[i]), int(ranks[i])))
+    return plan
+
+
+def mixed_linear(i: int, M: int = 512, seed: int = 0, plan=None,
+                 shape_override: Optional[Tuple[int, int]] = None) -> Linear:
+    """Linear number ``i`` of the mixed stack (independent of the others).
+
+    ``shape_override`` keeps the drawn (bits, rank) but shrinks (N, K); tests use
+    it to run the stack at sizes the oracle finishes quickly.
+    """
+    plan = plan or mixed_plan(seed)
+    N, K, bits, r = plan[i]
+    if shape_override is not None:
+        N, K = shape_override
+    return make_linear(f"mixed_{i}", 4, N, K, M, sigma=0.02, wdtype="f16", bits=bits, r=r,
+                       alpha=16.0, abdtype="bf16", xdtype="bf16", sub=1000 + i, seed=seed)
