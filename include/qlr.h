@@ -1,0 +1,230 @@
+/*
+ * qlr.h: C ABI of the quantized-base + low-rank-adapter linear layer for
+ * AMD MI355X (gfx950).
+ *
+ * What the library computes (pages as printed; sections named on each call):
+ *   - "QLoRA" (aizip.shop methodologies page), section "1. 4-bit NormalFloat
+ *     (NF4) quantization": a k-bit codebook of normal quantiles.
+ *   - same page, section "2. Double Quantization": blockwise absmax scaling with
+ *     blocks of 64 weights, and the absmax constants themselves re-quantized to
+ *     8 bits.
+ *   - same page, memory-decomposition equation: frozen 4-bit base weights and
+ *     bf16 adapters.
+ *   - "LoRDBA" (gist.science summary), sections 1-2: the adapter is served
+ *     unmerged ("adapter mode"), as a separate branch beside the frozen base.
+ *   - "AutoQRA" (gist.science summary), section 3.1: every layer has its own
+ *     bit width and adapter rank.
+ *
+ * Conventions for every call:
+ *   - W is rows x cols = N x K, row-major ("out x in").  x is M x K, y is M x N,
+ *     A is r x K, B is N x r, all row-major and densely packed.
+ *   - Pointers marked (device) are HIP device pointers; the caller owns every
+ *     buffer.  The library allocates nothing and keeps no per-call state; it
+ *     holds no handle.  Device pointers must be 16-byte aligned.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).  All
+ *     calls are asynchronous on that stream unless stated otherwise.
+ *   - Every call returns a qlr_status; nothing is thrown across the ABI.
+ *     Argument errors are detected on the host before anything is launched.
+ *     qlr_last_error() returns a thread-local description of the last failure.
+ *   - Calls that share a workspace must not overlap in time (same stream, or
+ *     ordered by the caller).
+ */
+#ifndef QLR_H
+#define QLR_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define QLR_FORMAT_VERSION 1u /* codebook, tie rule, packing, double-quant format */
+#define QLR_BLOCK 64          /* weights per first-level absmax constant */
+#define QLR_GROUP 256         /* first-level constants per second-level constant */
+
+typedef enum {
+  QLR_OK = 0,
+  QLR_ERR_NULL = 1,      /* a required pointer is NULL */
+  QLR_ERR_SHAPE = 2,     /* a size is negative, zero where not allowed, or inconsistent */
+  QLR_ERR_DTYPE = 3,     /* dtype not supported for this argument */
+  QLR_ERR_BITS = 4,      /* bits not in {2, 3, 4, 8} */
+  QLR_ERR_BLOCK = 5,     /* block != 64 or group != 256 */
+  QLR_ERR_ALIGN = 6,     /* a device pointer is not 16-byte aligned */
+  QLR_ERR_NONFINITE = 7, /* quantize: W holds NaN or Inf */
+  QLR_ERR_WORKSPACE = 8, /* workspace NULL or smaller than qlr_workspace_bytes() */
+  QLR_ERR_ALIAS = 9,     /* mixed: an output overlaps an input or another output */
+  QLR_ERR_HIP = 10,      /* a HIP runtime call or launch failed (text in qlr_last_error) */
+  QLR_ERR_FORMAT = 11,   /* qlr_qweight.format_version unknown */
+  QLR_ERR_PATH = 12      /* forced path cannot run these arguments */
+} qlr_status;
+
+typedef enum { QLR_F32 = 0, QLR_F16 = 1, QLR_BF16 = 2 } qlr_dtype;
+
+/* Kernel families of qlr_linear_fwd (QLR_PATH_AUTO picks by M and dtype). */
+typedef enum {
+  QLR_PATH_AUTO = 0,
+  QLR_PATH_F32 = 1,  /* float32 arithmetic, any M and dtype; the accuracy-first path */
+  QLR_PATH_GEMV = 2, /* bf16 x, M <= 16: bandwidth-bound decode (bf16 MFMA, fp32 accumulate) */
+  QLR_PATH_GEMM = 3  /* bf16 x, any M: LDS-tiled prefill GEMM (bf16 MFMA, fp32 accumulate) */
+} qlr_path;
+
+typedef enum { QLR_OP_QUANTIZE = 0, QLR_OP_LINEAR = 1 } qlr_op;
+
+/*
+ * A quantized frozen weight (QLoRA page, sections "1. 4-bit NormalFloat" and
+ * "2. Double Quantization"; format version 1):
+ *   codes     (device) ceil(rows*cols/64) * 8*bits bytes.  Block j = the 64
+ *             consecutive elements [64j, 64j+64) of the row-major flattened W;
+ *             its codes fill bytes [8*bits*j, 8*bits*(j+1)), element e of the
+ *             block at bits [bits*e, bits*e+bits) of that little-endian bit
+ *             string.  Code i stands for codebook level i (ascending).
+ *   absmax_q8 (device) one byte per block: the 8-bit code m of the block's
+ *             absmax, which dequantizes to m * absmax_c[j / 256].
+ *   absmax_c  (device) one float32 per 256 consecutive blocks: the step
+ *             fl32(g / 255), g the largest absmax in the group.
+ * A dequantized weight is fl32(level[code] * fl32(m * step)).
+ */
+typedef struct {
+  uint32_t format_version; /* QLR_FORMAT_VERSION */
+  int32_t bits;            /* 2, 3, 4 or 8 */
+  int32_t block;           /* QLR_BLOCK */
+  int32_t group;           /* QLR_GROUP */
+  int64_t rows;            /* N */
+  int64_t cols;            /* K */
+  void* codes;             /* device */
+  uint8_t* absmax_q8;      /* device */
+  float* absmax_c;         /* device */
+} qlr_qweight;
+
+/* One entry of a mixed stack (AutoQRA page, section 3.1: per-layer bits and rank). */
+typedef struct {
+  const qlr_qweight* w; /* host pointer to the layer's quantized weight */
+  const void* x;        /* device, M x w->cols */
+  const void* A;        /* device, r x w->cols (NULL if r == 0) */
+  const void* B;        /* device, w->rows x r (NULL if r == 0) */
+  int32_t r;            /* adapter rank, >= 0 */
+  float scale;          /* alpha / r */
+  void* y;              /* device, M x w->rows */
+} qlr_layer;
+
+/* Library version (major*10000 + minor*100 + patch). */
+int qlr_version(void);
+/* Static text for a status code. */
+const char* qlr_status_string(qlr_status s);
+/* Thread-local text of the last error raised on this thread ("" if none). */
+const char* qlr_last_error(void);
+
+/*
+ * Codebook (QLoRA page, section "1. 4-bit NormalFloat (NF4) quantization",
+ * codebook equation).  Writes the 2^bits ascending float32 levels to `out`
+ * (host).  Level i = Q((i + 1/2) / 2^bits) / Q((2^bits - 1/2) / 2^bits),
+ * Q the standard-normal quantile (0-based i; the printed equation's
+ * (i - 1/2) is read with a 1-based index), the lower half computed and the
+ * upper half its mirror image, each rounded once to float32.
+ * Host only.  Errors: QLR_ERR_NULL, QLR_ERR_BITS.
+ */
+qlr_status qlr_codebook(int32_t bits, float* out);
+
+/*
+ * Sizes in bytes of the three arrays of a rows x cols quantized weight
+ * (QLoRA page, section "2. Double Quantization": bits + 8/64 + 32/(64*256)
+ * bits per weight).  Any rows, cols >= 0 (a trailing partial block and group
+ * are allowed).  Host only.  Errors: QLR_ERR_NULL, QLR_ERR_SHAPE,
+ * QLR_ERR_BITS, QLR_ERR_BLOCK.
+ */
+qlr_status qlr_qweight_sizes(int64_t rows, int64_t cols, int32_t bits, int32_t block,
+                             size_t* codes_bytes, size_t* absmax_q8_bytes,
+                             size_t* absmax_c_bytes);
+
+/*
+ * Device workspace needed by an operation.  QLR_OP_QUANTIZE: 256 bytes (the
+ * non-finite flag); M, N, K, r are ignored.  QLR_OP_LINEAR: the adapter
+ * product t = x A^T for M rows and rank r, plus alignment.  Host only.
+ */
+qlr_status qlr_workspace_bytes(qlr_op op, int64_t M, int64_t N, int64_t K, int32_t r,
+                               size_t* bytes);
+
+/*
+ * Quantize (QLoRA page, sections "1. 4-bit NormalFloat (NF4) quantization" and
+ * "2. Double Quantization").  W (device) rows x cols in wdt (f32, f16, bf16),
+ * widened exactly to float32.  For block j with float32 absmax a, element w
+ * gets the code of the nearest level*a, ties to the lower code
+ * (#{i : 2w > (level[i] + level[i+1]) * a}, decided exactly); a == 0 gives
+ * code 0.  Groups of 256 absmax values get step s = fl32(g / 255) and each
+ * absmax the code of the nearest multiple m*s, ties to the lower m.
+ * `out` (host struct) must carry format_version, bits, block, group, rows,
+ * cols and the three device buffers sized by qlr_qweight_sizes; the call fills
+ * the buffers.  ws (device) >= qlr_workspace_bytes(QLR_OP_QUANTIZE).
+ * BLOCKING: synchronises `stream` to read the non-finite flag.
+ * Errors: QLR_ERR_NULL, QLR_ERR_SHAPE, QLR_ERR_DTYPE, QLR_ERR_BITS,
+ * QLR_ERR_BLOCK, QLR_ERR_ALIGN, QLR_ERR_WORKSPACE, QLR_ERR_FORMAT,
+ * QLR_ERR_NONFINITE (buffers then hold unspecified data), QLR_ERR_HIP.
+ */
+qlr_status qlr_quantize(const void* W, qlr_dtype wdt, int64_t rows, int64_t cols, int32_t bits,
+                        int32_t block, qlr_qweight* out, void* ws, size_t ws_bytes,
+                        void* stream);
+
+/*
+ * Same as qlr_quantize but asynchronous: the non-finite flag is left in the
+ * first 4 bytes of ws (uint32, nonzero if W held NaN or Inf) for the caller.
+ */
+qlr_status qlr_quantize_async(const void* W, qlr_dtype wdt, int64_t rows, int64_t cols,
+                              int32_t bits, int32_t block, qlr_qweight* out, void* ws,
+                              size_t ws_bytes, void* stream);
+
+/*
+ * Dequantize (QLoRA page, section "Limitations": the base is dequantized
+ * whenever it is used).  out (device) rows*cols elements of odt:
+ * QLR_F32 gives fl32(level[c] * fl32(m * step)) exactly (two float32
+ * multiplies in that order, signed zeros kept); QLR_BF16 gives that value
+ * rounded to nearest-even bf16.  Errors: QLR_ERR_NULL, QLR_ERR_DTYPE,
+ * QLR_ERR_BITS, QLR_ERR_BLOCK, QLR_ERR_ALIGN, QLR_ERR_FORMAT, QLR_ERR_SHAPE,
+ * QLR_ERR_HIP.
+ */
+qlr_status qlr_dequantize(const qlr_qweight* w, void* out, qlr_dtype odt, void* stream);
+
+/*
+ * Forward of the frozen base with an unmerged adapter (QLoRA page,
+ * memory-decomposition equation; LoRDBA page, "adapter mode"):
+ *     y = x W'^T + scale * (x A^T) B^T,   W' the dequantized weight.
+ * x (device) M x K in xdt (f32 or bf16); A (device) r x K and B (device) N x r
+ * in abdt (f32 or bf16), both NULL when r == 0; y (device) M x N in ydt
+ * (f32 or bf16).  Requires cols % 64 == 0 (whole blocks per row).  M may be 0
+ * (nothing is launched).  Each y element is within
+ * 1e-3 * sum_k |x[m,k] w'[n,k]| + 1e-5 of the exact result (plus half a bf16
+ * ulp when ydt is bf16).  ws (device) >= qlr_workspace_bytes(QLR_OP_LINEAR,
+ * M, N, K, r).  Asynchronous, allocation-free, no host synchronisation.
+ * Errors: QLR_ERR_NULL, QLR_ERR_SHAPE, QLR_ERR_DTYPE, QLR_ERR_BITS,
+ * QLR_ERR_BLOCK, QLR_ERR_ALIGN, QLR_ERR_FORMAT, QLR_ERR_WORKSPACE,
+ * QLR_ERR_PATH, QLR_ERR_HIP.
+ */
+qlr_status qlr_linear_fwd(const void* x, qlr_dtype xdt, int64_t M, const qlr_qweight* w,
+                          const void* A, const void* B, qlr_dtype abdt, int32_t r, float scale,
+                          void* y, qlr_dtype ydt, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Mixed stack (AutoQRA page, section 3.1: each layer has its own bit width
+ * and rank).  `layers` (host array of n entries) are independent linears, all
+ * with the same M and dtypes, each computed as qlr_linear_fwd would.  No y
+ * may overlap any x, A, B or other y of the call (QLR_ERR_ALIAS, checked on
+ * the host).  ws >= the sum over entries of qlr_workspace_bytes(QLR_OP_LINEAR,
+ * M, rows, cols, r).  Asynchronous.
+ */
+qlr_status qlr_linear_fwd_mixed(const qlr_layer* layers, int32_t n, int64_t M, qlr_dtype xdt,
+                                qlr_dtype abdt, qlr_dtype ydt, void* ws, size_t ws_bytes,
+                                void* stream);
+
+/*
+ * Force the kernel family used by qlr_linear_fwd and qlr_linear_fwd_mixed on
+ * the calling thread (for tests and measurement).  QLR_PATH_AUTO restores the
+ * default choice: F32 for float32 x or float32 adapters, GEMV for M <= 16,
+ * GEMM otherwise.  Host only.  Errors: QLR_ERR_PATH for an unknown value.
+ */
+qlr_status qlr_force_path(qlr_path path);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* QLR_H */

@@ -1,0 +1,403 @@
+// Host side of the qlr C ABI: argument validation, codebook construction,
+// size and workspace queries, and dispatch onto the gfx950 kernels.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "../../include/qlr.h"
+#include "qlr_internal.h"
+
+namespace {
+
+thread_local std::string t_error;
+thread_local qlr_path t_path = QLR_PATH_AUTO;
+
+qlr_status fail(qlr_status s, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  t_error = buf;
+  return s;
+}
+
+qlr_status hip_fail(hipError_t e, const char* what) {
+  return fail(QLR_ERR_HIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+// ---------------------------------------------------------------- codebook
+//
+// QLoRA page, section "1. 4-bit NormalFloat (NF4) quantization": level i is
+// the standard-normal quantile at (i + 1/2) / 2^b (0-based), divided by the
+// largest such quantile so the levels span [-1, 1]; the lower half is computed
+// and mirrored.  The quantile is found by bisection on Phi(z) = erfc(-z/sqrt2)/2
+// in long double (64-bit significand) and each level is rounded once to float.
+
+long double normal_cdf(long double z) { return 0.5L * std::erfc(-z / std::sqrt(2.0L)); }
+
+long double normal_quantile(long double p) {
+  long double lo = -40.0L, hi = 40.0L;
+  for (int it = 0; it < 400; ++it) {
+    const long double mid = 0.5L * (lo + hi);
+    if (mid <= lo || mid >= hi) break;
+    if (normal_cdf(mid) < p) lo = mid;
+    else hi = mid;
+  }
+  return 0.5L * (lo + hi);
+}
+
+struct CodebookCache {
+  std::once_flag once[9];
+  float levels[9][256];
+};
+CodebookCache g_cb;
+
+const float* codebook_levels(int bits) {
+  std::call_once(g_cb.once[bits], [bits]() {
+    const int n = 1 << bits;
+    const long double top = normal_quantile((2.0L * n - 1.0L) / (2.0L * n));
+    float* L = g_cb.levels[bits];
+    for (int i = 0; i < n / 2; ++i) {
+      const long double z = normal_quantile((2.0L * i + 1.0L) / (2.0L * n));
+      L[i] = (float)(z / top);
+      L[n - 1 - i] = -L[i];
+    }
+  });
+  return g_cb.levels[bits];
+}
+
+qlr::Levels levels_arg(int bits) {
+  qlr::Levels lv;
+  std::memset(&lv, 0, sizeof(lv));
+  std::memcpy(lv.v, codebook_levels(bits), sizeof(float) << bits);
+  return lv;
+}
+
+// ---------------------------------------------------------------- validation
+
+bool bits_ok(int32_t bits) { return bits == 2 || bits == 3 || bits == 4 || bits == 8; }
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+size_t dtype_size(qlr_dtype d) { return d == QLR_F32 ? 4 : 2; }
+bool dtype_ok(int d) { return d == QLR_F32 || d == QLR_F16 || d == QLR_BF16; }
+
+void sizes_of(int64_t rows, int64_t cols, int bits, size_t* cb, size_t* qb, size_t* kb) {
+  const int64_t numel = rows * cols;
+  const int64_t nblk = (numel + QLR_BLOCK - 1) / QLR_BLOCK;
+  const int64_t ngrp = (nblk + QLR_GROUP - 1) / QLR_GROUP;
+  *cb = (size_t)nblk * 8 * (size_t)bits;
+  *qb = (size_t)nblk;
+  *kb = (size_t)ngrp * 4;
+}
+
+qlr_status check_qweight(const qlr_qweight* w) {
+  if (!w) return fail(QLR_ERR_NULL, "qweight is NULL");
+  if (w->format_version != QLR_FORMAT_VERSION)
+    return fail(QLR_ERR_FORMAT, "format_version %u, expected %u", w->format_version, QLR_FORMAT_VERSION);
+  if (!bits_ok(w->bits)) return fail(QLR_ERR_BITS, "bits %d not in {2,3,4,8}", w->bits);
+  if (w->block != QLR_BLOCK || w->group != QLR_GROUP)
+    return fail(QLR_ERR_BLOCK, "block %d / group %d, expected 64 / 256", w->block, w->group);
+  if (w->rows < 0 || w->cols < 0) return fail(QLR_ERR_SHAPE, "negative rows/cols");
+  if (w->rows > 0 && w->cols > (INT64_C(1) << 40) / w->rows) return fail(QLR_ERR_SHAPE, "weight too large");
+  if (!w->codes || !w->absmax_q8 || !w->absmax_c) return fail(QLR_ERR_NULL, "qweight buffer is NULL");
+  if (!aligned16(w->codes) || !aligned16(w->absmax_q8) || !aligned16(w->absmax_c))
+    return fail(QLR_ERR_ALIGN, "qweight buffers must be 16-byte aligned");
+  return QLR_OK;
+}
+
+size_t linear_ws_bytes(int64_t M, int32_t r) {
+  if (M <= 0 || r <= 0) return 0;
+  return (((size_t)M * (size_t)r * sizeof(float)) + 255) & ~(size_t)255;
+}
+
+// choose the kernel family for a linear call
+qlr_status pick_path(int64_t M, qlr_dtype xdt, qlr_dtype abdt, int32_t r, qlr_path* out) {
+  const bool bf16_ok = xdt == QLR_BF16 && (r == 0 || abdt == QLR_BF16);
+  qlr_path p = t_path;
+  if (p == QLR_PATH_AUTO) {
+    if (!bf16_ok) p = QLR_PATH_F32;
+    else p = (M <= 16) ? QLR_PATH_GEMV : QLR_PATH_GEMM;
+  }
+  if ((p == QLR_PATH_GEMV || p == QLR_PATH_GEMM) && !bf16_ok)
+    return fail(QLR_ERR_PATH, "the MFMA paths need bf16 x and bf16 adapters");
+  if (p == QLR_PATH_GEMV && M > 16) return fail(QLR_ERR_PATH, "the GEMV path takes M <= 16");
+  *out = p;
+  return QLR_OK;
+}
+
+struct LinearCheck {
+  const void* x;
+  qlr_dtype xdt;
+  int64_t M;
+  const qlr_qweight* w;
+  const void* A;
+  const void* B;
+  qlr_dtype abdt;
+  int32_t r;
+  void* y;
+  qlr_dtype ydt;
+};
+
+qlr_status check_linear(const LinearCheck& c) {
+  qlr_status st = check_qweight(c.w);
+  if (st != QLR_OK) return st;
+  if (c.M < 0) return fail(QLR_ERR_SHAPE, "M < 0");
+  if (c.r < 0) return fail(QLR_ERR_SHAPE, "r < 0");
+  if (c.w->cols % QLR_BLOCK != 0) return fail(QLR_ERR_SHAPE, "cols %lld is not a multiple of 64", (long long)c.w->cols);
+  if (c.w->rows == 0 || c.w->cols == 0) return fail(QLR_ERR_SHAPE, "empty weight");
+  if (!(c.xdt == QLR_F32 || c.xdt == QLR_BF16)) return fail(QLR_ERR_DTYPE, "x dtype must be f32 or bf16");
+  if (!(c.ydt == QLR_F32 || c.ydt == QLR_BF16)) return fail(QLR_ERR_DTYPE, "y dtype must be f32 or bf16");
+  if (c.r > 0 && !(c.abdt == QLR_F32 || c.abdt == QLR_BF16)) return fail(QLR_ERR_DTYPE, "adapter dtype must be f32 or bf16");
+  if (c.M > 0) {
+    if (!c.x || !c.y) return fail(QLR_ERR_NULL, "x or y is NULL");
+    if (!aligned16(c.x) || !aligned16(c.y)) return fail(QLR_ERR_ALIGN, "x and y must be 16-byte aligned");
+  }
+  if (c.r > 0) {
+    if (!c.A || !c.B) return fail(QLR_ERR_NULL, "A or B is NULL with r > 0");
+    if (!aligned16(c.A) || !aligned16(c.B)) return fail(QLR_ERR_ALIGN, "A and B must be 16-byte aligned");
+  }
+  return QLR_OK;
+}
+
+qlr::LinearArgs make_args(const LinearCheck& c, float scale, const float* t) {
+  qlr::LinearArgs a;
+  a.x = c.x;
+  a.xdt = (int)c.xdt;
+  a.M = c.M;
+  a.N = c.w->rows;
+  a.K = c.w->cols;
+  a.bits = c.w->bits;
+  a.codes = reinterpret_cast<const uint8_t*>(c.w->codes);
+  a.q8 = c.w->absmax_q8;
+  a.cst = c.w->absmax_c;
+  a.t = t;
+  a.B = c.B;
+  a.abdt = (int)c.abdt;
+  a.r = c.r;
+  a.scale = scale;
+  a.y = c.y;
+  a.ydt = (int)c.ydt;
+  return a;
+}
+
+qlr_status run_linear(const LinearCheck& c, float scale, float* t, qlr_path path, hipStream_t s) {
+  if (c.M == 0) return QLR_OK;
+  hipError_t e = hipSuccess;
+  if (c.r > 0) {
+    e = qlr::launch_lora_t(c.x, (int)c.xdt, c.M, c.w->cols, c.A, (int)c.abdt, c.r, t, s);
+    if (e != hipSuccess) return hip_fail(e, "adapter product launch");
+  }
+  const qlr::LinearArgs a = make_args(c, scale, t);
+  const qlr::Levels lv = levels_arg(c.w->bits);
+  switch (path) {
+    case QLR_PATH_F32: e = qlr::launch_linear_f32(a, lv, s); break;
+    case QLR_PATH_GEMV: e = qlr::launch_gemv(a, lv, s); break;
+    default: e = qlr::launch_gemm(a, lv, s); break;
+  }
+  if (e != hipSuccess) return hip_fail(e, "linear launch");
+  return QLR_OK;
+}
+
+qlr_status quantize_common(const void* W, qlr_dtype wdt, int64_t rows, int64_t cols, int32_t bits,
+                           int32_t block, qlr_qweight* out, void* ws, size_t ws_bytes,
+                           hipStream_t s) {
+  if (!W || !out) return fail(QLR_ERR_NULL, "W or out is NULL");
+  if (!dtype_ok(wdt)) return fail(QLR_ERR_DTYPE, "W dtype must be f32, f16 or bf16");
+  if (!bits_ok(bits)) return fail(QLR_ERR_BITS, "bits %d not in {2,3,4,8}", bits);
+  if (block != QLR_BLOCK) return fail(QLR_ERR_BLOCK, "block %d, expected 64", block);
+  if (rows <= 0 || cols <= 0) return fail(QLR_ERR_SHAPE, "rows and cols must be positive");
+  if (out->rows != rows || out->cols != cols || out->bits != bits || out->block != block)
+    return fail(QLR_ERR_SHAPE, "out header does not match rows/cols/bits/block");
+  qlr_status st = check_qweight(out);
+  if (st != QLR_OK) return st;
+  if (!aligned16(W)) return fail(QLR_ERR_ALIGN, "W must be 16-byte aligned");
+  if (!ws || ws_bytes < 256) return fail(QLR_ERR_WORKSPACE, "workspace of at least 256 bytes required");
+  if (!aligned16(ws)) return fail(QLR_ERR_ALIGN, "workspace must be 16-byte aligned");
+  uint32_t* flag = reinterpret_cast<uint32_t*>(ws);
+  hipError_t e = qlr::launch_fill_u32(flag, 0u, 1, s);
+  if (e != hipSuccess) return hip_fail(e, "flag clear");
+  const qlr::Levels lv = levels_arg(bits);
+  e = qlr::launch_quantize(W, (int)wdt, rows * cols, bits, lv, reinterpret_cast<uint8_t*>(out->codes),
+                           out->absmax_q8, out->absmax_c, flag, s);
+  if (e != hipSuccess) return hip_fail(e, "quantize launch");
+  return QLR_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int qlr_version(void) { return 100; }
+
+const char* qlr_status_string(qlr_status s) {
+  switch (s) {
+    case QLR_OK: return "ok";
+    case QLR_ERR_NULL: return "null pointer";
+    case QLR_ERR_SHAPE: return "bad shape";
+    case QLR_ERR_DTYPE: return "unsupported dtype";
+    case QLR_ERR_BITS: return "unsupported bit width";
+    case QLR_ERR_BLOCK: return "unsupported block or group size";
+    case QLR_ERR_ALIGN: return "misaligned pointer";
+    case QLR_ERR_NONFINITE: return "non-finite weight";
+    case QLR_ERR_WORKSPACE: return "workspace too small";
+    case QLR_ERR_ALIAS: return "overlapping buffers";
+    case QLR_ERR_HIP: return "HIP error";
+    case QLR_ERR_FORMAT: return "unknown qweight format";
+    case QLR_ERR_PATH: return "path cannot run these arguments";
+  }
+  return "unknown status";
+}
+
+const char* qlr_last_error(void) { return t_error.c_str(); }
+
+qlr_status qlr_codebook(int32_t bits, float* out) {
+  if (!out) return fail(QLR_ERR_NULL, "out is NULL");
+  if (!bits_ok(bits)) return fail(QLR_ERR_BITS, "bits %d not in {2,3,4,8}", bits);
+  std::memcpy(out, codebook_levels(bits), sizeof(float) << bits);
+  return QLR_OK;
+}
+
+qlr_status qlr_qweight_sizes(int64_t rows, int64_t cols, int32_t bits, int32_t block,
+                             size_t* codes_bytes, size_t* absmax_q8_bytes, size_t* absmax_c_bytes) {
+  if (!codes_bytes || !absmax_q8_bytes || !absmax_c_bytes) return fail(QLR_ERR_NULL, "output pointer is NULL");
+  if (rows < 0 || cols < 0) return fail(QLR_ERR_SHAPE, "negative rows/cols");
+  if (!bits_ok(bits)) return fail(QLR_ERR_BITS, "bits %d not in {2,3,4,8}", bits);
+  if (block != QLR_BLOCK) return fail(QLR_ERR_BLOCK, "block %d, expected 64", block);
+  if (rows > 0 && cols > (INT64_C(1) << 40) / rows) return fail(QLR_ERR_SHAPE, "weight too large");
+  sizes_of(rows, cols, bits, codes_bytes, absmax_q8_bytes, absmax_c_bytes);
+  return QLR_OK;
+}
+
+qlr_status qlr_workspace_bytes(qlr_op op, int64_t M, int64_t N, int64_t K, int32_t r, size_t* bytes) {
+  (void)N;
+  (void)K;
+  if (!bytes) return fail(QLR_ERR_NULL, "bytes is NULL");
+  if (op == QLR_OP_QUANTIZE) {
+    *bytes = 256;
+    return QLR_OK;
+  }
+  if (op != QLR_OP_LINEAR) return fail(QLR_ERR_SHAPE, "unknown op %d", (int)op);
+  if (M < 0 || r < 0) return fail(QLR_ERR_SHAPE, "negative M or r");
+  *bytes = linear_ws_bytes(M, r);
+  return QLR_OK;
+}
+
+qlr_status qlr_quantize_async(const void* W, qlr_dtype wdt, int64_t rows, int64_t cols, int32_t bits,
+                              int32_t block, qlr_qweight* out, void* ws, size_t ws_bytes, void* stream) {
+  return quantize_common(W, wdt, rows, cols, bits, block, out, ws, ws_bytes,
+                         reinterpret_cast<hipStream_t>(stream));
+}
+
+qlr_status qlr_quantize(const void* W, qlr_dtype wdt, int64_t rows, int64_t cols, int32_t bits,
+                        int32_t block, qlr_qweight* out, void* ws, size_t ws_bytes, void* stream) {
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  qlr_status st = quantize_common(W, wdt, rows, cols, bits, block, out, ws, ws_bytes, s);
+  if (st != QLR_OK) return st;
+  uint32_t flag = 0;
+  hipError_t e = hipMemcpyAsync(&flag, ws, sizeof(flag), hipMemcpyDeviceToHost, s);
+  if (e != hipSuccess) return hip_fail(e, "flag read");
+  e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "stream synchronize");
+  if (flag != 0) return fail(QLR_ERR_NONFINITE, "W holds NaN or Inf");
+  return QLR_OK;
+}
+
+qlr_status qlr_dequantize(const qlr_qweight* w, void* out, qlr_dtype odt, void* stream) {
+  qlr_status st = check_qweight(w);
+  if (st != QLR_OK) return st;
+  if (!out) return fail(QLR_ERR_NULL, "out is NULL");
+  if (!(odt == QLR_F32 || odt == QLR_BF16)) return fail(QLR_ERR_DTYPE, "output dtype must be f32 or bf16");
+  if (!aligned16(out)) return fail(QLR_ERR_ALIGN, "out must be 16-byte aligned");
+  const int64_t numel = w->rows * w->cols;
+  if (numel == 0) return QLR_OK;
+  const qlr::Levels lv = levels_arg(w->bits);
+  hipError_t e = qlr::launch_dequantize(reinterpret_cast<const uint8_t*>(w->codes), w->absmax_q8, w->absmax_c,
+                                        numel, w->bits, lv, out, (int)odt,
+                                        reinterpret_cast<hipStream_t>(stream));
+  if (e != hipSuccess) return hip_fail(e, "dequantize launch");
+  return QLR_OK;
+}
+
+qlr_status qlr_linear_fwd(const void* x, qlr_dtype xdt, int64_t M, const qlr_qweight* w, const void* A,
+                          const void* B, qlr_dtype abdt, int32_t r, float scale, void* y, qlr_dtype ydt,
+                          void* ws, size_t ws_bytes, void* stream) {
+  const LinearCheck c{x, xdt, M, w, A, B, abdt, r, y, ydt};
+  qlr_status st = check_linear(c);
+  if (st != QLR_OK) return st;
+  const size_t need = linear_ws_bytes(M, r);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(QLR_ERR_WORKSPACE, "workspace of %zu bytes required, got %zu", need, ws ? ws_bytes : (size_t)0);
+  if (need > 0 && !aligned16(ws)) return fail(QLR_ERR_ALIGN, "workspace must be 16-byte aligned");
+  qlr_path path;
+  st = pick_path(M, xdt, abdt, r, &path);
+  if (st != QLR_OK) return st;
+  return run_linear(c, scale, reinterpret_cast<float*>(ws), path, reinterpret_cast<hipStream_t>(stream));
+}
+
+qlr_status qlr_linear_fwd_mixed(const qlr_layer* layers, int32_t n, int64_t M, qlr_dtype xdt, qlr_dtype abdt,
+                                qlr_dtype ydt, void* ws, size_t ws_bytes, void* stream) {
+  if (n < 0) return fail(QLR_ERR_SHAPE, "n < 0");
+  if (n > 0 && !layers) return fail(QLR_ERR_NULL, "layers is NULL");
+  size_t need = 0;
+  std::vector<std::pair<uintptr_t, uintptr_t>> outs, ins;
+  for (int32_t i = 0; i < n; ++i) {
+    const qlr_layer& L = layers[i];
+    const LinearCheck c{L.x, xdt, M, L.w, L.A, L.B, abdt, L.r, L.y, ydt};
+    qlr_status st = check_linear(c);
+    if (st != QLR_OK) return fail(st, "layer %d: %s", i, t_error.c_str());
+    qlr_path path;
+    st = pick_path(M, xdt, abdt, L.r, &path);
+    if (st != QLR_OK) return fail(st, "layer %d: %s", i, t_error.c_str());
+    need += linear_ws_bytes(M, L.r);
+    if (M > 0) {
+      const uintptr_t y0 = reinterpret_cast<uintptr_t>(L.y);
+      outs.push_back({y0, y0 + (uintptr_t)(M * L.w->rows) * dtype_size(ydt)});
+      const uintptr_t x0 = reinterpret_cast<uintptr_t>(L.x);
+      ins.push_back({x0, x0 + (uintptr_t)(M * L.w->cols) * dtype_size(xdt)});
+    }
+    if (L.r > 0) {
+      const uintptr_t a0 = reinterpret_cast<uintptr_t>(L.A), b0 = reinterpret_cast<uintptr_t>(L.B);
+      ins.push_back({a0, a0 + (uintptr_t)((int64_t)L.r * L.w->cols) * dtype_size(abdt)});
+      ins.push_back({b0, b0 + (uintptr_t)((int64_t)L.r * L.w->rows) * dtype_size(abdt)});
+    }
+  }
+  auto overlap = [](const std::pair<uintptr_t, uintptr_t>& p, const std::pair<uintptr_t, uintptr_t>& q) {
+    return p.first < q.second && q.first < p.second;
+  };
+  for (size_t i = 0; i < outs.size(); ++i) {
+    for (size_t j = i + 1; j < outs.size(); ++j)
+      if (overlap(outs[i], outs[j])) return fail(QLR_ERR_ALIAS, "outputs %zu and %zu overlap", i, j);
+    for (size_t j = 0; j < ins.size(); ++j)
+      if (overlap(outs[i], ins[j])) return fail(QLR_ERR_ALIAS, "output %zu overlaps an input", i);
+  }
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(QLR_ERR_WORKSPACE, "workspace of %zu bytes required", need);
+  if (need > 0 && !aligned16(ws)) return fail(QLR_ERR_ALIGN, "workspace must be 16-byte aligned");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* wsp = reinterpret_cast<char*>(ws);
+  for (int32_t i = 0; i < n; ++i) {
+    const qlr_layer& L = layers[i];
+    const LinearCheck c{L.x, xdt, M, L.w, L.A, L.B, abdt, L.r, L.y, ydt};
+    qlr_path path;
+    pick_path(M, xdt, abdt, L.r, &path);
+    qlr_status st = run_linear(c, L.scale, reinterpret_cast<float*>(wsp), path, s);
+    if (st != QLR_OK) return st;
+    wsp += linear_ws_bytes(M, L.r);
+  }
+  return QLR_OK;
+}
+
+qlr_status qlr_force_path(qlr_path path) {
+  if (path < QLR_PATH_AUTO || path > QLR_PATH_GEMM) return fail(QLR_ERR_PATH, "unknown path %d", (int)path);
+  t_path = path;
+  return QLR_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,53 @@
+// Internal launch interface between the host library (qlr_host.cpp) and the
+// kernel translation units.  Arguments are validated by the host library
+// before any of these is called.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "qlr_device.h"
+
+namespace qlr {
+
+hipError_t launch_fill_u32(uint32_t* p, uint32_t value, int64_t n, hipStream_t s);
+
+// Quantize numel elements of W (dtype wdt) into codes / absmax_q8 / absmax_c;
+// sets *flag nonzero if W holds a non-finite value (flag must be zero before).
+hipError_t launch_quantize(const void* W, int wdt, int64_t numel, int bits, const Levels& lv,
+                           uint8_t* codes, uint8_t* q8, float* cst, uint32_t* flag,
+                           hipStream_t s);
+
+hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* q8, const float* cst,
+                             int64_t numel, int bits, const Levels& lv, void* out, int odt,
+                             hipStream_t s);
+
+// t[M x r] (float32) = x[M x K] A[r x K]^T.
+hipError_t launch_lora_t(const void* x, int xdt, int64_t M, int64_t K, const void* A, int abdt,
+                         int r, float* t, hipStream_t s);
+
+struct LinearArgs {
+  const void* x;
+  int xdt;
+  int64_t M, N, K;
+  int bits;
+  const uint8_t* codes;
+  const uint8_t* q8;
+  const float* cst;
+  const float* t;  // M x r float32 (NULL if r == 0)
+  const void* B;   // N x r
+  int abdt;
+  int r;
+  float scale;
+  void* y;
+  int ydt;
+};
+
+// float32 path: any dtypes, any M.
+hipError_t launch_linear_f32(const LinearArgs& a, const Levels& lv, hipStream_t s);
+// bf16 decode path, M <= 16.
+hipError_t launch_gemv(const LinearArgs& a, const Levels& lv, hipStream_t s);
+// bf16 tiled GEMM path.
+hipError_t launch_gemm(const LinearArgs& a, const Levels& lv, hipStream_t s);
+
+}  // namespace qlr

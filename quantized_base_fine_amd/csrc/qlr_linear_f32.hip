@@ -1,0 +1,190 @@
+// Adapter product t = x A^T, and the float32 forward path.
+//
+// The forward is y = x W'^T + scale * (x A^T) B^T with the adapter kept as a
+// separate, unmerged branch (LoRDBA page, "adapter mode"; QLoRA page,
+// memory-decomposition equation: frozen quantized base, bf16 adapters).
+#include "qlr_internal.h"
+
+namespace qlr {
+
+namespace {
+
+// ---------------------------------------------------------------- t = x A^T
+
+// float32 arithmetic for any dtypes: one wave per (m, j), lanes split K.
+template <int XDT, int ADT>
+__global__ __launch_bounds__(256) void k_lora_t_valu(const void* __restrict__ x, int64_t M,
+                                                     int64_t K, const void* __restrict__ A, int r,
+                                                     float* __restrict__ t) {
+  const int lane = threadIdx.x & 63;
+  const int64_t item = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (item >= M * r) return;
+  const int64_t m = item / r;
+  const int j = (int)(item % r);
+  float acc = 0.0f;
+  for (int64_t k = lane; k < K; k += 64)
+    acc = fmaf(load_elem<XDT>(x, m * K + k), load_elem<ADT>(A, (int64_t)j * K + k), acc);
+  acc = wave_sum(acc);
+  if (lane == 0) t[m * r + j] = acc;
+}
+
+// bf16 x and A through 16x16x32 bf16 MFMA with float32 accumulation.  A
+// workgroup owns a 16-row tile of x and up to 64 adapter rows; its WAVES waves
+// split K and are reduced through LDS.
+template <int WAVES>
+__global__ __launch_bounds__(WAVES * 64) void k_lora_t_mfma(const uint16_t* __restrict__ x,
+                                                            int64_t M, int64_t K,
+                                                            const uint16_t* __restrict__ A, int r,
+                                                            float* __restrict__ t) {
+  __shared__ float sRed[WAVES][4][256];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int row = lane & 15, g = lane >> 4;
+  const int64_t m0 = (int64_t)blockIdx.x * 16;
+  const int j0 = blockIdx.y * 64;
+  const bool xv = m0 + row < M;
+  const uint16_t* xp = x + (xv ? (m0 + row) : 0) * K + g * 8;
+  const uint16_t* ap[4];
+  bool av[4];
+#pragma unroll
+  for (int jt = 0; jt < 4; ++jt) {
+    const int j = j0 + jt * 16 + row;
+    av[jt] = j < r;
+    ap[jt] = A + (int64_t)(av[jt] ? j : 0) * K + g * 8;
+  }
+  const int64_t nsteps = K / 32;
+  const int64_t s0 = nsteps * wave / WAVES, s1 = nsteps * (wave + 1) / WAVES;
+  f32x4_t acc[4] = {};
+  const u32x4_t zero = {0u, 0u, 0u, 0u};
+#pragma unroll 2
+  for (int64_t st = s0; st < s1; ++st) {
+    const int64_t k = st * 32;
+    const u32x4_t xa = xv ? *reinterpret_cast<const u32x4_t*>(xp + k) : zero;
+#pragma unroll
+    for (int jt = 0; jt < 4; ++jt) {
+      const u32x4_t ab = av[jt] ? *reinterpret_cast<const u32x4_t*>(ap[jt] + k) : zero;
+      acc[jt] = mfma16x16x32(as_bf16x8(xa), as_bf16x8(ab), acc[jt]);
+    }
+  }
+#pragma unroll
+  for (int jt = 0; jt < 4; ++jt)
+#pragma unroll
+    for (int v = 0; v < 4; ++v) sRed[wave][jt][lane * 4 + v] = acc[jt][v];
+  __syncthreads();
+  for (int idx = threadIdx.x; idx < 4 * 256; idx += WAVES * 64) {
+    const int jt = idx >> 8, e = idx & 255;
+    float s = 0.0f;
+#pragma unroll
+    for (int w = 0; w < WAVES; ++w) s += sRed[w][jt][e];
+    const int l = e >> 2, v = e & 3;
+    const int64_t m = m0 + 4 * (l >> 4) + v;  // MFMA output row
+    const int j = j0 + jt * 16 + (l & 15);     // MFMA output column
+    if (m < M && j < r) t[m * r + j] = s;
+  }
+}
+
+// ---------------------------------------------------------------- float32 forward
+
+// One wave per output row n; lanes take the 64 elements of each block; x rows in
+// chunks of 8.  w' is formed exactly as dequantization defines it.
+template <int BITS, int XDT, int BDT, int YDT>
+__global__ __launch_bounds__(256) void k_linear_f32(LinearArgs a, Levels lv) {
+  constexpr int NL = 1 << BITS;
+  __shared__ float sL[NL];
+  for (int i = threadIdx.x; i < NL; i += blockDim.x) sL[i] = lv.v[i];
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int64_t n = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (n >= a.N) return;
+  const int64_t nb = a.K / 64;
+  const int bit0 = BITS * lane, byte0 = bit0 >> 3, sh = bit0 & 7;
+  for (int64_t m0 = 0; m0 < a.M; m0 += 8) {
+    float acc[8] = {};
+    for (int64_t kb = 0; kb < nb; ++kb) {
+      const int64_t blk = n * nb + kb;
+      const uint8_t* cb = a.codes + blk * (8 * BITS);
+      uint32_t two = cb[byte0];
+      if (byte0 + 1 < 8 * BITS) two |= (uint32_t)cb[byte0 + 1] << 8;
+      const int c = (int)((two >> sh) & (NL - 1));
+      const float ap = (float)a.q8[blk] * a.cst[blk >> 8];
+      const float w = sL[c] * ap;
+      const int64_t k = kb * 64 + lane;
+#pragma unroll
+      for (int mm = 0; mm < 8; ++mm)
+        if (m0 + mm < a.M) acc[mm] = fmaf(load_elem<XDT>(a.x, (m0 + mm) * a.K + k), w, acc[mm]);
+    }
+#pragma unroll
+    for (int mm = 0; mm < 8; ++mm) {
+      const int64_t m = m0 + mm;
+      if (m >= a.M) break;
+      float base = wave_sum(acc[mm]);
+      float lo = 0.0f;
+      for (int j = lane; j < a.r; j += 64) lo = fmaf(a.t[m * a.r + j], load_elem<BDT>(a.B, n * a.r + j), lo);
+      lo = wave_sum(lo);
+      const float out = fmaf(a.scale, lo, base);
+      if (lane == 0) {
+        if constexpr (YDT == DT_F32) reinterpret_cast<float*>(a.y)[m * a.N + n] = out;
+        else reinterpret_cast<uint16_t*>(a.y)[m * a.N + n] = (uint16_t)f32_to_bf16_bits(out);
+      }
+    }
+  }
+}
+
+template <int BITS, int XDT, int BDT>
+hipError_t launch_f32_b3(const LinearArgs& a, const Levels& lv, hipStream_t s) {
+  dim3 grid((unsigned)((a.N + 3) / 4)), block(256);
+  if (a.ydt == DT_F32) hipLaunchKernelGGL((k_linear_f32<BITS, XDT, BDT, DT_F32>), grid, block, 0, s, a, lv);
+  else hipLaunchKernelGGL((k_linear_f32<BITS, XDT, BDT, DT_BF16>), grid, block, 0, s, a, lv);
+  return hipGetLastError();
+}
+
+template <int BITS, int XDT>
+hipError_t launch_f32_b2(const LinearArgs& a, const Levels& lv, hipStream_t s) {
+  if (a.abdt == DT_F32) return launch_f32_b3<BITS, XDT, DT_F32>(a, lv, s);
+  return launch_f32_b3<BITS, XDT, DT_BF16>(a, lv, s);
+}
+
+template <int BITS>
+hipError_t launch_f32_b1(const LinearArgs& a, const Levels& lv, hipStream_t s) {
+  if (a.xdt == DT_F32) return launch_f32_b2<BITS, DT_F32>(a, lv, s);
+  return launch_f32_b2<BITS, DT_BF16>(a, lv, s);
+}
+
+}  // namespace
+
+hipError_t launch_lora_t(const void* x, int xdt, int64_t M, int64_t K, const void* A, int abdt,
+                         int r, float* t, hipStream_t s) {
+  if (M == 0 || r == 0) return hipSuccess;
+  if (xdt == DT_BF16 && abdt == DT_BF16) {
+    dim3 grid((unsigned)((M + 15) / 16), (unsigned)((r + 63) / 64));
+    if (M <= 16) {
+      hipLaunchKernelGGL((k_lora_t_mfma<16>), grid, dim3(1024), 0, s,
+                         reinterpret_cast<const uint16_t*>(x), M, K,
+                         reinterpret_cast<const uint16_t*>(A), r, t);
+    } else {
+      hipLaunchKernelGGL((k_lora_t_mfma<4>), grid, dim3(256), 0, s,
+                         reinterpret_cast<const uint16_t*>(x), M, K,
+                         reinterpret_cast<const uint16_t*>(A), r, t);
+    }
+    return hipGetLastError();
+  }
+  const int64_t items = M * r;
+  dim3 grid((unsigned)((items + 3) / 4)), block(256);
+  if (xdt == DT_F32 && abdt == DT_F32)
+    hipLaunchKernelGGL((k_lora_t_valu<DT_F32, DT_F32>), grid, block, 0, s, x, M, K, A, r, t);
+  else if (xdt == DT_F32)
+    hipLaunchKernelGGL((k_lora_t_valu<DT_F32, DT_BF16>), grid, block, 0, s, x, M, K, A, r, t);
+  else
+    hipLaunchKernelGGL((k_lora_t_valu<DT_BF16, DT_F32>), grid, block, 0, s, x, M, K, A, r, t);
+  return hipGetLastError();
+}
+
+hipError_t launch_linear_f32(const LinearArgs& a, const Levels& lv, hipStream_t s) {
+  switch (a.bits) {
+    case 2: return launch_f32_b1<2>(a, lv, s);
+    case 3: return launch_f32_b1<3>(a, lv, s);
+    case 4: return launch_f32_b1<4>(a, lv, s);
+    default: return launch_f32_b1<8>(a, lv, s);
+  }
+}
+
+}  // namespace qlr

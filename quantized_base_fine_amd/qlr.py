@@ -1,0 +1,276 @@
+"""ctypes binding of ``libqlr.so`` (C ABI in ``include/qlr.h``).
+
+Argument marshalling only: torch tensors provide device memory and the
+current HIP stream; every step of the computation runs in the library's gfx950
+kernels.  There is no CPU fallback: if the library cannot be loaded, every call
+raises.
+"""
+from __future__ import annotations
+
+import contextlib
+import ctypes as C
+import os
+import threading
+from dataclasses import dataclass
+from typing import List, Optional, Sequence
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libqlr.so")
+
+FORMAT_VERSION = 1
+BLOCK = 64
+GROUP = 256
+
+QLR_F32, QLR_F16, QLR_BF16 = 0, 1, 2
+PATH_AUTO, PATH_F32, PATH_GEMV, PATH_GEMM = 0, 1, 2, 3
+OP_QUANTIZE, OP_LINEAR = 0, 1
+
+STATUS = {
+    0: "QLR_OK", 1: "QLR_ERR_NULL", 2: "QLR_ERR_SHAPE", 3: "QLR_ERR_DTYPE", 4: "QLR_ERR_BITS",
+    5: "QLR_ERR_BLOCK", 6: "QLR_ERR_ALIGN", 7: "QLR_ERR_NONFINITE", 8: "QLR_ERR_WORKSPACE",
+    9: "QLR_ERR_ALIAS", 10: "QLR_ERR_HIP", 11: "QLR_ERR_FORMAT", 12: "QLR_ERR_PATH",
+}
+
+
+class QlrError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        self.status = status
+        self.name = STATUS.get(status, str(status))
+        super().__init__(f"{self.name}: {detail}")
+
+
+class CQWeight(C.Structure):
+    _fields_ = [
+        ("format_version", C.c_uint32), ("bits", C.c_int32), ("block", C.c_int32),
+        ("group", C.c_int32), ("rows", C.c_int64), ("cols", C.c_int64),
+        ("codes", C.c_void_p), ("absmax_q8", C.c_void_p), ("absmax_c", C.c_void_p),
+    ]
+
+
+class CLayer(C.Structure):
+    _fields_ = [
+        ("w", C.POINTER(CQWeight)), ("x", C.c_void_p), ("A", C.c_void_p), ("B", C.c_void_p),
+        ("r", C.c_int32), ("scale", C.c_float), ("y", C.c_void_p),
+    ]
+
+
+EXPORTS = {
+    "qlr_version": (C.c_int, []),
+    "qlr_status_string": (C.c_char_p, [C.c_int]),
+    "qlr_last_error": (C.c_char_p, []),
+    "qlr_codebook": (C.c_int, [C.c_int32, C.POINTER(C.c_float)]),
+    "qlr_qweight_sizes": (C.c_int, [C.c_int64, C.c_int64, C.c_int32, C.c_int32,
+                                    C.POINTER(C.c_size_t), C.POINTER(C.c_size_t),
+                                    C.POINTER(C.c_size_t)]),
+    "qlr_workspace_bytes": (C.c_int, [C.c_int, C.c_int64, C.c_int64, C.c_int64, C.c_int32,
+                                      C.POINTER(C.c_size_t)]),
+    "qlr_quantize": (C.c_int, [C.c_void_p, C.c_int, C.c_int64, C.c_int64, C.c_int32, C.c_int32,
+                               C.POINTER(CQWeight), C.c_void_p, C.c_size_t, C.c_void_p]),
+    "qlr_quantize_async": (C.c_int, [C.c_void_p, C.c_int, C.c_int64, C.c_int64, C.c_int32,
+                                     C.c_int32, C.POINTER(CQWeight), C.c_void_p, C.c_size_t,
+                                     C.c_void_p]),
+    "qlr_dequantize": (C.c_int, [C.POINTER(CQWeight), C.c_void_p, C.c_int, C.c_void_p]),
+    "qlr_linear_fwd": (C.c_int, [C.c_void_p, C.c_int, C.c_int64, C.POINTER(CQWeight),
+                                 C.c_void_p, C.c_void_p, C.c_int, C.c_int32, C.c_float,
+                                 C.c_void_p, C.c_int, C.c_void_p, C.c_size_t, C.c_void_p]),
+    "qlr_linear_fwd_mixed": (C.c_int, [C.POINTER(CLayer), C.c_int32, C.c_int64, C.c_int, C.c_int,
+                                       C.c_int, C.c_void_p, C.c_size_t, C.c_void_p]),
+    "qlr_force_path": (C.c_int, [C.c_int]),
+}
+
+_lib = None
+_lock = threading.Lock()
+
+
+def lib():
+    """Load libqlr.so (building it first only if it does not exist)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    with _lock:
+        if _lib is None:
+            if not os.path.exists(LIB_PATH):
+                from .build import build
+                build()
+            handle = C.CDLL(LIB_PATH)
+            for name, (res, args) in EXPORTS.items():
+                fn = getattr(handle, name)
+                fn.restype = res
+                fn.argtypes = args
+            _lib = handle
+    return _lib
+
+
+def check(status: int) -> None:
+    if status != 0:
+        raise QlrError(status, lib().qlr_last_error().decode())
+
+
+# ---------------------------------------------------------------- host-only calls
+
+def codebook(bits: int) -> List[float]:
+    out = (C.c_float * (1 << bits))() if 1 <= bits <= 8 else (C.c_float * 1)()
+    check(lib().qlr_codebook(bits, out))
+    return list(out)
+
+
+def qweight_sizes(rows: int, cols: int, bits: int, block: int = BLOCK):
+    a, b, c = C.c_size_t(), C.c_size_t(), C.c_size_t()
+    check(lib().qlr_qweight_sizes(rows, cols, bits, block, C.byref(a), C.byref(b), C.byref(c)))
+    return a.value, b.value, c.value
+
+
+def workspace_bytes(op: int, M: int = 0, N: int = 0, K: int = 0, r: int = 0) -> int:
+    out = C.c_size_t()
+    check(lib().qlr_workspace_bytes(op, M, N, K, r, C.byref(out)))
+    return out.value
+
+
+_tls = threading.local()
+
+
+def force_path(path: int) -> None:
+    check(lib().qlr_force_path(path))
+    _tls.path = path
+
+
+@contextlib.contextmanager
+def path(p: int):
+    prev = getattr(_tls, "path", PATH_AUTO)
+    force_path(p)
+    try:
+        yield
+    finally:
+        force_path(prev)
+
+
+# ---------------------------------------------------------------- device calls (torch memory)
+
+def _torch():
+    import torch
+    return torch
+
+
+def _dt(t) -> int:
+    torch = _torch()
+    return {torch.float32: QLR_F32, torch.float16: QLR_F16, torch.bfloat16: QLR_BF16}[t.dtype]
+
+
+def _stream(device=None) -> C.c_void_p:
+    torch = _torch()
+    return C.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _ptr(t) -> Optional[int]:
+    return None if t is None else t.data_ptr()
+
+
+def _require_cuda(*tensors):
+    for t in tensors:
+        if t is not None and not t.is_cuda:
+            raise ValueError("qlr works on GPU tensors only")
+
+
+@dataclass
+class QWeight:
+    """A quantized frozen weight: header + three device buffers (torch uint8/float32)."""
+    bits: int
+    rows: int
+    cols: int
+    codes: "object"
+    absmax_q8: "object"
+    absmax_c: "object"
+
+    def c_struct(self) -> CQWeight:
+        return CQWeight(FORMAT_VERSION, self.bits, BLOCK, GROUP, self.rows, self.cols,
+                        self.codes.data_ptr(), self.absmax_q8.data_ptr(), self.absmax_c.data_ptr())
+
+    @staticmethod
+    def empty(rows: int, cols: int, bits: int, device) -> "QWeight":
+        torch = _torch()
+        cb, qb, kb = qweight_sizes(rows, cols, bits)
+        return QWeight(bits, rows, cols,
+                       torch.empty(max(cb, 1), dtype=torch.uint8, device=device),
+                       torch.empty(max(qb, 1), dtype=torch.uint8, device=device),
+                       torch.empty(max(kb // 4, 1), dtype=torch.float32, device=device))
+
+
+def quantize(W, bits: int, out: Optional[QWeight] = None, ws=None, blocking: bool = True) -> QWeight:
+    """Quantize a 2-D (rows x cols) float32/float16/bfloat16 device tensor."""
+    torch = _torch()
+    _require_cuda(W)
+    W = W.contiguous()
+    rows, cols = (W.shape[0], W.shape[1]) if W.dim() == 2 else (1, W.numel())
+    qw = out or QWeight.empty(rows, cols, bits, W.device)
+    if ws is None:
+        ws = torch.empty(workspace_bytes(OP_QUANTIZE), dtype=torch.uint8, device=W.device)
+    cw = qw.c_struct()
+    fn = lib().qlr_quantize if blocking else lib().qlr_quantize_async
+    check(fn(W.data_ptr(), _dt(W), rows, cols, bits, BLOCK, C.byref(cw), ws.data_ptr(),
+             ws.numel(), _stream(W.device)))
+    return qw
+
+
+def dequantize(qw: QWeight, dtype=None):
+    torch = _torch()
+    dtype = dtype or torch.float32
+    out = torch.empty((qw.rows, qw.cols), dtype=dtype, device=qw.codes.device)
+    cw = qw.c_struct()
+    check(lib().qlr_dequantize(C.byref(cw), out.data_ptr(), _dt(out), _stream(out.device)))
+    return out
+
+
+def linear(x, qw: QWeight, A=None, B=None, scale: float = 0.0, out_dtype=None, out=None, ws=None):
+    """y = x W'^T + scale (x A^T) B^T; x (M, K) float32/bfloat16 on the GPU."""
+    torch = _torch()
+    _require_cuda(x, A, B)
+    M = x.shape[0]
+    r = 0 if A is None else A.shape[0]
+    if x.shape[1] != qw.cols:
+        raise ValueError("x columns must equal the weight's cols")
+    if r > 0 and (A.shape != (r, qw.cols) or B.shape != (qw.rows, r) or A.dtype != B.dtype):
+        raise ValueError("A must be (r, K) and B (N, r) with one dtype")
+    y = out if out is not None else torch.empty((M, qw.rows), dtype=out_dtype or x.dtype, device=x.device)
+    need = workspace_bytes(OP_LINEAR, M, qw.rows, qw.cols, r)
+    if ws is None and need > 0:
+        ws = torch.empty(need, dtype=torch.uint8, device=x.device)
+    abdt = _dt(A) if r > 0 else QLR_BF16
+    cw = qw.c_struct()
+    check(lib().qlr_linear_fwd(x.data_ptr(), _dt(x), M, C.byref(cw), _ptr(A), _ptr(B), abdt, r,
+                               float(scale), y.data_ptr(), _dt(y), _ptr(ws),
+                               0 if ws is None else ws.numel(), _stream(x.device)))
+    return y
+
+
+def linear_mixed(entries: Sequence[dict], out_dtype=None, ws=None):
+    """Independent linears with per-entry (bits, rank).  Each entry: dict(x, qw, A, B, scale[, y])."""
+    torch = _torch()
+    if not entries:
+        return []
+    x0 = entries[0]["x"]
+    M = x0.shape[0]
+    ys, cws, layers = [], [], []
+    need = 0
+    abdt = QLR_BF16
+    for e in entries:
+        qw, x, A, B = e["qw"], e["x"], e.get("A"), e.get("B")
+        _require_cuda(x, A, B)
+        r = 0 if A is None else A.shape[0]
+        if r > 0:
+            abdt = _dt(A)
+        y = e.get("y")
+        if y is None:
+            y = torch.empty((M, qw.rows), dtype=out_dtype or x.dtype, device=x.device)
+        ys.append(y)
+        cws.append(qw.c_struct())
+        need += workspace_bytes(OP_LINEAR, M, qw.rows, qw.cols, r)
+    arr = (CLayer * len(entries))()
+    for i, e in enumerate(entries):
+        r = 0 if e.get("A") is None else e["A"].shape[0]
+        arr[i] = CLayer(C.pointer(cws[i]), e["x"].data_ptr(), _ptr(e.get("A")), _ptr(e.get("B")), r,
+                        float(e.get("scale", 0.0)), ys[i].data_ptr())
+    if ws is None and need > 0:
+        ws = torch.empty(need, dtype=torch.uint8, device=x0.device)
+    check(lib().qlr_linear_fwd_mixed(arr, len(entries), M, _dt(x0), abdt, _dt(ys[0]), _ptr(ws),
+                                     0 if ws is None else ws.numel(), _stream(x0.device)))
+    return ys

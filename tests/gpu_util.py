@@ -1,0 +1,96 @@
+"""Helpers for the GPU parity tests (host <-> device marshalling, oracle on sampled rows)."""
+import numpy as np
+
+import oracle
+
+BLOCK, GROUP = 64, 256
+
+
+def dev(arr, dtype, device="cuda"):
+    """numpy storage array -> torch device tensor ('bf16' arrays are uint16 bit patterns)."""
+    import torch
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(arr).view(np.int16)).to(device).view(torch.bfloat16)
+    if dtype == "f16":
+        return torch.from_numpy(np.ascontiguousarray(arr)).to(device)
+    return torch.from_numpy(np.ascontiguousarray(arr, dtype=np.float32)).to(device)
+
+
+def host(t):
+    """torch device tensor -> numpy (bf16 returned as uint16 bits)."""
+    import torch
+    t = t.detach().cpu()
+    if t.dtype == torch.bfloat16:
+        return t.view(torch.int16).numpy().view(np.uint16)
+    return t.numpy()
+
+
+def f32_of(t):
+    import torch
+    return t.detach().float().cpu().numpy()
+
+
+def groups_covering(K, rows, numel):
+    """Sorted DQ-group indices that contain the blocks of the given weight rows."""
+    nb = K // BLOCK
+    gs = set()
+    for n in rows:
+        gs.update(range((n * nb) // GROUP, ((n + 1) * nb - 1) // GROUP + 1))
+    return sorted(gs)
+
+
+def oracle_groups(W, wdtype, bits, groups):
+    """Oracle quantization of the listed DQ groups of a weight (flattened).
+
+    Returns {group: QuantizedWeight of that group's 16384 elements}.  Groups are
+    independent, so quantizing a group alone gives the same codes and scales as
+    quantizing the whole weight.
+    """
+    flat = W.reshape(-1)
+    out = {}
+    per = BLOCK * GROUP
+    for g in groups:
+        out[g] = oracle.quantize(flat[g * per:(g + 1) * per], wdtype, bits)
+    return out
+
+
+def oracle_rows_dequant(W, wdtype, bits, rows):
+    """float32 dequantized rows (len(rows), K) computed by the oracle alone."""
+    N, K = W.shape
+    qg = oracle_groups(W, wdtype, bits, groups_covering(K, rows, W.size))
+    per = BLOCK * GROUP
+    out = np.empty((len(rows), K), dtype=np.float32)
+    for i, n in enumerate(rows):
+        e0, e1 = n * K, (n + 1) * K
+        seg = []
+        g = e0 // per
+        while g * per < e1:
+            q = qg[g]
+            d = oracle.dequantize(q.codes, q.absmax_q8, q.absmax_c, bits, q.numel)
+            lo, hi = max(e0, g * per) - g * per, min(e1, (g + 1) * per) - g * per
+            seg.append(d[lo:hi])
+            g += 1
+        out[i] = np.concatenate(seg)
+    return out
+
+
+def check_linear(y_gpu, lin, wdeq_rows, rows, ydt="f32", ms=None):
+    """Per-element bound |y - y_ref| <= 1e-3 * S + 1e-5 (+ half a bf16 ulp for bf16 y).
+
+    ``wdeq_rows``: oracle-dequantized rows ``rows`` of W'; ``ms``: x rows to check.
+    Returns the worst ratio error / bound.
+    """
+    x = lin.x if ms is None else lin.x[ms]
+    A, B = lin.A, (None if lin.B is None else lin.B[rows])
+    yref = oracle.linear(x, lin.xdtype, wdeq_rows, A, B, lin.abdtype, lin.scale)
+    S = oracle.linear_tolerance(x, lin.xdtype, wdeq_rows)
+    bound = 1e-3 * S + 1e-5
+    if ydt == "bf16":
+        bound = bound + np.abs(yref) * 2.0 ** -9
+    got = y_gpu if ms is None else y_gpu[ms]
+    got = got[:, rows].astype(np.float64)
+    err = np.abs(got - yref)
+    ratio = float(np.max(err / bound)) if err.size else 0.0
+    assert np.all(np.isfinite(got))
+    assert np.all(err <= bound), f"max err/bound {ratio:.3f}"
+    return ratio

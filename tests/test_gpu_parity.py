@@ -1,0 +1,266 @@
+"""GPU parity: the HIP path against the CPU oracle, through the C ABI.
+
+Codes, 8-bit absmax codes, group steps and dequantized float32 weights must be
+bit-exact; linear outputs must satisfy |y - y_ref| <= 1e-3 sum_k |x w'| + 1e-5
+per element (plus half a bf16 ulp for bf16 outputs).
+"""
+import numpy as np
+import pytest
+
+import oracle
+import workloads
+from gpu_util import check_linear, dev, f32_of, host, oracle_groups, oracle_rows_dequant
+
+torch = pytest.importorskip("torch")
+pytestmark = pytest.mark.gpu
+
+from quantized_base_fine_amd import qlr  # noqa: E402
+
+BITS = [2, 3, 4, 8]
+
+
+def _gpu_quant(W, wdtype, bits):
+    Wd = dev(W, wdtype)
+    qw = qlr.quantize(Wd if Wd.dim() == 2 else Wd.reshape(1, -1), bits)
+    torch.cuda.synchronize()
+    return qw
+
+
+def _assert_qweight_equal(qw, ref, groups=None):
+    codes, q8, cst = host(qw.codes), host(qw.absmax_q8), host(qw.absmax_c)
+    if groups is None:
+        assert np.array_equal(codes[: ref.codes.size], ref.codes)
+        assert np.array_equal(q8[: ref.absmax_q8.size], ref.absmax_q8)
+        assert np.array_equal(cst[: ref.absmax_c.size].view(np.uint32), ref.absmax_c.view(np.uint32))
+        return
+    for g, rq in groups.items():
+        cb = 8 * qw.bits * 256
+        assert np.array_equal(codes[g * cb:(g + 1) * cb], rq.codes), g
+        assert np.array_equal(q8[g * 256:(g + 1) * 256], rq.absmax_q8), g
+        assert cst[g].view(np.uint32) == rq.absmax_c[0].view(np.uint32), g
+
+
+def _rand_w(shape, dtype, seed, scale=0.02):
+    rng = np.random.default_rng(seed)
+    w = (rng.standard_normal(shape) * scale).astype(np.float32)
+    return workloads.store(w, dtype)
+
+
+# ---------------------------------------------------------------- quantize / dequantize
+
+@pytest.mark.parametrize("bits", BITS)
+@pytest.mark.parametrize("wdtype", ["f32", "f16", "bf16"])
+@pytest.mark.parametrize("shape", [(256, 256), (37, 101), (3, 2 * 16384 + 64 * 5 + 3)])
+def test_quantize_bitexact(bits, wdtype, shape):
+    W = _rand_w(shape, wdtype, seed=bits * 100 + len(wdtype) + shape[0])
+    qw = _gpu_quant(W, wdtype, bits)
+    ref = oracle.quantize(W.reshape(-1), wdtype, bits)
+    _assert_qweight_equal(qw, ref)
+
+
+@pytest.mark.parametrize("bits", BITS)
+def test_quantize_special_values(bits):
+    """Zero blocks, +-0, exact ties at level midpoints, absmax on both signs."""
+    L = oracle.quantile_codebook(bits)
+    n = L.size
+    w = np.zeros((8, 64), dtype=np.float32)
+    w[1, 0], w[1, 1], w[1, 2], w[1, 3] = 0.5, -0.0, 0.0, -0.5
+    w[2, :] = -3.0
+    mids = [(float(L[i]) + float(L[i + 1])) for i in range(n - 1)]
+    k = 0
+    for i, m in enumerate(mids):  # exact midpoints for absmax 2.0 (tie -> lower)
+        if float(np.float32(m)) == m and abs(m) <= 2.0 and k < 63:
+            w[3, 1 + k] = m
+            k += 1
+    w[3, 0] = 2.0
+    w[4, :] = np.float32(1e-40)  # subnormal absmax
+    w[5, ::2] = 1e-30
+    w[6, 5] = -7.0
+    qw = _gpu_quant(w.reshape(1, -1), "f32", bits)
+    ref = oracle.quantize(w.reshape(-1), "f32", bits)
+    _assert_qweight_equal(qw, ref)
+    back = host(qlr.dequantize(qw, torch.float32)).reshape(-1)
+    refd = oracle.dequantize(ref.codes, ref.absmax_q8, ref.absmax_c, bits, w.size)
+    assert np.array_equal(back.view(np.uint32), refd.view(np.uint32))
+
+
+@pytest.mark.parametrize("bits", BITS)
+@pytest.mark.parametrize("shape", [(256, 256), (37, 101), (300, 1000)])
+def test_dequantize_bitexact(bits, shape):
+    W = _rand_w(shape, "f16", seed=7 + bits)
+    qw = _gpu_quant(W, "f16", bits)
+    ref = oracle.quantize(W.reshape(-1), "f16", bits)
+    refd = oracle.dequantize(ref.codes, ref.absmax_q8, ref.absmax_c, bits, W.size)
+    got = host(qlr.dequantize(qw, torch.float32)).reshape(-1)
+    assert np.array_equal(got.view(np.uint32), refd.view(np.uint32))  # signed zeros included
+    gotb = host(qlr.dequantize(qw, torch.bfloat16)).reshape(-1)
+    assert np.array_equal(gotb, workloads.to_bf16_bits(refd))
+
+
+def test_quantize_nonfinite_rejected():
+    W = _rand_w((64, 128), "f16", seed=1)
+    W[10, 77] = np.float16(np.inf)
+    with pytest.raises(qlr.QlrError) as ei:
+        _gpu_quant(W, "f16", 4)
+    assert ei.value.name == "QLR_ERR_NONFINITE"
+    W[10, 77] = np.float16(np.nan)
+    Wd = dev(W, "f16")
+    ws = torch.zeros(256, dtype=torch.uint8, device="cuda")
+    qlr.quantize(Wd, 4, ws=ws, blocking=False)
+    torch.cuda.synchronize()
+    assert host(ws)[:4].view(np.uint32)[0] != 0
+
+
+def test_quantize_attn_full():
+    """7B-class attention projection, 4096 x 4096 fp16 with 0.1% x20 outliers: every code."""
+    lin = workloads.attn(1)
+    qw = _gpu_quant(lin.W, "f16", 4)
+    ref = oracle.quantize(lin.W.reshape(-1), "f16", 4)
+    _assert_qweight_equal(qw, ref)
+    got = host(qlr.dequantize(qw, torch.float32)).reshape(-1)
+    refd = oracle.dequantize(ref.codes, ref.absmax_q8, ref.absmax_c, 4, lin.W.size)
+    assert np.array_equal(got.view(np.uint32), refd.view(np.uint32))
+
+
+@pytest.mark.parametrize("which", ["up", "down", "big65"])
+def test_quantize_large_sampled_groups(which):
+    """MLP and 65B-class weights: sampled double-quantization groups, bit-exact."""
+    lin = workloads.big65(1) if which == "big65" else workloads.mlp(which, 1)
+    qw = _gpu_quant(lin.W, "f16", 4)
+    ngroups = qw.absmax_c.numel()
+    rng = np.random.default_rng(5)
+    groups = sorted(set([0, ngroups - 1] + rng.choice(ngroups, size=24, replace=False).tolist()))
+    _assert_qweight_equal(qw, None, oracle_groups(lin.W, "f16", 4, groups))
+
+
+# ---------------------------------------------------------------- linear forward
+
+def _run_linear(lin, qw, ydt="f32", path=qlr.PATH_AUTO):
+    x = dev(lin.x, lin.xdtype)
+    A = dev(lin.A, lin.abdtype) if lin.r > 0 else None
+    B = dev(lin.B, lin.abdtype) if lin.r > 0 else None
+    with qlr.path(path):
+        y = qlr.linear(x, qw, A, B, lin.scale, out_dtype=torch.float32 if ydt == "f32" else torch.bfloat16)
+    torch.cuda.synchronize()
+    return f32_of(y)
+
+
+def _small_linear(N, K, M, bits, r, seed, xdtype="bf16", abdtype="bf16"):
+    return workloads.make_linear(f"s{seed}", 50 + seed, N, K, M, sigma=0.02, wdtype="f16", bits=bits,
+                                 r=r, alpha=16.0, abdtype=abdtype, xdtype=xdtype)
+
+
+PATHS = {"gemv": qlr.PATH_GEMV, "gemm": qlr.PATH_GEMM, "f32": qlr.PATH_F32}
+
+
+@pytest.mark.parametrize("bits", BITS)
+@pytest.mark.parametrize("path,M", [("gemv", 1), ("gemv", 5), ("gemv", 16), ("gemm", 1), ("gemm", 100),
+                                    ("gemm", 300), ("f32", 3), ("f32", 20)])
+@pytest.mark.parametrize("r", [0, 4, 16, 72])
+def test_linear_paths_small(bits, path, M, r):
+    """Ragged N (not a multiple of 16 or 128), K of 10 blocks, every path, bits and rank."""
+    lin = _small_linear(333, 640, M, bits, r, seed=bits + M + r)
+    qw = _gpu_quant(lin.W, "f16", bits)
+    rows = list(range(lin.N))
+    wd = oracle_rows_dequant(lin.W, "f16", bits, rows)
+    for ydt in ("f32", "bf16"):
+        y = _run_linear(lin, qw, ydt, PATHS[path])
+        check_linear(y, lin, wd, rows, ydt)
+
+
+@pytest.mark.parametrize("path", ["gemv", "gemm", "f32"])
+def test_linear_long_k_tail(path):
+    """K = 11008 (172 blocks: DQ groups straddle rows), N = 100, every path."""
+    M = 7 if path != "gemm" else 130
+    lin = _small_linear(100, 11008, M, 4, 64, seed=3)
+    qw = _gpu_quant(lin.W, "f16", 4)
+    rows = list(range(lin.N))
+    wd = oracle_rows_dequant(lin.W, "f16", 4, rows)
+    check_linear(_run_linear(lin, qw, "f32", PATHS[path]), lin, wd, rows)
+
+
+def test_linear_tiny_config():
+    """256x256 fp32 weights, rank-4 fp32 adapters, 8x256 fp32 x (float32 path)."""
+    lin = workloads.tiny()
+    qw = _gpu_quant(lin.W, "f32", 4)
+    rows = list(range(lin.N))
+    wd = oracle_rows_dequant(lin.W, "f32", 4, rows)
+    check_linear(_run_linear(lin, qw), lin, wd, rows)
+
+
+def test_linear_attn_full():
+    """4096x4096 with outliers, r16: M=1 (decode) and M=2048 (prefill), every output."""
+    base = workloads.attn(1)
+    qw = _gpu_quant(base.W, "f16", 4)
+    rows = list(range(base.N))
+    ref = oracle.quantize(base.W.reshape(-1), "f16", 4)
+    wd = oracle.dequantize(ref.codes, ref.absmax_q8, ref.absmax_c, 4, base.W.size).reshape(base.W.shape)
+    for M in (1, 2048):
+        lin = workloads.attn(M, W=base.W)
+        check_linear(_run_linear(lin, qw, "bf16"), lin, wd, rows, "bf16")
+        check_linear(_run_linear(lin, qw, "f32"), lin, wd, rows, "f32")
+
+
+@pytest.mark.parametrize("which", ["up", "down"])
+def test_linear_mlp_sampled(which):
+    """7B-class MLP projections, r64: M = 1, 16, 2048 on sampled output columns."""
+    base = workloads.mlp(which, 1)
+    qw = _gpu_quant(base.W, "f16", 4)
+    rng = np.random.default_rng(2)
+    rows = sorted(set([0, base.N - 1] + rng.choice(base.N, size=30, replace=False).tolist()))
+    wd = oracle_rows_dequant(base.W, "f16", 4, rows)
+    for M in (1, 16, 2048):
+        lin = workloads.mlp(which, M, W=base.W)
+        check_linear(_run_linear(lin, qw, "bf16"), lin, wd, rows, "bf16")
+
+
+def test_linear_big65_sampled():
+    """65B-class 22016x8192, r64: M = 1 and 4096 on sampled rows and columns."""
+    base = workloads.big65(1)
+    qw = _gpu_quant(base.W, "f16", 4)
+    rng = np.random.default_rng(3)
+    rows = sorted(set([0, base.N - 1] + rng.choice(base.N, size=24, replace=False).tolist()))
+    wd = oracle_rows_dequant(base.W, "f16", 4, rows)
+    for M in (1, 4096):
+        lin = workloads.big65(M, W=base.W)
+        ms = sorted(set([0, M - 1] + rng.choice(M, size=min(M, 40), replace=False).tolist()))
+        check_linear(_run_linear(lin, qw, "bf16"), lin, wd, rows, "bf16", ms=ms)
+
+
+def test_linear_edge_cases():
+    lin = _small_linear(96, 256, 4, 4, 8, seed=9)
+    qw = _gpu_quant(lin.W, "f16", 4)
+    x = dev(lin.x, "bf16")
+    A, B = dev(lin.A, "bf16"), dev(lin.B, "bf16")
+    for p in (qlr.PATH_GEMV, qlr.PATH_GEMM, qlr.PATH_F32):
+        with qlr.path(p):
+            y0 = qlr.linear(x, qw, out_dtype=torch.float32)                  # r = 0
+            yb = qlr.linear(x, qw, A, torch.zeros_like(B), 2.0, out_dtype=torch.float32)  # B = 0
+            y1 = qlr.linear(x, qw, A, B, lin.scale, out_dtype=torch.float32)
+            y2 = qlr.linear(x, qw, A, B, lin.scale, out_dtype=torch.float32)
+            e = qlr.linear(x[:0], qw, A, B, lin.scale, out_dtype=torch.float32)  # M = 0
+        torch.cuda.synchronize()
+        assert torch.equal(y0, yb)
+        assert torch.equal(y1, y2)  # deterministic: no atomics on the output path
+        assert e.shape == (0, 96)
+
+
+# ---------------------------------------------------------------- mixed stack
+
+def test_mixed_small():
+    """Per-layer (bits, rank) drawn as for the mixed stack, shrunk shapes, M = 48 and M = 8."""
+    plan = workloads.mixed_plan()
+    for M in (48, 8):
+        lins = [workloads.mixed_linear(i, M=M, plan=plan, shape_override=(200 + 16 * (i % 3), 384 + 64 * (i % 2)))
+                for i in range(10)]
+        entries, qws = [], []
+        for lin in lins:
+            qw = _gpu_quant(lin.W, "f16", lin.bits)
+            qws.append(qw)
+            entries.append(dict(x=dev(lin.x, "bf16"), qw=qw, A=dev(lin.A, "bf16"), B=dev(lin.B, "bf16"),
+                                scale=lin.scale))
+        ys = qlr.linear_mixed(entries, out_dtype=torch.float32)
+        torch.cuda.synchronize()
+        for lin, y in zip(lins, ys):
+            rows = list(range(lin.N))
+            check_linear(f32_of(y), lin, oracle_rows_dequant(lin.W, "f16", lin.bits, rows), rows)

@@ -1,0 +1,156 @@
+"""Host-side tests of libqlr.so: it loads, exports every declared symbol, and its
+host logic (codebook, size queries, argument validation) behaves.  No kernel is
+launched here: every call below either is host-only or fails validation before
+any HIP call."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from quantized_base_fine_amd import qlr
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def declared_symbols():
+    text = open(os.path.join(ROOT, "include", "qlr.h")).read()
+    return sorted(set(re.findall(r"^\w[\w\s\*]*?\b(qlr_\w+)\(", text, flags=re.M)))
+
+
+def test_header_declares_the_entry_points():
+    syms = declared_symbols()
+    for name in ["qlr_quantize", "qlr_dequantize", "qlr_linear_fwd", "qlr_linear_fwd_mixed",
+                 "qlr_codebook", "qlr_qweight_sizes", "qlr_workspace_bytes"]:
+        assert name in syms
+
+
+def test_library_exports_every_declared_symbol():
+    lib = qlr.lib()
+    for name in declared_symbols():
+        assert hasattr(lib, name), name
+        assert name in qlr.EXPORTS, name  # the binding knows its signature
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+def test_codebook_bit_equal_to_oracle(bits):
+    got = np.array(qlr.codebook(bits), dtype=np.float32)
+    ref = oracle.quantile_codebook(bits)
+    assert np.array_equal(got.view(np.uint32), ref.view(np.uint32))
+
+
+@pytest.mark.parametrize("bits", [2, 3, 4, 8])
+@pytest.mark.parametrize("shape", [(1, 1), (1, 64), (37, 101), (256, 256), (4096, 11008), (22016, 8192)])
+def test_sizes_match_oracle(bits, shape):
+    assert qlr.qweight_sizes(shape[0], shape[1], bits) == oracle.qweight_sizes(shape[0], shape[1], bits)
+
+
+def test_workspace_sizes():
+    assert qlr.workspace_bytes(qlr.OP_QUANTIZE) == 256
+    assert qlr.workspace_bytes(qlr.OP_LINEAR, 0, 4096, 4096, 16) == 0
+    assert qlr.workspace_bytes(qlr.OP_LINEAR, 7, 4096, 4096, 0) == 0
+    assert qlr.workspace_bytes(qlr.OP_LINEAR, 2048, 4096, 4096, 16) == 2048 * 16 * 4
+    assert qlr.workspace_bytes(qlr.OP_LINEAR, 3, 10, 64, 5) == 256
+
+
+def _status(fn, *args):
+    return qlr.STATUS[fn(*args)]
+
+
+def test_status_strings_and_last_error():
+    lib = qlr.lib()
+    for code in qlr.STATUS:
+        assert lib.qlr_status_string(code)
+    assert lib.qlr_codebook(5, (C.c_float * 32)()) == 4
+    assert b"bits 5" in lib.qlr_last_error()
+
+
+def test_size_query_errors():
+    lib = qlr.lib()
+    a = C.c_size_t()
+    assert _status(lib.qlr_qweight_sizes, 4, 4, 5, 64, C.byref(a), C.byref(a), C.byref(a)) == "QLR_ERR_BITS"
+    assert _status(lib.qlr_qweight_sizes, 4, 4, 4, 32, C.byref(a), C.byref(a), C.byref(a)) == "QLR_ERR_BLOCK"
+    assert _status(lib.qlr_qweight_sizes, -1, 4, 4, 64, C.byref(a), C.byref(a), C.byref(a)) == "QLR_ERR_SHAPE"
+    assert _status(lib.qlr_qweight_sizes, 4, 4, 4, 64, None, C.byref(a), C.byref(a)) == "QLR_ERR_NULL"
+    assert _status(lib.qlr_codebook, 4, None) == "QLR_ERR_NULL"
+    assert _status(lib.qlr_force_path, 9) == "QLR_ERR_PATH"
+
+
+FAKE = 0x10000  # a 16-byte-aligned address that validation never dereferences
+
+
+def _qw(bits=4, rows=64, cols=128, ver=1, block=64, group=256, codes=FAKE, q8=FAKE, c=FAKE):
+    return qlr.CQWeight(ver, bits, block, group, rows, cols, codes, q8, c)
+
+
+def _lin(w, x=FAKE, xdt=qlr.QLR_BF16, M=4, A=FAKE, B=FAKE, abdt=qlr.QLR_BF16, r=4, y=FAKE,
+         ydt=qlr.QLR_F32, ws=FAKE, wsb=1 << 20):
+    lib = qlr.lib()
+    return qlr.STATUS[lib.qlr_linear_fwd(x, xdt, M, C.byref(w), A, B, abdt, r, 1.0, y, ydt, ws, wsb, None)]
+
+
+def test_linear_validation_errors():
+    assert _lin(_qw(bits=5)) == "QLR_ERR_BITS"
+    assert _lin(_qw(ver=2)) == "QLR_ERR_FORMAT"
+    assert _lin(_qw(block=32)) == "QLR_ERR_BLOCK"
+    assert _lin(_qw(group=128)) == "QLR_ERR_BLOCK"
+    assert _lin(_qw(cols=100)) == "QLR_ERR_SHAPE"
+    assert _lin(_qw(codes=0)) == "QLR_ERR_NULL"
+    assert _lin(_qw(q8=FAKE + 8)) == "QLR_ERR_ALIGN"
+    assert _lin(_qw(), x=0) == "QLR_ERR_NULL"
+    assert _lin(_qw(), x=FAKE + 2) == "QLR_ERR_ALIGN"
+    assert _lin(_qw(), A=0) == "QLR_ERR_NULL"
+    assert _lin(_qw(), M=-1) == "QLR_ERR_SHAPE"
+    assert _lin(_qw(), r=-1) == "QLR_ERR_SHAPE"
+    assert _lin(_qw(), xdt=qlr.QLR_F16) == "QLR_ERR_DTYPE"
+    assert _lin(_qw(), ydt=7) == "QLR_ERR_DTYPE"
+    assert _lin(_qw(), ws=0) == "QLR_ERR_WORKSPACE"
+    assert _lin(_qw(), wsb=16) == "QLR_ERR_WORKSPACE"
+    assert _lin(_qw(), M=0, x=0, y=0) == "QLR_OK"  # nothing to do, nothing launched
+
+
+def test_forced_path_errors():
+    lib = qlr.lib()
+    try:
+        lib.qlr_force_path(qlr.PATH_GEMV)
+        assert _lin(_qw(), M=17) == "QLR_ERR_PATH"
+        assert _lin(_qw(), xdt=qlr.QLR_F32) == "QLR_ERR_PATH"
+        lib.qlr_force_path(qlr.PATH_GEMM)
+        assert _lin(_qw(), abdt=qlr.QLR_F32) == "QLR_ERR_PATH"
+    finally:
+        lib.qlr_force_path(qlr.PATH_AUTO)
+
+
+def _quant(W=FAKE, wdt=qlr.QLR_F16, rows=64, cols=128, bits=4, block=64, out=None, ws=FAKE, wsb=256):
+    out = out or _qw(bits=bits, rows=rows, cols=cols)
+    return qlr.STATUS[qlr.lib().qlr_quantize(W, wdt, rows, cols, bits, block, C.byref(out), ws, wsb, None)]
+
+
+def test_quantize_validation_errors():
+    assert _quant(W=0) == "QLR_ERR_NULL"
+    assert _quant(wdt=9) == "QLR_ERR_DTYPE"
+    assert _quant(bits=5) == "QLR_ERR_BITS"
+    assert _quant(block=128) == "QLR_ERR_BLOCK"
+    assert _quant(rows=0) == "QLR_ERR_SHAPE"
+    assert _quant(out=_qw(rows=65, cols=128)) == "QLR_ERR_SHAPE"
+    assert _quant(W=FAKE + 4) == "QLR_ERR_ALIGN"
+    assert _quant(ws=0) == "QLR_ERR_WORKSPACE"
+    assert _quant(wsb=64) == "QLR_ERR_WORKSPACE"
+
+
+def test_mixed_alias_detection():
+    lib = qlr.lib()
+    w = _qw(rows=64, cols=128)
+    arr = (qlr.CLayer * 2)()
+    arr[0] = qlr.CLayer(C.pointer(w), 0x100000, 0, 0, 0, 0.0, 0x200000)
+    arr[1] = qlr.CLayer(C.pointer(w), 0x300000, 0, 0, 0, 0.0, 0x200000 + 64)  # overlaps y0
+    assert qlr.STATUS[lib.qlr_linear_fwd_mixed(arr, 2, 4, qlr.QLR_BF16, qlr.QLR_BF16, qlr.QLR_F32,
+                                               None, 0, None)] == "QLR_ERR_ALIAS"
+    arr[1] = qlr.CLayer(C.pointer(w), 0x200000 + 16, 0, 0, 0, 0.0, 0x400000)  # x1 inside y0
+    assert qlr.STATUS[lib.qlr_linear_fwd_mixed(arr, 2, 4, qlr.QLR_BF16, qlr.QLR_BF16, qlr.QLR_F32,
+                                               None, 0, None)] == "QLR_ERR_ALIAS"
+    arr[1] = qlr.CLayer(C.pointer(_qw(bits=7)), 0x300000, 0, 0, 0, 0.0, 0x500000)
+    assert qlr.STATUS[lib.qlr_linear_fwd_mixed(arr, 2, 4, qlr.QLR_BF16, qlr.QLR_BF16, qlr.QLR_F32,
+                                               None, 0, None)] == "QLR_ERR_BITS"
