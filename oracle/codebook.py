@@ -16,6 +16,8 @@ Readings (the page leaves these open or prints them garbled):
 """
 from __future__ import annotations
 
+import functools
+
 import mpmath
 import numpy as np
 
@@ -40,6 +42,11 @@ def _round_f32(v: mpmath.mpf) -> float:
 
 def quantile_codebook(bits: int) -> np.ndarray:
     """The 2^bits ascending float32 levels L[0..2^bits-1] (readings above)."""
+    return _codebook(bits).copy()
+
+
+@functools.lru_cache(maxsize=None)
+def _codebook(bits: int) -> np.ndarray:
     if bits < 1 or bits > 8:
         raise ValueError("bits must be in 1..8")
     n = 1 << bits

@@ -62,6 +62,18 @@ __device__ __forceinline__ f32x16_t mfma32x32x16(bf16x8_t a, bf16x8_t b, f32x16_
   return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
 }
 
+// Copy the NL codebook levels of the by-value kernel argument into LDS.  The
+// loop index is the same for every lane, so the argument is read with scalar
+// loads; indexing the argument per lane would turn into slow vector loads from
+// the kernel-argument segment.  Callers synchronise the workgroup afterwards.
+template <int NL>
+__device__ __forceinline__ void stage_levels(const Levels& lv, float* sL) {
+  if (threadIdx.x == 0) {
+#pragma unroll
+    for (int i = 0; i < NL; ++i) sL[i] = lv.v[i];
+  }
+}
+
 __device__ __forceinline__ bf16x8_t as_bf16x8(u32x4_t v) { return __builtin_bit_cast(bf16x8_t, v); }
 
 }  // namespace qlr

@@ -53,7 +53,7 @@ __global__ __launch_bounds__(256) void k_gemm(LinearArgs a, Levels lv) {
   __shared__ float sL[NL];
 
   const int tid = threadIdx.x;
-  for (int i = tid; i < NL; i += 256) sL[i] = lv.v[i];
+  stage_levels<NL>(lv, sL);
 
   const int lane = tid & 63, wave = tid >> 6;
   const int wm = wave >> 1, wn = wave & 1;
@@ -141,7 +141,9 @@ __global__ __launch_bounds__(256) void k_gemm(LinearArgs a, Levels lv) {
           const int j = kk < rp ? kk : kk - rp;
           if (j < r) {
             if (xv) {
-              const float st = a.scale * a.t[xm * r + j];
+              float tj = 0.0f;
+              for (int sp = 0; sp < a.t_splits; ++sp) tj += a.t[((int64_t)sp * M + xm) * r + j];
+              const float st = a.scale * tj;
               const uint32_t hi = f32_to_bf16_bits(st);
               xv16 = (uint16_t)(kk < rp ? hi : f32_to_bf16_bits(st - bf16_bits_to_f32(hi)));
             }

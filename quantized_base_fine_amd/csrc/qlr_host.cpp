@@ -11,7 +11,7 @@
 #include <string>
 #include <vector>
 
-#include "../../include/qlr.h"
+#include "qlr.h"
 #include "qlr_internal.h"
 
 namespace {
@@ -112,9 +112,15 @@ qlr_status check_qweight(const qlr_qweight* w) {
   return QLR_OK;
 }
 
-size_t linear_ws_bytes(int64_t M, int32_t r) {
+// Workspace of one linear call: 256 bytes of synchronisation words, then the
+// adapter product x A^T as float32 partial sums (M x r each): `splits` of them
+// from the separate kernel, or up to 32 from the fused decode kernel.  The
+// count depends only on M and K (the bf16 count bounds the others).
+size_t linear_ws_bytes(int64_t M, int64_t K, int32_t r) {
   if (M <= 0 || r <= 0) return 0;
-  return (((size_t)M * (size_t)r * sizeof(float)) + 255) & ~(size_t)255;
+  size_t parts = (size_t)qlr::lora_t_splits(M, K, qlr::DT_BF16, qlr::DT_BF16);
+  if (M * r <= 256) parts = std::max(parts, (size_t)qlr::kMaxAdapterParts);
+  return qlr::kSyncBytes + (((parts * (size_t)M * (size_t)r * sizeof(float)) + 255) & ~(size_t)255);
 }
 
 // choose the kernel family for a linear call
@@ -166,7 +172,7 @@ qlr_status check_linear(const LinearCheck& c) {
   return QLR_OK;
 }
 
-qlr::LinearArgs make_args(const LinearCheck& c, float scale, const float* t) {
+qlr::LinearArgs make_args(const LinearCheck& c, float scale, char* ws, int splits) {
   qlr::LinearArgs a;
   a.x = c.x;
   a.xdt = (int)c.xdt;
@@ -177,8 +183,11 @@ qlr::LinearArgs make_args(const LinearCheck& c, float scale, const float* t) {
   a.codes = reinterpret_cast<const uint8_t*>(c.w->codes);
   a.q8 = c.w->absmax_q8;
   a.cst = c.w->absmax_c;
-  a.t = t;
+  a.t = ws ? reinterpret_cast<const float*>(ws + qlr::kSyncBytes) : nullptr;
+  a.t_splits = splits;
+  a.A = c.A;
   a.B = c.B;
+  a.sync = reinterpret_cast<qlr::SyncWords*>(ws);
   a.abdt = (int)c.abdt;
   a.r = c.r;
   a.scale = scale;
@@ -187,14 +196,18 @@ qlr::LinearArgs make_args(const LinearCheck& c, float scale, const float* t) {
   return a;
 }
 
-qlr_status run_linear(const LinearCheck& c, float scale, float* t, qlr_path path, hipStream_t s) {
+qlr_status run_linear(const LinearCheck& c, float scale, char* ws, qlr_path path, hipStream_t s) {
   if (c.M == 0) return QLR_OK;
   hipError_t e = hipSuccess;
-  if (c.r > 0) {
-    e = qlr::launch_lora_t(c.x, (int)c.xdt, c.M, c.w->cols, c.A, (int)c.abdt, c.r, t, s);
+  const int splits = qlr::lora_t_splits(c.M, c.w->cols, (int)c.xdt, (int)c.abdt);
+  const bool fused = path == QLR_PATH_GEMV &&
+                     qlr::gemv_fuses_adapter(c.M, c.w->rows, c.w->cols, c.r, (int)c.xdt, (int)c.abdt);
+  if (c.r > 0 && !fused) {
+    e = qlr::launch_lora_t(c.x, (int)c.xdt, c.M, c.w->cols, c.A, (int)c.abdt, c.r,
+                           reinterpret_cast<float*>(ws + qlr::kSyncBytes), splits, s);
     if (e != hipSuccess) return hip_fail(e, "adapter product launch");
   }
-  const qlr::LinearArgs a = make_args(c, scale, t);
+  const qlr::LinearArgs a = make_args(c, scale, ws, splits);
   const qlr::Levels lv = levels_arg(c.w->bits);
   switch (path) {
     case QLR_PATH_F32: e = qlr::launch_linear_f32(a, lv, s); break;
@@ -285,7 +298,7 @@ qlr_status qlr_workspace_bytes(qlr_op op, int64_t M, int64_t N, int64_t K, int32
   }
   if (op != QLR_OP_LINEAR) return fail(QLR_ERR_SHAPE, "unknown op %d", (int)op);
   if (M < 0 || r < 0) return fail(QLR_ERR_SHAPE, "negative M or r");
-  *bytes = linear_ws_bytes(M, r);
+  *bytes = linear_ws_bytes(M, K, r);
   return QLR_OK;
 }
 
@@ -331,14 +344,14 @@ qlr_status qlr_linear_fwd(const void* x, qlr_dtype xdt, int64_t M, const qlr_qwe
   const LinearCheck c{x, xdt, M, w, A, B, abdt, r, y, ydt};
   qlr_status st = check_linear(c);
   if (st != QLR_OK) return st;
-  const size_t need = linear_ws_bytes(M, r);
+  const size_t need = linear_ws_bytes(M, w->cols, r);
   if (need > 0 && (!ws || ws_bytes < need))
     return fail(QLR_ERR_WORKSPACE, "workspace of %zu bytes required, got %zu", need, ws ? ws_bytes : (size_t)0);
   if (need > 0 && !aligned16(ws)) return fail(QLR_ERR_ALIGN, "workspace must be 16-byte aligned");
   qlr_path path;
   st = pick_path(M, xdt, abdt, r, &path);
   if (st != QLR_OK) return st;
-  return run_linear(c, scale, reinterpret_cast<float*>(ws), path, reinterpret_cast<hipStream_t>(stream));
+  return run_linear(c, scale, reinterpret_cast<char*>(ws), path, reinterpret_cast<hipStream_t>(stream));
 }
 
 qlr_status qlr_linear_fwd_mixed(const qlr_layer* layers, int32_t n, int64_t M, qlr_dtype xdt, qlr_dtype abdt,
@@ -355,7 +368,7 @@ qlr_status qlr_linear_fwd_mixed(const qlr_layer* layers, int32_t n, int64_t M, q
     qlr_path path;
     st = pick_path(M, xdt, abdt, L.r, &path);
     if (st != QLR_OK) return fail(st, "layer %d: %s", i, t_error.c_str());
-    need += linear_ws_bytes(M, L.r);
+    need += linear_ws_bytes(M, L.w->cols, L.r);
     if (M > 0) {
       const uintptr_t y0 = reinterpret_cast<uintptr_t>(L.y);
       outs.push_back({y0, y0 + (uintptr_t)(M * L.w->rows) * dtype_size(ydt)});
@@ -387,9 +400,10 @@ qlr_status qlr_linear_fwd_mixed(const qlr_layer* layers, int32_t n, int64_t M, q
     const LinearCheck c{L.x, xdt, M, L.w, L.A, L.B, abdt, L.r, L.y, ydt};
     qlr_path path;
     pick_path(M, xdt, abdt, L.r, &path);
-    qlr_status st = run_linear(c, L.scale, reinterpret_cast<float*>(wsp), path, s);
+    const size_t need_l = linear_ws_bytes(M, L.w->cols, L.r);
+    qlr_status st = run_linear(c, L.scale, need_l > 0 ? wsp : nullptr, path, s);
     if (st != QLR_OK) return st;
-    wsp += linear_ws_bytes(M, L.r);
+    wsp += need_l;
   }
   return QLR_OK;
 }

@@ -22,9 +22,30 @@ hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* q8, const floa
                              int64_t numel, int bits, const Levels& lv, void* out, int odt,
                              hipStream_t s);
 
-// t[M x r] (float32) = x[M x K] A[r x K]^T.
+// Number of K-splits of the adapter product t = x A^T for M rows and K columns:
+// the product is written as `splits` partial sums p[s][M][r] (float32) that the
+// consumers add in split order.
+int lora_t_splits(int64_t M, int64_t K, int xdt, int abdt);
+
+// p[s][m][j] = sum over split s's K range of x[m,k] A[j,k]  (float32 partials).
 hipError_t launch_lora_t(const void* x, int xdt, int64_t M, int64_t K, const void* A, int abdt,
-                         int r, float* t, hipStream_t s);
+                         int r, float* t, int splits, hipStream_t s);
+
+// Device-side synchronisation words at the start of a linear workspace.  They
+// must be zero before the first call; every call leaves them zero again.
+struct SyncWords {
+  uint32_t arrive;  // adapter-partial producers that have published
+  uint32_t done;    // workgroups past their last wait (the last one resets both)
+  uint32_t error;   // nonzero if a bounded wait timed out
+  uint32_t pad[61];
+};
+constexpr size_t kSyncBytes = sizeof(SyncWords);  // 256
+
+// Decode path: does this call compute x A^T inside the GEMV kernel (one launch)?
+bool gemv_fuses_adapter(int64_t M, int64_t N, int64_t K, int r, int xdt, int abdt);
+// Adapter-partial producers of the fused decode path (at most 32).
+int gemv_adapter_parts(int64_t N, int64_t K);
+constexpr int kMaxAdapterParts = 32;
 
 struct LinearArgs {
   const void* x;
@@ -34,8 +55,11 @@ struct LinearArgs {
   const uint8_t* codes;
   const uint8_t* q8;
   const float* cst;
-  const float* t;  // M x r float32 (NULL if r == 0)
+  const float* t;  // splits x M x r float32 partials of x A^T (NULL if r == 0)
+  int t_splits;
+  const void* A;   // r x K (used by the fused decode path)
   const void* B;   // N x r
+  SyncWords* sync; // workspace synchronisation words
   int abdt;
   int r;
   float scale;

@@ -3,6 +3,8 @@
 // The forward is y = x W'^T + scale * (x A^T) B^T with the adapter kept as a
 // separate, unmerged branch (LoRDBA page, "adapter mode"; QLoRA page,
 // memory-decomposition equation: frozen quantized base, bf16 adapters).
+#include <algorithm>
+
 #include "qlr_internal.h"
 
 namespace qlr {
@@ -28,19 +30,19 @@ __global__ __launch_bounds__(256) void k_lora_t_valu(const void* __restrict__ x,
   if (lane == 0) t[m * r + j] = acc;
 }
 
-// bf16 x and A through 16x16x32 bf16 MFMA with float32 accumulation.  A
-// workgroup owns a 16-row tile of x and up to 64 adapter rows; its WAVES waves
-// split K and are reduced through LDS.
-template <int WAVES>
-__global__ __launch_bounds__(WAVES * 64) void k_lora_t_mfma(const uint16_t* __restrict__ x,
-                                                            int64_t M, int64_t K,
-                                                            const uint16_t* __restrict__ A, int r,
-                                                            float* __restrict__ t) {
-  __shared__ float sRed[WAVES][4][256];
+// bf16 x and A through 16x16x32 bf16 MFMA with float32 accumulation.
+// blockIdx.x: 16-row tile of x; blockIdx.y: group of 64 adapter rows;
+// blockIdx.z: K split.  The 4 waves share the split's 32-wide K steps and are
+// reduced through LDS; the split's partial sum goes to p[z][m][j].
+__global__ __launch_bounds__(256) void k_lora_t_mfma(const uint16_t* __restrict__ x, int64_t M,
+                                                     int64_t K, const uint16_t* __restrict__ A,
+                                                     int r, float* __restrict__ p) {
+  __shared__ float sRed[4][4][256];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = lane & 15, g = lane >> 4;
   const int64_t m0 = (int64_t)blockIdx.x * 16;
   const int j0 = blockIdx.y * 64;
+  const int S = gridDim.z, sidx = blockIdx.z;
   const bool xv = m0 + row < M;
   const uint16_t* xp = x + (xv ? (m0 + row) : 0) * K + g * 8;
   const uint16_t* ap[4];
@@ -52,11 +54,11 @@ __global__ __launch_bounds__(WAVES * 64) void k_lora_t_mfma(const uint16_t* __re
     ap[jt] = A + (int64_t)(av[jt] ? j : 0) * K + g * 8;
   }
   const int64_t nsteps = K / 32;
-  const int64_t s0 = nsteps * wave / WAVES, s1 = nsteps * (wave + 1) / WAVES;
+  const int64_t c0 = nsteps * sidx / S, c1 = nsteps * (sidx + 1) / S;
   f32x4_t acc[4] = {};
   const u32x4_t zero = {0u, 0u, 0u, 0u};
-#pragma unroll 2
-  for (int64_t st = s0; st < s1; ++st) {
+#pragma unroll 4
+  for (int64_t st = c0 + wave; st < c1; st += 4) {
     const int64_t k = st * 32;
     const u32x4_t xa = xv ? *reinterpret_cast<const u32x4_t*>(xp + k) : zero;
 #pragma unroll
@@ -70,15 +72,13 @@ __global__ __launch_bounds__(WAVES * 64) void k_lora_t_mfma(const uint16_t* __re
 #pragma unroll
     for (int v = 0; v < 4; ++v) sRed[wave][jt][lane * 4 + v] = acc[jt][v];
   __syncthreads();
-  for (int idx = threadIdx.x; idx < 4 * 256; idx += WAVES * 64) {
+  for (int idx = threadIdx.x; idx < 4 * 256; idx += 256) {
     const int jt = idx >> 8, e = idx & 255;
-    float s = 0.0f;
-#pragma unroll
-    for (int w = 0; w < WAVES; ++w) s += sRed[w][jt][e];
+    const float s = (sRed[0][jt][e] + sRed[1][jt][e]) + (sRed[2][jt][e] + sRed[3][jt][e]);
     const int l = e >> 2, v = e & 3;
     const int64_t m = m0 + 4 * (l >> 4) + v;  // MFMA output row
     const int j = j0 + jt * 16 + (l & 15);     // MFMA output column
-    if (m < M && j < r) t[m * r + j] = s;
+    if (m < M && j < r) p[((int64_t)sidx * M + m) * r + j] = s;
   }
 }
 
@@ -90,7 +90,7 @@ template <int BITS, int XDT, int BDT, int YDT>
 __global__ __launch_bounds__(256) void k_linear_f32(LinearArgs a, Levels lv) {
   constexpr int NL = 1 << BITS;
   __shared__ float sL[NL];
-  for (int i = threadIdx.x; i < NL; i += blockDim.x) sL[i] = lv.v[i];
+  stage_levels<NL>(lv, sL);
   __syncthreads();
   const int lane = threadIdx.x & 63;
   const int64_t n = (int64_t)blockIdx.x * 4 + (threadIdx.x >> 6);
@@ -118,7 +118,11 @@ __global__ __launch_bounds__(256) void k_linear_f32(LinearArgs a, Levels lv) {
       if (m >= a.M) break;
       float base = wave_sum(acc[mm]);
       float lo = 0.0f;
-      for (int j = lane; j < a.r; j += 64) lo = fmaf(a.t[m * a.r + j], load_elem<BDT>(a.B, n * a.r + j), lo);
+      for (int j = lane; j < a.r; j += 64) {
+        float tj = 0.0f;
+        for (int sp = 0; sp < a.t_splits; ++sp) tj += a.t[((int64_t)sp * a.M + m) * a.r + j];
+        lo = fmaf(tj, load_elem<BDT>(a.B, n * a.r + j), lo);
+      }
       lo = wave_sum(lo);
       const float out = fmaf(a.scale, lo, base);
       if (lane == 0) {
@@ -151,20 +155,21 @@ hipError_t launch_f32_b1(const LinearArgs& a, const Levels& lv, hipStream_t s) {
 
 }  // namespace
 
+int lora_t_splits(int64_t M, int64_t K, int xdt, int abdt) {
+  if (!(xdt == DT_BF16 && abdt == DT_BF16)) return 1;
+  const int64_t steps = K / 32, mtiles = (M + 15) / 16;
+  int64_t s = std::min<int64_t>(steps / 4, (256 + mtiles - 1) / mtiles);
+  s = std::min<int64_t>(s, 64);
+  return (int)std::max<int64_t>(s, 1);
+}
+
 hipError_t launch_lora_t(const void* x, int xdt, int64_t M, int64_t K, const void* A, int abdt,
-                         int r, float* t, hipStream_t s) {
+                         int r, float* t, int splits, hipStream_t s) {
   if (M == 0 || r == 0) return hipSuccess;
   if (xdt == DT_BF16 && abdt == DT_BF16) {
-    dim3 grid((unsigned)((M + 15) / 16), (unsigned)((r + 63) / 64));
-    if (M <= 16) {
-      hipLaunchKernelGGL((k_lora_t_mfma<16>), grid, dim3(1024), 0, s,
-                         reinterpret_cast<const uint16_t*>(x), M, K,
-                         reinterpret_cast<const uint16_t*>(A), r, t);
-    } else {
-      hipLaunchKernelGGL((k_lora_t_mfma<4>), grid, dim3(256), 0, s,
-                         reinterpret_cast<const uint16_t*>(x), M, K,
-                         reinterpret_cast<const uint16_t*>(A), r, t);
-    }
+    dim3 grid((unsigned)((M + 15) / 16), (unsigned)((r + 63) / 64), (unsigned)splits);
+    hipLaunchKernelGGL(k_lora_t_mfma, grid, dim3(256), 0, s, reinterpret_cast<const uint16_t*>(x), M,
+                       K, reinterpret_cast<const uint16_t*>(A), r, t);
     return hipGetLastError();
   }
   const int64_t items = M * r;

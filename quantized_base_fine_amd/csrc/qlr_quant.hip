@@ -81,8 +81,11 @@ __global__ __launch_bounds__(kThreads) void k_quantize(const void* __restrict__ 
   __shared__ float sA[256];  // first-level absmax of the group's blocks
   __shared__ float sMax[kThreads / 64];
 
+  __shared__ float sL[NL];
   const int tid = threadIdx.x;
-  for (int i = tid; i < NL - 1; i += kThreads) sT[i] = (double)lv.v[i] + (double)lv.v[i + 1];
+  stage_levels<NL>(lv, sL);
+  __syncthreads();
+  for (int i = tid; i < NL - 1; i += kThreads) sT[i] = (double)sL[i] + (double)sL[i + 1];
   const int64_t nblk_total = (numel + 63) / 64;
   const int64_t blk0 = (int64_t)blockIdx.x * 256;
   const int nblk_here = (int)min<int64_t>(256, nblk_total - blk0);
@@ -167,7 +170,7 @@ __global__ __launch_bounds__(256) void k_dequantize(const uint8_t* __restrict__ 
                                                     Levels lv, void* __restrict__ out) {
   constexpr int NL = 1 << BITS;
   __shared__ float sL[NL];
-  for (int i = threadIdx.x; i < NL; i += blockDim.x) sL[i] = lv.v[i];
+  stage_levels<NL>(lv, sL);
   __syncthreads();
   const int64_t nchunk = (numel + 7) / 8;
   for (int64_t ch = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; ch < nchunk;

@@ -264,3 +264,46 @@ def test_mixed_small():
         for lin, y in zip(lins, ys):
             rows = list(range(lin.N))
             check_linear(f32_of(y), lin, oracle_rows_dequant(lin.W, "f16", lin.bits, rows), rows)
+
+
+# ---------------------------------------------------------------- decode synchronisation words
+
+def test_decode_fused_adapter_repeats_and_resets_sync_words():
+    """The fused decode kernel publishes adapter partials through counters in the
+    workspace; back-to-back calls on one workspace agree bit for bit and leave
+    the counters zero."""
+    lin = workloads.mlp("down", 1)
+    qw = _gpu_quant(lin.W, "f16", 4)
+    x, A, B = dev(lin.x, "bf16"), dev(lin.A, "bf16"), dev(lin.B, "bf16")
+    ws = torch.zeros(qlr.workspace_bytes(qlr.OP_LINEAR, 1, lin.N, lin.K, lin.r), dtype=torch.uint8, device="cuda")
+    ys = [qlr.linear(x, qw, A, B, lin.scale, out_dtype=torch.float32, ws=ws) for _ in range(4)]
+    torch.cuda.synchronize()
+    for y in ys[1:]:
+        assert torch.equal(y, ys[0])
+    words = host(ws)[:12].view(np.uint32)
+    assert words.tolist() == [0, 0, 0], words  # arrive, done, error
+    rows = list(range(0, lin.N, 97))
+    check_linear(f32_of(ys[0]), lin, oracle_rows_dequant(lin.W, "f16", 4, rows), rows)
+
+
+def test_decode_graph_replays_match_eager():
+    """Decode calls captured in a HIP graph: every replay equals the eager result."""
+    lin = workloads.attn(1)
+    qw = _gpu_quant(lin.W, "f16", 4)
+    x, A, B = dev(lin.x, "bf16"), dev(lin.A, "bf16"), dev(lin.B, "bf16")
+    ws = torch.zeros(qlr.workspace_bytes(qlr.OP_LINEAR, 1, lin.N, lin.K, lin.r), dtype=torch.uint8, device="cuda")
+    y = torch.empty((1, lin.N), dtype=torch.bfloat16, device="cuda")
+    qlr.linear(x, qw, A, B, lin.scale, out=y, ws=ws)
+    torch.cuda.synchronize()
+    eager = y.clone()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        qlr.linear(x, qw, A, B, lin.scale, out=y, ws=ws)
+        qlr.linear(x, qw, A, B, lin.scale, out=y, ws=ws)
+    for i in range(3):
+        y.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert torch.equal(y, eager), i
+        _ = (x.float() * 2).sum().item()  # unrelated eager work between replays
+    assert host(ws)[:12].view(np.uint32).tolist() == [0, 0, 0]
