@@ -1,186 +1,632 @@
-// Prefill path (bf16 x, any M): the frozen base dequantized into LDS-staged
-// bf16 tiles feeding 32x32x16 bf16 MFMA with float32 accumulation, and the
-// unmerged adapter branch added as extra K steps.
+// Prefill path (bf16 x, any M): dequantizing GEMM on 32x32x16 bf16 MFMA with
+// float32 accumulation, plus the unmerged adapter branch.
 //
 // QLoRA page, section "Limitations": the quantized base is dequantized every
-// time it is used; here that happens once per 128x64 weight tile and
-// workgroup, straight into LDS.  LoRDBA page, "adapter mode": the adapter is a
-// separate branch, y = x W'^T + scale (x A^T) B^T; with t = x A^T precomputed,
-// the branch is the product [hi(s t) | lo(s t)] [B | B]^T, where hi/lo split
-// s*t into two bf16 terms so the adapter product keeps about 16 bits.
+// time it is used.  LoRDBA page, "adapter mode": the adapter stays a separate
+// branch, y = x W'^T + scale (x A^T) B^T.
+//
+// Tiling.  A workgroup of 4 waves owns a 256 (M) x 128 (N) output tile.  Wave
+// w = 2 kh + mh computes rows [128 mh, 128 mh + 128) x all 128 columns (4 x 4
+// MFMA tiles of 32x32, 256 accumulator registers) over the K half kh of every
+// 64-element block; the two K halves are added through LDS at the end.
+// Splitting K rather than N halves the fragment bytes read from LDS per MFMA.
+//
+// Operand staging.  Per 64-element K block the workgroup writes two LDS tiles,
+// both stored as 128-byte rows whose 16-byte chunks are XOR-swizzled by the row
+// index: chunk c of row q sits at q*128 + ((c ^ g(q mod 16)) * 16) with
+// g(r) = (r ^ bit2(r) ^ bit3(r)) mod 8.  Fragment reads (16 rows, one chunk)
+// and both tile writes then hit distinct banks whether the LDS serves 8 lanes
+// x 16 bytes over 32 banks or 16 lanes over 64 banks per cycle; a plain
+// g(q) = q mod 8 leaves 2-way conflicts on the fragment reads in the latter:
+//  * x: 256 rows, loaded with coalesced buffer loads (8 lanes per 128-byte row;
+//    rows past M read as zero).  MFMA fragments loaded straight from global
+//    memory would touch 32 rows per instruction, which the L1 serves at about a
+//    third of the rate.
+//  * W: the tile's 128 weight rows, dequantized by all 256 threads (two per
+//    row, 32 codes each) to bf16 = round(level(code) * absmax).
+// Tiles are triple-buffered (block k in buffer k mod 3, static in the 3-way
+// unrolled loop): block k+2 is written while block k is multiplied, so the
+// first fragments of block k+1 can be read before the barrier that ends block
+// k.  One barrier per block.
+//
+// 4-bit levels are looked up in registers: the codebook is symmetric, so a
+// code c selects one of the 8 positive levels (c - 8 or 7 - c) and the sign is
+// bit 3 of c; the 8 scaled bf16 levels of a (row, block) form two 8-byte byte
+// tables that v_perm indexes four codes at a time.  Other widths look up
+// float32 levels in lane-private LDS tables.
+//
+// Tile order.  Workgroups are dealt to the 8 XCDs round robin; tile ids are
+// remapped so that each XCD walks a contiguous, row-major range of tiles, which
+// keeps one 256-row slab of x hot in that XCD's L2.
+//
+// Adapter.  t = x A^T (float32 partial sums from the adapter-product kernel) is
+// split into hi = bf16(s t) and lo = bf16(s t - hi) and multiplied with B as
+// extra K steps: [hi | lo] [B | B]^T.
+#include <algorithm>
+#include <type_traits>
+
 #include "qlr_internal.h"
+#include "qlr_lut.h"
 
 namespace qlr {
 
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 64, LDK = BK + 8;  // LDS row stride (bf16): 144 bytes
+constexpr int BM = 256, BN = 128;
+constexpr uint32_t kXTile = BM * 128;  // bytes of one x tile (256 rows x 64 bf16)
+constexpr uint32_t kWTile = BN * 128;  // bytes of one weight tile (128 rows x 64 bf16)
+constexpr uint32_t kXOff = 0, kWOff = 3 * kXTile, kTOff = kWOff + 3 * kWTile;
+
+// LDS bytes of the level table for each code width (4-bit levels live in registers).
+template <int BITS>
+struct GemmTable {
+  static constexpr uint32_t kBytes = (BITS == 4) ? 0 : (BITS == 8) ? 256 * 16 * 4 : PairTableF32<BITS>::kBytes;
+};
+template <int BITS>
+constexpr uint32_t gemm_lds_bytes() { return kTOff + GemmTable<BITS>::kBytes; }
+static_assert(gemm_lds_bytes<3>() <= 160 * 1024 && gemm_lds_bytes<8>() <= 160 * 1024, "LDS budget");
+
+// Raw codes of one thread for one block: the 32 codes [32h, 32h+32) of a weight row.
+template <int BITS>
+struct Codes32 {
+  uint32_t w[BITS];  // 32*BITS bits
+};
 
 template <int BITS>
-__device__ __forceinline__ void load_codes32(const uint8_t* p, uint32_t (&c)[BITS]) {
-  // the 32 codes of half a block: 4*BITS bytes at p (4-byte aligned for BITS != 3)
-  if constexpr (BITS == 3) {
-    const uint16_t* h = reinterpret_cast<const uint16_t*>(p);
-#pragma unroll
-    for (int i = 0; i < 3; ++i) c[i] = (uint32_t)h[2 * i] | ((uint32_t)h[2 * i + 1] << 16);
-  } else if constexpr (BITS == 2) {
+__device__ __forceinline__ Codes32<BITS> load_codes32(const uint8_t* p) {
+  Codes32<BITS> c;
+  if constexpr (BITS == 2) {
     const uint2 u = *reinterpret_cast<const uint2*>(p);
-    c[0] = u.x; c[1] = u.y;
+    c.w[0] = u.x; c.w[1] = u.y;
+  } else if constexpr (BITS == 3) {
+    const uint32_t* q = reinterpret_cast<const uint32_t*>(p);  // 12 bytes at a 4-byte boundary
+    c.w[0] = q[0]; c.w[1] = q[1]; c.w[2] = q[2];
   } else if constexpr (BITS == 4) {
     const uint4 u = *reinterpret_cast<const uint4*>(p);
-    c[0] = u.x; c[1] = u.y; c[2] = u.z; c[3] = u.w;
+    c.w[0] = u.x; c.w[1] = u.y; c.w[2] = u.z; c.w[3] = u.w;
   } else {
     const uint4 u0 = *reinterpret_cast<const uint4*>(p);
     const uint4 u1 = *reinterpret_cast<const uint4*>(p + 16);
-    c[0] = u0.x; c[1] = u0.y; c[2] = u0.z; c[3] = u0.w;
-    c[4] = u1.x; c[5] = u1.y; c[6] = u1.z; c[7] = u1.w;
+    c.w[0] = u0.x; c.w[1] = u0.y; c.w[2] = u0.z; c.w[3] = u0.w;
+    c.w[4] = u1.x; c.w[5] = u1.y; c.w[6] = u1.z; c.w[7] = u1.w;
+  }
+  return c;
+}
+
+// LDS accesses at a byte address of the dynamic LDS block, which starts at LDS
+// address 0 (the kernel has no static LDS; the launcher checks this).
+typedef float f32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float2 lds_pair(uint32_t byte_addr) {
+  const f32x2_t v = *reinterpret_cast<const __attribute__((address_space(3))) f32x2_t*>((uintptr_t)byte_addr);
+  return make_float2(v.x, v.y);
+}
+__device__ __forceinline__ float lds_f32(uint32_t byte_addr) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) float*>((uintptr_t)byte_addr);
+}
+__device__ __forceinline__ u32x4_t lds_u32x4(uint32_t byte_addr) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>((uintptr_t)byte_addr);
+}
+__device__ __forceinline__ void lds_store_u32x4(uint32_t byte_addr, u32x4_t v) {
+  *reinterpret_cast<__attribute__((address_space(3))) u32x4_t*>((uintptr_t)byte_addr) = v;
+}
+__device__ __forceinline__ void lds_store_f32x4(uint32_t byte_addr, f32x4_t v) {
+  *reinterpret_cast<__attribute__((address_space(3))) f32x4_t*>((uintptr_t)byte_addr) = v;
+}
+__device__ __forceinline__ f32x4_t lds_f32x4(uint32_t byte_addr) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) f32x4_t*>((uintptr_t)byte_addr);
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+
+// round-to-nearest-even bf16 pair of (a, b) in one packed conversion
+__device__ __forceinline__ uint32_t cvt_pk_bf16(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector(f32x2_t{a, b}, bf16x2_t));
+}
+
+__device__ __forceinline__ uint32_t perm(uint32_t hi4, uint32_t lo4, uint32_t sel) {
+  return __builtin_amdgcn_perm(hi4, lo4, sel);
+}
+
+// ---- 4-bit register lookup
+// Byte tables of the 8 positive scaled levels P[j] = bf16(L[8 + j] * ap):
+// lo = low bytes of P[0..7], hi = high bytes, 8 bytes each (two registers).
+struct Lut4 {
+  uint32_t lo_a, lo_b, hi_a, hi_b;
+};
+
+__device__ __forceinline__ Lut4 make_lut4(const Levels& lv, float ap) {
+  const uint32_t p01 = cvt_pk_bf16(lv.v[8] * ap, lv.v[9] * ap);
+  const uint32_t p23 = cvt_pk_bf16(lv.v[10] * ap, lv.v[11] * ap);
+  const uint32_t p45 = cvt_pk_bf16(lv.v[12] * ap, lv.v[13] * ap);
+  const uint32_t p67 = cvt_pk_bf16(lv.v[14] * ap, lv.v[15] * ap);
+  return {perm(p23, p01, 0x06040200u), perm(p67, p45, 0x06040200u),
+          perm(p23, p01, 0x07050301u), perm(p67, p45, 0x07050301u)};
+}
+
+// Eight 4-bit codes (LSB first) -> four bf16 pairs in code order.  Code c maps
+// to P[c - 8] for c >= 8 and to -P[7 - c] for c < 8: the index is c ^ 7 when
+// bit 3 is clear, and the sign is bit 3 clear, set into bit 15 of the bf16.
+__device__ __forceinline__ void lut4_word(uint32_t w, const Lut4& t, uint32_t* o) {
+  const uint32_t neg = ~w & 0x88888888u;  // bit 3 of every negative code
+  const uint32_t m = neg >> 3;
+  const uint32_t idx = w ^ ((m << 3) - m);  // low 3 bits of each nibble: level index
+  const uint32_t se = idx & 0x07070707u, so = (idx >> 4) & 0x07070707u;  // even / odd codes
+  const uint32_t loe = perm(t.lo_b, t.lo_a, se), loo = perm(t.lo_b, t.lo_a, so);
+  const uint32_t hie = perm(t.hi_b, t.hi_a, se) | ((neg << 4) & 0x80808080u);
+  const uint32_t hio = perm(t.hi_b, t.hi_a, so) | (neg & 0x80808080u);
+  const uint32_t l03 = perm(loo, loe, 0x05010400u), h03 = perm(hio, hie, 0x05010400u);
+  const uint32_t l47 = perm(loo, loe, 0x07030602u), h47 = perm(hio, hie, 0x07030602u);
+  o[0] = perm(h03, l03, 0x05010400u);
+  o[1] = perm(h03, l03, 0x07030602u);
+  o[2] = perm(h47, l47, 0x05010400u);
+  o[3] = perm(h47, l47, 0x07030602u);
+}
+
+// Pairs [J0, J1) of the 16 bf16 pairs of one thread's 32 codes, for widths
+// other than 4 (float32 levels from a lane-private LDS table; tp = this lane's
+// copy): o[j] = bf16 pair of codes 2j, 2j+1.
+template <int BITS, int J0, int J1>
+__device__ __forceinline__ void dequant_pairs(const Codes32<BITS>& c, float ap, uint32_t tp, uint32_t (&o)[16]) {
+#pragma unroll
+  for (int j = J0; j < J1; ++j) {
+    if constexpr (BITS == 8) {
+      // one float32 level per code; 16 lane copies, entry e of copy l at e*64 + 4l
+      const uint32_t w = c.w[j >> 1] >> (16 * (j & 1));
+      o[j] = cvt_pk_bf16(lds_f32(tp + ((w & 255u) << 6)) * ap, lds_f32(tp + (((w >> 8) & 255u) << 6)) * ap);
+    } else {
+      // float32 level pairs of two neighbouring codes; 32 lane copies, entry e at e*256 + 8l
+      uint32_t e;
+      if constexpr (BITS == 2) {
+        e = (c.w[j >> 3] >> (4 * (j & 7))) & 15u;
+      } else {
+        const int bit = 6 * j, wd = bit >> 5, sh = bit & 31;
+        uint32_t v = c.w[wd] >> sh;
+        if (sh + 6 > 32) v |= c.w[wd + 1] << (32 - sh);
+        e = v & 63u;
+      }
+      const float2 p = lds_pair(tp + (e << 8));
+      o[j] = cvt_pk_bf16(p.x * ap, p.y * ap);
+    }
   }
 }
 
+// XOR swizzle of the 16-byte chunks of LDS tile row r (see the header).
+__device__ __forceinline__ uint32_t swz(uint32_t r) {
+  return (r ^ ((r >> 2) & 1u) ^ ((r >> 3) & 1u)) & 7u;
+}
+
+// Level table in LDS for widths other than 4 (built once per workgroup).
 template <int BITS>
-__device__ __forceinline__ int code_at(const uint32_t (&c)[BITS], int e) {
-  const int bit = BITS * e, w = bit >> 5, sh = bit & 31;
-  uint32_t v = c[w] >> sh;
-  if (sh + BITS > 32) v |= c[w + 1] << (32 - sh);
-  return (int)(v & ((1u << BITS) - 1));
+__device__ __forceinline__ void build_gemm_table(const float* sL, int tid) {
+  if constexpr (BITS == 8) {
+    for (int idx = tid; idx < 256 * 16; idx += 256) {
+      *reinterpret_cast<__attribute__((address_space(3))) float*>((uintptr_t)(kTOff + 4 * idx)) = sL[idx >> 4];
+    }
+  } else if constexpr (BITS != 4) {
+    constexpr int NL = 1 << BITS;
+    constexpr int E = PairTableF32<BITS>::kEntries;
+    for (int idx = tid; idx < E * 32; idx += 256) {
+      const int e = idx >> 5;
+      *reinterpret_cast<__attribute__((address_space(3))) f32x2_t*>((uintptr_t)(kTOff + 8 * idx)) =
+          f32x2_t{sL[e & (NL - 1)], sL[e >> BITS]};
+    }
+  }
+}
+
+struct GemmParams {
+  LinearArgs a;
+  int64_t m_begin, m_end;  // rows [m_begin, m_end) of x and y in this launch
+  int64_t mtiles, ntiles, per_xcd;
+};
+
+template <int BITS, int YDT>
+__global__ __launch_bounds__(256, 1) void k_gemm(GemmParams P, Levels lv) {
+  extern __shared__ uint32_t smem[];
+  const LinearArgs& a = P.a;
+  const int64_t N = a.N, K = a.K, nb = K >> 6;
+  const int64_t M = P.m_end;
+  // XCD-aware tile order: workgroup b runs on XCD b % 8
+  const int64_t xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
+  const int64_t tile = xcd * P.per_xcd + local;
+  if (local >= P.per_xcd || tile >= P.mtiles * P.ntiles) return;  // whole workgroup exits
+  const int64_t mt = tile / P.ntiles, nt = tile % P.ntiles;
+  const int64_t m0 = P.m_begin + mt * BM, n0 = nt * BN;
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63, wave = tid >> 6;
+  const int mh = wave & 1, kh = wave >> 1;  // row half and K half of this wave
+  const int fr = lane & 31, h = lane >> 5;
+
+  // x of this launch as a buffer resource: reads past its last row return zero
+  const uint16_t* xs_base = reinterpret_cast<const uint16_t*>(a.x) + P.m_begin * K;
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(xs_base), (short)0, (int)((P.m_end - P.m_begin) * K * 2), 0x00020000);
+  // staging load j (0..7): tile row 64 wave + 8 j + lane / 8, 16-byte chunk lane % 8
+  const uint32_t xg0 = (uint32_t)(((m0 - P.m_begin) + 64 * wave + (lane >> 3)) * K + 8 * (lane & 7)) * 2u;
+  const uint32_t xg_row8 = (uint32_t)(8 * K * 2);
+  // its LDS slot: row 64 wave + 8 j + t (t = lane / 8), swizzle g = t ^ bit2(t) ^ (j & 1)
+  uint32_t xst[2];
+#pragma unroll
+  for (int p = 0; p < 2; ++p) {
+    const uint32_t t = (uint32_t)(lane >> 3);
+    xst[p] = kXOff + (uint32_t)((64 * wave + t) * 128) + ((((uint32_t)lane & 7u) ^ swz(t + 8u * p)) << 4);
+  }
+
+  // fragment of step s (0, 1) of this wave: row fr (+32 i or +32 c), chunk 4 kh + 2 s + h
+  uint32_t fo[2];
+#pragma unroll
+  for (int s = 0; s < 2; ++s) fo[s] = (uint32_t)(fr * 128) + ((((uint32_t)(4 * kh + 2 * s + h)) ^ swz((uint32_t)fr & 15u)) << 4);
+  const uint32_t xrow0 = (uint32_t)(128 * mh * 128);  // first tile row of this wave's A fragments
+
+  // weight row this thread dequantizes: rr = tid / 2, codes [32 dh, 32 dh + 32) of each block
+  const int rr = tid >> 1, dh = tid & 1;
+  const int64_t wn = n0 + rr;
+  const bool wv = wn < N;
+  const int64_t wblk = (wv ? wn : N - 1) * nb;
+  uint32_t wst[4];  // LDS slot of chunk 4 dh + q of row rr
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+    wst[q] = kWOff + (uint32_t)(rr * 128) + ((((uint32_t)(4 * dh + q)) ^ swz((uint32_t)rr & 15u)) << 4);
+  const uint32_t tp = kTOff + (BITS == 8 ? 4u * (lane & 15) : 8u * fr);
+
+  struct XS { u32x4_t v[8]; };
+  struct CS { Codes32<BITS> c; uint32_t q8; float sc; };
+  auto load_x = [&](XS& st, int64_t kb) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      st.v[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(xr, xg0 + j * xg_row8, (int)(kb * 128), 0));
+  };
+  auto store_x = [&](const XS& st, int buf) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) lds_store_u32x4(xst[j & 1] + buf * kXTile + 1024u * j, st.v[j]);
+  };
+  auto load_c = [&](CS& st, int64_t kb) {
+    const int64_t blk = wblk + kb;
+    st.c = load_codes32<BITS>(a.codes + blk * (8 * BITS) + dh * (4 * BITS));
+    st.q8 = a.q8[blk];
+    st.sc = a.cst[blk >> 8];
+  };
+  auto store_w = [&](const uint32_t (&o)[16], int buf) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q)
+      lds_store_u32x4(wst[q] + buf * kWTile, u32x4_t{o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]});
+  };
+  // Dequantization of one thread's 32 codes in two halves (o[0..7], o[8..15]).
+  struct DQ { Codes32<BITS> c; float ap; Lut4 t; };
+  auto dq_begin = [&](const CS& cs) {
+    // Pin the codes here: an empty register-only asm makes them opaque, so
+    // instruction selection cannot start their arithmetic right after the load
+    // (which would wait for codes still in flight).
+    DQ d;
+    d.c = cs.c;
+    uint32_t q8 = cs.q8;
+    float sc = cs.sc;
+#pragma unroll
+    for (int i = 0; i < BITS; ++i) asm volatile("" : "+v"(d.c.w[i]));
+    asm volatile("" : "+v"(q8), "+v"(sc));
+    d.ap = wv ? (float)q8 * sc : 0.0f;
+    if constexpr (BITS == 4) d.t = make_lut4(lv, d.ap);
+    return d;
+  };
+  auto dq_half = [&](const DQ& d, auto half, uint32_t (&o)[16]) {
+    constexpr int H = decltype(half)::value;
+    if constexpr (BITS == 4) {
+      lut4_word(d.c.w[2 * H], d.t, o + 8 * H);
+      lut4_word(d.c.w[2 * H + 1], d.t, o + 8 * H + 4);
+    } else {
+      dequant_pairs<BITS, 8 * H, 8 * H + 8>(d.c, d.ap, tp, o);
+    }
+  };
+  // Values computed before this point stay before it: instruction selection
+  // otherwise places pure arithmetic next to its uses (here: the tile stores at
+  // the end of the block), out of the phase it is meant to overlap.
+  auto pin8 = [](uint32_t (&o)[16], int j0) {
+#pragma unroll
+    for (int j = 0; j < 8; ++j) asm volatile("" : "+v"(o[j0 + j]));
+  };
+  auto dequant = [&](const CS& cs, uint32_t (&o)[16]) {
+    const DQ d = dq_begin(cs);
+    dq_half(d, std::integral_constant<int, 0>{}, o);
+    dq_half(d, std::integral_constant<int, 1>{}, o);
+  };
+
+  f32x16_t acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) acc[i][c][v] = 0.0f;
+
+  // Loads past the last block reload the last block (harmless: they fill spare
+  // buffers nobody reads), so no load sits behind a branch.
+  const int64_t kbl = nb - 1;
+  XS xs;
+  CS c0, c1, c2;
+  load_x(xs, 0);
+  load_c(c0, 0);
+  load_c(c1, min<int64_t>(1, kbl));
+  load_c(c2, min<int64_t>(2, kbl));
+  if constexpr (BITS != 4) {
+    float* sL = reinterpret_cast<float*>(smem) + kXOff / 4;
+    stage_levels<1 << BITS>(lv, sL);
+    __syncthreads();
+    build_gemm_table<BITS>(sL, tid);
+    __syncthreads();
+  }
+  {
+    uint32_t o[16];
+    store_x(xs, 0);
+    dequant(c0, o);
+    store_w(o, 0);
+    load_x(xs, min<int64_t>(1, kbl));
+    load_c(c0, min<int64_t>(3, kbl));
+    dequant(c1, o);
+    store_w(o, 1);
+    store_x(xs, 1);
+  }
+  __syncthreads();
+
+  // fragments of step 0 of block 0
+  u32x4_t fa[2][4], fb[2][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) fa[0][i] = lds_u32x4(kXOff + xrow0 + fo[0] + 4096u * i);
+#pragma unroll
+  for (int c = 0; c < 4; ++c) fb[0][c] = lds_u32x4(kWOff + fo[0] + 4096u * c);
+
+  // One block k (buffer bc = k % 3), in pinned phases (sched_barrier keeps the
+  // scheduler from sinking fragment reads next to their MFMAs or hoisting later
+  // blocks' work):
+  //  1. loads of x(k+2) and codes(k+4); LDS reads of step 1's fragments;
+  //  2. 16 MFMAs of step 0 interleaved with the first half of the dequantization
+  //     of block k+2;
+  //  3. LDS reads of step 0's fragments of block k+1 (buffer bn, written one
+  //     block earlier);
+  //  4. 16 MFMAs of step 1 with the second half of the dequantization;
+  //  5. block k+2's weight and x tiles into buffer bw; one barrier.
+  auto step = [&](const CS& cd, CS& cl, int64_t k, int bc, int bn, int bw) {
+    __builtin_amdgcn_sched_barrier(0);
+    load_x(xs, min(k + 2, kbl));
+    load_c(cl, min(k + 4, kbl));
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[1][i] = lds_u32x4(kXOff + bc * kXTile + xrow0 + fo[1] + 4096u * i);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) fb[1][c] = lds_u32x4(kWOff + bc * kWTile + fo[1] + 4096u * c);
+    __builtin_amdgcn_sched_barrier(0);
+    uint32_t o[16];
+    const DQ d = dq_begin(cd);
+    dq_half(d, std::integral_constant<int, 0>{}, o);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[i][c] = mfma32x32x16(as_bf16x8(fa[0][i]), as_bf16x8(fb[0][c]), acc[i][c]);
+#pragma unroll
+    for (int g = 0; g < 16; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // up to 4 VALU
+    }
+    pin8(o, 0);  // the first half is computed in this phase
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) fa[0][i] = lds_u32x4(kXOff + bn * kXTile + xrow0 + fo[0] + 4096u * i);
+#pragma unroll
+    for (int c = 0; c < 4; ++c) fb[0][c] = lds_u32x4(kWOff + bn * kWTile + fo[0] + 4096u * c);
+    dq_half(d, std::integral_constant<int, 1>{}, o);
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int c = 0; c < 4; ++c) acc[i][c] = mfma32x32x16(as_bf16x8(fa[1][i]), as_bf16x8(fb[1][c]), acc[i][c]);
+    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // the 8 fragment reads first
+#pragma unroll
+    for (int g = 0; g < 16; ++g) {
+      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
+    }
+    pin8(o, 8);
+    __builtin_amdgcn_sched_barrier(0);
+    store_w(o, bw);
+    store_x(xs, bw);
+    __syncthreads();
+    __builtin_amdgcn_sched_barrier(0);
+  };
+
+  // codes: block k+2 is in set (k+2) % 3; block k+4 is loaded into set (k+1) % 3
+  const int64_t nb3 = nb - nb % 3;
+  int64_t kb = 0;
+  for (; kb < nb3; kb += 3) {
+    step(c2, c1, kb, 0, 1, 2);
+    step(c0, c2, kb + 1, 1, 2, 0);
+    step(c1, c0, kb + 2, 2, 0, 1);
+  }
+  if (kb < nb) step(c2, c1, kb, 0, 1, 2);
+  if (kb + 1 < nb) step(c0, c2, kb + 1, 1, 2, 0);
+
+  // ---- adapter branch: extra K steps [hi(s t) | lo(s t)] x [B | B], step q on K half q % 2
+  if (a.r > 0) {
+    const int r = a.r;
+    const uint16_t* Bl = reinterpret_cast<const uint16_t*>(a.B);
+    const int nsteps = (r + 15) / 16;
+    const bool vec = (r % 8) == 0;  // B rows hold whole 16-byte groups
+    for (int q = kh; q < nsteps; q += 2) {
+      const int j0 = 16 * q + 8 * h;  // this lane's 8 adapter columns
+      u32x4_t bf[4];
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const int64_t n = n0 + 32 * c + fr;
+        bf[c] = u32x4_t{0u, 0u, 0u, 0u};
+        if (n < N) {
+          const uint16_t* bp = Bl + n * (int64_t)r;
+          if (vec && j0 + 8 <= r) {
+            bf[c] = *reinterpret_cast<const u32x4_t*>(bp + j0);
+          } else {
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+              const uint32_t lo = (j0 + 2 * e2 < r) ? bp[j0 + 2 * e2] : 0u;
+              const uint32_t hi = (j0 + 2 * e2 + 1 < r) ? bp[j0 + 2 * e2 + 1] : 0u;
+              bf[c][e2] = lo | (hi << 16);
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t m = m0 + 128 * mh + 32 * i + fr;
+        const bool mv = m < M;
+        float v8[8];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) v8[e] = 0.0f;
+        for (int sp = 0; sp < a.t_splits; ++sp) {
+          const float* tq = a.t + ((int64_t)sp * a.M + (mv ? m : 0)) * r;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) v8[e] += (mv && j0 + e < r) ? tq[j0 + e] : 0.0f;
+        }
+        u32x4_t thi, tlo;
+#pragma unroll
+        for (int e2 = 0; e2 < 4; ++e2) {
+          const float u0 = a.scale * v8[2 * e2], u1 = a.scale * v8[2 * e2 + 1];
+          const uint32_t hb0 = f32_to_bf16_bits(u0), hb1 = f32_to_bf16_bits(u1);
+          thi[e2] = hb0 | (hb1 << 16);
+          tlo[e2] = pack_bf16x2(u0 - bf16_bits_to_f32(hb0), u1 - bf16_bits_to_f32(hb1));
+        }
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          acc[i][c] = mfma32x32x16(as_bf16x8(thi), as_bf16x8(bf[c]), acc[i][c]);
+          acc[i][c] = mfma32x32x16(as_bf16x8(tlo), as_bf16x8(bf[c]), acc[i][c]);
+        }
+      }
+    }
+  }
+
+  // ---- K-half reduction.  Wave (mh, kh) keeps row tiles 2 kh, 2 kh + 1 and
+  // hands the other two to its partner (mh, 1 - kh) through LDS (lane-major, 16
+  // bytes per lane per register group: conflict-free).  kh is uniform per wave,
+  // so each branch indexes the accumulators statically.
+  const uint32_t xch = (uint32_t)wave * 32768u;       // this wave's outgoing half
+  const uint32_t xin = (uint32_t)(wave ^ 2) * 32768u;  // the partner's
+  auto send_tiles = [&](const f32x16_t (&t0)[4], const f32x16_t (&t1)[4]) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        lds_store_f32x4(xch + (uint32_t)(((c * 4 + g) * 64 + lane) * 16),
+                        f32x4_t{t0[c][4 * g], t0[c][4 * g + 1], t0[c][4 * g + 2], t0[c][4 * g + 3]});
+        lds_store_f32x4(xch + (uint32_t)((((4 + c) * 4 + g) * 64 + lane) * 16),
+                        f32x4_t{t1[c][4 * g], t1[c][4 * g + 1], t1[c][4 * g + 2], t1[c][4 * g + 3]});
+      }
+  };
+  if (kh == 0) send_tiles(acc[2], acc[3]);
+  else send_tiles(acc[0], acc[1]);
+  __syncthreads();
+  f32x16_t res[2][4];
+  auto receive = [&](const f32x16_t (&t0)[4], const f32x16_t (&t1)[4]) {
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int g = 0; g < 4; ++g) {
+        const f32x4_t p0 = lds_f32x4(xin + (uint32_t)(((c * 4 + g) * 64 + lane) * 16));
+        const f32x4_t p1 = lds_f32x4(xin + (uint32_t)((((4 + c) * 4 + g) * 64 + lane) * 16));
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          res[0][c][4 * g + e] = t0[c][4 * g + e] + p0[e];
+          res[1][c][4 * g + e] = t1[c][4 * g + e] + p1[e];
+        }
+      }
+  };
+  if (kh == 0) receive(acc[0], acc[1]);
+  else receive(acc[2], acc[3]);
+  __syncthreads();
+
+  // ---- store through a row-major LDS staging tile of this wave's 64 rows:
+  // lane (fr, h), register v of tile (ii, c) -> row 32 ii + 8 (v / 4) + 4 h + v % 4, column 32 c + fr
+  constexpr int ES = (YDT == DT_F32) ? 4 : 2;
+  constexpr uint32_t RS = 128 * ES + 16;  // padded row stride (bytes)
+  const uint32_t stg = (uint32_t)wave * (64 * RS);
+#pragma unroll
+  for (int ii = 0; ii < 2; ++ii)
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const uint32_t row = 32 * ii + 8 * (v >> 2) + 4 * h + (v & 3);
+        const uint32_t addr = stg + row * RS + (uint32_t)(32 * c + fr) * ES;
+        if constexpr (YDT == DT_F32)
+          *reinterpret_cast<__attribute__((address_space(3))) float*>((uintptr_t)addr) = res[ii][c][v];
+        else
+          *reinterpret_cast<__attribute__((address_space(3))) uint16_t*>((uintptr_t)addr) =
+              (uint16_t)f32_to_bf16_bits(res[ii][c][v]);
+      }
+  // the staging tile is private to this wave: LDS instructions of a wave run in order
+  const int64_t rbase = m0 + 128 * mh + 64 * kh;
+  constexpr int CPR = 128 * ES / 16;  // 16-byte chunks per row
+  const bool vec_store = ((N * ES) % 16) == 0;
+  char* y = reinterpret_cast<char*>(a.y);
+#pragma unroll
+  for (int it = 0; it < 64 * CPR / 64; ++it) {
+    const int idx = it * 64 + lane;
+    const int row = idx / CPR, ch = idx % CPR;
+    const int64_t gr = rbase + row;
+    const int64_t gc = n0 + ch * (16 / ES);
+    const u32x4_t v = lds_u32x4(stg + (uint32_t)row * RS + (uint32_t)ch * 16);
+    if (gr < M) {
+      char* dst = y + (gr * N + gc) * ES;
+      if (vec_store && gc + 16 / ES <= N) {
+        *reinterpret_cast<u32x4_t*>(dst) = v;
+      } else {
+#pragma unroll
+        for (int e = 0; e < 16 / ES; ++e) {
+          if (gc + e < N) {
+            // (copy the element out first: bit-casting a vector-element lvalue
+            // directly reads element 0)
+            const uint32_t ve = v[e];
+            if constexpr (YDT == DT_F32) reinterpret_cast<float*>(dst)[e] = __uint_as_float(ve);
+            else reinterpret_cast<uint16_t*>(dst)[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+          }
+        }
+      }
+    }
+  }
 }
 
 template <int BITS, int YDT>
-__global__ __launch_bounds__(256) void k_gemm(LinearArgs a, Levels lv) {
-  constexpr int NL = 1 << BITS;
-  __shared__ __attribute__((aligned(16))) uint16_t sX[BM * LDK];
-  __shared__ __attribute__((aligned(16))) uint16_t sW[BN * LDK];
-  __shared__ float sL[NL];
-
-  const int tid = threadIdx.x;
-  stage_levels<NL>(lv, sL);
-
-  const int lane = tid & 63, wave = tid >> 6;
-  const int wm = wave >> 1, wn = wave & 1;
-  const int64_t M = a.M, N = a.N, K = a.K, nb = K >> 6;
-  const int64_t m0 = (int64_t)blockIdx.y * BM, n0 = (int64_t)blockIdx.x * BN;
-  const uint16_t* x = reinterpret_cast<const uint16_t*>(a.x);
-
-  // loader mapping: row (tid >> 1), half block (tid & 1): 32 elements each
-  const int lrow = tid >> 1, lhalf = tid & 1;
-  const int64_t xm = m0 + lrow, wn_row = n0 + lrow;
-  const bool xv = xm < M, wv = wn_row < N;
-  const uint16_t* xsrc = x + (xv ? xm : 0) * K + lhalf * 32;
-  const int64_t wblk_row = (wv ? wn_row : 0) * nb;
-  uint16_t* xdst = sX + lrow * LDK + lhalf * 32;
-  uint16_t* wdst = sW + lrow * LDK + lhalf * 32;
-
-  f32x16_t acc[2][2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.0f;
-
-  const int fr = lane & 31, fk = (lane >> 5) * 8;
-  auto mma_tile = [&]() {
-#pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      u32x4_t af[2], bfr[2];
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-        af[i] = *reinterpret_cast<const u32x4_t*>(sX + (wm * 64 + i * 32 + fr) * LDK + ks * 16 + fk);
-#pragma unroll
-      for (int j = 0; j < 2; ++j)
-        bfr[j] = *reinterpret_cast<const u32x4_t*>(sW + (wn * 64 + j * 32 + fr) * LDK + ks * 16 + fk);
-#pragma unroll
-      for (int i = 0; i < 2; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j) acc[i][j] = mfma32x32x16(as_bf16x8(af[i]), as_bf16x8(bfr[j]), acc[i][j]);
-    }
-  };
-
-  __syncthreads();
-  const uint4 z4 = make_uint4(0u, 0u, 0u, 0u);
-#pragma unroll 1
-  for (int64_t kb = 0; kb < nb; ++kb) {
-    uint4 xr[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) xr[i] = xv ? *reinterpret_cast<const uint4*>(xsrc + kb * 64 + i * 8) : z4;
-    uint32_t c[BITS];
-    float ap = 0.0f;
-    if (wv) {
-      const int64_t blk = wblk_row + kb;
-      load_codes32<BITS>(a.codes + blk * (8 * BITS) + lhalf * (4 * BITS), c);
-      ap = (float)a.q8[blk] * a.cst[blk >> 8];
-    } else {
-#pragma unroll
-      for (int i = 0; i < BITS; ++i) c[i] = 0u;
-    }
-    uint32_t wp[16];
-#pragma unroll
-    for (int i = 0; i < 16; ++i)
-      wp[i] = pack_bf16x2(sL[code_at<BITS>(c, 2 * i)] * ap, sL[code_at<BITS>(c, 2 * i + 1)] * ap);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) *reinterpret_cast<uint4*>(xdst + i * 8) = xr[i];
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      *reinterpret_cast<uint4*>(wdst + i * 8) = make_uint4(wp[4 * i], wp[4 * i + 1], wp[4 * i + 2], wp[4 * i + 3]);
-    __syncthreads();
-    mma_tile();
-    __syncthreads();
+hipError_t launch_gemm_t(const LinearArgs& a, const Levels& lv, hipStream_t s) {
+  const size_t shmem = gemm_lds_bytes<BITS>();
+  auto kern = k_gemm<BITS, YDT>;
+  static bool attr = false;
+  if (!attr) {
+    // the kernel addresses LDS from 0: it must not have static LDS
+    hipFuncAttributes fa;
+    hipError_t e = hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(kern));
+    if (e != hipSuccess) return e;
+    if (fa.sharedSizeBytes != 0) return hipErrorInvalidKernelFile;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
+    if (e != hipSuccess) return e;
+    attr = true;
   }
-
-  // adapter branch as extra K: columns [0, rp) hold hi(s t), [rp, 2rp) lo(s t)
-  if (a.r > 0) {
-    const int r = a.r, rp = (r + 15) & ~15, ke = 2 * rp;
-    const uint16_t* Bl = reinterpret_cast<const uint16_t*>(a.B);
-#pragma unroll 1
-    for (int kc = 0; kc < ke; kc += BK) {
-#pragma unroll 4
-      for (int i = 0; i < 32; ++i) {
-        const int kk = kc + lhalf * 32 + i;
-        uint16_t xv16 = 0, wv16 = 0;
-        if (kk < ke) {
-          const int j = kk < rp ? kk : kk - rp;
-          if (j < r) {
-            if (xv) {
-              float tj = 0.0f;
-              for (int sp = 0; sp < a.t_splits; ++sp) tj += a.t[((int64_t)sp * M + xm) * r + j];
-              const float st = a.scale * tj;
-              const uint32_t hi = f32_to_bf16_bits(st);
-              xv16 = (uint16_t)(kk < rp ? hi : f32_to_bf16_bits(st - bf16_bits_to_f32(hi)));
-            }
-            if (wv) wv16 = Bl[wn_row * r + j];
-          }
-        }
-        xdst[i] = xv16;
-        wdst[i] = wv16;
-      }
-      __syncthreads();
-      mma_tile();
-      __syncthreads();
-    }
+  // x is read through a buffer resource with 32-bit offsets: one launch covers
+  // at most 2^31 bytes of x (whole 256-row tiles)
+  const int64_t row_bytes = a.K * 2;
+  if (row_bytes * (BM + 8) >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+  const int64_t max_rows = std::max<int64_t>(BM, ((int64_t(1) << 31) - 1) / row_bytes / BM * BM);
+  for (int64_t mb = 0; mb < a.M; mb += max_rows) {
+    GemmParams P;
+    P.a = a;
+    P.m_begin = mb;
+    P.m_end = std::min(a.M, mb + max_rows);
+    P.mtiles = (P.m_end - mb + BM - 1) / BM;
+    P.ntiles = (a.N + BN - 1) / BN;
+    P.per_xcd = (P.mtiles * P.ntiles + 7) / 8;
+    hipLaunchKernelGGL(kern, dim3((unsigned)(8 * P.per_xcd)), dim3(256), shmem, s, P, lv);
+    const hipError_t e = hipGetLastError();
+    if (e != hipSuccess) return e;
   }
-
-  // store: 32x32 output layout, lane l / register v -> row 8(v/4) + 4(l/32) + v%4, column l%32
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int64_t row = m0 + wm * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        const int64_t col = n0 + wn * 64 + j * 32 + (lane & 31);
-        if (row < M && col < N) {
-          if constexpr (YDT == DT_F32) reinterpret_cast<float*>(a.y)[row * N + col] = acc[i][j][v];
-          else reinterpret_cast<uint16_t*>(a.y)[row * N + col] = (uint16_t)f32_to_bf16_bits(acc[i][j][v]);
-        }
-      }
+  return hipSuccess;
 }
 
 template <int BITS>
 hipError_t launch_gemm_b(const LinearArgs& a, const Levels& lv, hipStream_t s) {
-  dim3 grid((unsigned)((a.N + BN - 1) / BN), (unsigned)((a.M + BM - 1) / BM)), block(256);
-  if (a.ydt == DT_F32) hipLaunchKernelGGL((k_gemm<BITS, DT_F32>), grid, block, 0, s, a, lv);
-  else hipLaunchKernelGGL((k_gemm<BITS, DT_BF16>), grid, block, 0, s, a, lv);
-  return hipGetLastError();
+  if (a.ydt == DT_F32) return launch_gemm_t<BITS, DT_F32>(a, lv, s);
+  return launch_gemm_t<BITS, DT_BF16>(a, lv, s);
 }
 
 }  // namespace
