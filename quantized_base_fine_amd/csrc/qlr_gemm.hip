@@ -220,7 +220,7 @@ struct GemmParams {
 };
 
 template <int BITS, int YDT>
-__global__ __launch_bounds__(256, 1) void k_gemm(GemmParams P, Levels lv) {
+__global__ __launch_bounds__(512, 1) void k_gemm(GemmParams P, Levels lv) {
   extern __shared__ uint32_t smem[];
   const LinearArgs& a = P.a;
   const int64_t N = a.N, K = a.K, nb = K >> 6;
@@ -234,352 +234,326 @@ __global__ __launch_bounds__(256, 1) void k_gemm(GemmParams P, Levels lv) {
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
-  const int mh = wave & 1, kh = wave >> 1;  // row half and K half of this wave
   const int fr = lane & 31, h = lane >> 5;
-
-  // x of this launch as a buffer resource: reads past its last row return zero
-  const uint16_t* xs_base = reinterpret_cast<const uint16_t*>(a.x) + P.m_begin * K;
-  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(xs_base), (short)0, (int)((P.m_end - P.m_begin) * K * 2), 0x00020000);
-  // staging load j (0..7): tile row 64 wave + 8 j + lane / 8, 16-byte chunk lane % 8
-  const uint32_t xg0 = (uint32_t)(((m0 - P.m_begin) + 64 * wave + (lane >> 3)) * K + 8 * (lane & 7)) * 2u;
-  const uint32_t xg_row8 = (uint32_t)(8 * K * 2);
-  // its LDS slot: row 64 wave + 8 j + t (t = lane / 8), swizzle g = t ^ bit2(t) ^ (j & 1)
-  uint32_t xst[2];
-#pragma unroll
-  for (int p = 0; p < 2; ++p) {
-    const uint32_t t = (uint32_t)(lane >> 3);
-    xst[p] = kXOff + (uint32_t)((64 * wave + t) * 128) + ((((uint32_t)lane & 7u) ^ swz(t + 8u * p)) << 4);
-  }
-
-  // fragment of step s (0, 1) of this wave: row fr (+32 i or +32 c), chunk 4 kh + 2 s + h
-  uint32_t fo[2];
-#pragma unroll
-  for (int s = 0; s < 2; ++s) fo[s] = (uint32_t)(fr * 128) + ((((uint32_t)(4 * kh + 2 * s + h)) ^ swz((uint32_t)fr & 15u)) << 4);
-  const uint32_t xrow0 = (uint32_t)(128 * mh * 128);  // first tile row of this wave's A fragments
-
-  // weight row this thread dequantizes: rr = tid / 2, codes [32 dh, 32 dh + 32) of each block
-  const int rr = tid >> 1, dh = tid & 1;
-  const int64_t wn = n0 + rr;
-  const bool wv = wn < N;
-  const int64_t wblk = (wv ? wn : N - 1) * nb;
-  uint32_t wst[4];  // LDS slot of chunk 4 dh + q of row rr
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-    wst[q] = kWOff + (uint32_t)(rr * 128) + ((((uint32_t)(4 * dh + q)) ^ swz((uint32_t)rr & 15u)) << 4);
-  const uint32_t tp = kTOff + (BITS == 8 ? 4u * (lane & 15) : 8u * fr);
-
-  struct XS { u32x4_t v[8]; };
-  struct CS { Codes32<BITS> c; uint32_t q8; float sc; };
-  auto load_x = [&](XS& st, int64_t kb) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j)
-      st.v[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(xr, xg0 + j * xg_row8, (int)(kb * 128), 0));
-  };
-  auto store_x = [&](const XS& st, int buf) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) lds_store_u32x4(xst[j & 1] + buf * kXTile + 1024u * j, st.v[j]);
-  };
-  auto load_c = [&](CS& st, int64_t kb) {
-    const int64_t blk = wblk + kb;
-    st.c = load_codes32<BITS>(a.codes + blk * (8 * BITS) + dh * (4 * BITS));
-    st.q8 = a.q8[blk];
-    st.sc = a.cst[blk >> 8];
-  };
-  auto store_w = [&](const uint32_t (&o)[16], int buf) {
-#pragma unroll
-    for (int q = 0; q < 4; ++q)
-      lds_store_u32x4(wst[q] + buf * kWTile, u32x4_t{o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]});
-  };
-  // Dequantization of one thread's 32 codes in two halves (o[0..7], o[8..15]).
-  struct DQ { Codes32<BITS> c; float ap; Lut4 t; };
-  auto dq_begin = [&](const CS& cs) {
-    // Pin the codes here: an empty register-only asm makes them opaque, so
-    // instruction selection cannot start their arithmetic right after the load
-    // (which would wait for codes still in flight).
-    DQ d;
-    d.c = cs.c;
-    uint32_t q8 = cs.q8;
-    float sc = cs.sc;
-#pragma unroll
-    for (int i = 0; i < BITS; ++i) asm volatile("" : "+v"(d.c.w[i]));
-    asm volatile("" : "+v"(q8), "+v"(sc));
-    d.ap = wv ? (float)q8 * sc : 0.0f;
-    if constexpr (BITS == 4) d.t = make_lut4(lv, d.ap);
-    return d;
-  };
-  auto dq_half = [&](const DQ& d, auto half, uint32_t (&o)[16]) {
-    constexpr int H = decltype(half)::value;
-    if constexpr (BITS == 4) {
-      lut4_word(d.c.w[2 * H], d.t, o + 8 * H);
-      lut4_word(d.c.w[2 * H + 1], d.t, o + 8 * H + 4);
-    } else {
-      dequant_pairs<BITS, 8 * H, 8 * H + 8>(d.c, d.ap, tp, o);
-    }
-  };
-  // Values computed before this point stay before it: instruction selection
-  // otherwise places pure arithmetic next to its uses (here: the tile stores at
-  // the end of the block), out of the phase it is meant to overlap.
-  auto pin8 = [](uint32_t (&o)[16], int j0) {
-#pragma unroll
-    for (int j = 0; j < 8; ++j) asm volatile("" : "+v"(o[j0 + j]));
-  };
-  auto dequant = [&](const CS& cs, uint32_t (&o)[16]) {
-    const DQ d = dq_begin(cs);
-    dq_half(d, std::integral_constant<int, 0>{}, o);
-    dq_half(d, std::integral_constant<int, 1>{}, o);
-  };
-
-  f32x16_t acc[4][4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i)
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) acc[i][c][v] = 0.0f;
-
-  // Loads past the last block reload the last block (harmless: they fill spare
-  // buffers nobody reads), so no load sits behind a branch.
   const int64_t kbl = nb - 1;
-  XS xs;
-  CS c0, c1, c2;
-  load_x(xs, 0);
-  load_c(c0, 0);
-  load_c(c1, min<int64_t>(1, kbl));
-  load_c(c2, min<int64_t>(2, kbl));
+
   if constexpr (BITS != 4) {
     float* sL = reinterpret_cast<float*>(smem) + kXOff / 4;
     stage_levels<1 << BITS>(lv, sL);
     __syncthreads();
     build_gemm_table<BITS>(sL, tid);
-    __syncthreads();
-  }
-  {
-    uint32_t o[16];
-    store_x(xs, 0);
-    dequant(c0, o);
-    store_w(o, 0);
-    load_x(xs, min<int64_t>(1, kbl));
-    load_c(c0, min<int64_t>(3, kbl));
-    dequant(c1, o);
-    store_w(o, 1);
-    store_x(xs, 1);
   }
   __syncthreads();
 
-  // fragments of step 0 of block 0
-  u32x4_t fa[2][4], fb[2][4];
+  if (wave >= 4) {
+    // =================== producers: x staging and dequantization ===================
+    const int pt = tid - 256;  // 0..255
+    const int pw = wave - 4;
+    // x of this launch as a buffer resource: reads past its last row return zero
+    const uint16_t* xs_base = reinterpret_cast<const uint16_t*>(a.x) + P.m_begin * K;
+    const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint16_t*>(xs_base), (short)0, (int)((P.m_end - P.m_begin) * K * 2), 0x00020000);
+    // staging load j (0..7): tile row 64 pw + 8 j + t (t = lane / 8), 16-byte chunk lane % 8
+    const uint32_t t8 = (uint32_t)(lane >> 3);
+    const uint32_t xg0 = (uint32_t)(((m0 - P.m_begin) + 64 * pw + t8) * K + 8 * (lane & 7)) * 2u;
+    const uint32_t xg_row8 = (uint32_t)(8 * K * 2);
+    uint32_t xst[2];  // LDS slot of row 64 pw + 8 j + t: swizzle depends on j only through j & 1
 #pragma unroll
-  for (int i = 0; i < 4; ++i) fa[0][i] = lds_u32x4(kXOff + xrow0 + fo[0] + 4096u * i);
+    for (int p = 0; p < 2; ++p)
+      xst[p] = kXOff + (uint32_t)((64 * pw + t8) * 128) + ((((uint32_t)lane & 7u) ^ swz(t8 + 8u * p)) << 4);
+    // weight row this thread dequantizes: rr = pt / 2, codes [32 dh, 32 dh + 32) of each block
+    const int rr = pt >> 1, dh = pt & 1;
+    const int64_t wn = n0 + rr;
+    const bool wv = wn < N;
+    const int64_t wblk = (wv ? wn : N - 1) * nb;
+    uint32_t wst[4];  // LDS slot of chunk 4 dh + q of row rr
 #pragma unroll
-  for (int c = 0; c < 4; ++c) fb[0][c] = lds_u32x4(kWOff + fo[0] + 4096u * c);
+    for (int q = 0; q < 4; ++q)
+      wst[q] = kWOff + (uint32_t)(rr * 128) + ((((uint32_t)(4 * dh + q)) ^ swz((uint32_t)rr & 15u)) << 4);
+    const uint32_t tp = kTOff + (BITS == 8 ? 4u * (lane & 15) : 8u * fr);
 
-  // One block k (buffer bc = k % 3), in pinned phases (sched_barrier keeps the
-  // scheduler from sinking fragment reads next to their MFMAs or hoisting later
-  // blocks' work):
-  //  1. loads of x(k+2) and codes(k+4); LDS reads of step 1's fragments;
-  //  2. 16 MFMAs of step 0 interleaved with the first half of the dequantization
-  //     of block k+2;
-  //  3. LDS reads of step 0's fragments of block k+1 (buffer bn, written one
-  //     block earlier);
-  //  4. 16 MFMAs of step 1 with the second half of the dequantization;
-  //  5. block k+2's weight and x tiles into buffer bw; one barrier.
-  auto step = [&](const CS& cd, CS& cl, int64_t k, int bc, int bn, int bw) {
-    __builtin_amdgcn_sched_barrier(0);
-    load_x(xs, min(k + 2, kbl));
-    load_c(cl, min(k + 4, kbl));
+    struct XS { u32x4_t v[8]; };
+    struct CS { Codes32<BITS> c; uint32_t q8; float sc; };
+    auto load_xj = [&](XS& st, int64_t kb, int j) {
+      st.v[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(xr, xg0 + j * xg_row8, (int)(kb * 128), 0));
+    };
+    auto load_x = [&](XS& st, int64_t kb) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) fa[1][i] = lds_u32x4(kXOff + bc * kXTile + xrow0 + fo[1] + 4096u * i);
+      for (int j = 0; j < 8; ++j) load_xj(st, kb, j);
+    };
+    auto store_x = [&](const XS& st, int buf) {
 #pragma unroll
-    for (int c = 0; c < 4; ++c) fb[1][c] = lds_u32x4(kWOff + bc * kWTile + fo[1] + 4096u * c);
-    __builtin_amdgcn_sched_barrier(0);
-    uint32_t o[16];
-    const DQ d = dq_begin(cd);
-    dq_half(d, std::integral_constant<int, 0>{}, o);
+      for (int j = 0; j < 8; ++j) lds_store_u32x4(xst[j & 1] + buf * kXTile + 1024u * j, st.v[j]);
+    };
+    auto load_c = [&](CS& st, int64_t kb) {
+      const int64_t blk = wblk + kb;
+      st.c = load_codes32<BITS>(a.codes + blk * (8 * BITS) + dh * (4 * BITS));
+      st.q8 = a.q8[blk];
+      st.sc = a.cst[blk >> 8];
+    };
+    // Dequantization of block kb's codes (pinned first: an empty register-only
+    // asm makes them opaque, so instruction selection cannot start their
+    // arithmetic right after the load, which would wait for codes in flight).
+    struct DQ { Codes32<BITS> c; float ap; Lut4 t; };
+    auto dq_begin = [&](const CS& cs) {
+      DQ d;
+      d.c = cs.c;
+      uint32_t q8 = cs.q8;
+      float sc = cs.sc;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+      for (int i = 0; i < BITS; ++i) asm volatile("" : "+v"(d.c.w[i]));
+      asm volatile("" : "+v"(q8), "+v"(sc));
+      d.ap = wv ? (float)q8 * sc : 0.0f;
+      if constexpr (BITS == 4) d.t = make_lut4(lv, d.ap);
+      return d;
+    };
+    // pairs [4 i, 4 i + 4) of the 16 output pairs (for 4-bit: code word i); the
+    // results are pinned so that they are computed here, not next to the stores
+    auto dq_part = [&](const DQ& d, auto part, uint32_t (&o)[16]) {
+      constexpr int I = decltype(part)::value;
+      if constexpr (BITS == 4) lut4_word(d.c.w[I], d.t, o + 4 * I);
+      else dequant_pairs<BITS, 4 * I, 4 * I + 4>(d.c, d.ap, tp, o);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) acc[i][c] = mfma32x32x16(as_bf16x8(fa[0][i]), as_bf16x8(fb[0][c]), acc[i][c]);
+      for (int j = 4 * I; j < 4 * I + 4; ++j) asm volatile("" : "+v"(o[j]));
+    };
+    auto store_w = [&](const uint32_t (&o)[16], int buf) {
 #pragma unroll
-    for (int g = 0; g < 16; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // 1 MFMA
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);  // up to 4 VALU
-    }
-    pin8(o, 0);  // the first half is computed in this phase
-    __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-    for (int i = 0; i < 4; ++i) fa[0][i] = lds_u32x4(kXOff + bn * kXTile + xrow0 + fo[0] + 4096u * i);
-#pragma unroll
-    for (int c = 0; c < 4; ++c) fb[0][c] = lds_u32x4(kWOff + bn * kWTile + fo[0] + 4096u * c);
-    dq_half(d, std::integral_constant<int, 1>{}, o);
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int c = 0; c < 4; ++c) acc[i][c] = mfma32x32x16(as_bf16x8(fa[1][i]), as_bf16x8(fb[1][c]), acc[i][c]);
-    __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // the 8 fragment reads first
-#pragma unroll
-    for (int g = 0; g < 16; ++g) {
-      __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-      __builtin_amdgcn_sched_group_barrier(0x002, 4, 0);
-    }
-    pin8(o, 8);
-    __builtin_amdgcn_sched_barrier(0);
-    store_w(o, bw);
-    store_x(xs, bw);
+      for (int q = 0; q < 4; ++q)
+        lds_store_u32x4(wst[q] + buf * kWTile, u32x4_t{o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]});
+    };
+    auto dequant_store = [&](const CS& cs, int buf) {
+      const DQ d = dq_begin(cs);
+      uint32_t o[16];
+      dq_part(d, std::integral_constant<int, 0>{}, o);
+      dq_part(d, std::integral_constant<int, 1>{}, o);
+      dq_part(d, std::integral_constant<int, 2>{}, o);
+      dq_part(d, std::integral_constant<int, 3>{}, o);
+      store_w(o, buf);
+    };
+
+    // Block k+2 is written while the consumers multiply block k.  x(k+2) was
+    // loaded one block earlier (set (k+2) % 3), codes(k+2) two blocks earlier.
+    XS x0, x1, x2;
+    CS c0, c1, c2;
+    load_x(x0, 0);
+    load_c(c0, 0);
+    load_x(x1, min<int64_t>(1, kbl));
+    load_c(c1, min<int64_t>(1, kbl));
+    load_c(c2, min<int64_t>(2, kbl));
+    load_x(x2, min<int64_t>(2, kbl));
+    store_x(x0, 0);
+    dequant_store(c0, 0);
+    load_c(c0, min<int64_t>(3, kbl));
+    store_x(x1, 1);
+    dequant_store(c1, 1);
     __syncthreads();
-    __builtin_amdgcn_sched_barrier(0);
-  };
-
-  // codes: block k+2 is in set (k+2) % 3; block k+4 is loaded into set (k+1) % 3
-  const int64_t nb3 = nb - nb % 3;
-  int64_t kb = 0;
-  for (; kb < nb3; kb += 3) {
-    step(c2, c1, kb, 0, 1, 2);
-    step(c0, c2, kb + 1, 1, 2, 0);
-    step(c1, c0, kb + 2, 2, 0, 1);
-  }
-  if (kb < nb) step(c2, c1, kb, 0, 1, 2);
-  if (kb + 1 < nb) step(c0, c2, kb + 1, 1, 2, 0);
-
-  // ---- adapter branch: extra K steps [hi(s t) | lo(s t)] x [B | B], step q on K half q % 2
-  if (a.r > 0) {
-    const int r = a.r;
-    const uint16_t* Bl = reinterpret_cast<const uint16_t*>(a.B);
-    const int nsteps = (r + 15) / 16;
-    const bool vec = (r % 8) == 0;  // B rows hold whole 16-byte groups
-    for (int q = kh; q < nsteps; q += 2) {
-      const int j0 = 16 * q + 8 * h;  // this lane's 8 adapter columns
-      u32x4_t bf[4];
+    // step k: load x(k+3) into set k % 3 and codes(k+4) into set (k+1) % 3; write block k+2
+    // Step k: load x(k+3) into set k % 3 and codes(k+4) into set (k+1) % 3;
+    // write x(k+2) and the dequantized block k+2 into buffer (k+2) % 3.  The
+    // step runs in pinned chunks, each a few loads plus the arithmetic of one
+    // code word, so the wave keeps computing while the load queue drains.
+    auto pstep = [&](XS& xl, const XS& xw, CS& cl, const CS& cw, int64_t k, int bw) {
+      __builtin_amdgcn_sched_barrier(0);
+      load_c(cl, min(k + 4, kbl));
+      const DQ d = dq_begin(cw);
+      uint32_t o[16];
+      dq_part(d, std::integral_constant<int, 0>{}, o);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const int64_t n = n0 + 32 * c + fr;
-        bf[c] = u32x4_t{0u, 0u, 0u, 0u};
-        if (n < N) {
-          const uint16_t* bp = Bl + n * (int64_t)r;
-          if (vec && j0 + 8 <= r) {
-            bf[c] = *reinterpret_cast<const u32x4_t*>(bp + j0);
-          } else {
+      for (int j = 0; j < 3; ++j) load_xj(xl, min(k + 3, kbl), j);
 #pragma unroll
-            for (int e2 = 0; e2 < 4; ++e2) {
-              const uint32_t lo = (j0 + 2 * e2 < r) ? bp[j0 + 2 * e2] : 0u;
-              const uint32_t hi = (j0 + 2 * e2 + 1 < r) ? bp[j0 + 2 * e2 + 1] : 0u;
-              bf[c][e2] = lo | (hi << 16);
+      for (int j = 0; j < 3; ++j) lds_store_u32x4(xst[j & 1] + bw * kXTile + 1024u * j, xw.v[j]);
+      dq_part(d, std::integral_constant<int, 1>{}, o);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 3; j < 6; ++j) load_xj(xl, min(k + 3, kbl), j);
+#pragma unroll
+      for (int j = 3; j < 6; ++j) lds_store_u32x4(xst[j & 1] + bw * kXTile + 1024u * j, xw.v[j]);
+      dq_part(d, std::integral_constant<int, 2>{}, o);
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int j = 6; j < 8; ++j) load_xj(xl, min(k + 3, kbl), j);
+#pragma unroll
+      for (int j = 6; j < 8; ++j) lds_store_u32x4(xst[j & 1] + bw * kXTile + 1024u * j, xw.v[j]);
+      dq_part(d, std::integral_constant<int, 3>{}, o);
+      store_w(o, bw);
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
+      __builtin_amdgcn_sched_barrier(0);
+    };
+    const int64_t nb3 = nb - nb % 3;
+    int64_t kb = 0;
+    for (; kb < nb3; kb += 3) {
+      pstep(x0, x2, c1, c2, kb, 2);
+      pstep(x1, x0, c2, c0, kb + 1, 0);
+      pstep(x2, x1, c0, c1, kb + 2, 1);
+    }
+    if (kb < nb) pstep(x0, x2, c1, c2, kb, 2);
+    if (kb + 1 < nb) pstep(x1, x0, c2, c0, kb + 1, 0);
+    // the consumers' two epilogue barriers: tiles free, then the output staged
+    __syncthreads();
+    __syncthreads();
+  } else {
+    // =================== consumers: MFMA on 128 x 64 of the tile ===================
+    const int mh = wave & 1, nh = wave >> 1;
+    // fragment of step s (0..3): row fr (+32 i or +32 c), chunk 2 s + h
+    uint32_t fo[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) fo[s] = (uint32_t)(fr * 128) + ((((uint32_t)(2 * s + h)) ^ swz((uint32_t)fr & 15u)) << 4);
+    const uint32_t xrow0 = (uint32_t)(128 * mh * 128);
+    const uint32_t wrow0 = (uint32_t)(64 * nh * 128);
+
+    f32x16_t acc[4][2];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int c = 0; c < 2; ++c)
+#pragma unroll
+        for (int v = 0; v < 16; ++v) acc[i][c][v] = 0.0f;
+
+    __syncthreads();  // producers: blocks 0 and 1 written
+    u32x4_t fa[2][4], fb[2][2];
+    auto read_frags = [&](int buf, int s, int slot) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) fa[slot][i] = lds_u32x4(kXOff + buf * kXTile + xrow0 + fo[s] + 4096u * i);
+#pragma unroll
+      for (int c = 0; c < 2; ++c) fb[slot][c] = lds_u32x4(kWOff + buf * kWTile + wrow0 + fo[s] + 4096u * c);
+    };
+    auto mfmas = [&](int slot) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int c = 0; c < 2; ++c) acc[i][c] = mfma32x32x16(as_bf16x8(fa[slot][i]), as_bf16x8(fb[slot][c]), acc[i][c]);
+    };
+    read_frags(0, 0, 0);
+    // block k: four MFMA steps, each first reading the next step's fragments
+    // (after step 3: step 0 of block k+1, buffer bn, written one block earlier)
+    auto cstep = [&](int bc, int bn) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s) {
+        __builtin_amdgcn_sched_barrier(0);
+        if (s < 3) read_frags(bc, s + 1, (s + 1) & 1);
+        else read_frags(bn, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        mfmas(s & 1);
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      __syncthreads();
+    };
+    const int64_t nb3 = nb - nb % 3;
+    int64_t kb = 0;
+    for (; kb < nb3; kb += 3) {
+      cstep(0, 1);
+      cstep(1, 2);
+      cstep(2, 0);
+    }
+    if (kb < nb) cstep(0, 1);
+    if (kb + 1 < nb) cstep(1, 2);
+
+    // ---- adapter branch: extra K steps [hi(s t) | lo(s t)] x [B | B]
+    if (a.r > 0) {
+      const int r = a.r;
+      const uint16_t* Bl = reinterpret_cast<const uint16_t*>(a.B);
+      const int nsteps = (r + 15) / 16;
+      const bool vec = (r % 8) == 0;  // B rows hold whole 16-byte groups
+      for (int q = 0; q < nsteps; ++q) {
+        const int j0 = 16 * q + 8 * h;  // this lane's 8 adapter columns
+        u32x4_t bf[2];
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const int64_t n = n0 + 64 * nh + 32 * c + fr;
+          bf[c] = u32x4_t{0u, 0u, 0u, 0u};
+          if (n < N) {
+            const uint16_t* bp = Bl + n * (int64_t)r;
+            if (vec && j0 + 8 <= r) {
+              bf[c] = *reinterpret_cast<const u32x4_t*>(bp + j0);
+            } else {
+#pragma unroll
+              for (int e2 = 0; e2 < 4; ++e2) {
+                const uint32_t lo = (j0 + 2 * e2 < r) ? bp[j0 + 2 * e2] : 0u;
+                const uint32_t hi = (j0 + 2 * e2 + 1 < r) ? bp[j0 + 2 * e2 + 1] : 0u;
+                bf[c][e2] = lo | (hi << 16);
+              }
             }
           }
         }
-      }
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t m = m0 + 128 * mh + 32 * i + fr;
-        const bool mv = m < M;
-        float v8[8];
+        for (int i = 0; i < 4; ++i) {
+          const int64_t m = m0 + 128 * mh + 32 * i + fr;
+          const bool mv = m < M;
+          float v8[8];
 #pragma unroll
-        for (int e = 0; e < 8; ++e) v8[e] = 0.0f;
-        for (int sp = 0; sp < a.t_splits; ++sp) {
-          const float* tq = a.t + ((int64_t)sp * a.M + (mv ? m : 0)) * r;
+          for (int e = 0; e < 8; ++e) v8[e] = 0.0f;
+          for (int sp = 0; sp < a.t_splits; ++sp) {
+            const float* tq = a.t + ((int64_t)sp * a.M + (mv ? m : 0)) * r;
 #pragma unroll
-          for (int e = 0; e < 8; ++e) v8[e] += (mv && j0 + e < r) ? tq[j0 + e] : 0.0f;
-        }
-        u32x4_t thi, tlo;
+            for (int e = 0; e < 8; ++e) v8[e] += (mv && j0 + e < r) ? tq[j0 + e] : 0.0f;
+          }
+          u32x4_t thi, tlo;
 #pragma unroll
-        for (int e2 = 0; e2 < 4; ++e2) {
-          const float u0 = a.scale * v8[2 * e2], u1 = a.scale * v8[2 * e2 + 1];
-          const uint32_t hb0 = f32_to_bf16_bits(u0), hb1 = f32_to_bf16_bits(u1);
-          thi[e2] = hb0 | (hb1 << 16);
-          tlo[e2] = pack_bf16x2(u0 - bf16_bits_to_f32(hb0), u1 - bf16_bits_to_f32(hb1));
-        }
+          for (int e2 = 0; e2 < 4; ++e2) {
+            const float u0 = a.scale * v8[2 * e2], u1 = a.scale * v8[2 * e2 + 1];
+            const uint32_t hb0 = f32_to_bf16_bits(u0), hb1 = f32_to_bf16_bits(u1);
+            thi[e2] = hb0 | (hb1 << 16);
+            tlo[e2] = pack_bf16x2(u0 - bf16_bits_to_f32(hb0), u1 - bf16_bits_to_f32(hb1));
+          }
 #pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          acc[i][c] = mfma32x32x16(as_bf16x8(thi), as_bf16x8(bf[c]), acc[i][c]);
-          acc[i][c] = mfma32x32x16(as_bf16x8(tlo), as_bf16x8(bf[c]), acc[i][c]);
+          for (int c = 0; c < 2; ++c) {
+            acc[i][c] = mfma32x32x16(as_bf16x8(thi), as_bf16x8(bf[c]), acc[i][c]);
+            acc[i][c] = mfma32x32x16(as_bf16x8(tlo), as_bf16x8(bf[c]), acc[i][c]);
+          }
         }
       }
     }
-  }
+    __syncthreads();  // every wave is past its last tile read: the staging area is free
 
-  // ---- K-half reduction.  Wave (mh, kh) keeps row tiles 2 kh, 2 kh + 1 and
-  // hands the other two to its partner (mh, 1 - kh) through LDS (lane-major, 16
-  // bytes per lane per register group: conflict-free).  kh is uniform per wave,
-  // so each branch indexes the accumulators statically.
-  const uint32_t xch = (uint32_t)wave * 32768u;       // this wave's outgoing half
-  const uint32_t xin = (uint32_t)(wave ^ 2) * 32768u;  // the partner's
-  auto send_tiles = [&](const f32x16_t (&t0)[4], const f32x16_t (&t1)[4]) {
+    // ---- row-major staging of the 256 x 128 output tile in LDS:
+    // lane (fr, h), register v of tile (i, c) -> row 32 i + 8 (v / 4) + 4 h + v % 4, column 32 c + fr
+    constexpr int ES = (YDT == DT_F32) ? 4 : 2;
+    constexpr uint32_t RS = 128 * ES + 16;  // padded row stride (bytes)
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        lds_store_f32x4(xch + (uint32_t)(((c * 4 + g) * 64 + lane) * 16),
-                        f32x4_t{t0[c][4 * g], t0[c][4 * g + 1], t0[c][4 * g + 2], t0[c][4 * g + 3]});
-        lds_store_f32x4(xch + (uint32_t)((((4 + c) * 4 + g) * 64 + lane) * 16),
-                        f32x4_t{t1[c][4 * g], t1[c][4 * g + 1], t1[c][4 * g + 2], t1[c][4 * g + 3]});
-      }
-  };
-  if (kh == 0) send_tiles(acc[2], acc[3]);
-  else send_tiles(acc[0], acc[1]);
-  __syncthreads();
-  f32x16_t res[2][4];
-  auto receive = [&](const f32x16_t (&t0)[4], const f32x16_t (&t1)[4]) {
+      for (int c = 0; c < 2; ++c)
 #pragma unroll
-    for (int c = 0; c < 4; ++c)
-#pragma unroll
-      for (int g = 0; g < 4; ++g) {
-        const f32x4_t p0 = lds_f32x4(xin + (uint32_t)(((c * 4 + g) * 64 + lane) * 16));
-        const f32x4_t p1 = lds_f32x4(xin + (uint32_t)((((4 + c) * 4 + g) * 64 + lane) * 16));
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          res[0][c][4 * g + e] = t0[c][4 * g + e] + p0[e];
-          res[1][c][4 * g + e] = t1[c][4 * g + e] + p1[e];
+        for (int v = 0; v < 16; ++v) {
+          const uint32_t row = 128 * mh + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+          const uint32_t addr = row * RS + (uint32_t)(64 * nh + 32 * c + fr) * ES;
+          if constexpr (YDT == DT_F32)
+            *reinterpret_cast<__attribute__((address_space(3))) float*>((uintptr_t)addr) = acc[i][c][v];
+          else
+            *reinterpret_cast<__attribute__((address_space(3))) uint16_t*>((uintptr_t)addr) =
+                (uint16_t)f32_to_bf16_bits(acc[i][c][v]);
         }
-      }
-  };
-  if (kh == 0) receive(acc[0], acc[1]);
-  else receive(acc[2], acc[3]);
-  __syncthreads();
-
-  // ---- store through a row-major LDS staging tile of this wave's 64 rows:
-  // lane (fr, h), register v of tile (ii, c) -> row 32 ii + 8 (v / 4) + 4 h + v % 4, column 32 c + fr
-  constexpr int ES = (YDT == DT_F32) ? 4 : 2;
-  constexpr uint32_t RS = 128 * ES + 16;  // padded row stride (bytes)
-  const uint32_t stg = (uint32_t)wave * (64 * RS);
+    __syncthreads();  // staging written
+  }
+  // ---- coalesced global stores of the staged tile by all 512 threads
+  {
+    constexpr int ES = (YDT == DT_F32) ? 4 : 2;
+    constexpr uint32_t RS = 128 * ES + 16;
+    constexpr int CPR = 128 * ES / 16;  // 16-byte chunks per row
+    const bool vec_store = ((N * ES) % 16) == 0;
+    char* y = reinterpret_cast<char*>(a.y);
+#pragma unroll 4
+    for (int idx = tid; idx < 256 * CPR; idx += 512) {
+      const int row = idx / CPR, ch = idx % CPR;
+      const int64_t gr = m0 + row;
+      const int64_t gc = n0 + ch * (16 / ES);
+      const u32x4_t v = lds_u32x4((uint32_t)row * RS + (uint32_t)ch * 16);
+      if (gr < M && gc < N) {
+        char* dst = y + (gr * N + gc) * ES;
+        if (vec_store && gc + 16 / ES <= N) {
+          *reinterpret_cast<u32x4_t*>(dst) = v;
+        } else {
 #pragma unroll
-  for (int ii = 0; ii < 2; ++ii)
-#pragma unroll
-    for (int c = 0; c < 4; ++c)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const uint32_t row = 32 * ii + 8 * (v >> 2) + 4 * h + (v & 3);
-        const uint32_t addr = stg + row * RS + (uint32_t)(32 * c + fr) * ES;
-        if constexpr (YDT == DT_F32)
-          *reinterpret_cast<__attribute__((address_space(3))) float*>((uintptr_t)addr) = res[ii][c][v];
-        else
-          *reinterpret_cast<__attribute__((address_space(3))) uint16_t*>((uintptr_t)addr) =
-              (uint16_t)f32_to_bf16_bits(res[ii][c][v]);
-      }
-  // the staging tile is private to this wave: LDS instructions of a wave run in order
-  const int64_t rbase = m0 + 128 * mh + 64 * kh;
-  constexpr int CPR = 128 * ES / 16;  // 16-byte chunks per row
-  const bool vec_store = ((N * ES) % 16) == 0;
-  char* y = reinterpret_cast<char*>(a.y);
-#pragma unroll
-  for (int it = 0; it < 64 * CPR / 64; ++it) {
-    const int idx = it * 64 + lane;
-    const int row = idx / CPR, ch = idx % CPR;
-    const int64_t gr = rbase + row;
-    const int64_t gc = n0 + ch * (16 / ES);
-    const u32x4_t v = lds_u32x4(stg + (uint32_t)row * RS + (uint32_t)ch * 16);
-    if (gr < M) {
-      char* dst = y + (gr * N + gc) * ES;
-      if (vec_store && gc + 16 / ES <= N) {
-        *reinterpret_cast<u32x4_t*>(dst) = v;
-      } else {
-#pragma unroll
-        for (int e = 0; e < 16 / ES; ++e) {
-          if (gc + e < N) {
+          for (int e = 0; e < 16 / ES; ++e) {
             // (copy the element out first: bit-casting a vector-element lvalue
             // directly reads element 0)
             const uint32_t ve = v[e];
-            if constexpr (YDT == DT_F32) reinterpret_cast<float*>(dst)[e] = __uint_as_float(ve);
-            else reinterpret_cast<uint16_t*>(dst)[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+            if (gc + e < N) {
+              if constexpr (YDT == DT_F32) reinterpret_cast<float*>(dst)[e] = __uint_as_float(ve);
+              else reinterpret_cast<uint16_t*>(dst)[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
+            }
           }
         }
       }
@@ -616,7 +590,7 @@ hipError_t launch_gemm_t(const LinearArgs& a, const Levels& lv, hipStream_t s) {
     P.mtiles = (P.m_end - mb + BM - 1) / BM;
     P.ntiles = (a.N + BN - 1) / BN;
     P.per_xcd = (P.mtiles * P.ntiles + 7) / 8;
-    hipLaunchKernelGGL(kern, dim3((unsigned)(8 * P.per_xcd)), dim3(256), shmem, s, P, lv);
+    hipLaunchKernelGGL(kern, dim3((unsigned)(8 * P.per_xcd)), dim3(512), shmem, s, P, lv);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
   }
