@@ -6,12 +6,20 @@
 // weight), so the kernel is bound by HBM bandwidth; the dequantization the
 // QLoRA page's limitations section mentions is fused into the load path.
 //
-// Work decomposition: a persistent grid of 1024-thread workgroups (one per CU)
-// walks 16-row tiles of W; inside a workgroup the 16 waves split K (whole
+// Work decomposition: a persistent grid of 512-thread workgroups (one per CU)
+// walks 16-row tiles of W; inside a workgroup the 8 waves split K (whole
 // 64-element blocks) and are reduced through LDS at the end of every tile.
-// Each wave streams its code slice in chunks of up to CH blocks and keeps one
-// chunk in flight ahead of the one it computes, across tile boundaries too, so
-// HBM requests stay outstanding while the previous tile is reduced.
+// Each wave streams its K slice in chunks of 4 blocks and keeps the next chunk
+// in flight (in registers) while it computes the current one, across tile
+// boundaries too.
+//
+// Loads are shaped for the vector memory pipeline, which serves a group of 4
+// consecutive lanes per cycle when they read one 64-byte segment: the code
+// bytes of a chunk (16 rows x 4 blocks) are read as 16-byte pieces, 8
+// consecutive lanes per row, through a buffer resource (rows past N read as
+// zero), and staged in a wave-private LDS slice; the absmax codes and group
+// constants are read one (row, block) per lane, 4 consecutive blocks of a row
+// per lane quad, turned into scales and staged beside them.
 //
 // Layout on the 16x16x32 bf16 MFMA (A = x rows, B = unscaled levels):
 //   lane l: x row / weight row (l & 15), lane group g = l >> 4 owns the 16
@@ -32,19 +40,38 @@ namespace qlr {
 
 namespace {
 
-constexpr int kWaves = 16;
+constexpr int kWaves = 8;
 constexpr int kThreads = kWaves * 64;
-constexpr int CH = 8;  // blocks per chunk and wave
+constexpr int CH = 4;  // blocks per chunk and wave
 
-// One chunk of a wave's stream: up to CH blocks of one 16-row tile.  Only raw
-// loaded values live here: nothing is computed from them until the chunk is
-// used, so a prefetched chunk never forces a wait on its loads.
+// Per-chunk geometry for BITS-bit codes: the code bytes of 16 rows x CH blocks
+// are loaded as PB-byte pieces (8 bytes for 3-bit codes, whose 24-byte blocks
+// are only 8-byte aligned) and staged with a row stride RS chosen to keep the
+// MFMA-layout reads within 2-way bank conflicts.
 template <int BITS>
-struct Chunk {
-  Raw<BITS> raw[CH];
-  uint32_t q8[CH];
-  float sc[CH];
+struct ChunkGeo {
+  static constexpr int kRowBytes = CH * 8 * BITS;
+  static constexpr int PB = (BITS == 3) ? 8 : 16;
+  static constexpr int PR = kRowBytes / PB;          // pieces per row
+  static constexpr int NP = (16 * PR + 63) / 64;     // pieces per lane
+  static constexpr int RS = kRowBytes + (BITS == 8 ? 16 : 8);
+  static constexpr int kStage = 16 * RS + 16 * CH * 4;  // codes + scales, one buffer
 };
+
+// One chunk of a wave's stream held in registers between its loads and its
+// staging: raw code pieces, the (row, block) absmax code and group constant of
+// this lane, and the x fragments of the chunk's blocks.
+template <int BITS, bool XLDS>
+struct Chunk {
+  u32x4_t piece[ChunkGeo<BITS>::NP];
+  uint32_t q8;
+  float sc;
+  u32x4_t x[XLDS ? 1 : CH][2];  // x fragments (unused when x is staged in LDS)
+};
+
+// Largest x (bytes) staged once per workgroup in LDS instead of being read per
+// chunk in the MFMA layout (which repeats every x row 16 times per wave).
+constexpr size_t kXLdsMax = 32 * 1024;
 
 struct Params {
   LinearArgs a;
@@ -61,12 +88,81 @@ __device__ __forceinline__ float coherent_load(const float* p) {
   return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
 }
 
+// Wait until this thread's outstanding vector-memory operations (its stores
+// included) have completed: s_waitcnt vmcnt(0) with expcnt and lgkmcnt left
+// unconstrained (gfx9 encoding).
+__device__ __forceinline__ void wait_vm_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
+
+// LDS byte address in the dynamic block (which starts at LDS address 0: the
+// kernel has no static LDS).
+__device__ __forceinline__ u32x4_t lds_rd128(uint32_t addr) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) u32x4_t*>((uintptr_t)addr);
+}
+__device__ __forceinline__ void lds_wr128(uint32_t addr, u32x4_t v) {
+  *reinterpret_cast<__attribute__((address_space(3))) u32x4_t*>((uintptr_t)addr) = v;
+}
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ uint2 lds_rd64(uint32_t addr) {
+  const u32x2_t v = *reinterpret_cast<const __attribute__((address_space(3))) u32x2_t*>((uintptr_t)addr);
+  return uint2{v.x, v.y};
+}
+__device__ __forceinline__ void lds_wr64(uint32_t addr, uint2 v) {
+  *reinterpret_cast<__attribute__((address_space(3))) u32x2_t*>((uintptr_t)addr) = u32x2_t{v.x, v.y};
+}
+__device__ __forceinline__ uint32_t lds_rd32(uint32_t addr) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) uint32_t*>((uintptr_t)addr);
+}
+__device__ __forceinline__ uint32_t lds_rd16(uint32_t addr) {
+  return *reinterpret_cast<const __attribute__((address_space(3))) uint16_t*>((uintptr_t)addr);
+}
+
+// Raw codes of lane group g (16 codes) of block u of staged row at `row_addr`.
+template <int BITS>
+__device__ __forceinline__ Raw<BITS> raw_from_lds(uint32_t row_addr, int u, int g) {
+  Raw<BITS> r;
+  const uint32_t ad = row_addr + (uint32_t)(u * 8 * BITS + g * 2 * BITS);
+  if constexpr (BITS == 2) {
+    r.v = lds_rd32(ad);
+  } else if constexpr (BITS == 4) {
+    const uint2 v = lds_rd64(ad);
+    r.a = v.x; r.b = v.y;
+  } else if constexpr (BITS == 8) {
+    const u32x4_t v = lds_rd128(ad);
+    r.a = v[0]; r.b = v[1]; r.c = v[2]; r.d = v[3];
+  } else {
+    r.lo = lds_rd16(ad) | (lds_rd16(ad + 2) << 16);
+    r.hi = lds_rd16(ad + 4);
+  }
+  return r;
+}
+
+// The lane-private pair table, built straight from the by-value levels:
+// thread t of wave w writes entry e = w + 8 i (i = 0, 1, ...) of its lane's copy,
+// so the level indices are uniform across the wave and the levels are read
+// with scalar loads (no LDS round trip per entry).
+template <int BITS>
+__device__ __forceinline__ void build_table_kernarg(uint32_t* tbl, const Levels& lv, int tid) {
+  constexpr int NL = 1 << BITS;
+  constexpr int E = PairTable<BITS>::kEntries;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+#pragma unroll 4
+  for (int e = w; e < E; e += kWaves) {
+    uint32_t v;
+    if constexpr (BITS == 8) v = f32_to_bf16_bits(lv.v[e]);
+    else v = pack_bf16x2(lv.v[e & (NL - 1)], lv.v[e >> BITS]);
+    tbl[e * 64 + lane] = v;
+  }
+}
+
 // FUSED: the first P.nparts workgroups also compute the adapter product x A^T
 // over one K-chunk each and publish it; every workgroup waits for all of them
 // before its first epilogue.  The grid never exceeds one workgroup per CU, so
 // all workgroups are resident together and the wait ends; it is also bounded.
 template <int BITS, int YDT, bool XLDS, bool FUSED>
 __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
+  using G = ChunkGeo<BITS>;
+  using Ch = Chunk<BITS, XLDS>;
   extern __shared__ uint32_t smem[];
   const LinearArgs& a = P.a;
   const int64_t N = a.N, K = a.K, nb = K >> 6;
@@ -74,11 +170,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
   const int r = a.r;
   const int mr = M * r;
   uint32_t* tbl = smem;
-  float* sRed = reinterpret_cast<float*>(smem + PairTable<BITS>::kBytes / 4);
-  float* sL = sRed + kWaves * 256;  // codebook levels (256 floats)
-  float* sT = sL + 256;
-  uint16_t* sX = reinterpret_cast<uint16_t*>(sT + (P.tlds ? ((mr + 3) & ~3) : 0));  // 16-byte aligned
-  const int64_t xstride = K + 8;
+  // LDS: level table | per-wave staging (2 buffers) | sRed (waves x 256) | sT | sX
+  const uint32_t stage0 = (uint32_t)PairTable<BITS>::kBytes;
+  float* sRed = reinterpret_cast<float*>(reinterpret_cast<char*>(smem) + stage0 + kWaves * 2 * G::kStage);
+  float* sT = sRed + kWaves * 256;
+  const uint32_t sX = (uint32_t)((reinterpret_cast<char*>(sT) - reinterpret_cast<char*>(smem)) +
+                                 (P.tlds ? ((mr + 3) & ~3) * 4 : 0));  // LDS byte address, 16-byte aligned
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -87,36 +184,79 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
   const int64_t kb0 = nb * wave / kWaves, kb1 = nb * (wave + 1) / kWaves;
   const int nchunk = (int)((kb1 - kb0 + CH - 1) / CH);
   const int nitem = nchunk > 0 ? nchunk : 1;  // items (chunks) per tile for this wave
-  const bool xvalid = nl < M;
-  const uint16_t* xg = reinterpret_cast<const uint16_t*>(a.x) + (int64_t)(xvalid ? nl : 0) * K + 16 * g;
   const u32x4_t zero = {0u, 0u, 0u, 0u};
+  // x row of this lane's A fragments (rows past M are zeroed after the load)
+  const bool xvalid = nl < M;
+  const uint16_t* xg = reinterpret_cast<const uint16_t*>(a.x) + (int64_t)(xvalid ? nl : M - 1) * K + 16 * g;
+  // code bytes as a buffer resource: pieces past the end read as zero
+  const int64_t code_bytes = N * nb * 8 * BITS;
+  const __amdgpu_buffer_rsrc_t cr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint8_t*>(a.codes), (short)0, (int)code_bytes, 0x00020000);
+  const uint32_t wstage = stage0 + (uint32_t)wave * 2 * G::kStage;
+  // scale-loading lane: (row lane / 4, block lane % 4) of a chunk
+  const int srow = lane >> 2, sblk = lane & 3;
 
-  // ---- issue the first chunk's loads before the table build so they overlap it
-  auto load_chunk = [&](int64_t tile, int c, Chunk<BITS>& ch) {
-    const int64_t n = tile * 16 + nl;
-    const int64_t blk_row = (n < N ? n : N - 1) * nb;
+  auto load_chunk = [&](int64_t tile, int c, Ch& ch) {
     const int64_t kbs = kb0 + (int64_t)c * CH;
+    // code pieces: piece p -> row p / PR, byte (p % PR) * PB of the chunk row
 #pragma unroll
-    for (int u = 0; u < CH; ++u) {
-      const int64_t kb = kbs + u;
-      if (kb < kb1) {
-        const int64_t blk = blk_row + kb;
-        ch.raw[u] = load_raw<BITS>(a.codes + blk * (8 * BITS), g);
-        ch.q8[u] = a.q8[blk];
-        ch.sc[u] = a.cst[blk >> 8];
+    for (int i = 0; i < G::NP; ++i) {
+      const int p = i * 64 + lane;
+      const int row = p / G::PR, col = p % G::PR;
+      const int64_t off = ((tile * 16 + row) * nb + kbs) * (8 * BITS) + (int64_t)col * G::PB;
+      const bool in = (p < 16 * G::PR) && (tile * 16 + row < N);
+      const uint32_t o32 = in ? (uint32_t)off : 0xFFFFFFF0u;  // out-of-range offsets read zero
+      if constexpr (G::PB == 16) {
+        ch.piece[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(cr, o32, 0, 0));
+      } else {
+        const u32x2_t w2 = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(cr, o32, 0, 0));
+        ch.piece[i] = u32x4_t{w2.x, w2.y, 0u, 0u};
+      }
+    }
+    // scale of (row srow, block kbs + sblk), clamped into the matrix
+    {
+      const int64_t n = tile * 16 + srow;
+      const int64_t kb = min(kbs + sblk, nb - 1);
+      const int64_t blk = (n < N ? n : N - 1) * nb + kb;
+      ch.q8 = a.q8[blk];
+      ch.sc = a.cst[blk >> 8];
+    }
+    // x fragments of the chunk's blocks (clamped into the row; unused past kb1)
+    if constexpr (!XLDS) {
+#pragma unroll
+      for (int u = 0; u < CH; ++u) {
+        const int64_t kb = min(kbs + u, nb - 1);
+        ch.x[u][0] = *reinterpret_cast<const u32x4_t*>(xg + kb * 64);
+        ch.x[u][1] = *reinterpret_cast<const u32x4_t*>(xg + kb * 64 + 8);
       }
     }
   };
 
+  // Small x: one coalesced copy into LDS per workgroup (rows at stride K + 8),
+  // loaded before the code stream so that waiting for it does not wait for codes.
+  constexpr int kXPer = (int)(kXLdsMax / 16 / kThreads);  // 16-byte pieces per thread (4)
+  u32x4_t xst[kXPer];
+  const int64_t xpieces = (int64_t)M * (K / 8);
+  if constexpr (XLDS) {
+    const uint16_t* x = reinterpret_cast<const uint16_t*>(a.x);
+#pragma unroll
+    for (int i = 0; i < kXPer; ++i) {
+      const int64_t q = tid + (int64_t)i * kThreads;
+      const int64_t qc = q < xpieces ? q : 0;
+      xst[i] = *reinterpret_cast<const u32x4_t*>(x + qc * 8);
+    }
+  }
+
   int64_t tile = blockIdx.x;
   int item = 0;
-  Chunk<BITS> bufA, bufB;
+  Ch bufA, bufB;
   if (tile < P.ntiles) load_chunk(tile, 0, bufA);
 
   // ---- fused adapter product: this workgroup's K-chunk, at most one block per wave
   const bool producer = FUSED && (int)blockIdx.x < P.nparts;
   int64_t tkb = -1;
   u32x4_t af[4][2];
+  u32x4_t tx0 = zero, tx1 = zero;
   if constexpr (FUSED) {
     if (producer) {
       const int64_t c = blockIdx.x;
@@ -124,49 +264,34 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
       if (b0 + wave < b1) {
         tkb = b0 + wave;
         const uint16_t* Ap = reinterpret_cast<const uint16_t*>(a.A);
+        // unconditional loads (rows past r clamped, zeroed at use): no load sits
+        // behind a lane-dependent branch, so no conservative wait follows
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt) {
-          const int j = jt * 16 + nl;
-          if (j < r) {
-            const uint16_t* q = Ap + (int64_t)j * K + tkb * 64 + 16 * g;
-            af[jt][0] = *reinterpret_cast<const u32x4_t*>(q);
-            af[jt][1] = *reinterpret_cast<const u32x4_t*>(q + 8);
-          } else {
-            af[jt][0] = zero;
-            af[jt][1] = zero;
-          }
+          const int j = min(jt * 16 + nl, r - 1);
+          const uint16_t* q = Ap + (int64_t)j * K + tkb * 64 + 16 * g;
+          af[jt][0] = *reinterpret_cast<const u32x4_t*>(q);
+          af[jt][1] = *reinterpret_cast<const u32x4_t*>(q + 8);
         }
+        tx0 = *reinterpret_cast<const u32x4_t*>(xg + tkb * 64);
+        tx1 = *reinterpret_cast<const u32x4_t*>(xg + tkb * 64 + 8);
       }
     }
   }
 
-  stage_levels<1 << BITS>(lv, sL);
-  __syncthreads();
-  build_table<BITS>(tbl, sL, tid, kThreads);
   if constexpr (XLDS) {
-    const uint16_t* x = reinterpret_cast<const uint16_t*>(a.x);
-    const int64_t per_row = K / 8;  // 16-byte pieces per row
-    for (int64_t i = tid; i < (int64_t)M * per_row; i += kThreads) {
-      const int64_t m = i / per_row, q = i % per_row;
-      *reinterpret_cast<uint4*>(sX + m * xstride + q * 8) = *reinterpret_cast<const uint4*>(x + m * K + q * 8);
-    }
-  }
-  __syncthreads();
-
-  auto x_frag = [&](int64_t kb, u32x4_t& x0, u32x4_t& x1) {
-    x0 = zero;
-    x1 = zero;
-    if (xvalid) {
-      if constexpr (XLDS) {
-        const uint16_t* xs = sX + (int64_t)nl * xstride + kb * 64 + 16 * g;
-        x0 = *reinterpret_cast<const u32x4_t*>(xs);
-        x1 = *reinterpret_cast<const u32x4_t*>(xs + 8);
-      } else {
-        x0 = *reinterpret_cast<const u32x4_t*>(xg + kb * 64);
-        x1 = *reinterpret_cast<const u32x4_t*>(xg + kb * 64 + 8);
+#pragma unroll
+    for (int i = 0; i < kXPer; ++i) {
+      const int64_t q = tid + (int64_t)i * kThreads;
+      if (q < xpieces) {
+        const int64_t m = q / (K / 8), c8 = q % (K / 8);
+        *reinterpret_cast<__attribute__((address_space(3))) u32x4_t*>(
+            (uintptr_t)(sX + (uint32_t)((m * (K + 8) + c8 * 8) * 2))) = xst[i];
       }
     }
-  };
+  }
+  build_table_kernarg<BITS>(tbl, lv, tid);
+  __syncthreads();
 
   // ---- fused adapter product: reduce over waves, publish the partial sum
   if constexpr (FUSED) {
@@ -175,12 +300,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
 #pragma unroll
       for (int jt = 0; jt < 4; ++jt) at[jt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       if (tkb >= 0) {
-        u32x4_t x0, x1;
-        x_frag(tkb, x0, x1);
+        const u32x4_t x0 = xvalid ? tx0 : zero, x1 = xvalid ? tx1 : zero;
 #pragma unroll
         for (int jt = 0; jt < 4; ++jt) {
-          at[jt] = mfma16x16x32(as_bf16x8(x0), as_bf16x8(af[jt][0]), at[jt]);
-          at[jt] = mfma16x16x32(as_bf16x8(x1), as_bf16x8(af[jt][1]), at[jt]);
+          const bool jv = jt * 16 + nl < r;
+          at[jt] = mfma16x16x32(as_bf16x8(x0), as_bf16x8(jv ? af[jt][0] : zero), at[jt]);
+          at[jt] = mfma16x16x32(as_bf16x8(x1), as_bf16x8(jv ? af[jt][1] : zero), at[jt]);
         }
       }
       float* dst = P.tpart + (int64_t)blockIdx.x * mr;
@@ -202,10 +327,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
           __syncthreads();
         }
       }
-      // each thread's (agent-scope) stores complete, then one agent-scope release
-      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup");
+      // Publish without an agent-scope release: on this chip such a release
+      // writes back the whole (per-XCD, non-coherent) L2.  The partials are
+      // device-coherent stores, so it is enough that every thread's stores
+      // have completed (vmcnt(0)) before the counter is incremented.
+      wait_vm_stores();
       __syncthreads();
-      if (tid == 0) __hip_atomic_fetch_add(&a.sync->arrive, 1u, __ATOMIC_RELEASE, __HIP_MEMORY_SCOPE_AGENT);
+      if (tid == 0) __hip_atomic_fetch_add(&a.sync->arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
     }
   }
 
@@ -233,21 +361,46 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
 
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](const Chunk<BITS>& ch, int64_t tl, int c) {
-    const bool nvalid = tl * 16 + nl < N;
+  // Stage a chunk's codes and scales in this wave's LDS buffer `buf` (only this
+  // wave reads them, and a wave's LDS instructions run in order), then compute.
+  auto compute = [&](const Ch& ch, int64_t tl, int c, int buf) {
+    const uint32_t sb = wstage + (uint32_t)buf * G::kStage;
+#pragma unroll
+    for (int i = 0; i < G::NP; ++i) {
+      const int p = i * 64 + lane;
+      if (p < 16 * G::PR) {
+        const uint32_t ad = sb + (uint32_t)((p / G::PR) * G::RS + (p % G::PR) * G::PB);
+        if constexpr (G::PB == 16) lds_wr128(ad, ch.piece[i]);
+        else lds_wr64(ad, uint2{ch.piece[i][0], ch.piece[i][1]});
+      }
+    }
+    const uint32_t sscale = sb + 16 * G::RS;
+    {
+      const bool nvalid = tl * 16 + srow < N;
+      const float ap = nvalid ? (float)ch.q8 * ch.sc : 0.0f;
+      *reinterpret_cast<__attribute__((address_space(3))) float*>((uintptr_t)(sscale + (uint32_t)(srow * CH + sblk) * 4)) = ap;
+    }
+    const u32x4_t aps = lds_rd128(sscale + (uint32_t)nl * (CH * 4));
+    const uint32_t rowad = sb + (uint32_t)nl * G::RS;
     const int64_t kbs = kb0 + (int64_t)c * CH;
 #pragma unroll
     for (int u = 0; u < CH; ++u) {
-      const int64_t kb = kbs + u;
-      if (kb < kb1) {
+      if (kbs + u < kb1) {
         u32x4_t x0, x1;
-        x_frag(kb, x0, x1);
+        if constexpr (XLDS) {
+          const uint32_t xa = sX + (uint32_t)((nl * (K + 8) + (kbs + u) * 64 + 16 * g) * 2);
+          x0 = xvalid ? lds_rd128(xa) : zero;
+          x1 = xvalid ? lds_rd128(xa + 16) : zero;
+        } else {
+          x0 = xvalid ? ch.x[u][0] : zero;
+          x1 = xvalid ? ch.x[u][1] : zero;
+        }
         u32x4_t b0, b1;
-        decode16<BITS>(ch.raw[u], tbl, lane4, b0, b1);
+        decode16<BITS>(raw_from_lds<BITS>(rowad, u, g), tbl, lane4, b0, b1);
         f32x4_t d = {0.f, 0.f, 0.f, 0.f};
         d = mfma16x16x32(as_bf16x8(x0), as_bf16x8(b0), d);
         d = mfma16x16x32(as_bf16x8(x1), as_bf16x8(b1), d);
-        const float ap = nvalid ? (float)ch.q8[u] * ch.sc[u] : 0.0f;
+        const float ap = __uint_as_float(aps[u]);
         acc[0] = fmaf(ap, d[0], acc[0]);
         acc[1] = fmaf(ap, d[1], acc[1]);
         acc[2] = fmaf(ap, d[2], acc[2]);
@@ -256,12 +409,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
     }
   };
 
-  // reduce the 16 K slices of a finished tile and write its outputs
+  // reduce the K slices of a finished tile and write its outputs
   auto finish_tile = [&](int64_t tl) {
     if (FUSED && !t_ready) {
       // all adapter partials published? (one lane polls, the workgroup waits on it)
-      // Poll with relaxed loads (an acquire on every poll would invalidate the
-      // cache under the in-flight code stream), then acquire once.
+      // No acquire fence: on this chip an agent-scope acquire invalidates the
+      // L2 under the in-flight code stream.  The partials are read with
+      // device-coherent loads (which bypass the non-coherent L2), issued only
+      // after the count has been observed.
       if (tid == 0) {
         uint32_t it = 0;
         while (__hip_atomic_load(&a.sync->arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
@@ -272,7 +427,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
             break;
           }
         }
-        __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
       }
       __syncthreads();
       stage_t(P.tpart, P.nparts);
@@ -313,12 +467,14 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
   };
 
   // One item: prefetch the stream's next chunk into `fill`, compute `use`.
-  auto step = [&](const Chunk<BITS>& use, Chunk<BITS>& fill) {
+  int buf = 0;
+  auto step = [&](const Ch& use, Ch& fill) {
     const bool last = (item + 1 == nitem);
     const int64_t ntile = last ? tile + gridDim.x : tile;
     const int nitm = last ? 0 : item + 1;
     if (ntile < P.ntiles) load_chunk(ntile, nitm, fill);
-    compute(use, tile, item);
+    if (nchunk > 0) compute(use, tile, item, buf);
+    buf ^= 1;
     if (last) finish_tile(tile);
     tile = ntile;
     item = nitm;
@@ -363,8 +519,13 @@ hipError_t launch_k(const Params& P, int64_t grid, size_t shmem, const Levels& l
   auto kern = k_gemv<BITS, YDT, XLDS, FUSED>;
   static bool attr = false;
   if (!attr) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsMax);
+    // the kernel addresses LDS from 0: it must not have static LDS
+    hipFuncAttributes fa;
+    hipError_t e = hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(kern));
+    if (e != hipSuccess) return e;
+    if (fa.sharedSizeBytes != 0) return hipErrorInvalidKernelFile;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)kLdsMax);
     if (e != hipSuccess) return e;
     attr = true;
   }
@@ -372,21 +533,17 @@ hipError_t launch_k(const Params& P, int64_t grid, size_t shmem, const Levels& l
   return hipGetLastError();
 }
 
-template <int BITS, int YDT, bool FUSED>
-hipError_t launch_x(const Params& P, int64_t grid, size_t with_t, bool xlds, size_t xbytes,
-                    const Levels& lv, hipStream_t s) {
-  if (xlds) return launch_k<BITS, YDT, true, FUSED>(P, grid, with_t + xbytes, lv, s);
-  return launch_k<BITS, YDT, false, FUSED>(P, grid, with_t, lv, s);
-}
-
 template <int BITS, int YDT>
 hipError_t launch_gemv_b(const LinearArgs& a, const Levels& lv, hipStream_t s) {
   Params P;
   P.a = a;
   P.ntiles = (a.N + 15) / 16;
+  // code bytes are addressed with 32-bit buffer offsets
+  if (a.N * (a.K / 64) * 8 * a.bits >= (int64_t(1) << 31)) return hipErrorInvalidValue;
   const int64_t grid = std::min<int64_t>(P.ntiles, device_cus());
   const bool fused = gemv_fuses_adapter(a.M, a.N, a.K, a.r, a.xdt, a.abdt);
-  const size_t base = PairTable<BITS>::kBytes + (size_t)(kWaves + 1) * 256 * sizeof(float);
+  const size_t base = PairTable<BITS>::kBytes + (size_t)kWaves * 2 * ChunkGeo<BITS>::kStage +
+                      (size_t)kWaves * 256 * sizeof(float);
   const size_t tbytes = (((size_t)a.M * (size_t)a.r + 3) & ~(size_t)3) * sizeof(float);
   P.tlds = (a.r > 0 && base + tbytes <= kLdsMax) ? 1 : 0;
   if (fused) {
@@ -397,10 +554,15 @@ hipError_t launch_gemv_b(const LinearArgs& a, const Levels& lv, hipStream_t s) {
     P.tpart = nullptr;
   }
   const size_t with_t = base + (P.tlds ? tbytes : 0);
+  // x staged in LDS (rows at stride K + 8 bf16) when small enough
   const size_t xbytes = (size_t)a.M * (size_t)(a.K + 8) * 2;
-  const bool xlds = with_t + xbytes <= kLdsMax;
-  if (fused) return launch_x<BITS, YDT, true>(P, grid, with_t, xlds, xbytes, lv, s);
-  return launch_x<BITS, YDT, false>(P, grid, with_t, xlds, xbytes, lv, s);
+  const bool xlds = (size_t)a.M * (size_t)a.K * 2 <= kXLdsMax && with_t + xbytes <= kLdsMax;
+  if (fused) {
+    if (xlds) return launch_k<BITS, YDT, true, true>(P, grid, with_t + xbytes, lv, s);
+    return launch_k<BITS, YDT, false, true>(P, grid, with_t, lv, s);
+  }
+  if (xlds) return launch_k<BITS, YDT, true, false>(P, grid, with_t + xbytes, lv, s);
+  return launch_k<BITS, YDT, false, false>(P, grid, with_t, lv, s);
 }
 
 template <int BITS>
