@@ -139,11 +139,10 @@ qlr_status qlr_qweight_sizes(int64_t rows, int64_t cols, int32_t bits, int32_t b
 
 /*
  * Device workspace needed by an operation.  QLR_OP_QUANTIZE: 256 bytes (the
- * non-finite flag); M, N, K, r are ignored.  QLR_OP_LINEAR: 256 bytes of
- * synchronisation words followed by the adapter product t = x A^T for M rows
- * and rank r as float32 partial sums (0 bytes when M or r is 0).  A linear
- * workspace must be zero-filled once before its first use; every call leaves
- * its synchronisation words zero again.  Host only.
+ * non-finite flag); M, N, K, r are ignored.  QLR_OP_LINEAR: the adapter
+ * product t = x A^T for M rows and rank r as float32 partial sums over K
+ * splits, rounded up to 256 bytes (0 bytes when M or r is 0).  Its contents
+ * need no initialisation.  Host only.
  */
 qlr_status qlr_workspace_bytes(qlr_op op, int64_t M, int64_t N, int64_t K, int32_t r,
                                size_t* bytes);
@@ -197,7 +196,7 @@ qlr_status qlr_dequantize(const qlr_qweight* w, void* out, qlr_dtype odt, void* 
  * (nothing is launched).  Each y element is within
  * 1e-3 * sum_k |x[m,k] w'[n,k]| + 1e-5 of the exact result (plus half a bf16
  * ulp when ydt is bf16).  ws (device) >= qlr_workspace_bytes(QLR_OP_LINEAR,
- * M, N, K, r), zero-filled before its first use (see qlr_workspace_bytes).
+ * M, N, K, r) (scratch for x A^T; any contents).
  * Asynchronous, allocation-free, no host synchronisation.
  * Errors: QLR_ERR_NULL, QLR_ERR_SHAPE, QLR_ERR_DTYPE, QLR_ERR_BITS,
  * QLR_ERR_BLOCK, QLR_ERR_ALIGN, QLR_ERR_FORMAT, QLR_ERR_WORKSPACE,

@@ -1,5 +1,8 @@
 // Decode path (M <= 16, bf16 x): the dequantizing GEMV of the frozen base with
-// the unmerged adapter added in the epilogue.
+// the unmerged adapter added in the epilogue (t = x A^T comes from the
+// adapter-product kernel launched just before; measured on this chip, a second
+// launch costs less than handing t between workgroups of one launch, whose
+// cross-XCD round trips sit on the critical path).
 //
 // The frozen base is read once, as packed k-bit codes (QLoRA page,
 // memory-decomposition equation: the 4-bit base takes about half a byte per
@@ -77,21 +80,9 @@ struct Params {
   LinearArgs a;
   int64_t ntiles;
   int tlds;     // summed adapter product staged in LDS (M x r float32)
-  int nparts;   // adapter partial sums: producers (fused) or K splits of the separate kernel
-  float* tpart; // fused: nparts x M x r partials in the workspace (else a.t)
 };
 
-constexpr int kMaxFusedParts = 32;
-constexpr uint32_t kSpinLimit = 1u << 22;
 
-__device__ __forceinline__ float coherent_load(const float* p) {
-  return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-}
-
-// Wait until this thread's outstanding vector-memory operations (its stores
-// included) have completed: s_waitcnt vmcnt(0) with expcnt and lgkmcnt left
-// unconstrained (gfx9 encoding).
-__device__ __forceinline__ void wait_vm_stores() { __builtin_amdgcn_s_waitcnt(0x0F70); }
 
 // LDS byte address in the dynamic block (which starts at LDS address 0: the
 // kernel has no static LDS).
@@ -155,11 +146,7 @@ __device__ __forceinline__ void build_table_kernarg(uint32_t* tbl, const Levels&
   }
 }
 
-// FUSED: the first P.nparts workgroups also compute the adapter product x A^T
-// over one K-chunk each and publish it; every workgroup waits for all of them
-// before its first epilogue.  The grid never exceeds one workgroup per CU, so
-// all workgroups are resident together and the wait ends; it is also bounded.
-template <int BITS, int YDT, bool XLDS, bool FUSED>
+template <int BITS, int YDT, bool XLDS>
 __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
   using G = ChunkGeo<BITS>;
   using Ch = Chunk<BITS, XLDS>;
@@ -252,33 +239,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
   Ch bufA, bufB;
   if (tile < P.ntiles) load_chunk(tile, 0, bufA);
 
-  // ---- fused adapter product: this workgroup's K-chunk, at most one block per wave
-  const bool producer = FUSED && (int)blockIdx.x < P.nparts;
-  int64_t tkb = -1;
-  u32x4_t af[4][2];
-  u32x4_t tx0 = zero, tx1 = zero;
-  if constexpr (FUSED) {
-    if (producer) {
-      const int64_t c = blockIdx.x;
-      const int64_t b0 = nb * c / P.nparts, b1 = nb * (c + 1) / P.nparts;
-      if (b0 + wave < b1) {
-        tkb = b0 + wave;
-        const uint16_t* Ap = reinterpret_cast<const uint16_t*>(a.A);
-        // unconditional loads (rows past r clamped, zeroed at use): no load sits
-        // behind a lane-dependent branch, so no conservative wait follows
-#pragma unroll
-        for (int jt = 0; jt < 4; ++jt) {
-          const int j = min(jt * 16 + nl, r - 1);
-          const uint16_t* q = Ap + (int64_t)j * K + tkb * 64 + 16 * g;
-          af[jt][0] = *reinterpret_cast<const u32x4_t*>(q);
-          af[jt][1] = *reinterpret_cast<const u32x4_t*>(q + 8);
-        }
-        tx0 = *reinterpret_cast<const u32x4_t*>(xg + tkb * 64);
-        tx1 = *reinterpret_cast<const u32x4_t*>(xg + tkb * 64 + 8);
-      }
-    }
-  }
-
   if constexpr (XLDS) {
 #pragma unroll
     for (int i = 0; i < kXPer; ++i) {
@@ -293,56 +253,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
   build_table_kernarg<BITS>(tbl, lv, tid);
   __syncthreads();
 
-  // ---- fused adapter product: reduce over waves, publish the partial sum
-  if constexpr (FUSED) {
-    if (producer) {
-      f32x4_t at[4];
-#pragma unroll
-      for (int jt = 0; jt < 4; ++jt) at[jt] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-      if (tkb >= 0) {
-        const u32x4_t x0 = xvalid ? tx0 : zero, x1 = xvalid ? tx1 : zero;
-#pragma unroll
-        for (int jt = 0; jt < 4; ++jt) {
-          const bool jv = jt * 16 + nl < r;
-          at[jt] = mfma16x16x32(as_bf16x8(x0), as_bf16x8(jv ? af[jt][0] : zero), at[jt]);
-          at[jt] = mfma16x16x32(as_bf16x8(x1), as_bf16x8(jv ? af[jt][1] : zero), at[jt]);
-        }
-      }
-      float* dst = P.tpart + (int64_t)blockIdx.x * mr;
-#pragma unroll
-      for (int jt = 0; jt < 4; ++jt) {
-        if (jt * 16 < r) {
-#pragma unroll
-          for (int v = 0; v < 4; ++v) sRed[wave * 256 + lane * 4 + v] = at[jt][v];
-          __syncthreads();
-          if (tid < 256) {
-            float sum = 0.0f;
-#pragma unroll
-            for (int w = 0; w < kWaves; ++w) sum += sRed[w * 256 + tid];
-            const int l = tid >> 2, v = tid & 3;
-            const int m = 4 * (l >> 4) + v, j = jt * 16 + (l & 15);
-            if (m < M && j < r)
-              __hip_atomic_store(dst + m * r + j, sum, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-          }
-          __syncthreads();
-        }
-      }
-      // Publish without an agent-scope release: on this chip such a release
-      // writes back the whole (per-XCD, non-coherent) L2.  The partials are
-      // device-coherent stores, so it is enough that every thread's stores
-      // have completed (vmcnt(0)) before the counter is incremented.
-      wait_vm_stores();
-      __syncthreads();
-      if (tid == 0) __hip_atomic_fetch_add(&a.sync->arrive, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-    }
-  }
-
   // sT[i] = sum over parts of src[part][i], in part order, staged through sRed
   auto stage_t = [&](const float* src, int nparts) {
     const int per = mr > 0 ? max(1, (kWaves * 256) / mr) : 1;
     for (int p0 = 0; p0 < nparts; p0 += per) {
       const int np = min(per, nparts - p0);
-      for (int idx = tid; idx < np * mr; idx += kThreads) sRed[idx] = coherent_load(src + (int64_t)p0 * mr + idx);
+      for (int idx = tid; idx < np * mr; idx += kThreads) sRed[idx] = src[(int64_t)p0 * mr + idx];
       __syncthreads();
       for (int i = tid; i < mr; i += kThreads) {
         float acc = (p0 == 0) ? 0.0f : sT[i];
@@ -353,11 +269,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
     }
   };
 
-  bool t_ready = !P.tlds || r == 0;
-  if (!FUSED && !t_ready) {
-    stage_t(a.t, P.nparts);
-    t_ready = true;
-  }
+  // t = x A^T (written by the previous kernel) summed into LDS; the code
+  // stream is already in flight, so this round trip overlaps it
+  if (P.tlds && r > 0) stage_t(a.t, a.t_splits);
 
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 
@@ -411,27 +325,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
 
   // reduce the K slices of a finished tile and write its outputs
   auto finish_tile = [&](int64_t tl) {
-    if (FUSED && !t_ready) {
-      // all adapter partials published? (one lane polls, the workgroup waits on it)
-      // No acquire fence: on this chip an agent-scope acquire invalidates the
-      // L2 under the in-flight code stream.  The partials are read with
-      // device-coherent loads (which bypass the non-coherent L2), issued only
-      // after the count has been observed.
-      if (tid == 0) {
-        uint32_t it = 0;
-        while (__hip_atomic_load(&a.sync->arrive, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT) <
-               (uint32_t)P.nparts) {
-          __builtin_amdgcn_s_sleep(2);
-          if (++it == kSpinLimit) {
-            __hip_atomic_store(&a.sync->error, 1u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-            break;
-          }
-        }
-      }
-      __syncthreads();
-      stage_t(P.tpart, P.nparts);
-      t_ready = true;
-    }
 #pragma unroll
     for (int v = 0; v < 4; ++v) sRed[wave * 256 + lane * 4 + v] = acc[v];
     acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
@@ -453,7 +346,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
           } else {
             for (int j = 0; j < r; ++j) {
               float tj = 0.0f;
-              for (int sp = 0; sp < P.nparts; ++sp) tj += a.t[((int64_t)sp * M + m) * r + j];
+              for (int sp = 0; sp < a.t_splits; ++sp) tj += a.t[((int64_t)sp * M + m) * r + j];
               lo = fmaf(tj, bf16_bits_to_f32(br[j]), lo);
             }
           }
@@ -486,17 +379,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
     if (tile >= P.ntiles) break;
     step(bufB, bufA);
   }
-
-  if constexpr (FUSED) {
-    // the last workgroup past its wait resets the words for the next call
-    if (tid == 0) {
-      const uint32_t old = __hip_atomic_fetch_add(&a.sync->done, 1u, __ATOMIC_ACQ_REL, __HIP_MEMORY_SCOPE_AGENT);
-      if (old + 1 == gridDim.x) {
-        __hip_atomic_store(&a.sync->arrive, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-        __hip_atomic_store(&a.sync->done, 0u, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
-      }
-    }
-  }
 }
 
 constexpr size_t kLdsMax = 160 * 1024;
@@ -514,9 +396,9 @@ int device_cus() {
   return cus;
 }
 
-template <int BITS, int YDT, bool XLDS, bool FUSED>
+template <int BITS, int YDT, bool XLDS>
 hipError_t launch_k(const Params& P, int64_t grid, size_t shmem, const Levels& lv, hipStream_t s) {
-  auto kern = k_gemv<BITS, YDT, XLDS, FUSED>;
+  auto kern = k_gemv<BITS, YDT, XLDS>;
   static bool attr = false;
   if (!attr) {
     // the kernel addresses LDS from 0: it must not have static LDS
@@ -541,28 +423,16 @@ hipError_t launch_gemv_b(const LinearArgs& a, const Levels& lv, hipStream_t s) {
   // code bytes are addressed with 32-bit buffer offsets
   if (a.N * (a.K / 64) * 8 * a.bits >= (int64_t(1) << 31)) return hipErrorInvalidValue;
   const int64_t grid = std::min<int64_t>(P.ntiles, device_cus());
-  const bool fused = gemv_fuses_adapter(a.M, a.N, a.K, a.r, a.xdt, a.abdt);
   const size_t base = PairTable<BITS>::kBytes + (size_t)kWaves * 2 * ChunkGeo<BITS>::kStage +
                       (size_t)kWaves * 256 * sizeof(float);
   const size_t tbytes = (((size_t)a.M * (size_t)a.r + 3) & ~(size_t)3) * sizeof(float);
   P.tlds = (a.r > 0 && base + tbytes <= kLdsMax) ? 1 : 0;
-  if (fused) {
-    P.nparts = gemv_adapter_parts(a.N, a.K);
-    P.tpart = reinterpret_cast<float*>(reinterpret_cast<char*>(a.sync) + kSyncBytes);
-  } else {
-    P.nparts = a.t_splits;
-    P.tpart = nullptr;
-  }
   const size_t with_t = base + (P.tlds ? tbytes : 0);
   // x staged in LDS (rows at stride K + 8 bf16) when small enough
   const size_t xbytes = (size_t)a.M * (size_t)(a.K + 8) * 2;
   const bool xlds = (size_t)a.M * (size_t)a.K * 2 <= kXLdsMax && with_t + xbytes <= kLdsMax;
-  if (fused) {
-    if (xlds) return launch_k<BITS, YDT, true, true>(P, grid, with_t + xbytes, lv, s);
-    return launch_k<BITS, YDT, false, true>(P, grid, with_t, lv, s);
-  }
-  if (xlds) return launch_k<BITS, YDT, true, false>(P, grid, with_t + xbytes, lv, s);
-  return launch_k<BITS, YDT, false, false>(P, grid, with_t, lv, s);
+  if (xlds) return launch_k<BITS, YDT, true>(P, grid, with_t + xbytes, lv, s);
+  return launch_k<BITS, YDT, false>(P, grid, with_t, lv, s);
 }
 
 template <int BITS>
@@ -572,19 +442,6 @@ hipError_t launch_gemv_y(const LinearArgs& a, const Levels& lv, hipStream_t s) {
 }
 
 }  // namespace
-
-int gemv_adapter_parts(int64_t N, int64_t K) {
-  const int64_t nb = K / 64;
-  const int64_t grid = std::min<int64_t>((N + 15) / 16, device_cus());
-  return (int)std::min<int64_t>(std::min<int64_t>(kMaxFusedParts, nb), grid);
-}
-
-bool gemv_fuses_adapter(int64_t M, int64_t N, int64_t K, int r, int xdt, int abdt) {
-  if (!(r > 0 && r <= 64 && M * r <= 256 && xdt == DT_BF16 && abdt == DT_BF16)) return false;
-  const int64_t nb = K / 64;
-  const int64_t parts = gemv_adapter_parts(N, K);
-  return parts > 0 && parts * kWaves >= nb;  // at most one block per producer wave
-}
 
 hipError_t launch_gemv(const LinearArgs& a, const Levels& lv, hipStream_t s) {
   switch (a.bits) {

@@ -112,15 +112,13 @@ qlr_status check_qweight(const qlr_qweight* w) {
   return QLR_OK;
 }
 
-// Workspace of one linear call: 256 bytes of synchronisation words, then the
-// adapter product x A^T as float32 partial sums (M x r each): `splits` of them
-// from the separate kernel, or up to 32 from the fused decode kernel.  The
-// count depends only on M and K (the bf16 count bounds the others).
+// Workspace of one linear call: the adapter product x A^T as `splits` float32
+// partial sums (M x r each) from the adapter-product kernel.  The count depends
+// only on M and K (the bf16 count bounds the others).
 size_t linear_ws_bytes(int64_t M, int64_t K, int32_t r) {
   if (M <= 0 || r <= 0) return 0;
-  size_t parts = (size_t)qlr::lora_t_splits(M, K, qlr::DT_BF16, qlr::DT_BF16);
-  if (M * r <= 256) parts = std::max(parts, (size_t)qlr::kMaxAdapterParts);
-  return qlr::kSyncBytes + (((parts * (size_t)M * (size_t)r * sizeof(float)) + 255) & ~(size_t)255);
+  const size_t parts = (size_t)qlr::lora_t_splits(M, K, qlr::DT_BF16, qlr::DT_BF16);
+  return ((parts * (size_t)M * (size_t)r * sizeof(float)) + 255) & ~(size_t)255;
 }
 
 // choose the kernel family for a linear call
@@ -183,11 +181,10 @@ qlr::LinearArgs make_args(const LinearCheck& c, float scale, char* ws, int split
   a.codes = reinterpret_cast<const uint8_t*>(c.w->codes);
   a.q8 = c.w->absmax_q8;
   a.cst = c.w->absmax_c;
-  a.t = ws ? reinterpret_cast<const float*>(ws + qlr::kSyncBytes) : nullptr;
+  a.t = reinterpret_cast<const float*>(ws);
   a.t_splits = splits;
   a.A = c.A;
   a.B = c.B;
-  a.sync = reinterpret_cast<qlr::SyncWords*>(ws);
   a.abdt = (int)c.abdt;
   a.r = c.r;
   a.scale = scale;
@@ -200,11 +197,9 @@ qlr_status run_linear(const LinearCheck& c, float scale, char* ws, qlr_path path
   if (c.M == 0) return QLR_OK;
   hipError_t e = hipSuccess;
   const int splits = qlr::lora_t_splits(c.M, c.w->cols, (int)c.xdt, (int)c.abdt);
-  const bool fused = path == QLR_PATH_GEMV &&
-                     qlr::gemv_fuses_adapter(c.M, c.w->rows, c.w->cols, c.r, (int)c.xdt, (int)c.abdt);
-  if (c.r > 0 && !fused) {
+  if (c.r > 0) {
     e = qlr::launch_lora_t(c.x, (int)c.xdt, c.M, c.w->cols, c.A, (int)c.abdt, c.r,
-                           reinterpret_cast<float*>(ws + qlr::kSyncBytes), splits, s);
+                           reinterpret_cast<float*>(ws), splits, s);
     if (e != hipSuccess) return hip_fail(e, "adapter product launch");
   }
   const qlr::LinearArgs a = make_args(c, scale, ws, splits);

@@ -31,22 +31,6 @@ int lora_t_splits(int64_t M, int64_t K, int xdt, int abdt);
 hipError_t launch_lora_t(const void* x, int xdt, int64_t M, int64_t K, const void* A, int abdt,
                          int r, float* t, int splits, hipStream_t s);
 
-// Device-side synchronisation words at the start of a linear workspace.  They
-// must be zero before the first call; every call leaves them zero again.
-struct SyncWords {
-  uint32_t arrive;  // adapter-partial producers that have published
-  uint32_t done;    // workgroups past their last wait (the last one resets both)
-  uint32_t error;   // nonzero if a bounded wait timed out
-  uint32_t pad[61];
-};
-constexpr size_t kSyncBytes = sizeof(SyncWords);  // 256
-
-// Decode path: does this call compute x A^T inside the GEMV kernel (one launch)?
-bool gemv_fuses_adapter(int64_t M, int64_t N, int64_t K, int r, int xdt, int abdt);
-// Adapter-partial producers of the fused decode path (at most 32).
-int gemv_adapter_parts(int64_t N, int64_t K);
-constexpr int kMaxAdapterParts = 32;
-
 struct LinearArgs {
   const void* x;
   int xdt;
@@ -57,9 +41,8 @@ struct LinearArgs {
   const float* cst;
   const float* t;  // splits x M x r float32 partials of x A^T (NULL if r == 0)
   int t_splits;
-  const void* A;   // r x K (used by the fused decode path)
+  const void* A;   // r x K
   const void* B;   // N x r
-  SyncWords* sync; // workspace synchronisation words
   int abdt;
   int r;
   float scale;

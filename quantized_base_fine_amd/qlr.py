@@ -233,7 +233,7 @@ def linear(x, qw: QWeight, A=None, B=None, scale: float = 0.0, out_dtype=None, o
     y = out if out is not None else torch.empty((M, qw.rows), dtype=out_dtype or x.dtype, device=x.device)
     need = workspace_bytes(OP_LINEAR, M, qw.rows, qw.cols, r)
     if ws is None and need > 0:
-        ws = torch.zeros(need, dtype=torch.uint8, device=x.device)  # zero before first use
+        ws = torch.empty(need, dtype=torch.uint8, device=x.device)
     abdt = _dt(A) if r > 0 else QLR_BF16
     cw = qw.c_struct()
     check(lib().qlr_linear_fwd(x.data_ptr(), _dt(x), M, C.byref(cw), _ptr(A), _ptr(B), abdt, r,
@@ -270,7 +270,7 @@ def linear_mixed(entries: Sequence[dict], out_dtype=None, ws=None):
         arr[i] = CLayer(C.pointer(cws[i]), e["x"].data_ptr(), _ptr(e.get("A")), _ptr(e.get("B")), r,
                         float(e.get("scale", 0.0)), ys[i].data_ptr())
     if ws is None and need > 0:
-        ws = torch.zeros(need, dtype=torch.uint8, device=x0.device)  # zero before first use
+        ws = torch.empty(need, dtype=torch.uint8, device=x0.device)
     check(lib().qlr_linear_fwd_mixed(arr, len(entries), M, _dt(x0), abdt, _dt(ys[0]), _ptr(ws),
                                      0 if ws is None else ws.numel(), _stream(x0.device)))
     return ys

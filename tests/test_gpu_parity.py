@@ -266,22 +266,19 @@ def test_mixed_small():
             check_linear(f32_of(y), lin, oracle_rows_dequant(lin.W, "f16", lin.bits, rows), rows)
 
 
-# ---------------------------------------------------------------- decode synchronisation words
+# ---------------------------------------------------------------- decode repeats and graph replays
 
-def test_decode_fused_adapter_repeats_and_resets_sync_words():
-    """The fused decode kernel publishes adapter partials through counters in the
-    workspace; back-to-back calls on one workspace agree bit for bit and leave
-    the counters zero."""
+def test_decode_repeats_bit_identical():
+    """Back-to-back decode calls on one (uninitialised) workspace agree bit for bit."""
     lin = workloads.mlp("down", 1)
     qw = _gpu_quant(lin.W, "f16", 4)
     x, A, B = dev(lin.x, "bf16"), dev(lin.A, "bf16"), dev(lin.B, "bf16")
-    ws = torch.zeros(qlr.workspace_bytes(qlr.OP_LINEAR, 1, lin.N, lin.K, lin.r), dtype=torch.uint8, device="cuda")
+    ws = torch.full((qlr.workspace_bytes(qlr.OP_LINEAR, 1, lin.N, lin.K, lin.r),), 0xA5, dtype=torch.uint8,
+                    device="cuda")
     ys = [qlr.linear(x, qw, A, B, lin.scale, out_dtype=torch.float32, ws=ws) for _ in range(4)]
     torch.cuda.synchronize()
     for y in ys[1:]:
         assert torch.equal(y, ys[0])
-    words = host(ws)[:12].view(np.uint32)
-    assert words.tolist() == [0, 0, 0], words  # arrive, done, error
     rows = list(range(0, lin.N, 97))
     check_linear(f32_of(ys[0]), lin, oracle_rows_dequant(lin.W, "f16", 4, rows), rows)
 
@@ -306,4 +303,3 @@ def test_decode_graph_replays_match_eager():
         torch.cuda.synchronize()
         assert torch.equal(y, eager), i
         _ = (x.float() * 2).sum().item()  # unrelated eager work between replays
-    assert host(ws)[:12].view(np.uint32).tolist() == [0, 0, 0]
