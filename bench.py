@@ -9,16 +9,26 @@ from the seeded generators in ``workloads``.
 One step is one pass of the whole path over a stack of R distinct copies of
 the layer (R chosen so the packed weights exceed twice the 256 MB last-level
 cache, so the decode figure is HBM bandwidth, not cache bandwidth):
-  quantize   all R weights (codes, 8-bit absmax codes, group steps)
-  dequantize one weight to float32 (export path)
-  decode     y = x W'^T + s (x A^T) B^T at M = 1 for all R layers
-  prefill    the same at M = 2048 for all R layers
-Each phase is timed with HIP events on the stream the kernels run on.
+  quantize      all R weights (codes, 8-bit absmax codes, group steps)
+  dequantize    one weight to float32 (export path)
+  prefill       y = x W'^T + s (x A^T) B^T at M = 2048 for all R layers
+  prefill base  the same without the adapter (one GEMM kernel per call)
+  decode        y = x W'^T + s (x A^T) B^T at M = 1 for all R layers
+  decode base   the same without the adapter (one GEMV kernel per call)
+Each phase is bracketed by HIP events on the stream its calls run on (events
+between the calls of a phase would add a queue barrier per call).  Calls are
+prepared (marshalled once); the prefill phases are GPU-bound and issued eagerly,
+the launch-bound decode phases replay HIP graphs of their R calls (checked
+against the eager outputs first).  A phase is its calls back to back, and its
+time / R is the average launch duration (kernel time plus the dispatch gap
+between back-to-back kernels, about 1.8 us on this GPU).
 
-value       = decode effective GB/s (algorithmic bytes of all decode calls /
-              decode phase time); bytes = codes + absmax codes + group steps
-              + A + B + x + y.
-value_prefill = prefill TFLOP/s with 2MNK + 2Mr(K+N) flops per call.
+value          = decode effective GB/s (algorithmic bytes of all decode calls /
+                 decode phase time); bytes = codes + absmax codes + group steps
+                 + A + B + x + y.
+value_prefill  = prefill TFLOP/s with 2MNK + 2Mr(K+N) flops per call.
+roofline       = the decode GEMV kernel (base calls: one kernel per call).
+roofline_prefill = the prefill GEMM kernel (base calls).
 """
 from __future__ import annotations
 
@@ -124,6 +134,9 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    # One stream of our own carries every call; prepared calls bind to it and the
+    # graphs are captured on it.
+    torch.cuda.set_stream(torch.cuda.Stream(dev))
     cb, qb, kb = qlr.qweight_sizes(N_, K_, BITS)
     R = args.layers or (2 * MALL_BYTES) // (cb + qb + kb) + 1
 
@@ -137,16 +150,22 @@ def main():
     W = to_dev(lin1.W, "f16")
     x1, xp = to_dev(lin1.x, "bf16"), to_dev(linp.x, "bf16")
     A0, B0 = to_dev(lin1.A, "bf16"), to_dev(lin1.B, "bf16")
+    qws = torch.empty(qlr.workspace_bytes(qlr.OP_QUANTIZE), dtype=torch.uint8, device=dev)
+    ws1 = torch.empty(max(qlr.workspace_bytes(qlr.OP_LINEAR, M_DECODE, N_, K_, R_), 16), dtype=torch.uint8, device=dev)
+    wsp = torch.empty(max(qlr.workspace_bytes(qlr.OP_LINEAR, M_PREFILL, N_, K_, R_), 16), dtype=torch.uint8, device=dev)
+    wdeq = torch.empty((N_, K_), dtype=torch.float32, device=dev)
     layers = []
     for _ in range(R):
-        layers.append(dict(qw=qlr.QWeight.empty(N_, K_, BITS, dev), A=A0.clone(), B=B0.clone(),
-                           y1=torch.empty((M_DECODE, N_), dtype=torch.bfloat16, device=dev),
-                           yp=torch.empty((M_PREFILL, N_), dtype=torch.bfloat16, device=dev)))
-    qws = torch.empty(qlr.workspace_bytes(qlr.OP_QUANTIZE), dtype=torch.uint8, device=dev)
-    # linear workspaces are zero-filled once before their first use
-    ws1 = torch.zeros(max(qlr.workspace_bytes(qlr.OP_LINEAR, M_DECODE, N_, K_, R_), 16), dtype=torch.uint8, device=dev)
-    wsp = torch.zeros(max(qlr.workspace_bytes(qlr.OP_LINEAR, M_PREFILL, N_, K_, R_), 16), dtype=torch.uint8, device=dev)
-    wdeq = torch.empty((N_, K_), dtype=torch.float32, device=dev)
+        qw = qlr.QWeight.empty(N_, K_, BITS, dev)
+        A, B = A0.clone(), B0.clone()
+        y1 = torch.empty((M_DECODE, N_), dtype=torch.bfloat16, device=dev)
+        yp = torch.empty((M_PREFILL, N_), dtype=torch.bfloat16, device=dev)
+        layers.append(dict(
+            qw=qw,
+            prefill=qlr.LinearCall(xp, qw, A, B, linp.scale, out=yp, ws=wsp),
+            prefill_base=qlr.LinearCall(xp, qw, out=yp),
+            decode=qlr.LinearCall(x1, qw, A, B, lin1.scale, out=y1, ws=ws1),
+            decode_base=qlr.LinearCall(x1, qw, out=y1)))
     if args.copy_calibration:
         src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -176,7 +195,7 @@ def main():
     quantize_all()
     torch.cuda.synchronize()
     g_quant = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g_quant):
+    with torch.cuda.graph(g_quant, stream=stream):
         quantize_all()
     for _ in range(2):
         layers[-1]["qw"].codes.zero_()
@@ -184,71 +203,75 @@ def main():
         torch.cuda.synchronize()
         assert torch.equal(layers[-1]["qw"].codes, ref_codes), "graph replay differs from eager quantize"
 
-    def run_step(record):
-        """quantize (graph) -> dequantize -> prefill -> decode, phase marks on `stream`.
+    PHASES = ("prefill", "prefill_base", "decode", "decode_base")
 
-        Prefill is GPU-bound and queued before decode, so the host is far ahead
-        of the GPU when the short decode calls run: the per-call events bracket
-        GPU work only, with no host gaps between calls.
-        """
-        marks = [ev() for _ in range(5)]
-        per = {"decode": [], "prefill": []}
+    # The decode phases (short, launch-bound calls) also run as HIP graphs of the
+    # R prepared calls; every replay is checked against the eager outputs first.
+    graphs = {}
+    for ph in ("decode", "decode_base"):
+        for L in layers:
+            L[ph]()
+        torch.cuda.synchronize()
+        ref = [L[ph].y.clone() for L in layers]
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for L in layers:
+                L[ph]()
+        for _ in range(2):
+            for L in layers:
+                L[ph].y.zero_()
+            g.replay()
+            torch.cuda.synchronize()
+            assert all(torch.equal(L[ph].y, r0) for L, r0 in zip(layers, ref)), f"{ph}: graph replay differs"
+        graphs[ph] = g
+
+    def run_step(marks):
+        """quantize (graph) -> dequantize -> the four linear phases, marks on `stream`."""
         marks[0].record(stream)
         g_quant.replay()
         marks[1].record(stream)
         qlr_deq(layers[0]["qw"], wdeq)
         marks[2].record(stream)
-        for L in layers:
-            if record:
-                a, b = ev(), ev()
-                a.record(stream)
-            qlr.linear(xp, L["qw"], L["A"], L["B"], linp.scale, out=L["yp"], ws=wsp)
-            if record:
-                b.record(stream)
-                per["prefill"].append((a, b))
-        marks[3].record(stream)
-        for L in layers:
-            if record:
-                a, b = ev(), ev()
-                a.record(stream)
-            qlr.linear(x1, L["qw"], L["A"], L["B"], lin1.scale, out=L["y1"], ws=ws1)
-            if record:
-                b.record(stream)
-                per["decode"].append((a, b))
-        marks[4].record(stream)
-        return marks, per
+        for i, ph in enumerate(PHASES):
+            if ph in graphs:
+                graphs[ph].replay()
+            else:
+                for L in layers:
+                    L[ph]()
+            marks[3 + i].record(stream)
 
+    nmarks = 3 + len(PHASES)
     for _ in range(args.warmup):
-        run_step(False)
+        run_step([ev() for _ in range(nmarks)])
+    recs = [[ev() for _ in range(nmarks)] for _ in range(args.steps)]  # created before timing
     torch.cuda.synchronize()
     t_wall0 = time.perf_counter()
     start, end = ev(), ev()
     start.record(stream)
-    recs = [run_step(True) for _ in range(args.steps)]
+    for marks in recs:
+        run_step(marks)
     end.record(stream)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_wall0
     total_ms = start.elapsed_time(end)
 
-    phase_ms = {"quantize": 0.0, "dequantize": 0.0, "prefill": 0.0, "decode": 0.0}
-    kern_ms = {"decode": [], "prefill": []}
-    for marks, per in recs:
+    phase_ms = {k: 0.0 for k in ("quantize", "dequantize") + PHASES}
+    for marks in recs:
         phase_ms["quantize"] += marks[0].elapsed_time(marks[1])
         phase_ms["dequantize"] += marks[1].elapsed_time(marks[2])
-        phase_ms["prefill"] += marks[2].elapsed_time(marks[3])
-        phase_ms["decode"] += marks[3].elapsed_time(marks[4])
-        for k, pairs in per.items():
-            kern_ms[k] += [a.elapsed_time(b) for a, b in pairs]
+        for i, ph in enumerate(PHASES):
+            phase_ms[ph] += marks[2 + i].elapsed_time(marks[3 + i])
     S = args.steps
+    mean = {p: 1e3 * phase_ms[p] / (S * R) for p in PHASES}  # average launch duration, us
     dec_gbs = S * R * decode_bytes() / (phase_ms["decode"] / 1e3) / 1e9
     pre_tfs = S * R * prefill_flops() / (phase_ms["prefill"] / 1e3) / 1e12
     q_gbs = S * R * quantize_bytes() / (phase_ms["quantize"] / 1e3) / 1e9
     deq_gbs = S * (N_ * K_ * (4 + BITS / 8) + N_ * K_ / 64) / (phase_ms["dequantize"] / 1e3) / 1e9
-    dec_us = 1e3 * float(np.mean(kern_ms["decode"]))
-    pre_us = 1e3 * float(np.mean(kern_ms["prefill"]))
     q_us = 1e3 * phase_ms["quantize"] / (S * R)
-    dec_ach = decode_bytes() / (dec_us * 1e-6) / 1e9
-    pre_ach = prefill_flops() / (pre_us * 1e-6) / 1e12
+    gemv_bytes = decode_bytes(r=0)
+    gemm_flops = prefill_flops(r=0)
+    gemv_ach = gemv_bytes / (mean["decode_base"] * 1e-6) / 1e9
+    gemm_ach = gemm_flops / (mean["prefill_base"] * 1e-6) / 1e12
 
     out = {
         "metric": METRIC,
@@ -269,20 +292,21 @@ def main():
                    "x_dtype": "bf16", "y_dtype": "bf16", "outliers": "0.1% x20"},
         "value_prefill": round(pre_tfs, 2),
         "unit_prefill": "TFLOP/s",
+        "call_us": {p: round(v, 3) for p, v in mean.items()},
         "phases_ms_per_step": {k: round(v / S, 4) for k, v in phase_ms.items()},
         "quantize_gbs": round(q_gbs, 1),
         "dequantize_gbs": round(deq_gbs, 1),
         "roofline": {
-            "bound": "hbm", "kernel": "decode linear M=1 (adapter product + fused dequant GEMV)",
-            "achieved": round(dec_ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-            "frac": round(dec_ach / HBM_PEAK_GBS, 4), "launch_us": round(dec_us, 3),
-            "bytes_per_launch": decode_bytes(), "traffic": traffic_from_profile("decode"),
+            "bound": "hbm", "kernel": "k_gemv (decode dequant GEMV, M=1, no adapter: one kernel per call)",
+            "achieved": round(gemv_ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(gemv_ach / HBM_PEAK_GBS, 4), "launch_us": round(mean["decode_base"], 3),
+            "bytes_per_launch": gemv_bytes, "traffic": traffic_from_profile("decode"),
         },
         "roofline_prefill": {
-            "bound": "mfma", "kernel": "prefill linear M=2048 (adapter product + fused dequant GEMM)",
-            "achieved": round(pre_ach, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
-            "frac": round(pre_ach / BF16_PEAK_TFLOPS, 4), "launch_us": round(pre_us, 3),
-            "flops_per_launch": prefill_flops(), "traffic": traffic_from_profile("prefill"),
+            "bound": "mfma", "kernel": "k_gemm (prefill dequant GEMM, M=2048, no adapter: one kernel per call)",
+            "achieved": round(gemm_ach, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+            "frac": round(gemm_ach / BF16_PEAK_TFLOPS, 4), "launch_us": round(mean["prefill_base"], 3),
+            "flops_per_launch": gemm_flops, "traffic": traffic_from_profile("prefill"),
         },
         "roofline_quantize": {
             "bound": "hbm", "kernel": "quantize (flag clear + quantize, graph replay, per layer)",

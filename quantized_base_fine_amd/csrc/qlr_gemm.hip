@@ -219,7 +219,9 @@ struct GemmParams {
   int64_t mtiles, ntiles, per_xcd;
 };
 
-template <int BITS, int YDT>
+// ADP: the call has an adapter branch (r > 0).  Calls without one run a separate
+// instantiation (no adapter tail), which also gives it its own kernel name.
+template <int BITS, int YDT, bool ADP>
 __global__ __launch_bounds__(512, 1) void k_gemm(GemmParams P, Levels lv) {
   extern __shared__ uint32_t smem[];
   const LinearArgs& a = P.a;
@@ -451,23 +453,61 @@ __global__ __launch_bounds__(512, 1) void k_gemm(GemmParams P, Levels lv) {
     if (kb + 1 < nb) cstep(1, 2);
 
     // ---- adapter branch: extra K steps [hi(s t) | lo(s t)] x [B | B]
-    if (a.r > 0) {
+    if constexpr (ADP) {
       const int r = a.r;
       const uint16_t* Bl = reinterpret_cast<const uint16_t*>(a.B);
       const int nsteps = (r + 15) / 16;
-      const bool vec = (r % 8) == 0;  // B rows hold whole 16-byte groups
+      // r % 8 == 0: a lane's 8 adapter columns are whole 16-byte groups of a B
+      // row and whole 32-byte groups of a t row, read with unconditional vector
+      // loads (clamped rows, zeroed at use) so that they are all in flight at
+      // once; otherwise element loads.
+      const bool vec = (r % 8) == 0;
+      const u32x4_t zero4 = {0u, 0u, 0u, 0u};
       for (int q = 0; q < nsteps; ++q) {
         const int j0 = 16 * q + 8 * h;  // this lane's 8 adapter columns
+        const bool jv = j0 < r;
+        const int jc = jv ? j0 : 0;
         u32x4_t bf[2];
+        float v8[4][8];
+        if (vec) {
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const int64_t n = n0 + 64 * nh + 32 * c + fr;
-          bf[c] = u32x4_t{0u, 0u, 0u, 0u};
-          if (n < N) {
-            const uint16_t* bp = Bl + n * (int64_t)r;
-            if (vec && j0 + 8 <= r) {
-              bf[c] = *reinterpret_cast<const u32x4_t*>(bp + j0);
-            } else {
+          for (int c = 0; c < 2; ++c) {
+            const int64_t n = n0 + 64 * nh + 32 * c + fr;
+            const u32x4_t raw = *reinterpret_cast<const u32x4_t*>(Bl + (n < N ? n : N - 1) * (int64_t)r + jc);
+            bf[c] = (n < N && jv) ? raw : zero4;
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i)
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v8[i][e] = 0.0f;
+#pragma unroll 2
+          for (int sp = 0; sp < a.t_splits; ++sp) {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+              const int64_t m = m0 + 128 * mh + 32 * i + fr;
+              const float* tq = a.t + ((int64_t)sp * a.M + (m < M ? m : M - 1)) * r + jc;
+              const f32x4_t p0 = *reinterpret_cast<const f32x4_t*>(tq);
+              const f32x4_t p1 = *reinterpret_cast<const f32x4_t*>(tq + 4);
+#pragma unroll
+              for (int e = 0; e < 4; ++e) {
+                v8[i][e] += p0[e];
+                v8[i][4 + e] += p1[e];
+              }
+            }
+          }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const bool ok = (m0 + 128 * mh + 32 * i + fr < M) && jv;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v8[i][e] = ok ? v8[i][e] : 0.0f;
+          }
+        } else {
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            const int64_t n = n0 + 64 * nh + 32 * c + fr;
+            bf[c] = zero4;
+            if (n < N) {
+              const uint16_t* bp = Bl + n * (int64_t)r;
 #pragma unroll
               for (int e2 = 0; e2 < 4; ++e2) {
                 const uint32_t lo = (j0 + 2 * e2 < r) ? bp[j0 + 2 * e2] : 0u;
@@ -476,23 +516,25 @@ __global__ __launch_bounds__(512, 1) void k_gemm(GemmParams P, Levels lv) {
               }
             }
           }
+#pragma unroll
+          for (int i = 0; i < 4; ++i) {
+            const int64_t m = m0 + 128 * mh + 32 * i + fr;
+            const bool mv = m < M;
+#pragma unroll
+            for (int e = 0; e < 8; ++e) v8[i][e] = 0.0f;
+            for (int sp = 0; sp < a.t_splits; ++sp) {
+              const float* tq = a.t + ((int64_t)sp * a.M + (mv ? m : 0)) * r;
+#pragma unroll
+              for (int e = 0; e < 8; ++e) v8[i][e] += (mv && j0 + e < r) ? tq[j0 + e] : 0.0f;
+            }
+          }
         }
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-          const int64_t m = m0 + 128 * mh + 32 * i + fr;
-          const bool mv = m < M;
-          float v8[8];
-#pragma unroll
-          for (int e = 0; e < 8; ++e) v8[e] = 0.0f;
-          for (int sp = 0; sp < a.t_splits; ++sp) {
-            const float* tq = a.t + ((int64_t)sp * a.M + (mv ? m : 0)) * r;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v8[e] += (mv && j0 + e < r) ? tq[j0 + e] : 0.0f;
-          }
           u32x4_t thi, tlo;
 #pragma unroll
           for (int e2 = 0; e2 < 4; ++e2) {
-            const float u0 = a.scale * v8[2 * e2], u1 = a.scale * v8[2 * e2 + 1];
+            const float u0 = a.scale * v8[i][2 * e2], u1 = a.scale * v8[i][2 * e2 + 1];
             const uint32_t hb0 = f32_to_bf16_bits(u0), hb1 = f32_to_bf16_bits(u1);
             thi[e2] = hb0 | (hb1 << 16);
             tlo[e2] = pack_bf16x2(u0 - bf16_bits_to_f32(hb0), u1 - bf16_bits_to_f32(hb1));
@@ -561,10 +603,10 @@ __global__ __launch_bounds__(512, 1) void k_gemm(GemmParams P, Levels lv) {
   }
 }
 
-template <int BITS, int YDT>
+template <int BITS, int YDT, bool ADP>
 hipError_t launch_gemm_t(const LinearArgs& a, const Levels& lv, hipStream_t s) {
   const size_t shmem = gemm_lds_bytes<BITS>();
-  auto kern = k_gemm<BITS, YDT>;
+  auto kern = k_gemm<BITS, YDT, ADP>;
   static bool attr = false;
   if (!attr) {
     // the kernel addresses LDS from 0: it must not have static LDS
@@ -599,8 +641,12 @@ hipError_t launch_gemm_t(const LinearArgs& a, const Levels& lv, hipStream_t s) {
 
 template <int BITS>
 hipError_t launch_gemm_b(const LinearArgs& a, const Levels& lv, hipStream_t s) {
-  if (a.ydt == DT_F32) return launch_gemm_t<BITS, DT_F32>(a, lv, s);
-  return launch_gemm_t<BITS, DT_BF16>(a, lv, s);
+  if (a.r > 0) {
+    if (a.ydt == DT_F32) return launch_gemm_t<BITS, DT_F32, true>(a, lv, s);
+    return launch_gemm_t<BITS, DT_BF16, true>(a, lv, s);
+  }
+  if (a.ydt == DT_F32) return launch_gemm_t<BITS, DT_F32, false>(a, lv, s);
+  return launch_gemm_t<BITS, DT_BF16, false>(a, lv, s);
 }
 
 }  // namespace

@@ -146,7 +146,9 @@ __device__ __forceinline__ void build_table_kernarg(uint32_t* tbl, const Levels&
   }
 }
 
-template <int BITS, int YDT, bool XLDS>
+// ADP: the call has an adapter branch (r > 0); calls without one run a separate
+// instantiation, which also gives it its own kernel name.
+template <int BITS, int YDT, bool XLDS, bool ADP>
 __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
   using G = ChunkGeo<BITS>;
   using Ch = Chunk<BITS, XLDS>;
@@ -271,7 +273,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
 
   // t = x A^T (written by the previous kernel) summed into LDS; the code
   // stream is already in flight, so this round trip overlaps it
-  if (P.tlds && r > 0) stage_t(a.t, a.t_splits);
+  if (ADP && P.tlds) stage_t(a.t, a.t_splits);
 
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
 
@@ -338,7 +340,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
       const int64_t nn = tl * 16 + (l & 15);
       if (m < M && nn < N) {
         float lo = 0.0f;
-        if (r > 0) {
+        if (ADP) {
           const uint16_t* br = reinterpret_cast<const uint16_t*>(a.B) + nn * r;
           if (P.tlds) {
             const float* tr = sT + m * r;
@@ -396,9 +398,9 @@ int device_cus() {
   return cus;
 }
 
-template <int BITS, int YDT, bool XLDS>
+template <int BITS, int YDT, bool XLDS, bool ADP>
 hipError_t launch_k(const Params& P, int64_t grid, size_t shmem, const Levels& lv, hipStream_t s) {
-  auto kern = k_gemv<BITS, YDT, XLDS>;
+  auto kern = k_gemv<BITS, YDT, XLDS, ADP>;
   static bool attr = false;
   if (!attr) {
     // the kernel addresses LDS from 0: it must not have static LDS
@@ -431,8 +433,12 @@ hipError_t launch_gemv_b(const LinearArgs& a, const Levels& lv, hipStream_t s) {
   // x staged in LDS (rows at stride K + 8 bf16) when small enough
   const size_t xbytes = (size_t)a.M * (size_t)(a.K + 8) * 2;
   const bool xlds = (size_t)a.M * (size_t)a.K * 2 <= kXLdsMax && with_t + xbytes <= kLdsMax;
-  if (xlds) return launch_k<BITS, YDT, true>(P, grid, with_t + xbytes, lv, s);
-  return launch_k<BITS, YDT, false>(P, grid, with_t, lv, s);
+  if (a.r > 0) {
+    if (xlds) return launch_k<BITS, YDT, true, true>(P, grid, with_t + xbytes, lv, s);
+    return launch_k<BITS, YDT, false, true>(P, grid, with_t, lv, s);
+  }
+  if (xlds) return launch_k<BITS, YDT, true, false>(P, grid, with_t + xbytes, lv, s);
+  return launch_k<BITS, YDT, false, false>(P, grid, with_t, lv, s);
 }
 
 template <int BITS>

@@ -242,6 +242,40 @@ def linear(x, qw: QWeight, A=None, B=None, scale: float = 0.0, out_dtype=None, o
     return y
 
 
+class LinearCall:
+    """A prepared ``qlr_linear_fwd`` call: the arguments are marshalled once, so a
+    repeated call (a decode loop) costs one foreign call.  The tensors are kept
+    alive by the object; their contents may change between calls, their
+    storage may not."""
+
+    def __init__(self, x, qw: QWeight, A=None, B=None, scale: float = 0.0, out=None, ws=None,
+                 out_dtype=None):
+        torch = _torch()
+        _require_cuda(x, A, B)
+        M = x.shape[0]
+        r = 0 if A is None else A.shape[0]
+        if x.shape[1] != qw.cols:
+            raise ValueError("x columns must equal the weight's cols")
+        if r > 0 and (A.shape != (r, qw.cols) or B.shape != (qw.rows, r) or A.dtype != B.dtype):
+            raise ValueError("A must be (r, K) and B (N, r) with one dtype")
+        self.y = out if out is not None else torch.empty((M, qw.rows), dtype=out_dtype or x.dtype,
+                                                         device=x.device)
+        need = workspace_bytes(OP_LINEAR, M, qw.rows, qw.cols, r)
+        if ws is None and need > 0:
+            ws = torch.empty(need, dtype=torch.uint8, device=x.device)
+        self._keep = (x, qw, A, B, ws)
+        self._cw = qw.c_struct()
+        abdt = _dt(A) if r > 0 else QLR_BF16
+        self._args = (x.data_ptr(), _dt(x), M, C.byref(self._cw), _ptr(A), _ptr(B), abdt, r, float(scale),
+                      self.y.data_ptr(), _dt(self.y), _ptr(ws), 0 if ws is None else ws.numel(),
+                      _stream(x.device))
+        self._fn = lib().qlr_linear_fwd
+
+    def __call__(self):
+        check(self._fn(*self._args))
+        return self.y
+
+
 def linear_mixed(entries: Sequence[dict], out_dtype=None, ws=None):
     """Independent linears with per-entry (bits, rank).  Each entry: dict(x, qw, A, B, scale[, y])."""
     torch = _torch()
