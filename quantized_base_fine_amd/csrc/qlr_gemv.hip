@@ -35,6 +35,7 @@
 // bits of two neighbouring weights (entry e of lane L at byte e*256 + 4L), so
 // 64 lanes never collide on a bank; one table read yields a bf16 pair.
 #include <algorithm>
+#include <type_traits>
 
 #include "qlr_internal.h"
 #include "qlr_lut.h"
@@ -51,6 +52,8 @@ constexpr int CH = 4;  // blocks per chunk and wave
 // are loaded as PB-byte pieces (8 bytes for 3-bit codes, whose 24-byte blocks
 // are only 8-byte aligned) and staged with a row stride RS chosen to keep the
 // MFMA-layout reads within 2-way bank conflicts.
+typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
+
 template <int BITS>
 struct ChunkGeo {
   static constexpr int kRowBytes = CH * 8 * BITS;
@@ -59,30 +62,64 @@ struct ChunkGeo {
   static constexpr int NP = (16 * PR + 63) / 64;     // pieces per lane
   static constexpr int RS = kRowBytes + (BITS == 8 ? 16 : 8);
   static constexpr int kStage = 16 * RS + 16 * CH * 4;  // codes + scales, one buffer
+  typedef typename std::conditional<PB == 16, u32x4_t, u32x2_t>::type Piece;
 };
 
 // One chunk of a wave's stream held in registers between its loads and its
 // staging: raw code pieces, the (row, block) absmax code and group constant of
-// this lane, and the x fragments of the chunk's blocks.
+// this lane, the x fragments of the chunk's blocks (when x is not in LDS) and,
+// for the adapter, one 16-byte piece of the tile's B rows (loaded with the
+// last chunk of a tile only; every other chunk reads it out of range, as zero).
 template <int BITS, bool XLDS>
 struct Chunk {
-  u32x4_t piece[ChunkGeo<BITS>::NP];
+  typename ChunkGeo<BITS>::Piece piece[ChunkGeo<BITS>::NP];
   uint32_t q8;
   float sc;
   u32x4_t x[XLDS ? 1 : CH][2];  // x fragments (unused when x is staged in LDS)
+  u32x4_t bp;
 };
+
+// Chunks a wave keeps in flight (the ring depth D): 4 for long streams, 2 when
+// a wave's whole stream is at most 2 chunks or x rides with the chunks.  Every
+// load instruction costs address-unit time even when it reads out of range,
+// so the ring is no deeper than the stream.
 
 // Largest x (bytes) staged once per workgroup in LDS instead of being read per
 // chunk in the MFMA layout (which repeats every x row 16 times per wave).
 constexpr size_t kXLdsMax = 32 * 1024;
+// Adapter partial sums (float32) prefetched into registers, per thread.
+constexpr int kTPre = 4;
+
+// How the epilogue gets the adapter product t = x A^T (split partial sums).
+enum { T_GLOBAL = 0, T_LOOP = 1, T_PREFETCH = 2 };
 
 struct Params {
   LinearArgs a;
   int64_t ntiles;
-  int tlds;     // summed adapter product staged in LDS (M x r float32)
+  int tmode;     // T_GLOBAL: summed per output from global memory; T_LOOP: summed
+                 // into LDS after the first barrier; T_PREFETCH: partials loaded
+                 // with the first chunks, summed into LDS
+  int bpre;      // B rows of each tile ride with the tile's last chunk into LDS
+  uint32_t sT;   // LDS byte addresses: summed t (M x r), raw partials, B tile, x
+  uint32_t sTP;
+  uint32_t sB;
+  uint32_t sX;
+  uint32_t sZ;   // 128 zero bytes (x fragments of rows past M)
 };
 
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, int64_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p), (short)0, (int)bytes, 0x00020000);
+}
+constexpr uint32_t kOOB = 0xFFFFFFF0u;  // buffer offset past every resource: reads zero, writes dropped
 
+// `ok ? off : kOOB`, with `off` computed unconditionally: the pin keeps the
+// compiler from turning the select into a branch around the access (which
+// would give the accesses of one stream different counts on different paths
+// and force full waits on the memory counter).
+__device__ __forceinline__ uint32_t buf_off(bool ok, uint32_t off) {
+  asm volatile("" : "+v"(off));
+  return ok ? off : kOOB;
+}
 
 // LDS byte address in the dynamic block (which starts at LDS address 0: the
 // kernel has no static LDS).
@@ -92,7 +129,6 @@ __device__ __forceinline__ u32x4_t lds_rd128(uint32_t addr) {
 __device__ __forceinline__ void lds_wr128(uint32_t addr, u32x4_t v) {
   *reinterpret_cast<__attribute__((address_space(3))) u32x4_t*>((uintptr_t)addr) = v;
 }
-typedef uint32_t u32x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ uint2 lds_rd64(uint32_t addr) {
   const u32x2_t v = *reinterpret_cast<const __attribute__((address_space(3))) u32x2_t*>((uintptr_t)addr);
   return uint2{v.x, v.y};
@@ -127,44 +163,113 @@ __device__ __forceinline__ Raw<BITS> raw_from_lds(uint32_t row_addr, int u, int 
   return r;
 }
 
-// The lane-private pair table, built straight from the by-value levels:
-// thread t of wave w writes entry e = w + 8 i (i = 0, 1, ...) of its lane's copy,
-// so the level indices are uniform across the wave and the levels are read
-// with scalar loads (no LDS round trip per entry).
+// The lane-private pair table, built straight from the by-value levels: wave
+// w writes entries [w E/8, (w+1) E/8) of every lane's copy, so an entry's level
+// indices are uniform across the wave; for 3- and 4-bit codes the low level
+// index runs over all levels within a wave and is a compile-time index (one
+// batched scalar load), the high one takes E/8/NL values per wave.
 template <int BITS>
 __device__ __forceinline__ void build_table_kernarg(uint32_t* tbl, const Levels& lv, int tid) {
   constexpr int NL = 1 << BITS;
   constexpr int E = PairTable<BITS>::kEntries;
+  constexpr int EPW = E / kWaves;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-#pragma unroll 4
-  for (int e = w; e < E; e += kWaves) {
-    uint32_t v;
-    if constexpr (BITS == 8) v = f32_to_bf16_bits(lv.v[e]);
-    else v = pack_bf16x2(lv.v[e & (NL - 1)], lv.v[e >> BITS]);
-    tbl[e * 64 + lane] = v;
+  uint32_t* t = tbl + (w * EPW) * 64 + lane;
+  if constexpr (BITS == 8) {
+#pragma unroll
+    for (int i = 0; i < EPW; ++i) t[i * 64] = f32_to_bf16_bits(lv.v[w * EPW + i]);
+  } else if constexpr (EPW >= NL) {
+    float lo[NL];
+#pragma unroll
+    for (int j = 0; j < NL; ++j) lo[j] = lv.v[j];
+#pragma unroll
+    for (int i = 0; i < EPW; ++i) t[i * 64] = pack_bf16x2(lo[i & (NL - 1)], lv.v[w * (EPW / NL) + (i >> BITS)]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < EPW; ++i) {
+      const int e = w * EPW + i;
+      t[i * 64] = pack_bf16x2(lv.v[e & (NL - 1)], lv.v[e >> BITS]);
+    }
   }
+}
+
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
+}
+
+// Single-row products: sum over the 128 / BITS codes of one 16-byte piece of
+// level(code) * x, with the levels looked up as bf16 pairs in the lane-private
+// table (at LDS address 0) and multiplied with the matching x pairs (xv holds
+// the piece's x values in order, 8 per 16-byte vector).  Two accumulation
+// chains, added at the end.
+template <int BITS>
+__device__ __forceinline__ float dot_piece(const u32x4_t& pc, const u32x4_t* xv, uint32_t lane4) {
+  float s0 = 0.0f, s1 = 0.0f;
+  if constexpr (BITS == 4) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        const uint32_t lvp = lds_word(__builtin_amdgcn_perm(pc[w], lane4, 0x0C0C0000u | ((uint32_t)(4 + b) << 8)));
+        if (b & 1) s1 = dot2(lvp, xv[w][b], s1);
+        else s0 = dot2(lvp, xv[w][b], s0);
+      }
+  } else if constexpr (BITS == 2) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+#pragma unroll
+      for (int n = 0; n < 8; ++n) {
+        const uint32_t lvp = lds_word((((pc[w] >> (4 * n)) & 15u) << 8) | lane4);
+        if (n & 1) s1 = dot2(lvp, xv[2 * w + (n >> 2)][n & 3], s1);
+        else s0 = dot2(lvp, xv[2 * w + (n >> 2)][n & 3], s0);
+      }
+  } else {
+#pragma unroll
+    for (int w = 0; w < 4; ++w)
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        const uint32_t lo = lds_word((((pc[w] >> (16 * j)) & 255u) << 8) | lane4);
+        const uint32_t hi = lds_word((((pc[w] >> (16 * j + 8)) & 255u) << 8) | lane4);
+        const uint32_t xp = xv[w >> 1][2 * (w & 1) + j];
+        if (j) s1 = dot2(lo | (hi << 16), xp, s1);
+        else s0 = dot2(lo | (hi << 16), xp, s0);
+      }
+  }
+  return s0 + s1;
 }
 
 // ADP: the call has an adapter branch (r > 0); calls without one run a separate
 // instantiation, which also gives it its own kernel name.
-template <int BITS, int YDT, bool XLDS, bool ADP>
+// DOT (a single x row, 2-, 4- or 8-bit codes): the codes are used straight from
+// the registers they were loaded into, each lane taking 16-byte pieces of
+// rows; level pairs are looked up and multiplied with x pairs by packed bf16
+// dot products, and the row sums are reduced across the lanes of a row and the
+// waves at the end of a tile.  Otherwise the codes are staged through LDS into
+// the 16x16x32 MFMA layout (x rows as the A operand).
+//
+// Every global access of the chunk stream is issued unconditionally (out-of-
+// range pieces read zero through buffer resources), so the compiler's memory
+// counters see the same outstanding loads on every path and a chunk's compute
+// waits for that chunk only, never for the chunks issued after it.
+template <int BITS, int YDT, bool XLDS, bool ADP, int D, bool DOT>
 __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
+  static_assert(!DOT || (XLDS && BITS != 3), "the single-row path reads x from LDS and 16-byte pieces of whole codes");
   using G = ChunkGeo<BITS>;
   using Ch = Chunk<BITS, XLDS>;
+  constexpr int ES = (YDT == DT_F32) ? 4 : 2;
   extern __shared__ uint32_t smem[];
   const LinearArgs& a = P.a;
   const int64_t N = a.N, K = a.K, nb = K >> 6;
   const int M = (int)a.M;
-  const int r = a.r;
+  const int r = ADP ? a.r : 0;
   const int mr = M * r;
   uint32_t* tbl = smem;
-  // LDS: level table | per-wave staging (2 buffers) | sRed (waves x 256) | sT | sX
+  // LDS: level table | per-wave staging (2 buffers) | sRed (waves x 256) | t | t partials | B tile | x
   const uint32_t stage0 = (uint32_t)PairTable<BITS>::kBytes;
   float* sRed = reinterpret_cast<float*>(reinterpret_cast<char*>(smem) + stage0 + kWaves * 2 * G::kStage);
-  float* sT = sRed + kWaves * 256;
-  const uint32_t sX = (uint32_t)((reinterpret_cast<char*>(sT) - reinterpret_cast<char*>(smem)) +
-                                 (P.tlds ? ((mr + 3) & ~3) * 4 : 0));  // LDS byte address, 16-byte aligned
+  float* sT = reinterpret_cast<float*>(reinterpret_cast<char*>(smem) + P.sT);
 
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
@@ -174,41 +279,51 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
   const int nchunk = (int)((kb1 - kb0 + CH - 1) / CH);
   const int nitem = nchunk > 0 ? nchunk : 1;  // items (chunks) per tile for this wave
   const u32x4_t zero = {0u, 0u, 0u, 0u};
-  // x row of this lane's A fragments (rows past M are zeroed after the load)
+  // x row of this lane's A fragments: in LDS, lanes of rows past M read a
+  // 128-byte zero strip at a fixed address; from global memory, they are zeroed
+  // after the load
   const bool xvalid = nl < M;
+  const uint32_t xlane = xvalid ? P.sX + (uint32_t)(nl * (K + 8) * 2 + 32 * g) : P.sZ + 32u * g;
+  const uint32_t xstep = xvalid ? 128u : 0u;
   const uint16_t* xg = reinterpret_cast<const uint16_t*>(a.x) + (int64_t)(xvalid ? nl : M - 1) * K + 16 * g;
-  // code bytes as a buffer resource: pieces past the end read as zero
-  const int64_t code_bytes = N * nb * 8 * BITS;
-  const __amdgpu_buffer_rsrc_t cr = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint8_t*>(a.codes), (short)0, (int)code_bytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t cr = rsrc(a.codes, N * nb * 8 * BITS);
+  const __amdgpu_buffer_rsrc_t qr = rsrc(a.q8, N * nb);
+  const __amdgpu_buffer_rsrc_t sr = rsrc(a.cst, ((N * nb + 255) >> 8) * 4);
   const uint32_t wstage = stage0 + (uint32_t)wave * 2 * G::kStage;
   // scale-loading lane: (row lane / 4, block lane % 4) of a chunk
   const int srow = lane >> 2, sblk = lane & 3;
 
+  // Offsets are formed in 32 bits (every valid one is below 2^31; invalid ones
+  // are replaced by kOOB).
+  const uint32_t nb32 = (uint32_t)nb;
   auto load_chunk = [&](int64_t tile, int c, Ch& ch) {
+    const bool tv = tile < P.ntiles;
     const int64_t kbs = kb0 + (int64_t)c * CH;
+    const uint32_t row0 = (uint32_t)tile * 16u, kbs32 = (uint32_t)kbs;
     // code pieces: piece p -> row p / PR, byte (p % PR) * PB of the chunk row
 #pragma unroll
     for (int i = 0; i < G::NP; ++i) {
       const int p = i * 64 + lane;
       const int row = p / G::PR, col = p % G::PR;
-      const int64_t off = ((tile * 16 + row) * nb + kbs) * (8 * BITS) + (int64_t)col * G::PB;
-      const bool in = (p < 16 * G::PR) && (tile * 16 + row < N);
-      const uint32_t o32 = in ? (uint32_t)off : 0xFFFFFFF0u;  // out-of-range offsets read zero
+      // (the pin keeps the multiply-add in 32 bits: a fused 64-bit form reads
+      // a register pair whose unused high half may be a load in flight)
+      uint32_t blkb = ((row0 + (uint32_t)row) * nb32 + kbs32) * (8u * BITS);
+      asm volatile("" : "+v"(blkb));
+      const uint32_t off = blkb + (uint32_t)(col * G::PB);
+      const uint32_t o32 = buf_off(tv && tile * 16 + row < N, off);
       if constexpr (G::PB == 16) {
         ch.piece[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(cr, o32, 0, 0));
       } else {
-        const u32x2_t w2 = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(cr, o32, 0, 0));
-        ch.piece[i] = u32x4_t{w2.x, w2.y, 0u, 0u};
+        ch.piece[i] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(cr, o32, 0, 0));
       }
     }
-    // scale of (row srow, block kbs + sblk), clamped into the matrix
+    // absmax code and group constant of (row srow, block kbs + sblk)
     {
-      const int64_t n = tile * 16 + srow;
-      const int64_t kb = min(kbs + sblk, nb - 1);
-      const int64_t blk = (n < N ? n : N - 1) * nb + kb;
-      ch.q8 = a.q8[blk];
-      ch.sc = a.cst[blk >> 8];
+      const int64_t n = tile * 16 + srow, kb = kbs + sblk;
+      const uint32_t blk = (row0 + (uint32_t)srow) * nb32 + kbs32 + (uint32_t)sblk;
+      const bool sv = tv && n < N && kb < nb;
+      ch.q8 = __builtin_amdgcn_raw_buffer_load_b8(qr, buf_off(sv, blk), 0, 0);
+      ch.sc = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(sr, buf_off(sv, (blk >> 8) * 4u), 0, 0));
     }
     // x fragments of the chunk's blocks (clamped into the row; unused past kb1)
     if constexpr (!XLDS) {
@@ -219,10 +334,20 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
         ch.x[u][1] = *reinterpret_cast<const u32x4_t*>(xg + kb * 64 + 8);
       }
     }
+    // the tile's B rows (16 x r bf16, contiguous): piece wave * 64 + lane
+    if constexpr (ADP) {
+      const int pc = wave * 64 + lane;
+      const bool bv = P.bpre && tv && c == nitem - 1 && pc < 2 * r;
+      const __amdgpu_buffer_rsrc_t brs = rsrc(a.B, N * r * 2);
+      ch.bp = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                              brs, buf_off(bv, row0 * (uint32_t)(2 * r) + (uint32_t)pc * 16u), 0, 0));
+    }
   };
 
   // Small x: one coalesced copy into LDS per workgroup (rows at stride K + 8),
-  // loaded before the code stream so that waiting for it does not wait for codes.
+  // loaded first, so that waiting for it does not wait for the code stream.
+  // Load i is issued only if some thread has a piece in it (a workgroup-wide
+  // condition).
   constexpr int kXPer = (int)(kXLdsMax / 16 / kThreads);  // 16-byte pieces per thread (4)
   u32x4_t xst[kXPer];
   const int64_t xpieces = (int64_t)M * (K / 8);
@@ -230,29 +355,55 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
     const uint16_t* x = reinterpret_cast<const uint16_t*>(a.x);
 #pragma unroll
     for (int i = 0; i < kXPer; ++i) {
-      const int64_t q = tid + (int64_t)i * kThreads;
-      const int64_t qc = q < xpieces ? q : 0;
-      xst[i] = *reinterpret_cast<const u32x4_t*>(x + qc * 8);
+      if ((int64_t)i * kThreads < xpieces) {
+        const int64_t q = tid + (int64_t)i * kThreads;
+        const int64_t qc = q < xpieces ? q : 0;
+        xst[i] = *reinterpret_cast<const u32x4_t*>(x + qc * 8);
+      }
+    }
+  }
+  // adapter partials, when prefetched: element tid + 512 i of the splits x M x r array
+  float tp[kTPre];
+  const int tcount = (ADP && P.tmode == T_PREFETCH) ? a.t_splits * mr : 0;
+  if constexpr (ADP) {
+    const __amdgpu_buffer_rsrc_t trs = rsrc(a.t, (int64_t)tcount * 4);
+#pragma unroll
+    for (int i = 0; i < kTPre; ++i) {
+      const int q = tid + i * kThreads;
+      tp[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(trs, buf_off(q < tcount, (uint32_t)q * 4u), 0, 0));
     }
   }
 
-  int64_t tile = blockIdx.x;
-  int item = 0;
-  Ch bufA, bufB;
-  if (tile < P.ntiles) load_chunk(tile, 0, bufA);
+  // the first D chunks of this wave's stream (tiles blockIdx.x, + gridDim.x, ...)
+  Ch ring[D];
+  int64_t ltile = blockIdx.x;
+  int lc = 0;
+#pragma unroll
+  for (int s = 0; s < D; ++s) {
+    load_chunk(ltile, lc, ring[s]);
+    if (++lc == nitem) { lc = 0; ltile += gridDim.x; }
+  }
 
+  build_table_kernarg<BITS>(tbl, lv, tid);
   if constexpr (XLDS) {
+    if (tid < 8) lds_wr128(P.sZ + 16u * tid, zero);
 #pragma unroll
     for (int i = 0; i < kXPer; ++i) {
       const int64_t q = tid + (int64_t)i * kThreads;
       if (q < xpieces) {
         const int64_t m = q / (K / 8), c8 = q % (K / 8);
-        *reinterpret_cast<__attribute__((address_space(3))) u32x4_t*>(
-            (uintptr_t)(sX + (uint32_t)((m * (K + 8) + c8 * 8) * 2))) = xst[i];
+        lds_wr128(P.sX + (uint32_t)((m * (K + 8) + c8 * 8) * 2), xst[i]);
       }
     }
   }
-  build_table_kernarg<BITS>(tbl, lv, tid);
+  if constexpr (ADP) {
+    float* sTP = reinterpret_cast<float*>(reinterpret_cast<char*>(smem) + P.sTP);
+#pragma unroll
+    for (int i = 0; i < kTPre; ++i) {
+      const int q = tid + i * kThreads;
+      if (q < tcount) sTP[q] = tp[i];
+    }
+  }
   __syncthreads();
 
   // sT[i] = sum over parts of src[part][i], in part order, staged through sRed
@@ -270,12 +421,54 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
       __syncthreads();
     }
   };
-
-  // t = x A^T (written by the previous kernel) summed into LDS; the code
-  // stream is already in flight, so this round trip overlaps it
-  if (ADP && P.tlds) stage_t(a.t, a.t_splits);
+  if constexpr (ADP) {
+    if (P.tmode == T_PREFETCH) {
+      // summed in part order; read by the epilogue after the first tile's barrier
+      const float* sTP = reinterpret_cast<const float*>(reinterpret_cast<const char*>(smem) + P.sTP);
+      for (int i = tid; i < mr; i += kThreads) {
+        float acc = 0.0f;
+        for (int q = 0; q < a.t_splits; ++q) acc += sTP[q * mr + i];
+        sT[i] = acc;
+      }
+    } else if (P.tmode == T_LOOP) {
+      stage_t(a.t, a.t_splits);
+    }
+  }
 
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  float accd[G::NP];  // single-row path: one row sum per piece
+#pragma unroll
+  for (int i = 0; i < G::NP; ++i) accd[i] = 0.0f;
+  constexpr int CP = 128 / BITS;                   // codes per 16-byte piece
+  constexpr int PPB = (BITS == 3) ? 1 : 64 / CP;   // pieces per block
+
+  // Single-row chunk: lane's pieces i cover rows (64 i + lane) / PR, the same
+  // K range (piece column lane % PR), so one x read serves all of them.
+  auto compute_dot = [&](const Ch& ch, int64_t tl, int c, int buf) {
+    if constexpr (DOT) {
+      const uint32_t sscale = wstage + (uint32_t)buf * G::kStage + 16 * G::RS;
+      {
+        const bool nvalid = tl * 16 + srow < N;
+        const float ap = nvalid ? (float)ch.q8 * ch.sc : 0.0f;
+        *reinterpret_cast<__attribute__((address_space(3))) float*>((uintptr_t)(sscale + (uint32_t)(srow * CH + sblk) * 4)) = ap;
+      }
+      const int64_t kbs = kb0 + (int64_t)c * CH;
+      const int col = lane % G::PR;
+      const int u = col / PPB;
+      const bool bval = kbs + u < kb1;  // blocks past the wave's range are read but not added
+      const uint32_t xa = P.sX + (uint32_t)((kbs * 64 + col * CP) * 2);
+      u32x4_t xv[CP / 8];
+  #pragma unroll
+      for (int q = 0; q < CP / 8; ++q) xv[q] = lds_rd128(xa + 16u * q);
+  #pragma unroll
+      for (int i = 0; i < G::NP; ++i) {
+        const int row = (i * 64 + lane) / G::PR;
+        const float ap = __uint_as_float(lds_rd32(sscale + (uint32_t)(row * CH + u) * 4));
+        const float sp = dot_piece<BITS>(__builtin_bit_cast(u32x4_t, ch.piece[i]), xv, lane4);
+        accd[i] = fmaf(ap, bval ? sp : 0.0f, accd[i]);
+      }
+    }
+  };
 
   // Stage a chunk's codes and scales in this wave's LDS buffer `buf` (only this
   // wave reads them, and a wave's LDS instructions run in order), then compute.
@@ -287,7 +480,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
       if (p < 16 * G::PR) {
         const uint32_t ad = sb + (uint32_t)((p / G::PR) * G::RS + (p % G::PR) * G::PB);
         if constexpr (G::PB == 16) lds_wr128(ad, ch.piece[i]);
-        else lds_wr64(ad, uint2{ch.piece[i][0], ch.piece[i][1]});
+        else lds_wr64(ad, uint2{ch.piece[i].x, ch.piece[i].y});
       }
     }
     const uint32_t sscale = sb + 16 * G::RS;
@@ -299,87 +492,169 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
     const u32x4_t aps = lds_rd128(sscale + (uint32_t)nl * (CH * 4));
     const uint32_t rowad = sb + (uint32_t)nl * G::RS;
     const int64_t kbs = kb0 + (int64_t)c * CH;
-#pragma unroll
-    for (int u = 0; u < CH; ++u) {
-      if (kbs + u < kb1) {
-        u32x4_t x0, x1;
-        if constexpr (XLDS) {
-          const uint32_t xa = sX + (uint32_t)((nl * (K + 8) + (kbs + u) * 64 + 16 * g) * 2);
-          x0 = xvalid ? lds_rd128(xa) : zero;
-          x1 = xvalid ? lds_rd128(xa + 16) : zero;
-        } else {
-          x0 = xvalid ? ch.x[u][0] : zero;
-          x1 = xvalid ? ch.x[u][1] : zero;
-        }
-        u32x4_t b0, b1;
-        decode16<BITS>(raw_from_lds<BITS>(rowad, u, g), tbl, lane4, b0, b1);
-        f32x4_t d = {0.f, 0.f, 0.f, 0.f};
-        d = mfma16x16x32(as_bf16x8(x0), as_bf16x8(b0), d);
-        d = mfma16x16x32(as_bf16x8(x1), as_bf16x8(b1), d);
-        const float ap = __uint_as_float(aps[u]);
-        acc[0] = fmaf(ap, d[0], acc[0]);
-        acc[1] = fmaf(ap, d[1], acc[1]);
-        acc[2] = fmaf(ap, d[2], acc[2]);
-        acc[3] = fmaf(ap, d[3], acc[3]);
+    // block u of the chunk: two 16x16x32 products of the lane's x and level fragments
+    auto block = [&](int u) {
+      u32x4_t x0, x1;
+      if constexpr (XLDS) {
+        const uint32_t xa = xlane + (uint32_t)(kbs + u) * xstep;
+        x0 = lds_rd128(xa);
+        x1 = lds_rd128(xa + 16);
+      } else {
+        x0 = xvalid ? ch.x[u][0] : zero;
+        x1 = xvalid ? ch.x[u][1] : zero;
       }
+      u32x4_t b0, b1;
+      decode16<BITS>(raw_from_lds<BITS>(rowad, u, g), lane4, b0, b1);
+      f32x4_t d = {0.f, 0.f, 0.f, 0.f};
+      d = mfma16x16x32(as_bf16x8(x0), as_bf16x8(b0), d);
+      return mfma16x16x32(as_bf16x8(x1), as_bf16x8(b1), d);
+    };
+    auto accumulate = [&](int u, const f32x4_t& d) {
+      const float ap = __uint_as_float(aps[u]);
+      acc[0] = fmaf(ap, d[0], acc[0]);
+      acc[1] = fmaf(ap, d[1], acc[1]);
+      acc[2] = fmaf(ap, d[2], acc[2]);
+      acc[3] = fmaf(ap, d[3], acc[3]);
+    };
+    if (kbs + CH <= kb1) {
+      // whole chunk in the wave's K range: no branches between the blocks, so
+      // their LDS reads, lookups and products overlap
+      f32x4_t d[CH];
+#pragma unroll
+      for (int u = 0; u < CH; ++u) d[u] = block(u);
+#pragma unroll
+      for (int u = 0; u < CH; ++u) accumulate(u, d[u]);
+    } else {
+#pragma unroll
+      for (int u = 0; u < CH; ++u)
+        if (kbs + u < kb1) accumulate(u, block(u));
     }
   };
 
-  // reduce the K slices of a finished tile and write its outputs
-  auto finish_tile = [&](int64_t tl) {
+  const __amdgpu_buffer_rsrc_t yr = rsrc(a.y, (int64_t)M * N * ES);
+  // Reduce the K slices of a finished tile and write its outputs.  All 512
+  // threads run the epilogue (threads 256.. repeat outputs 0..255 and store out
+  // of range), so the stores are issued on every path.
+  // Output (m, row nn = tile row l15) = s + scale * sum_j t[m][j] B[nn][j], stored
+  // when ov (else out of range).
+  auto epilogue = [&](int m, int l15, int64_t nn, bool ov, float s) {
+    float lo = 0.0f;
+    if constexpr (ADP) {
+      const int mc = m < M ? m : M - 1;
+      const int64_t nc = nn < N ? nn : N - 1;
+      if (P.bpre) {
+        const uint32_t brow = P.sB + (uint32_t)(l15 * r * 2);
+        if (P.tmode != T_GLOBAL && (r & 7) == 0) {
+          // 8 ranks per step from 16-byte LDS reads (t rows and B rows are
+          // 16-byte aligned when r is a multiple of 8), same order of sums
+          const uint32_t trow = P.sT + (uint32_t)(mc * r * 4);
+#pragma unroll 2
+          for (int j = 0; j < r; j += 8) {
+            const u32x4_t t0 = lds_rd128(trow + 4u * j), t1 = lds_rd128(trow + 4u * j + 16u);
+            const u32x4_t bb = lds_rd128(brow + 2u * j);
 #pragma unroll
-    for (int v = 0; v < 4; ++v) sRed[wave * 256 + lane * 4 + v] = acc[v];
-    acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-    __syncthreads();
-    if (tid < 256) {
-      float s = 0.0f;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) s += sRed[w * 256 + tid];
-      const int l = tid >> 2, v = tid & 3;
-      const int m = 4 * (l >> 4) + v;  // MFMA output row (x row)
-      const int64_t nn = tl * 16 + (l & 15);
-      if (m < M && nn < N) {
-        float lo = 0.0f;
-        if (ADP) {
-          const uint16_t* br = reinterpret_cast<const uint16_t*>(a.B) + nn * r;
-          if (P.tlds) {
-            const float* tr = sT + m * r;
-            for (int j = 0; j < r; ++j) lo = fmaf(tr[j], bf16_bits_to_f32(br[j]), lo);
-          } else {
-            for (int j = 0; j < r; ++j) {
-              float tj = 0.0f;
-              for (int sp = 0; sp < a.t_splits; ++sp) tj += a.t[((int64_t)sp * M + m) * r + j];
-              lo = fmaf(tj, bf16_bits_to_f32(br[j]), lo);
+            for (int q = 0; q < 4; ++q) {
+              lo = fmaf(__uint_as_float(q < 2 ? t0[2 * q] : t1[2 * q - 4]), bf16_bits_to_f32(bb[q] & 0xFFFFu), lo);
+              lo = fmaf(__uint_as_float(q < 2 ? t0[2 * q + 1] : t1[2 * q - 3]), bf16_bits_to_f32(bb[q] >> 16), lo);
             }
           }
+        } else if (P.tmode != T_GLOBAL) {
+          const float* tr = sT + mc * r;
+          for (int j = 0; j < r; ++j) lo = fmaf(tr[j], bf16_bits_to_f32(lds_rd16(brow + 2 * j)), lo);
+        } else {
+          for (int j = 0; j < r; ++j) {
+            float tj = 0.0f;
+            for (int sp = 0; sp < a.t_splits; ++sp) tj += a.t[((int64_t)sp * M + mc) * r + j];
+            lo = fmaf(tj, bf16_bits_to_f32(lds_rd16(brow + 2 * j)), lo);
+          }
         }
-        const float out = fmaf(a.scale, lo, s);
-        if constexpr (YDT == DT_F32) reinterpret_cast<float*>(a.y)[(int64_t)m * N + nn] = out;
-        else reinterpret_cast<uint16_t*>(a.y)[(int64_t)m * N + nn] = (uint16_t)f32_to_bf16_bits(out);
+      } else {
+        const uint16_t* br = reinterpret_cast<const uint16_t*>(a.B) + nc * r;
+        if (P.tmode != T_GLOBAL) {
+          const float* tr = sT + mc * r;
+          for (int j = 0; j < r; ++j) lo = fmaf(tr[j], bf16_bits_to_f32(br[j]), lo);
+        } else {
+          for (int j = 0; j < r; ++j) {
+            float tj = 0.0f;
+            for (int sp = 0; sp < a.t_splits; ++sp) tj += a.t[((int64_t)sp * M + mc) * r + j];
+            lo = fmaf(tj, bf16_bits_to_f32(br[j]), lo);
+          }
+        }
       }
+    }
+    const float out = fmaf(a.scale, lo, s);
+    const uint32_t yo = buf_off(ov, (uint32_t)(((int64_t)m * N + nn) * ES));
+    if constexpr (YDT == DT_F32) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(out), yr, yo, 0, 0);
+    else __builtin_amdgcn_raw_buffer_store_b16((uint16_t)f32_to_bf16_bits(out), yr, yo, 0, 0);
+  };
+
+  // Reduce the K slices of a finished tile and write its outputs.  All 512
+  // threads run the epilogue (threads past the outputs repeat one and store
+  // out of range), so the stores are issued on every path.
+  auto finish_tile = [&](int64_t tl) {
+    if constexpr (DOT) {
+#pragma unroll
+      for (int i = 0; i < G::NP; ++i) {
+        float v = accd[i];
+#pragma unroll
+        for (int off = 1; off < G::PR; off <<= 1) v += __shfl_xor(v, off, 64);
+        if (lane % G::PR == 0) sRed[wave * 16 + (i * 64 + lane) / G::PR] = v;
+        accd[i] = 0.0f;
+      }
+      __syncthreads();
+      const int o = tid & 15;
+      float s = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) s += sRed[w * 16 + o];
+      const int64_t nn = tl * 16 + o;
+      epilogue(0, o, nn, tid < 16 && nn < N, s);
+    } else {
+#pragma unroll
+      for (int v = 0; v < 4; ++v) sRed[wave * 256 + lane * 4 + v] = acc[v];
+      acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
+      __syncthreads();
+      const int o = tid & 255;
+      float s = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) s += sRed[w * 256 + o];
+      const int l = o >> 2, v = o & 3;
+      const int m = 4 * (l >> 4) + v;  // MFMA output row (x row)
+      const int64_t nn = tl * 16 + (l & 15);
+      epilogue(m, l & 15, nn, tid < 256 && m < M && nn < N, s);
     }
     __syncthreads();
   };
 
-  // One item: prefetch the stream's next chunk into `fill`, compute `use`.
-  int buf = 0;
-  auto step = [&](const Ch& use, Ch& fill) {
-    const bool last = (item + 1 == nitem);
-    const int64_t ntile = last ? tile + gridDim.x : tile;
-    const int nitm = last ? 0 : item + 1;
-    if (ntile < P.ntiles) load_chunk(ntile, nitm, fill);
-    if (nchunk > 0) compute(use, tile, item, buf);
-    buf ^= 1;
-    if (last) finish_tile(tile);
-    tile = ntile;
-    item = nitm;
-  };
-
-  // ping-pong between two register buffers (no copies of in-flight loads)
-  while (tile < P.ntiles) {
-    step(bufA, bufB);
-    if (tile >= P.ntiles) break;
-    step(bufB, bufA);
+  // The stream: chunk j is item j % nitem of tile blockIdx.x + (j / nitem) gridDim.x;
+  // slot j % D of the ring is computed and then refilled with chunk j + D.
+  const int64_t T = (P.ntiles - blockIdx.x + gridDim.x - 1) / gridDim.x;
+  const int64_t total = T * nitem;
+  int64_t ctile = blockIdx.x;
+  int cc = 0, buf = 0;
+  for (int64_t j0 = 0; j0 < total; j0 += D) {
+#pragma unroll
+    for (int s = 0; s < D; ++s) {
+      if (j0 + s < total) {
+        if (nchunk > 0) {
+          if constexpr (DOT) compute_dot(ring[s], ctile, cc, buf);
+          else compute(ring[s], ctile, cc, buf);
+        }
+        buf ^= 1;
+        if (cc == nitem - 1) {
+          if constexpr (ADP) {
+            const int pc = wave * 64 + lane;
+            if (P.bpre && pc < 2 * r) lds_wr128(P.sB + (uint32_t)pc * 16u, ring[s].bp);
+          }
+          finish_tile(ctile);
+          cc = 0;
+          ctile += gridDim.x;
+        } else {
+          ++cc;
+        }
+      }
+      load_chunk(ltile, lc, ring[s]);
+      if (++lc == nitem) { lc = 0; ltile += gridDim.x; }
+    }
   }
 }
 
@@ -398,9 +673,9 @@ int device_cus() {
   return cus;
 }
 
-template <int BITS, int YDT, bool XLDS, bool ADP>
+template <int BITS, int YDT, bool XLDS, bool ADP, int D, bool DOT = false>
 hipError_t launch_k(const Params& P, int64_t grid, size_t shmem, const Levels& lv, hipStream_t s) {
-  auto kern = k_gemv<BITS, YDT, XLDS, ADP>;
+  auto kern = k_gemv<BITS, YDT, XLDS, ADP, D, DOT>;
   static bool attr = false;
   if (!attr) {
     // the kernel addresses LDS from 0: it must not have static LDS
@@ -422,23 +697,73 @@ hipError_t launch_gemv_b(const LinearArgs& a, const Levels& lv, hipStream_t s) {
   Params P;
   P.a = a;
   P.ntiles = (a.N + 15) / 16;
-  // code bytes are addressed with 32-bit buffer offsets
-  if (a.N * (a.K / 64) * 8 * a.bits >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+  const int64_t r = a.r > 0 ? a.r : 0;
+  const int64_t ES = (YDT == DT_F32) ? 4 : 2;
+  // codes, absmax codes, y and B rows are addressed with 32-bit buffer offsets
+  const int64_t lim = int64_t(1) << 31;
+  if (a.N * (a.K / 64) * 8 * a.bits >= lim || a.M * a.N * ES >= lim || a.N * r * 2 >= lim)
+    return hipErrorInvalidValue;
   const int64_t grid = std::min<int64_t>(P.ntiles, device_cus());
-  const size_t base = PairTable<BITS>::kBytes + (size_t)kWaves * 2 * ChunkGeo<BITS>::kStage +
-                      (size_t)kWaves * 256 * sizeof(float);
-  const size_t tbytes = (((size_t)a.M * (size_t)a.r + 3) & ~(size_t)3) * sizeof(float);
-  P.tlds = (a.r > 0 && base + tbytes <= kLdsMax) ? 1 : 0;
-  const size_t with_t = base + (P.tlds ? tbytes : 0);
-  // x staged in LDS (rows at stride K + 8 bf16) when small enough
-  const size_t xbytes = (size_t)a.M * (size_t)(a.K + 8) * 2;
-  const bool xlds = (size_t)a.M * (size_t)a.K * 2 <= kXLdsMax && with_t + xbytes <= kLdsMax;
-  if (a.r > 0) {
-    if (xlds) return launch_k<BITS, YDT, true, true>(P, grid, with_t + xbytes, lv, s);
-    return launch_k<BITS, YDT, false, true>(P, grid, with_t, lv, s);
+  auto r16 = [](size_t b) { return (b + 15) & ~(size_t)15; };
+  size_t lds = PairTable<BITS>::kBytes + (size_t)kWaves * 2 * ChunkGeo<BITS>::kStage +
+               (size_t)kWaves * 256 * sizeof(float);
+  // adapter product: partials prefetched when they fit the registers, else summed by a loop
+  const size_t mr = (size_t)a.M * (size_t)r;
+  const size_t tparts = (size_t)a.t_splits * mr;
+  P.tmode = T_GLOBAL;
+  P.sT = P.sTP = P.sB = P.sX = 0;
+  P.bpre = 0;
+  if (r > 0) {
+    P.sT = (uint32_t)lds;
+    if (tparts <= (size_t)kTPre * kThreads && lds + r16(mr * 4) + r16(tparts * 4) <= kLdsMax) {
+      P.tmode = T_PREFETCH;
+      lds += r16(mr * 4);
+      P.sTP = (uint32_t)lds;
+      lds += r16(tparts * 4);
+    } else if (lds + r16(mr * 4) <= kLdsMax) {
+      P.tmode = T_LOOP;
+      lds += r16(mr * 4);
+    }
+    // B rows of a tile: 2r 16-byte pieces over the 512 threads, from a 16-byte aligned B
+    if (2 * r <= kThreads && (reinterpret_cast<uintptr_t>(a.B) & 15) == 0 && lds + r16(32 * r) <= kLdsMax) {
+      P.bpre = 1;
+      P.sB = (uint32_t)lds;
+      lds += r16(32 * r);
+    }
   }
-  if (xlds) return launch_k<BITS, YDT, true, false>(P, grid, with_t + xbytes, lv, s);
-  return launch_k<BITS, YDT, false, false>(P, grid, with_t, lv, s);
+  // x staged in LDS (rows at stride K + 8 bf16) when small enough
+  // (+512 bytes: the single-row path reads up to 256 elements past a row's end,
+  // for blocks it does not add)
+  const size_t xbytes = (size_t)a.M * (size_t)(a.K + 8) * 2 + 512;
+  const bool xlds = (size_t)a.M * (size_t)a.K * 2 <= kXLdsMax && lds + 128 + xbytes <= kLdsMax;
+  P.sZ = (uint32_t)lds;
+  lds += 128;
+  P.sX = (uint32_t)lds;
+  // longest chunk stream of a wave: tiles per workgroup x chunks per tile
+  const int64_t nb = a.K / 64;
+  const int64_t stream = ((P.ntiles + grid - 1) / grid) * std::max<int64_t>(1, ((nb + kWaves - 1) / kWaves + CH - 1) / CH);
+  const bool deep = stream > 2;
+  constexpr bool kDot = BITS != 3;
+  if (kDot && a.M == 1 && xlds) {
+    if (r > 0) {
+      if (deep) return launch_k<BITS, YDT, true, true, 4, kDot>(P, grid, lds + xbytes, lv, s);
+      return launch_k<BITS, YDT, true, true, 2, kDot>(P, grid, lds + xbytes, lv, s);
+    }
+    if (deep) return launch_k<BITS, YDT, true, false, 4, kDot>(P, grid, lds + xbytes, lv, s);
+    return launch_k<BITS, YDT, true, false, 2, kDot>(P, grid, lds + xbytes, lv, s);
+  }
+  if (r > 0) {
+    if (xlds) {
+      if (deep) return launch_k<BITS, YDT, true, true, 4>(P, grid, lds + xbytes, lv, s);
+      return launch_k<BITS, YDT, true, true, 2>(P, grid, lds + xbytes, lv, s);
+    }
+    return launch_k<BITS, YDT, false, true, 2>(P, grid, lds, lv, s);
+  }
+  if (xlds) {
+    if (deep) return launch_k<BITS, YDT, true, false, 4>(P, grid, lds + xbytes, lv, s);
+    return launch_k<BITS, YDT, true, false, 2>(P, grid, lds + xbytes, lv, s);
+  }
+  return launch_k<BITS, YDT, false, false, 2>(P, grid, lds, lv, s);
 }
 
 template <int BITS>

@@ -168,10 +168,9 @@ def test_linear_paths_small(bits, path, M, r):
         check_linear(y, lin, wd, rows, ydt)
 
 
-@pytest.mark.parametrize("path", ["gemv", "gemm", "f32"])
-def test_linear_long_k_tail(path):
-    """K = 11008 (172 blocks: DQ groups straddle rows), N = 100, every path."""
-    M = 7 if path != "gemm" else 130
+@pytest.mark.parametrize("path,M", [("gemv", 1), ("gemv", 7), ("gemm", 130), ("f32", 7)])
+def test_linear_long_k_tail(path, M):
+    """K = 11008 (172 blocks: DQ groups straddle rows, waves get partial chunks), N = 100, every path."""
     lin = _small_linear(100, 11008, M, 4, 64, seed=3)
     qw = _gpu_quant(lin.W, "f16", 4)
     rows = list(range(lin.N))
