@@ -90,15 +90,19 @@ constexpr size_t kXLdsMax = 32 * 1024;
 // Adapter partial sums (float32) prefetched into registers, per thread.
 constexpr int kTPre = 4;
 
-// How the epilogue gets the adapter product t = x A^T (split partial sums).
-enum { T_GLOBAL = 0, T_LOOP = 1, T_PREFETCH = 2 };
+// How the epilogue gets the adapter product t = x A^T: from the split partial
+// sums of the adapter-product kernel (T_GLOBAL, T_LOOP, T_PREFETCH), or
+// computed by every workgroup itself (T_FUSED, single row, r <= kFuseR).
+enum { T_GLOBAL = 0, T_LOOP = 1, T_PREFETCH = 2, T_FUSED = 3 };
+constexpr int kFuseR = 16;
 
 struct Params {
   LinearArgs a;
   int64_t ntiles;
   int tmode;     // T_GLOBAL: summed per output from global memory; T_LOOP: summed
                  // into LDS after the first barrier; T_PREFETCH: partials loaded
-                 // with the first chunks, summed into LDS
+                 // with the first chunks, summed into LDS; T_FUSED: x A^T
+                 // computed in the kernel (per-wave sums at sTP)
   int bpre;      // B rows of each tile ride with the tile's last chunk into LDS
   uint32_t sT;   // LDS byte addresses: summed t (M x r), raw partials, B tile, x
   uint32_t sTP;
@@ -253,9 +257,16 @@ __device__ __forceinline__ float dot_piece(const u32x4_t& pc, const u32x4_t* xv,
 // range pieces read zero through buffer resources), so the compiler's memory
 // counters see the same outstanding loads on every path and a chunk's compute
 // waits for that chunk only, never for the chunks issued after it.
-template <int BITS, int YDT, bool XLDS, bool ADP, int D, bool DOT>
+// TF (single-row path, adapter rank <= 16, one 512-element K sweep per wave):
+// every workgroup also computes t = x A^T itself, from A rows read after the
+// code stream has been issued (L2-resident after the first workgroup of each
+// XCD), instead of reading the partial sums of a separate kernel.
+template <int BITS, int YDT, bool XLDS, bool ADP, int D, bool DOT, bool TF>
 __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
   static_assert(!DOT || (XLDS && BITS != 3), "the single-row path reads x from LDS and 16-byte pieces of whole codes");
+  static_assert(!TF || (DOT && ADP), "the fused adapter product belongs to the single-row path");
+  // per-wave LDS staging buffer: codes and scales, or scales only (single-row path)
+  constexpr uint32_t kStageW = DOT ? 16 * CH * 4 : ChunkGeo<BITS>::kStage;
   using G = ChunkGeo<BITS>;
   using Ch = Chunk<BITS, XLDS>;
   constexpr int ES = (YDT == DT_F32) ? 4 : 2;
@@ -268,7 +279,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
   uint32_t* tbl = smem;
   // LDS: level table | per-wave staging (2 buffers) | sRed (waves x 256) | t | t partials | B tile | x
   const uint32_t stage0 = (uint32_t)PairTable<BITS>::kBytes;
-  float* sRed = reinterpret_cast<float*>(reinterpret_cast<char*>(smem) + stage0 + kWaves * 2 * G::kStage);
+  float* sRed = reinterpret_cast<float*>(reinterpret_cast<char*>(smem) + stage0 + kWaves * 2 * kStageW);
   float* sT = reinterpret_cast<float*>(reinterpret_cast<char*>(smem) + P.sT);
 
   const int tid = threadIdx.x;
@@ -289,7 +300,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
   const __amdgpu_buffer_rsrc_t cr = rsrc(a.codes, N * nb * 8 * BITS);
   const __amdgpu_buffer_rsrc_t qr = rsrc(a.q8, N * nb);
   const __amdgpu_buffer_rsrc_t sr = rsrc(a.cst, ((N * nb + 255) >> 8) * 4);
-  const uint32_t wstage = stage0 + (uint32_t)wave * 2 * G::kStage;
+  const uint32_t wstage = stage0 + (uint32_t)wave * 2 * kStageW;
   // scale-loading lane: (row lane / 4, block lane % 4) of a chunk
   const int srow = lane >> 2, sblk = lane & 3;
 
@@ -337,7 +348,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
     // the tile's B rows (16 x r bf16, contiguous): piece wave * 64 + lane
     if constexpr (ADP) {
       const int pc = wave * 64 + lane;
-      const bool bv = P.bpre && tv && c == nitem - 1 && pc < 2 * r;
+      const bool bv = (TF || P.bpre) && tv && c == nitem - 1 && pc < 2 * r;
       const __amdgpu_buffer_rsrc_t brs = rsrc(a.B, N * r * 2);
       ch.bp = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
                                               brs, buf_off(bv, row0 * (uint32_t)(2 * r) + (uint32_t)pc * 16u), 0, 0));
@@ -364,8 +375,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
   }
   // adapter partials, when prefetched: element tid + 512 i of the splits x M x r array
   float tp[kTPre];
-  const int tcount = (ADP && P.tmode == T_PREFETCH) ? a.t_splits * mr : 0;
-  if constexpr (ADP) {
+  const int tcount = (ADP && !TF && P.tmode == T_PREFETCH) ? a.t_splits * mr : 0;
+  if constexpr (ADP && !TF) {
     const __amdgpu_buffer_rsrc_t trs = rsrc(a.t, (int64_t)tcount * 4);
 #pragma unroll
     for (int i = 0; i < kTPre; ++i) {
@@ -384,6 +395,19 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
     if (++lc == nitem) { lc = 0; ltile += gridDim.x; }
   }
 
+  // fused adapter product: lane's 8 elements k0 .. k0 + 7 of every A row j < 16
+  // (rows past r and elements past the wave's range read as zero)
+  u32x4_t afr[TF ? kFuseR : 1];
+  const int64_t tk0 = kb0 * 64 + 8 * lane;
+  const bool tkv = tk0 < kb1 * 64;
+  if constexpr (TF) {
+    const __amdgpu_buffer_rsrc_t ars = rsrc(a.A, (int64_t)r * K * 2);
+#pragma unroll
+    for (int j = 0; j < kFuseR; ++j)
+      afr[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                               ars, buf_off(tkv && j < r, (uint32_t)((j * K + tk0) * 2)), 0, 0));
+  }
+
   build_table_kernarg<BITS>(tbl, lv, tid);
   if constexpr (XLDS) {
     if (tid < 8) lds_wr128(P.sZ + 16u * tid, zero);
@@ -396,7 +420,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
       }
     }
   }
-  if constexpr (ADP) {
+  if constexpr (ADP && !TF) {
     float* sTP = reinterpret_cast<float*>(reinterpret_cast<char*>(smem) + P.sTP);
 #pragma unroll
     for (int i = 0; i < kTPre; ++i) {
@@ -421,7 +445,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
       __syncthreads();
     }
   };
-  if constexpr (ADP) {
+  if constexpr (ADP && !TF) {
     if (P.tmode == T_PREFETCH) {
       // summed in part order; read by the epilogue after the first tile's barrier
       const float* sTP = reinterpret_cast<const float*>(reinterpret_cast<const char*>(smem) + P.sTP);
@@ -446,7 +470,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
   // K range (piece column lane % PR), so one x read serves all of them.
   auto compute_dot = [&](const Ch& ch, int64_t tl, int c, int buf) {
     if constexpr (DOT) {
-      const uint32_t sscale = wstage + (uint32_t)buf * G::kStage + 16 * G::RS;
+      const uint32_t sscale = wstage + (uint32_t)buf * kStageW;
       {
         const bool nvalid = tl * 16 + srow < N;
         const float ap = nvalid ? (float)ch.q8 * ch.sc : 0.0f;
@@ -535,6 +559,37 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
   // Reduce the K slices of a finished tile and write its outputs.  All 512
   // threads run the epilogue (threads 256.. repeat outputs 0..255 and store out
   // of range), so the stores are issued on every path.
+  // Fused adapter product, per wave: t_j over the wave's K range, reduced over
+  // the 64 lanes by halving exchanges (lane l ends with j = l >> 2), written
+  // to the wave's 16 slots at sTP; the waves are summed after the next barrier.
+  auto compute_t = [&]() {
+    if constexpr (TF) {
+      const u32x4_t xv = lds_rd128(P.sX + (uint32_t)(tkv ? tk0 * 2 : 0));
+      float v[kFuseR];
+#pragma unroll
+      for (int j = 0; j < kFuseR; ++j) {
+        float sj = 0.0f;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) sj = dot2(afr[j][q], xv[q], sj);
+        v[j] = tkv ? sj : 0.0f;
+      }
+#pragma unroll
+      for (int h = 32, n = kFuseR; h >= 4; h >>= 1, n >>= 1) {
+        const bool up = (lane & h) != 0;
+#pragma unroll
+        for (int i = 0; i < n / 2; ++i) {
+          const float send = up ? v[i] : v[i + n / 2];
+          const float keep = up ? v[i + n / 2] : v[i];
+          v[i] = keep + __shfl_xor(send, h, 64);
+        }
+      }
+      v[0] += __shfl_xor(v[0], 2, 64);
+      v[0] += __shfl_xor(v[0], 1, 64);
+      if ((lane & 3) == 0)
+        *reinterpret_cast<__attribute__((address_space(3))) float*>((uintptr_t)(P.sTP + 4u * (wave * kFuseR + (lane >> 2)))) = v[0];
+    }
+  };
+
   // Output (m, row nn = tile row l15) = s + scale * sum_j t[m][j] B[nn][j], stored
   // when ov (else out of range).
   auto epilogue = [&](int m, int l15, int64_t nn, bool ov, float s) {
@@ -542,9 +597,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
     if constexpr (ADP) {
       const int mc = m < M ? m : M - 1;
       const int64_t nc = nn < N ? nn : N - 1;
-      if (P.bpre) {
+      // (the fused product always has t and the B tile in LDS)
+      const bool bpre = TF || P.bpre;
+      const bool tlds = TF || P.tmode != T_GLOBAL;
+      if (bpre) {
         const uint32_t brow = P.sB + (uint32_t)(l15 * r * 2);
-        if (P.tmode != T_GLOBAL && (r & 7) == 0) {
+        if (tlds && (r & 7) == 0) {
           // 8 ranks per step from 16-byte LDS reads (t rows and B rows are
           // 16-byte aligned when r is a multiple of 8), same order of sums
           const uint32_t trow = P.sT + (uint32_t)(mc * r * 4);
@@ -558,7 +616,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
               lo = fmaf(__uint_as_float(q < 2 ? t0[2 * q + 1] : t1[2 * q - 3]), bf16_bits_to_f32(bb[q] >> 16), lo);
             }
           }
-        } else if (P.tmode != T_GLOBAL) {
+        } else if (tlds) {
           const float* tr = sT + mc * r;
           for (int j = 0; j < r; ++j) lo = fmaf(tr[j], bf16_bits_to_f32(lds_rd16(brow + 2 * j)), lo);
         } else {
@@ -570,7 +628,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
         }
       } else {
         const uint16_t* br = reinterpret_cast<const uint16_t*>(a.B) + nc * r;
-        if (P.tmode != T_GLOBAL) {
+        if (tlds) {
           const float* tr = sT + mc * r;
           for (int j = 0; j < r; ++j) lo = fmaf(tr[j], bf16_bits_to_f32(br[j]), lo);
         } else {
@@ -602,6 +660,19 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
         accd[i] = 0.0f;
       }
       __syncthreads();
+      if constexpr (TF) {
+        if (tl == blockIdx.x) {
+          // t of the fused product: the waves' sums, in wave order
+          if (tid < r) {
+            float t = 0.0f;
+#pragma unroll
+            for (int w = 0; w < kWaves; ++w)
+              t += *reinterpret_cast<const __attribute__((address_space(3))) float*>((uintptr_t)(P.sTP + 4u * (w * kFuseR + tid)));
+            sT[tid] = t;
+          }
+          __syncthreads();
+        }
+      }
       const int o = tid & 15;
       float s = 0.0f;
 #pragma unroll
@@ -631,29 +702,42 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
   const int64_t total = T * nitem;
   int64_t ctile = blockIdx.x;
   int cc = 0, buf = 0;
-  for (int64_t j0 = 0; j0 < total; j0 += D) {
-#pragma unroll
-    for (int s = 0; s < D; ++s) {
-      if (j0 + s < total) {
-        if (nchunk > 0) {
-          if constexpr (DOT) compute_dot(ring[s], ctile, cc, buf);
-          else compute(ring[s], ctile, cc, buf);
-        }
-        buf ^= 1;
-        if (cc == nitem - 1) {
-          if constexpr (ADP) {
-            const int pc = wave * 64 + lane;
-            if (P.bpre && pc < 2 * r) lds_wr128(P.sB + (uint32_t)pc * 16u, ring[s].bp);
-          }
-          finish_tile(ctile);
-          cc = 0;
-          ctile += gridDim.x;
-        } else {
-          ++cc;
-        }
+  // compute slot s (chunk j = j0 + s) and finish its tile at the tile's last chunk
+  auto consume = [&](int s, int64_t j) {
+    if (j < total) {
+      if (nchunk > 0) {
+        if constexpr (DOT) compute_dot(ring[s], ctile, cc, buf);
+        else compute(ring[s], ctile, cc, buf);
       }
-      load_chunk(ltile, lc, ring[s]);
-      if (++lc == nitem) { lc = 0; ltile += gridDim.x; }
+      buf ^= 1;
+      if (cc == nitem - 1) {
+        if constexpr (ADP) {
+          const int pc = wave * 64 + lane;
+          if ((TF || P.bpre) && pc < 2 * r) lds_wr128(P.sB + (uint32_t)pc * 16u, ring[s].bp);
+        }
+        if constexpr (TF) {
+          if (ctile == blockIdx.x) compute_t();
+        }
+        finish_tile(ctile);
+        cc = 0;
+        ctile += gridDim.x;
+      } else {
+        ++cc;
+      }
+    }
+  };
+  if constexpr (TF) {
+    // the whole stream is in the ring (at most D chunks): straight-line, no refills
+#pragma unroll
+    for (int s = 0; s < D; ++s) consume(s, s);
+  } else {
+    for (int64_t j0 = 0; j0 < total; j0 += D) {
+#pragma unroll
+      for (int s = 0; s < D; ++s) {
+        consume(s, j0 + s);
+        load_chunk(ltile, lc, ring[s]);
+        if (++lc == nitem) { lc = 0; ltile += gridDim.x; }
+      }
     }
   }
 }
@@ -673,9 +757,9 @@ int device_cus() {
   return cus;
 }
 
-template <int BITS, int YDT, bool XLDS, bool ADP, int D, bool DOT = false>
+template <int BITS, int YDT, bool XLDS, bool ADP, int D, bool DOT = false, bool TF = false>
 hipError_t launch_k(const Params& P, int64_t grid, size_t shmem, const Levels& lv, hipStream_t s) {
-  auto kern = k_gemv<BITS, YDT, XLDS, ADP, D, DOT>;
+  auto kern = k_gemv<BITS, YDT, XLDS, ADP, D, DOT, TF>;
   static bool attr = false;
   if (!attr) {
     // the kernel addresses LDS from 0: it must not have static LDS
@@ -692,76 +776,121 @@ hipError_t launch_k(const Params& P, int64_t grid, size_t shmem, const Levels& l
   return hipGetLastError();
 }
 
-template <int BITS, int YDT>
-hipError_t launch_gemv_b(const LinearArgs& a, const Levels& lv, hipStream_t s) {
+// Launch plan of one call: parameters, grid, dynamic LDS and the variant.
+struct Plan {
   Params P;
+  int64_t grid = 0;
+  size_t lds = 0;
+  bool ok = false;    // 32-bit buffer addressing holds
+  bool xlds = false;  // x staged in LDS
+  bool deep = false;  // a wave's chunk stream is longer than 2 (ring depth 4)
+  bool dot = false;   // single-row path
+  bool tf = false;    // fused adapter product
+};
+
+template <int BITS>
+Plan plan_gemv(const LinearArgs& a) {
+  Plan pl;
+  Params& P = pl.P;
   P.a = a;
   P.ntiles = (a.N + 15) / 16;
   const int64_t r = a.r > 0 ? a.r : 0;
-  const int64_t ES = (YDT == DT_F32) ? 4 : 2;
-  // codes, absmax codes, y and B rows are addressed with 32-bit buffer offsets
+  const int64_t ES = (a.ydt == DT_F32) ? 4 : 2;
+  // codes, absmax codes, y, A and B rows are addressed with 32-bit buffer offsets
   const int64_t lim = int64_t(1) << 31;
-  if (a.N * (a.K / 64) * 8 * a.bits >= lim || a.M * a.N * ES >= lim || a.N * r * 2 >= lim)
-    return hipErrorInvalidValue;
-  const int64_t grid = std::min<int64_t>(P.ntiles, device_cus());
-  auto r16 = [](size_t b) { return (b + 15) & ~(size_t)15; };
-  size_t lds = PairTable<BITS>::kBytes + (size_t)kWaves * 2 * ChunkGeo<BITS>::kStage +
-               (size_t)kWaves * 256 * sizeof(float);
-  // adapter product: partials prefetched when they fit the registers, else summed by a loop
-  const size_t mr = (size_t)a.M * (size_t)r;
-  const size_t tparts = (size_t)a.t_splits * mr;
-  P.tmode = T_GLOBAL;
-  P.sT = P.sTP = P.sB = P.sX = 0;
-  P.bpre = 0;
-  if (r > 0) {
-    P.sT = (uint32_t)lds;
-    if (tparts <= (size_t)kTPre * kThreads && lds + r16(mr * 4) + r16(tparts * 4) <= kLdsMax) {
-      P.tmode = T_PREFETCH;
-      lds += r16(mr * 4);
-      P.sTP = (uint32_t)lds;
-      lds += r16(tparts * 4);
-    } else if (lds + r16(mr * 4) <= kLdsMax) {
-      P.tmode = T_LOOP;
-      lds += r16(mr * 4);
-    }
-    // B rows of a tile: 2r 16-byte pieces over the 512 threads, from a 16-byte aligned B
-    if (2 * r <= kThreads && (reinterpret_cast<uintptr_t>(a.B) & 15) == 0 && lds + r16(32 * r) <= kLdsMax) {
-      P.bpre = 1;
-      P.sB = (uint32_t)lds;
-      lds += r16(32 * r);
-    }
-  }
-  // x staged in LDS (rows at stride K + 8 bf16) when small enough
-  // (+512 bytes: the single-row path reads up to 256 elements past a row's end,
-  // for blocks it does not add)
-  const size_t xbytes = (size_t)a.M * (size_t)(a.K + 8) * 2 + 512;
-  const bool xlds = (size_t)a.M * (size_t)a.K * 2 <= kXLdsMax && lds + 128 + xbytes <= kLdsMax;
-  P.sZ = (uint32_t)lds;
-  lds += 128;
-  P.sX = (uint32_t)lds;
+  if (a.N * (a.K / 64) * 8 * a.bits >= lim || a.M * a.N * ES >= lim || a.N * r * 2 >= lim || r * a.K * 2 >= lim)
+    return pl;
+  pl.ok = true;
+  pl.grid = std::min<int64_t>(P.ntiles, device_cus());
   // longest chunk stream of a wave: tiles per workgroup x chunks per tile
   const int64_t nb = a.K / 64;
-  const int64_t stream = ((P.ntiles + grid - 1) / grid) * std::max<int64_t>(1, ((nb + kWaves - 1) / kWaves + CH - 1) / CH);
-  const bool deep = stream > 2;
-  constexpr bool kDot = BITS != 3;
-  if (kDot && a.M == 1 && xlds) {
+  const int64_t stream = ((P.ntiles + pl.grid - 1) / pl.grid) * std::max<int64_t>(1, ((nb + kWaves - 1) / kWaves + CH - 1) / CH);
+  pl.deep = stream > 2;
+  auto r16 = [](size_t b) { return (b + 15) & ~(size_t)15; };
+  for (int attempt = 0; attempt < 2; ++attempt) {
+    const bool dot = attempt == 0 && BITS != 3 && a.M == 1 && (size_t)a.K * 2 <= kXLdsMax;
+    const bool tf = dot && r > 0 && r <= kFuseR && nb <= 8 * kWaves && !pl.deep &&
+                    (reinterpret_cast<uintptr_t>(a.A) & 15) == 0;
+    const size_t stage = dot ? 16 * CH * 4 : ChunkGeo<BITS>::kStage;
+    size_t lds = PairTable<BITS>::kBytes + (size_t)kWaves * 2 * stage + (size_t)kWaves * 256 * sizeof(float);
+    // adapter product: fused, partials prefetched when they fit the registers, else summed by a loop
+    const size_t mr = (size_t)a.M * (size_t)r;
+    const size_t tparts = (size_t)a.t_splits * mr;
+    P.tmode = T_GLOBAL;
+    P.sT = P.sTP = P.sB = P.sX = P.sZ = 0;
+    P.bpre = 0;
     if (r > 0) {
-      if (deep) return launch_k<BITS, YDT, true, true, 4, kDot>(P, grid, lds + xbytes, lv, s);
-      return launch_k<BITS, YDT, true, true, 2, kDot>(P, grid, lds + xbytes, lv, s);
+      P.sT = (uint32_t)lds;
+      if (tf) {
+        P.tmode = T_FUSED;
+        lds += r16(mr * 4);
+        P.sTP = (uint32_t)lds;
+        lds += (size_t)kWaves * kFuseR * 4;
+      } else if (tparts <= (size_t)kTPre * kThreads && lds + r16(mr * 4) + r16(tparts * 4) <= kLdsMax) {
+        P.tmode = T_PREFETCH;
+        lds += r16(mr * 4);
+        P.sTP = (uint32_t)lds;
+        lds += r16(tparts * 4);
+      } else if (lds + r16(mr * 4) <= kLdsMax) {
+        P.tmode = T_LOOP;
+        lds += r16(mr * 4);
+      }
+      // B rows of a tile: 2r 16-byte pieces over the 512 threads, from a 16-byte aligned B
+      if (2 * r <= kThreads && (reinterpret_cast<uintptr_t>(a.B) & 15) == 0 && lds + r16(32 * r) <= kLdsMax) {
+        P.bpre = 1;
+        P.sB = (uint32_t)lds;
+        lds += r16(32 * r);
+      }
     }
-    if (deep) return launch_k<BITS, YDT, true, false, 4, kDot>(P, grid, lds + xbytes, lv, s);
-    return launch_k<BITS, YDT, true, false, 2, kDot>(P, grid, lds + xbytes, lv, s);
+    // x staged in LDS (rows at stride K + 8 bf16) when small enough (+512 bytes:
+    // the single-row path reads up to 256 elements past a row's end, for
+    // blocks it does not add), after a 128-byte zero strip
+    const size_t xbytes = (size_t)a.M * (size_t)(a.K + 8) * 2 + 512;
+    const bool xlds = (size_t)a.M * (size_t)a.K * 2 <= kXLdsMax && lds + 128 + xbytes <= kLdsMax;
+    if (dot && !xlds) continue;  // the single-row path needs x in LDS
+    if (tf && (P.tmode != T_FUSED || !P.bpre)) continue;
+    P.sZ = (uint32_t)lds;
+    lds += 128;
+    P.sX = (uint32_t)lds;
+    pl.xlds = xlds;
+    pl.dot = dot;
+    pl.tf = tf && P.tmode == T_FUSED;
+    pl.lds = lds + (xlds ? xbytes : 0);
+    return pl;
   }
-  if (r > 0) {
-    if (xlds) {
-      if (deep) return launch_k<BITS, YDT, true, true, 4>(P, grid, lds + xbytes, lv, s);
-      return launch_k<BITS, YDT, true, true, 2>(P, grid, lds + xbytes, lv, s);
+  pl.ok = false;
+  return pl;
+}
+
+template <int BITS, int YDT>
+hipError_t launch_gemv_b(const LinearArgs& a, const Levels& lv, hipStream_t s) {
+  const Plan pl = plan_gemv<BITS>(a);
+  if (!pl.ok) return hipErrorInvalidValue;
+  const Params& P = pl.P;
+  const int64_t grid = pl.grid;
+  const size_t lds = pl.lds;
+  const bool adp = a.r > 0;
+  if constexpr (BITS != 3) {
+    if (pl.dot) {
+      if (pl.tf) return launch_k<BITS, YDT, true, true, 2, true, true>(P, grid, lds, lv, s);
+      if (adp) {
+        if (pl.deep) return launch_k<BITS, YDT, true, true, 4, true>(P, grid, lds, lv, s);
+        return launch_k<BITS, YDT, true, true, 2, true>(P, grid, lds, lv, s);
+      }
+      if (pl.deep) return launch_k<BITS, YDT, true, false, 4, true>(P, grid, lds, lv, s);
+      return launch_k<BITS, YDT, true, false, 2, true>(P, grid, lds, lv, s);
+    }
+  }
+  if (adp) {
+    if (pl.xlds) {
+      if (pl.deep) return launch_k<BITS, YDT, true, true, 4>(P, grid, lds, lv, s);
+      return launch_k<BITS, YDT, true, true, 2>(P, grid, lds, lv, s);
     }
     return launch_k<BITS, YDT, false, true, 2>(P, grid, lds, lv, s);
   }
-  if (xlds) {
-    if (deep) return launch_k<BITS, YDT, true, false, 4>(P, grid, lds + xbytes, lv, s);
-    return launch_k<BITS, YDT, true, false, 2>(P, grid, lds + xbytes, lv, s);
+  if (pl.xlds) {
+    if (pl.deep) return launch_k<BITS, YDT, true, false, 4>(P, grid, lds, lv, s);
+    return launch_k<BITS, YDT, true, false, 2>(P, grid, lds, lv, s);
   }
   return launch_k<BITS, YDT, false, false, 2>(P, grid, lds, lv, s);
 }
@@ -773,6 +902,16 @@ hipError_t launch_gemv_y(const LinearArgs& a, const Levels& lv, hipStream_t s) {
 }
 
 }  // namespace
+
+bool gemv_fuses_adapter(const LinearArgs& a) {
+  if (a.r <= 0 || a.M <= 0) return false;
+  switch (a.bits) {
+    case 2: return plan_gemv<2>(a).tf;
+    case 3: return plan_gemv<3>(a).tf;
+    case 4: return plan_gemv<4>(a).tf;
+    default: return plan_gemv<8>(a).tf;
+  }
+}
 
 hipError_t launch_gemv(const LinearArgs& a, const Levels& lv, hipStream_t s) {
   switch (a.bits) {

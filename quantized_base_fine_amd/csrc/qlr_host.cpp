@@ -197,12 +197,12 @@ qlr_status run_linear(const LinearCheck& c, float scale, char* ws, qlr_path path
   if (c.M == 0) return QLR_OK;
   hipError_t e = hipSuccess;
   const int splits = qlr::lora_t_splits(c.M, c.w->cols, (int)c.xdt, (int)c.abdt);
-  if (c.r > 0) {
+  const qlr::LinearArgs a = make_args(c, scale, ws, splits);
+  if (c.r > 0 && !(path == QLR_PATH_GEMV && qlr::gemv_fuses_adapter(a))) {
     e = qlr::launch_lora_t(c.x, (int)c.xdt, c.M, c.w->cols, c.A, (int)c.abdt, c.r,
                            reinterpret_cast<float*>(ws), splits, s);
     if (e != hipSuccess) return hip_fail(e, "adapter product launch");
   }
-  const qlr::LinearArgs a = make_args(c, scale, ws, splits);
   const qlr::Levels lv = levels_arg(c.w->bits);
   switch (path) {
     case QLR_PATH_F32: e = qlr::launch_linear_f32(a, lv, s); break;

@@ -54,6 +54,10 @@ struct LinearArgs {
 hipError_t launch_linear_f32(const LinearArgs& a, const Levels& lv, hipStream_t s);
 // bf16 decode path, M <= 16.
 hipError_t launch_gemv(const LinearArgs& a, const Levels& lv, hipStream_t s);
+// True when launch_gemv computes t = x A^T itself for this call (a single x
+// row and a small rank): the adapter-product kernel is then not launched and
+// a.t is not read.
+bool gemv_fuses_adapter(const LinearArgs& a);
 // bf16 tiled GEMM path.
 hipError_t launch_gemm(const LinearArgs& a, const Levels& lv, hipStream_t s);
 
