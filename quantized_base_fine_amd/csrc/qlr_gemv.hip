@@ -198,6 +198,24 @@ __device__ __forceinline__ void build_table_kernarg(uint32_t* tbl, const Levels&
   }
 }
 
+// Sum over aligned groups of G consecutive lanes (G = 2, 4, 8 or 16), every
+// lane of a group getting the group's sum, by row-local data-parallel moves:
+// neighbour pairs, then quads, then the mirrored half of an 8-lane group, then
+// the mirrored half of the 16-lane row.
+template <int CTRL>
+__device__ __forceinline__ float dpp_mov(float v) {
+  return __uint_as_float(__builtin_amdgcn_update_dpp(0u, __float_as_uint(v), CTRL, 0xF, 0xF, false));
+}
+template <int G>
+__device__ __forceinline__ float group_sum(float v) {
+  static_assert(G == 2 || G == 4 || G == 8 || G == 16, "group of 2, 4, 8 or 16 lanes");
+  v += dpp_mov<0xB1>(v);                      // lane ^ 1
+  if constexpr (G >= 4) v += dpp_mov<0x4E>(v);  // lane ^ 2
+  if constexpr (G >= 8) v += dpp_mov<0x141>(v); // 7 - lane within 8
+  if constexpr (G >= 16) v += dpp_mov<0x140>(v);  // 15 - lane within 16
+  return v;
+}
+
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
@@ -395,19 +413,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
     if (++lc == nitem) { lc = 0; ltile += gridDim.x; }
   }
 
-  // fused adapter product: lane's 8 elements k0 .. k0 + 7 of every A row j < 16
-  // (rows past r and elements past the wave's range read as zero)
-  u32x4_t afr[TF ? kFuseR : 1];
-  const int64_t tk0 = kb0 * 64 + 8 * lane;
-  const bool tkv = tk0 < kb1 * 64;
-  if constexpr (TF) {
-    const __amdgpu_buffer_rsrc_t ars = rsrc(a.A, (int64_t)r * K * 2);
-#pragma unroll
-    for (int j = 0; j < kFuseR; ++j)
-      afr[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                               ars, buf_off(tkv && j < r, (uint32_t)((j * K + tk0) * 2)), 0, 0));
-  }
-
   build_table_kernarg<BITS>(tbl, lv, tid);
   if constexpr (XLDS) {
     if (tid < 8) lds_wr128(P.sZ + 16u * tid, zero);
@@ -427,6 +432,19 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
       const int q = tid + i * kThreads;
       if (q < tcount) sTP[q] = tp[i];
     }
+  }
+  // fused adapter product: lane's 8 elements k0 .. k0 + 7 of every A row j < 16
+  // (rows past r and elements past the wave's range read as zero), issued after
+  // the table and x are in LDS (issuing them holds the wave for a while)
+  u32x4_t afr[TF ? kFuseR : 1];
+  const int64_t tk0 = kb0 * 64 + 8 * lane;
+  const bool tkv = tk0 < kb1 * 64;
+  if constexpr (TF) {
+    const __amdgpu_buffer_rsrc_t ars = rsrc(a.A, (int64_t)r * K * 2);
+#pragma unroll
+    for (int j = 0; j < kFuseR; ++j)
+      afr[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                               ars, buf_off(tkv && j < r, (uint32_t)((j * K + tk0) * 2)), 0, 0));
   }
   __syncthreads();
 
@@ -573,20 +591,26 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
         for (int q = 0; q < 4; ++q) sj = dot2(afr[j][q], xv[q], sj);
         v[j] = tkv ? sj : 0.0f;
       }
+      // exchange distances 32 and 16: swaps of lane halves (lanes without the
+      // distance bit keep value i, the others value i + n/2, each summed with
+      // its partner's)
 #pragma unroll
-      for (int h = 32, n = kFuseR; h >= 4; h >>= 1, n >>= 1) {
-        const bool up = (lane & h) != 0;
-#pragma unroll
-        for (int i = 0; i < n / 2; ++i) {
-          const float send = up ? v[i] : v[i + n / 2];
-          const float keep = up ? v[i + n / 2] : v[i];
-          v[i] = keep + __shfl_xor(send, h, 64);
-        }
+      for (int i = 0; i < 8; ++i) {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[i]), __float_as_uint(v[i + 8]), false, false);
+        v[i] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
       }
-      v[0] += __shfl_xor(v[0], 2, 64);
-      v[0] += __shfl_xor(v[0], 1, 64);
-      if ((lane & 3) == 0)
-        *reinterpret_cast<__attribute__((address_space(3))) float*>((uintptr_t)(P.sTP + 4u * (wave * kFuseR + (lane >> 2)))) = v[0];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[i]), __float_as_uint(v[i + 4]), false, false);
+        v[i] = __uint_as_float(sw[0]) + __uint_as_float(sw[1]);
+      }
+      // lanes of row R (lane / 16) now hold j = 4R .. 4R + 3 summed over 4
+      // lanes; the row sums complete them, and lane 16R writes the four
+#pragma unroll
+      for (int i = 0; i < 4; ++i) v[i] = group_sum<16>(v[i]);
+      if ((lane & 15) == 0)
+        lds_wr128(P.sTP + 4u * (wave * kFuseR + (lane >> 2)),
+                  u32x4_t{__float_as_uint(v[0]), __float_as_uint(v[1]), __float_as_uint(v[2]), __float_as_uint(v[3])});
     }
   };
 
@@ -653,32 +677,38 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
     if constexpr (DOT) {
 #pragma unroll
       for (int i = 0; i < G::NP; ++i) {
-        float v = accd[i];
-#pragma unroll
-        for (int off = 1; off < G::PR; off <<= 1) v += __shfl_xor(v, off, 64);
+        const float v = group_sum<G::PR>(accd[i]);
         if (lane % G::PR == 0) sRed[wave * 16 + (i * 64 + lane) / G::PR] = v;
         accd[i] = 0.0f;
       }
       __syncthreads();
       if constexpr (TF) {
-        if (tl == blockIdx.x) {
-          // t of the fused product: the waves' sums, in wave order
-          if (tid < r) {
-            float t = 0.0f;
+        // thread (o, j) = (tid / 16 % 16, tid % 16): t_j (the waves' sums, in
+        // wave order) times B[row o][j], summed over the 16 j lanes; lane j = 0
+        // adds the row sum and stores output o (threads 256.. repeat, out of range)
+        const int o = (tid >> 4) & 15, j = tid & 15;
+        float tj = 0.0f;
 #pragma unroll
-            for (int w = 0; w < kWaves; ++w)
-              t += *reinterpret_cast<const __attribute__((address_space(3))) float*>((uintptr_t)(P.sTP + 4u * (w * kFuseR + tid)));
-            sT[tid] = t;
-          }
-          __syncthreads();
-        }
+        for (int w = 0; w < kWaves; ++w)
+          tj += *reinterpret_cast<const __attribute__((address_space(3))) float*>((uintptr_t)(P.sTP + 4u * (w * kFuseR + j)));
+        const float bj = j < r ? bf16_bits_to_f32(lds_rd16(P.sB + (uint32_t)((o * r + j) * 2))) : 0.0f;
+        const float lo = group_sum<16>(tj * bj);
+        float s = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) s += sRed[w * 16 + o];
+        const int64_t nn = tl * 16 + o;
+        const float out = fmaf(a.scale, lo, s);
+        const uint32_t yo = buf_off(tid < 256 && j == 0 && nn < N, (uint32_t)(nn * ES));
+        if constexpr (YDT == DT_F32) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(out), yr, yo, 0, 0);
+        else __builtin_amdgcn_raw_buffer_store_b16((uint16_t)f32_to_bf16_bits(out), yr, yo, 0, 0);
+      } else {
+        const int o = tid & 15;
+        float s = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) s += sRed[w * 16 + o];
+        const int64_t nn = tl * 16 + o;
+        epilogue(0, o, nn, tid < 16 && nn < N, s);
       }
-      const int o = tid & 15;
-      float s = 0.0f;
-#pragma unroll
-      for (int w = 0; w < kWaves; ++w) s += sRed[w * 16 + o];
-      const int64_t nn = tl * 16 + o;
-      epilogue(0, o, nn, tid < 16 && nn < N, s);
     } else {
 #pragma unroll
       for (int v = 0; v < 4; ++v) sRed[wave * 256 + lane * 4 + v] = acc[v];
