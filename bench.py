@@ -82,6 +82,66 @@ def traffic_from_profile(kernel_key: str):
     return rec["bytes_per_launch"]
 
 
+# Kernels whose HBM traffic the counter runs measure, with the sources they are
+# built from (the stored figure is dropped when any of them changes).
+_CSRC = "quantized_base_fine_amd/csrc/"
+TRAFFIC_KERNELS = {
+    "decode": ("k_gemv<4, 2, true, false, 2, true, false>",
+               [_CSRC + f for f in ("qlr_gemv.hip", "qlr_lut.h", "qlr_device.h", "qlr_internal.h")]),
+    "prefill": ("k_gemm<4, 2, false>",
+                [_CSRC + f for f in ("qlr_gemm.hip", "qlr_lut.h", "qlr_device.h", "qlr_internal.h")]),
+}
+COPY_BYTES = 256 << 20  # the calibration copy reads and writes this many bytes
+
+
+def traffic_from_counters(fetch_dir: str, write_dir: str):
+    """profiles/traffic.json from two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE in KiB
+    per dispatch) of `bench.py --eager --copy-calibration`: the mean per launch of each
+    kernel, scaled by what the counter reads for the calibration copy of known size."""
+    import csv
+    import glob
+    import hashlib
+
+    def load(d, counter):
+        per = {}
+        for path in glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True):
+            with open(path) as f:
+                for row in csv.DictReader(f):
+                    if row["Counter_Name"] == counter:
+                        per.setdefault(row["Kernel_Name"], []).append(float(row["Counter_Value"]))
+        return per
+
+    fetch, write = load(fetch_dir, "FETCH_SIZE"), load(write_dir, "WRITE_SIZE")
+
+    def copy_kib(per):
+        vals = [v for k, vs in per.items() if "elementwise" in k for v in vs]
+        return max(vals) if vals else None
+
+    cf, cw = copy_kib(fetch), copy_kib(write)
+    if not cf or not cw:
+        raise SystemExit("no calibration copy in the counter runs (run bench.py with --copy-calibration)")
+    scale_f, scale_w = COPY_BYTES / (cf * 1024), COPY_BYTES / (cw * 1024)
+    out = {}
+    for key, (kname, sources) in TRAFFIC_KERNELS.items():
+        fv = [v for k, vs in fetch.items() if kname in k for v in vs]
+        wv = [v for k, vs in write.items() if kname in k for v in vs]
+        if not fv or not wv:
+            continue
+        h = hashlib.sha256()
+        for src in sources:
+            with open(os.path.join(ROOT, src), "rb") as f:
+                h.update(f.read())
+        fk, wk = sum(fv) / len(fv), sum(wv) / len(wv)
+        out[key] = {"kernel": kname, "sources": sources, "sha256": h.hexdigest(),
+                    "launches": len(fv), "fetch_kib": round(fk, 1), "write_kib": round(wk, 1),
+                    "calibration": {"copy_fetch_kib": cf, "copy_write_kib": cw,
+                                    "fetch_scale": round(scale_f, 4), "write_scale": round(scale_w, 4)},
+                    "bytes_per_launch": int(round(fk * 1024 * scale_f + wk * 1024 * scale_w))}
+    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+        json.dump(out, f, indent=1)
+    print(json.dumps(out, indent=1))
+
+
 def cpu_baseline(budget_s: float = 12.0):
     """The oracle (numpy float64) on the host cores, on a bounded sample."""
     import numpy as np
@@ -120,7 +180,14 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one elementwise copy of 256 MiB (counter calibration)")
+    ap.add_argument("--eager", action="store_true",
+                    help="no HIP graphs (every launch visible to per-dispatch counter collection)")
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="no GPU: write profiles/traffic.json from two rocprofv3 --pmc runs")
     args = ap.parse_args()
+    if args.traffic_from:
+        traffic_from_counters(*args.traffic_from)
+        return
     if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
         print("bench.py measures one GPU: this build has no multi-GPU path "
               "(sharding is described in the design notes); run with --gpus 1", file=sys.stderr)
@@ -191,24 +258,26 @@ def main():
 
     # The quantize phase runs as a HIP graph (launch-bound: two short kernels per
     # layer); it is checked against the eager result before timing.
-    ref_codes = layers[-1]["qw"].codes.clone()
-    quantize_all()
-    torch.cuda.synchronize()
-    g_quant = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g_quant, stream=stream):
+    g_quant = None
+    if not args.eager:
+        ref_codes = layers[-1]["qw"].codes.clone()
         quantize_all()
-    for _ in range(2):
-        layers[-1]["qw"].codes.zero_()
-        g_quant.replay()
         torch.cuda.synchronize()
-        assert torch.equal(layers[-1]["qw"].codes, ref_codes), "graph replay differs from eager quantize"
+        g_quant = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g_quant, stream=stream):
+            quantize_all()
+        for _ in range(2):
+            layers[-1]["qw"].codes.zero_()
+            g_quant.replay()
+            torch.cuda.synchronize()
+            assert torch.equal(layers[-1]["qw"].codes, ref_codes), "graph replay differs from eager quantize"
 
     PHASES = ("prefill", "prefill_base", "decode", "decode_base")
 
     # The decode phases (short, launch-bound calls) also run as HIP graphs of the
     # R prepared calls; every replay is checked against the eager outputs first.
     graphs = {}
-    for ph in ("decode", "decode_base"):
+    for ph in (() if args.eager else ("decode", "decode_base")):
         for L in layers:
             L[ph]()
         torch.cuda.synchronize()
@@ -228,7 +297,10 @@ def main():
     def run_step(marks):
         """quantize (graph) -> dequantize -> the four linear phases, marks on `stream`."""
         marks[0].record(stream)
-        g_quant.replay()
+        if g_quant is not None:
+            g_quant.replay()
+        else:
+            quantize_all()
         marks[1].record(stream)
         qlr_deq(layers[0]["qw"], wdeq)
         marks[2].record(stream)
