@@ -45,6 +45,9 @@
 #include <algorithm>
 #include <type_traits>
 
+#include <climits>
+#include <cstdint>
+
 #include "qlr_internal.h"
 #include "qlr_lut.h"
 
@@ -213,10 +216,31 @@ __device__ __forceinline__ void build_gemm_table(const float* sL, int tid) {
   }
 }
 
+// One launch covers up to kGroupMax independent linears of one code width and
+// one M (a mixed stack is launched as groups; a single linear is a group of
+// one).  Tiles are numbered layer by layer, row tiles outer; the per-layer
+// fields are read from the kernel arguments with scalar loads.
+constexpr int kGroupMax = 16;
+struct GemmLayer {
+  const void* x;
+  const uint8_t* codes;
+  const uint8_t* q8;
+  const float* cst;
+  const float* t;   // splits x M x r partial sums of x A^T (r > 0)
+  const void* B;    // N x r
+  void* y;
+  int64_t N, K;
+  int32_t r, t_splits;
+  float scale;
+  int32_t ntiles;   // column tiles (BN rows of W each)
+  int64_t tile0;    // first tile of this layer in the launch
+};
 struct GemmParams {
-  LinearArgs a;
-  int64_t m_begin, m_end;  // rows [m_begin, m_end) of x and y in this launch
-  int64_t mtiles, ntiles, per_xcd;
+  int64_t M;               // rows of x and y of every layer
+  int64_t m_begin, m_end;  // rows [m_begin, m_end) in this launch
+  int64_t mtiles, per_xcd, ntotal;
+  int32_t nl;
+  GemmLayer L[kGroupMax];
 };
 
 // ADP: the call has an adapter branch (r > 0).  Calls without one run a separate
@@ -224,14 +248,31 @@ struct GemmParams {
 template <int BITS, int YDT, bool ADP>
 __global__ __launch_bounds__(512, 1) void k_gemm(GemmParams P, Levels lv) {
   extern __shared__ uint32_t smem[];
-  const LinearArgs& a = P.a;
-  const int64_t N = a.N, K = a.K, nb = K >> 6;
-  const int64_t M = P.m_end;
   // XCD-aware tile order: workgroup b runs on XCD b % 8
   const int64_t xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
   const int64_t tile = xcd * P.per_xcd + local;
-  if (local >= P.per_xcd || tile >= P.mtiles * P.ntiles) return;  // whole workgroup exits
-  const int64_t mt = tile / P.ntiles, nt = tile % P.ntiles;
+  if (local >= P.per_xcd || tile >= P.ntotal) return;  // whole workgroup exits
+  int li = 0;
+  while (li + 1 < P.nl && tile >= P.L[li + 1].tile0) ++li;
+  const GemmLayer& Lr = P.L[li];
+  LinearArgs a;
+  a.x = Lr.x;
+  a.M = P.M;
+  a.N = Lr.N;
+  a.K = Lr.K;
+  a.codes = Lr.codes;
+  a.q8 = Lr.q8;
+  a.cst = Lr.cst;
+  a.t = Lr.t;
+  a.t_splits = Lr.t_splits;
+  a.B = Lr.B;
+  a.r = Lr.r;
+  a.scale = Lr.scale;
+  a.y = Lr.y;
+  const int64_t N = a.N, K = a.K, nb = K >> 6;
+  const int64_t M = P.m_end;
+  const int64_t lt = tile - Lr.tile0;
+  const int64_t mt = lt / Lr.ntiles, nt = lt % Lr.ntiles;
   const int64_t m0 = P.m_begin + mt * BM, n0 = nt * BN;
 
   const int tid = threadIdx.x;
@@ -603,8 +644,16 @@ __global__ __launch_bounds__(512, 1) void k_gemm(GemmParams P, Levels lv) {
   }
 }
 
+// x is read through a buffer resource with 32-bit offsets: one launch covers at
+// most 2^31 bytes of x per layer (whole 256-row tiles).
+int64_t gemm_max_rows(int64_t K) {
+  const int64_t row_bytes = K * 2;
+  if (row_bytes * (BM + 8) >= (int64_t(1) << 31)) return 0;
+  return std::max<int64_t>(BM, ((int64_t(1) << 31) - 1) / row_bytes / BM * BM);
+}
+
 template <int BITS, int YDT, bool ADP>
-hipError_t launch_gemm_t(const LinearArgs& a, const Levels& lv, hipStream_t s) {
+hipError_t launch_gemm_t(const LinearArgs* ls, int n, const Levels& lv, hipStream_t s) {
   const size_t shmem = gemm_lds_bytes<BITS>();
   auto kern = k_gemm<BITS, YDT, ADP>;
   static bool attr = false;
@@ -619,19 +668,43 @@ hipError_t launch_gemm_t(const LinearArgs& a, const Levels& lv, hipStream_t s) {
     if (e != hipSuccess) return e;
     attr = true;
   }
-  // x is read through a buffer resource with 32-bit offsets: one launch covers
-  // at most 2^31 bytes of x (whole 256-row tiles)
-  const int64_t row_bytes = a.K * 2;
-  if (row_bytes * (BM + 8) >= (int64_t(1) << 31)) return hipErrorInvalidValue;
-  const int64_t max_rows = std::max<int64_t>(BM, ((int64_t(1) << 31) - 1) / row_bytes / BM * BM);
-  for (int64_t mb = 0; mb < a.M; mb += max_rows) {
+  if (n <= 0 || n > kGroupMax) return hipErrorInvalidValue;
+  const int64_t M = ls[0].M;
+  int64_t max_rows = INT64_MAX;
+  for (int i = 0; i < n; ++i) {
+    const int64_t mr = gemm_max_rows(ls[i].K);
+    if (mr == 0 || ls[i].M != M) return hipErrorInvalidValue;
+    max_rows = std::min(max_rows, mr);
+  }
+  for (int64_t mb = 0; mb < M; mb += max_rows) {
     GemmParams P;
-    P.a = a;
+    P.M = M;
     P.m_begin = mb;
-    P.m_end = std::min(a.M, mb + max_rows);
+    P.m_end = std::min(M, mb + max_rows);
     P.mtiles = (P.m_end - mb + BM - 1) / BM;
-    P.ntiles = (a.N + BN - 1) / BN;
-    P.per_xcd = (P.mtiles * P.ntiles + 7) / 8;
+    P.nl = n;
+    int64_t t0 = 0;
+    for (int i = 0; i < n; ++i) {
+      const LinearArgs& a = ls[i];
+      GemmLayer& L = P.L[i];
+      L.x = a.x;
+      L.codes = a.codes;
+      L.q8 = a.q8;
+      L.cst = a.cst;
+      L.t = a.t;
+      L.B = a.B;
+      L.y = a.y;
+      L.N = a.N;
+      L.K = a.K;
+      L.r = a.r;
+      L.t_splits = a.t_splits;
+      L.scale = a.scale;
+      L.ntiles = (int32_t)((a.N + BN - 1) / BN);
+      L.tile0 = t0;
+      t0 += P.mtiles * L.ntiles;
+    }
+    P.ntotal = t0;
+    P.per_xcd = (P.ntotal + 7) / 8;
     hipLaunchKernelGGL(kern, dim3((unsigned)(8 * P.per_xcd)), dim3(512), shmem, s, P, lv);
     const hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
@@ -640,23 +713,34 @@ hipError_t launch_gemm_t(const LinearArgs& a, const Levels& lv, hipStream_t s) {
 }
 
 template <int BITS>
-hipError_t launch_gemm_b(const LinearArgs& a, const Levels& lv, hipStream_t s) {
-  if (a.r > 0) {
-    if (a.ydt == DT_F32) return launch_gemm_t<BITS, DT_F32, true>(a, lv, s);
-    return launch_gemm_t<BITS, DT_BF16, true>(a, lv, s);
+hipError_t launch_gemm_b(const LinearArgs* ls, int n, const Levels& lv, hipStream_t s) {
+  bool adp = false;
+  for (int i = 0; i < n; ++i) adp = adp || ls[i].r > 0;
+  if (adp) {
+    if (ls[0].ydt == DT_F32) return launch_gemm_t<BITS, DT_F32, true>(ls, n, lv, s);
+    return launch_gemm_t<BITS, DT_BF16, true>(ls, n, lv, s);
   }
-  if (a.ydt == DT_F32) return launch_gemm_t<BITS, DT_F32, false>(a, lv, s);
-  return launch_gemm_t<BITS, DT_BF16, false>(a, lv, s);
+  if (ls[0].ydt == DT_F32) return launch_gemm_t<BITS, DT_F32, false>(ls, n, lv, s);
+  return launch_gemm_t<BITS, DT_BF16, false>(ls, n, lv, s);
 }
 
 }  // namespace
 
 hipError_t launch_gemm(const LinearArgs& a, const Levels& lv, hipStream_t s) {
-  switch (a.bits) {
-    case 2: return launch_gemm_b<2>(a, lv, s);
-    case 3: return launch_gemm_b<3>(a, lv, s);
-    case 4: return launch_gemm_b<4>(a, lv, s);
-    default: return launch_gemm_b<8>(a, lv, s);
+  return launch_gemm_group(&a, 1, lv, s);
+}
+
+int gemm_group_max() { return kGroupMax; }
+
+hipError_t launch_gemm_group(const LinearArgs* ls, int n, const Levels& lv, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  for (int i = 1; i < n; ++i)
+    if (ls[i].bits != ls[0].bits || ls[i].ydt != ls[0].ydt) return hipErrorInvalidValue;
+  switch (ls[0].bits) {
+    case 2: return launch_gemm_b<2>(ls, n, lv, s);
+    case 3: return launch_gemm_b<3>(ls, n, lv, s);
+    case 4: return launch_gemm_b<4>(ls, n, lv, s);
+    default: return launch_gemm_b<8>(ls, n, lv, s);
   }
 }
 

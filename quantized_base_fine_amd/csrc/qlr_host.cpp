@@ -390,16 +390,41 @@ qlr_status qlr_linear_fwd_mixed(const qlr_layer* layers, int32_t n, int64_t M, q
   if (need > 0 && !aligned16(ws)) return fail(QLR_ERR_ALIGN, "workspace must be 16-byte aligned");
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* wsp = reinterpret_cast<char*>(ws);
+  // GEMM-path layers run as grouped launches (one code width and adapter flag
+  // per group, in layer order), after their adapter products; the others one by one
+  std::vector<qlr::LinearArgs> groups[2][4];
+  auto widx = [](int bits) { return bits == 2 ? 0 : bits == 3 ? 1 : bits == 4 ? 2 : 3; };
   for (int32_t i = 0; i < n; ++i) {
     const qlr_layer& L = layers[i];
     const LinearCheck c{L.x, xdt, M, L.w, L.A, L.B, abdt, L.r, L.y, ydt};
     qlr_path path;
     pick_path(M, xdt, abdt, L.r, &path);
     const size_t need_l = linear_ws_bytes(M, L.w->cols, L.r);
-    qlr_status st = run_linear(c, L.scale, need_l > 0 ? wsp : nullptr, path, s);
-    if (st != QLR_OK) return st;
+    char* wl = need_l > 0 ? wsp : nullptr;
     wsp += need_l;
+    if (path == QLR_PATH_GEMM && M > 0) {
+      const int splits = qlr::lora_t_splits(M, L.w->cols, (int)xdt, (int)abdt);
+      if (L.r > 0) {
+        const hipError_t e = qlr::launch_lora_t(L.x, (int)xdt, M, L.w->cols, L.A, (int)abdt, L.r,
+                                                reinterpret_cast<float*>(wl), splits, s);
+        if (e != hipSuccess) return hip_fail(e, "adapter product launch");
+      }
+      groups[L.r > 0 ? 1 : 0][widx(L.w->bits)].push_back(make_args(c, L.scale, wl, splits));
+      continue;
+    }
+    qlr_status st = run_linear(c, L.scale, wl, path, s);
+    if (st != QLR_OK) return st;
   }
+  const int gmax = qlr::gemm_group_max();
+  for (int ad = 0; ad < 2; ++ad)
+    for (int w = 0; w < 4; ++w) {
+      const std::vector<qlr::LinearArgs>& g = groups[ad][w];
+      for (size_t b = 0; b < g.size(); b += gmax) {
+        const int cnt = (int)std::min<size_t>(gmax, g.size() - b);
+        const hipError_t e = qlr::launch_gemm_group(g.data() + b, cnt, levels_arg(g[b].bits), s);
+        if (e != hipSuccess) return hip_fail(e, "grouped linear launch");
+      }
+    }
   return QLR_OK;
 }
 

@@ -60,5 +60,9 @@ hipError_t launch_gemv(const LinearArgs& a, const Levels& lv, hipStream_t s);
 bool gemv_fuses_adapter(const LinearArgs& a);
 // bf16 tiled GEMM path.
 hipError_t launch_gemm(const LinearArgs& a, const Levels& lv, hipStream_t s);
+// Up to gemm_group_max() independent linears of one code width, one M and one
+// output dtype in one launch (mixed stacks); lv holds that width's levels.
+int gemm_group_max();
+hipError_t launch_gemm_group(const LinearArgs* ls, int n, const Levels& lv, hipStream_t s);
 
 }  // namespace qlr

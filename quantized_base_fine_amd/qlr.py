@@ -276,35 +276,52 @@ class LinearCall:
         return self.y
 
 
+class MixedCall:
+    """A prepared ``qlr_linear_fwd_mixed`` call over independent linears with per-entry
+    (bits, rank); each entry is dict(x, qw, A, B, scale[, y]).  Marshalled once; the
+    tensors are kept alive by the object."""
+
+    def __init__(self, entries: Sequence[dict], out_dtype=None, ws=None):
+        torch = _torch()
+        self.ys = []
+        self._fn = None
+        if not entries:
+            return
+        x0 = entries[0]["x"]
+        M = x0.shape[0]
+        cws = []
+        need = 0
+        abdt = QLR_BF16
+        for e in entries:
+            qw, x, A, B = e["qw"], e["x"], e.get("A"), e.get("B")
+            _require_cuda(x, A, B)
+            r = 0 if A is None else A.shape[0]
+            if r > 0:
+                abdt = _dt(A)
+            y = e.get("y")
+            if y is None:
+                y = torch.empty((M, qw.rows), dtype=out_dtype or x.dtype, device=x.device)
+            self.ys.append(y)
+            cws.append(qw.c_struct())
+            need += workspace_bytes(OP_LINEAR, M, qw.rows, qw.cols, r)
+        arr = (CLayer * len(entries))()
+        for i, e in enumerate(entries):
+            r = 0 if e.get("A") is None else e["A"].shape[0]
+            arr[i] = CLayer(C.pointer(cws[i]), e["x"].data_ptr(), _ptr(e.get("A")), _ptr(e.get("B")), r,
+                            float(e.get("scale", 0.0)), self.ys[i].data_ptr())
+        if ws is None and need > 0:
+            ws = torch.empty(need, dtype=torch.uint8, device=x0.device)
+        self._keep = (list(entries), cws, arr, ws)
+        self._args = (arr, len(entries), M, _dt(x0), abdt, _dt(self.ys[0]), _ptr(ws),
+                      0 if ws is None else ws.numel(), _stream(x0.device))
+        self._fn = lib().qlr_linear_fwd_mixed
+
+    def __call__(self):
+        if self._fn is not None:
+            check(self._fn(*self._args))
+        return self.ys
+
+
 def linear_mixed(entries: Sequence[dict], out_dtype=None, ws=None):
     """Independent linears with per-entry (bits, rank).  Each entry: dict(x, qw, A, B, scale[, y])."""
-    torch = _torch()
-    if not entries:
-        return []
-    x0 = entries[0]["x"]
-    M = x0.shape[0]
-    ys, cws, layers = [], [], []
-    need = 0
-    abdt = QLR_BF16
-    for e in entries:
-        qw, x, A, B = e["qw"], e["x"], e.get("A"), e.get("B")
-        _require_cuda(x, A, B)
-        r = 0 if A is None else A.shape[0]
-        if r > 0:
-            abdt = _dt(A)
-        y = e.get("y")
-        if y is None:
-            y = torch.empty((M, qw.rows), dtype=out_dtype or x.dtype, device=x.device)
-        ys.append(y)
-        cws.append(qw.c_struct())
-        need += workspace_bytes(OP_LINEAR, M, qw.rows, qw.cols, r)
-    arr = (CLayer * len(entries))()
-    for i, e in enumerate(entries):
-        r = 0 if e.get("A") is None else e["A"].shape[0]
-        arr[i] = CLayer(C.pointer(cws[i]), e["x"].data_ptr(), _ptr(e.get("A")), _ptr(e.get("B")), r,
-                        float(e.get("scale", 0.0)), ys[i].data_ptr())
-    if ws is None and need > 0:
-        ws = torch.empty(need, dtype=torch.uint8, device=x0.device)
-    check(lib().qlr_linear_fwd_mixed(arr, len(entries), M, _dt(x0), abdt, _dt(ys[0]), _ptr(ws),
-                                     0 if ws is None else ws.numel(), _stream(x0.device)))
-    return ys
+    return MixedCall(entries, out_dtype=out_dtype, ws=ws)()

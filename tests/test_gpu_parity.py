@@ -265,6 +265,30 @@ def test_mixed_small():
             check_linear(f32_of(y), lin, oracle_rows_dequant(lin.W, "f16", lin.bits, rows), rows)
 
 
+def test_mixed_grouped_equals_single():
+    """Grouped launches of the mixed call (one code width and adapter flag per group,
+    more layers than one launch holds) equal the single-layer calls bit for bit."""
+    # the first 18 layers share one code width (two launches of it), the rest keep their draw
+    plan = [(n, k, 4 if i < 18 else b, r) for i, (n, k, b, r) in enumerate(workloads.mixed_plan())]
+    M = 300
+    entries, singles = [], []
+    for i in range(24):
+        lin = workloads.mixed_linear(i, M=M, plan=plan, shape_override=(144 + 16 * (i % 4), 320 + 64 * (i % 3)))
+        qw = _gpu_quant(lin.W, "f16", lin.bits)
+        x = dev(lin.x, "bf16")
+        if i % 5 == 4:  # some layers without an adapter
+            e = dict(x=x, qw=qw, scale=0.0)
+        else:
+            e = dict(x=x, qw=qw, A=dev(lin.A, "bf16"), B=dev(lin.B, "bf16"), scale=lin.scale)
+        entries.append(e)
+        with qlr.path(qlr.PATH_GEMM):
+            singles.append(qlr.linear(x, qw, e.get("A"), e.get("B"), e["scale"], out_dtype=torch.float32))
+    ys = qlr.linear_mixed(entries, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    for i, (y, y1) in enumerate(zip(ys, singles)):
+        assert torch.equal(y, y1), f"layer {i}"
+
+
 # ---------------------------------------------------------------- decode repeats and graph replays
 
 def test_decode_repeats_bit_identical():
