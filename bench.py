@@ -142,6 +142,32 @@ def traffic_from_counters(fetch_dir: str, write_dir: str):
     print(json.dumps(out, indent=1))
 
 
+MIXED_M = 512
+
+
+def build_mixed(torch, qlr, workloads, dev):
+    """The mixed stack at full size: 32 layers x 7 independent linears with per-linear
+    (bits, rank) drawn by the stack's seed, M = 512.  Weights, x and adapters are drawn
+    on the GPU from a seeded generator with the same distributions as the parity
+    workloads (W N(0, 0.02^2) fp16, A N(0, 1/K), B N(0, 0.01^2) bf16, x N(0, 1) bf16) and
+    quantized once.  Returns the prepared call and its algorithmic flops."""
+    import math
+    gen = torch.Generator(device=dev)
+    gen.manual_seed(4)
+    qws = torch.empty(qlr.workspace_bytes(qlr.OP_QUANTIZE), dtype=torch.uint8, device=dev)
+    entries, flops = [], 0
+    for N, K, b, r in workloads.mixed_plan():
+        W = (torch.randn((N, K), generator=gen, device=dev) * 0.02).to(torch.float16)
+        qw = qlr.quantize(W, b, ws=qws)
+        del W
+        x = torch.randn((MIXED_M, K), generator=gen, device=dev).to(torch.bfloat16)
+        A = (torch.randn((r, K), generator=gen, device=dev) / math.sqrt(K)).to(torch.bfloat16)
+        B = (torch.randn((N, r), generator=gen, device=dev) * 0.01).to(torch.bfloat16)
+        entries.append(dict(x=x, qw=qw, A=A, B=B, scale=16.0 / r))
+        flops += 2 * MIXED_M * N * K + 2 * MIXED_M * r * (K + N)
+    return qlr.MixedCall(entries, out_dtype=torch.bfloat16), flops, len(entries)
+
+
 def cpu_baseline(budget_s: float = 12.0):
     """The oracle (numpy float64) on the host cores, on a bounded sample."""
     import numpy as np
@@ -178,6 +204,7 @@ def main():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--layers", type=int, default=0, help="distinct layer copies (default: > 2x MALL)")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-mixed", action="store_true", help="skip the mixed-stack phase")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one elementwise copy of 256 MiB (counter calibration)")
     ap.add_argument("--eager", action="store_true",
@@ -273,6 +300,11 @@ def main():
             assert torch.equal(layers[-1]["qw"].codes, ref_codes), "graph replay differs from eager quantize"
 
     PHASES = ("prefill", "prefill_base", "decode", "decode_base")
+    mixed = None
+    if not args.no_mixed:
+        mixed, mixed_flops, mixed_n = build_mixed(torch, qlr, workloads, dev)
+        mixed()
+        torch.cuda.synchronize()
 
     # The decode phases (short, launch-bound calls) also run as HIP graphs of the
     # R prepared calls; every replay is checked against the eager outputs first.
@@ -311,8 +343,11 @@ def main():
                 for L in layers:
                     L[ph]()
             marks[3 + i].record(stream)
+        if mixed is not None:
+            mixed()
+            marks[3 + len(PHASES)].record(stream)
 
-    nmarks = 3 + len(PHASES)
+    nmarks = 4 + len(PHASES)
     for _ in range(args.warmup):
         run_step([ev() for _ in range(nmarks)])
     recs = [[ev() for _ in range(nmarks)] for _ in range(args.steps)]  # created before timing
@@ -327,12 +362,14 @@ def main():
     wall = time.perf_counter() - t_wall0
     total_ms = start.elapsed_time(end)
 
-    phase_ms = {k: 0.0 for k in ("quantize", "dequantize") + PHASES}
+    phase_ms = {k: 0.0 for k in ("quantize", "dequantize") + PHASES + (("mixed",) if mixed else ())}
     for marks in recs:
         phase_ms["quantize"] += marks[0].elapsed_time(marks[1])
         phase_ms["dequantize"] += marks[1].elapsed_time(marks[2])
         for i, ph in enumerate(PHASES):
             phase_ms[ph] += marks[2 + i].elapsed_time(marks[3 + i])
+        if mixed is not None:
+            phase_ms["mixed"] += marks[2 + len(PHASES)].elapsed_time(marks[3 + len(PHASES)])
     S = args.steps
     mean = {p: 1e3 * phase_ms[p] / (S * R) for p in PHASES}  # average launch duration, us
     dec_gbs = S * R * decode_bytes() / (phase_ms["decode"] / 1e3) / 1e9
@@ -388,6 +425,17 @@ def main():
         },
         "wall_s": round(wall, 3),
     }
+    if mixed is not None:
+        mixed_ms = phase_ms["mixed"] / S
+        mixed_tfs = mixed_flops / (mixed_ms * 1e-3) / 1e12
+        out["mixed"] = {
+            "workload": f"mixed stack: 32 layers x 7 linears (4096x4096 x4, 11008x4096 x2, 4096x11008), "
+                        f"bits and ranks by seed, M={MIXED_M}",
+            "linears": mixed_n, "flops_per_call": mixed_flops, "ms_per_call": round(mixed_ms, 4),
+            "value": round(mixed_tfs, 2), "unit": "TFLOP/s",
+            "roofline": {"bound": "mfma", "achieved": round(mixed_tfs, 1), "peak": BF16_PEAK_TFLOPS,
+                         "unit": "TFLOP/s", "frac": round(mixed_tfs / BF16_PEAK_TFLOPS, 4)},
+        }
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out))

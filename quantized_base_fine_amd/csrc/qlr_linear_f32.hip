@@ -30,7 +30,86 @@ __global__ __launch_bounds__(256) void k_lora_t_valu(const void* __restrict__ x,
   if (lane == 0) t[m * r + j] = acc;
 }
 
-// bf16 x and A through 16x16x32 bf16 MFMA with float32 accumulation.
+// bf16 x and A, M > 16: t[m][j] in one pass (no K split).  blockIdx.x: 16-row
+// tile of x; blockIdx.y: 16 adapter rows.  The 4 waves split K in 64-element
+// blocks.  A wave loads its x and A pieces coalesced (16-byte pieces, 8 lanes
+// per 128-byte row segment, through buffer resources: rows past M or r and
+// blocks past the wave's range read zero, so every load is unconditional),
+// keeps the next block in flight in registers, stages the current one in its
+// own LDS slice (a wave's LDS accesses run in order, so no barrier) and reads it
+// back in the 16x16x32 bf16 MFMA layout (x rows as the A operand, adapter rows
+// as B; rows 144 bytes apart, conflict-free for those reads).  The waves' 16x16
+// sums are added through LDS in wave order.
+constexpr uint32_t kTRow = 144;                 // LDS row stride (128 bytes + 16)
+constexpr uint32_t kTSlice = 2 * 16 * kTRow;     // one wave: x rows, then A rows
+__device__ __forceinline__ uint32_t t_off(bool ok, uint32_t off) {
+  asm volatile("" : "+v"(off));  // keep the select a select (no branch around the load)
+  return ok ? off : 0xFFFFFFF0u;
+}
+__global__ __launch_bounds__(256) void k_lora_t_tile(const uint16_t* __restrict__ x, int64_t M, int64_t K,
+                                                     const uint16_t* __restrict__ A, int r,
+                                                     float* __restrict__ t) {
+  __shared__ __attribute__((aligned(16))) char lds[4 * kTSlice];
+  __shared__ float red[4][256];
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int64_t m0 = (int64_t)blockIdx.x * 16, j0 = (int64_t)blockIdx.y * 16;
+  const int64_t nb = K / 64;
+  const int64_t kb0 = nb * wave / 4, kb1 = nb * (wave + 1) / 4;
+  const int64_t mrows = std::min<int64_t>(16, M - m0), jrows = std::min<int64_t>(16, (int64_t)r - j0);
+  const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(x + m0 * K), (short)0, (int)(mrows * K * 2), 0x00020000);
+  const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc(
+      const_cast<uint16_t*>(A + j0 * K), (short)0, (int)(jrows * K * 2), 0x00020000);
+  struct Blk { u32x4_t xa[2], aa[2]; };
+  auto load = [&](int64_t kb, Blk& b) {
+    const bool kv = kb < kb1;
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int q = i * 64 + lane;
+      const uint32_t off = t_off(kv, (uint32_t)(((q >> 3) * K + kb * 64 + (q & 7) * 8) * 2));
+      b.xa[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
+      b.aa[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ar, off, 0, 0));
+    }
+  };
+  char* slice = lds + wave * kTSlice;
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
+  auto compute = [&](const Blk& b) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int q = i * 64 + lane;
+      const uint32_t o = (uint32_t)(q >> 3) * kTRow + (uint32_t)(q & 7) * 16;
+      *reinterpret_cast<u32x4_t*>(slice + o) = b.xa[i];
+      *reinterpret_cast<u32x4_t*>(slice + 16 * kTRow + o) = b.aa[i];
+    }
+#pragma unroll
+    for (int ks = 0; ks < 2; ++ks) {
+      const uint32_t o = (uint32_t)(lane & 15) * kTRow + (uint32_t)(4 * ks + (lane >> 4)) * 16;
+      const u32x4_t xf = *reinterpret_cast<const u32x4_t*>(slice + o);
+      const u32x4_t af = *reinterpret_cast<const u32x4_t*>(slice + 16 * kTRow + o);
+      acc = mfma16x16x32(as_bf16x8(xf), as_bf16x8(af), acc);
+    }
+  };
+  Blk b0, b1;
+  load(kb0, b0);
+  load(kb0 + 1, b1);
+  for (int64_t kb = kb0; kb < kb1; kb += 2) {
+    compute(b0);
+    load(kb + 2, b0);
+    if (kb + 1 < kb1) compute(b1);
+    load(kb + 3, b1);
+  }
+#pragma unroll
+  for (int v = 0; v < 4; ++v) red[wave][lane * 4 + v] = acc[v];
+  __syncthreads();
+  const int e = threadIdx.x;
+  const float sum = (red[0][e] + red[1][e]) + (red[2][e] + red[3][e]);
+  const int l = e >> 2, v = e & 3;
+  const int64_t m = m0 + 4 * (l >> 4) + v;  // MFMA output row
+  const int64_t j = j0 + (l & 15);          // MFMA output column
+  if (m < M && j < r) t[m * r + j] = sum;
+}
+
+// bf16 x and A, M <= 16, through 16x16x32 bf16 MFMA with float32 accumulation.
 // blockIdx.x: 16-row tile of x; blockIdx.y: group of 64 adapter rows;
 // blockIdx.z: K split.  The 4 waves share the split's 32-wide K steps and are
 // reduced through LDS; the split's partial sum goes to p[z][m][j].
@@ -156,7 +235,7 @@ hipError_t launch_f32_b1(const LinearArgs& a, const Levels& lv, hipStream_t s) {
 }  // namespace
 
 int lora_t_splits(int64_t M, int64_t K, int xdt, int abdt) {
-  if (!(xdt == DT_BF16 && abdt == DT_BF16)) return 1;
+  if (!(xdt == DT_BF16 && abdt == DT_BF16) || M > 16) return 1;
   const int64_t steps = K / 32, mtiles = (M + 15) / 16;
   int64_t s = std::min<int64_t>(steps / 4, (256 + mtiles - 1) / mtiles);
   s = std::min<int64_t>(s, 64);
@@ -166,6 +245,14 @@ int lora_t_splits(int64_t M, int64_t K, int xdt, int abdt) {
 hipError_t launch_lora_t(const void* x, int xdt, int64_t M, int64_t K, const void* A, int abdt,
                          int r, float* t, int splits, hipStream_t s) {
   if (M == 0 || r == 0) return hipSuccess;
+  if (xdt == DT_BF16 && abdt == DT_BF16 && M > 16) {
+    // 16 rows of x or A are addressed with 32-bit buffer offsets
+    if (16 * K * 2 >= (int64_t(1) << 31) || splits != 1) return hipErrorInvalidValue;
+    dim3 grid((unsigned)((M + 15) / 16), (unsigned)((r + 15) / 16));
+    hipLaunchKernelGGL(k_lora_t_tile, grid, dim3(256), 0, s, reinterpret_cast<const uint16_t*>(x), M, K,
+                       reinterpret_cast<const uint16_t*>(A), r, t);
+    return hipGetLastError();
+  }
   if (xdt == DT_BF16 && abdt == DT_BF16) {
     dim3 grid((unsigned)((M + 15) / 16), (unsigned)((r + 63) / 64), (unsigned)splits);
     hipLaunchKernelGGL(k_lora_t_mfma, grid, dim3(256), 0, s, reinterpret_cast<const uint16_t*>(x), M,

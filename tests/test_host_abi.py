@@ -52,8 +52,8 @@ def test_workspace_sizes():
     assert qlr.workspace_bytes(qlr.OP_LINEAR, 0, 4096, 4096, 16) == 0
     assert qlr.workspace_bytes(qlr.OP_LINEAR, 7, 4096, 4096, 0) == 0
     # float32 partial sums of x A^T over the adapter product's K splits, rounded
-    # to 256 bytes: 2 splits at M=2048, K=4096; 32 at M=1; 1 at K=64
-    assert qlr.workspace_bytes(qlr.OP_LINEAR, 2048, 4096, 4096, 16) == 2 * 2048 * 16 * 4
+    # to 256 bytes: one pass (no split) for M > 16; 32 splits at M=1, K=4096; 1 at K=64
+    assert qlr.workspace_bytes(qlr.OP_LINEAR, 2048, 4096, 4096, 16) == 2048 * 16 * 4  # M > 16: one K pass
     assert qlr.workspace_bytes(qlr.OP_LINEAR, 1, 4096, 4096, 16) == 32 * 16 * 4
     assert qlr.workspace_bytes(qlr.OP_LINEAR, 3, 10, 64, 5) == 256
 
