@@ -393,6 +393,7 @@ qlr_status qlr_linear_fwd_mixed(const qlr_layer* layers, int32_t n, int64_t M, q
   // GEMM-path layers run as grouped launches (one code width and adapter flag
   // per group, in layer order), after their adapter products; the others one by one
   std::vector<qlr::LinearArgs> groups[2][4];
+  std::vector<qlr::LoraTItem> tgroup;
   auto widx = [](int bits) { return bits == 2 ? 0 : bits == 3 ? 1 : bits == 4 ? 2 : 3; };
   for (int32_t i = 0; i < n; ++i) {
     const qlr_layer& L = layers[i];
@@ -405,15 +406,25 @@ qlr_status qlr_linear_fwd_mixed(const qlr_layer* layers, int32_t n, int64_t M, q
     if (path == QLR_PATH_GEMM && M > 0) {
       const int splits = qlr::lora_t_splits(M, L.w->cols, (int)xdt, (int)abdt);
       if (L.r > 0) {
-        const hipError_t e = qlr::launch_lora_t(L.x, (int)xdt, M, L.w->cols, L.A, (int)abdt, L.r,
-                                                reinterpret_cast<float*>(wl), splits, s);
-        if (e != hipSuccess) return hip_fail(e, "adapter product launch");
+        if (M > 16 && xdt == QLR_BF16 && abdt == QLR_BF16) {
+          tgroup.push_back(qlr::LoraTItem{L.x, L.A, reinterpret_cast<float*>(wl), L.w->cols, L.r});
+        } else {
+          const hipError_t e = qlr::launch_lora_t(L.x, (int)xdt, M, L.w->cols, L.A, (int)abdt, L.r,
+                                                  reinterpret_cast<float*>(wl), splits, s);
+          if (e != hipSuccess) return hip_fail(e, "adapter product launch");
+        }
       }
       groups[L.r > 0 ? 1 : 0][widx(L.w->bits)].push_back(make_args(c, L.scale, wl, splits));
       continue;
     }
     qlr_status st = run_linear(c, L.scale, wl, path, s);
     if (st != QLR_OK) return st;
+  }
+  // adapter products of the grouped layers, then their GEMMs
+  for (size_t b = 0; b < tgroup.size(); b += qlr::lora_t_group_max()) {
+    const int cnt = (int)std::min<size_t>(qlr::lora_t_group_max(), tgroup.size() - b);
+    const hipError_t e = qlr::launch_lora_t_group(tgroup.data() + b, cnt, M, s);
+    if (e != hipSuccess) return hip_fail(e, "grouped adapter product launch");
   }
   const int gmax = qlr::gemm_group_max();
   for (int ad = 0; ad < 2; ++ad)

@@ -31,6 +31,18 @@ int lora_t_splits(int64_t M, int64_t K, int xdt, int abdt);
 hipError_t launch_lora_t(const void* x, int xdt, int64_t M, int64_t K, const void* A, int abdt,
                          int r, float* t, int splits, hipStream_t s);
 
+// bf16 products of several linears with one M > 16 (a mixed stack's adapters):
+// up to lora_t_group_max() per launch, each written in one K pass (splits 1).
+struct LoraTItem {
+  const void* x;   // M x K bf16
+  const void* A;   // r x K bf16
+  float* t;        // M x r float32
+  int64_t K;
+  int r;
+};
+int lora_t_group_max();
+hipError_t launch_lora_t_group(const LoraTItem* items, int n, int64_t M, hipStream_t s);
+
 struct LinearArgs {
   const void* x;
   int xdt;

@@ -46,13 +46,37 @@ __device__ __forceinline__ uint32_t t_off(bool ok, uint32_t off) {
   asm volatile("" : "+v"(off));  // keep the select a select (no branch around the load)
   return ok ? off : 0xFFFFFFF0u;
 }
-__global__ __launch_bounds__(256) void k_lora_t_tile(const uint16_t* __restrict__ x, int64_t M, int64_t K,
-                                                     const uint16_t* __restrict__ A, int r,
-                                                     float* __restrict__ t) {
+// One launch covers up to kTGroupMax independent products of one M (a mixed
+// stack's adapters in groups; a single product is a group of one).  Tiles are
+// numbered layer by layer, x-row tiles outer, adapter-row tiles inner.
+constexpr int kTGroupMax = 16;
+struct TLayer {
+  const uint16_t* x;
+  const uint16_t* A;
+  float* t;
+  int64_t K;
+  int32_t r, jtiles;
+  int64_t tile0;
+};
+struct TGroup {
+  int64_t M;
+  int32_t nl;
+  TLayer L[kTGroupMax];
+};
+__global__ __launch_bounds__(256) void k_lora_t_tile(TGroup G) {
   __shared__ __attribute__((aligned(16))) char lds[4 * kTSlice];
   __shared__ float red[4][256];
+  int li = 0;
+  while (li + 1 < G.nl && (int64_t)blockIdx.x >= G.L[li + 1].tile0) ++li;
+  const TLayer& Ly = G.L[li];
+  const uint16_t* __restrict__ x = Ly.x;
+  const uint16_t* __restrict__ A = Ly.A;
+  float* __restrict__ t = Ly.t;
+  const int64_t M = G.M, K = Ly.K;
+  const int r = Ly.r;
+  const int64_t lt = (int64_t)blockIdx.x - Ly.tile0;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t m0 = (int64_t)blockIdx.x * 16, j0 = (int64_t)blockIdx.y * 16;
+  const int64_t m0 = (lt / Ly.jtiles) * 16, j0 = (lt % Ly.jtiles) * 16;
   const int64_t nb = K / 64;
   const int64_t kb0 = nb * wave / 4, kb1 = nb * (wave + 1) / 4;
   const int64_t mrows = std::min<int64_t>(16, M - m0), jrows = std::min<int64_t>(16, (int64_t)r - j0);
@@ -246,12 +270,9 @@ hipError_t launch_lora_t(const void* x, int xdt, int64_t M, int64_t K, const voi
                          int r, float* t, int splits, hipStream_t s) {
   if (M == 0 || r == 0) return hipSuccess;
   if (xdt == DT_BF16 && abdt == DT_BF16 && M > 16) {
-    // 16 rows of x or A are addressed with 32-bit buffer offsets
-    if (16 * K * 2 >= (int64_t(1) << 31) || splits != 1) return hipErrorInvalidValue;
-    dim3 grid((unsigned)((M + 15) / 16), (unsigned)((r + 15) / 16));
-    hipLaunchKernelGGL(k_lora_t_tile, grid, dim3(256), 0, s, reinterpret_cast<const uint16_t*>(x), M, K,
-                       reinterpret_cast<const uint16_t*>(A), r, t);
-    return hipGetLastError();
+    if (splits != 1) return hipErrorInvalidValue;
+    const LoraTItem it{x, A, t, K, r};
+    return launch_lora_t_group(&it, 1, M, s);
   }
   if (xdt == DT_BF16 && abdt == DT_BF16) {
     dim3 grid((unsigned)((M + 15) / 16), (unsigned)((r + 63) / 64), (unsigned)splits);
@@ -277,6 +298,36 @@ hipError_t launch_linear_f32(const LinearArgs& a, const Levels& lv, hipStream_t 
     case 4: return launch_f32_b1<4>(a, lv, s);
     default: return launch_f32_b1<8>(a, lv, s);
   }
+}
+
+int lora_t_group_max() { return kTGroupMax; }
+
+hipError_t launch_lora_t_group(const LoraTItem* items, int n, int64_t M, hipStream_t s) {
+  if (n <= 0 || M <= 0) return hipSuccess;
+  if (n > kTGroupMax || M <= 16) return hipErrorInvalidValue;
+  TGroup G;
+  G.M = M;
+  G.nl = 0;
+  int64_t t0 = 0;
+  const int64_t mtiles = (M + 15) / 16;
+  for (int i = 0; i < n; ++i) {
+    const LoraTItem& it = items[i];
+    if (it.r <= 0) continue;
+    // 16 rows of x or A are addressed with 32-bit buffer offsets
+    if (16 * it.K * 2 >= (int64_t(1) << 31)) return hipErrorInvalidValue;
+    TLayer& L = G.L[G.nl++];
+    L.x = reinterpret_cast<const uint16_t*>(it.x);
+    L.A = reinterpret_cast<const uint16_t*>(it.A);
+    L.t = it.t;
+    L.K = it.K;
+    L.r = it.r;
+    L.jtiles = (it.r + 15) / 16;
+    L.tile0 = t0;
+    t0 += mtiles * L.jtiles;
+  }
+  if (G.nl == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_lora_t_tile, dim3((unsigned)t0), dim3(256), 0, s, G);
+  return hipGetLastError();
 }
 
 }  // namespace qlr
