@@ -429,7 +429,11 @@ qlr_status qlr_linear_fwd_mixed(const qlr_layer* layers, int32_t n, int64_t M, q
   const int gmax = qlr::gemm_group_max();
   for (int ad = 0; ad < 2; ++ad)
     for (int w = 0; w < 4; ++w) {
-      const std::vector<qlr::LinearArgs>& g = groups[ad][w];
+      std::vector<qlr::LinearArgs>& g = groups[ad][w];
+      // longest tiles (largest K) first: workgroups are dispatched in order, so
+      // the short tiles fill in behind the long ones
+      std::stable_sort(g.begin(), g.end(),
+                       [](const qlr::LinearArgs& p, const qlr::LinearArgs& q) { return p.K > q.K; });
       for (size_t b = 0; b < g.size(); b += gmax) {
         const int cnt = (int)std::min<size_t>(gmax, g.size() - b);
         const hipError_t e = qlr::launch_gemm_group(g.data() + b, cnt, levels_arg(g[b].bits), s);
