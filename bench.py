@@ -145,6 +145,48 @@ def traffic_from_counters(fetch_dir: str, write_dir: str):
 MIXED_M = 512
 
 
+def decode_by_bits(torch, qlr, W, x1, A0, B0, scale, dev, reps=5):
+    """Decode GEMV (M = 1) of the same 4096x4096 layer at the other code widths, without
+    and with the r16 adapter: per-call time (HIP graph of R distinct copies, R sized to
+    exceed twice the last-level cache) and effective GB/s of each call's algorithmic bytes."""
+    out = {}
+    for b in (2, 3, 8):
+        cb, qb, kb = qlr.qweight_sizes(N_, K_, b)
+        R = (2 * MALL_BYTES) // (cb + qb + kb) + 1
+        qws = torch.empty(qlr.workspace_bytes(qlr.OP_QUANTIZE), dtype=torch.uint8, device=dev)
+        ws = torch.empty(max(qlr.workspace_bytes(qlr.OP_LINEAR, 1, N_, K_, R_), 16), dtype=torch.uint8, device=dev)
+        y = torch.empty((1, N_), dtype=torch.bfloat16, device=dev)
+        layers = [qlr.quantize(W, b, ws=qws) for _ in range(R)]
+        rec = {}
+        for name, mk in (("base", lambda q: qlr.LinearCall(x1, q, out=y)),
+                         ("adapter", lambda q: qlr.LinearCall(x1, q, A0, B0, scale, out=y, ws=ws))):
+            calls = [mk(q) for q in layers]
+            for c in calls:
+                c()
+            torch.cuda.synchronize()
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=torch.cuda.current_stream(dev)):
+                for c in calls:
+                    c()
+            g.replay()
+            torch.cuda.synchronize()
+            s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            s.record()
+            for _ in range(reps):
+                g.replay()
+            e.record()
+            torch.cuda.synchronize()
+            us = s.elapsed_time(e) * 1e3 / (reps * R)
+            nbytes = decode_bytes(b=b, r=R_ if name == "adapter" else 0)
+            rec[name] = {"us_per_call": round(us, 3), "gbs": round(nbytes / (us * 1e-6) / 1e9, 1),
+                         "bytes_per_call": nbytes}
+        rec["layers"] = R
+        out[str(b)] = rec
+        del layers
+    return out
+
+
+
 def build_mixed(torch, qlr, workloads, dev):
     """The mixed stack at full size: 32 layers x 7 independent linears with per-linear
     (bits, rank) drawn by the stack's seed, M = 512.  Weights, x and adapters are drawn
@@ -425,6 +467,7 @@ def main():
         },
         "wall_s": round(wall, 3),
     }
+    out["decode_by_bits"] = decode_by_bits(torch, qlr, W, x1, A0, B0, lin1.scale, dev)
     if mixed is not None:
         mixed_ms = phase_ms["mixed"] / S
         mixed_tfs = mixed_flops / (mixed_ms * 1e-3) / 1e12
