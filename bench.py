@@ -467,7 +467,8 @@ def main():
         },
         "wall_s": round(wall, 3),
     }
-    out["decode_by_bits"] = decode_by_bits(torch, qlr, W, x1, A0, B0, lin1.scale, dev)
+    if not args.eager:
+        out["decode_by_bits"] = decode_by_bits(torch, qlr, W, x1, A0, B0, lin1.scale, dev)
     if mixed is not None:
         mixed_ms = phase_ms["mixed"] / S
         mixed_tfs = mixed_flops / (mixed_ms * 1e-3) / 1e12
