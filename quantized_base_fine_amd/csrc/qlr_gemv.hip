@@ -723,7 +723,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
       const int64_t nn = tl * 16 + (l & 15);
       epilogue(m, l & 15, nn, tid < 256 && m < M && nn < N, s);
     }
-    __syncthreads();
+    // the next tile reuses sRed and the B tile; after the workgroup's last tile
+    // nothing is reused
+    if (tl + gridDim.x < P.ntiles) __syncthreads();
   };
 
   // The stream: chunk j is item j % nitem of tile blockIdx.x + (j / nitem) gridDim.x;
