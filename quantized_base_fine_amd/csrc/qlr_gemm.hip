@@ -374,8 +374,9 @@ __global__ __launch_bounds__(512, 1) void k_gemm(GemmParams P, Levels lv) {
       store_w(o, buf);
     };
 
-    // Block k+2 is written while the consumers multiply block k.  x(k+2) was
-    // loaded one block earlier (set (k+2) % 3), codes(k+2) two blocks earlier.
+    // Block k+2 is written while the consumers multiply block k.  x(j) and
+    // codes(j) live in register set j % 3 and are loaded two blocks before they
+    // are written (a set is free again once its block is in LDS).
     XS x0, x1, x2;
     CS c0, c1, c2;
     load_x(x0, 0);
@@ -385,13 +386,13 @@ __global__ __launch_bounds__(512, 1) void k_gemm(GemmParams P, Levels lv) {
     load_c(c2, min<int64_t>(2, kbl));
     load_x(x2, min<int64_t>(2, kbl));
     store_x(x0, 0);
+    load_x(x0, min<int64_t>(3, kbl));
     dequant_store(c0, 0);
     load_c(c0, min<int64_t>(3, kbl));
     store_x(x1, 1);
     dequant_store(c1, 1);
     __syncthreads();
-    // step k: load x(k+3) into set k % 3 and codes(k+4) into set (k+1) % 3; write block k+2
-    // Step k: load x(k+3) into set k % 3 and codes(k+4) into set (k+1) % 3;
+    // Step k: load x(k+4) into set (k+1) % 3 and codes(k+4) into set (k+1) % 3;
     // write x(k+2) and the dequantized block k+2 into buffer (k+2) % 3.  The
     // step runs in pinned chunks, each a few loads plus the arithmetic of one
     // code word, so the wave keeps computing while the load queue drains.
@@ -403,19 +404,19 @@ __global__ __launch_bounds__(512, 1) void k_gemm(GemmParams P, Levels lv) {
       dq_part(d, std::integral_constant<int, 0>{}, o);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int j = 0; j < 3; ++j) load_xj(xl, min(k + 3, kbl), j);
+      for (int j = 0; j < 3; ++j) load_xj(xl, min(k + 4, kbl), j);
 #pragma unroll
       for (int j = 0; j < 3; ++j) lds_store_u32x4(xst[j & 1] + bw * kXTile + 1024u * j, xw.v[j]);
       dq_part(d, std::integral_constant<int, 1>{}, o);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int j = 3; j < 6; ++j) load_xj(xl, min(k + 3, kbl), j);
+      for (int j = 3; j < 6; ++j) load_xj(xl, min(k + 4, kbl), j);
 #pragma unroll
       for (int j = 3; j < 6; ++j) lds_store_u32x4(xst[j & 1] + bw * kXTile + 1024u * j, xw.v[j]);
       dq_part(d, std::integral_constant<int, 2>{}, o);
       __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-      for (int j = 6; j < 8; ++j) load_xj(xl, min(k + 3, kbl), j);
+      for (int j = 6; j < 8; ++j) load_xj(xl, min(k + 4, kbl), j);
 #pragma unroll
       for (int j = 6; j < 8; ++j) lds_store_u32x4(xst[j & 1] + bw * kXTile + 1024u * j, xw.v[j]);
       dq_part(d, std::integral_constant<int, 3>{}, o);
@@ -427,12 +428,12 @@ __global__ __launch_bounds__(512, 1) void k_gemm(GemmParams P, Levels lv) {
     const int64_t nb3 = nb - nb % 3;
     int64_t kb = 0;
     for (; kb < nb3; kb += 3) {
-      pstep(x0, x2, c1, c2, kb, 2);
-      pstep(x1, x0, c2, c0, kb + 1, 0);
-      pstep(x2, x1, c0, c1, kb + 2, 1);
+      pstep(x1, x2, c1, c2, kb, 2);
+      pstep(x2, x0, c2, c0, kb + 1, 0);
+      pstep(x0, x1, c0, c1, kb + 2, 1);
     }
-    if (kb < nb) pstep(x0, x2, c1, c2, kb, 2);
-    if (kb + 1 < nb) pstep(x1, x0, c2, c0, kb + 1, 0);
+    if (kb < nb) pstep(x1, x2, c1, c2, kb, 2);
+    if (kb + 1 < nb) pstep(x2, x0, c2, c0, kb + 1, 0);
     // the consumers' two epilogue barriers: tiles free, then the output staged
     __syncthreads();
     __syncthreads();
