@@ -28,7 +28,8 @@ from .codebook import normal_quantile, quantile_codebook
 from .quant import (widen, block_absmax, nearest_codes, pack_codes, unpack_codes,
                     double_quantize, dequantize_scales, dequantize, quantize,
                     qweight_sizes, QuantizedWeight)
-from .linear import lora_t, linear, linear_tolerance, mixed
+from .linear import (lora_t, linear, linear_tolerance, mixed, linear_backward,
+                     linear_backward_tolerance)
 
 __all__ = [
     "normal_quantile", "quantile_codebook", "widen", "block_absmax", "nearest_codes",

@@ -50,3 +50,65 @@ def linear_tolerance(x, xdtype, wdeq32):
 def mixed(entries):
     """Independent linears: ``entries`` is a list of kwargs for ``linear``."""
     return [linear(**e) for e in entries]
+
+
+def linear_backward(dy, dydtype, x, xdtype, wdeq32, A=None, B=None, abdtype="f32", scale=0.0):
+    """Gradients of the forward above for an upstream gradient dy (M x N), float64.
+
+    The pages freeze the quantized base and train only the adapter (QLoRA page,
+    memory-decomposition equation: frozen 4-bit weights, bf16 adapters with
+    optimizer state; AutoQRA page, "1. Problem statement": the quantized backbone
+    stays frozen while lightweight adapters are trained).  The gradients are not
+    written out on the pages; they are the chain rule of the forward, the plain
+    definition used here:
+        u  = dy B                    (M x r)
+        t  = x A^T                   (M x r)
+        dx = dy W' + scale u A       (M x K)   input gradient through the frozen base
+        dA = scale u^T x             (r x K)
+        dB = scale dy^T t            (N x r)
+    W' itself gets no gradient.  Returns (dx, dA, dB); dA and dB are None when
+    the call has no adapter.
+    """
+    g = _f64(dy, dydtype)
+    xf = _f64(x, xdtype)
+    w = wdeq32.astype(np.float64)
+    if g.ndim != 2 or xf.ndim != 2 or w.ndim != 2:
+        raise ValueError("dy, x and W' must be matrices")
+    if xf.shape[1] != w.shape[1] or g.shape != (xf.shape[0], w.shape[0]):
+        raise ValueError("x must be (M, K), W' (N, K) and dy (M, N)")
+    dx = g @ w
+    if A is None or B is None or A.shape[0] == 0:
+        return dx, None, None
+    Af, Bf = _f64(A, abdtype), _f64(B, abdtype)
+    if Af.shape[1] != w.shape[1] or Bf.shape != (w.shape[0], Af.shape[0]):
+        raise ValueError("A must be (r, K) and B (N, r)")
+    s = float(scale)
+    u = g @ Bf
+    t = xf @ Af.T
+    dx = dx + s * (u @ Af)
+    dA = s * (u.T @ xf)
+    dB = s * (g.T @ t)
+    return dx, dA, dB
+
+
+def linear_backward_tolerance(dy, dydtype, x, xdtype, wdeq32, A=None, B=None, abdtype="f32", scale=0.0):
+    """Magnitude sums that scale the per-element error bound of each gradient.
+
+    Every term of each gradient is replaced by its absolute value, and so is every
+    term of the intermediate u = dy B and t = x A^T that feeds it (their rounding
+    errors are bounded by the same sums):
+        Sdx[m,k] = sum_n |dy w'| + |s| sum_j U[m,j] |A[j,k]|,  U = |dy| |B|
+        SdA[j,k] = |s| sum_m U[m,j] |x[m,k]|
+        SdB[n,j] = |s| sum_m |dy[m,n]| T[m,j],                 T = |x| |A|^T
+    """
+    g = np.abs(_f64(dy, dydtype))
+    xf = np.abs(_f64(x, xdtype))
+    w = np.abs(wdeq32.astype(np.float64))
+    sdx = g @ w
+    if A is None or B is None or A.shape[0] == 0:
+        return sdx, None, None
+    Af, Bf = np.abs(_f64(A, abdtype)), np.abs(_f64(B, abdtype))
+    s = abs(float(scale))
+    U = g @ Bf
+    T = xf @ Af.T
+    return sdx + s * (U @ Af), s * (U.T @ xf), s * (g.T @ T)
