@@ -69,7 +69,7 @@ typedef enum {
   QLR_PATH_GEMM = 3  /* bf16 x, any M: LDS-tiled prefill GEMM (bf16 MFMA, fp32 accumulate) */
 } qlr_path;
 
-typedef enum { QLR_OP_QUANTIZE = 0, QLR_OP_LINEAR = 1 } qlr_op;
+typedef enum { QLR_OP_QUANTIZE = 0, QLR_OP_LINEAR = 1, QLR_OP_LINEAR_BWD = 2 } qlr_op;
 
 /*
  * A quantized frozen weight (QLoRA page, sections "1. 4-bit NormalFloat" and
@@ -141,8 +141,10 @@ qlr_status qlr_qweight_sizes(int64_t rows, int64_t cols, int32_t bits, int32_t b
  * Device workspace needed by an operation.  QLR_OP_QUANTIZE: 256 bytes (the
  * non-finite flag); M, N, K, r are ignored.  QLR_OP_LINEAR: the adapter
  * product t = x A^T for M rows and rank r as float32 partial sums over K
- * splits, rounded up to 256 bytes (0 bytes when M or r is 0).  Its contents
- * need no initialisation.  Host only.
+ * splits, rounded up to 256 bytes (0 bytes when M or r is 0).
+ * QLR_OP_LINEAR_BWD (N = rows, K = cols of the weight): the partial sums of
+ * x A^T and dy B, B transposed, and float32 partials of the adapter gradients
+ * (0 bytes when r is 0).  Contents need no initialisation.  Host only.
  */
 qlr_status qlr_workspace_bytes(qlr_op op, int64_t M, int64_t N, int64_t K, int32_t r,
                                size_t* bytes);
@@ -217,6 +219,41 @@ qlr_status qlr_linear_fwd(const void* x, qlr_dtype xdt, int64_t M, const qlr_qwe
 qlr_status qlr_linear_fwd_mixed(const qlr_layer* layers, int32_t n, int64_t M, qlr_dtype xdt,
                                 qlr_dtype abdt, qlr_dtype ydt, void* ws, size_t ws_bytes,
                                 void* stream);
+
+/*
+ * Backward for adapter training (the step after the forward in fine-tuning:
+ * QLoRA page, memory-decomposition equation, frozen 4-bit base with trained
+ * bf16 adapters; AutoQRA page, "1. Problem statement", frozen quantized
+ * backbone with trained adapters).  For the forward of qlr_linear_fwd and an
+ * upstream gradient dy, with u = dy B and t = x A^T:
+ *     dx = dy W' + scale * u A      (M x K)  input gradient through the frozen base
+ *     dA = scale * u^T x            (r x K)
+ *     dB = scale * dy^T t           (N x r)
+ * W' gets no gradient (it is frozen).  dy (device) M x N in dydt (f32 or bf16);
+ * x (device) M x K in xdt, which must equal dydt when r > 0 (x is not read
+ * when r == 0 and may be NULL); A, B as in qlr_linear_fwd; dx (device) M x K
+ * in dxdt (f32 or bf16), or NULL to skip the input gradient; dA (device, r x K)
+ * and dB (device, N x r) float32, overwritten (zero when M == 0), required when
+ * r > 0.  No output may overlap an input or another output (QLR_ERR_ALIAS).
+ * Requires cols % 64 == 0.  Kernel families: with bf16 dy, x and adapters and
+ * rows % 64 == 0 the input gradient runs on bf16 MFMA (the weight dequantized
+ * to bf16, float32 accumulation); otherwise, or under QLR_PATH_F32, on float32
+ * arithmetic (qlr_force_path: QLR_PATH_GEMV selects the MFMA family here, as
+ * the backward has no separate decode kernel).  u, t, dA and dB are float32
+ * sums of exactly widened inputs.  Per element, each result is within
+ * 1e-3 * S + 1e-5 of the exact value, S the sum of the absolute values of the
+ * terms that define it (with |u| and |t| likewise bounded by sums of absolute
+ * products), plus half a bf16 ulp for a bf16 dx.  ws (device) >=
+ * qlr_workspace_bytes(QLR_OP_LINEAR_BWD, M, rows, cols, r).  Asynchronous,
+ * allocation-free; the results do not depend on timing.
+ * Errors: QLR_ERR_NULL, QLR_ERR_SHAPE, QLR_ERR_DTYPE, QLR_ERR_BITS,
+ * QLR_ERR_BLOCK, QLR_ERR_ALIGN, QLR_ERR_FORMAT, QLR_ERR_WORKSPACE,
+ * QLR_ERR_ALIAS, QLR_ERR_PATH, QLR_ERR_HIP.
+ */
+qlr_status qlr_linear_bwd(const void* dy, qlr_dtype dydt, const void* x, qlr_dtype xdt, int64_t M,
+                          const qlr_qweight* w, const void* A, const void* B, qlr_dtype abdt, int32_t r,
+                          float scale, void* dx, qlr_dtype dxdt, float* dA, float* dB, void* ws,
+                          size_t ws_bytes, void* stream);
 
 /*
  * Force the kernel family used by qlr_linear_fwd and qlr_linear_fwd_mixed on

@@ -29,11 +29,12 @@ from .quant import (widen, block_absmax, nearest_codes, pack_codes, unpack_codes
                     double_quantize, dequantize_scales, dequantize, quantize,
                     qweight_sizes, QuantizedWeight)
 from .linear import (lora_t, linear, linear_tolerance, mixed, linear_backward,
-                     linear_backward_tolerance)
+                     linear_backward_tolerance, adapter_grads, adapter_grads_tolerance)
 
 __all__ = [
     "normal_quantile", "quantile_codebook", "widen", "block_absmax", "nearest_codes",
     "pack_codes", "unpack_codes", "double_quantize", "dequantize_scales", "dequantize",
     "quantize", "qweight_sizes", "QuantizedWeight", "lora_t", "linear",
-    "linear_tolerance", "mixed",
+    "linear_tolerance", "mixed", "linear_backward", "linear_backward_tolerance", "adapter_grads",
+    "adapter_grads_tolerance",
 ]

@@ -82,13 +82,22 @@ def linear_backward(dy, dydtype, x, xdtype, wdeq32, A=None, B=None, abdtype="f32
     Af, Bf = _f64(A, abdtype), _f64(B, abdtype)
     if Af.shape[1] != w.shape[1] or Bf.shape != (w.shape[0], Af.shape[0]):
         raise ValueError("A must be (r, K) and B (N, r)")
+    dx = dx + float(scale) * ((g @ Bf) @ Af)
+    dA, dB = adapter_grads(dy, dydtype, x, xdtype, A, B, abdtype, scale)
+    return dx, dA, dB
+
+
+def adapter_grads(dy, dydtype, x, xdtype, A, B, abdtype, scale):
+    """The adapter's gradients alone (they do not involve W'), float64:
+    dA = scale (dy B)^T x  (r x K),  dB = scale dy^T (x A^T)  (N x r)."""
+    g, xf = _f64(dy, dydtype), _f64(x, xdtype)
+    Af, Bf = _f64(A, abdtype), _f64(B, abdtype)
+    if Af.shape[1] != xf.shape[1] or Bf.shape != (g.shape[1], Af.shape[0]) or g.shape[0] != xf.shape[0]:
+        raise ValueError("dy (M, N), x (M, K), A (r, K) and B (N, r) do not fit together")
     s = float(scale)
     u = g @ Bf
     t = xf @ Af.T
-    dx = dx + s * (u @ Af)
-    dA = s * (u.T @ xf)
-    dB = s * (g.T @ t)
-    return dx, dA, dB
+    return s * (u.T @ xf), s * (g.T @ t)
 
 
 def linear_backward_tolerance(dy, dydtype, x, xdtype, wdeq32, A=None, B=None, abdtype="f32", scale=0.0):
@@ -108,7 +117,16 @@ def linear_backward_tolerance(dy, dydtype, x, xdtype, wdeq32, A=None, B=None, ab
     if A is None or B is None or A.shape[0] == 0:
         return sdx, None, None
     Af, Bf = np.abs(_f64(A, abdtype)), np.abs(_f64(B, abdtype))
+    sdx = sdx + abs(float(scale)) * ((g @ Bf) @ Af)
+    sdA, sdB = adapter_grads_tolerance(dy, dydtype, x, xdtype, A, B, abdtype, scale)
+    return sdx, sdA, sdB
+
+
+def adapter_grads_tolerance(dy, dydtype, x, xdtype, A, B, abdtype, scale):
+    """SdA and SdB of linear_backward_tolerance alone."""
+    g, xf = np.abs(_f64(dy, dydtype)), np.abs(_f64(x, xdtype))
+    Af, Bf = np.abs(_f64(A, abdtype)), np.abs(_f64(B, abdtype))
     s = abs(float(scale))
     U = g @ Bf
     T = xf @ Af.T
-    return sdx + s * (U @ Af), s * (U.T @ xf), s * (g.T @ T)
+    return s * (U.T @ xf), s * (g.T @ T)

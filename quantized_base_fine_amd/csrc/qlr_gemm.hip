@@ -118,6 +118,15 @@ __device__ __forceinline__ void lds_store_f32x4(uint32_t byte_addr, f32x4_t v) {
 __device__ __forceinline__ f32x4_t lds_f32x4(uint32_t byte_addr) {
   return *reinterpret_cast<const __attribute__((address_space(3))) f32x4_t*>((uintptr_t)byte_addr);
 }
+// LDS transpose read of 16-bit elements (ds_read_b64_tr_b16): within each group
+// of 16 lanes, lane i receives element i % 4 of the 8-byte reads of lanes
+// i / 4, i / 4 + 4, i / 4 + 8 and i / 4 + 12, in that order.
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+typedef s16x4_t u16x4_t;
+__device__ __forceinline__ u16x4_t lds_tr16(uint32_t byte_addr) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+      reinterpret_cast<__attribute__((address_space(3))) s16x4_t*>((uintptr_t)byte_addr));
+}
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 
@@ -245,7 +254,17 @@ struct GemmParams {
 
 // ADP: the call has an adapter branch (r > 0).  Calls without one run a separate
 // instantiation (no adapter tail), which also gives it its own kernel name.
-template <int BITS, int YDT, bool ADP>
+//
+// TR: the input gradient of the backward, dx = dy W' + scale u A with
+// u = dy B (float32 partials in t), contracting over W's rows instead of its
+// columns.  The x operand is dy (M x N), the output dx (M x K), the adapter
+// operand A (r x K).  Per 64-row step the producers dequantize a 64 x 128
+// slice of W' (two blocks of each of 64 rows; four lanes read a row's codes
+// together) into a row-major LDS tile whose 16-byte chunks are XOR-swizzled by
+// 5 (row mod 4).  The consumers read the B fragments (8 consecutive rows of one
+// column per lane) with the LDS transpose read, two 4-row reads per fragment;
+// 4 consecutive rows then fall in 4 distinct 64-byte windows of the banks.
+template <int BITS, int YDT, bool ADP, bool TR>
 __global__ __launch_bounds__(512, 1) void k_gemm(GemmParams P, Levels lv) {
   extern __shared__ uint32_t smem[];
   // XCD-aware tile order: workgroup b runs on XCD b % 8
@@ -269,7 +288,10 @@ __global__ __launch_bounds__(512, 1) void k_gemm(GemmParams P, Levels lv) {
   a.r = Lr.r;
   a.scale = Lr.scale;
   a.y = Lr.y;
-  const int64_t N = a.N, K = a.K, nb = K >> 6;
+  const int64_t N = a.N, K = a.K;
+  const int64_t KC = TR ? N : K;  // contraction length (a multiple of 64)
+  const int64_t NO = TR ? K : N;  // output columns
+  const int64_t nb = KC >> 6;
   const int64_t M = P.m_end;
   const int64_t lt = tile - Lr.tile0;
   const int64_t mt = lt / Lr.ntiles, nt = lt % Lr.ntiles;
@@ -293,26 +315,42 @@ __global__ __launch_bounds__(512, 1) void k_gemm(GemmParams P, Levels lv) {
     const int pt = tid - 256;  // 0..255
     const int pw = wave - 4;
     // x of this launch as a buffer resource: reads past its last row return zero
-    const uint16_t* xs_base = reinterpret_cast<const uint16_t*>(a.x) + P.m_begin * K;
+    const uint16_t* xs_base = reinterpret_cast<const uint16_t*>(a.x) + P.m_begin * KC;
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
-        const_cast<uint16_t*>(xs_base), (short)0, (int)((P.m_end - P.m_begin) * K * 2), 0x00020000);
+        const_cast<uint16_t*>(xs_base), (short)0, (int)((P.m_end - P.m_begin) * KC * 2), 0x00020000);
     // staging load j (0..7): tile row 64 pw + 8 j + t (t = lane / 8), 16-byte chunk lane % 8
     const uint32_t t8 = (uint32_t)(lane >> 3);
-    const uint32_t xg0 = (uint32_t)(((m0 - P.m_begin) + 64 * pw + t8) * K + 8 * (lane & 7)) * 2u;
-    const uint32_t xg_row8 = (uint32_t)(8 * K * 2);
+    const uint32_t xg0 = (uint32_t)(((m0 - P.m_begin) + 64 * pw + t8) * KC + 8 * (lane & 7)) * 2u;
+    const uint32_t xg_row8 = (uint32_t)(8 * KC * 2);
     uint32_t xst[2];  // LDS slot of row 64 pw + 8 j + t: swizzle depends on j only through j & 1
 #pragma unroll
     for (int p = 0; p < 2; ++p)
       xst[p] = kXOff + (uint32_t)((64 * pw + t8) * 128) + ((((uint32_t)lane & 7u) ^ swz(t8 + 8u * p)) << 4);
-    // weight row this thread dequantizes: rr = pt / 2, codes [32 dh, 32 dh + 32) of each block
-    const int rr = pt >> 1, dh = pt & 1;
-    const int64_t wn = n0 + rr;
-    const bool wv = wn < N;
-    const int64_t wblk = (wv ? wn : N - 1) * nb;
-    uint32_t wst[4];  // LDS slot of chunk 4 dh + q of row rr
+    // Forward: weight row n0 + rr (rr = pt / 2), codes [32 dh, 32 dh + 32) of
+    // block kb.  TR: weight row 64 kb + rr (rr = pt / 4), codes [32 dh, 32 dh +
+    // 32) of block column n0 / 64 + bq.
+    const int rr = TR ? (pt >> 2) : (pt >> 1), dh = pt & 1, bq = TR ? ((pt >> 1) & 1) : 0;
+    bool wv;
+    int64_t wblk, wstep;
+    if constexpr (TR) {
+      const int64_t nbK = K >> 6, wcol = (n0 >> 6) + bq;
+      wv = wcol < nbK;
+      wblk = (int64_t)rr * nbK + (wv ? wcol : nbK - 1);
+      wstep = 64 * nbK;
+    } else {
+      const int64_t wn = n0 + rr;
+      wv = wn < N;
+      wblk = (wv ? wn : N - 1) * nb;
+      wstep = 1;
+    }
+    uint32_t wst[4];  // LDS slot of the thread's chunk q of row rr
 #pragma unroll
-    for (int q = 0; q < 4; ++q)
-      wst[q] = kWOff + (uint32_t)(rr * 128) + ((((uint32_t)(4 * dh + q)) ^ swz((uint32_t)rr & 15u)) << 4);
+    for (int q = 0; q < 4; ++q) {
+      if constexpr (TR)
+        wst[q] = kWOff + (uint32_t)(rr * 256) + ((((uint32_t)(8 * bq + 4 * dh + q)) ^ (5u * ((uint32_t)rr & 3u))) << 4);
+      else
+        wst[q] = kWOff + (uint32_t)(rr * 128) + ((((uint32_t)(4 * dh + q)) ^ swz((uint32_t)rr & 15u)) << 4);
+    }
     const uint32_t tp = kTOff + (BITS == 8 ? 4u * (lane & 15) : 8u * fr);
 
     struct XS { u32x4_t v[8]; };
@@ -329,7 +367,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm(GemmParams P, Levels lv) {
       for (int j = 0; j < 8; ++j) lds_store_u32x4(xst[j & 1] + buf * kXTile + 1024u * j, st.v[j]);
     };
     auto load_c = [&](CS& st, int64_t kb) {
-      const int64_t blk = wblk + kb;
+      const int64_t blk = wblk + kb * wstep;
       st.c = load_codes32<BITS>(a.codes + blk * (8 * BITS) + dh * (4 * BITS));
       st.q8 = a.q8[blk];
       st.sc = a.cst[blk >> 8];
@@ -446,6 +484,17 @@ __global__ __launch_bounds__(512, 1) void k_gemm(GemmParams P, Levels lv) {
     for (int s = 0; s < 4; ++s) fo[s] = (uint32_t)(fr * 128) + ((((uint32_t)(2 * s + h)) ^ swz((uint32_t)fr & 15u)) << 4);
     const uint32_t xrow0 = (uint32_t)(128 * mh * 128);
     const uint32_t wrow0 = (uint32_t)(64 * nh * 128);
+    // TR: transpose-read address of 16-lane group g, lane sp, for column tile c
+    // (rows 8 h + sp / 4 of the 16-row slice, four columns from 16 (g & 1) + 4 (sp & 3)).
+    uint32_t tbo[2];
+    if constexpr (TR) {
+      const uint32_t g = (uint32_t)lane >> 4, sp = (uint32_t)lane & 15u;
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const uint32_t chunk = 8u * nh + 4u * c + 2u * (g & 1u) + ((sp >> 1) & 1u);
+        tbo[c] = (8u * h + (sp >> 2)) * 256u + ((chunk ^ (5u * (sp >> 2))) << 4) + 8u * (sp & 1u);
+      }
+    }
 
     f32x16_t acc[4][2];
 #pragma unroll
@@ -461,7 +510,17 @@ __global__ __launch_bounds__(512, 1) void k_gemm(GemmParams P, Levels lv) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) fa[slot][i] = lds_u32x4(kXOff + buf * kXTile + xrow0 + fo[s] + 4096u * i);
 #pragma unroll
-      for (int c = 0; c < 2; ++c) fb[slot][c] = lds_u32x4(kWOff + buf * kWTile + wrow0 + fo[s] + 4096u * c);
+      for (int c = 0; c < 2; ++c) {
+        if constexpr (TR) {
+          // rows 16 s + 8 h + {0..3} and {4..7} of the lane's column
+          const uint32_t ad = kWOff + buf * kWTile + tbo[c] + 4096u * s;
+          const u16x4_t lo = lds_tr16(ad), hi = lds_tr16(ad + 1024u);
+          fb[slot][c] = u32x4_t{__builtin_bit_cast(uint2, lo).x, __builtin_bit_cast(uint2, lo).y,
+                                __builtin_bit_cast(uint2, hi).x, __builtin_bit_cast(uint2, hi).y};
+        } else {
+          fb[slot][c] = lds_u32x4(kWOff + buf * kWTile + wrow0 + fo[s] + 4096u * c);
+        }
+      }
     };
     auto mfmas = [&](int slot) {
 #pragma unroll
@@ -511,9 +570,25 @@ __global__ __launch_bounds__(512, 1) void k_gemm(GemmParams P, Levels lv) {
         const int jc = jv ? j0 : 0;
         u32x4_t bf[2];
         float v8[4][8];
-        if (vec) {
+        if constexpr (TR) {
+          // A[j0 + e][k] for the lane's output column k (A is r x K): element loads,
+          // 32 lanes read 64 contiguous bytes of one A row per load
 #pragma unroll
           for (int c = 0; c < 2; ++c) {
+            const int64_t k = n0 + 64 * nh + 32 * c + fr;
+            const bool kv = k < K;
+            const uint16_t* ap = Bl + (kv ? k : 0);
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+              const uint32_t lo = (kv && j0 + 2 * e2 < r) ? ap[(int64_t)(j0 + 2 * e2) * K] : 0u;
+              const uint32_t hi = (kv && j0 + 2 * e2 + 1 < r) ? ap[(int64_t)(j0 + 2 * e2 + 1) * K] : 0u;
+              bf[c][e2] = lo | (hi << 16);
+            }
+          }
+        }
+        if (vec) {
+#pragma unroll
+          for (int c = 0; c < 2 && !TR; ++c) {
             const int64_t n = n0 + 64 * nh + 32 * c + fr;
             const u32x4_t raw = *reinterpret_cast<const u32x4_t*>(Bl + (n < N ? n : N - 1) * (int64_t)r + jc);
             bf[c] = (n < N && jv) ? raw : zero4;
@@ -545,7 +620,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm(GemmParams P, Levels lv) {
           }
         } else {
 #pragma unroll
-          for (int c = 0; c < 2; ++c) {
+          for (int c = 0; c < 2 && !TR; ++c) {
             const int64_t n = n0 + 64 * nh + 32 * c + fr;
             bf[c] = zero4;
             if (n < N) {
@@ -616,7 +691,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm(GemmParams P, Levels lv) {
     constexpr int ES = (YDT == DT_F32) ? 4 : 2;
     constexpr uint32_t RS = 128 * ES + 16;
     constexpr int CPR = 128 * ES / 16;  // 16-byte chunks per row
-    const bool vec_store = ((N * ES) % 16) == 0;
+    const bool vec_store = ((NO * ES) % 16) == 0;
     char* y = reinterpret_cast<char*>(a.y);
 #pragma unroll 4
     for (int idx = tid; idx < 256 * CPR; idx += 512) {
@@ -624,9 +699,9 @@ __global__ __launch_bounds__(512, 1) void k_gemm(GemmParams P, Levels lv) {
       const int64_t gr = m0 + row;
       const int64_t gc = n0 + ch * (16 / ES);
       const u32x4_t v = lds_u32x4((uint32_t)row * RS + (uint32_t)ch * 16);
-      if (gr < M && gc < N) {
-        char* dst = y + (gr * N + gc) * ES;
-        if (vec_store && gc + 16 / ES <= N) {
+      if (gr < M && gc < NO) {
+        char* dst = y + (gr * NO + gc) * ES;
+        if (vec_store && gc + 16 / ES <= NO) {
           *reinterpret_cast<u32x4_t*>(dst) = v;
         } else {
 #pragma unroll
@@ -634,7 +709,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm(GemmParams P, Levels lv) {
             // (copy the element out first: bit-casting a vector-element lvalue
             // directly reads element 0)
             const uint32_t ve = v[e];
-            if (gc + e < N) {
+            if (gc + e < NO) {
               if constexpr (YDT == DT_F32) reinterpret_cast<float*>(dst)[e] = __uint_as_float(ve);
               else reinterpret_cast<uint16_t*>(dst)[e] = (uint16_t)(v[e >> 1] >> (16 * (e & 1)));
             }
@@ -653,10 +728,10 @@ int64_t gemm_max_rows(int64_t K) {
   return std::max<int64_t>(BM, ((int64_t(1) << 31) - 1) / row_bytes / BM * BM);
 }
 
-template <int BITS, int YDT, bool ADP>
+template <int BITS, int YDT, bool ADP, bool TR>
 hipError_t launch_gemm_t(const LinearArgs* ls, int n, const Levels& lv, hipStream_t s) {
   const size_t shmem = gemm_lds_bytes<BITS>();
-  auto kern = k_gemm<BITS, YDT, ADP>;
+  auto kern = k_gemm<BITS, YDT, ADP, TR>;
   static bool attr = false;
   if (!attr) {
     // the kernel addresses LDS from 0: it must not have static LDS
@@ -673,8 +748,9 @@ hipError_t launch_gemm_t(const LinearArgs* ls, int n, const Levels& lv, hipStrea
   const int64_t M = ls[0].M;
   int64_t max_rows = INT64_MAX;
   for (int i = 0; i < n; ++i) {
-    const int64_t mr = gemm_max_rows(ls[i].K);
+    const int64_t mr = gemm_max_rows(TR ? ls[i].N : ls[i].K);
     if (mr == 0 || ls[i].M != M) return hipErrorInvalidValue;
+    if (TR && (ls[i].N % 64 != 0 || ls[i].K % 64 != 0)) return hipErrorInvalidValue;
     max_rows = std::min(max_rows, mr);
   }
   for (int64_t mb = 0; mb < M; mb += max_rows) {
@@ -700,7 +776,7 @@ hipError_t launch_gemm_t(const LinearArgs* ls, int n, const Levels& lv, hipStrea
       L.r = a.r;
       L.t_splits = a.t_splits;
       L.scale = a.scale;
-      L.ntiles = (int32_t)((a.N + BN - 1) / BN);
+      L.ntiles = (int32_t)(((TR ? a.K : a.N) + BN - 1) / BN);
       L.tile0 = t0;
       t0 += P.mtiles * L.ntiles;
     }
@@ -713,16 +789,16 @@ hipError_t launch_gemm_t(const LinearArgs* ls, int n, const Levels& lv, hipStrea
   return hipSuccess;
 }
 
-template <int BITS>
+template <int BITS, bool TR>
 hipError_t launch_gemm_b(const LinearArgs* ls, int n, const Levels& lv, hipStream_t s) {
   bool adp = false;
   for (int i = 0; i < n; ++i) adp = adp || ls[i].r > 0;
   if (adp) {
-    if (ls[0].ydt == DT_F32) return launch_gemm_t<BITS, DT_F32, true>(ls, n, lv, s);
-    return launch_gemm_t<BITS, DT_BF16, true>(ls, n, lv, s);
+    if (ls[0].ydt == DT_F32) return launch_gemm_t<BITS, DT_F32, true, TR>(ls, n, lv, s);
+    return launch_gemm_t<BITS, DT_BF16, true, TR>(ls, n, lv, s);
   }
-  if (ls[0].ydt == DT_F32) return launch_gemm_t<BITS, DT_F32, false>(ls, n, lv, s);
-  return launch_gemm_t<BITS, DT_BF16, false>(ls, n, lv, s);
+  if (ls[0].ydt == DT_F32) return launch_gemm_t<BITS, DT_F32, false, TR>(ls, n, lv, s);
+  return launch_gemm_t<BITS, DT_BF16, false, TR>(ls, n, lv, s);
 }
 
 }  // namespace
@@ -733,15 +809,26 @@ hipError_t launch_gemm(const LinearArgs& a, const Levels& lv, hipStream_t s) {
 
 int gemm_group_max() { return kGroupMax; }
 
+int64_t gemm_max_rows_of(int64_t KC) { return gemm_max_rows(KC); }
+
 hipError_t launch_gemm_group(const LinearArgs* ls, int n, const Levels& lv, hipStream_t s) {
   if (n <= 0) return hipSuccess;
   for (int i = 1; i < n; ++i)
     if (ls[i].bits != ls[0].bits || ls[i].ydt != ls[0].ydt) return hipErrorInvalidValue;
   switch (ls[0].bits) {
-    case 2: return launch_gemm_b<2>(ls, n, lv, s);
-    case 3: return launch_gemm_b<3>(ls, n, lv, s);
-    case 4: return launch_gemm_b<4>(ls, n, lv, s);
-    default: return launch_gemm_b<8>(ls, n, lv, s);
+    case 2: return launch_gemm_b<2, false>(ls, n, lv, s);
+    case 3: return launch_gemm_b<3, false>(ls, n, lv, s);
+    case 4: return launch_gemm_b<4, false>(ls, n, lv, s);
+    default: return launch_gemm_b<8, false>(ls, n, lv, s);
+  }
+}
+
+hipError_t launch_gemm_dx(const LinearArgs& a, const Levels& lv, hipStream_t s) {
+  switch (a.bits) {
+    case 2: return launch_gemm_b<2, true>(&a, 1, lv, s);
+    case 3: return launch_gemm_b<3, true>(&a, 1, lv, s);
+    case 4: return launch_gemm_b<4, true>(&a, 1, lv, s);
+    default: return launch_gemm_b<8, true>(&a, 1, lv, s);
   }
 }
 

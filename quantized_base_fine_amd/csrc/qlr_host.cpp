@@ -121,6 +121,28 @@ size_t linear_ws_bytes(int64_t M, int64_t K, int32_t r) {
   return ((parts * (size_t)M * (size_t)r * sizeof(float)) + 255) & ~(size_t)255;
 }
 
+// Workspace of one backward call, as four 256-byte-aligned regions: t = x A^T
+// and u = dy B as float32 partial splits (the bf16 counts bound the others),
+// B transposed (r x N, 4-byte elements bound both dtypes), and the float32
+// partials of the adapter gradients.
+struct BwdLayout {
+  size_t t, u, bt, part, total;
+};
+BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K, int32_t r) {
+  BwdLayout L{0, 0, 0, 0, 0};
+  if (r <= 0) return L;
+  auto up = [](size_t b) { return (b + 255) & ~(size_t)255; };
+  const size_t mr = (size_t)std::max<int64_t>(M, 0) * (size_t)r * sizeof(float);
+  const size_t st = M > 0 ? (size_t)qlr::lora_t_splits(M, K, qlr::DT_BF16, qlr::DT_BF16) : 0;
+  const size_t su = M > 0 ? (size_t)qlr::lora_t_splits(M, N, qlr::DT_BF16, qlr::DT_BF16) : 0;
+  L.t = 0;
+  L.u = L.t + up(st * mr);
+  L.bt = L.u + up(su * mr);
+  L.part = L.bt + up((size_t)r * (size_t)N * 4);
+  L.total = L.part + up(M > 0 ? qlr::grad_partial_floats(M, N, K, r) * sizeof(float) : 0);
+  return L;
+}
+
 // choose the kernel family for a linear call
 qlr_status pick_path(int64_t M, qlr_dtype xdt, qlr_dtype abdt, int32_t r, qlr_path* out) {
   const bool bf16_ok = xdt == QLR_BF16 && (r == 0 || abdt == QLR_BF16);
@@ -291,8 +313,13 @@ qlr_status qlr_workspace_bytes(qlr_op op, int64_t M, int64_t N, int64_t K, int32
     *bytes = 256;
     return QLR_OK;
   }
-  if (op != QLR_OP_LINEAR) return fail(QLR_ERR_SHAPE, "unknown op %d", (int)op);
+  if (op != QLR_OP_LINEAR && op != QLR_OP_LINEAR_BWD) return fail(QLR_ERR_SHAPE, "unknown op %d", (int)op);
   if (M < 0 || r < 0) return fail(QLR_ERR_SHAPE, "negative M or r");
+  if (op == QLR_OP_LINEAR_BWD) {
+    if (N < 0 || K < 0) return fail(QLR_ERR_SHAPE, "negative N or K");
+    *bytes = bwd_layout(M, N, K, r).total;
+    return QLR_OK;
+  }
   *bytes = linear_ws_bytes(M, K, r);
   return QLR_OK;
 }
@@ -440,6 +467,119 @@ qlr_status qlr_linear_fwd_mixed(const qlr_layer* layers, int32_t n, int64_t M, q
         if (e != hipSuccess) return hip_fail(e, "grouped linear launch");
       }
     }
+  return QLR_OK;
+}
+
+qlr_status qlr_linear_bwd(const void* dy, qlr_dtype dydt, const void* x, qlr_dtype xdt, int64_t M,
+                          const qlr_qweight* w, const void* A, const void* B, qlr_dtype abdt, int32_t r,
+                          float scale, void* dx, qlr_dtype dxdt, float* dA, float* dB, void* ws,
+                          size_t ws_bytes, void* stream) {
+  qlr_status st = check_qweight(w);
+  if (st != QLR_OK) return st;
+  if (M < 0) return fail(QLR_ERR_SHAPE, "M < 0");
+  if (r < 0) return fail(QLR_ERR_SHAPE, "r < 0");
+  if (w->cols % QLR_BLOCK != 0) return fail(QLR_ERR_SHAPE, "cols %lld is not a multiple of 64", (long long)w->cols);
+  if (w->rows == 0 || w->cols == 0) return fail(QLR_ERR_SHAPE, "empty weight");
+  if (!(dydt == QLR_F32 || dydt == QLR_BF16)) return fail(QLR_ERR_DTYPE, "dy dtype must be f32 or bf16");
+  if (!(dxdt == QLR_F32 || dxdt == QLR_BF16)) return fail(QLR_ERR_DTYPE, "dx dtype must be f32 or bf16");
+  if (r > 0) {
+    if (!(abdt == QLR_F32 || abdt == QLR_BF16)) return fail(QLR_ERR_DTYPE, "adapter dtype must be f32 or bf16");
+    if (xdt != dydt) return fail(QLR_ERR_DTYPE, "x and dy must share a dtype when r > 0");
+    if (!A || !B || !dA || !dB) return fail(QLR_ERR_NULL, "A, B, dA or dB is NULL with r > 0");
+    if (!aligned16(A) || !aligned16(B) || !aligned16(dA) || !aligned16(dB))
+      return fail(QLR_ERR_ALIGN, "A, B, dA and dB must be 16-byte aligned");
+  }
+  const int64_t N = w->rows, K = w->cols;
+  if (M > 0) {
+    if (!dy) return fail(QLR_ERR_NULL, "dy is NULL");
+    if (r > 0 && !x) return fail(QLR_ERR_NULL, "x is NULL with r > 0");
+    if (!aligned16(dy) || (dx && !aligned16(dx)) || (r > 0 && !aligned16(x)))
+      return fail(QLR_ERR_ALIGN, "dy, x and dx must be 16-byte aligned");
+  }
+  // no output may overlap an input or another output
+  {
+    std::vector<std::pair<uintptr_t, uintptr_t>> outs, ins;
+    auto span = [](const void* p, size_t n) {
+      const uintptr_t a = reinterpret_cast<uintptr_t>(p);
+      return std::make_pair(a, a + n);
+    };
+    if (M > 0 && dx) outs.push_back(span(dx, (size_t)(M * K) * dtype_size(dxdt)));
+    if (r > 0) {
+      outs.push_back(span(dA, (size_t)r * (size_t)K * 4));
+      outs.push_back(span(dB, (size_t)r * (size_t)N * 4));
+      ins.push_back(span(A, (size_t)r * (size_t)K * dtype_size(abdt)));
+      ins.push_back(span(B, (size_t)r * (size_t)N * dtype_size(abdt)));
+      if (M > 0) ins.push_back(span(x, (size_t)(M * K) * dtype_size(xdt)));
+    }
+    if (M > 0) ins.push_back(span(dy, (size_t)(M * N) * dtype_size(dydt)));
+    auto overlap = [](const std::pair<uintptr_t, uintptr_t>& p, const std::pair<uintptr_t, uintptr_t>& q) {
+      return p.first < q.second && q.first < p.second;
+    };
+    for (size_t i = 0; i < outs.size(); ++i) {
+      for (size_t j = i + 1; j < outs.size(); ++j)
+        if (overlap(outs[i], outs[j])) return fail(QLR_ERR_ALIAS, "two outputs overlap");
+      for (const auto& in : ins)
+        if (overlap(outs[i], in)) return fail(QLR_ERR_ALIAS, "an output overlaps an input");
+    }
+  }
+  const BwdLayout lay = bwd_layout(M, N, K, r);
+  if (lay.total > 0 && (!ws || ws_bytes < lay.total))
+    return fail(QLR_ERR_WORKSPACE, "workspace of %zu bytes required, got %zu", lay.total, ws ? ws_bytes : (size_t)0);
+  if (lay.total > 0 && !aligned16(ws)) return fail(QLR_ERR_ALIGN, "workspace must be 16-byte aligned");
+  // kernel family: the transposed bf16 GEMM needs bf16 operands and whole 64-row steps
+  const bool bf16_ok = dydt == QLR_BF16 && (r == 0 || (xdt == QLR_BF16 && abdt == QLR_BF16)) && N % 64 == 0;
+  qlr_path path = t_path;
+  if (path == QLR_PATH_AUTO) path = bf16_ok ? QLR_PATH_GEMM : QLR_PATH_F32;
+  if (path == QLR_PATH_GEMV) path = QLR_PATH_GEMM;
+  if (path == QLR_PATH_GEMM && !bf16_ok)
+    return fail(QLR_ERR_PATH, "the MFMA backward needs bf16 dy, x and adapters and rows %% 64 == 0");
+  if (path == QLR_PATH_GEMM && M > 0 && qlr::gemm_max_rows_of(N) == 0)
+    return fail(QLR_ERR_SHAPE, "rows too large for the MFMA backward");
+
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* wsp = reinterpret_cast<char*>(ws);
+  float* tws = r > 0 ? reinterpret_cast<float*>(wsp + lay.t) : nullptr;
+  float* uws = r > 0 ? reinterpret_cast<float*>(wsp + lay.u) : nullptr;
+  const int st_t = M > 0 ? qlr::lora_t_splits(M, K, (int)xdt, (int)abdt) : 1;
+  const int st_u = M > 0 ? qlr::lora_t_splits(M, N, (int)dydt, (int)abdt) : 1;
+  hipError_t e = hipSuccess;
+  if (r > 0 && M > 0) {
+    e = qlr::launch_transpose_nr(B, (int)abdt, N, r, wsp + lay.bt, s);
+    if (e != hipSuccess) return hip_fail(e, "adapter transpose launch");
+    e = qlr::launch_lora_t(x, (int)xdt, M, K, A, (int)abdt, r, tws, st_t, s);
+    if (e != hipSuccess) return hip_fail(e, "adapter product (x A^T) launch");
+    e = qlr::launch_lora_t(dy, (int)dydt, M, N, wsp + lay.bt, (int)abdt, r, uws, st_u, s);
+    if (e != hipSuccess) return hip_fail(e, "adapter product (dy B) launch");
+  }
+  if (dx && M > 0) {
+    qlr::LinearArgs a;
+    a.x = dy;
+    a.xdt = (int)dydt;
+    a.M = M;
+    a.N = N;
+    a.K = K;
+    a.bits = w->bits;
+    a.codes = reinterpret_cast<const uint8_t*>(w->codes);
+    a.q8 = w->absmax_q8;
+    a.cst = w->absmax_c;
+    a.t = uws;
+    a.t_splits = st_u;
+    a.A = nullptr;
+    a.B = A;
+    a.abdt = (int)abdt;
+    a.r = r;
+    a.scale = scale;
+    a.y = dx;
+    a.ydt = (int)dxdt;
+    const qlr::Levels lv = levels_arg(w->bits);
+    e = path == QLR_PATH_F32 ? qlr::launch_dx_f32(a, lv, s) : qlr::launch_gemm_dx(a, lv, s);
+    if (e != hipSuccess) return hip_fail(e, "input-gradient launch");
+  }
+  if (r > 0) {
+    e = qlr::launch_lora_grads(uws, st_u, tws, st_t, x, dy, (int)xdt, M, N, K, r, scale, dA, dB,
+                               reinterpret_cast<float*>(wsp + lay.part), s);
+    if (e != hipSuccess) return hip_fail(e, "adapter-gradient launch");
+  }
   return QLR_OK;
 }
 

@@ -24,7 +24,9 @@ hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* q8, const floa
 
 // Number of K-splits of the adapter product t = x A^T for M rows and K columns:
 // the product is written as `splits` partial sums p[s][M][r] (float32) that the
-// consumers add in split order.
+// consumers add in split order.  K need not be a multiple of 64 (the backward's
+// u = dy B contracts over the weight's rows); such products run one split on
+// the float32 kernel.
 int lora_t_splits(int64_t M, int64_t K, int xdt, int abdt);
 
 // p[s][m][j] = sum over split s's K range of x[m,k] A[j,k]  (float32 partials).
@@ -76,5 +78,25 @@ hipError_t launch_gemm(const LinearArgs& a, const Levels& lv, hipStream_t s);
 // output dtype in one launch (mixed stacks); lv holds that width's levels.
 int gemm_group_max();
 hipError_t launch_gemm_group(const LinearArgs* ls, int n, const Levels& lv, hipStream_t s);
+
+// ---- backward (adapter training)
+// Input gradient dx = dy W' + scale u A on the transposed bf16 GEMM: a.x = dy
+// (M x N bf16), a.y = dx (M x K), a.t = u partials (t_splits x M x r float32),
+// a.B = A (r x K bf16), a.N / a.K the weight's rows / columns (both multiples
+// of 64).
+hipError_t launch_gemm_dx(const LinearArgs& a, const Levels& lv, hipStream_t s);
+// Rows of x per GEMM launch for a contraction length KC (0: KC too large).
+int64_t gemm_max_rows_of(int64_t KC);
+// The same on the float32 path (any dtypes, any N).
+hipError_t launch_dx_f32(const LinearArgs& a, const Levels& lv, hipStream_t s);
+// Bt (r x N) = B^T for B (N x r) of dtype dt.
+hipError_t launch_transpose_nr(const void* B, int dt, int64_t N, int r, void* Bt, hipStream_t s);
+// dA = scale u^T x (r x K) and dB = scale dy^T t (N x r), float32, from the
+// float32 partials of u (M x r) and t (M x r); x and dy share dtype qdt.
+// part: grad_partial_floats(M, N, K, r) floats of scratch.
+size_t grad_partial_floats(int64_t M, int64_t N, int64_t K, int r);
+hipError_t launch_lora_grads(const float* u, int u_splits, const float* t, int t_splits, const void* x,
+                             const void* dy, int qdt, int64_t M, int64_t N, int64_t K, int r, float scale,
+                             float* dA, float* dB, float* part, hipStream_t s);
 
 }  // namespace qlr

@@ -259,7 +259,7 @@ hipError_t launch_f32_b1(const LinearArgs& a, const Levels& lv, hipStream_t s) {
 }  // namespace
 
 int lora_t_splits(int64_t M, int64_t K, int xdt, int abdt) {
-  if (!(xdt == DT_BF16 && abdt == DT_BF16) || M > 16) return 1;
+  if (!(xdt == DT_BF16 && abdt == DT_BF16) || M > 16 || K % 64 != 0) return 1;
   const int64_t steps = K / 32, mtiles = (M + 15) / 16;
   int64_t s = std::min<int64_t>(steps / 4, (256 + mtiles - 1) / mtiles);
   s = std::min<int64_t>(s, 64);
@@ -269,12 +269,13 @@ int lora_t_splits(int64_t M, int64_t K, int xdt, int abdt) {
 hipError_t launch_lora_t(const void* x, int xdt, int64_t M, int64_t K, const void* A, int abdt,
                          int r, float* t, int splits, hipStream_t s) {
   if (M == 0 || r == 0) return hipSuccess;
-  if (xdt == DT_BF16 && abdt == DT_BF16 && M > 16) {
+  const bool mfma = xdt == DT_BF16 && abdt == DT_BF16 && K % 64 == 0;
+  if (mfma && M > 16) {
     if (splits != 1) return hipErrorInvalidValue;
     const LoraTItem it{x, A, t, K, r};
     return launch_lora_t_group(&it, 1, M, s);
   }
-  if (xdt == DT_BF16 && abdt == DT_BF16) {
+  if (mfma) {
     dim3 grid((unsigned)((M + 15) / 16), (unsigned)((r + 63) / 64), (unsigned)splits);
     hipLaunchKernelGGL(k_lora_t_mfma, grid, dim3(256), 0, s, reinterpret_cast<const uint16_t*>(x), M,
                        K, reinterpret_cast<const uint16_t*>(A), r, t);
@@ -286,8 +287,10 @@ hipError_t launch_lora_t(const void* x, int xdt, int64_t M, int64_t K, const voi
     hipLaunchKernelGGL((k_lora_t_valu<DT_F32, DT_F32>), grid, block, 0, s, x, M, K, A, r, t);
   else if (xdt == DT_F32)
     hipLaunchKernelGGL((k_lora_t_valu<DT_F32, DT_BF16>), grid, block, 0, s, x, M, K, A, r, t);
-  else
+  else if (abdt == DT_F32)
     hipLaunchKernelGGL((k_lora_t_valu<DT_BF16, DT_F32>), grid, block, 0, s, x, M, K, A, r, t);
+  else
+    hipLaunchKernelGGL((k_lora_t_valu<DT_BF16, DT_BF16>), grid, block, 0, s, x, M, K, A, r, t);
   return hipGetLastError();
 }
 

@@ -23,7 +23,7 @@ GROUP = 256
 
 QLR_F32, QLR_F16, QLR_BF16 = 0, 1, 2
 PATH_AUTO, PATH_F32, PATH_GEMV, PATH_GEMM = 0, 1, 2, 3
-OP_QUANTIZE, OP_LINEAR = 0, 1
+OP_QUANTIZE, OP_LINEAR, OP_LINEAR_BWD = 0, 1, 2
 
 STATUS = {
     0: "QLR_OK", 1: "QLR_ERR_NULL", 2: "QLR_ERR_SHAPE", 3: "QLR_ERR_DTYPE", 4: "QLR_ERR_BITS",
@@ -75,6 +75,10 @@ EXPORTS = {
                                  C.c_void_p, C.c_int, C.c_void_p, C.c_size_t, C.c_void_p]),
     "qlr_linear_fwd_mixed": (C.c_int, [C.POINTER(CLayer), C.c_int32, C.c_int64, C.c_int, C.c_int,
                                        C.c_int, C.c_void_p, C.c_size_t, C.c_void_p]),
+    "qlr_linear_bwd": (C.c_int, [C.c_void_p, C.c_int, C.c_void_p, C.c_int, C.c_int64,
+                                 C.POINTER(CQWeight), C.c_void_p, C.c_void_p, C.c_int, C.c_int32,
+                                 C.c_float, C.c_void_p, C.c_int, C.c_void_p, C.c_void_p,
+                                 C.c_void_p, C.c_size_t, C.c_void_p]),
     "qlr_force_path": (C.c_int, [C.c_int]),
 }
 
@@ -325,3 +329,51 @@ class MixedCall:
 def linear_mixed(entries: Sequence[dict], out_dtype=None, ws=None):
     """Independent linears with per-entry (bits, rank).  Each entry: dict(x, qw, A, B, scale[, y])."""
     return MixedCall(entries, out_dtype=out_dtype, ws=ws)()
+
+
+class LinearBwdCall:
+    """A prepared ``qlr_linear_bwd`` call: dx = dy W' + scale (dy B) A,
+    dA = scale (dy B)^T x, dB = scale dy^T (x A^T).  dy (M, N) and x (M, K) on the
+    GPU; dA and dB are float32; ``need_dx=False`` skips the input gradient.
+    Marshalled once (the stream current at construction is used); the tensors
+    are kept alive by the object."""
+
+    def __init__(self, dy, x, qw: QWeight, A=None, B=None, scale: float = 0.0, dx_dtype=None,
+                 need_dx: bool = True, dx=None, dA=None, dB=None, ws=None):
+        torch = _torch()
+        _require_cuda(dy, x, A, B)
+        M = dy.shape[0]
+        r = 0 if A is None else A.shape[0]
+        if dy.shape[1] != qw.rows or (x is not None and x.shape != (M, qw.cols)):
+            raise ValueError("dy must be (M, N) and x (M, K) for an N x K weight")
+        if r > 0 and (A.shape != (r, qw.cols) or B.shape != (qw.rows, r) or A.dtype != B.dtype):
+            raise ValueError("A must be (r, K) and B (N, r) with one dtype")
+        dev = dy.device
+        if need_dx and dx is None:
+            dx = torch.empty((M, qw.cols), dtype=dx_dtype or dy.dtype, device=dev)
+        self.dx = dx if need_dx else None
+        if r > 0:
+            self.dA = dA if dA is not None else torch.empty((r, qw.cols), dtype=torch.float32, device=dev)
+            self.dB = dB if dB is not None else torch.empty((qw.rows, r), dtype=torch.float32, device=dev)
+        else:
+            self.dA = self.dB = None
+        need = workspace_bytes(OP_LINEAR_BWD, M, qw.rows, qw.cols, r)
+        if ws is None and need > 0:
+            ws = torch.empty(need, dtype=torch.uint8, device=dev)
+        self._keep = (dy, x, qw, A, B, ws)
+        self._cw = qw.c_struct()
+        abdt = _dt(A) if r > 0 else QLR_BF16
+        xdt = _dt(x) if x is not None else _dt(dy)
+        self._args = (dy.data_ptr(), _dt(dy), _ptr(x), xdt, M, C.byref(self._cw), _ptr(A), _ptr(B), abdt, r,
+                      float(scale), _ptr(self.dx), _dt(self.dx) if self.dx is not None else QLR_F32,
+                      _ptr(self.dA), _ptr(self.dB), _ptr(ws), 0 if ws is None else ws.numel(), _stream(dev))
+        self._fn = lib().qlr_linear_bwd
+
+    def __call__(self):
+        check(self._fn(*self._args))
+        return self.dx, self.dA, self.dB
+
+
+def linear_bwd(dy, x, qw: QWeight, A=None, B=None, scale: float = 0.0, dx_dtype=None, need_dx: bool = True):
+    """Gradients (dx, dA, dB) of the layer for an upstream gradient dy; see LinearBwdCall."""
+    return LinearBwdCall(dy, x, qw, A, B, scale, dx_dtype=dx_dtype, need_dx=need_dx)()

@@ -94,3 +94,43 @@ def check_linear(y_gpu, lin, wdeq_rows, rows, ydt="f32", ms=None):
     assert np.all(np.isfinite(got))
     assert np.all(err <= bound), f"max err/bound {ratio:.3f}"
     return ratio
+
+
+def check_backward(got, lin, dy, wdeq, ks=None, dxdt="f32"):
+    """Per-element bound 1e-3 * S + 1e-5 on dx, dA and dB (+ half a bf16 ulp for a bf16 dx).
+
+    ``got`` = (dx, dA, dB) as float32 numpy arrays (dA, dB None when r == 0);
+    ``wdeq``: the oracle's dequantized W' (all rows), restricted to the columns
+    ``ks`` when given (dx and dA are then checked on those columns only, dB in
+    full).  Returns the worst ratio error / bound of each gradient.
+    """
+    dx, dA, dB = got
+    cols = slice(None) if ks is None else ks
+    xs = lin.x[:, cols]
+    As = None if lin.r == 0 else lin.A[:, cols]
+    ref = oracle.linear_backward(dy, lin.xdtype, xs, lin.xdtype, wdeq, As, lin.B, lin.abdtype, lin.scale)
+    S = oracle.linear_backward_tolerance(dy, lin.xdtype, xs, lin.xdtype, wdeq, As, lin.B, lin.abdtype, lin.scale)
+    ratios = []
+
+    def one(g, r_, s_, extra=0.0):
+        bound = 1e-3 * s_ + 1e-5 + extra * np.abs(r_)
+        g = g.astype(np.float64)
+        assert g.shape == r_.shape
+        assert np.all(np.isfinite(g))
+        err = np.abs(g - r_)
+        ratio = float(np.max(err / bound)) if err.size else 0.0
+        assert np.all(err <= bound), f"max err/bound {ratio:.3f}"
+        ratios.append(ratio)
+
+    if dx is not None:
+        one(dx[:, cols], ref[0], S[0], 2.0 ** -9 if dxdt == "bf16" else 0.0)
+    if lin.r > 0:
+        one(dA[:, cols], ref[1], S[1])
+        if ks is None:
+            one(dB, ref[2], S[2])
+        else:
+            rA, rB = oracle.adapter_grads(dy, lin.xdtype, lin.x, lin.xdtype, lin.A, lin.B, lin.abdtype, lin.scale)
+            sA, sB = oracle.adapter_grads_tolerance(dy, lin.xdtype, lin.x, lin.xdtype, lin.A, lin.B,
+                                                    lin.abdtype, lin.scale)
+            one(dB, rB, sB)
+    return ratios

@@ -157,3 +157,49 @@ def test_mixed_alias_detection():
     arr[1] = qlr.CLayer(C.pointer(_qw(bits=7)), 0x300000, 0, 0, 0, 0.0, 0x500000)
     assert qlr.STATUS[lib.qlr_linear_fwd_mixed(arr, 2, 4, qlr.QLR_BF16, qlr.QLR_BF16, qlr.QLR_F32,
                                                None, 0, None)] == "QLR_ERR_BITS"
+
+
+def _bwd(w, dy=0x100000, dydt=qlr.QLR_BF16, x=0x200000, xdt=qlr.QLR_BF16, M=4, A=0x300000, B=0x400000,
+         abdt=qlr.QLR_BF16, r=4, dx=0x500000, dxdt=qlr.QLR_F32, dA=0x600000, dB=0x700000, ws=0x800000,
+         wsb=1 << 20):
+    lib = qlr.lib()
+    return qlr.STATUS[lib.qlr_linear_bwd(dy, dydt, x, xdt, M, C.byref(w), A, B, abdt, r, 1.0, dx, dxdt,
+                                         dA, dB, ws, wsb, None)]
+
+
+def test_backward_validation_errors():
+    assert _bwd(_qw(bits=5)) == "QLR_ERR_BITS"
+    assert _bwd(_qw(cols=100)) == "QLR_ERR_SHAPE"
+    assert _bwd(_qw(), M=-1) == "QLR_ERR_SHAPE"
+    assert _bwd(_qw(), dy=0) == "QLR_ERR_NULL"
+    assert _bwd(_qw(), x=0) == "QLR_ERR_NULL"
+    assert _bwd(_qw(), dA=0) == "QLR_ERR_NULL"
+    assert _bwd(_qw(), B=0) == "QLR_ERR_NULL"
+    assert _bwd(_qw(), dx=0x500008) == "QLR_ERR_ALIGN"
+    assert _bwd(_qw(), dydt=qlr.QLR_F16) == "QLR_ERR_DTYPE"
+    assert _bwd(_qw(), xdt=qlr.QLR_F32) == "QLR_ERR_DTYPE"  # x and dy must share a dtype
+    assert _bwd(_qw(), dxdt=9) == "QLR_ERR_DTYPE"
+    assert _bwd(_qw(), dA=0x100000) == "QLR_ERR_ALIAS"  # dA on top of dy
+    assert _bwd(_qw(), dB=0x600000 + 256) == "QLR_ERR_ALIAS"  # dB inside dA
+    assert _bwd(_qw(), dx=0x200000) == "QLR_ERR_ALIAS"  # dx on top of x
+    assert _bwd(_qw(), ws=0) == "QLR_ERR_WORKSPACE"
+    assert _bwd(_qw(), wsb=64) == "QLR_ERR_WORKSPACE"
+    # no adapter: x is not read and no workspace is needed; M = 0 with r = 0 launches nothing
+    assert _bwd(_qw(), M=0, r=0, x=0, dy=0, dx=0, A=0, B=0, dA=0, dB=0, ws=0) == "QLR_OK"
+    lib = qlr.lib()
+    try:
+        lib.qlr_force_path(qlr.PATH_GEMM)
+        assert _bwd(_qw(rows=65)) == "QLR_ERR_PATH"  # the MFMA backward takes whole 64-row steps
+        assert _bwd(_qw(), abdt=qlr.QLR_F32) == "QLR_ERR_PATH"
+    finally:
+        lib.qlr_force_path(qlr.PATH_AUTO)
+
+
+def test_backward_workspace_sizes():
+    assert qlr.workspace_bytes(qlr.OP_LINEAR_BWD, 2048, 4096, 4096, 0) == 0
+    small = qlr.workspace_bytes(qlr.OP_LINEAR_BWD, 3, 64, 128, 4)
+    # t and u (one split each), B transposed (r x N float32-sized), no gradient partials at M = 3
+    assert small == 256 + 256 + 1024
+    big = qlr.workspace_bytes(qlr.OP_LINEAR_BWD, 2048, 4096, 4096, 16)
+    assert big >= 2 * 2048 * 16 * 4 + 16 * 4096 * 4
+    assert big % 256 == 0

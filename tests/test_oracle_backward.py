@@ -119,3 +119,29 @@ def test_tolerance_sums_bound_and_are_tight_on_nonnegative_inputs():
     S = oracle.linear_backward_tolerance(pos[0], "f32", pos[1], "f32", pos[2], pos[3], pos[4], "f32", s)
     for a, b in zip(g, S):
         assert np.allclose(a, b, rtol=1e-13, atol=0)
+
+
+def test_adapter_grads_alone_need_no_weight():
+    """dA and dB do not involve W': the same values with any base weight, and from adapter_grads."""
+    dy, x, w, A, B = _case(6, M=3, N=4, K=7, r=2)
+    _, dA, dB = oracle.linear_backward(dy, "f32", x, "f32", w, A, B, "f32", 0.5)
+    _, dA2, dB2 = oracle.linear_backward(dy, "f32", x, "f32", 3 * w + 1, A, B, "f32", 0.5)
+    dA3, dB3 = oracle.adapter_grads(dy, "f32", x, "f32", A, B, "f32", 0.5)
+    assert np.array_equal(dA, dA2) and np.array_equal(dB, dB2)
+    assert np.array_equal(dA, dA3) and np.array_equal(dB, dB3)
+    S = oracle.linear_backward_tolerance(dy, "f32", x, "f32", w, A, B, "f32", 0.5)
+    S2 = oracle.adapter_grads_tolerance(dy, "f32", x, "f32", A, B, "f32", 0.5)
+    assert np.array_equal(S[1], S2[0]) and np.array_equal(S[2], S2[1])
+
+
+def test_column_restriction_of_the_input_gradient():
+    """dx[:, ks] and dA[:, ks] only need the columns ks of W', A and x (what sampled checks use)."""
+    rng = np.random.default_rng(8)
+    M, N, K, r, s = 4, 6, 40, 3, 0.5
+    dy, x, w, A, B = (rng.standard_normal(sh).astype(np.float32)
+                      for sh in ((M, N), (M, K), (N, K), (r, K), (N, r)))
+    full = oracle.linear_backward(dy, "f32", x, "f32", w, A, B, "f32", s)
+    ks = [0, 7, 39]
+    part = oracle.linear_backward(dy, "f32", x[:, ks], "f32", w[:, ks], A[:, ks], B, "f32", s)
+    assert np.allclose(full[0][:, ks], part[0], rtol=1e-13, atol=0)
+    assert np.allclose(full[1][:, ks], part[1], rtol=1e-13, atol=0)

@@ -24,7 +24,7 @@ from typing import List, Optional, Tuple
 import numpy as np
 
 # tensor ids inside one config
-T_W, T_A, T_B, T_X, T_OUTLIER, T_DRAW = 0, 1, 2, 3, 4, 5
+T_W, T_A, T_B, T_X, T_OUTLIER, T_DRAW, T_DY = 0, 1, 2, 3, 4, 5, 6
 
 BITS_CHOICES = (2, 3, 4, 8)
 RANK_CHOICES = (4, 8, 16, 32, 64)
@@ -75,6 +75,8 @@ class Linear:
     abdtype: str
     x: np.ndarray
     xdtype: str
+    cfg: int = 0
+    sub: int = 0
 
     @property
     def N(self) -> int:
@@ -115,7 +117,16 @@ def make_linear(name: str, cfg: int, N: int, K: int, M: int, *, sigma: float, wd
     A = store(normal((r, K), a_sigma, cfg, T_A, sub, seed=seed), abdtype) if r > 0 else None
     B = store(normal((N, r), b_sigma, cfg, T_B, sub, seed=seed), abdtype) if r > 0 else None
     x = store(normal((M, K), 1.0, cfg, T_X, sub, M, seed=seed), xdtype)
-    return Linear(name, W, wdtype, bits, r, alpha, A, B, abdtype, x, xdtype)
+    return Linear(name, W, wdtype, bits, r, alpha, A, B, abdtype, x, xdtype, cfg, sub)
+
+
+def upstream_grad(lin: Linear, seed: int = 0) -> np.ndarray:
+    """A synthetic upstream gradient dy (M x N) for the backward, N(0, 1) in x's dtype.
+
+    The pages give no gradient statistics; a standard normal of the output's
+    shape is the plain stand-in (the same draw as x, on the other side).
+    """
+    return store(normal((lin.M, lin.N), 1.0, lin.cfg, T_DY, lin.sub, lin.M, seed=seed), lin.xdtype)
 
 
 # ---------------------------------------------------------------- the five workloads
