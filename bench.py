@@ -15,6 +15,9 @@ cache, so the decode figure is HBM bandwidth, not cache bandwidth):
   prefill base  the same without the adapter (one GEMM kernel per call)
   decode        y = x W'^T + s (x A^T) B^T at M = 1 for all R layers
   decode base   the same without the adapter (one GEMV kernel per call)
+  backward      dx = dy W' + s (dy B) A, dA = s (dy B)^T x, dB = s dy^T (x A^T)
+                at M = 2048 for all R layers (dy bf16 ~ N(0, 1), dx bf16, dA/dB fp32)
+  backward base dx = dy W' alone (one transposed GEMM kernel per call)
 Each phase is bracketed by HIP events on the stream its calls run on (events
 between the calls of a phase would add a queue barrier per call).  Calls are
 prepared (marshalled once); the prefill phases are GPU-bound and issued eagerly,
@@ -29,6 +32,8 @@ value          = decode effective GB/s (algorithmic bytes of all decode calls /
 value_prefill  = prefill TFLOP/s with 2MNK + 2Mr(K+N) flops per call.
 roofline       = the decode GEMV kernel (base calls: one kernel per call).
 roofline_prefill = the prefill GEMM kernel (base calls).
+backward       = backward TFLOP/s with 2MNK + 2Mr(3K + 2N) flops per call;
+                 its roofline is the transposed GEMM kernel (base calls).
 """
 from __future__ import annotations
 
@@ -56,6 +61,11 @@ def decode_bytes(M=M_DECODE, N=N_, K=K_, b=BITS, r=R_):
 
 def prefill_flops(M=M_PREFILL, N=N_, K=K_, r=R_):
     return 2 * M * N * K + 2 * M * r * (K + N)
+
+
+def backward_flops(M=M_PREFILL, N=N_, K=K_, r=R_):
+    # dx = dy W' (2MNK) + u A (2MrK); u = dy B (2MNr); t = x A^T (2MKr); dA (2MrK); dB (2MNr)
+    return 2 * M * N * K + 2 * M * r * (3 * K + 2 * N)
 
 
 def quantize_bytes(N=N_, K=K_, b=BITS):
@@ -88,8 +98,10 @@ _CSRC = "quantized_base_fine_amd/csrc/"
 TRAFFIC_KERNELS = {
     "decode": ("k_gemv<4, 2, true, false, 2, true, false>",
                [_CSRC + f for f in ("qlr_gemv.hip", "qlr_lut.h", "qlr_device.h", "qlr_internal.h")]),
-    "prefill": ("k_gemm<4, 2, false>",
+    "prefill": ("k_gemm<4, 2, false, false>",
                 [_CSRC + f for f in ("qlr_gemm.hip", "qlr_lut.h", "qlr_device.h", "qlr_internal.h")]),
+    "backward": ("k_gemm<4, 2, false, true>",
+                 [_CSRC + f for f in ("qlr_gemm.hip", "qlr_lut.h", "qlr_device.h", "qlr_internal.h")]),
 }
 COPY_BYTES = 256 << 20  # the calibration copy reads and writes this many bytes
 
@@ -290,6 +302,12 @@ def main():
     ws1 = torch.empty(max(qlr.workspace_bytes(qlr.OP_LINEAR, M_DECODE, N_, K_, R_), 16), dtype=torch.uint8, device=dev)
     wsp = torch.empty(max(qlr.workspace_bytes(qlr.OP_LINEAR, M_PREFILL, N_, K_, R_), 16), dtype=torch.uint8, device=dev)
     wdeq = torch.empty((N_, K_), dtype=torch.float32, device=dev)
+    dyp = to_dev(workloads.upstream_grad(linp), "bf16")
+    wsb = torch.empty(max(qlr.workspace_bytes(qlr.OP_LINEAR_BWD, M_PREFILL, N_, K_, R_), 16), dtype=torch.uint8,
+                      device=dev)
+    dxp = torch.empty((M_PREFILL, K_), dtype=torch.bfloat16, device=dev)
+    dA = torch.empty((R_, K_), dtype=torch.float32, device=dev)
+    dB = torch.empty((N_, R_), dtype=torch.float32, device=dev)
     layers = []
     for _ in range(R):
         qw = qlr.QWeight.empty(N_, K_, BITS, dev)
@@ -301,7 +319,9 @@ def main():
             prefill=qlr.LinearCall(xp, qw, A, B, linp.scale, out=yp, ws=wsp),
             prefill_base=qlr.LinearCall(xp, qw, out=yp),
             decode=qlr.LinearCall(x1, qw, A, B, lin1.scale, out=y1, ws=ws1),
-            decode_base=qlr.LinearCall(x1, qw, out=y1)))
+            decode_base=qlr.LinearCall(x1, qw, out=y1),
+            backward=qlr.LinearBwdCall(dyp, xp, qw, A, B, linp.scale, dx=dxp, dA=dA, dB=dB, ws=wsb),
+            backward_base=qlr.LinearBwdCall(dyp, xp, qw, dx=dxp)))
     if args.copy_calibration:
         src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -341,7 +361,7 @@ def main():
             torch.cuda.synchronize()
             assert torch.equal(layers[-1]["qw"].codes, ref_codes), "graph replay differs from eager quantize"
 
-    PHASES = ("prefill", "prefill_base", "decode", "decode_base")
+    PHASES = ("prefill", "prefill_base", "decode", "decode_base", "backward", "backward_base")
     mixed = None
     if not args.no_mixed:
         mixed, mixed_flops, mixed_n = build_mixed(torch, qlr, workloads, dev)
@@ -423,6 +443,9 @@ def main():
     gemm_flops = prefill_flops(r=0)
     gemv_ach = gemv_bytes / (mean["decode_base"] * 1e-6) / 1e9
     gemm_ach = gemm_flops / (mean["prefill_base"] * 1e-6) / 1e12
+    bwd_tfs = S * R * backward_flops() / (phase_ms["backward"] / 1e3) / 1e12
+    dx_flops = backward_flops(r=0)
+    dx_ach = dx_flops / (mean["backward_base"] * 1e-6) / 1e12
 
     out = {
         "metric": METRIC,
@@ -464,6 +487,17 @@ def main():
             "achieved": round(quantize_bytes() / (q_us * 1e-6) / 1e9, 1),
             "peak": HBM_PEAK_GBS, "unit": "GB/s", "launch_us": round(q_us, 3),
             "bytes_per_launch": quantize_bytes(),
+        },
+        "backward": {
+            "workload": "attn_proj_4096x4096_nf4_dq_r16 backward at M=2048 (dy bf16, dx bf16, dA/dB fp32)",
+            "flops_per_call": backward_flops(), "us_per_call": round(mean["backward"], 3),
+            "value": round(bwd_tfs, 2), "unit": "TFLOP/s",
+            "roofline": {
+                "bound": "mfma", "kernel": "k_gemm TR (input gradient dy W', M=2048, no adapter: one kernel per call)",
+                "achieved": round(dx_ach, 1), "peak": BF16_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(dx_ach / BF16_PEAK_TFLOPS, 4), "launch_us": round(mean["backward_base"], 3),
+                "flops_per_launch": dx_flops, "traffic": traffic_from_profile("backward"),
+            },
         },
         "wall_s": round(wall, 3),
     }

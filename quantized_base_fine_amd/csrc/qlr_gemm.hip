@@ -292,6 +292,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm(GemmParams P, Levels lv) {
   const int64_t KC = TR ? N : K;  // contraction length (a multiple of 64)
   const int64_t NO = TR ? K : N;  // output columns
   const int64_t nb = KC >> 6;
+  // ADP: the adapter branch runs as nbt - nb extra K blocks of 32 adapter columns each
+  const int64_t nbt = nb + (ADP ? (a.r + 31) / 32 : 0);
   const int64_t M = P.m_end;
   const int64_t lt = tile - Lr.tile0;
   const int64_t mt = lt / Lr.ntiles, nt = lt % Lr.ntiles;
@@ -427,8 +429,99 @@ __global__ __launch_bounds__(512, 1) void k_gemm(GemmParams P, Levels lv) {
     load_x(x0, min<int64_t>(3, kbl));
     dequant_store(c0, 0);
     load_c(c0, min<int64_t>(3, kbl));
-    store_x(x1, 1);
-    dequant_store(c1, 1);
+    // ADP: adapter block j >= nb (a = j - nb, adapter columns [32 a, 32 a + 32))
+    // into buffer j % 3.  x side (thread = tile row): [hi(s t) | lo(s t)], t the
+    // float32 adapter product of that row, split into bf16 hi = bf16(s t) and
+    // lo = bf16(s t - hi).  Weight side: forward, row n of the tile holds
+    // [B[n][32 a ..] | the same]; TR, rows 0..31 and 32..63 both hold A[32 a + row % 32]
+    // over the tile's columns.  Runs in steps where the producers would otherwise
+    // idle; its operands are mostly L2-resident (shared by the tile's neighbours).
+    auto adapter_write = [&](int64_t j) {
+      if constexpr (ADP) {
+        const int aa = (int)(j - nb), r = a.r;
+        const uint32_t bw = (uint32_t)(j % 3);
+        const uint16_t* Bl = reinterpret_cast<const uint16_t*>(a.B);
+        const u32x4_t zero4 = {0u, 0u, 0u, 0u};
+        u32x4_t wv[4];
+        if constexpr (TR) {
+          const int jj = 32 * aa + (rr & 31);
+          const uint16_t* ap = Bl + (int64_t)min(jj, r - 1) * K;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int64_t c = n0 + 64 * bq + 32 * dh + 8 * q;
+            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(ap + min(c, K - 8));
+            wv[q] = (jj < r && c < K) ? v : zero4;
+          }
+        } else {
+          const int64_t n = n0 + rr;
+          const bool nv = n < N;
+          const uint16_t* bp = Bl + (nv ? n : N - 1) * (int64_t)r;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const int jq = 32 * aa + 8 * q;
+            if (r % 8 == 0) {
+              const u32x4_t v = *reinterpret_cast<const u32x4_t*>(bp + min(jq, r - 8));
+              wv[q] = (nv && jq < r) ? v : zero4;
+            } else {
+#pragma unroll
+              for (int e2 = 0; e2 < 4; ++e2) {
+                const uint32_t lo = (nv && jq + 2 * e2 < r) ? bp[jq + 2 * e2] : 0u;
+                const uint32_t hi = (nv && jq + 2 * e2 + 1 < r) ? bp[jq + 2 * e2 + 1] : 0u;
+                wv[q][e2] = lo | (hi << 16);
+              }
+            }
+          }
+        }
+        // x side: row pt of the tile
+        const int64_t m = m0 + pt;
+        const bool mv = m < M;
+        float tv[32];
+#pragma unroll
+        for (int i = 0; i < 32; ++i) tv[i] = 0.0f;
+        if (a.t_splits == 1 && r % 4 == 0) {
+          // all eight 16-byte loads in flight at once (clamped addresses, zeroed at use)
+          const float* tq = a.t + (mv ? m : M - 1) * (int64_t)r;
+          f32x4_t v[8];
+#pragma unroll
+          for (int q4 = 0; q4 < 8; ++q4) v[q4] = *reinterpret_cast<const f32x4_t*>(tq + min(32 * aa + 4 * q4, r - 4));
+#pragma unroll
+          for (int q4 = 0; q4 < 8; ++q4)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) tv[4 * q4 + e] = (32 * aa + 4 * q4 < r) ? v[q4][e] : 0.0f;
+        } else {
+          for (int sp = 0; sp < a.t_splits; ++sp) {
+            const float* tq = a.t + ((int64_t)sp * a.M + (mv ? m : M - 1)) * r;
+#pragma unroll
+            for (int i = 0; i < 32; ++i)
+              if (32 * aa + i < r) tv[i] += tq[32 * aa + i];
+          }
+        }
+        const uint32_t xrow = kXOff + bw * kXTile + (uint32_t)pt * 128u;
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          u32x4_t hv, lv;
+#pragma unroll
+          for (int e2 = 0; e2 < 4; ++e2) {
+            const float u0 = mv ? a.scale * tv[8 * c + 2 * e2] : 0.0f;
+            const float u1 = mv ? a.scale * tv[8 * c + 2 * e2 + 1] : 0.0f;
+            const uint32_t hb0 = f32_to_bf16_bits(u0), hb1 = f32_to_bf16_bits(u1);
+            hv[e2] = hb0 | (hb1 << 16);
+            lv[e2] = pack_bf16x2(u0 - bf16_bits_to_f32(hb0), u1 - bf16_bits_to_f32(hb1));
+          }
+          lds_store_u32x4(xrow + ((((uint32_t)c) ^ swz((uint32_t)pt & 15u)) << 4), hv);
+          lds_store_u32x4(xrow + ((((uint32_t)(4 + c)) ^ swz((uint32_t)pt & 15u)) << 4), lv);
+        }
+#pragma unroll
+        for (int q = 0; q < 4; ++q) lds_store_u32x4(wst[q] + bw * kWTile, wv[q]);
+      }
+    };
+
+    if (ADP && nb == 1) {
+      adapter_write(1);
+    } else {
+      store_x(x1, 1);
+      dequant_store(c1, 1);
+    }
     __syncthreads();
     // Step k: load x(k+4) into set (k+1) % 3 and codes(k+4) into set (k+1) % 3;
     // write x(k+2) and the dequantized block k+2 into buffer (k+2) % 3.  The
@@ -463,15 +556,25 @@ __global__ __launch_bounds__(512, 1) void k_gemm(GemmParams P, Levels lv) {
       __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
     };
-    const int64_t nb3 = nb - nb % 3;
+    // regular steps write blocks 2 .. nb - 1 (without an adapter, two more steps
+    // write unused copies: every step ends with the barrier of one consumer block)
+    const int64_t nreg = ADP ? (nb > 2 ? nb - 2 : 0) : nb;
+    const int64_t nr3 = nreg - nreg % 3;
     int64_t kb = 0;
-    for (; kb < nb3; kb += 3) {
+    for (; kb < nr3; kb += 3) {
       pstep(x1, x2, c1, c2, kb, 2);
       pstep(x2, x0, c2, c0, kb + 1, 0);
       pstep(x0, x1, c0, c1, kb + 2, 1);
     }
-    if (kb < nb) pstep(x1, x2, c1, c2, kb, 2);
-    if (kb + 1 < nb) pstep(x2, x0, c2, c0, kb + 1, 0);
+    if (kb < nreg) pstep(x1, x2, c1, c2, kb, 2);
+    if (kb + 1 < nreg) pstep(x2, x0, c2, c0, kb + 1, 0);
+    if constexpr (ADP) {
+      // steps nreg .. nbt - 1 write the adapter blocks (j = k + 2 >= nb)
+      for (int64_t k = nreg; k < nbt; ++k) {
+        if (k + 2 < nbt) adapter_write(k + 2);
+        __syncthreads();
+      }
+    }
     // the consumers' two epilogue barriers: tiles free, then the output staged
     __syncthreads();
     __syncthreads();
@@ -543,127 +646,18 @@ __global__ __launch_bounds__(512, 1) void k_gemm(GemmParams P, Levels lv) {
       __builtin_amdgcn_sched_barrier(0);
       __syncthreads();
     };
-    const int64_t nb3 = nb - nb % 3;
+    // the regular blocks, then (ADP) the adapter blocks nb .. nbt - 1 that the
+    // producers append: the same MFMA steps over [hi | lo] x [B | B] tiles
+    const int64_t nb3 = nbt - nbt % 3;
     int64_t kb = 0;
     for (; kb < nb3; kb += 3) {
       cstep(0, 1);
       cstep(1, 2);
       cstep(2, 0);
     }
-    if (kb < nb) cstep(0, 1);
-    if (kb + 1 < nb) cstep(1, 2);
+    if (kb < nbt) cstep(0, 1);
+    if (kb + 1 < nbt) cstep(1, 2);
 
-    // ---- adapter branch: extra K steps [hi(s t) | lo(s t)] x [B | B]
-    if constexpr (ADP) {
-      const int r = a.r;
-      const uint16_t* Bl = reinterpret_cast<const uint16_t*>(a.B);
-      const int nsteps = (r + 15) / 16;
-      // r % 8 == 0: a lane's 8 adapter columns are whole 16-byte groups of a B
-      // row and whole 32-byte groups of a t row, read with unconditional vector
-      // loads (clamped rows, zeroed at use) so that they are all in flight at
-      // once; otherwise element loads.
-      const bool vec = (r % 8) == 0;
-      const u32x4_t zero4 = {0u, 0u, 0u, 0u};
-      for (int q = 0; q < nsteps; ++q) {
-        const int j0 = 16 * q + 8 * h;  // this lane's 8 adapter columns
-        const bool jv = j0 < r;
-        const int jc = jv ? j0 : 0;
-        u32x4_t bf[2];
-        float v8[4][8];
-        if constexpr (TR) {
-          // A[j0 + e][k] for the lane's output column k (A is r x K): element loads,
-          // 32 lanes read 64 contiguous bytes of one A row per load
-#pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            const int64_t k = n0 + 64 * nh + 32 * c + fr;
-            const bool kv = k < K;
-            const uint16_t* ap = Bl + (kv ? k : 0);
-#pragma unroll
-            for (int e2 = 0; e2 < 4; ++e2) {
-              const uint32_t lo = (kv && j0 + 2 * e2 < r) ? ap[(int64_t)(j0 + 2 * e2) * K] : 0u;
-              const uint32_t hi = (kv && j0 + 2 * e2 + 1 < r) ? ap[(int64_t)(j0 + 2 * e2 + 1) * K] : 0u;
-              bf[c][e2] = lo | (hi << 16);
-            }
-          }
-        }
-        if (vec) {
-#pragma unroll
-          for (int c = 0; c < 2 && !TR; ++c) {
-            const int64_t n = n0 + 64 * nh + 32 * c + fr;
-            const u32x4_t raw = *reinterpret_cast<const u32x4_t*>(Bl + (n < N ? n : N - 1) * (int64_t)r + jc);
-            bf[c] = (n < N && jv) ? raw : zero4;
-          }
-#pragma unroll
-          for (int i = 0; i < 4; ++i)
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v8[i][e] = 0.0f;
-#pragma unroll 2
-          for (int sp = 0; sp < a.t_splits; ++sp) {
-#pragma unroll
-            for (int i = 0; i < 4; ++i) {
-              const int64_t m = m0 + 128 * mh + 32 * i + fr;
-              const float* tq = a.t + ((int64_t)sp * a.M + (m < M ? m : M - 1)) * r + jc;
-              const f32x4_t p0 = *reinterpret_cast<const f32x4_t*>(tq);
-              const f32x4_t p1 = *reinterpret_cast<const f32x4_t*>(tq + 4);
-#pragma unroll
-              for (int e = 0; e < 4; ++e) {
-                v8[i][e] += p0[e];
-                v8[i][4 + e] += p1[e];
-              }
-            }
-          }
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const bool ok = (m0 + 128 * mh + 32 * i + fr < M) && jv;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v8[i][e] = ok ? v8[i][e] : 0.0f;
-          }
-        } else {
-#pragma unroll
-          for (int c = 0; c < 2 && !TR; ++c) {
-            const int64_t n = n0 + 64 * nh + 32 * c + fr;
-            bf[c] = zero4;
-            if (n < N) {
-              const uint16_t* bp = Bl + n * (int64_t)r;
-#pragma unroll
-              for (int e2 = 0; e2 < 4; ++e2) {
-                const uint32_t lo = (j0 + 2 * e2 < r) ? bp[j0 + 2 * e2] : 0u;
-                const uint32_t hi = (j0 + 2 * e2 + 1 < r) ? bp[j0 + 2 * e2 + 1] : 0u;
-                bf[c][e2] = lo | (hi << 16);
-              }
-            }
-          }
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int64_t m = m0 + 128 * mh + 32 * i + fr;
-            const bool mv = m < M;
-#pragma unroll
-            for (int e = 0; e < 8; ++e) v8[i][e] = 0.0f;
-            for (int sp = 0; sp < a.t_splits; ++sp) {
-              const float* tq = a.t + ((int64_t)sp * a.M + (mv ? m : 0)) * r;
-#pragma unroll
-              for (int e = 0; e < 8; ++e) v8[i][e] += (mv && j0 + e < r) ? tq[j0 + e] : 0.0f;
-            }
-          }
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          u32x4_t thi, tlo;
-#pragma unroll
-          for (int e2 = 0; e2 < 4; ++e2) {
-            const float u0 = a.scale * v8[i][2 * e2], u1 = a.scale * v8[i][2 * e2 + 1];
-            const uint32_t hb0 = f32_to_bf16_bits(u0), hb1 = f32_to_bf16_bits(u1);
-            thi[e2] = hb0 | (hb1 << 16);
-            tlo[e2] = pack_bf16x2(u0 - bf16_bits_to_f32(hb0), u1 - bf16_bits_to_f32(hb1));
-          }
-#pragma unroll
-          for (int c = 0; c < 2; ++c) {
-            acc[i][c] = mfma32x32x16(as_bf16x8(thi), as_bf16x8(bf[c]), acc[i][c]);
-            acc[i][c] = mfma32x32x16(as_bf16x8(tlo), as_bf16x8(bf[c]), acc[i][c]);
-          }
-        }
-      }
-    }
     __syncthreads();  // every wave is past its last tile read: the staging area is free
 
     // ---- row-major staging of the 256 x 128 output tile in LDS:

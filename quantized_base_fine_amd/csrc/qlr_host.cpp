@@ -546,10 +546,17 @@ qlr_status qlr_linear_bwd(const void* dy, qlr_dtype dydt, const void* x, qlr_dty
   if (r > 0 && M > 0) {
     e = qlr::launch_transpose_nr(B, (int)abdt, N, r, wsp + lay.bt, s);
     if (e != hipSuccess) return hip_fail(e, "adapter transpose launch");
-    e = qlr::launch_lora_t(x, (int)xdt, M, K, A, (int)abdt, r, tws, st_t, s);
-    if (e != hipSuccess) return hip_fail(e, "adapter product (x A^T) launch");
-    e = qlr::launch_lora_t(dy, (int)dydt, M, N, wsp + lay.bt, (int)abdt, r, uws, st_u, s);
-    if (e != hipSuccess) return hip_fail(e, "adapter product (dy B) launch");
+    if (M > 16 && xdt == QLR_BF16 && abdt == QLR_BF16 && N % 64 == 0) {
+      // t = x A^T and u = dy Bt^T as one grouped launch of the tiled product
+      const qlr::LoraTItem items[2] = {{x, A, tws, K, r}, {dy, wsp + lay.bt, uws, N, r}};
+      e = qlr::launch_lora_t_group(items, 2, M, s);
+      if (e != hipSuccess) return hip_fail(e, "adapter products (x A^T, dy B) launch");
+    } else {
+      e = qlr::launch_lora_t(x, (int)xdt, M, K, A, (int)abdt, r, tws, st_t, s);
+      if (e != hipSuccess) return hip_fail(e, "adapter product (x A^T) launch");
+      e = qlr::launch_lora_t(dy, (int)dydt, M, N, wsp + lay.bt, (int)abdt, r, uws, st_u, s);
+      if (e != hipSuccess) return hip_fail(e, "adapter product (dy B) launch");
+    }
   }
   if (dx && M > 0) {
     qlr::LinearArgs a;
@@ -576,8 +583,8 @@ qlr_status qlr_linear_bwd(const void* dy, qlr_dtype dydt, const void* x, qlr_dty
     if (e != hipSuccess) return hip_fail(e, "input-gradient launch");
   }
   if (r > 0) {
-    e = qlr::launch_lora_grads(uws, st_u, tws, st_t, x, dy, (int)xdt, M, N, K, r, scale, dA, dB,
-                               reinterpret_cast<float*>(wsp + lay.part), s);
+    e = qlr::launch_lora_grads(uws, st_u, tws, st_t, x, dy, (int)xdt, path == QLR_PATH_GEMM, M, N, K, r, scale,
+                               dA, dB, reinterpret_cast<float*>(wsp + lay.part), s);
     if (e != hipSuccess) return hip_fail(e, "adapter-gradient launch");
   }
   return QLR_OK;

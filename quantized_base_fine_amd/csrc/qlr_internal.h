@@ -93,10 +93,11 @@ hipError_t launch_dx_f32(const LinearArgs& a, const Levels& lv, hipStream_t s);
 hipError_t launch_transpose_nr(const void* B, int dt, int64_t N, int r, void* Bt, hipStream_t s);
 // dA = scale u^T x (r x K) and dB = scale dy^T t (N x r), float32, from the
 // float32 partials of u (M x r) and t (M x r); x and dy share dtype qdt.
+// mfma: bf16 MFMA kernel (qdt bf16, K and N multiples of 8), else float32 FMA.
 // part: grad_partial_floats(M, N, K, r) floats of scratch.
 size_t grad_partial_floats(int64_t M, int64_t N, int64_t K, int r);
 hipError_t launch_lora_grads(const float* u, int u_splits, const float* t, int t_splits, const void* x,
-                             const void* dy, int qdt, int64_t M, int64_t N, int64_t K, int r, float scale,
-                             float* dA, float* dB, float* part, hipStream_t s);
+                             const void* dy, int qdt, bool mfma, int64_t M, int64_t N, int64_t K, int r,
+                             float scale, float* dA, float* dB, float* part, hipStream_t s);
 
 }  // namespace qlr
