@@ -434,7 +434,7 @@ qlr_status qlr_linear_fwd_mixed(const qlr_layer* layers, int32_t n, int64_t M, q
       const int splits = qlr::lora_t_splits(M, L.w->cols, (int)xdt, (int)abdt);
       if (L.r > 0) {
         if (M > 16 && xdt == QLR_BF16 && abdt == QLR_BF16) {
-          tgroup.push_back(qlr::LoraTItem{L.x, L.A, reinterpret_cast<float*>(wl), L.w->cols, L.r});
+          tgroup.push_back(qlr::LoraTItem{L.x, L.A, reinterpret_cast<float*>(wl), L.w->cols, L.r, false});
         } else {
           const hipError_t e = qlr::launch_lora_t(L.x, (int)xdt, M, L.w->cols, L.A, (int)abdt, L.r,
                                                   reinterpret_cast<float*>(wl), splits, s);
@@ -544,14 +544,14 @@ qlr_status qlr_linear_bwd(const void* dy, qlr_dtype dydt, const void* x, qlr_dty
   const int st_u = M > 0 ? qlr::lora_t_splits(M, N, (int)dydt, (int)abdt) : 1;
   hipError_t e = hipSuccess;
   if (r > 0 && M > 0) {
-    e = qlr::launch_transpose_nr(B, (int)abdt, N, r, wsp + lay.bt, s);
-    if (e != hipSuccess) return hip_fail(e, "adapter transpose launch");
-    if (M > 16 && xdt == QLR_BF16 && abdt == QLR_BF16 && N % 64 == 0) {
-      // t = x A^T and u = dy Bt^T as one grouped launch of the tiled product
-      const qlr::LoraTItem items[2] = {{x, A, tws, K, r}, {dy, wsp + lay.bt, uws, N, r}};
+    if (M > 16 && xdt == QLR_BF16 && abdt == QLR_BF16 && N % 64 == 0 && r % 8 == 0) {
+      // t = x A^T and u = dy B as one grouped launch of the tiled product (B read as is)
+      const qlr::LoraTItem items[2] = {{x, A, tws, K, r, false}, {dy, B, uws, N, r, true}};
       e = qlr::launch_lora_t_group(items, 2, M, s);
       if (e != hipSuccess) return hip_fail(e, "adapter products (x A^T, dy B) launch");
     } else {
+      e = qlr::launch_transpose_nr(B, (int)abdt, N, r, wsp + lay.bt, s);
+      if (e != hipSuccess) return hip_fail(e, "adapter transpose launch");
       e = qlr::launch_lora_t(x, (int)xdt, M, K, A, (int)abdt, r, tws, st_t, s);
       if (e != hipSuccess) return hip_fail(e, "adapter product (x A^T) launch");
       e = qlr::launch_lora_t(dy, (int)dydt, M, N, wsp + lay.bt, (int)abdt, r, uws, st_u, s);

@@ -37,10 +37,11 @@ hipError_t launch_lora_t(const void* x, int xdt, int64_t M, int64_t K, const voi
 // up to lora_t_group_max() per launch, each written in one K pass (splits 1).
 struct LoraTItem {
   const void* x;   // M x K bf16
-  const void* A;   // r x K bf16
+  const void* A;   // r x K bf16, or K x r when bt (then r % 8 == 0)
   float* t;        // M x r float32
   int64_t K;
   int r;
+  bool bt;
 };
 int lora_t_group_max();
 hipError_t launch_lora_t_group(const LoraTItem* items, int n, int64_t M, hipStream_t s);

@@ -42,6 +42,17 @@ __global__ __launch_bounds__(256) void k_lora_t_valu(const void* __restrict__ x,
 // sums are added through LDS in wave order.
 constexpr uint32_t kTRow = 144;                 // LDS row stride (128 bytes + 16)
 constexpr uint32_t kTSlice = 2 * 16 * kTRow;     // one wave: x rows, then A rows
+// LDS transpose read of 16-bit elements (ds_read_b64_tr_b16): within each group
+// of 16 lanes, lane i receives element i % 4 of the 8-byte reads of lanes
+// i / 4, i / 4 + 4, i / 4 + 8 and i / 4 + 12, in that order.
+typedef short s16x4_t __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ s16x4_t lds_tr16(const char* p) {
+  return __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) s16x4_t*)(const_cast<char*>(p)));
+}
+// Byte offset of row k (0..63) of a 64 x 16 bf16 block stored with 32-byte rows;
+// rows 8..15 of every 16 swap their 128-byte halves, so the transpose reads of
+// rows {q..q+3} and {q+8..q+11} by one half-wave hit distinct banks.
+__device__ __forceinline__ uint32_t bt_row(uint32_t k) { return (k * 32u) ^ (((k >> 3) & 1u) << 7); }
 __device__ __forceinline__ uint32_t t_off(bool ok, uint32_t off) {
   asm volatile("" : "+v"(off));  // keep the select a select (no branch around the load)
   return ok ? off : 0xFFFFFFF0u;
@@ -52,10 +63,10 @@ __device__ __forceinline__ uint32_t t_off(bool ok, uint32_t off) {
 constexpr int kTGroupMax = 16;
 struct TLayer {
   const uint16_t* x;
-  const uint16_t* A;
+  const uint16_t* A;  // r x K, or (bt) K x r
   float* t;
   int64_t K;
-  int32_t r, jtiles;
+  int32_t r, jtiles, bt;
   int64_t tile0;
 };
 struct TGroup {
@@ -82,8 +93,14 @@ __global__ __launch_bounds__(256) void k_lora_t_tile(TGroup G) {
   const int64_t mrows = std::min<int64_t>(16, M - m0), jrows = std::min<int64_t>(16, (int64_t)r - j0);
   const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(x + m0 * K), (short)0, (int)(mrows * K * 2), 0x00020000);
-  const __amdgpu_buffer_rsrc_t ar = __builtin_amdgcn_make_buffer_rsrc(
-      const_cast<uint16_t*>(A + j0 * K), (short)0, (int)(jrows * K * 2), 0x00020000);
+  // bt: the adapter operand is given as K x r (the backward's B, for u = dy B);
+  // its 64 x 16 block (rows k, 16 adapter columns from j0) is read as 128
+  // 16-byte pieces: piece q = row q / 2, columns 8 (q % 2) .. + 8
+  const bool bt = Ly.bt != 0;
+  const __amdgpu_buffer_rsrc_t ar = bt ? __builtin_amdgcn_make_buffer_rsrc(
+                                             const_cast<uint16_t*>(A + j0), (short)0, (int)((K * r - j0) * 2), 0x00020000)
+                                       : __builtin_amdgcn_make_buffer_rsrc(
+                                             const_cast<uint16_t*>(A + j0 * K), (short)0, (int)(jrows * K * 2), 0x00020000);
   struct Blk { u32x4_t xa[2], aa[2]; };
   auto load = [&](int64_t kb, Blk& b) {
     const bool kv = kb < kb1;
@@ -92,7 +109,11 @@ __global__ __launch_bounds__(256) void k_lora_t_tile(TGroup G) {
       const int q = i * 64 + lane;
       const uint32_t off = t_off(kv, (uint32_t)(((q >> 3) * K + kb * 64 + (q & 7) * 8) * 2));
       b.xa[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(xr, off, 0, 0));
-      b.aa[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ar, off, 0, 0));
+      // bt: columns past r are zeroed (a piece is 8 columns; r % 8 == 0)
+      const uint32_t boff = t_off(kv && 8 * (q & 1) < jrows, (uint32_t)(((kb * 64 + (q >> 1)) * r + 8 * (q & 1)) * 2));
+      uint32_t ao = bt ? boff : off;
+      asm volatile("" : "+v"(ao));  // keep the select a select (no branch around the load)
+      b.aa[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ar, ao, 0, 0));
     }
   };
   char* slice = lds + wave * kTSlice;
@@ -103,13 +124,25 @@ __global__ __launch_bounds__(256) void k_lora_t_tile(TGroup G) {
       const int q = i * 64 + lane;
       const uint32_t o = (uint32_t)(q >> 3) * kTRow + (uint32_t)(q & 7) * 16;
       *reinterpret_cast<u32x4_t*>(slice + o) = b.xa[i];
-      *reinterpret_cast<u32x4_t*>(slice + 16 * kTRow + o) = b.aa[i];
+      if (bt) *reinterpret_cast<u32x4_t*>(slice + 16 * kTRow + bt_row(q >> 1) + 16u * (q & 1)) = b.aa[i];
+      else *reinterpret_cast<u32x4_t*>(slice + 16 * kTRow + o) = b.aa[i];
     }
 #pragma unroll
     for (int ks = 0; ks < 2; ++ks) {
       const uint32_t o = (uint32_t)(lane & 15) * kTRow + (uint32_t)(4 * ks + (lane >> 4)) * 16;
       const u32x4_t xf = *reinterpret_cast<const u32x4_t*>(slice + o);
-      const u32x4_t af = *reinterpret_cast<const u32x4_t*>(slice + 16 * kTRow + o);
+      u32x4_t af;
+      if (bt) {
+        // rows 32 ks + 8 g + {0..3} and {4..7} (g = lane / 16) of adapter column lane % 16
+        const uint32_t g = (uint32_t)lane >> 4, sp = (uint32_t)lane & 15u;
+        const char* base = slice + 16 * kTRow + 8u * (sp & 3u);
+        const uint32_t row = 32u * ks + 8u * g + (sp >> 2);
+        const s16x4_t lo = lds_tr16(base + bt_row(row)), hi = lds_tr16(base + bt_row(row + 4));
+        af = u32x4_t{__builtin_bit_cast(uint2, lo).x, __builtin_bit_cast(uint2, lo).y,
+                     __builtin_bit_cast(uint2, hi).x, __builtin_bit_cast(uint2, hi).y};
+      } else {
+        af = *reinterpret_cast<const u32x4_t*>(slice + 16 * kTRow + o);
+      }
       acc = mfma16x16x32(as_bf16x8(xf), as_bf16x8(af), acc);
     }
   };
@@ -325,6 +358,8 @@ hipError_t launch_lora_t_group(const LoraTItem* items, int n, int64_t M, hipStre
     L.K = it.K;
     L.r = it.r;
     L.jtiles = (it.r + 15) / 16;
+    L.bt = it.bt ? 1 : 0;
+    if (it.bt && it.r % 8 != 0) return hipErrorInvalidValue;
     L.tile0 = t0;
     t0 += mtiles * L.jtiles;
   }
