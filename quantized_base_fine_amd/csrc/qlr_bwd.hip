@@ -446,10 +446,13 @@ __global__ __launch_bounds__(256) void k_lora_grad_mfma(GradParams G) {
   }
 }
 
-// out = s * (sum over the M ranges, in range order) of the partials.  Eight
-// ranges' loads are in flight at once.
+// out = s * (sum over the M ranges, in range order) of the partials.  A thread
+// owns 4 consecutive columns of one adapter row (16-byte loads; C % 4 == 0,
+// else one column), and eight ranges' loads are in flight at once.
+template <bool V4>
 __global__ __launch_bounds__(256) void k_lora_grad_reduce(GradParams G) {
-  const int64_t i0 = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  constexpr int W = V4 ? 4 : 1;
+  const int64_t i0 = ((int64_t)blockIdx.x * 256 + threadIdx.x) * W;
   const int64_t n0 = (int64_t)G.r * G.J[0].C;
   const int ji = (G.nj > 1 && i0 >= n0) ? 1 : 0;
   const float* __restrict__ part = G.J[ji].part;
@@ -460,16 +463,27 @@ __global__ __launch_bounds__(256) void k_lora_grad_reduce(GradParams G) {
   if (i >= (int64_t)r * C) return;
   const int64_t j = i / C, c = i % C;
   const int64_t stride = (int64_t)r * C;
-  float s = 0.0f;
+  using V = typename std::conditional<V4, f32x4_t, float>::type;
+  V s = {};
   for (int z0 = 0; z0 < ms; z0 += 8) {
-    float v[8];
+    V v[8];
 #pragma unroll
-    for (int b = 0; b < 8; ++b) v[b] = part[(int64_t)min(z0 + b, ms - 1) * stride + i];
+    for (int b = 0; b < 8; ++b) v[b] = *reinterpret_cast<const V*>(part + (int64_t)min(z0 + b, ms - 1) * stride + i);
 #pragma unroll
-    for (int b = 0; b < 8; ++b) s += (z0 + b < ms) ? v[b] : 0.0f;
+    for (int b = 0; b < 8; ++b)
+      if (z0 + b < ms) s += v[b];
   }
-  if (G.J[ji].cols_major) out[c * r + j] = G.scale * s;
-  else out[i] = G.scale * s;
+  if constexpr (V4) {
+    if (G.J[ji].cols_major) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) out[(c + e) * r + j] = G.scale * s[e];
+    } else {
+      *reinterpret_cast<f32x4_t*>(out + i) = G.scale * s;
+    }
+  } else {
+    if (G.J[ji].cols_major) out[c * r + j] = G.scale * s;
+    else out[i] = G.scale * s;
+  }
 }
 
 __global__ __launch_bounds__(256) void k_zero_f32(float* __restrict__ p, int64_t n) {
@@ -666,7 +680,10 @@ hipError_t launch_lora_grads(const float* u, int u_splits, const float* t, int t
   }
   if (e != hipSuccess || G.msplit == 1) return e;
   const int64_t outs = (int64_t)r * (K + N);
-  hipLaunchKernelGGL(k_lora_grad_reduce, dim3((unsigned)((outs + 255) / 256)), dim3(256), 0, s, G);
+  if (K % 4 == 0 && N % 4 == 0)
+    hipLaunchKernelGGL(k_lora_grad_reduce<true>, dim3((unsigned)((outs / 4 + 255) / 256)), dim3(256), 0, s, G);
+  else
+    hipLaunchKernelGGL(k_lora_grad_reduce<false>, dim3((unsigned)((outs + 255) / 256)), dim3(256), 0, s, G);
   return hipGetLastError();
 }
 
