@@ -5,13 +5,13 @@
 // time it is used.  LoRDBA page, "adapter mode": the adapter stays a separate
 // branch, y = x W'^T + scale (x A^T) B^T.
 //
-// Tiling.  A workgroup of 4 waves owns a 256 (M) x 128 (N) output tile.  Wave
-// w = 2 kh + mh computes rows [128 mh, 128 mh + 128) x all 128 columns (4 x 4
-// MFMA tiles of 32x32, 256 accumulator registers) over the K half kh of every
-// 64-element block; the two K halves are added through LDS at the end.
-// Splitting K rather than N halves the fragment bytes read from LDS per MFMA.
+// Tiling.  A workgroup of 8 waves owns a 256 (M) x 128 (N) output tile: 4
+// producer waves stage operands in LDS and 4 consumer waves multiply them.
+// Consumer wave w = 2 nh + mh computes rows [128 mh, 128 mh + 128) x columns
+// [64 nh, 64 nh + 64) (4 x 2 MFMA tiles of 32x32, 128 accumulator registers)
+// over every 64-element K block.
 //
-// Operand staging.  Per 64-element K block the workgroup writes two LDS tiles,
+// Operand staging.  Per 64-element K block the producers write two LDS tiles,
 // both stored as 128-byte rows whose 16-byte chunks are XOR-swizzled by the row
 // index: chunk c of row q sits at q*128 + ((c ^ g(q mod 16)) * 16) with
 // g(r) = (r ^ bit2(r) ^ bit3(r)) mod 8.  Fragment reads (16 rows, one chunk)
@@ -22,8 +22,8 @@
 //    rows past M read as zero).  MFMA fragments loaded straight from global
 //    memory would touch 32 rows per instruction, which the L1 serves at about a
 //    third of the rate.
-//  * W: the tile's 128 weight rows, dequantized by all 256 threads (two per
-//    row, 32 codes each) to bf16 = round(level(code) * absmax).
+//  * W: the tile's 128 weight rows, dequantized by the 256 producer threads (two
+//    per row, 32 codes each) to bf16 = round(level(code) * absmax).
 // Tiles are triple-buffered (block k in buffer k mod 3, static in the 3-way
 // unrolled loop): block k+2 is written while block k is multiplied, so the
 // first fragments of block k+1 can be read before the barrier that ends block
@@ -39,9 +39,13 @@
 // remapped so that each XCD walks a contiguous, row-major range of tiles, which
 // keeps one 256-row slab of x hot in that XCD's L2.
 //
-// Adapter.  t = x A^T (float32 partial sums from the adapter-product kernel) is
-// split into hi = bf16(s t) and lo = bf16(s t - hi) and multiplied with B as
-// extra K steps: [hi | lo] [B | B]^T.
+// Adapter.  t = x A^T (float32, from the adapter-product kernel) enters as
+// extra K blocks after the last weight block, 32 adapter columns each: the x
+// side holds [hi(s t) | lo(s t)] with hi = bf16(s t) and lo = bf16(s t - hi)
+// (about 16 significant bits of s t), the weight side [B | B].  The producers
+// build them in the steps where the pipeline has no weight block left to
+// write, so their loads overlap the last weight blocks' products and the
+// consumers run the same MFMA steps over them.
 #include <algorithm>
 #include <type_traits>
 
