@@ -69,7 +69,7 @@ typedef enum {
   QLR_PATH_GEMM = 3  /* bf16 x, any M: LDS-tiled prefill GEMM (bf16 MFMA, fp32 accumulate) */
 } qlr_path;
 
-typedef enum { QLR_OP_QUANTIZE = 0, QLR_OP_LINEAR = 1, QLR_OP_LINEAR_BWD = 2 } qlr_op;
+typedef enum { QLR_OP_QUANTIZE = 0, QLR_OP_LINEAR = 1, QLR_OP_LINEAR_BWD = 2, QLR_OP_LINEAR_DBA = 3 } qlr_op;
 
 /*
  * A quantized frozen weight (QLoRA page, sections "1. 4-bit NormalFloat" and
@@ -107,6 +107,24 @@ typedef struct {
   float scale;          /* alpha / r */
   void* y;              /* device, M x w->rows */
 } qlr_layer;
+
+/*
+ * A double-binary adapter (LoRDBA page, section 2 "Core architecture"):
+ * dW = sum_{i<ell} diag(alpha_i) B1 diag(beta_i) B2 diag(gamma_i), with sign
+ * factors B1 (rows x rank) and B2 (rank x cols) in {-1, +1} at one bit per
+ * entry, shared by the ell terms, and fp16 channel scales.  Bit 1 stands for
+ * +1, bit 0 for -1; a row of c entries is ceil(c/32) uint32 words, entry e at
+ * bit e % 32 of word e / 32 (padding bits ignored).
+ */
+typedef struct {
+  int32_t rank;          /* R >= 1 */
+  int32_t ell;           /* envelope rank >= 1 (rank * ell <= 4096) */
+  const uint32_t* b1;    /* device, rows x ceil(R/32) words */
+  const uint32_t* b2;    /* device, R x ceil(cols/32) words */
+  const uint16_t* alpha; /* device, fp16 bits, ell x rows */
+  const uint16_t* beta;  /* device, fp16 bits, ell x R */
+  const uint16_t* gamma; /* device, fp16 bits, ell x cols */
+} qlr_dba;
 
 /* Library version (major*10000 + minor*100 + patch). */
 int qlr_version(void);
@@ -219,6 +237,24 @@ qlr_status qlr_linear_fwd(const void* x, qlr_dtype xdt, int64_t M, const qlr_qwe
 qlr_status qlr_linear_fwd_mixed(const qlr_layer* layers, int32_t n, int64_t M, qlr_dtype xdt,
                                 qlr_dtype abdt, qlr_dtype ydt, void* ws, size_t ws_bytes,
                                 void* stream);
+
+/*
+ * Forward with a double-binary adapter in adapter mode (LoRDBA page,
+ * sections 1-2: the adapter stays unmerged beside the frozen base):
+ *     y = x W'^T + sum_i alpha_i * (((x * gamma_i) B2^T) * beta_i) B1^T
+ * (* the per-channel product).  x, y, M, w as in qlr_linear_fwd (cols % 64 ==
+ * 0).  The branch runs as an exact rank-2*ell*R branch of the forward kernels:
+ * its first stage (float32 sums of +-x*gamma, times beta) and the alpha-signed
+ * second factor (alpha split exactly into two bf16 halves) are formed in the
+ * workspace, then the quantized-base kernel adds it in its epilogue or its
+ * adapter K blocks.  Same error bound as qlr_linear_fwd, with S extended by
+ * sum_i |alpha_i[n]| sum_j |beta_i[j]| sum_k |x[m,k] gamma_i[k]|.
+ * ws (device) >= qlr_workspace_bytes(QLR_OP_LINEAR_DBA, M, rows, cols,
+ * rank * ell).  Asynchronous, allocation-free.
+ * Errors: as qlr_linear_fwd (QLR_ERR_SHAPE also for rank or ell < 1).
+ */
+qlr_status qlr_linear_fwd_dba(const void* x, qlr_dtype xdt, int64_t M, const qlr_qweight* w, const qlr_dba* adapter,
+                              void* y, qlr_dtype ydt, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Backward for adapter training (the step after the forward in fine-tuning:

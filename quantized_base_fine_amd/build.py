@@ -18,7 +18,8 @@ CSRC = os.path.join(HERE, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libqlr.so")
 
-SOURCES = ["qlr_host.cpp", "qlr_quant.hip", "qlr_linear_f32.hip", "qlr_gemv.hip", "qlr_gemm.hip", "qlr_bwd.hip"]
+SOURCES = ["qlr_host.cpp", "qlr_quant.hip", "qlr_linear_f32.hip", "qlr_gemv.hip", "qlr_gemm.hip", "qlr_bwd.hip",
+           "qlr_dba.hip"]
 
 
 def hipcc() -> str:

@@ -841,7 +841,7 @@ Plan plan_gemv(const LinearArgs& a) {
   auto r16 = [](size_t b) { return (b + 15) & ~(size_t)15; };
   for (int attempt = 0; attempt < 2; ++attempt) {
     const bool dot = attempt == 0 && BITS != 3 && a.M == 1 && (size_t)a.K * 2 <= kXLdsMax;
-    const bool tf = dot && r > 0 && r <= kFuseR && nb <= 8 * kWaves && !pl.deep &&
+    const bool tf = dot && r > 0 && r <= kFuseR && nb <= 8 * kWaves && !pl.deep && a.A != nullptr &&
                     (reinterpret_cast<uintptr_t>(a.A) & 15) == 0;
     const size_t stage = dot ? 16 * CH * 4 : ChunkGeo<BITS>::kStage;
     size_t lds = PairTable<BITS>::kBytes + (size_t)kWaves * 2 * stage + (size_t)kWaves * 256 * sizeof(float);

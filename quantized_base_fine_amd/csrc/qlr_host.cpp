@@ -143,6 +143,23 @@ BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K, int32_t r) {
   return L;
 }
 
+// Workspace of a double-binary adapter call: t2 (splits x M x 2lR float32) and
+// Beff (N x 2lR bf16), 256-byte aligned.
+struct DbaLayout {
+  size_t t2, beff, total;
+  int splits;
+};
+DbaLayout dba_layout(int64_t M, int64_t N, int64_t K, int R, int ell, int xdt) {
+  auto up = [](size_t b) { return (b + 255) & ~(size_t)255; };
+  DbaLayout L;
+  L.splits = M > 0 ? qlr::dba_t_splits(M, K, xdt, R, ell) : 1;
+  const size_t lr2 = 2 * (size_t)R * (size_t)ell;
+  L.t2 = 0;
+  L.beff = up((size_t)L.splits * (size_t)std::max<int64_t>(M, 0) * lr2 * 4);
+  L.total = L.beff + up((size_t)N * lr2 * 2);
+  return L;
+}
+
 // choose the kernel family for a linear call
 qlr_status pick_path(int64_t M, qlr_dtype xdt, qlr_dtype abdt, int32_t r, qlr_path* out) {
   const bool bf16_ok = xdt == QLR_BF16 && (r == 0 || abdt == QLR_BF16);
@@ -311,6 +328,15 @@ qlr_status qlr_workspace_bytes(qlr_op op, int64_t M, int64_t N, int64_t K, int32
   if (!bytes) return fail(QLR_ERR_NULL, "bytes is NULL");
   if (op == QLR_OP_QUANTIZE) {
     *bytes = 256;
+    return QLR_OK;
+  }
+  if (op == QLR_OP_LINEAR_DBA) {
+    // r = ell * R of the double-binary adapter; the bf16 split count bounds the others
+    if (M < 0 || N < 0 || K < 0 || r < 1) return fail(QLR_ERR_SHAPE, "negative size or r < 1");
+    const int64_t lr2 = 2 * (int64_t)r;
+    const size_t splits = M > 0 ? (size_t)qlr::dba_t_splits(M, K, qlr::DT_BF16, r, 1) : 1;
+    auto up = [](size_t b) { return (b + 255) & ~(size_t)255; };
+    *bytes = up(splits * (size_t)M * (size_t)lr2 * 4) + up((size_t)N * (size_t)lr2 * 2);
     return QLR_OK;
   }
   if (op != QLR_OP_LINEAR && op != QLR_OP_LINEAR_BWD) return fail(QLR_ERR_SHAPE, "unknown op %d", (int)op);
@@ -587,6 +613,52 @@ qlr_status qlr_linear_bwd(const void* dy, qlr_dtype dydt, const void* x, qlr_dty
                                dA, dB, reinterpret_cast<float*>(wsp + lay.part), s);
     if (e != hipSuccess) return hip_fail(e, "adapter-gradient launch");
   }
+  return QLR_OK;
+}
+
+qlr_status qlr_linear_fwd_dba(const void* x, qlr_dtype xdt, int64_t M, const qlr_qweight* w, const qlr_dba* ad,
+                              void* y, qlr_dtype ydt, void* ws, size_t ws_bytes, void* stream) {
+  if (!ad) return fail(QLR_ERR_NULL, "adapter is NULL");
+  if (ad->rank < 1 || ad->ell < 1 || (int64_t)ad->rank * ad->ell > 4096)
+    return fail(QLR_ERR_SHAPE, "rank and ell must be >= 1 with rank * ell <= 4096");
+  if (!ad->b1 || !ad->b2 || !ad->alpha || !ad->beta || !ad->gamma) return fail(QLR_ERR_NULL, "adapter array is NULL");
+  if (!aligned16(ad->b1) || !aligned16(ad->b2) || !aligned16(ad->alpha) || !aligned16(ad->beta) ||
+      !aligned16(ad->gamma))
+    return fail(QLR_ERR_ALIGN, "adapter arrays must be 16-byte aligned");
+  const LinearCheck c{x, xdt, M, w, nullptr, nullptr, QLR_BF16, 0, y, ydt};
+  qlr_status st = check_linear(c);
+  if (st != QLR_OK) return st;
+  const int64_t N = w->rows, K = w->cols;
+  const int R = ad->rank, ell = ad->ell;
+  const DbaLayout lay = dba_layout(M, N, K, R, ell, (int)xdt);
+  if (!ws || ws_bytes < lay.total)
+    return fail(QLR_ERR_WORKSPACE, "workspace of %zu bytes required, got %zu", lay.total, ws ? ws_bytes : (size_t)0);
+  if (!aligned16(ws)) return fail(QLR_ERR_ALIGN, "workspace must be 16-byte aligned");
+  // the branch runs as an exact rank-2lR adapter of the bf16 kernels (B = Beff in bf16)
+  const int32_t r2 = 2 * R * ell;
+  qlr_path path;
+  st = pick_path(M, xdt, QLR_BF16, r2, &path);
+  if (st != QLR_OK) return st;
+  if (M == 0) return QLR_OK;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* wsp = reinterpret_cast<char*>(ws);
+  const qlr::DbaArgs d{R, ell, ad->b1, ad->b2, ad->alpha, ad->beta, ad->gamma};
+  float* t2 = reinterpret_cast<float*>(wsp + lay.t2);
+  uint16_t* beff = reinterpret_cast<uint16_t*>(wsp + lay.beff);
+  hipError_t e = qlr::launch_dba_prep(d, x, (int)xdt, M, N, K, t2, lay.splits, beff, s);
+  if (e != hipSuccess) return hip_fail(e, "adapter stage launch");
+  qlr::LinearArgs a = make_args(c, 1.0f, wsp + lay.t2, lay.splits);
+  a.A = nullptr;
+  a.B = beff;
+  a.abdt = qlr::DT_BF16;
+  a.r = r2;
+  const qlr::Levels lv = levels_arg(w->bits);
+  switch (path) {
+    case QLR_PATH_F32: e = qlr::launch_linear_f32(a, lv, s); break;
+    case QLR_PATH_GEMV: e = qlr::launch_gemv(a, lv, s); break;
+    default: e = qlr::launch_gemm(a, lv, s); break;
+  }
+  if (e != hipSuccess) return hip_fail(e, "linear launch");
   return QLR_OK;
 }
 

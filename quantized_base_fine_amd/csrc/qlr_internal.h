@@ -80,6 +80,23 @@ hipError_t launch_gemm(const LinearArgs& a, const Levels& lv, hipStream_t s);
 int gemm_group_max();
 hipError_t launch_gemm_group(const LinearArgs* ls, int n, const Levels& lv, hipStream_t s);
 
+// ---- double-binary adapter branch
+struct DbaArgs {
+  int R, ell;
+  const uint32_t* b1;     // N x ceil(R/32) words
+  const uint32_t* b2;     // R x ceil(K/32) words
+  const uint16_t* alpha;  // fp16, ell x N
+  const uint16_t* beta;   // fp16, ell x R
+  const uint16_t* gamma;  // fp16, ell x K
+};
+// K splits of the branch's first stage (float32 partials that the forward
+// kernels add, like the adapter product's).
+int dba_t_splits(int64_t M, int64_t K, int xdt, int R, int ell);
+// t2 (splits x M x 2 ell R float32) = [t' | t'] and beff (N x 2 ell R bf16): the
+// branch as an exact rank-2 ell R adapter with scale 1.
+hipError_t launch_dba_prep(const DbaArgs& d, const void* x, int xdt, int64_t M, int64_t N, int64_t K, float* t2,
+                           int splits, uint16_t* beff, hipStream_t s);
+
 // ---- backward (adapter training)
 // Input gradient dx = dy W' + scale u A on the transposed bf16 GEMM: a.x = dy
 // (M x N bf16), a.y = dx (M x K), a.t = u partials (t_splits x M x r float32),

@@ -23,7 +23,7 @@ GROUP = 256
 
 QLR_F32, QLR_F16, QLR_BF16 = 0, 1, 2
 PATH_AUTO, PATH_F32, PATH_GEMV, PATH_GEMM = 0, 1, 2, 3
-OP_QUANTIZE, OP_LINEAR, OP_LINEAR_BWD = 0, 1, 2
+OP_QUANTIZE, OP_LINEAR, OP_LINEAR_BWD, OP_LINEAR_DBA = 0, 1, 2, 3
 
 STATUS = {
     0: "QLR_OK", 1: "QLR_ERR_NULL", 2: "QLR_ERR_SHAPE", 3: "QLR_ERR_DTYPE", 4: "QLR_ERR_BITS",
@@ -54,6 +54,13 @@ class CLayer(C.Structure):
     ]
 
 
+class CDba(C.Structure):
+    _fields_ = [
+        ("rank", C.c_int32), ("ell", C.c_int32), ("b1", C.c_void_p), ("b2", C.c_void_p),
+        ("alpha", C.c_void_p), ("beta", C.c_void_p), ("gamma", C.c_void_p),
+    ]
+
+
 EXPORTS = {
     "qlr_version": (C.c_int, []),
     "qlr_status_string": (C.c_char_p, [C.c_int]),
@@ -79,6 +86,8 @@ EXPORTS = {
                                  C.POINTER(CQWeight), C.c_void_p, C.c_void_p, C.c_int, C.c_int32,
                                  C.c_float, C.c_void_p, C.c_int, C.c_void_p, C.c_void_p,
                                  C.c_void_p, C.c_size_t, C.c_void_p]),
+    "qlr_linear_fwd_dba": (C.c_int, [C.c_void_p, C.c_int, C.c_int64, C.POINTER(CQWeight), C.POINTER(CDba),
+                                     C.c_void_p, C.c_int, C.c_void_p, C.c_size_t, C.c_void_p]),
     "qlr_force_path": (C.c_int, [C.c_int]),
 }
 
@@ -377,3 +386,43 @@ class LinearBwdCall:
 def linear_bwd(dy, x, qw: QWeight, A=None, B=None, scale: float = 0.0, dx_dtype=None, need_dx: bool = True):
     """Gradients (dx, dA, dB) of the layer for an upstream gradient dy; see LinearBwdCall."""
     return LinearBwdCall(dy, x, qw, A, B, scale, dx_dtype=dx_dtype, need_dx=need_dx)()
+
+
+class DbaCall:
+    """A prepared ``qlr_linear_fwd_dba`` call: y = x W'^T + the double-binary adapter
+    branch.  ``b1`` (N, ceil(R/32)) and ``b2`` (R, ceil(K/32)) are int32/uint32
+    device tensors of sign words; ``alpha`` (l, N), ``beta`` (l, R), ``gamma`` (l, K)
+    float16 device tensors.  Marshalled once (the stream current at construction
+    is used); the tensors are kept alive by the object."""
+
+    def __init__(self, x, qw: QWeight, b1, b2, alpha, beta, gamma, out_dtype=None, out=None, ws=None):
+        torch = _torch()
+        _require_cuda(x, b1, b2, alpha, beta, gamma)
+        M = x.shape[0]
+        ell, R = beta.shape
+        if x.shape[1] != qw.cols or alpha.shape != (ell, qw.rows) or gamma.shape != (ell, qw.cols):
+            raise ValueError("x (M, K), alpha (l, N), beta (l, R), gamma (l, K) do not fit the weight")
+        if b1.shape != (qw.rows, (R + 31) // 32) or b2.shape != (R, (qw.cols + 31) // 32):
+            raise ValueError("sign words must be (N, ceil(R/32)) and (R, ceil(K/32))")
+        if any(t.dtype != torch.float16 for t in (alpha, beta, gamma)):
+            raise ValueError("alpha, beta, gamma must be float16")
+        self.y = out if out is not None else torch.empty((M, qw.rows), dtype=out_dtype or x.dtype, device=x.device)
+        need = workspace_bytes(OP_LINEAR_DBA, M, qw.rows, qw.cols, R * ell)
+        if ws is None:
+            ws = torch.empty(max(need, 16), dtype=torch.uint8, device=x.device)
+        tensors = [t.contiguous() for t in (b1, b2, alpha, beta, gamma)]
+        self._keep = (x, qw, ws, tensors)
+        self._cw = qw.c_struct()
+        self._ad = CDba(R, ell, *[t.data_ptr() for t in tensors])
+        self._args = (x.data_ptr(), _dt(x), M, C.byref(self._cw), C.byref(self._ad), self.y.data_ptr(),
+                      _dt(self.y), ws.data_ptr(), ws.numel(), _stream(x.device))
+        self._fn = lib().qlr_linear_fwd_dba
+
+    def __call__(self):
+        check(self._fn(*self._args))
+        return self.y
+
+
+def linear_dba(x, qw: QWeight, b1, b2, alpha, beta, gamma, out_dtype=None):
+    """y = x W'^T + sum_i alpha_i * (((x * gamma_i) B2^T) * beta_i) B1^T; see DbaCall."""
+    return DbaCall(x, qw, b1, b2, alpha, beta, gamma, out_dtype=out_dtype)()

@@ -203,3 +203,24 @@ def test_backward_workspace_sizes():
     big = qlr.workspace_bytes(qlr.OP_LINEAR_BWD, 2048, 4096, 4096, 16)
     assert big >= 2 * 2048 * 16 * 4 + 16 * 4096 * 4
     assert big % 256 == 0
+
+
+def test_dba_validation_and_workspace():
+    lib = qlr.lib()
+    w = _qw(rows=64, cols=128)
+    good = qlr.CDba(16, 1, 0x100000, 0x200000, 0x300000, 0x400000, 0x500000)
+
+    def call(ad, ws=0x900000, wsb=1 << 20, M=4, x=0x600000, y=0x700000):
+        return qlr.STATUS[lib.qlr_linear_fwd_dba(x, qlr.QLR_BF16, M, C.byref(w), C.byref(ad) if ad else None, y,
+                                                 qlr.QLR_F32, ws, wsb, None)]
+    assert call(None) == "QLR_ERR_NULL"
+    assert call(qlr.CDba(0, 1, 0x100000, 0x200000, 0x300000, 0x400000, 0x500000)) == "QLR_ERR_SHAPE"
+    assert call(qlr.CDba(16, 0, 0x100000, 0x200000, 0x300000, 0x400000, 0x500000)) == "QLR_ERR_SHAPE"
+    assert call(qlr.CDba(16, 1, 0, 0x200000, 0x300000, 0x400000, 0x500000)) == "QLR_ERR_NULL"
+    assert call(qlr.CDba(16, 1, 0x100004, 0x200000, 0x300000, 0x400000, 0x500000)) == "QLR_ERR_ALIGN"
+    assert call(good, ws=0) == "QLR_ERR_WORKSPACE"
+    assert call(good, wsb=64) == "QLR_ERR_WORKSPACE"
+    # workspace: [t' | t'] float32 splits x M x 2 l R, then the alpha-signed factor N x 2 l R bf16
+    need = qlr.workspace_bytes(qlr.OP_LINEAR_DBA, 2048, 4096, 4096, 16)
+    assert need == 2048 * 32 * 4 + 4096 * 32 * 2
+    assert qlr.workspace_bytes(qlr.OP_LINEAR_DBA, 0, 64, 128, 16) == 64 * 32 * 2

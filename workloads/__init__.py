@@ -120,6 +120,38 @@ def make_linear(name: str, cfg: int, N: int, K: int, M: int, *, sigma: float, wd
     return Linear(name, W, wdtype, bits, r, alpha, A, B, abdtype, x, xdtype, cfg, sub)
 
 
+T_DBA = 7
+
+
+@dataclasses.dataclass
+class DbaAdapter:
+    """A double-binary adapter's synthetic storage: random sign words and fp16 scales.
+
+    b1 (N, ceil(R/32)) and b2 (R, ceil(K/32)) uint32 words of independent fair
+    bits (padding bits random too: the format ignores them); alpha (l, N),
+    beta (l, R), gamma (l, K) fp16 draws of N(0, 0.01^2), N(0, 1) and N(0, 1/K),
+    so that one term of the update has the scale of a LoRA update with
+    B ~ N(0, 0.01^2) and A ~ N(0, 1/K).
+    """
+    R: int
+    ell: int
+    b1: np.ndarray
+    b2: np.ndarray
+    alpha: np.ndarray
+    beta: np.ndarray
+    gamma: np.ndarray
+
+
+def dba_adapter(N: int, K: int, R: int, ell: int, cfg: int = 0, sub: int = 0, seed: int = 0) -> DbaAdapter:
+    g = rng_for(cfg, T_DBA, sub, R, ell, seed=seed)
+    b1 = g.integers(0, 2 ** 32, size=(N, (R + 31) // 32), dtype=np.uint64).astype(np.uint32)
+    b2 = g.integers(0, 2 ** 32, size=(R, (K + 31) // 32), dtype=np.uint64).astype(np.uint32)
+    alpha = (g.standard_normal((ell, N), dtype=np.float32) * np.float32(0.01)).astype(np.float16)
+    beta = g.standard_normal((ell, R), dtype=np.float32).astype(np.float16)
+    gamma = (g.standard_normal((ell, K), dtype=np.float32) * np.float32(np.sqrt(1.0 / K))).astype(np.float16)
+    return DbaAdapter(R, ell, b1, b2, alpha, beta, gamma)
+
+
 def upstream_grad(lin: Linear, seed: int = 0) -> np.ndarray:
     """A synthetic upstream gradient dy (M x N) for the backward, N(0, 1) in x's dtype.
 
