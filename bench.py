@@ -18,6 +18,8 @@ cache, so the decode figure is HBM bandwidth, not cache bandwidth):
   backward      dx = dy W' + s (dy B) A, dA = s (dy B)^T x, dB = s dy^T (x A^T)
                 at M = 2048 for all R layers (dy bf16 ~ N(0, 1), dx bf16, dA/dB fp32)
   backward base dx = dy W' alone (one transposed GEMM kernel per call)
+  dba decode / dba prefill   the forward with a double-binary adapter branch
+                (R = 16, l = 1) in place of the fp16 adapter, at M = 1 (graph) and M = 2048
 Each phase is bracketed by HIP events on the stream its calls run on (events
 between the calls of a phase would add a queue barrier per call).  Calls are
 prepared (marshalled once); the prefill phases are GPU-bound and issued eagerly,
@@ -66,6 +68,17 @@ def prefill_flops(M=M_PREFILL, N=N_, K=K_, r=R_):
 def backward_flops(M=M_PREFILL, N=N_, K=K_, r=R_):
     # dx = dy W' (2MNK) + u A (2MrK); u = dy B (2MNr); t = x A^T (2MKr); dA (2MrK); dB (2MNr)
     return 2 * M * N * K + 2 * M * r * (3 * K + 2 * N)
+
+
+def dba_bytes(M=M_DECODE, N=N_, K=K_, b=BITS, R=R_, ell=1):
+    # codes + absmax codes + group steps + sign words (N R + R K bits) + fp16 scales + x + y
+    numel = N * K
+    return (numel * b // 8 + numel // 64 + 4 * (numel // 16384) + (N * R + R * K) // 8 + 2 * ell * (N + R + K)
+            + 2 * M * K + 2 * M * N)
+
+
+def dba_flops(M=M_PREFILL, N=N_, K=K_, R=R_, ell=1):
+    return 2 * M * N * K + 2 * M * ell * R * (K + N)
 
 
 def quantize_bytes(N=N_, K=K_, b=BITS):
@@ -308,6 +321,11 @@ def main():
     dxp = torch.empty((M_PREFILL, K_), dtype=torch.bfloat16, device=dev)
     dA = torch.empty((R_, K_), dtype=torch.float32, device=dev)
     dB = torch.empty((N_, R_), dtype=torch.float32, device=dev)
+    ad = workloads.dba_adapter(N_, K_, R_, 1, cfg=2)
+    dba_t = [torch.from_numpy(np.ascontiguousarray(a).view(np.int32)).to(dev) for a in (ad.b1, ad.b2)]
+    dba_t += [torch.from_numpy(np.ascontiguousarray(a)).to(dev) for a in (ad.alpha, ad.beta, ad.gamma)]
+    ws_d1 = torch.empty(qlr.workspace_bytes(qlr.OP_LINEAR_DBA, M_DECODE, N_, K_, R_), dtype=torch.uint8, device=dev)
+    ws_dp = torch.empty(qlr.workspace_bytes(qlr.OP_LINEAR_DBA, M_PREFILL, N_, K_, R_), dtype=torch.uint8, device=dev)
     layers = []
     for _ in range(R):
         qw = qlr.QWeight.empty(N_, K_, BITS, dev)
@@ -321,7 +339,9 @@ def main():
             decode=qlr.LinearCall(x1, qw, A, B, lin1.scale, out=y1, ws=ws1),
             decode_base=qlr.LinearCall(x1, qw, out=y1),
             backward=qlr.LinearBwdCall(dyp, xp, qw, A, B, linp.scale, dx=dxp, dA=dA, dB=dB, ws=wsb),
-            backward_base=qlr.LinearBwdCall(dyp, xp, qw, dx=dxp)))
+            backward_base=qlr.LinearBwdCall(dyp, xp, qw, dx=dxp),
+            dba_decode=qlr.DbaCall(x1, qw, *dba_t, out=y1, ws=ws_d1),
+            dba_prefill=qlr.DbaCall(xp, qw, *dba_t, out=yp, ws=ws_dp)))
     if args.copy_calibration:
         src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -361,7 +381,8 @@ def main():
             torch.cuda.synchronize()
             assert torch.equal(layers[-1]["qw"].codes, ref_codes), "graph replay differs from eager quantize"
 
-    PHASES = ("prefill", "prefill_base", "decode", "decode_base", "backward", "backward_base")
+    PHASES = ("prefill", "prefill_base", "decode", "decode_base", "backward", "backward_base", "dba_decode",
+              "dba_prefill")
     mixed = None
     if not args.no_mixed:
         mixed, mixed_flops, mixed_n = build_mixed(torch, qlr, workloads, dev)
@@ -371,7 +392,7 @@ def main():
     # The decode phases (short, launch-bound calls) also run as HIP graphs of the
     # R prepared calls; every replay is checked against the eager outputs first.
     graphs = {}
-    for ph in (() if args.eager else ("decode", "decode_base")):
+    for ph in (() if args.eager else ("decode", "decode_base", "dba_decode")):
         for L in layers:
             L[ph]()
         torch.cuda.synchronize()
@@ -498,6 +519,16 @@ def main():
                 "frac": round(dx_ach / BF16_PEAK_TFLOPS, 4), "launch_us": round(mean["backward_base"], 3),
                 "flops_per_launch": dx_flops, "traffic": traffic_from_profile("backward"),
             },
+        },
+        "dba": {
+            "workload": "attn_proj_4096x4096_nf4_dq with a double-binary adapter (R=16, l=1) instead of the fp16 one",
+            "decode_us": round(mean["dba_decode"], 3),
+            "decode_gbs": round(dba_bytes() / (mean["dba_decode"] * 1e-6) / 1e9, 1),
+            "decode_bytes_per_call": dba_bytes(),
+            "prefill_us": round(mean["dba_prefill"], 3),
+            "prefill_tflops": round(dba_flops() / (mean["dba_prefill"] * 1e-6) / 1e12, 1),
+            "adapter_bytes": (N_ * R_ + R_ * K_) // 8 + 2 * (N_ + R_ + K_),
+            "fp16_adapter_bytes": 2 * R_ * (N_ + K_),
         },
         "wall_s": round(wall, 3),
     }

@@ -29,9 +29,8 @@ __device__ __forceinline__ void split_f16(float v, uint32_t& hi, uint32_t& lo) {
 }
 
 // Beff[n][jj] for jj < lR: hi(alpha_i[n]) sign(B1[n][j]), jj = iR + j; Beff[n][lR + jj]: the lo part.
-__global__ __launch_bounds__(256) void k_dba_beff(DbaArgs d, int64_t N, uint16_t* __restrict__ beff) {
+__device__ __forceinline__ void dba_beff_item(const DbaArgs& d, int64_t N, uint16_t* __restrict__ beff, int64_t idx) {
   const int lr = d.ell * d.R;
-  const int64_t idx = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (idx >= N * lr) return;
   const int64_t n = idx / lr;
   const int jj = (int)(idx % lr), i = jj / d.R, j = jj % d.R;
@@ -44,57 +43,106 @@ __global__ __launch_bounds__(256) void k_dba_beff(DbaArgs d, int64_t N, uint16_t
   beff[n * 2 * lr + lr + jj] = (uint16_t)(lo ^ flip);
 }
 
-// t' for bf16 x on 16x16x32 bf16 MFMA, float32 accumulation.  blockIdx.x: 16
-// rows of x; blockIdx.y: (i, 16 adapter rows j); blockIdx.z: K split.  The 4
-// waves share the split's 32-wide K steps and are added through LDS.  Per step
-// a lane reads 8 elements of its x row (A operand) and builds its B operand,
-// sign(B2[j][k]) gamma_i[k] for 8 k, as two exact bf16 halves (the sign applied
-// by flipping sign bits), multiplied in two MFMAs into one accumulator.
-__global__ __launch_bounds__(256) void k_dba_t_mfma(DbaArgs d, const uint16_t* __restrict__ x, int64_t M,
-                                                    int64_t K, float* __restrict__ t2) {
-  __shared__ float sRed[4][256];
+// One launch: workgroups [0, tblocks) compute t' for bf16 x on 16x16x32 bf16
+// MFMA (float32 accumulation), the rest expand Beff (one item per thread).
+// A t' workgroup owns 16 rows of x, 16 adapter rows j of one term i and one K
+// split.  It first splits gamma_i over its K range into bf16 hi and lo halves
+// in LDS (once, shared by all its rows and adapter rows); its 16 waves then
+// take every 16th 32-wide K step, all of a wave's steps loaded before any is
+// multiplied (kDbaSteps at a time), and are added through LDS.  Per step a
+// lane reads 8 elements of its x row (A operand) and 8 hi and 8 lo halves of
+// gamma, flips the sign bits where B2[j][k] is -1 (B operand) and multiplies
+// both halves into one accumulator.
+constexpr int kDbaWaves = 16, kDbaSteps = 4;
+struct DbaGrid {
+  int64_t mtiles, tblocks;
+  int rch, splits;
+  int64_t kspan;  // largest K range of a split (elements), for the LDS halves
+};
+__global__ __launch_bounds__(1024) void k_dba_prep(DbaArgs d, DbaGrid gd, const uint16_t* __restrict__ x, int64_t M,
+                                                   int64_t N, int64_t K, float* __restrict__ t2,
+                                                   uint16_t* __restrict__ beff) {
+  __shared__ float sRed[kDbaWaves][256];
+  extern __shared__ __attribute__((aligned(16))) char sG[];  // hi halves, then lo halves (kspan each)
+  if ((int64_t)blockIdx.x >= gd.tblocks) {
+    dba_beff_item(d, N, beff, ((int64_t)blockIdx.x - gd.tblocks) * 1024 + threadIdx.x);
+    return;
+  }
+  const int64_t bid = blockIdx.x;
+  const int64_t mt = bid % gd.mtiles, rest = bid / gd.mtiles;
+  const int yc = (int)(rest % ((int64_t)d.ell * gd.rch)), sidx = (int)(rest / ((int64_t)d.ell * gd.rch));
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = lane & 15, g = lane >> 4;
-  const int rch = (d.R + 15) / 16;
-  const int i = blockIdx.y / rch, j0 = 16 * (blockIdx.y % rch);
-  const int64_t m0 = (int64_t)blockIdx.x * 16;
-  const int S = gridDim.z, sidx = blockIdx.z;
+  const int i = yc / gd.rch, j0 = 16 * (yc % gd.rch);
+  const int64_t m0 = mt * 16;
+  const int S = gd.splits;
   const bool xv = m0 + row < M;
   const uint16_t* xp = x + (xv ? m0 + row : 0) * K + 8 * g;
   const int j = j0 + row;
   const bool jv = j < d.R;
   const int64_t w2 = (K + 31) / 32;
   const uint32_t* bp = d.b2 + (int64_t)(jv ? j : 0) * w2;
-  const uint16_t* gp = d.gamma + (int64_t)i * K + 8 * g;
   const int64_t nsteps = K / 32;
   const int64_t c0 = nsteps * sidx / S, c1 = nsteps * (sidx + 1) / S;
+  const int64_t kb = c0 * 32;
+  uint16_t* sGh = reinterpret_cast<uint16_t*>(sG);
+  uint16_t* sGl = sGh + gd.kspan;
+
+  u32x4_t xa[kDbaSteps];
+  uint32_t bw[kDbaSteps];
+  auto load = [&](int64_t sb) {
+#pragma unroll
+    for (int q = 0; q < kDbaSteps; ++q) {
+      const int64_t st = min(sb + (int64_t)q * kDbaWaves, c1 - 1);  // clamped: a valid step
+      const int64_t k = st * 32;
+      xa[q] = *reinterpret_cast<const u32x4_t*>(xp + k);
+      bw[q] = bp[(k + 8 * g) >> 5];
+    }
+  };
+  const int64_t sb0 = c0 + wave;
+  if (sb0 < c1) load(sb0);
+  // gamma_i over [kb, 32 c1) split into exact bf16 halves, once
+  for (int64_t k = kb + threadIdx.x; k < c1 * 32; k += 1024) {
+    uint32_t hi, lo;
+    split_f16(half_bits_to_f32(d.gamma[(int64_t)i * K + k]), hi, lo);
+    sGh[k - kb] = (uint16_t)hi;
+    sGl[k - kb] = (uint16_t)lo;
+  }
+  __syncthreads();
+
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
   const u32x4_t zero = {0u, 0u, 0u, 0u};
-#pragma unroll 2
-  for (int64_t st = c0 + wave; st < c1; st += 4) {
-    const int64_t k = st * 32;
-    const u32x4_t xa = xv ? *reinterpret_cast<const u32x4_t*>(xp + k) : zero;
-    const u32x4_t gv = *reinterpret_cast<const u32x4_t*>(gp + k);
-    const uint32_t bits = (bp[(k + 8 * g) >> 5] >> ((k + 8 * g) & 31)) & 0xFFu;
-    u32x4_t bh, bl;
+  for (int64_t sb = sb0; sb < c1; sb += kDbaWaves * kDbaSteps) {
+    if (sb != sb0) load(sb);
 #pragma unroll
-    for (int e2 = 0; e2 < 4; ++e2) {
-      uint32_t h0, l0, h1, l1;
-      split_f16(half_bits_to_f32(gv[e2] & 0xFFFFu), h0, l0);
-      split_f16(half_bits_to_f32(gv[e2] >> 16), h1, l1);
-      const uint32_t f0 = ((bits >> (2 * e2)) & 1u) ? 0u : 0x8000u;
-      const uint32_t f1 = ((bits >> (2 * e2 + 1)) & 1u) ? 0u : 0x8000u;
-      bh[e2] = jv ? ((h0 ^ f0) | ((h1 ^ f1) << 16)) : 0u;
-      bl[e2] = jv ? ((l0 ^ f0) | ((l1 ^ f1) << 16)) : 0u;
+    for (int q = 0; q < kDbaSteps; ++q) {
+      const int64_t st = sb + (int64_t)q * kDbaWaves;
+      const bool sv = st < c1 && xv;  // wave-uniform st; rows past M add zero
+      const int64_t ko = min(st, c1 - 1) * 32 + 8 * g - kb;  // this lane's 8 gamma halves
+      const u32x4_t gh = *reinterpret_cast<const u32x4_t*>(sGh + ko);
+      const u32x4_t gl = *reinterpret_cast<const u32x4_t*>(sGl + ko);
+      // sign masks: bit e of the byte clear -> flip the sign of element e
+      const uint32_t nb = ~(bw[q] >> ((st * 32 + 8 * g) & 31));
+      u32x4_t bh, bl;
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) {
+        const uint32_t f = (((nb >> (2 * e2)) & 1u) << 15) | (((nb >> (2 * e2 + 1)) & 1u) << 31);
+        bh[e2] = jv ? (gh[e2] ^ f) : 0u;
+        bl[e2] = jv ? (gl[e2] ^ f) : 0u;
+      }
+      const u32x4_t xq = sv ? xa[q] : zero;
+      acc = mfma16x16x32(as_bf16x8(xq), as_bf16x8(bh), acc);
+      acc = mfma16x16x32(as_bf16x8(xq), as_bf16x8(bl), acc);
     }
-    acc = mfma16x16x32(as_bf16x8(xa), as_bf16x8(bh), acc);
-    acc = mfma16x16x32(as_bf16x8(xa), as_bf16x8(bl), acc);
   }
 #pragma unroll
   for (int v = 0; v < 4; ++v) sRed[wave][lane * 4 + v] = acc[v];
   __syncthreads();
+  if (threadIdx.x >= 256) return;
   const int e = threadIdx.x;
-  const float sum = (sRed[0][e] + sRed[1][e]) + (sRed[2][e] + sRed[3][e]);
+  float sum = 0.0f;
+#pragma unroll
+  for (int w = 0; w < kDbaWaves; ++w) sum += sRed[w][e];
   const int l = e >> 2, v = e & 3;
   const int64_t m = m0 + 4 * (l >> 4) + v;  // MFMA output row
   const int jo = j0 + (l & 15);             // MFMA output column
@@ -105,6 +153,10 @@ __global__ __launch_bounds__(256) void k_dba_t_mfma(DbaArgs d, const uint16_t* _
     tr[i * d.R + jo] = val;
     tr[lr + i * d.R + jo] = val;
   }
+}
+
+__global__ __launch_bounds__(256) void k_dba_beff(DbaArgs d, int64_t N, uint16_t* __restrict__ beff) {
+  dba_beff_item(d, N, beff, (int64_t)blockIdx.x * 256 + threadIdx.x);
 }
 
 // t' for float32 x (float32 arithmetic): one wave per (m, i, j), lanes split K.
@@ -133,29 +185,46 @@ __global__ __launch_bounds__(256) void k_dba_t_valu(DbaArgs d, const float* __re
 }  // namespace
 
 int dba_t_splits(int64_t M, int64_t K, int xdt, int R, int ell) {
-  // one pass for M > 16 (the prefill kernels read t2 once per tile row; split
-  // partials there would be re-added per tile)
-  if (xdt != DT_BF16 || M > 16) return 1;
+  // enough workgroups for the chip; at M > 16 at most 4 splits (the prefill
+  // kernels re-add the split partials of every tile row they read)
+  if (xdt != DT_BF16) return 1;
   const int64_t steps = K / 32, mtiles = (M + 15) / 16, ych = (int64_t)ell * ((R + 15) / 16);
-  int64_t s = std::min<int64_t>(steps / 4, (256 + mtiles * ych - 1) / (mtiles * ych));
-  s = std::min<int64_t>(s, 64);
+  int64_t s = std::min<int64_t>(steps / kDbaWaves, (256 + mtiles * ych - 1) / (mtiles * ych));
+  s = std::min<int64_t>(s, M > 16 ? 4 : 64);
   return (int)std::max<int64_t>(s, 1);
 }
 
 hipError_t launch_dba_prep(const DbaArgs& d, const void* x, int xdt, int64_t M, int64_t N, int64_t K, float* t2,
                            int splits, uint16_t* beff, hipStream_t s) {
   const int64_t lr = (int64_t)d.ell * d.R;
+  if (xdt == DT_BF16 && M > 0) {
+    DbaGrid gd;
+    gd.mtiles = (M + 15) / 16;
+    gd.rch = (d.R + 15) / 16;
+    gd.splits = splits;
+    gd.tblocks = gd.mtiles * d.ell * gd.rch * splits;
+    const int64_t nsteps = K / 32;
+    gd.kspan = 32 * ((nsteps + splits - 1) / splits + 1);
+    const size_t shmem = (size_t)gd.kspan * 4;
+    if (shmem > 96 * 1024) return hipErrorInvalidValue;
+    static bool attr = false;
+    if (!attr) {
+      const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_dba_prep),
+                                               hipFuncAttributeMaxDynamicSharedMemorySize, 96 * 1024);
+      if (e != hipSuccess) return e;
+      attr = true;
+    }
+    const int64_t eblocks = (N * lr + 1023) / 1024;
+    hipLaunchKernelGGL(k_dba_prep, dim3((unsigned)(gd.tblocks + eblocks)), dim3(1024), shmem, s, d, gd,
+                       reinterpret_cast<const uint16_t*>(x), M, N, K, t2, beff);
+    return hipGetLastError();
+  }
   hipLaunchKernelGGL(k_dba_beff, dim3((unsigned)((N * lr + 255) / 256)), dim3(256), 0, s, d, N, beff);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess || M == 0) return e;
-  if (xdt == DT_BF16) {
-    dim3 grid((unsigned)((M + 15) / 16), (unsigned)(d.ell * ((d.R + 15) / 16)), (unsigned)splits);
-    hipLaunchKernelGGL(k_dba_t_mfma, grid, dim3(256), 0, s, d, reinterpret_cast<const uint16_t*>(x), M, K, t2);
-  } else {
-    if (splits != 1) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_dba_t_valu, dim3((unsigned)((M * lr + 3) / 4)), dim3(256), 0, s, d,
-                       reinterpret_cast<const float*>(x), M, K, t2);
-  }
+  if (splits != 1) return hipErrorInvalidValue;
+  hipLaunchKernelGGL(k_dba_t_valu, dim3((unsigned)((M * lr + 3) / 4)), dim3(256), 0, s, d,
+                     reinterpret_cast<const float*>(x), M, K, t2);
   return hipGetLastError();
 }
 

@@ -482,16 +482,19 @@ __global__ __launch_bounds__(512, 1) void k_gemm(GemmParams P, Levels lv) {
         float tv[32];
 #pragma unroll
         for (int i = 0; i < 32; ++i) tv[i] = 0.0f;
-        if (a.t_splits == 1 && r % 4 == 0) {
-          // all eight 16-byte loads in flight at once (clamped addresses, zeroed at use)
-          const float* tq = a.t + (mv ? m : M - 1) * (int64_t)r;
-          f32x4_t v[8];
+        if (r % 4 == 0) {
+          // per split, all eight 16-byte loads in flight at once (clamped
+          // addresses, zeroed at use); splits added in order
+          for (int sp = 0; sp < a.t_splits; ++sp) {
+            const float* tq = a.t + ((int64_t)sp * a.M + (mv ? m : M - 1)) * r;
+            f32x4_t v[8];
 #pragma unroll
-          for (int q4 = 0; q4 < 8; ++q4) v[q4] = *reinterpret_cast<const f32x4_t*>(tq + min(32 * aa + 4 * q4, r - 4));
+            for (int q4 = 0; q4 < 8; ++q4) v[q4] = *reinterpret_cast<const f32x4_t*>(tq + min(32 * aa + 4 * q4, r - 4));
 #pragma unroll
-          for (int q4 = 0; q4 < 8; ++q4)
+            for (int q4 = 0; q4 < 8; ++q4)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) tv[4 * q4 + e] = (32 * aa + 4 * q4 < r) ? v[q4][e] : 0.0f;
+              for (int e = 0; e < 4; ++e) tv[4 * q4 + e] += (32 * aa + 4 * q4 < r) ? v[q4][e] : 0.0f;
+          }
         } else {
           for (int sp = 0; sp < a.t_splits; ++sp) {
             const float* tq = a.t + ((int64_t)sp * a.M + (mv ? m : M - 1)) * r;

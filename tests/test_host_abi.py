@@ -222,5 +222,5 @@ def test_dba_validation_and_workspace():
     assert call(good, wsb=64) == "QLR_ERR_WORKSPACE"
     # workspace: [t' | t'] float32 splits x M x 2 l R, then the alpha-signed factor N x 2 l R bf16
     need = qlr.workspace_bytes(qlr.OP_LINEAR_DBA, 2048, 4096, 4096, 16)
-    assert need == 2048 * 32 * 4 + 4096 * 32 * 2
+    assert need == 2 * 2048 * 32 * 4 + 4096 * 32 * 2  # two K splits of the first stage at M = 2048
     assert qlr.workspace_bytes(qlr.OP_LINEAR_DBA, 0, 64, 128, 16) == 64 * 32 * 2
