@@ -21,6 +21,8 @@ Pages (titles as printed):
     layer; section 1: the quantized backbone is frozen and adapters are trained
     (the backward in ``linear``).
   * "LoRDBA" section 2: the double-binary adapter branch (``dba``).
+  * "QFT" (gist.science summary), section 2.2: the hybrid outlier split
+    (``outliers``).
 
 Every function here is pinned by a ``-m "not gpu"`` test against something
 other than itself (closed forms, brute force over exact rationals, invariants,
@@ -32,12 +34,12 @@ from .quant import (widen, block_absmax, nearest_codes, pack_codes, unpack_codes
                     qweight_sizes, QuantizedWeight)
 from .linear import (lora_t, linear, linear_tolerance, mixed, linear_backward,
                      linear_backward_tolerance, adapter_grads, adapter_grads_tolerance)
-from . import dba
+from . import dba, outliers
 
 __all__ = [
     "normal_quantile", "quantile_codebook", "widen", "block_absmax", "nearest_codes",
     "pack_codes", "unpack_codes", "double_quantize", "dequantize_scales", "dequantize",
     "quantize", "qweight_sizes", "QuantizedWeight", "lora_t", "linear",
     "linear_tolerance", "mixed", "linear_backward", "linear_backward_tolerance", "adapter_grads",
-    "adapter_grads_tolerance", "dba",
+    "adapter_grads_tolerance", "dba", "outliers",
 ]
