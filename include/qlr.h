@@ -69,7 +69,14 @@ typedef enum {
   QLR_PATH_GEMM = 3  /* bf16 x, any M: LDS-tiled prefill GEMM (bf16 MFMA, fp32 accumulate) */
 } qlr_path;
 
-typedef enum { QLR_OP_QUANTIZE = 0, QLR_OP_LINEAR = 1, QLR_OP_LINEAR_BWD = 2, QLR_OP_LINEAR_DBA = 3 } qlr_op;
+typedef enum {
+  QLR_OP_QUANTIZE = 0,
+  QLR_OP_LINEAR = 1,
+  QLR_OP_LINEAR_BWD = 2,
+  QLR_OP_LINEAR_DBA = 3,
+  QLR_OP_QUANTIZE_OUTLIERS = 4, /* M = the outlier count k, N = rows, K = cols */
+  QLR_OP_LINEAR_OUTLIERS = 5
+} qlr_op;
 
 /*
  * A quantized frozen weight (QLoRA page, sections "1. 4-bit NormalFloat" and
@@ -125,6 +132,21 @@ typedef struct {
   const uint16_t* beta;  /* device, fp16 bits, ell x R */
   const uint16_t* gamma; /* device, fp16 bits, ell x cols */
 } qlr_dba;
+
+/*
+ * Sparse side channel of a weight's outliers (QFT page, section 2.2 "Hybrid
+ * feature quantizer"): CSR by weight row, columns ascending within a row.
+ * val holds float32 residuals w - w' against the dense part's dequantized value
+ * at that position (the quantile codebook has no exact zero level).
+ */
+typedef struct {
+  int64_t rows;     /* = the weight's rows */
+  int64_t cols;     /* = the weight's cols */
+  int64_t nnz;      /* k */
+  int32_t* row_ptr; /* device, rows + 1 */
+  int32_t* col;     /* device, nnz */
+  float* val;       /* device, nnz */
+} qlr_sparse;
 
 /* Library version (major*10000 + minor*100 + patch). */
 int qlr_version(void);
@@ -237,6 +259,37 @@ qlr_status qlr_linear_fwd(const void* x, qlr_dtype xdt, int64_t M, const qlr_qwe
 qlr_status qlr_linear_fwd_mixed(const qlr_layer* layers, int32_t n, int64_t M, qlr_dtype xdt,
                                 qlr_dtype abdt, qlr_dtype ydt, void* ws, size_t ws_bytes,
                                 void* stream);
+
+/*
+ * Quantize with a hybrid outlier split (QFT page, section 2.2: about 1 % of
+ * the weights, the outliers that stretch the range, kept at full precision;
+ * the dense rest quantized).  The k entries of largest |w| (float32 after
+ * exact widening; ties to the lower flat index) are set to 0 and the result is
+ * quantized as qlr_quantize does (out); sp receives, for each of them in
+ * row-major order, its column and the float32 residual fl32(w - w'), w' the
+ * dense part's dequantized value there, and sp->row_ptr the CSR row offsets.
+ * The caller sets sp->rows, sp->cols, sp->nnz = k and provides its buffers.
+ * rows * cols < 2^31, 0 <= k <= rows * cols.  ws (device) >=
+ * qlr_workspace_bytes(QLR_OP_QUANTIZE_OUTLIERS, k, rows, cols, 0).
+ * BLOCKING (reads the non-finite flags).  Errors: as qlr_quantize, plus
+ * QLR_ERR_SHAPE for k or a mismatching sp header.
+ */
+qlr_status qlr_quantize_outliers(const void* W, qlr_dtype wdt, int64_t rows, int64_t cols, int32_t bits,
+                                 int32_t block, int64_t k, qlr_qweight* out, qlr_sparse* sp, void* ws,
+                                 size_t ws_bytes, void* stream);
+
+/*
+ * Forward with the sparse side channel: y = x W'^T + x S^T + scale (x A^T) B^T,
+ * S the CSR outliers of qlr_quantize_outliers (any S of the weight's shape).
+ * The sparse term is formed in float32 (outliers in CSR order) and added to
+ * each output before rounding.  Arguments otherwise as qlr_linear_fwd; the
+ * error bound's S also sums |x[m, col] val| over the row's outliers.
+ * ws >= qlr_workspace_bytes(QLR_OP_LINEAR_OUTLIERS, M, rows, cols, r).
+ * Asynchronous, allocation-free.
+ */
+qlr_status qlr_linear_fwd_outliers(const void* x, qlr_dtype xdt, int64_t M, const qlr_qweight* w,
+                                   const qlr_sparse* sp, const void* A, const void* B, qlr_dtype abdt, int32_t r,
+                                   float scale, void* y, qlr_dtype ydt, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Forward with a double-binary adapter in adapter mode (LoRDBA page,

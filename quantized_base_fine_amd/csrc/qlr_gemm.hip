@@ -242,6 +242,7 @@ struct GemmLayer {
   const float* t;   // splits x M x r partial sums of x A^T (r > 0)
   const void* B;    // N x r
   void* y;
+  const float* addend;  // M x N float32 or null (forward only)
   int64_t N, K;
   int32_t r, t_splits;
   float scale;
@@ -292,6 +293,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm(GemmParams P, Levels lv) {
   a.r = Lr.r;
   a.scale = Lr.scale;
   a.y = Lr.y;
+  a.addend = Lr.addend;
   const int64_t N = a.N, K = a.K;
   const int64_t KC = TR ? N : K;  // contraction length (a multiple of 64)
   const int64_t NO = TR ? K : N;  // output columns
@@ -671,6 +673,21 @@ __global__ __launch_bounds__(512, 1) void k_gemm(GemmParams P, Levels lv) {
     // lane (fr, h), register v of tile (i, c) -> row 32 i + 8 (v / 4) + 4 h + v % 4, column 32 c + fr
     constexpr int ES = (YDT == DT_F32) ? 4 : 2;
     constexpr uint32_t RS = 128 * ES + 16;  // padded row stride (bytes)
+    if (!TR && a.addend) {
+      // the sparse side channel's term, added before rounding (32 lanes read 32
+      // consecutive columns of one row)
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int c = 0; c < 2; ++c)
+#pragma unroll
+          for (int v = 0; v < 16; ++v) {
+            const int64_t gr = m0 + 128 * mh + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+            const int64_t gc = n0 + 64 * nh + 32 * c + fr;
+            const float ad = a.addend[(gr < M ? gr : M - 1) * NO + (gc < NO ? gc : NO - 1)];
+            acc[i][c][v] += (gr < M && gc < NO) ? ad : 0.0f;
+          }
+    }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -772,6 +789,7 @@ hipError_t launch_gemm_t(const LinearArgs* ls, int n, const Levels& lv, hipStrea
       L.t = a.t;
       L.B = a.B;
       L.y = a.y;
+      L.addend = a.addend;
       L.N = a.N;
       L.K = a.K;
       L.r = a.r;

@@ -664,7 +664,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
         }
       }
     }
-    const float out = fmaf(a.scale, lo, s);
+    float out = fmaf(a.scale, lo, s);
+    if (a.addend && ov) out += a.addend[(int64_t)m * N + nn];
     const uint32_t yo = buf_off(ov, (uint32_t)(((int64_t)m * N + nn) * ES));
     if constexpr (YDT == DT_F32) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(out), yr, yo, 0, 0);
     else __builtin_amdgcn_raw_buffer_store_b16((uint16_t)f32_to_bf16_bits(out), yr, yo, 0, 0);
@@ -697,7 +698,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) s += sRed[w * 16 + o];
         const int64_t nn = tl * 16 + o;
-        const float out = fmaf(a.scale, lo, s);
+        float out = fmaf(a.scale, lo, s);
+        if (a.addend && tid < 256 && j == 0 && nn < N) out += a.addend[nn];
         const uint32_t yo = buf_off(tid < 256 && j == 0 && nn < N, (uint32_t)(nn * ES));
         if constexpr (YDT == DT_F32) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(out), yr, yo, 0, 0);
         else __builtin_amdgcn_raw_buffer_store_b16((uint16_t)f32_to_bf16_bits(out), yr, yo, 0, 0);

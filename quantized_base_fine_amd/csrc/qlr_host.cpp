@@ -232,11 +232,13 @@ qlr::LinearArgs make_args(const LinearCheck& c, float scale, char* ws, int split
   return a;
 }
 
-qlr_status run_linear(const LinearCheck& c, float scale, char* ws, qlr_path path, hipStream_t s) {
+qlr_status run_linear(const LinearCheck& c, float scale, char* ws, qlr_path path, hipStream_t s,
+                      const float* addend = nullptr) {
   if (c.M == 0) return QLR_OK;
   hipError_t e = hipSuccess;
   const int splits = qlr::lora_t_splits(c.M, c.w->cols, (int)c.xdt, (int)c.abdt);
-  const qlr::LinearArgs a = make_args(c, scale, ws, splits);
+  qlr::LinearArgs a = make_args(c, scale, ws, splits);
+  a.addend = addend;
   if (c.r > 0 && !(path == QLR_PATH_GEMV && qlr::gemv_fuses_adapter(a))) {
     e = qlr::launch_lora_t(c.x, (int)c.xdt, c.M, c.w->cols, c.A, (int)c.abdt, c.r,
                            reinterpret_cast<float*>(ws), splits, s);
@@ -328,6 +330,17 @@ qlr_status qlr_workspace_bytes(qlr_op op, int64_t M, int64_t N, int64_t K, int32
   if (!bytes) return fail(QLR_ERR_NULL, "bytes is NULL");
   if (op == QLR_OP_QUANTIZE) {
     *bytes = 256;
+    return QLR_OK;
+  }
+  if (op == QLR_OP_QUANTIZE_OUTLIERS) {
+    // N = rows, K = cols, M = the outlier count
+    if (M < 0 || N < 0 || K < 0) return fail(QLR_ERR_SHAPE, "negative size");
+    *bytes = std::max<size_t>(256, qlr::outlier_ws_bytes(N * K, M) + 256);
+    return QLR_OK;
+  }
+  if (op == QLR_OP_LINEAR_OUTLIERS) {
+    if (M < 0 || N < 0 || K < 0 || r < 0) return fail(QLR_ERR_SHAPE, "negative size");
+    *bytes = linear_ws_bytes(M, K, r) + (((size_t)M * (size_t)N * 4 + 255) & ~(size_t)255);
     return QLR_OK;
   }
   if (op == QLR_OP_LINEAR_DBA) {
@@ -660,6 +673,91 @@ qlr_status qlr_linear_fwd_dba(const void* x, qlr_dtype xdt, int64_t M, const qlr
   }
   if (e != hipSuccess) return hip_fail(e, "linear launch");
   return QLR_OK;
+}
+
+qlr_status qlr_quantize_outliers(const void* W, qlr_dtype wdt, int64_t rows, int64_t cols, int32_t bits,
+                                 int32_t block, int64_t k, qlr_qweight* out, qlr_sparse* sp, void* ws,
+                                 size_t ws_bytes, void* stream) {
+  if (!W || !out || !sp) return fail(QLR_ERR_NULL, "W, out or sp is NULL");
+  if (!dtype_ok(wdt)) return fail(QLR_ERR_DTYPE, "W dtype must be f32, f16 or bf16");
+  if (!bits_ok(bits)) return fail(QLR_ERR_BITS, "bits %d not in {2,3,4,8}", bits);
+  if (block != QLR_BLOCK) return fail(QLR_ERR_BLOCK, "block %d, expected 64", block);
+  if (rows <= 0 || cols <= 0) return fail(QLR_ERR_SHAPE, "rows and cols must be positive");
+  if (rows * cols >= (INT64_C(1) << 31)) return fail(QLR_ERR_SHAPE, "rows * cols must be below 2^31");
+  if (k < 0 || k > rows * cols) return fail(QLR_ERR_SHAPE, "k must be in [0, rows * cols]");
+  if (out->rows != rows || out->cols != cols || out->bits != bits || out->block != block)
+    return fail(QLR_ERR_SHAPE, "out header does not match rows/cols/bits/block");
+  qlr_status st = check_qweight(out);
+  if (st != QLR_OK) return st;
+  if (sp->rows != rows || sp->cols != cols || sp->nnz != k) return fail(QLR_ERR_SHAPE, "sp header does not match");
+  if (!sp->row_ptr || (k > 0 && (!sp->col || !sp->val))) return fail(QLR_ERR_NULL, "sparse buffer is NULL");
+  if (!aligned16(W) || !aligned16(sp->row_ptr) || (k > 0 && (!aligned16(sp->col) || !aligned16(sp->val))))
+    return fail(QLR_ERR_ALIGN, "W and the sparse buffers must be 16-byte aligned");
+  size_t need = 0;
+  qlr_workspace_bytes(QLR_OP_QUANTIZE_OUTLIERS, k, rows, cols, 0, &need);
+  if (!ws || ws_bytes < need) return fail(QLR_ERR_WORKSPACE, "workspace of %zu bytes required", need);
+  if (!aligned16(ws)) return fail(QLR_ERR_ALIGN, "workspace must be 16-byte aligned");
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  const qlr::Levels lv = levels_arg(bits);
+  hipError_t e;
+  uint32_t* qflag = reinterpret_cast<uint32_t*>(ws);  // the dense quantize's non-finite flag
+  char* rest = reinterpret_cast<char*>(ws) + 256;
+  void* dense = const_cast<void*>(W);
+  uint32_t* sflag = nullptr;
+  int32_t* oidx = nullptr;
+  float* oval = nullptr;
+  e = qlr::launch_fill_u32(qflag, 0u, 1, s);
+  if (e != hipSuccess) return hip_fail(e, "flag clear");
+  if (k > 0) {
+    e = qlr::launch_outlier_split(W, (int)wdt, rows * cols, k, rest, &dense, &sflag, &oidx, &oval, s);
+    if (e != hipSuccess) return hip_fail(e, "outlier selection launch");
+  }
+  e = qlr::launch_quantize(dense, (int)wdt, rows * cols, bits, lv, reinterpret_cast<uint8_t*>(out->codes),
+                           out->absmax_q8, out->absmax_c, qflag, s);
+  if (e != hipSuccess) return hip_fail(e, "quantize launch");
+  e = qlr::launch_outlier_finish(rows, cols, k, bits, lv, reinterpret_cast<const uint8_t*>(out->codes),
+                                 out->absmax_q8, out->absmax_c, oidx, oval, sp->row_ptr, sp->col, sp->val, s);
+  if (e != hipSuccess) return hip_fail(e, "outlier finish launch");
+  uint32_t flags[2] = {0, 0};
+  e = hipMemcpyAsync(&flags[0], qflag, 4, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess && sflag) e = hipMemcpyAsync(&flags[1], sflag, 4, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess) e = hipStreamSynchronize(s);
+  if (e != hipSuccess) return hip_fail(e, "flag read");
+  if (flags[0] || flags[1]) return fail(QLR_ERR_NONFINITE, "W holds NaN or Inf");
+  return QLR_OK;
+}
+
+qlr_status qlr_linear_fwd_outliers(const void* x, qlr_dtype xdt, int64_t M, const qlr_qweight* w,
+                                   const qlr_sparse* sp, const void* A, const void* B, qlr_dtype abdt, int32_t r,
+                                   float scale, void* y, qlr_dtype ydt, void* ws, size_t ws_bytes, void* stream) {
+  if (!sp) return fail(QLR_ERR_NULL, "sp is NULL");
+  const LinearCheck c{x, xdt, M, w, A, B, abdt, r, y, ydt};
+  qlr_status st = check_linear(c);
+  if (st != QLR_OK) return st;
+  if (sp->rows != w->rows || sp->cols != w->cols || sp->nnz < 0) return fail(QLR_ERR_SHAPE, "sp does not match w");
+  if (!sp->row_ptr || (sp->nnz > 0 && (!sp->col || !sp->val))) return fail(QLR_ERR_NULL, "sparse buffer is NULL");
+  if (!aligned16(sp->row_ptr) || (sp->nnz > 0 && (!aligned16(sp->col) || !aligned16(sp->val))))
+    return fail(QLR_ERR_ALIGN, "sparse buffers must be 16-byte aligned");
+  size_t need = 0;
+  qlr_workspace_bytes(QLR_OP_LINEAR_OUTLIERS, M, w->rows, w->cols, r, &need);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(QLR_ERR_WORKSPACE, "workspace of %zu bytes required, got %zu", need, ws ? ws_bytes : (size_t)0);
+  if (need > 0 && !aligned16(ws)) return fail(QLR_ERR_ALIGN, "workspace must be 16-byte aligned");
+  qlr_path path;
+  st = pick_path(M, xdt, abdt, r, &path);
+  if (st != QLR_OK) return st;
+  if (M == 0) return QLR_OK;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  char* wsp = reinterpret_cast<char*>(ws);
+  float* C = reinterpret_cast<float*>(wsp + linear_ws_bytes(M, w->cols, r));
+  const float* addend = nullptr;
+  if (sp->nnz > 0) {
+    const hipError_t e = qlr::launch_sparse_addend(x, (int)xdt, M, w->cols, w->rows, sp->row_ptr, sp->col, sp->val,
+                                                   C, s);
+    if (e != hipSuccess) return hip_fail(e, "sparse term launch");
+    addend = C;
+  }
+  return run_linear(c, scale, wsp, path, s, addend);
 }
 
 qlr_status qlr_force_path(qlr_path path) {

@@ -63,6 +63,9 @@ struct LinearArgs {
   float scale;
   void* y;
   int ydt;
+  // optional float32 M x N term added to every output before rounding (the
+  // sparse side channel's x S^T); null when absent
+  const float* addend = nullptr;
 };
 
 // float32 path: any dtypes, any M.
@@ -96,6 +99,21 @@ int dba_t_splits(int64_t M, int64_t K, int xdt, int R, int ell);
 // branch as an exact rank-2 ell R adapter with scale 1.
 hipError_t launch_dba_prep(const DbaArgs& d, const void* x, int xdt, int64_t M, int64_t N, int64_t K, float* t2,
                            int splits, uint16_t* beff, hipStream_t s);
+
+// ---- hybrid outlier split
+size_t outlier_ws_bytes(int64_t numel, int64_t k);
+// Select the k largest |w| (ties to the lower index), compact their flat
+// indices (ascending) and values, and write W with them zeroed (same dtype) into
+// the workspace; *flag (device) becomes nonzero if W holds NaN or Inf.
+hipError_t launch_outlier_split(const void* W, int wdt, int64_t numel, int64_t k, void* ws, void** dense,
+                                uint32_t** flag, int32_t** oidx, float** oval, hipStream_t s);
+// After the dense part is quantized: row_ptr, columns, and residuals w - w'.
+hipError_t launch_outlier_finish(int64_t rows, int64_t cols, int64_t k, int bits, const Levels& lv,
+                                 const uint8_t* codes, const uint8_t* q8, const float* cst, const int32_t* oidx,
+                                 const float* oval, int32_t* row_ptr, int32_t* col, float* val, hipStream_t s);
+// C (M x N float32) = x S^T for S in CSR (N rows, K columns).
+hipError_t launch_sparse_addend(const void* x, int xdt, int64_t M, int64_t K, int64_t N, const int32_t* row_ptr,
+                                const int32_t* col, const float* val, float* C, hipStream_t s);
 
 // ---- backward (adapter training)
 // Input gradient dx = dy W' + scale u A on the transposed bf16 GEMM: a.x = dy

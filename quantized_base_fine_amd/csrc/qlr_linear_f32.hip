@@ -260,7 +260,8 @@ __global__ __launch_bounds__(256) void k_linear_f32(LinearArgs a, Levels lv) {
         lo = fmaf(tj, load_elem<BDT>(a.B, n * a.r + j), lo);
       }
       lo = wave_sum(lo);
-      const float out = fmaf(a.scale, lo, base);
+      float out = fmaf(a.scale, lo, base);
+      if (a.addend) out += a.addend[m * a.N + n];
       if (lane == 0) {
         if constexpr (YDT == DT_F32) reinterpret_cast<float*>(a.y)[m * a.N + n] = out;
         else reinterpret_cast<uint16_t*>(a.y)[m * a.N + n] = (uint16_t)f32_to_bf16_bits(out);

@@ -1,0 +1,416 @@
+// Hybrid outlier split of a frozen weight (QFT page, section 2.2 "Hybrid
+// feature quantizer"): the k entries of largest |w| are kept at full precision
+// in a sparse side channel and the dense rest is quantized.  The dense rest
+// uses the blockwise quantile format; the side channel holds, per outlier, the
+// float32 residual w - w' against the dense part's dequantized value there (the
+// codebook has no exact zero level), as CSR by weight row.
+//
+// Selection: the k largest keys |w| (float32 bits, monotone for |w| >= 0), ties
+// to the lower flat index.  A radix select finds the k-th largest key T in
+// three passes over 11, 11 and 9 key bits (per-workgroup LDS histograms merged
+// with global atomics, one single-workgroup step per pass narrowing the prefix);
+// then every key > T is taken and the keys == T in index order until k.
+#include <algorithm>
+
+#include "qlr_internal.h"
+
+namespace qlr {
+
+namespace {
+
+constexpr int kOlBins = 2048;
+constexpr int kOlElems = 4096;  // elements per workgroup in the count / emit passes
+
+template <int WDT>
+__device__ __forceinline__ uint32_t ol_key(const void* W, int64_t i, float* wv) {
+  const float w = load_elem<WDT>(W, i);
+  *wv = w;
+  return __float_as_uint(w) & 0x7FFFFFFFu;
+}
+
+// state: [0] prefix, [1] mask, [2] k still to place below the prefix's bin, [3] keys > prefix counted so far,
+// [4] non-finite flag
+template <int WDT>
+__global__ __launch_bounds__(256) void k_ol_hist(const void* W, int64_t n, int shift, int nbits,
+                                                 uint32_t* __restrict__ state, uint32_t* __restrict__ hist) {
+  __shared__ uint32_t h[kOlBins];
+  for (int b = threadIdx.x; b < kOlBins; b += 256) h[b] = 0;
+  __syncthreads();
+  const uint32_t prefix = state[0], mask = state[1];
+  const uint32_t bmask = (1u << nbits) - 1u;
+  bool bad = false;
+  for (int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (int64_t)gridDim.x * 256) {
+    float w;
+    const uint32_t key = ol_key<WDT>(W, i, &w);
+    bad |= !(fabsf(w) <= 3.402823466e38f);
+    if ((key & mask) == prefix) atomicAdd(&h[(key >> shift) & bmask], 1u);
+  }
+  if (bad) state[4] = 1u;
+  __syncthreads();
+  for (int b = threadIdx.x; b <= (int)bmask; b += 256)
+    if (h[b]) atomicAdd(&hist[b], h[b]);
+}
+
+// one workgroup: find the bin holding the k-th largest remaining key; clears hist for the next pass
+__global__ __launch_bounds__(1024) void k_ol_select(int shift, int nbits, uint32_t* __restrict__ state,
+                                                    uint32_t* __restrict__ hist) {
+  __shared__ uint32_t h[kOlBins];
+  const int nb = 1 << nbits;
+  for (int b = threadIdx.x; b < nb; b += 1024) {
+    h[b] = hist[b];
+    hist[b] = 0;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t need = state[2], above = 0;
+    int b = nb - 1;
+    for (; b > 0; --b) {
+      if (above + h[b] >= need) break;
+      above += h[b];
+    }
+    state[0] |= (uint32_t)b << shift;
+    state[1] |= (uint32_t)(nb - 1) << shift;
+    state[2] = need - above;
+    state[3] += above;
+  }
+}
+
+// per workgroup of kOlElems elements: counts of keys > T and == T
+template <int WDT>
+__global__ __launch_bounds__(256) void k_ol_count(const void* W, int64_t n, const uint32_t* __restrict__ state,
+                                                  uint32_t* __restrict__ cnt) {
+  __shared__ uint32_t sgt, seq;
+  if (threadIdx.x == 0) sgt = seq = 0;
+  __syncthreads();
+  const uint32_t T = state[0];
+  uint32_t gt = 0, eq = 0;
+  const int64_t b0 = (int64_t)blockIdx.x * kOlElems;
+  for (int t = threadIdx.x; t < kOlElems; t += 256) {
+    const int64_t i = b0 + t;
+    if (i >= n) break;
+    float w;
+    const uint32_t key = ol_key<WDT>(W, i, &w);
+    gt += key > T;
+    eq += key == T;
+  }
+  atomicAdd(&sgt, gt);
+  atomicAdd(&seq, eq);
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    cnt[2 * blockIdx.x] = sgt;
+    cnt[2 * blockIdx.x + 1] = seq;
+  }
+}
+
+// one workgroup: per block, the number of ties it takes and its first output slot (in index order)
+__global__ __launch_bounds__(1024) void k_ol_scan(int64_t nblocks, const uint32_t* __restrict__ state,
+                                                  const uint32_t* __restrict__ cnt, uint32_t* __restrict__ plan) {
+  __shared__ uint32_t seq[1024], ssel[1024];
+  __shared__ uint32_t carry_eq, carry_sel;
+  if (threadIdx.x == 0) carry_eq = carry_sel = 0;
+  __syncthreads();
+  const uint32_t need_eq = state[2];
+  for (int64_t c0 = 0; c0 < nblocks; c0 += 1024) {
+    const int64_t b = c0 + threadIdx.x;
+    const uint32_t gt = b < nblocks ? cnt[2 * b] : 0u, eq = b < nblocks ? cnt[2 * b + 1] : 0u;
+    seq[threadIdx.x] = eq;
+    __syncthreads();
+    // inclusive scan of eq (Hillis-Steele)
+    for (int o = 1; o < 1024; o <<= 1) {
+      const uint32_t v = threadIdx.x >= (unsigned)o ? seq[threadIdx.x - o] : 0u;
+      __syncthreads();
+      seq[threadIdx.x] += v;
+      __syncthreads();
+    }
+    const uint32_t eq_before = carry_eq + seq[threadIdx.x] - eq;
+    const uint32_t take = eq_before >= need_eq ? 0u : min(eq, need_eq - eq_before);
+    const uint32_t sel = gt + take;
+    ssel[threadIdx.x] = sel;
+    __syncthreads();
+    for (int o = 1; o < 1024; o <<= 1) {
+      const uint32_t v = threadIdx.x >= (unsigned)o ? ssel[threadIdx.x - o] : 0u;
+      __syncthreads();
+      ssel[threadIdx.x] += v;
+      __syncthreads();
+    }
+    if (b < nblocks) {
+      plan[2 * b] = take;
+      plan[2 * b + 1] = carry_sel + ssel[threadIdx.x] - sel;
+    }
+    __syncthreads();
+    if (threadIdx.x == 1023) {
+      carry_eq += seq[1023];
+      carry_sel += ssel[1023];
+    }
+    __syncthreads();
+  }
+}
+
+// per workgroup: mark, compact (flat index, w) in index order, write the dense copy
+template <int WDT>
+__global__ __launch_bounds__(256) void k_ol_emit(const void* W, int64_t n, const uint32_t* __restrict__ state,
+                                                 const uint32_t* __restrict__ plan, void* __restrict__ dense,
+                                                 int32_t* __restrict__ oidx, float* __restrict__ oval) {
+  // thread t handles elements b0 + 16 t .. + 15 (contiguous, so local ranks follow index order)
+  __shared__ uint32_t seq[256], ssel[256];
+  const uint32_t T = state[0];
+  const int64_t b0 = (int64_t)blockIdx.x * kOlElems + 16 * threadIdx.x;
+  uint32_t keys[16];
+  float ws[16];
+  uint32_t neq = 0;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int64_t i = b0 + e;
+    keys[e] = i < n ? ol_key<WDT>(W, i, &ws[e]) : 0u;
+    if (i >= n) ws[e] = 0.0f;
+    neq += (i < n && keys[e] == T);
+  }
+  seq[threadIdx.x] = neq;
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {
+    const uint32_t v = threadIdx.x >= (unsigned)o ? seq[threadIdx.x - o] : 0u;
+    __syncthreads();
+    seq[threadIdx.x] += v;
+    __syncthreads();
+  }
+  const uint32_t take = plan[2 * blockIdx.x];
+  uint32_t eq_rank = seq[threadIdx.x] - neq;
+  bool sel[16];
+  uint32_t nsel = 0;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int64_t i = b0 + e;
+    const bool valid = i < n;
+    const bool is_eq = valid && keys[e] == T;
+    sel[e] = valid && (keys[e] > T || (is_eq && eq_rank < take));
+    eq_rank += is_eq;
+    nsel += sel[e];
+  }
+  ssel[threadIdx.x] = nsel;
+  __syncthreads();
+  for (int o = 1; o < 256; o <<= 1) {
+    const uint32_t v = threadIdx.x >= (unsigned)o ? ssel[threadIdx.x - o] : 0u;
+    __syncthreads();
+    ssel[threadIdx.x] += v;
+    __syncthreads();
+  }
+  uint32_t pos = plan[2 * blockIdx.x + 1] + ssel[threadIdx.x] - nsel;
+#pragma unroll
+  for (int e = 0; e < 16; ++e) {
+    const int64_t i = b0 + e;
+    if (i >= n) break;
+    if (sel[e]) {
+      oidx[pos] = (int32_t)i;
+      oval[pos] = ws[e];
+      ++pos;
+    }
+    if constexpr (WDT == DT_F32) reinterpret_cast<float*>(dense)[i] = sel[e] ? 0.0f : ws[e];
+    else {
+      const uint16_t raw = reinterpret_cast<const uint16_t*>(W)[i];
+      reinterpret_cast<uint16_t*>(dense)[i] = sel[e] ? (uint16_t)0 : raw;
+    }
+  }
+}
+
+// per outlier: residual against the dense part's dequantized value, and its column
+template <int BITS>
+__global__ __launch_bounds__(256) void k_ol_finish(int64_t k, int64_t cols, const int32_t* __restrict__ oidx,
+                                                   const float* __restrict__ oval, const uint8_t* __restrict__ codes,
+                                                   const uint8_t* __restrict__ q8, const float* __restrict__ cst,
+                                                   Levels lv, int32_t* __restrict__ col, float* __restrict__ val) {
+  const int64_t j = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (j >= k) return;
+  const int64_t flat = oidx[j];
+  const int64_t blk = flat >> 6;
+  const int e = (int)(flat & 63);
+  const int bit0 = BITS * e;
+  const uint8_t* cb = codes + blk * (8 * BITS);
+  uint32_t two = cb[bit0 >> 3];
+  if ((bit0 >> 3) + 1 < 8 * BITS) two |= (uint32_t)cb[(bit0 >> 3) + 1] << 8;
+  const int c = (int)((two >> (bit0 & 7)) & ((1u << BITS) - 1u));
+  {
+    // two products and one difference, each rounded on its own: no fused multiply-add
+#pragma clang fp contract(off)
+    const float ap = (float)q8[blk] * cst[blk >> 8];
+    const float wd = lv.v[c] * ap;
+    val[j] = oval[j] - wd;
+  }
+  col[j] = (int32_t)(flat % cols);
+}
+
+// row_ptr[r] = number of outliers with flat index < r * cols (binary search over the ascending indices)
+__global__ __launch_bounds__(256) void k_ol_rowptr(int64_t rows, int64_t cols, int64_t k,
+                                                   const int32_t* __restrict__ oidx, int32_t* __restrict__ row_ptr) {
+  const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (r > rows) return;
+  const int64_t target = r * cols;
+  int64_t lo = 0, hi = k;
+  while (lo < hi) {
+    const int64_t mid = (lo + hi) >> 1;
+    if ((int64_t)oidx[mid] < target) lo = mid + 1;
+    else hi = mid;
+  }
+  row_ptr[r] = (int32_t)lo;
+}
+
+// C[m][n] = sum over row n's outliers j of val[j] x[m][col[j]] (float32, x widened
+// exactly, outliers in CSR order).  blockIdx.x: MR rows of x, staged in LDS as
+// float32 (MR = 0: one row read from global memory, for rows too long for LDS);
+// blockIdx.y: a range of weight rows, one thread per row.
+template <int XDT, int MR>
+__global__ __launch_bounds__(256) void k_sparse_addend(const void* __restrict__ x, int64_t M, int64_t K, int64_t N,
+                                                       const int32_t* __restrict__ row_ptr,
+                                                       const int32_t* __restrict__ col,
+                                                       const float* __restrict__ val, float* __restrict__ C,
+                                                       int64_t nchunk) {
+  extern __shared__ float sx[];
+  constexpr int R = MR > 0 ? MR : 1;
+  const int64_t m0 = (int64_t)blockIdx.x * R;
+  if constexpr (MR > 0) {
+    for (int64_t idx = threadIdx.x; idx < (int64_t)MR * K; idx += 256) {
+      const int64_t mm = idx / K, k = idx % K;
+      sx[idx] = m0 + mm < M ? load_elem<XDT>(x, (m0 + mm) * K + k) : 0.0f;
+    }
+    __syncthreads();
+  }
+  const int64_t nb = (int64_t)blockIdx.y * nchunk, ne = min(N, nb + nchunk);
+  for (int64_t n = nb + threadIdx.x; n < ne; n += 256) {
+    float acc[R];
+#pragma unroll
+    for (int mm = 0; mm < R; ++mm) acc[mm] = 0.0f;
+    const int32_t j1 = row_ptr[n + 1];
+    for (int32_t j = row_ptr[n]; j < j1; ++j) {
+      const int64_t c = col[j];
+      const float v = val[j];
+#pragma unroll
+      for (int mm = 0; mm < R; ++mm) {
+        const float xv = MR > 0 ? sx[mm * K + c] : load_elem<XDT>(x, (m0 + mm) * K + c);
+        acc[mm] = fmaf(v, xv, acc[mm]);
+      }
+    }
+#pragma unroll
+    for (int mm = 0; mm < R; ++mm)
+      if (m0 + mm < M) C[(m0 + mm) * N + n] = acc[mm];
+  }
+}
+
+template <int XDT, int MR>
+hipError_t sparse_addend_t(const void* x, int64_t M, int64_t K, int64_t N, const int32_t* row_ptr,
+                           const int32_t* col, const float* val, float* C, hipStream_t s) {
+  constexpr int R = MR > 0 ? MR : 1;
+  const int64_t xblocks = (M + R - 1) / R;
+  const int64_t nch = std::max<int64_t>(1, std::min<int64_t>((N + 255) / 256, (512 + xblocks - 1) / xblocks));
+  const int64_t nchunk = (N + nch - 1) / nch;
+  const size_t shmem = MR > 0 ? (size_t)MR * K * 4 : 0;
+  static bool attr = false;
+  if (!attr) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_sparse_addend<XDT, MR>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  hipLaunchKernelGGL((k_sparse_addend<XDT, MR>), dim3((unsigned)xblocks, (unsigned)nch), dim3(256), shmem, s, x, M,
+                     K, N, row_ptr, col, val, C, nchunk);
+  return hipGetLastError();
+}
+
+template <int XDT>
+hipError_t sparse_addend_x(const void* x, int64_t M, int64_t K, int64_t N, const int32_t* row_ptr,
+                           const int32_t* col, const float* val, float* C, hipStream_t s) {
+  const int64_t lim = 128 * 1024;
+  if (M > 4 && 8 * K * 4 <= lim) return sparse_addend_t<XDT, 8>(x, M, K, N, row_ptr, col, val, C, s);
+  if (M > 1 && 4 * K * 4 <= lim) return sparse_addend_t<XDT, 4>(x, M, K, N, row_ptr, col, val, C, s);
+  if (K * 4 <= lim) return sparse_addend_t<XDT, 1>(x, M, K, N, row_ptr, col, val, C, s);
+  return sparse_addend_t<XDT, 0>(x, M, K, N, row_ptr, col, val, C, s);
+}
+
+template <int WDT>
+hipError_t ol_select_emit(const void* W, int64_t n, int64_t k, uint32_t* state, uint32_t* hist, uint32_t* cnt,
+                          uint32_t* plan, void* dense, int32_t* oidx, float* oval, hipStream_t s) {
+  const int hgrid = (int)std::min<int64_t>(1024, (n + 255) / 256);
+  const int shifts[3] = {20, 9, 0}, bits[3] = {11, 11, 9};
+  for (int p = 0; p < 3; ++p) {
+    hipLaunchKernelGGL((k_ol_hist<WDT>), dim3(hgrid), dim3(256), 0, s, W, n, shifts[p], bits[p], state, hist);
+    hipLaunchKernelGGL(k_ol_select, dim3(1), dim3(1024), 0, s, shifts[p], bits[p], state, hist);
+  }
+  const int64_t nblocks = (n + kOlElems - 1) / kOlElems;
+  hipLaunchKernelGGL((k_ol_count<WDT>), dim3((unsigned)nblocks), dim3(256), 0, s, W, n, state, cnt);
+  hipLaunchKernelGGL(k_ol_scan, dim3(1), dim3(1024), 0, s, nblocks, state, cnt, plan);
+  hipLaunchKernelGGL((k_ol_emit<WDT>), dim3((unsigned)nblocks), dim3(256), 0, s, W, n, state, plan, dense, oidx,
+                     oval);
+  return hipGetLastError();
+}
+
+template <int BITS>
+hipError_t ol_finish_b(int64_t k, int64_t cols, const int32_t* oidx, const float* oval, const uint8_t* codes,
+                       const uint8_t* q8, const float* cst, const Levels& lv, int32_t* col, float* val,
+                       hipStream_t s) {
+  hipLaunchKernelGGL((k_ol_finish<BITS>), dim3((unsigned)((k + 255) / 256)), dim3(256), 0, s, k, cols, oidx, oval,
+                     codes, q8, cst, lv, col, val);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+size_t outlier_ws_bytes(int64_t numel, int64_t k) {
+  auto up = [](size_t b) { return (b + 255) & ~(size_t)255; };
+  const int64_t nblocks = (numel + kOlElems - 1) / kOlElems;
+  return up(64) + up(kOlBins * 4) + up((size_t)nblocks * 8) * 2 + up((size_t)k * 4) * 2 + up((size_t)numel * 4);
+}
+
+hipError_t launch_outlier_split(const void* W, int wdt, int64_t numel, int64_t k, void* ws, void** dense,
+                                uint32_t** flag, int32_t** oidx, float** oval, hipStream_t s) {
+  auto up = [](size_t b) { return (b + 255) & ~(size_t)255; };
+  const int64_t nblocks = (numel + kOlElems - 1) / kOlElems;
+  char* p = reinterpret_cast<char*>(ws);
+  uint32_t* state = reinterpret_cast<uint32_t*>(p);
+  p += up(64);
+  uint32_t* hist = reinterpret_cast<uint32_t*>(p);
+  p += up(kOlBins * 4);
+  uint32_t* cnt = reinterpret_cast<uint32_t*>(p);
+  p += up((size_t)nblocks * 8);
+  uint32_t* plan = reinterpret_cast<uint32_t*>(p);
+  p += up((size_t)nblocks * 8);
+  *oidx = reinterpret_cast<int32_t*>(p);
+  p += up((size_t)k * 4);
+  *oval = reinterpret_cast<float*>(p);
+  p += up((size_t)k * 4);
+  *dense = p;
+  *flag = state + 4;
+  // state = {prefix 0, mask 0, k, 0, flag 0}, histogram cleared (fill kernels: no memset nodes)
+  hipError_t e = launch_fill_u32(state, 0u, 16, s);
+  if (e != hipSuccess) return e;
+  e = launch_fill_u32(state + 2, (uint32_t)k, 1, s);
+  if (e != hipSuccess) return e;
+  e = launch_fill_u32(hist, 0u, kOlBins, s);
+  if (e != hipSuccess) return e;
+  switch (wdt) {
+    case DT_F32: return ol_select_emit<DT_F32>(W, numel, k, state, hist, cnt, plan, *dense, *oidx, *oval, s);
+    case DT_F16: return ol_select_emit<DT_F16>(W, numel, k, state, hist, cnt, plan, *dense, *oidx, *oval, s);
+    default: return ol_select_emit<DT_BF16>(W, numel, k, state, hist, cnt, plan, *dense, *oidx, *oval, s);
+  }
+}
+
+hipError_t launch_sparse_addend(const void* x, int xdt, int64_t M, int64_t K, int64_t N, const int32_t* row_ptr,
+                                const int32_t* col, const float* val, float* C, hipStream_t s) {
+  if (M == 0 || N == 0) return hipSuccess;
+  if (xdt == DT_F32) return sparse_addend_x<DT_F32>(x, M, K, N, row_ptr, col, val, C, s);
+  return sparse_addend_x<DT_BF16>(x, M, K, N, row_ptr, col, val, C, s);
+}
+
+hipError_t launch_outlier_finish(int64_t rows, int64_t cols, int64_t k, int bits, const Levels& lv,
+                                 const uint8_t* codes, const uint8_t* q8, const float* cst, const int32_t* oidx,
+                                 const float* oval, int32_t* row_ptr, int32_t* col, float* val, hipStream_t s) {
+  hipLaunchKernelGGL(k_ol_rowptr, dim3((unsigned)((rows + 1 + 255) / 256)), dim3(256), 0, s, rows, cols, k, oidx,
+                     row_ptr);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess || k == 0) return e;
+  switch (bits) {
+    case 2: return ol_finish_b<2>(k, cols, oidx, oval, codes, q8, cst, lv, col, val, s);
+    case 3: return ol_finish_b<3>(k, cols, oidx, oval, codes, q8, cst, lv, col, val, s);
+    case 4: return ol_finish_b<4>(k, cols, oidx, oval, codes, q8, cst, lv, col, val, s);
+    default: return ol_finish_b<8>(k, cols, oidx, oval, codes, q8, cst, lv, col, val, s);
+  }
+}
+
+}  // namespace qlr

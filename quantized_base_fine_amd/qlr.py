@@ -24,6 +24,7 @@ GROUP = 256
 QLR_F32, QLR_F16, QLR_BF16 = 0, 1, 2
 PATH_AUTO, PATH_F32, PATH_GEMV, PATH_GEMM = 0, 1, 2, 3
 OP_QUANTIZE, OP_LINEAR, OP_LINEAR_BWD, OP_LINEAR_DBA = 0, 1, 2, 3
+OP_QUANTIZE_OUTLIERS, OP_LINEAR_OUTLIERS = 4, 5
 
 STATUS = {
     0: "QLR_OK", 1: "QLR_ERR_NULL", 2: "QLR_ERR_SHAPE", 3: "QLR_ERR_DTYPE", 4: "QLR_ERR_BITS",
@@ -61,6 +62,13 @@ class CDba(C.Structure):
     ]
 
 
+class CSparse(C.Structure):
+    _fields_ = [
+        ("rows", C.c_int64), ("cols", C.c_int64), ("nnz", C.c_int64), ("row_ptr", C.c_void_p),
+        ("col", C.c_void_p), ("val", C.c_void_p),
+    ]
+
+
 EXPORTS = {
     "qlr_version": (C.c_int, []),
     "qlr_status_string": (C.c_char_p, [C.c_int]),
@@ -88,6 +96,13 @@ EXPORTS = {
                                  C.c_void_p, C.c_size_t, C.c_void_p]),
     "qlr_linear_fwd_dba": (C.c_int, [C.c_void_p, C.c_int, C.c_int64, C.POINTER(CQWeight), C.POINTER(CDba),
                                      C.c_void_p, C.c_int, C.c_void_p, C.c_size_t, C.c_void_p]),
+    "qlr_quantize_outliers": (C.c_int, [C.c_void_p, C.c_int, C.c_int64, C.c_int64, C.c_int32, C.c_int32,
+                                        C.c_int64, C.POINTER(CQWeight), C.POINTER(CSparse), C.c_void_p,
+                                        C.c_size_t, C.c_void_p]),
+    "qlr_linear_fwd_outliers": (C.c_int, [C.c_void_p, C.c_int, C.c_int64, C.POINTER(CQWeight),
+                                          C.POINTER(CSparse), C.c_void_p, C.c_void_p, C.c_int, C.c_int32,
+                                          C.c_float, C.c_void_p, C.c_int, C.c_void_p, C.c_size_t,
+                                          C.c_void_p]),
     "qlr_force_path": (C.c_int, [C.c_int]),
 }
 
@@ -426,3 +441,81 @@ class DbaCall:
 def linear_dba(x, qw: QWeight, b1, b2, alpha, beta, gamma, out_dtype=None):
     """y = x W'^T + sum_i alpha_i * (((x * gamma_i) B2^T) * beta_i) B1^T; see DbaCall."""
     return DbaCall(x, qw, b1, b2, alpha, beta, gamma, out_dtype=out_dtype)()
+
+
+@dataclass
+class Sparse:
+    """The CSR outlier side channel of a weight: row_ptr (rows + 1) and col (nnz)
+    int32, val (nnz) float32, all on the device."""
+    rows: int
+    cols: int
+    nnz: int
+    row_ptr: "object"
+    col: "object"
+    val: "object"
+
+    def c_struct(self) -> CSparse:
+        return CSparse(self.rows, self.cols, self.nnz, self.row_ptr.data_ptr(), self.col.data_ptr(),
+                       self.val.data_ptr())
+
+    @staticmethod
+    def empty(rows: int, cols: int, nnz: int, device) -> "Sparse":
+        torch = _torch()
+        return Sparse(rows, cols, nnz, torch.empty(rows + 1, dtype=torch.int32, device=device),
+                      torch.empty(max(nnz, 1), dtype=torch.int32, device=device),
+                      torch.empty(max(nnz, 1), dtype=torch.float32, device=device))
+
+
+def quantize_outliers(W, bits: int, k: int, out: Optional[QWeight] = None, sparse: Optional[Sparse] = None,
+                      ws=None):
+    """(QWeight of the dense part, Sparse residuals of the k largest-|w| entries) of a 2-D device tensor."""
+    torch = _torch()
+    _require_cuda(W)
+    W = W.contiguous()
+    rows, cols = W.shape
+    qw = out or QWeight.empty(rows, cols, bits, W.device)
+    sp = sparse or Sparse.empty(rows, cols, k, W.device)
+    if ws is None:
+        ws = torch.empty(workspace_bytes(OP_QUANTIZE_OUTLIERS, k, rows, cols), dtype=torch.uint8,
+                         device=W.device)
+    cw, cs = qw.c_struct(), sp.c_struct()
+    check(lib().qlr_quantize_outliers(W.data_ptr(), _dt(W), rows, cols, bits, BLOCK, k, C.byref(cw), C.byref(cs),
+                                      ws.data_ptr(), ws.numel(), _stream(W.device)))
+    return qw, sp
+
+
+class OutliersCall:
+    """A prepared ``qlr_linear_fwd_outliers`` call: y = x W'^T + x S^T + scale (x A^T) B^T.
+    Marshalled once (the stream current at construction is used); the tensors are
+    kept alive by the object."""
+
+    def __init__(self, x, qw: QWeight, sp: Sparse, A=None, B=None, scale: float = 0.0, out_dtype=None, out=None,
+                 ws=None):
+        torch = _torch()
+        _require_cuda(x, A, B)
+        M = x.shape[0]
+        r = 0 if A is None else A.shape[0]
+        if x.shape[1] != qw.cols or (sp.rows, sp.cols) != (qw.rows, qw.cols):
+            raise ValueError("x (M, K) and the sparse part must fit the weight")
+        if r > 0 and (A.shape != (r, qw.cols) or B.shape != (qw.rows, r) or A.dtype != B.dtype):
+            raise ValueError("A must be (r, K) and B (N, r) with one dtype")
+        self.y = out if out is not None else torch.empty((M, qw.rows), dtype=out_dtype or x.dtype, device=x.device)
+        need = workspace_bytes(OP_LINEAR_OUTLIERS, M, qw.rows, qw.cols, r)
+        if ws is None and need > 0:
+            ws = torch.empty(need, dtype=torch.uint8, device=x.device)
+        self._keep = (x, qw, sp, A, B, ws)
+        self._cw, self._cs = qw.c_struct(), sp.c_struct()
+        abdt = _dt(A) if r > 0 else QLR_BF16
+        self._args = (x.data_ptr(), _dt(x), M, C.byref(self._cw), C.byref(self._cs), _ptr(A), _ptr(B), abdt, r,
+                      float(scale), self.y.data_ptr(), _dt(self.y), _ptr(ws), 0 if ws is None else ws.numel(),
+                      _stream(x.device))
+        self._fn = lib().qlr_linear_fwd_outliers
+
+    def __call__(self):
+        check(self._fn(*self._args))
+        return self.y
+
+
+def linear_outliers(x, qw: QWeight, sp: Sparse, A=None, B=None, scale: float = 0.0, out_dtype=None):
+    """y = x W'^T + x S^T + scale (x A^T) B^T; see OutliersCall."""
+    return OutliersCall(x, qw, sp, A, B, scale, out_dtype=out_dtype)()

@@ -224,3 +224,48 @@ def test_dba_validation_and_workspace():
     need = qlr.workspace_bytes(qlr.OP_LINEAR_DBA, 2048, 4096, 4096, 16)
     assert need == 2 * 2048 * 32 * 4 + 4096 * 32 * 2  # two K splits of the first stage at M = 2048
     assert qlr.workspace_bytes(qlr.OP_LINEAR_DBA, 0, 64, 128, 16) == 64 * 32 * 2
+
+
+def test_outlier_validation_and_workspace():
+    lib = qlr.lib()
+    w = _qw(rows=64, cols=128)
+
+    def quant(k=10, sp=None, W=0x100000, wdt=qlr.QLR_F16, rows=64, cols=128, ws=0x900000, wsb=1 << 24, out=None):
+        sp = sp if sp is not None else qlr.CSparse(rows, cols, k, 0x200000, 0x300000, 0x400000)
+        out = out or _qw(rows=rows, cols=cols)
+        return qlr.STATUS[lib.qlr_quantize_outliers(W, wdt, rows, cols, 4, 64, k, C.byref(out), C.byref(sp), ws,
+                                                    wsb, None)]
+    assert quant(W=0) == "QLR_ERR_NULL"
+    assert quant(wdt=9) == "QLR_ERR_DTYPE"
+    assert quant(k=-1) == "QLR_ERR_SHAPE"
+    assert quant(k=64 * 128 + 1) == "QLR_ERR_SHAPE"
+    assert quant(rows=1 << 16, cols=1 << 15) == "QLR_ERR_SHAPE"  # flat indices must fit int32
+    assert quant(sp=qlr.CSparse(64, 128, 11, 0x200000, 0x300000, 0x400000)) == "QLR_ERR_SHAPE"  # nnz != k
+    assert quant(sp=qlr.CSparse(64, 128, 10, 0x200000, 0, 0x400000)) == "QLR_ERR_NULL"
+    assert quant(sp=qlr.CSparse(64, 128, 10, 0x200004, 0x300000, 0x400000)) == "QLR_ERR_ALIGN"
+    assert quant(ws=0) == "QLR_ERR_WORKSPACE"
+    assert quant(wsb=1024) == "QLR_ERR_WORKSPACE"
+    # workspace: flag, selection state, histogram, per-4096-element counts and plan, the k
+    # (index, value) pairs, and a dense float32-sized copy of the weight (256-byte aligned pieces)
+    up = lambda b: (b + 255) // 256 * 256
+    nel, k = 4096 * 4096, 16777
+    nblk = -(-nel // 4096)
+    assert qlr.workspace_bytes(qlr.OP_QUANTIZE_OUTLIERS, k, 4096, 4096) == (
+        256 + 256 + 2048 * 4 + 2 * up(8 * nblk) + 2 * up(4 * k) + 4 * nel)
+
+    def fwd(sp, M=4, ws=0x900000, wsb=1 << 24):
+        return qlr.STATUS[lib.qlr_linear_fwd_outliers(0x600000, qlr.QLR_BF16, M, C.byref(w),
+                                                      C.byref(sp) if sp else None, 0x500000, 0x500000,
+                                                      qlr.QLR_BF16, 4, 1.0, 0x700000, qlr.QLR_F32, ws, wsb, None)]
+    good = qlr.CSparse(64, 128, 10, 0x200000, 0x300000, 0x400000)
+    assert fwd(None) == "QLR_ERR_NULL"
+    assert fwd(qlr.CSparse(65, 128, 10, 0x200000, 0x300000, 0x400000)) == "QLR_ERR_SHAPE"
+    assert fwd(qlr.CSparse(64, 128, -1, 0x200000, 0x300000, 0x400000)) == "QLR_ERR_SHAPE"
+    assert fwd(qlr.CSparse(64, 128, 10, 0, 0x300000, 0x400000)) == "QLR_ERR_NULL"
+    assert fwd(qlr.CSparse(64, 128, 10, 0x200000, 0x300008, 0x400000)) == "QLR_ERR_ALIGN"
+    assert fwd(good, ws=0) == "QLR_ERR_WORKSPACE"
+    assert fwd(good, wsb=64) == "QLR_ERR_WORKSPACE"
+    assert fwd(good, M=0, ws=0, wsb=0) == "QLR_OK"
+    # the linear workspace, then the M x N float32 sparse term
+    assert qlr.workspace_bytes(qlr.OP_LINEAR_OUTLIERS, 2048, 4096, 4096, 16) == (
+        qlr.workspace_bytes(qlr.OP_LINEAR, 2048, 4096, 4096, 16) + 2048 * 4096 * 4)
