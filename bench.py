@@ -20,6 +20,11 @@ cache, so the decode figure is HBM bandwidth, not cache bandwidth):
   backward base dx = dy W' alone (one transposed GEMM kernel per call)
   dba decode / dba prefill   the forward with a double-binary adapter branch
                 (R = 16, l = 1) in place of the fp16 adapter, at M = 1 (graph) and M = 2048
+  outliers decode / prefill  the forward with the weight's 0.1 % largest-|w| entries
+                split off into a float32 CSR side channel (k = 16777) and the dense
+                rest quantized, with the fp16 adapter, at M = 1 (graph) and M = 2048
+The outlier split itself (qlr_quantize_outliers, blocking) is timed outside the
+step, on one layer.
 Each phase is bracketed by HIP events on the stream its calls run on (events
 between the calls of a phase would add a queue barrier per call).  Calls are
 prepared (marshalled once); the prefill phases are GPU-bound and issued eagerly,
@@ -79,6 +84,18 @@ def dba_bytes(M=M_DECODE, N=N_, K=K_, b=BITS, R=R_, ell=1):
 
 def dba_flops(M=M_PREFILL, N=N_, K=K_, R=R_, ell=1):
     return 2 * M * N * K + 2 * M * ell * R * (K + N)
+
+
+NNZ = int(round(0.001 * N_ * K_))  # the attention weight's planted outliers
+
+
+def outlier_bytes(M=M_DECODE, nnz=NNZ):
+    # the decode bytes plus the CSR side channel (row offsets, columns, float32 values)
+    return decode_bytes(M) + 4 * (N_ + 1) + 8 * nnz
+
+
+def outlier_flops(M=M_PREFILL, nnz=NNZ):
+    return prefill_flops(M) + 2 * M * nnz
 
 
 def quantize_bytes(N=N_, K=K_, b=BITS):
@@ -326,14 +343,20 @@ def main():
     dba_t += [torch.from_numpy(np.ascontiguousarray(a)).to(dev) for a in (ad.alpha, ad.beta, ad.gamma)]
     ws_d1 = torch.empty(qlr.workspace_bytes(qlr.OP_LINEAR_DBA, M_DECODE, N_, K_, R_), dtype=torch.uint8, device=dev)
     ws_dp = torch.empty(qlr.workspace_bytes(qlr.OP_LINEAR_DBA, M_PREFILL, N_, K_, R_), dtype=torch.uint8, device=dev)
+    ws_o1 = torch.empty(max(qlr.workspace_bytes(qlr.OP_LINEAR_OUTLIERS, M_DECODE, N_, K_, R_), 16), dtype=torch.uint8,
+                        device=dev)
+    ws_op = torch.empty(qlr.workspace_bytes(qlr.OP_LINEAR_OUTLIERS, M_PREFILL, N_, K_, R_), dtype=torch.uint8,
+                        device=dev)
+    ws_os = torch.empty(qlr.workspace_bytes(qlr.OP_QUANTIZE_OUTLIERS, NNZ, N_, K_), dtype=torch.uint8, device=dev)
     layers = []
     for _ in range(R):
         qw = qlr.QWeight.empty(N_, K_, BITS, dev)
+        qo, so = qlr.quantize_outliers(W, BITS, NNZ, ws=ws_os)
         A, B = A0.clone(), B0.clone()
         y1 = torch.empty((M_DECODE, N_), dtype=torch.bfloat16, device=dev)
         yp = torch.empty((M_PREFILL, N_), dtype=torch.bfloat16, device=dev)
         layers.append(dict(
-            qw=qw,
+            qw=qw, qo=qo, so=so,
             prefill=qlr.LinearCall(xp, qw, A, B, linp.scale, out=yp, ws=wsp),
             prefill_base=qlr.LinearCall(xp, qw, out=yp),
             decode=qlr.LinearCall(x1, qw, A, B, lin1.scale, out=y1, ws=ws1),
@@ -341,7 +364,9 @@ def main():
             backward=qlr.LinearBwdCall(dyp, xp, qw, A, B, linp.scale, dx=dxp, dA=dA, dB=dB, ws=wsb),
             backward_base=qlr.LinearBwdCall(dyp, xp, qw, dx=dxp),
             dba_decode=qlr.DbaCall(x1, qw, *dba_t, out=y1, ws=ws_d1),
-            dba_prefill=qlr.DbaCall(xp, qw, *dba_t, out=yp, ws=ws_dp)))
+            dba_prefill=qlr.DbaCall(xp, qw, *dba_t, out=yp, ws=ws_dp),
+            ol_decode=qlr.OutliersCall(x1, qo, so, A, B, lin1.scale, out=y1, ws=ws_o1),
+            ol_prefill=qlr.OutliersCall(xp, qo, so, A, B, linp.scale, out=yp, ws=ws_op)))
     if args.copy_calibration:
         src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -382,7 +407,7 @@ def main():
             assert torch.equal(layers[-1]["qw"].codes, ref_codes), "graph replay differs from eager quantize"
 
     PHASES = ("prefill", "prefill_base", "decode", "decode_base", "backward", "backward_base", "dba_decode",
-              "dba_prefill")
+              "dba_prefill", "ol_decode", "ol_prefill")
     mixed = None
     if not args.no_mixed:
         mixed, mixed_flops, mixed_n = build_mixed(torch, qlr, workloads, dev)
@@ -392,7 +417,7 @@ def main():
     # The decode phases (short, launch-bound calls) also run as HIP graphs of the
     # R prepared calls; every replay is checked against the eager outputs first.
     graphs = {}
-    for ph in (() if args.eager else ("decode", "decode_base", "dba_decode")):
+    for ph in (() if args.eager else ("decode", "decode_base", "dba_decode", "ol_decode")):
         for L in layers:
             L[ph]()
         torch.cuda.synchronize()
@@ -429,6 +454,18 @@ def main():
         if mixed is not None:
             mixed()
             marks[3 + len(PHASES)].record(stream)
+
+    # the outlier split of one layer (blocking: it reads the non-finite flags), timed on its own
+    for _ in range(2):
+        qlr.quantize_outliers(W, BITS, NNZ, out=layers[0]["qo"], sparse=layers[0]["so"], ws=ws_os)
+    split_ms = []
+    for _ in range(5):
+        e0, e1 = ev(), ev()
+        e0.record(stream)
+        qlr.quantize_outliers(W, BITS, NNZ, out=layers[0]["qo"], sparse=layers[0]["so"], ws=ws_os)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        split_ms.append(e0.elapsed_time(e1))
 
     nmarks = 4 + len(PHASES)
     for _ in range(args.warmup):
@@ -529,6 +566,17 @@ def main():
             "prefill_tflops": round(dba_flops() / (mean["dba_prefill"] * 1e-6) / 1e12, 1),
             "adapter_bytes": (N_ * R_ + R_ * K_) // 8 + 2 * (N_ + R_ + K_),
             "fp16_adapter_bytes": 2 * R_ * (N_ + K_),
+        },
+        "outliers": {
+            "workload": "attn_proj_4096x4096_nf4_dq_r16 with its 0.1% largest-|w| entries (k=16777) in a float32 "
+                        "CSR side channel",
+            "decode_us": round(mean["ol_decode"], 3),
+            "decode_gbs": round(outlier_bytes() / (mean["ol_decode"] * 1e-6) / 1e9, 1),
+            "decode_bytes_per_call": outlier_bytes(),
+            "prefill_us": round(mean["ol_prefill"], 3),
+            "prefill_tflops": round(outlier_flops() / (mean["ol_prefill"] * 1e-6) / 1e12, 1),
+            "split_us": round(1e3 * sorted(split_ms)[len(split_ms) // 2], 1),
+            "split_note": "qlr_quantize_outliers on one layer, median of 5, includes its flag read and sync",
         },
         "wall_s": round(wall, 3),
     }

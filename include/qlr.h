@@ -280,7 +280,9 @@ qlr_status qlr_quantize_outliers(const void* W, qlr_dtype wdt, int64_t rows, int
 
 /*
  * Forward with the sparse side channel: y = x W'^T + x S^T + scale (x A^T) B^T,
- * S the CSR outliers of qlr_quantize_outliers (any S of the weight's shape).
+ * S the CSR outliers of qlr_quantize_outliers, or any CSR of the weight's shape
+ * with row_ptr nondecreasing from 0 to nnz and columns in [0, cols) (a
+ * malformed one gives wrong values; the kernels clamp every index they read).
  * The sparse term is formed in float32 (outliers in CSR order) and added to
  * each output before rounding.  Arguments otherwise as qlr_linear_fwd; the
  * error bound's S also sums |x[m, col] val| over the row's outliers.

@@ -279,10 +279,11 @@ __device__ __forceinline__ float dot_piece(const u32x4_t& pc, const u32x4_t* xv,
 // every workgroup also computes t = x A^T itself, from A rows read after the
 // code stream has been issued (L2-resident after the first workgroup of each
 // XCD), instead of reading the partial sums of a separate kernel.
-template <int BITS, int YDT, bool XLDS, bool ADP, int D, bool DOT, bool TF>
+template <int BITS, int YDT, bool XLDS, bool ADP, int D, bool DOT, bool TF, bool SPX>
 __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
   static_assert(!DOT || (XLDS && BITS != 3), "the single-row path reads x from LDS and 16-byte pieces of whole codes");
   static_assert(!TF || (DOT && ADP), "the fused adapter product belongs to the single-row path");
+  static_assert(!SPX || DOT, "the fused side channel belongs to the single-row path");
   // per-wave LDS staging buffer: codes and scales, or scales only (single-row path)
   constexpr uint32_t kStageW = DOT ? 16 * CH * 4 : ChunkGeo<BITS>::kStage;
   using G = ChunkGeo<BITS>;
@@ -373,6 +374,29 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
     }
   };
 
+  // Sparse side channel (SPX, a single x row): thread tid & 15 of each wave
+  // holds tile row tid & 15's CSR offsets and its first 4 outliers (clamped,
+  // unconditional loads).  The first tile's offsets are loaded before
+  // everything else and its outliers right after x is in LDS, so both have
+  // long arrived when the tile ends; later tiles load theirs at the tile's end.
+  int64_t sp0 = 0, sp1 = 0;
+  int32_t spc[4] = {0, 0, 0, 0};
+  float spv[4] = {0.f, 0.f, 0.f, 0.f};
+  auto sp_rows = [&](int64_t tile) {
+    const int64_t n = min(tile * 16 + (tid & 15), N - 1);
+    sp0 = max<int64_t>(a.sp_row_ptr[n], 0);
+    sp1 = min<int64_t>(a.sp_row_ptr[n + 1], a.sp_nnz);
+  };
+  auto sp_entries = [&]() {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int64_t j = min(sp0 + e, a.sp_nnz - 1);
+      spc[e] = min<int32_t>(max<int32_t>(a.sp_col[j], 0), (int32_t)(K - 1));
+      spv[e] = a.sp_val[j];
+    }
+  };
+  if constexpr (SPX) sp_rows(blockIdx.x);
+
   // Small x: one coalesced copy into LDS per workgroup (rows at stride K + 8),
   // loaded first, so that waiting for it does not wait for the code stream.
   // Load i is issued only if some thread has a piece in it (a workgroup-wide
@@ -433,6 +457,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
       if (q < tcount) sTP[q] = tp[i];
     }
   }
+  if constexpr (SPX) sp_entries();
   // fused adapter product: lane's 8 elements k0 .. k0 + 7 of every A row j < 16
   // (rows past r and elements past the wave's range read as zero), issued after
   // the table and x are in LDS (issuing them holds the wave for a while)
@@ -682,6 +707,23 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
         if (lane % G::PR == 0) sRed[wave * 16 + (i * 64 + lane) / G::PR] = v;
         accd[i] = 0.0f;
       }
+      if constexpr (SPX) {
+        // side-channel sum of tile row tid (float32, outliers in CSR order) into sRed slot kWaves * 16 + tid
+        if (tl != blockIdx.x) {
+          sp_rows(tl);
+          sp_entries();
+        }
+        if (tid < 16) {
+          auto xv = [&](int32_t c) { return bf16_bits_to_f32(lds_rd16(P.sX + (uint32_t)c * 2u)); };
+          float sum = 0.0f;
+#pragma unroll
+          for (int e = 0; e < 4; ++e)
+            if (sp0 + e < sp1) sum = fmaf(spv[e], xv(spc[e]), sum);
+          for (int64_t j = sp0 + 4; j < sp1; ++j)
+            sum = fmaf(a.sp_val[j], xv(min<int32_t>(max<int32_t>(a.sp_col[j], 0), (int32_t)(K - 1))), sum);
+          sRed[kWaves * 16 + tid] = sum;
+        }
+      }
       __syncthreads();
       if constexpr (TF) {
         // thread (o, j) = (tid / 16 % 16, tid % 16): t_j (the waves' sums, in
@@ -699,6 +741,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
         for (int w = 0; w < kWaves; ++w) s += sRed[w * 16 + o];
         const int64_t nn = tl * 16 + o;
         float out = fmaf(a.scale, lo, s);
+        if constexpr (SPX) out += sRed[kWaves * 16 + o];
         if (a.addend && tid < 256 && j == 0 && nn < N) out += a.addend[nn];
         const uint32_t yo = buf_off(tid < 256 && j == 0 && nn < N, (uint32_t)(nn * ES));
         if constexpr (YDT == DT_F32) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(out), yr, yo, 0, 0);
@@ -709,6 +752,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) s += sRed[w * 16 + o];
         const int64_t nn = tl * 16 + o;
+        if constexpr (SPX) s += sRed[kWaves * 16 + o];
         epilogue(0, o, nn, tid < 16 && nn < N, s);
       }
     } else {
@@ -791,9 +835,9 @@ int device_cus() {
   return cus;
 }
 
-template <int BITS, int YDT, bool XLDS, bool ADP, int D, bool DOT = false, bool TF = false>
+template <int BITS, int YDT, bool XLDS, bool ADP, int D, bool DOT = false, bool TF = false, bool SPX = false>
 hipError_t launch_k(const Params& P, int64_t grid, size_t shmem, const Levels& lv, hipStream_t s) {
-  auto kern = k_gemv<BITS, YDT, XLDS, ADP, D, DOT, TF>;
+  auto kern = k_gemv<BITS, YDT, XLDS, ADP, D, DOT, TF, SPX>;
   static bool attr = false;
   if (!attr) {
     // the kernel addresses LDS from 0: it must not have static LDS
@@ -904,6 +948,17 @@ hipError_t launch_gemv_b(const LinearArgs& a, const Levels& lv, hipStream_t s) {
   const int64_t grid = pl.grid;
   const size_t lds = pl.lds;
   const bool adp = a.r > 0;
+  if (a.sp_row_ptr) {
+    // the side channel is summed in the kernel only on the single-row path with a short stream
+    if constexpr (BITS != 3) {
+      if (pl.dot && !pl.deep && a.sp_nnz > 0) {
+        if (pl.tf) return launch_k<BITS, YDT, true, true, 2, true, true, true>(P, grid, lds, lv, s);
+        if (adp) return launch_k<BITS, YDT, true, true, 2, true, false, true>(P, grid, lds, lv, s);
+        return launch_k<BITS, YDT, true, false, 2, true, false, true>(P, grid, lds, lv, s);
+      }
+    }
+    return hipErrorInvalidValue;
+  }
   if constexpr (BITS != 3) {
     if (pl.dot) {
       if (pl.tf) return launch_k<BITS, YDT, true, true, 2, true, true>(P, grid, lds, lv, s);
@@ -945,6 +1000,17 @@ bool gemv_fuses_adapter(const LinearArgs& a) {
     case 4: return plan_gemv<4>(a).tf;
     default: return plan_gemv<8>(a).tf;
   }
+}
+
+bool gemv_fuses_sparse(const LinearArgs& a) {
+  if (a.M != 1 || a.bits == 3) return false;
+  Plan pl;
+  switch (a.bits) {
+    case 2: pl = plan_gemv<2>(a); break;
+    case 4: pl = plan_gemv<4>(a); break;
+    default: pl = plan_gemv<8>(a); break;
+  }
+  return pl.ok && pl.dot && !pl.deep;
 }
 
 hipError_t launch_gemv(const LinearArgs& a, const Levels& lv, hipStream_t s) {

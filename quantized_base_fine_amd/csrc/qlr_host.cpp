@@ -232,13 +232,21 @@ qlr::LinearArgs make_args(const LinearCheck& c, float scale, char* ws, int split
   return a;
 }
 
+// The sparse side channel, when given, is summed inside the decode kernel (the
+// caller has checked sparse_fused); addend is the alternative, a precomputed term.
 qlr_status run_linear(const LinearCheck& c, float scale, char* ws, qlr_path path, hipStream_t s,
-                      const float* addend = nullptr) {
+                      const float* addend = nullptr, const qlr_sparse* sp = nullptr) {
   if (c.M == 0) return QLR_OK;
   hipError_t e = hipSuccess;
   const int splits = qlr::lora_t_splits(c.M, c.w->cols, (int)c.xdt, (int)c.abdt);
   qlr::LinearArgs a = make_args(c, scale, ws, splits);
   a.addend = addend;
+  if (sp) {
+    a.sp_row_ptr = sp->row_ptr;
+    a.sp_col = sp->col;
+    a.sp_val = sp->val;
+    a.sp_nnz = sp->nnz;
+  }
   if (c.r > 0 && !(path == QLR_PATH_GEMV && qlr::gemv_fuses_adapter(a))) {
     e = qlr::launch_lora_t(c.x, (int)c.xdt, c.M, c.w->cols, c.A, (int)c.abdt, c.r,
                            reinterpret_cast<float*>(ws), splits, s);
@@ -749,11 +757,15 @@ qlr_status qlr_linear_fwd_outliers(const void* x, qlr_dtype xdt, int64_t M, cons
   if (M == 0) return QLR_OK;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* wsp = reinterpret_cast<char*>(ws);
+  // a single x row on the decode kernel: the side channel is summed inside it
+  const qlr::LinearArgs probe = make_args(c, scale, wsp, qlr::lora_t_splits(M, w->cols, (int)xdt, (int)abdt));
+  if (sp->nnz > 0 && path == QLR_PATH_GEMV && qlr::gemv_fuses_sparse(probe))
+    return run_linear(c, scale, wsp, path, s, nullptr, sp);
   float* C = reinterpret_cast<float*>(wsp + linear_ws_bytes(M, w->cols, r));
   const float* addend = nullptr;
   if (sp->nnz > 0) {
     const hipError_t e = qlr::launch_sparse_addend(x, (int)xdt, M, w->cols, w->rows, sp->row_ptr, sp->col, sp->val,
-                                                   C, s);
+                                                   sp->nnz, C, s);
     if (e != hipSuccess) return hip_fail(e, "sparse term launch");
     addend = C;
   }

@@ -66,6 +66,12 @@ struct LinearArgs {
   // optional float32 M x N term added to every output before rounding (the
   // sparse side channel's x S^T); null when absent
   const float* addend = nullptr;
+  // optional CSR side channel (N rows) summed inside the single-row decode
+  // kernel (see gemv_fuses_sparse); null when absent
+  const int32_t* sp_row_ptr = nullptr;
+  const int32_t* sp_col = nullptr;
+  const float* sp_val = nullptr;
+  int64_t sp_nnz = 0;
 };
 
 // float32 path: any dtypes, any M.
@@ -76,6 +82,9 @@ hipError_t launch_gemv(const LinearArgs& a, const Levels& lv, hipStream_t s);
 // row and a small rank): the adapter-product kernel is then not launched and
 // a.t is not read.
 bool gemv_fuses_adapter(const LinearArgs& a);
+// True when launch_gemv can add a CSR side channel (a.sp_*) itself for this
+// call: the single-row path with a short chunk stream.
+bool gemv_fuses_sparse(const LinearArgs& a);
 // bf16 tiled GEMM path.
 hipError_t launch_gemm(const LinearArgs& a, const Levels& lv, hipStream_t s);
 // Up to gemm_group_max() independent linears of one code width, one M and one
@@ -113,7 +122,7 @@ hipError_t launch_outlier_finish(int64_t rows, int64_t cols, int64_t k, int bits
                                  const float* oval, int32_t* row_ptr, int32_t* col, float* val, hipStream_t s);
 // C (M x N float32) = x S^T for S in CSR (N rows, K columns).
 hipError_t launch_sparse_addend(const void* x, int xdt, int64_t M, int64_t K, int64_t N, const int32_t* row_ptr,
-                                const int32_t* col, const float* val, float* C, hipStream_t s);
+                                const int32_t* col, const float* val, int64_t nnz, float* C, hipStream_t s);
 
 // ---- backward (adapter training)
 // Input gradient dx = dy W' + scale u A on the transposed bf16 GEMM: a.x = dy

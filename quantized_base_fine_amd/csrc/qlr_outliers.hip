@@ -11,6 +11,7 @@
 // with global atomics, one single-workgroup step per pass narrowing the prefix);
 // then every key > T is taken and the keys == T in index order until k.
 #include <algorithm>
+#include <type_traits>
 
 #include "qlr_internal.h"
 
@@ -20,6 +21,7 @@ namespace {
 
 constexpr int kOlBins = 2048;
 constexpr int kOlElems = 4096;  // elements per workgroup in the count / emit passes
+constexpr int64_t kSparseLds = 64 * 1024;  // staged x rows of the sparse term (two workgroups per CU)
 
 template <int WDT>
 __device__ __forceinline__ uint32_t ol_key(const void* W, int64_t i, float* wv) {
@@ -254,74 +256,140 @@ __global__ __launch_bounds__(256) void k_ol_rowptr(int64_t rows, int64_t cols, i
 }
 
 // C[m][n] = sum over row n's outliers j of val[j] x[m][col[j]] (float32, x widened
-// exactly, outliers in CSR order).  blockIdx.x: MR rows of x, staged in LDS as
-// float32 (MR = 0: one row read from global memory, for rows too long for LDS);
-// blockIdx.y: a range of weight rows, one thread per row.
+// exactly, outliers in CSR order).
+//
+// blockIdx.x: MR rows of x, staged in LDS transposed (sx[c][mm], MR values of
+// one column contiguous, so one 16-byte read serves 8 bf16 rows); MR = 0 reads
+// one x row from global memory (rows too long for LDS).  blockIdx.y: a range of
+// weight rows; each thread takes 4 rows at a time, loads their row offsets and
+// their first 4 outliers together (unconditional, clamped loads, so they are in
+// flight at once), and walks longer rows' remaining outliers one by one.
 template <int XDT, int MR>
 __global__ __launch_bounds__(256) void k_sparse_addend(const void* __restrict__ x, int64_t M, int64_t K, int64_t N,
                                                        const int32_t* __restrict__ row_ptr,
                                                        const int32_t* __restrict__ col,
-                                                       const float* __restrict__ val, float* __restrict__ C,
-                                                       int64_t nchunk) {
-  extern __shared__ float sx[];
+                                                       const float* __restrict__ val, int64_t nnz,
+                                                       float* __restrict__ C, int64_t nchunk) {
+  using XT = std::conditional_t<XDT == DT_F32, float, uint16_t>;
   constexpr int R = MR > 0 ? MR : 1;
+  constexpr int EPC = 16 / (int)sizeof(XT);  // elements per 16-byte chunk of an x row
+  extern __shared__ uint4 smem_u4[];
+  XT* sx = reinterpret_cast<XT*>(smem_u4);
+  const XT* xg = reinterpret_cast<const XT*>(x);
+  const int tid = threadIdx.x;
   const int64_t m0 = (int64_t)blockIdx.x * R;
   if constexpr (MR > 0) {
-    for (int64_t idx = threadIdx.x; idx < (int64_t)MR * K; idx += 256) {
-      const int64_t mm = idx / K, k = idx % K;
-      sx[idx] = m0 + mm < M ? load_elem<XDT>(x, (m0 + mm) * K + k) : 0.0f;
+    // chunk q of the x rows: EPC consecutive columns of each of the MR rows
+    for (int64_t q = tid; q < K / EPC; q += 256) {
+      XT v[MR][EPC];
+#pragma unroll
+      for (int mm = 0; mm < MR; ++mm) {
+        const int64_t m = m0 + mm < M ? m0 + mm : M - 1;
+        const uint4 u = *reinterpret_cast<const uint4*>(xg + m * K + q * EPC);
+        const XT* e = reinterpret_cast<const XT*>(&u);
+#pragma unroll
+        for (int i = 0; i < EPC; ++i) v[mm][i] = m0 + mm < M ? e[i] : (XT)0;
+      }
+#pragma unroll
+      for (int i = 0; i < EPC; ++i)
+#pragma unroll
+        for (int mm = 0; mm < MR; ++mm) sx[(q * EPC + i) * MR + mm] = v[mm][i];
     }
     __syncthreads();
   }
+  auto xval = [&](int64_t c, int mm) -> float {
+    if constexpr (MR > 0) {
+      const XT e = sx[c * MR + mm];
+      if constexpr (XDT == DT_F32) return e;
+      else return bf16_bits_to_f32(e);
+    } else {
+      if constexpr (XDT == DT_F32) return xg[m0 * K + c];
+      else return bf16_bits_to_f32(xg[m0 * K + c]);
+    }
+  };
   const int64_t nb = (int64_t)blockIdx.y * nchunk, ne = min(N, nb + nchunk);
-  for (int64_t n = nb + threadIdx.x; n < ne; n += 256) {
-    float acc[R];
+  for (int64_t base = nb; base < ne; base += 4 * 256) {
+    int64_t p0[4], p1[4];
 #pragma unroll
-    for (int mm = 0; mm < R; ++mm) acc[mm] = 0.0f;
-    const int32_t j1 = row_ptr[n + 1];
-    for (int32_t j = row_ptr[n]; j < j1; ++j) {
-      const int64_t c = col[j];
-      const float v = val[j];
+    for (int u = 0; u < 4; ++u) {
+      const int64_t n = base + tid + 256 * u;
+      const int64_t nc = n < ne ? n : ne - 1;
+      // offsets and columns are clamped into range: a malformed CSR gives wrong sums, never a stray access
+      p0[u] = n < ne ? max<int64_t>(row_ptr[nc], 0) : 0;
+      p1[u] = n < ne ? min<int64_t>(row_ptr[nc + 1], nnz) : 0;
+    }
+    float acc[4][R];
+    int32_t cc[4][4];
+    float vv[4][4];
 #pragma unroll
-      for (int mm = 0; mm < R; ++mm) {
-        const float xv = MR > 0 ? sx[mm * K + c] : load_elem<XDT>(x, (m0 + mm) * K + c);
-        acc[mm] = fmaf(v, xv, acc[mm]);
+    for (int u = 0; u < 4; ++u)
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const int64_t j = p0[u] + e;
+        const int64_t jc = j < nnz ? j : nnz - 1;
+        cc[u][e] = min<int32_t>(max<int32_t>(col[jc], 0), (int32_t)(K - 1));
+        vv[u][e] = val[jc];
+      }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+#pragma unroll
+      for (int mm = 0; mm < R; ++mm) acc[u][mm] = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        if (p0[u] + e < p1[u]) {
+#pragma unroll
+          for (int mm = 0; mm < R; ++mm) acc[u][mm] = fmaf(vv[u][e], xval(cc[u][e], mm), acc[u][mm]);
+        }
+      }
+      for (int64_t j = p0[u] + 4; j < p1[u]; ++j) {
+        const int32_t c = min<int32_t>(max<int32_t>(col[j], 0), (int32_t)(K - 1));
+        const float v = val[j];
+#pragma unroll
+        for (int mm = 0; mm < R; ++mm) acc[u][mm] = fmaf(v, xval(c, mm), acc[u][mm]);
       }
     }
 #pragma unroll
-    for (int mm = 0; mm < R; ++mm)
-      if (m0 + mm < M) C[(m0 + mm) * N + n] = acc[mm];
+    for (int u = 0; u < 4; ++u) {
+      const int64_t n = base + tid + 256 * u;
+      if (n < ne) {
+#pragma unroll
+        for (int mm = 0; mm < R; ++mm)
+          if (m0 + mm < M) C[(m0 + mm) * N + n] = acc[u][mm];
+      }
+    }
   }
 }
 
 template <int XDT, int MR>
 hipError_t sparse_addend_t(const void* x, int64_t M, int64_t K, int64_t N, const int32_t* row_ptr,
-                           const int32_t* col, const float* val, float* C, hipStream_t s) {
+                           const int32_t* col, const float* val, int64_t nnz, float* C, hipStream_t s) {
   constexpr int R = MR > 0 ? MR : 1;
   const int64_t xblocks = (M + R - 1) / R;
   const int64_t nch = std::max<int64_t>(1, std::min<int64_t>((N + 255) / 256, (512 + xblocks - 1) / xblocks));
   const int64_t nchunk = (N + nch - 1) / nch;
-  const size_t shmem = MR > 0 ? (size_t)MR * K * 4 : 0;
+  const size_t es = XDT == DT_F32 ? 4 : 2;
+  const size_t shmem = MR > 0 ? (size_t)MR * K * es : 0;
   static bool attr = false;
   if (!attr) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_sparse_addend<XDT, MR>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, 128 * 1024);
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, kSparseLds);
     if (e != hipSuccess) return e;
     attr = true;
   }
   hipLaunchKernelGGL((k_sparse_addend<XDT, MR>), dim3((unsigned)xblocks, (unsigned)nch), dim3(256), shmem, s, x, M,
-                     K, N, row_ptr, col, val, C, nchunk);
+                     K, N, row_ptr, col, val, nnz, C, nchunk);
   return hipGetLastError();
 }
 
 template <int XDT>
 hipError_t sparse_addend_x(const void* x, int64_t M, int64_t K, int64_t N, const int32_t* row_ptr,
-                           const int32_t* col, const float* val, float* C, hipStream_t s) {
-  const int64_t lim = 128 * 1024;
-  if (M > 4 && 8 * K * 4 <= lim) return sparse_addend_t<XDT, 8>(x, M, K, N, row_ptr, col, val, C, s);
-  if (M > 1 && 4 * K * 4 <= lim) return sparse_addend_t<XDT, 4>(x, M, K, N, row_ptr, col, val, C, s);
-  if (K * 4 <= lim) return sparse_addend_t<XDT, 1>(x, M, K, N, row_ptr, col, val, C, s);
-  return sparse_addend_t<XDT, 0>(x, M, K, N, row_ptr, col, val, C, s);
+                           const int32_t* col, const float* val, int64_t nnz, float* C, hipStream_t s) {
+  const int64_t row = K * (XDT == DT_F32 ? 4 : 2);  // LDS bytes of one staged x row
+  if (M > 4 && 8 * row <= kSparseLds) return sparse_addend_t<XDT, 8>(x, M, K, N, row_ptr, col, val, nnz, C, s);
+  if (M > 2 && 4 * row <= kSparseLds) return sparse_addend_t<XDT, 4>(x, M, K, N, row_ptr, col, val, nnz, C, s);
+  if (M > 1 && 2 * row <= kSparseLds) return sparse_addend_t<XDT, 2>(x, M, K, N, row_ptr, col, val, nnz, C, s);
+  if (row <= kSparseLds) return sparse_addend_t<XDT, 1>(x, M, K, N, row_ptr, col, val, nnz, C, s);
+  return sparse_addend_t<XDT, 0>(x, M, K, N, row_ptr, col, val, nnz, C, s);
 }
 
 template <int WDT>
@@ -392,10 +460,10 @@ hipError_t launch_outlier_split(const void* W, int wdt, int64_t numel, int64_t k
 }
 
 hipError_t launch_sparse_addend(const void* x, int xdt, int64_t M, int64_t K, int64_t N, const int32_t* row_ptr,
-                                const int32_t* col, const float* val, float* C, hipStream_t s) {
+                                const int32_t* col, const float* val, int64_t nnz, float* C, hipStream_t s) {
   if (M == 0 || N == 0) return hipSuccess;
-  if (xdt == DT_F32) return sparse_addend_x<DT_F32>(x, M, K, N, row_ptr, col, val, C, s);
-  return sparse_addend_x<DT_BF16>(x, M, K, N, row_ptr, col, val, C, s);
+  if (xdt == DT_F32) return sparse_addend_x<DT_F32>(x, M, K, N, row_ptr, col, val, nnz, C, s);
+  return sparse_addend_x<DT_BF16>(x, M, K, N, row_ptr, col, val, nnz, C, s);
 }
 
 hipError_t launch_outlier_finish(int64_t rows, int64_t cols, int64_t k, int bits, const Levels& lv,

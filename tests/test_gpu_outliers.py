@@ -160,6 +160,19 @@ def test_fwd_long_rows(path, M):
     _check_fwd(_run(lin, qw, sp, "f32", PATHS[path]), lin, q, csr)
 
 
+@pytest.mark.parametrize("r", [0, 16])
+def test_fwd_decode_two_tiles_per_workgroup(r):
+    """N = 8192, K = 512, M = 1: 512 row tiles of the decode kernel on 256 workgroups (the side
+    channel of a workgroup's second tile is loaded at its end); 1 % outliers, so many rows hold
+    more than 4."""
+    lin, k = _layer(8192, 512, 1, r, seed=70 + r)
+    qw, sp = _gpu_split(lin.W, lin.wdtype, lin.bits, k)
+    q, csr = ool.quantize_with_outliers(lin.W, lin.wdtype, lin.bits, lin.N, lin.K, k)
+    assert np.max(np.diff(csr[0])) > 4
+    for ydt in ("f32", "bf16"):
+        _check_fwd(_run(lin, qw, sp, ydt, qlr.PATH_GEMV), lin, q, csr, ydt)
+
+
 def test_fwd_f32_inputs():
     """float32 x and adapters (the float32 family) with outliers."""
     lin, k = _layer(128, 256, 7, 4, seed=50, xdtype="f32", abdtype="f32")
