@@ -673,21 +673,22 @@ __global__ __launch_bounds__(512, 1) void k_gemm(GemmParams P, Levels lv) {
     // lane (fr, h), register v of tile (i, c) -> row 32 i + 8 (v / 4) + 4 h + v % 4, column 32 c + fr
     constexpr int ES = (YDT == DT_F32) ? 4 : 2;
     constexpr uint32_t RS = 128 * ES + 16;  // padded row stride (bytes)
-    if (!TR && a.addend) {
-      // the sparse side channel's term, added before rounding (32 lanes read 32
-      // consecutive columns of one row)
+    // with an addend (forward only) the tile is staged in float32 whatever the
+    // output type: the addend is added, and the sum rounded, by the store pass
+    const bool stage32 = !TR && a.addend != nullptr;
+    if (stage32) {
+      constexpr uint32_t RS4 = 128 * 4 + 16;
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int c = 0; c < 2; ++c)
 #pragma unroll
           for (int v = 0; v < 16; ++v) {
-            const int64_t gr = m0 + 128 * mh + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
-            const int64_t gc = n0 + 64 * nh + 32 * c + fr;
-            const float ad = a.addend[(gr < M ? gr : M - 1) * NO + (gc < NO ? gc : NO - 1)];
-            acc[i][c][v] += (gr < M && gc < NO) ? ad : 0.0f;
+            const uint32_t row = 128 * mh + 32 * i + 8 * (v >> 2) + 4 * h + (v & 3);
+            const uint32_t addr = row * RS4 + (uint32_t)(64 * nh + 32 * c + fr) * 4u;
+            *reinterpret_cast<__attribute__((address_space(3))) float*>((uintptr_t)addr) = acc[i][c][v];
           }
-    }
+    } else {
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -702,10 +703,55 @@ __global__ __launch_bounds__(512, 1) void k_gemm(GemmParams P, Levels lv) {
             *reinterpret_cast<__attribute__((address_space(3))) uint16_t*>((uintptr_t)addr) =
                 (uint16_t)f32_to_bf16_bits(acc[i][c][v]);
         }
+    }
     __syncthreads();  // staging written
   }
   // ---- coalesced global stores of the staged tile by all 512 threads
-  {
+  if (!TR && a.addend != nullptr) {
+    // float32 staging: 16-byte chunk idx = tid + 512 q holds columns 4 (idx % 32) ..
+    // + 3 of row idx / 32; all 16 addend chunks of a thread are loaded first
+    // (clamped addresses, 16-byte loads when the rows are 16-byte aligned)
+    constexpr uint32_t RS4 = 128 * 4 + 16;
+    const bool vec = (NO % 4) == 0;
+    const float* ad = a.addend;
+    f32x4_t av[16];
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int idx = tid + 512 * q;
+      const int64_t gr = min(m0 + (idx >> 5), M - 1), gc = n0 + 4 * (idx & 31);
+      if (vec) av[q] = *reinterpret_cast<const f32x4_t*>(ad + gr * NO + min(gc, NO - 4));
+    }
+    char* y = reinterpret_cast<char*>(a.y);
+#pragma unroll
+    for (int q = 0; q < 16; ++q) {
+      const int idx = tid + 512 * q;
+      const int row = idx >> 5, ch = idx & 31;
+      const int64_t gr = m0 + row, gc = n0 + 4 * ch;
+      f32x4_t v = lds_f32x4((uint32_t)row * RS4 + (uint32_t)ch * 16u);
+      if (gr < M && gc < NO) {
+        if (vec) {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) v[e] = v[e] + av[q][e];
+          if constexpr (YDT == DT_F32) {
+            *reinterpret_cast<f32x4_t*>(y + (gr * NO + gc) * 4) = v;
+          } else {
+            *reinterpret_cast<uint2*>(y + (gr * NO + gc) * 2) =
+                uint2{pack_bf16x2(v[0], v[1]), pack_bf16x2(v[2], v[3])};
+          }
+        } else {
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const float ve = v[e];
+            if (gc + e < NO) {
+              const float o = ve + ad[gr * NO + gc + e];
+              if constexpr (YDT == DT_F32) reinterpret_cast<float*>(y)[gr * NO + gc + e] = o;
+              else reinterpret_cast<uint16_t*>(y)[gr * NO + gc + e] = (uint16_t)f32_to_bf16_bits(o);
+            }
+          }
+        }
+      }
+    }
+  } else {
     constexpr int ES = (YDT == DT_F32) ? 4 : 2;
     constexpr uint32_t RS = 128 * ES + 16;
     constexpr int CPR = 128 * ES / 16;  // 16-byte chunks per row

@@ -53,24 +53,51 @@ __global__ __launch_bounds__(256) void k_ol_hist(const void* W, int64_t n, int s
     if (h[b]) atomicAdd(&hist[b], h[b]);
 }
 
-// one workgroup: find the bin holding the k-th largest remaining key; clears hist for the next pass
+// one workgroup: find the bin holding the k-th largest remaining key; clears hist
+// for the next pass.  Thread t owns bins nb-1-2t and nb-2-2t; an inclusive scan of
+// the pairs from the top gives, per bin, the count of keys in the bins above it,
+// and the one bin with above < need <= above + count writes the state (bin 0
+// when the counts fall short, as a sequential walk down the bins would end).
 __global__ __launch_bounds__(1024) void k_ol_select(int shift, int nbits, uint32_t* __restrict__ state,
                                                     uint32_t* __restrict__ hist) {
-  __shared__ uint32_t h[kOlBins];
+  __shared__ uint32_t sc[1024];
   const int nb = 1 << nbits;
-  for (int b = threadIdx.x; b < nb; b += 1024) {
-    h[b] = hist[b];
-    hist[b] = 0;
+  const int t = threadIdx.x;
+  const int b0 = nb - 1 - 2 * t, b1 = nb - 2 - 2 * t;
+  uint32_t h0 = 0, h1 = 0;
+  if (b0 >= 0) {
+    h0 = hist[b0];
+    hist[b0] = 0;
   }
+  if (b1 >= 0) {
+    h1 = hist[b1];
+    hist[b1] = 0;
+  }
+  const uint32_t need = state[2];
+  sc[t] = h0 + h1;
   __syncthreads();
-  if (threadIdx.x == 0) {
-    uint32_t need = state[2], above = 0;
-    int b = nb - 1;
-    for (; b > 0; --b) {
-      if (above + h[b] >= need) break;
-      above += h[b];
-    }
-    state[0] |= (uint32_t)b << shift;
+  for (int o = 1; o < 1024; o <<= 1) {
+    const uint32_t v = t >= o ? sc[t - o] : 0u;
+    __syncthreads();
+    sc[t] += v;
+    __syncthreads();
+  }
+  const uint32_t above0 = sc[t] - (h0 + h1), above1 = above0 + h0;
+  const uint32_t total = sc[1023];
+  int bin = -1;
+  uint32_t above = 0;
+  if (b0 >= 0 && above0 < need && need <= above0 + h0) {
+    bin = b0;
+    above = above0;
+  } else if (b1 >= 0 && above1 < need && need <= above1 + h1) {
+    bin = b1;
+    above = above1;
+  } else if (total < need && (b0 == 0 || b1 == 0)) {
+    bin = 0;
+    above = b0 == 0 ? above0 : above1;
+  }
+  if (bin >= 0) {
+    state[0] |= (uint32_t)bin << shift;
     state[1] |= (uint32_t)(nb - 1) << shift;
     state[2] = need - above;
     state[3] += above;
@@ -159,13 +186,47 @@ __global__ __launch_bounds__(256) void k_ol_emit(const void* W, int64_t n, const
   const int64_t b0 = (int64_t)blockIdx.x * kOlElems + 16 * threadIdx.x;
   uint32_t keys[16];
   float ws[16];
+  uint32_t rw[16];  // raw 16-bit words (16-bit weights)
   uint32_t neq = 0;
+  const bool full = b0 + 16 <= n;
+  if (full) {
+    // the thread's 16 elements in 16-byte loads (W is 16-byte aligned)
+    if constexpr (WDT == DT_F32) {
 #pragma unroll
-  for (int e = 0; e < 16; ++e) {
-    const int64_t i = b0 + e;
-    keys[e] = i < n ? ol_key<WDT>(W, i, &ws[e]) : 0u;
-    if (i >= n) ws[e] = 0.0f;
-    neq += (i < n && keys[e] == T);
+      for (int q = 0; q < 4; ++q) {
+        const float4 v = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(W) + b0)[q];
+        ws[4 * q] = v.x;
+        ws[4 * q + 1] = v.y;
+        ws[4 * q + 2] = v.z;
+        ws[4 * q + 3] = v.w;
+      }
+    } else {
+#pragma unroll
+      for (int q = 0; q < 2; ++q) {
+        const uint4 v = reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(W) + b0)[q];
+        const uint32_t w4[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const uint32_t h = (w4[e >> 1] >> (16 * (e & 1))) & 0xFFFFu;
+          rw[8 * q + e] = h;
+          ws[8 * q + e] = WDT == DT_F16 ? f16_bits_to_f32(h) : bf16_bits_to_f32(h);
+        }
+      }
+    }
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      keys[e] = __float_as_uint(ws[e]) & 0x7FFFFFFFu;
+      neq += keys[e] == T;
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int64_t i = b0 + e;
+      keys[e] = i < n ? ol_key<WDT>(W, i, &ws[e]) : 0u;
+      if (i >= n) ws[e] = 0.0f;
+      rw[e] = (WDT != DT_F32 && i < n) ? (uint32_t)reinterpret_cast<const uint16_t*>(W)[i] : 0u;
+      neq += (i < n && keys[e] == T);
+    }
   }
   seq[threadIdx.x] = neq;
   __syncthreads();
@@ -199,17 +260,37 @@ __global__ __launch_bounds__(256) void k_ol_emit(const void* W, int64_t n, const
   uint32_t pos = plan[2 * blockIdx.x + 1] + ssel[threadIdx.x] - nsel;
 #pragma unroll
   for (int e = 0; e < 16; ++e) {
-    const int64_t i = b0 + e;
-    if (i >= n) break;
     if (sel[e]) {
-      oidx[pos] = (int32_t)i;
+      oidx[pos] = (int32_t)(b0 + e);
       oval[pos] = ws[e];
       ++pos;
     }
-    if constexpr (WDT == DT_F32) reinterpret_cast<float*>(dense)[i] = sel[e] ? 0.0f : ws[e];
-    else {
-      const uint16_t raw = reinterpret_cast<const uint16_t*>(W)[i];
-      reinterpret_cast<uint16_t*>(dense)[i] = sel[e] ? (uint16_t)0 : raw;
+  }
+  // the dense copy: the weight with the selected entries zeroed
+  if (full) {
+    if constexpr (WDT == DT_F32) {
+#pragma unroll
+      for (int q = 0; q < 4; ++q)
+        reinterpret_cast<float4*>(reinterpret_cast<float*>(dense) + b0)[q] =
+            make_float4(sel[4 * q] ? 0.0f : ws[4 * q], sel[4 * q + 1] ? 0.0f : ws[4 * q + 1],
+                        sel[4 * q + 2] ? 0.0f : ws[4 * q + 2], sel[4 * q + 3] ? 0.0f : ws[4 * q + 3]);
+    } else {
+      uint32_t pk[8];
+#pragma unroll
+      for (int p = 0; p < 8; ++p)
+        pk[p] = (sel[2 * p] ? 0u : rw[2 * p]) | ((sel[2 * p + 1] ? 0u : rw[2 * p + 1]) << 16);
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        reinterpret_cast<uint4*>(reinterpret_cast<uint16_t*>(dense) + b0)[q] =
+            make_uint4(pk[4 * q], pk[4 * q + 1], pk[4 * q + 2], pk[4 * q + 3]);
+    }
+  } else {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int64_t i = b0 + e;
+      if (i >= n) break;
+      if constexpr (WDT == DT_F32) reinterpret_cast<float*>(dense)[i] = sel[e] ? 0.0f : ws[e];
+      else reinterpret_cast<uint16_t*>(dense)[i] = sel[e] ? (uint16_t)0 : (uint16_t)rw[e];
     }
   }
 }
@@ -261,9 +342,9 @@ __global__ __launch_bounds__(256) void k_ol_rowptr(int64_t rows, int64_t cols, i
 // blockIdx.x: MR rows of x, staged in LDS transposed (sx[c][mm], MR values of
 // one column contiguous, so one 16-byte read serves 8 bf16 rows); MR = 0 reads
 // one x row from global memory (rows too long for LDS).  blockIdx.y: a range of
-// weight rows; each thread takes 4 rows at a time, loads their row offsets and
-// their first 4 outliers together (unconditional, clamped loads, so they are in
-// flight at once), and walks longer rows' remaining outliers one by one.
+// weight rows; each thread takes 8 rows at a time and walks their outliers in
+// rounds of 4 per row, every load of a round issued before any is used
+// (unconditional, clamped loads).
 template <int XDT, int MR>
 __global__ __launch_bounds__(256) void k_sparse_addend(const void* __restrict__ x, int64_t M, int64_t K, int64_t N,
                                                        const int32_t* __restrict__ row_ptr,
@@ -278,6 +359,11 @@ __global__ __launch_bounds__(256) void k_sparse_addend(const void* __restrict__ 
   const XT* xg = reinterpret_cast<const XT*>(x);
   const int tid = threadIdx.x;
   const int64_t m0 = (int64_t)blockIdx.x * R;
+  // (bf16, 8 rows): column c's 8 values form one 16-byte record at slot
+  // sl(c) = c with its low 3 bits XORed by bits 3..5, so the 8 records a thread
+  // writes (columns 8 q .. 8 q + 7) and those of its neighbours fall in distinct banks
+  constexpr bool kRec = XDT == DT_BF16 && MR == 8;
+  auto sl = [](int64_t c) -> int64_t { return (c & ~int64_t(7)) | ((c & 7) ^ ((c >> 3) & 7)); };
   if constexpr (MR > 0) {
     // chunk q of the x rows: EPC consecutive columns of each of the MR rows
     for (int64_t q = tid; q < K / EPC; q += 256) {
@@ -290,66 +376,94 @@ __global__ __launch_bounds__(256) void k_sparse_addend(const void* __restrict__ 
 #pragma unroll
         for (int i = 0; i < EPC; ++i) v[mm][i] = m0 + mm < M ? e[i] : (XT)0;
       }
+      if constexpr (kRec) {
 #pragma unroll
-      for (int i = 0; i < EPC; ++i)
+        for (int i = 0; i < EPC; ++i) {
+          uint4 rec;
+          rec.x = (uint32_t)v[0][i] | ((uint32_t)v[1][i] << 16);
+          rec.y = (uint32_t)v[2][i] | ((uint32_t)v[3][i] << 16);
+          rec.z = (uint32_t)v[4][i] | ((uint32_t)v[5][i] << 16);
+          rec.w = (uint32_t)v[6][i] | ((uint32_t)v[7][i] << 16);
+          smem_u4[sl(q * EPC + i)] = rec;
+        }
+      } else {
 #pragma unroll
-        for (int mm = 0; mm < MR; ++mm) sx[(q * EPC + i) * MR + mm] = v[mm][i];
+        for (int i = 0; i < EPC; ++i)
+#pragma unroll
+          for (int mm = 0; mm < MR; ++mm) sx[(q * EPC + i) * MR + mm] = v[mm][i];
+      }
     }
     __syncthreads();
   }
-  auto xval = [&](int64_t c, int mm) -> float {
-    if constexpr (MR > 0) {
-      const XT e = sx[c * MR + mm];
-      if constexpr (XDT == DT_F32) return e;
-      else return bf16_bits_to_f32(e);
+  // the R x values of column c
+  auto xcol = [&](int64_t c, float (&xv)[R]) {
+    if constexpr (kRec) {
+      const uint4 rec = smem_u4[sl(c)];
+      const uint32_t w[4] = {rec.x, rec.y, rec.z, rec.w};
+#pragma unroll
+      for (int mm = 0; mm < 8; ++mm) xv[mm] = bf16_bits_to_f32((w[mm >> 1] >> (16 * (mm & 1))) & 0xFFFFu);
     } else {
-      if constexpr (XDT == DT_F32) return xg[m0 * K + c];
-      else return bf16_bits_to_f32(xg[m0 * K + c]);
+#pragma unroll
+      for (int mm = 0; mm < R; ++mm) {
+        if constexpr (MR > 0) {
+          const XT e = sx[c * MR + mm];
+          if constexpr (XDT == DT_F32) xv[mm] = e;
+          else xv[mm] = bf16_bits_to_f32(e);
+        } else {
+          if constexpr (XDT == DT_F32) xv[mm] = xg[m0 * K + c];
+          else xv[mm] = bf16_bits_to_f32(xg[m0 * K + c]);
+        }
+      }
     }
   };
   const int64_t nb = (int64_t)blockIdx.y * nchunk, ne = min(N, nb + nchunk);
-  for (int64_t base = nb; base < ne; base += 4 * 256) {
-    int64_t p0[4], p1[4];
+  constexpr int RB = 8;  // weight rows per thread per batch
+  for (int64_t base = nb; base < ne; base += RB * 256) {
+    int64_t p0[RB], p1[RB];
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < RB; ++u) {
       const int64_t n = base + tid + 256 * u;
       const int64_t nc = n < ne ? n : ne - 1;
       // offsets and columns are clamped into range: a malformed CSR gives wrong sums, never a stray access
       p0[u] = n < ne ? max<int64_t>(row_ptr[nc], 0) : 0;
       p1[u] = n < ne ? min<int64_t>(row_ptr[nc + 1], nnz) : 0;
     }
-    float acc[4][R];
-    int32_t cc[4][4];
-    float vv[4][4];
+    float acc[RB][R];
 #pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int64_t j = p0[u] + e;
-        const int64_t jc = j < nnz ? j : nnz - 1;
-        cc[u][e] = min<int32_t>(max<int32_t>(col[jc], 0), (int32_t)(K - 1));
-        vv[u][e] = val[jc];
-      }
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < RB; ++u)
 #pragma unroll
       for (int mm = 0; mm < R; ++mm) acc[u][mm] = 0.0f;
+    // rounds of 4 outliers per row: every row's loads of a round are in flight together
+    for (int64_t e0 = 0;; e0 += 4) {
+      bool more = false;
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        if (p0[u] + e < p1[u]) {
+      for (int u = 0; u < RB; ++u) more |= p0[u] + e0 < p1[u];
+      if (!more) break;
+      int32_t cc[RB][4];
+      float vv[RB][4];
 #pragma unroll
-          for (int mm = 0; mm < R; ++mm) acc[u][mm] = fmaf(vv[u][e], xval(cc[u][e], mm), acc[u][mm]);
+      for (int u = 0; u < RB; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int64_t j = p0[u] + e0 + e;
+          const int64_t jc = j < nnz ? j : nnz - 1;
+          cc[u][e] = min<int32_t>(max<int32_t>(col[jc], 0), (int32_t)(K - 1));
+          vv[u][e] = val[jc];
         }
-      }
-      for (int64_t j = p0[u] + 4; j < p1[u]; ++j) {
-        const int32_t c = min<int32_t>(max<int32_t>(col[j], 0), (int32_t)(K - 1));
-        const float v = val[j];
 #pragma unroll
-        for (int mm = 0; mm < R; ++mm) acc[u][mm] = fmaf(v, xval(c, mm), acc[u][mm]);
-      }
+      for (int u = 0; u < RB; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (p0[u] + e0 + e < p1[u]) {
+            float xv[R];
+            xcol(cc[u][e], xv);
+#pragma unroll
+            for (int mm = 0; mm < R; ++mm) acc[u][mm] = fmaf(vv[u][e], xv[mm], acc[u][mm]);
+          }
+        }
     }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) {
+    for (int u = 0; u < RB; ++u) {
       const int64_t n = base + tid + 256 * u;
       if (n < ne) {
 #pragma unroll

@@ -173,6 +173,16 @@ def test_fwd_decode_two_tiles_per_workgroup(r):
         _check_fwd(_run(lin, qw, sp, ydt, qlr.PATH_GEMV), lin, q, csr, ydt)
 
 
+@pytest.mark.parametrize("M", [40, 300])
+def test_fwd_gemm_ragged_columns(M):
+    """N = 330 (output rows not a multiple of 4: the scalar stores of the prefill kernel)."""
+    lin, k = _layer(330, 576, M, 16, seed=80 + M)
+    qw, sp = _gpu_split(lin.W, lin.wdtype, lin.bits, k)
+    q, csr = ool.quantize_with_outliers(lin.W, lin.wdtype, lin.bits, lin.N, lin.K, k)
+    for ydt in ("f32", "bf16"):
+        _check_fwd(_run(lin, qw, sp, ydt, qlr.PATH_GEMM), lin, q, csr, ydt)
+
+
 def test_fwd_f32_inputs():
     """float32 x and adapters (the float32 family) with outliers."""
     lin, k = _layer(128, 256, 7, 4, seed=50, xdtype="f32", abdtype="f32")
