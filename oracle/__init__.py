@@ -23,6 +23,8 @@ Pages (titles as printed):
   * "LoRDBA" section 2: the double-binary adapter branch (``dba``).
   * "QFT" (gist.science summary), section 2.2: the hybrid outlier split
     (``outliers``).
+  * "QWHA" (gist.science summary), section 2.1: the Walsh-Hadamard adapter
+    (``wha``).
 
 Every function here is pinned by a ``-m "not gpu"`` test against something
 other than itself (closed forms, brute force over exact rationals, invariants,
@@ -34,12 +36,12 @@ from .quant import (widen, block_absmax, nearest_codes, pack_codes, unpack_codes
                     qweight_sizes, QuantizedWeight)
 from .linear import (lora_t, linear, linear_tolerance, mixed, linear_backward,
                      linear_backward_tolerance, adapter_grads, adapter_grads_tolerance)
-from . import dba, outliers
+from . import dba, outliers, wha
 
 __all__ = [
     "normal_quantile", "quantile_codebook", "widen", "block_absmax", "nearest_codes",
     "pack_codes", "unpack_codes", "double_quantize", "dequantize_scales", "dequantize",
     "quantize", "qweight_sizes", "QuantizedWeight", "lora_t", "linear",
     "linear_tolerance", "mixed", "linear_backward", "linear_backward_tolerance", "adapter_grads",
-    "adapter_grads_tolerance", "dba", "outliers",
+    "adapter_grads_tolerance", "dba", "outliers", "wha",
 ]

@@ -152,6 +152,46 @@ def dba_adapter(N: int, K: int, R: int, ell: int, cfg: int = 0, sub: int = 0, se
     return DbaAdapter(R, ell, b1, b2, alpha, beta, gamma)
 
 
+T_WHA = 8
+
+
+def wha_coefficients(N: int, K: int, budget: int, cfg: int = 0, sub: int = 0, seed: int = 0,
+                     floor: int = 0, sigma: float = 0.5):
+    """A sparse coefficient matrix F (N x K) in CSR form (row_ptr int32, col int32, val float32).
+
+    ``budget`` coefficients in all, at least ``floor`` per row; the rest spread
+    over the rows in proportion to a lognormal per-row weight, so that some
+    rows get many more than others (the shape of an error-proportional
+    allocation).  Positions within a row are distinct, uniform, ascending;
+    values N(0, sigma^2).  The default sigma gives a 32-coefficient row at
+    P = 4096 the entry scale of a rank-16 LoRA update with B ~ N(0, 0.01^2),
+    A ~ N(0, 1/K).
+    """
+    g = rng_for(cfg, T_WHA, sub, budget, seed=seed)
+    if not N * floor <= budget <= N * K:
+        raise ValueError("budget out of range")
+    wgt = np.exp(g.standard_normal(N))
+    counts = np.full(N, floor, dtype=np.int64)
+    extra = g.multinomial(budget - N * floor, wgt / wgt.sum())
+    counts += extra
+    # cap at K and hand the excess to rows with room, in row order
+    over = np.maximum(counts - K, 0).sum()
+    counts = np.minimum(counts, K)
+    for n in range(N):
+        if over == 0:
+            break
+        add = min(K - counts[n], over)
+        counts[n] += add
+        over -= add
+    row_ptr = np.zeros(N + 1, dtype=np.int64)
+    row_ptr[1:] = np.cumsum(counts)
+    col = np.empty(budget, dtype=np.int32)
+    for n in range(N):
+        col[row_ptr[n]:row_ptr[n + 1]] = np.sort(g.choice(K, size=int(counts[n]), replace=False))
+    val = (g.standard_normal(budget, dtype=np.float32) * np.float32(sigma)).astype(np.float32)
+    return row_ptr.astype(np.int32), col, val
+
+
 def upstream_grad(lin: Linear, seed: int = 0) -> np.ndarray:
     """A synthetic upstream gradient dy (M x N) for the backward, N(0, 1) in x's dtype.
 
