@@ -23,6 +23,10 @@ cache, so the decode figure is HBM bandwidth, not cache bandwidth):
   outliers decode / prefill  the forward with the weight's 0.1 % largest-|w| entries
                 split off into a float32 CSR side channel (k = 16777) and the dense
                 rest quantized, with the fp16 adapter, at M = 1 (graph) and M = 2048
+  wha decode / wha prefill   the forward with a Walsh-Hadamard adapter in place of
+                the fp16 one: 131072 coefficients per layer (the parameter count of the
+                rank-16 adapter), one full transform over K = 4096, at M = 1 (graph) and
+                M = 2048
 The outlier split itself (qlr_quantize_outliers, blocking) is timed outside the
 step, on one layer.
 Each phase is bracketed by HIP events on the stream its calls run on (events
@@ -96,6 +100,20 @@ def outlier_bytes(M=M_DECODE, nnz=NNZ):
 
 def outlier_flops(M=M_PREFILL, nnz=NNZ):
     return prefill_flops(M) + 2 * M * nnz
+
+
+WHA_NNZ = R_ * (N_ + K_)  # coefficients of the Walsh-Hadamard adapter: the rank-16 adapter's parameter count
+
+
+def wha_bytes(M=M_DECODE, nnz=WHA_NNZ):
+    # the base's bytes, the coefficients (CSR: offsets, columns, float32 values), x and y
+    numel = N_ * K_
+    return numel * BITS // 8 + numel // 64 + 4 * (numel // 16384) + 4 * (N_ + 1) + 8 * nnz + 2 * M * K_ + 2 * M * N_
+
+
+def wha_flops(M=M_PREFILL, nnz=WHA_NNZ):
+    # base product, the transform's additions (K log2 K per row) and the sparse product
+    return 2 * M * N_ * K_ + M * K_ * 12 + 2 * M * nnz
 
 
 def quantize_bytes(N=N_, K=K_, b=BITS):
@@ -348,6 +366,10 @@ def main():
     ws_op = torch.empty(qlr.workspace_bytes(qlr.OP_LINEAR_OUTLIERS, M_PREFILL, N_, K_, R_), dtype=torch.uint8,
                         device=dev)
     ws_os = torch.empty(qlr.workspace_bytes(qlr.OP_QUANTIZE_OUTLIERS, NNZ, N_, K_), dtype=torch.uint8, device=dev)
+    ws_h1 = torch.empty(qlr.workspace_bytes(qlr.OP_LINEAR_WHA, M_DECODE, N_, K_), dtype=torch.uint8, device=dev)
+    ws_hp = torch.empty(qlr.workspace_bytes(qlr.OP_LINEAR_WHA, M_PREFILL, N_, K_), dtype=torch.uint8, device=dev)
+    wha_csr = workloads.wha_coefficients(N_, K_, WHA_NNZ, cfg=2, floor=8)
+    F0 = qlr.sparse_from_csr(N_, K_, *wha_csr, dev)
     layers = []
     for _ in range(R):
         qw = qlr.QWeight.empty(N_, K_, BITS, dev)
@@ -357,6 +379,7 @@ def main():
         yp = torch.empty((M_PREFILL, N_), dtype=torch.bfloat16, device=dev)
         layers.append(dict(
             qw=qw, qo=qo, so=so,
+            wha_decode=None, wha_prefill=None,
             prefill=qlr.LinearCall(xp, qw, A, B, linp.scale, out=yp, ws=wsp),
             prefill_base=qlr.LinearCall(xp, qw, out=yp),
             decode=qlr.LinearCall(x1, qw, A, B, lin1.scale, out=y1, ws=ws1),
@@ -367,6 +390,10 @@ def main():
             dba_prefill=qlr.DbaCall(xp, qw, *dba_t, out=yp, ws=ws_dp),
             ol_decode=qlr.OutliersCall(x1, qo, so, A, B, lin1.scale, out=y1, ws=ws_o1),
             ol_prefill=qlr.OutliersCall(xp, qo, so, A, B, linp.scale, out=yp, ws=ws_op)))
+        # each layer has its own coefficient arrays (a copy of one draw), like its own weight
+        F = qlr.Sparse(N_, K_, F0.nnz, F0.row_ptr.clone(), F0.col.clone(), F0.val.clone())
+        layers[-1]["wha_decode"] = qlr.WhaCall(x1, qw, F, K_, out=y1, ws=ws_h1)
+        layers[-1]["wha_prefill"] = qlr.WhaCall(xp, qw, F, K_, out=yp, ws=ws_hp)
     if args.copy_calibration:
         src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
         dst = torch.empty_like(src)
@@ -407,7 +434,7 @@ def main():
             assert torch.equal(layers[-1]["qw"].codes, ref_codes), "graph replay differs from eager quantize"
 
     PHASES = ("prefill", "prefill_base", "decode", "decode_base", "backward", "backward_base", "dba_decode",
-              "dba_prefill", "ol_decode", "ol_prefill")
+              "dba_prefill", "ol_decode", "ol_prefill", "wha_decode", "wha_prefill")
     mixed = None
     if not args.no_mixed:
         mixed, mixed_flops, mixed_n = build_mixed(torch, qlr, workloads, dev)
@@ -417,7 +444,7 @@ def main():
     # The decode phases (short, launch-bound calls) also run as HIP graphs of the
     # R prepared calls; every replay is checked against the eager outputs first.
     graphs = {}
-    for ph in (() if args.eager else ("decode", "decode_base", "dba_decode", "ol_decode")):
+    for ph in (() if args.eager else ("decode", "decode_base", "dba_decode", "ol_decode", "wha_decode")):
         for L in layers:
             L[ph]()
         torch.cuda.synchronize()
@@ -577,6 +604,16 @@ def main():
             "prefill_tflops": round(outlier_flops() / (mean["ol_prefill"] * 1e-6) / 1e12, 1),
             "split_us": round(1e3 * sorted(split_ms)[len(split_ms) // 2], 1),
             "split_note": "qlr_quantize_outliers on one layer, median of 5, includes its flag read and sync",
+        },
+        "wha": {
+            "workload": "attn_proj_4096x4096_nf4_dq with a Walsh-Hadamard adapter (one 4096-point transform, "
+                        "131072 coefficients) instead of the fp16 one",
+            "decode_us": round(mean["wha_decode"], 3),
+            "decode_gbs": round(wha_bytes() / (mean["wha_decode"] * 1e-6) / 1e9, 1),
+            "decode_bytes_per_call": wha_bytes(),
+            "prefill_us": round(mean["wha_prefill"], 3),
+            "prefill_tflops": round(wha_flops() / (mean["wha_prefill"] * 1e-6) / 1e12, 1),
+            "adapter_bytes": 4 * (N_ + 1) + 8 * WHA_NNZ,
         },
         "wall_s": round(wall, 3),
     }

@@ -75,7 +75,8 @@ typedef enum {
   QLR_OP_LINEAR_BWD = 2,
   QLR_OP_LINEAR_DBA = 3,
   QLR_OP_QUANTIZE_OUTLIERS = 4, /* M = the outlier count k, N = rows, K = cols */
-  QLR_OP_LINEAR_OUTLIERS = 5
+  QLR_OP_LINEAR_OUTLIERS = 5,
+  QLR_OP_LINEAR_WHA = 6 /* r is ignored */
 } qlr_op;
 
 /*
@@ -292,6 +293,27 @@ qlr_status qlr_quantize_outliers(const void* W, qlr_dtype wdt, int64_t rows, int
 qlr_status qlr_linear_fwd_outliers(const void* x, qlr_dtype xdt, int64_t M, const qlr_qweight* w,
                                    const qlr_sparse* sp, const void* A, const void* B, qlr_dtype abdt, int32_t r,
                                    float scale, void* y, qlr_dtype ydt, void* ws, size_t ws_bytes, void* stream);
+
+/*
+ * Forward with a Walsh-Hadamard adapter (QWHA page, section 2.1 "Adapter
+ * design"): y = x W'^T + x dW^T with dW = F H^-1, H the natural-order +-1
+ * Walsh-Hadamard matrix (H[i][j] = (-1)^popcount(i & j)) applied in blocks of
+ * hblock columns (a power of two dividing cols; hblock = cols is one full
+ * transform), so H^-1 = H / hblock, and F the sparse coefficient matrix
+ * (rows x cols CSR in the qlr_sparse format: row_ptr, col = transform index,
+ * val = the coefficient values c in float32).  Computed as z F^T with
+ * z = x blockdiag(H) / hblock: each x row is transformed by butterflies
+ * (additions and subtractions, float32), scaled exactly by 1 / hblock, then
+ * multiplied by F (float32), and the result is added to each output before
+ * rounding.  No low-rank adapter in this call (the branch replaces it).
+ *   x: M x cols, bf16 or f32 (bf16 on the decode and prefill kernels); cols <= 32768.
+ *   ws >= qlr_workspace_bytes(QLR_OP_LINEAR_WHA, M, rows, cols, 0) (M x rows float32).
+ * Tolerance as qlr_linear_fwd, with S extended by sum_j |c_j| (sum of |x| over
+ * j's block) / hblock.  Asynchronous, allocation-free.  Errors: as
+ * qlr_linear_fwd, plus QLR_ERR_SHAPE for hblock, cols or a mismatching F.
+ */
+qlr_status qlr_linear_fwd_wha(const void* x, qlr_dtype xdt, int64_t M, const qlr_qweight* w, const qlr_sparse* F,
+                              int32_t hblock, void* y, qlr_dtype ydt, void* ws, size_t ws_bytes, void* stream);
 
 /*
  * Forward with a double-binary adapter in adapter mode (LoRDBA page,

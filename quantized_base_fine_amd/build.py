@@ -19,7 +19,7 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(HERE, "libqlr.so")
 
 SOURCES = ["qlr_host.cpp", "qlr_quant.hip", "qlr_linear_f32.hip", "qlr_gemv.hip", "qlr_gemm.hip", "qlr_bwd.hip",
-           "qlr_dba.hip", "qlr_outliers.hip"]
+           "qlr_dba.hip", "qlr_outliers.hip", "qlr_wha.hip"]
 
 
 def hipcc() -> str:

@@ -351,6 +351,11 @@ qlr_status qlr_workspace_bytes(qlr_op op, int64_t M, int64_t N, int64_t K, int32
     *bytes = linear_ws_bytes(M, K, r) + (((size_t)M * (size_t)N * 4 + 255) & ~(size_t)255);
     return QLR_OK;
   }
+  if (op == QLR_OP_LINEAR_WHA) {
+    if (M < 0 || N < 0 || K < 0) return fail(QLR_ERR_SHAPE, "negative size");
+    *bytes = ((size_t)M * (size_t)N * 4 + 255) & ~(size_t)255;
+    return QLR_OK;
+  }
   if (op == QLR_OP_LINEAR_DBA) {
     // r = ell * R of the double-binary adapter; the bf16 split count bounds the others
     if (M < 0 || N < 0 || K < 0 || r < 1) return fail(QLR_ERR_SHAPE, "negative size or r < 1");
@@ -770,6 +775,45 @@ qlr_status qlr_linear_fwd_outliers(const void* x, qlr_dtype xdt, int64_t M, cons
     addend = C;
   }
   return run_linear(c, scale, wsp, path, s, addend);
+}
+
+qlr_status qlr_linear_fwd_wha(const void* x, qlr_dtype xdt, int64_t M, const qlr_qweight* w, const qlr_sparse* F,
+                              int32_t hblock, void* y, qlr_dtype ydt, void* ws, size_t ws_bytes, void* stream) {
+  if (!F) return fail(QLR_ERR_NULL, "F is NULL");
+  const LinearCheck c{x, xdt, M, w, nullptr, nullptr, QLR_BF16, 0, y, ydt};
+  qlr_status st = check_linear(c);
+  if (st != QLR_OK) return st;
+  const int64_t K = w->cols;
+  if (hblock < 1 || (hblock & (hblock - 1)) != 0 || K % hblock != 0)
+    return fail(QLR_ERR_SHAPE, "hblock %d must be a power of two dividing cols %lld", hblock, (long long)K);
+  if (K > qlr::wha_max_cols())
+    return fail(QLR_ERR_SHAPE, "cols %lld above %lld (x rows are transformed in LDS)", (long long)K,
+                (long long)qlr::wha_max_cols());
+  if (F->rows != w->rows || F->cols != K || F->nnz < 0) return fail(QLR_ERR_SHAPE, "F does not match w");
+  if (!F->row_ptr || (F->nnz > 0 && (!F->col || !F->val))) return fail(QLR_ERR_NULL, "F buffer is NULL");
+  if (!aligned16(F->row_ptr) || (F->nnz > 0 && (!aligned16(F->col) || !aligned16(F->val))))
+    return fail(QLR_ERR_ALIGN, "F buffers must be 16-byte aligned");
+  size_t need = 0;
+  qlr_workspace_bytes(QLR_OP_LINEAR_WHA, M, w->rows, K, 0, &need);
+  if (need > 0 && (!ws || ws_bytes < need))
+    return fail(QLR_ERR_WORKSPACE, "workspace of %zu bytes required, got %zu", need, ws ? ws_bytes : (size_t)0);
+  if (need > 0 && !aligned16(ws)) return fail(QLR_ERR_ALIGN, "workspace must be 16-byte aligned");
+  qlr_path path;
+  st = pick_path(M, xdt, QLR_BF16, 0, &path);
+  if (st != QLR_OK) return st;
+  if (M == 0) return QLR_OK;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  float* C = reinterpret_cast<float*>(ws);
+  const float* addend = nullptr;
+  if (F->nnz > 0) {
+    int lp = 0;
+    while ((1 << lp) < hblock) ++lp;
+    const hipError_t e = qlr::launch_wha_addend(x, (int)xdt, M, K, w->rows, lp, F->row_ptr, F->col, F->val, F->nnz,
+                                                C, s);
+    if (e != hipSuccess) return hip_fail(e, "adapter transform launch");
+    addend = C;
+  }
+  return run_linear(c, 0.0f, nullptr, path, s, addend);
 }
 
 qlr_status qlr_force_path(qlr_path path) {

@@ -124,6 +124,12 @@ hipError_t launch_outlier_finish(int64_t rows, int64_t cols, int64_t k, int bits
 hipError_t launch_sparse_addend(const void* x, int xdt, int64_t M, int64_t K, int64_t N, const int32_t* row_ptr,
                                 const int32_t* col, const float* val, int64_t nnz, float* C, hipStream_t s);
 
+// C (M x N float32) = z F^T, z = x blockdiag(H_P) / P (P = 2^lp), F in CSR (N rows, K columns);
+// K % 8 == 0 and K <= wha_max_cols(); nnz >= 1.
+hipError_t launch_wha_addend(const void* x, int xdt, int64_t M, int64_t K, int64_t N, int lp, const int32_t* row_ptr,
+                             const int32_t* col, const float* val, int64_t nnz, float* C, hipStream_t s);
+int64_t wha_max_cols();
+
 // ---- backward (adapter training)
 // Input gradient dx = dy W' + scale u A on the transposed bf16 GEMM: a.x = dy
 // (M x N bf16), a.y = dx (M x K), a.t = u partials (t_splits x M x r float32),

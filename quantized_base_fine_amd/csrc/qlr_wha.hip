@@ -1,0 +1,257 @@
+// Walsh-Hadamard adapter branch (QWHA page, section 2.1 "Adapter design:
+// Walsh-Hadamard adaptation"): dW = F H^-1 with H the +-1 Walsh-Hadamard matrix
+// and F sparse (values c at an index list).  H is symmetric and H^-1 = H / P, so
+// x dW^T = z F^T with z = x blockdiag(H_P) / P: a fast transform of each x row
+// (additions and subtractions only) and a sparse product.
+//
+// One kernel forms C = z F^T (float32, M x N), which the forward kernels add to
+// every output before rounding.  A workgroup stages MR rows of x in LDS as
+// float32 column records (MR values of one column together), transforms them
+// in place within blocks of P columns, and then walks the coefficients of a
+// range of F's rows: G lanes per row, each taking every G-th coefficient in
+// rounds of 4 (all loads of a round in flight together), summed over the G
+// lanes in a fixed butterfly order.
+#include <algorithm>
+
+#include "qlr_internal.h"
+
+namespace qlr {
+
+namespace {
+
+constexpr int64_t kWhaLds = 128 * 1024;
+
+// LDS slot of column c's record: its low 3 bits XORed with bits 3..5, so the 8
+// consecutive records a thread stages, and its neighbours', spread over the banks
+__device__ __forceinline__ int64_t wslot(int64_t c) { return (c & ~int64_t(7)) | ((c & 7) ^ ((c >> 3) & 7)); }
+
+template <int MR>
+struct Rec {
+  float v[MR];
+};
+
+template <int MR>
+__device__ __forceinline__ Rec<MR> rec_load(const float* z, int64_t c) {
+  Rec<MR> r;
+  const float* p = z + wslot(c) * MR;
+  if constexpr (MR % 4 == 0) {
+#pragma unroll
+    for (int q = 0; q < MR / 4; ++q) {
+      const float4 v = reinterpret_cast<const float4*>(p)[q];
+      r.v[4 * q] = v.x;
+      r.v[4 * q + 1] = v.y;
+      r.v[4 * q + 2] = v.z;
+      r.v[4 * q + 3] = v.w;
+    }
+  } else if constexpr (MR == 2) {
+    const float2 v = *reinterpret_cast<const float2*>(p);
+    r.v[0] = v.x;
+    r.v[1] = v.y;
+  } else {
+    r.v[0] = *p;
+  }
+  return r;
+}
+
+template <int MR>
+__device__ __forceinline__ void rec_store(float* z, int64_t c, const Rec<MR>& r) {
+  float* p = z + wslot(c) * MR;
+  if constexpr (MR % 4 == 0) {
+#pragma unroll
+    for (int q = 0; q < MR / 4; ++q)
+      reinterpret_cast<float4*>(p)[q] = make_float4(r.v[4 * q], r.v[4 * q + 1], r.v[4 * q + 2], r.v[4 * q + 3]);
+  } else if constexpr (MR == 2) {
+    *reinterpret_cast<float2*>(p) = make_float2(r.v[0], r.v[1]);
+  } else {
+    *p = r.v[0];
+  }
+}
+
+// blockIdx.x: x rows [MR bx, MR bx + MR); blockIdx.y: F rows [nchunk by, ...).
+// Each thread walks RB rows per pass, G lanes per row.
+template <int XDT, int MR, int G, int RB>
+__global__ __launch_bounds__(256) void k_wha_addend(const void* __restrict__ x, int64_t M, int64_t K, int64_t N,
+                                                    int lp, const int32_t* __restrict__ row_ptr,
+                                                    const int32_t* __restrict__ col, const float* __restrict__ val,
+                                                    int64_t nnz, float* __restrict__ C, int64_t nchunk) {
+  extern __shared__ float4 wha_smem[];
+  float* z = reinterpret_cast<float*>(wha_smem);
+  const int tid = threadIdx.x;
+  const int64_t m0 = (int64_t)blockIdx.x * MR;
+
+  // 1. stage: chunk q = columns 8 q .. 8 q + 7 of each of the MR rows (16-byte loads)
+  for (int64_t q = tid; q < K / 8; q += 256) {
+    float v[MR][8];
+#pragma unroll
+    for (int mm = 0; mm < MR; ++mm) {
+      const bool mv = m0 + mm < M;
+      const int64_t m = mv ? m0 + mm : M - 1;
+      if constexpr (XDT == DT_F32) {
+        const float4* p = reinterpret_cast<const float4*>(reinterpret_cast<const float*>(x) + m * K + 8 * q);
+        const float4 a = p[0], b = p[1];
+        const float e[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[mm][i] = mv ? e[i] : 0.0f;
+      } else {
+        const uint4 u = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(x) + m * K + 8 * q);
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) v[mm][i] = mv ? bf16_bits_to_f32((w[i >> 1] >> (16 * (i & 1))) & 0xFFFFu) : 0.0f;
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      Rec<MR> r;
+#pragma unroll
+      for (int mm = 0; mm < MR; ++mm) r.v[mm] = v[mm][i];
+      rec_store<MR>(z, 8 * q + i, r);
+    }
+  }
+  __syncthreads();
+
+  // 2. the transform within blocks of 2^lp columns, up to 3 bits of the column
+  // index per round: a task is the 8 (4, 2) columns that differ only in bits
+  // b .. b + nbit - 1, loaded, combined by butterflies in registers, stored back
+  for (int b = 0; b < lp; b += 3) {
+    const int nbit = min(3, lp - b);
+    const int R = 1 << nbit;
+    const int64_t h = int64_t(1) << b;
+    const int64_t tasks = K >> nbit;
+    for (int64_t t = tid; t < tasks; t += 256) {
+      const int64_t c0 = ((t >> b) << (b + nbit)) | (t & (h - 1));
+      Rec<MR> r[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (j < R) r[j] = rec_load<MR>(z, c0 + j * h);
+#pragma unroll
+      for (int s = 1; s < 8; s <<= 1) {
+        if (s < R) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            if (j < R && !(j & s)) {
+#pragma unroll
+              for (int mm = 0; mm < MR; ++mm) {
+                const float a = r[j].v[mm], c = r[j + s].v[mm];
+                r[j].v[mm] = a + c;
+                r[j + s].v[mm] = a - c;
+              }
+            }
+          }
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (j < R) rec_store<MR>(z, c0 + j * h, r[j]);
+    }
+    __syncthreads();
+  }
+
+  // 3. the sparse product over the transformed rows
+  const float inv_p = 1.0f / (float)(int64_t(1) << lp);  // exact: a power of two
+  const int g = tid % G;
+  constexpr int kRowsPass = (256 / G) * RB;
+  const int64_t nb = (int64_t)blockIdx.y * nchunk, ne = min(N, nb + nchunk);
+  for (int64_t base = nb; base < ne; base += kRowsPass) {
+    int64_t p0[RB], p1[RB];
+#pragma unroll
+    for (int u = 0; u < RB; ++u) {
+      const int64_t n = base + tid / G + (256 / G) * u;
+      const int64_t nc = n < ne ? n : ne - 1;
+      // offsets and columns clamped into range: a malformed CSR gives wrong sums, never a stray access
+      p0[u] = n < ne ? max<int64_t>(row_ptr[nc], 0) : 0;
+      p1[u] = n < ne ? min<int64_t>(row_ptr[nc + 1], nnz) : 0;
+    }
+    float acc[RB][MR];
+#pragma unroll
+    for (int u = 0; u < RB; ++u)
+#pragma unroll
+      for (int mm = 0; mm < MR; ++mm) acc[u][mm] = 0.0f;
+    for (int64_t e0 = 0;; e0 += 4 * G) {
+      bool more = false;
+#pragma unroll
+      for (int u = 0; u < RB; ++u) more |= p0[u] + e0 + g < p1[u];
+      if (!more) break;
+      int32_t cc[RB][4];
+      float vv[RB][4];
+#pragma unroll
+      for (int u = 0; u < RB; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int64_t j = p0[u] + e0 + g + (int64_t)G * e;
+          const int64_t jc = j < nnz ? j : nnz - 1;
+          cc[u][e] = min<int32_t>(max<int32_t>(col[jc], 0), (int32_t)(K - 1));
+          vv[u][e] = val[jc];
+        }
+#pragma unroll
+      for (int u = 0; u < RB; ++u)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          if (p0[u] + e0 + g + (int64_t)G * e < p1[u]) {
+            const Rec<MR> r = rec_load<MR>(z, cc[u][e]);
+#pragma unroll
+            for (int mm = 0; mm < MR; ++mm) acc[u][mm] = fmaf(vv[u][e], r.v[mm], acc[u][mm]);
+          }
+        }
+    }
+    // sum over the row's G lanes (adjacent lanes of one wave), fixed order
+#pragma unroll
+    for (int o = 1; o < G; o <<= 1)
+#pragma unroll
+      for (int u = 0; u < RB; ++u)
+#pragma unroll
+        for (int mm = 0; mm < MR; ++mm) acc[u][mm] += __shfl_xor(acc[u][mm], o, 64);
+#pragma unroll
+    for (int u = 0; u < RB; ++u) {
+      const int64_t n = base + tid / G + (256 / G) * u;
+      if (g == 0 && n < ne) {
+#pragma unroll
+        for (int mm = 0; mm < MR; ++mm)
+          if (m0 + mm < M) C[(m0 + mm) * N + n] = acc[u][mm] * inv_p;
+      }
+    }
+  }
+}
+
+template <int XDT, int MR, int G, int RB>
+hipError_t wha_t(const void* x, int64_t M, int64_t K, int64_t N, int lp, const int32_t* row_ptr, const int32_t* col,
+                 const float* val, int64_t nnz, float* C, hipStream_t s) {
+  const int64_t xblocks = (M + MR - 1) / MR;
+  constexpr int64_t kRowsPass = (256 / G) * RB;
+  const int64_t nch = std::max<int64_t>(1, std::min<int64_t>((N + kRowsPass - 1) / kRowsPass,
+                                                             (1024 + xblocks - 1) / xblocks));
+  const int64_t nchunk = (N + nch - 1) / nch;
+  const size_t shmem = (size_t)MR * K * 4;
+  static bool attr = false;
+  if (!attr) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_wha_addend<XDT, MR, G, RB>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kWhaLds);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  hipLaunchKernelGGL((k_wha_addend<XDT, MR, G, RB>), dim3((unsigned)xblocks, (unsigned)nch), dim3(256), shmem, s, x,
+                     M, K, N, lp, row_ptr, col, val, nnz, C, nchunk);
+  return hipGetLastError();
+}
+
+template <int XDT>
+hipError_t wha_x(const void* x, int64_t M, int64_t K, int64_t N, int lp, const int32_t* row_ptr, const int32_t* col,
+                 const float* val, int64_t nnz, float* C, hipStream_t s) {
+  if (M >= 8 && 8 * K * 4 <= kWhaLds) return wha_t<XDT, 8, 4, 2>(x, M, K, N, lp, row_ptr, col, val, nnz, C, s);
+  if (M >= 4 && 4 * K * 4 <= kWhaLds) return wha_t<XDT, 4, 4, 2>(x, M, K, N, lp, row_ptr, col, val, nnz, C, s);
+  if (M >= 2 && 2 * K * 4 <= kWhaLds) return wha_t<XDT, 2, 8, 2>(x, M, K, N, lp, row_ptr, col, val, nnz, C, s);
+  return wha_t<XDT, 1, 8, 2>(x, M, K, N, lp, row_ptr, col, val, nnz, C, s);
+}
+
+}  // namespace
+
+int64_t wha_max_cols() { return kWhaLds / 4; }
+
+hipError_t launch_wha_addend(const void* x, int xdt, int64_t M, int64_t K, int64_t N, int lp, const int32_t* row_ptr,
+                             const int32_t* col, const float* val, int64_t nnz, float* C, hipStream_t s) {
+  if (M == 0 || N == 0) return hipSuccess;
+  if (K > wha_max_cols() || K % 8 != 0) return hipErrorInvalidValue;
+  if (xdt == DT_F32) return wha_x<DT_F32>(x, M, K, N, lp, row_ptr, col, val, nnz, C, s);
+  return wha_x<DT_BF16>(x, M, K, N, lp, row_ptr, col, val, nnz, C, s);
+}
+
+}  // namespace qlr

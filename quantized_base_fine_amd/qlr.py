@@ -24,7 +24,7 @@ GROUP = 256
 QLR_F32, QLR_F16, QLR_BF16 = 0, 1, 2
 PATH_AUTO, PATH_F32, PATH_GEMV, PATH_GEMM = 0, 1, 2, 3
 OP_QUANTIZE, OP_LINEAR, OP_LINEAR_BWD, OP_LINEAR_DBA = 0, 1, 2, 3
-OP_QUANTIZE_OUTLIERS, OP_LINEAR_OUTLIERS = 4, 5
+OP_QUANTIZE_OUTLIERS, OP_LINEAR_OUTLIERS, OP_LINEAR_WHA = 4, 5, 6
 
 STATUS = {
     0: "QLR_OK", 1: "QLR_ERR_NULL", 2: "QLR_ERR_SHAPE", 3: "QLR_ERR_DTYPE", 4: "QLR_ERR_BITS",
@@ -103,6 +103,8 @@ EXPORTS = {
                                           C.POINTER(CSparse), C.c_void_p, C.c_void_p, C.c_int, C.c_int32,
                                           C.c_float, C.c_void_p, C.c_int, C.c_void_p, C.c_size_t,
                                           C.c_void_p]),
+    "qlr_linear_fwd_wha": (C.c_int, [C.c_void_p, C.c_int, C.c_int64, C.POINTER(CQWeight), C.POINTER(CSparse),
+                                     C.c_int32, C.c_void_p, C.c_int, C.c_void_p, C.c_size_t, C.c_void_p]),
     "qlr_force_path": (C.c_int, [C.c_int]),
 }
 
@@ -519,3 +521,47 @@ class OutliersCall:
 def linear_outliers(x, qw: QWeight, sp: Sparse, A=None, B=None, scale: float = 0.0, out_dtype=None):
     """y = x W'^T + x S^T + scale (x A^T) B^T; see OutliersCall."""
     return OutliersCall(x, qw, sp, A, B, scale, out_dtype=out_dtype)()
+
+
+class WhaCall:
+    """A prepared ``qlr_linear_fwd_wha`` call: y = x W'^T + x (F H^-1)^T with H the
+    Walsh-Hadamard matrix in blocks of ``hblock`` columns and F the sparse
+    coefficients (a ``Sparse`` of the weight's shape).  Marshalled once (the
+    stream current at construction is used); the tensors are kept alive by the object."""
+
+    def __init__(self, x, qw: QWeight, F: Sparse, hblock: int, out_dtype=None, out=None, ws=None):
+        torch = _torch()
+        _require_cuda(x)
+        M = x.shape[0]
+        if x.shape[1] != qw.cols or (F.rows, F.cols) != (qw.rows, qw.cols):
+            raise ValueError("x (M, K) and F must fit the weight")
+        self.y = out if out is not None else torch.empty((M, qw.rows), dtype=out_dtype or x.dtype, device=x.device)
+        need = workspace_bytes(OP_LINEAR_WHA, M, qw.rows, qw.cols)
+        if ws is None and need > 0:
+            ws = torch.empty(need, dtype=torch.uint8, device=x.device)
+        self._keep = (x, qw, F, ws)
+        self._cw, self._cf = qw.c_struct(), F.c_struct()
+        self._args = (x.data_ptr(), _dt(x), M, C.byref(self._cw), C.byref(self._cf), int(hblock), self.y.data_ptr(),
+                      _dt(self.y), _ptr(ws), 0 if ws is None else ws.numel(), _stream(x.device))
+        self._fn = lib().qlr_linear_fwd_wha
+
+    def __call__(self):
+        check(self._fn(*self._args))
+        return self.y
+
+
+def linear_wha(x, qw: QWeight, F: Sparse, hblock: int, out_dtype=None):
+    """y = x W'^T + x (F H^-1)^T; see WhaCall."""
+    return WhaCall(x, qw, F, hblock, out_dtype=out_dtype)()
+
+
+def sparse_from_csr(rows: int, cols: int, row_ptr, col, val, device) -> Sparse:
+    """A ``Sparse`` on the device from host CSR arrays (int32 offsets and columns, float32 values)."""
+    torch = _torch()
+    nnz = int(row_ptr[-1])
+    sp = Sparse.empty(rows, cols, nnz, device)
+    sp.row_ptr.copy_(torch.as_tensor(row_ptr, dtype=torch.int32))
+    if nnz > 0:
+        sp.col[:nnz].copy_(torch.as_tensor(col, dtype=torch.int32))
+        sp.val[:nnz].copy_(torch.as_tensor(val, dtype=torch.float32))
+    return sp

@@ -269,3 +269,29 @@ def test_outlier_validation_and_workspace():
     # the linear workspace, then the M x N float32 sparse term
     assert qlr.workspace_bytes(qlr.OP_LINEAR_OUTLIERS, 2048, 4096, 4096, 16) == (
         qlr.workspace_bytes(qlr.OP_LINEAR, 2048, 4096, 4096, 16) + 2048 * 4096 * 4)
+
+
+def test_wha_validation_and_workspace():
+    lib = qlr.lib()
+    w = _qw(rows=64, cols=128)
+    good = qlr.CSparse(64, 128, 10, 0x200000, 0x300000, 0x400000)
+
+    def call(F, hb=128, M=4, ws=0x900000, wsb=1 << 24):
+        return qlr.STATUS[lib.qlr_linear_fwd_wha(0x600000, qlr.QLR_BF16, M, C.byref(w), C.byref(F) if F else None, hb,
+                                                 0x700000, qlr.QLR_F32, ws, wsb, None)]
+    assert call(None) == "QLR_ERR_NULL"
+    for hb in (0, 3, 96, 256):  # not a power of two, or not dividing cols
+        assert call(good, hb=hb) == "QLR_ERR_SHAPE"
+    assert call(qlr.CSparse(64, 64, 10, 0x200000, 0x300000, 0x400000)) == "QLR_ERR_SHAPE"
+    assert call(qlr.CSparse(64, 128, 10, 0x200000, 0, 0x400000)) == "QLR_ERR_NULL"
+    assert call(qlr.CSparse(64, 128, 10, 0x200000, 0x300000, 0x400004)) == "QLR_ERR_ALIGN"
+    assert call(good, ws=0) == "QLR_ERR_WORKSPACE"
+    assert call(good, wsb=256) == "QLR_ERR_WORKSPACE"
+    assert call(good, M=0, ws=0, wsb=0) == "QLR_OK"
+    wide = _qw(rows=64, cols=65536)
+    assert qlr.STATUS[lib.qlr_linear_fwd_wha(0x600000, qlr.QLR_BF16, 4, C.byref(wide), C.byref(
+        qlr.CSparse(64, 65536, 10, 0x200000, 0x300000, 0x400000)), 65536, 0x700000, qlr.QLR_F32, 0x900000, 1 << 24,
+        None)] == "QLR_ERR_SHAPE"  # the transform holds x rows in LDS: cols <= 32768
+    # workspace: the M x N float32 branch term
+    assert qlr.workspace_bytes(qlr.OP_LINEAR_WHA, 2048, 4096, 4096) == 2048 * 4096 * 4
+    assert qlr.workspace_bytes(qlr.OP_LINEAR_WHA, 1, 4096, 4096) == 4096 * 4
