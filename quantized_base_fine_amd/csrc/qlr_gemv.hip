@@ -109,6 +109,7 @@ struct Params {
   uint32_t sB;
   uint32_t sX;
   uint32_t sZ;   // 128 zero bytes (x fragments of rows past M)
+  uint32_t sW;   // float32 transform of the x row (Walsh-Hadamard side channel)
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t rsrc(const void* p, int64_t bytes) {
@@ -279,11 +280,11 @@ __device__ __forceinline__ float dot_piece(const u32x4_t& pc, const u32x4_t* xv,
 // every workgroup also computes t = x A^T itself, from A rows read after the
 // code stream has been issued (L2-resident after the first workgroup of each
 // XCD), instead of reading the partial sums of a separate kernel.
-template <int BITS, int YDT, bool XLDS, bool ADP, int D, bool DOT, bool TF, bool SPX>
+template <int BITS, int YDT, bool XLDS, bool ADP, int D, bool DOT, bool TF, int SPX>
 __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
   static_assert(!DOT || (XLDS && BITS != 3), "the single-row path reads x from LDS and 16-byte pieces of whole codes");
   static_assert(!TF || (DOT && ADP), "the fused adapter product belongs to the single-row path");
-  static_assert(!SPX || DOT, "the fused side channel belongs to the single-row path");
+  static_assert(SPX == 0 || DOT, "the fused side channel belongs to the single-row path");
   // per-wave LDS staging buffer: codes and scales, or scales only (single-row path)
   constexpr uint32_t kStageW = DOT ? 16 * CH * 4 : ChunkGeo<BITS>::kStage;
   using G = ChunkGeo<BITS>;
@@ -374,28 +375,45 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
     }
   };
 
-  // Sparse side channel (SPX, a single x row): thread tid & 15 of each wave
-  // holds tile row tid & 15's CSR offsets and its first 4 outliers (clamped,
-  // unconditional loads).  The first tile's offsets are loaded before
-  // everything else and its outliers right after x is in LDS, so both have
-  // long arrived when the tile ends; later tiles load theirs at the tile's end.
+  // Sparse side channel (SPX, a single x row; SPX = 1: the entries multiply x,
+  // SPX = 2: they multiply the Walsh-Hadamard transform of x, formed in LDS).
+  // Tile row o = tid >> 5 belongs to 32 consecutive lanes (half a wave); lane
+  // i = tid & 31 holds the row's CSR offsets and its entries i + 32 e, e < 8
+  // (clamped, unconditional loads: each load instruction reads two contiguous
+  // runs), so 256 entries per row are in registers and the row's sum is a
+  // reduction across its 32 lanes.  The first tile's offsets are loaded before
+  // everything else and its entries right after x is in LDS, so both have long
+  // arrived when the tile ends; later tiles load theirs at the tile's end.
+  constexpr int kSpE = 8;
   int64_t sp0 = 0, sp1 = 0;
-  int32_t spc[4] = {0, 0, 0, 0};
-  float spv[4] = {0.f, 0.f, 0.f, 0.f};
+  int32_t spc[kSpE];
+  float spv[kSpE];
   auto sp_rows = [&](int64_t tile) {
-    const int64_t n = min(tile * 16 + (tid & 15), N - 1);
-    sp0 = max<int64_t>(a.sp_row_ptr[n], 0);
-    sp1 = min<int64_t>(a.sp_row_ptr[n + 1], a.sp_nnz);
+    const int64_t n = min(tile * 16 + (tid >> 5), N - 1);
+    // offsets clamped into range: a malformed CSR gives wrong sums, never a stray access
+    sp0 = min<int64_t>(max<int64_t>(a.sp_row_ptr[n], 0), a.sp_nnz);
+    sp1 = max<int64_t>(sp0, min<int64_t>(a.sp_row_ptr[n + 1], a.sp_nnz));
   };
   auto sp_entries = [&]() {
 #pragma unroll
-    for (int e = 0; e < 4; ++e) {
-      const int64_t j = min(sp0 + e, a.sp_nnz - 1);
+    for (int e = 0; e < kSpE; ++e) {
+      const int64_t j = min(sp0 + (tid & 31) + 32 * e, a.sp_nnz - 1);
       spc[e] = min<int32_t>(max<int32_t>(a.sp_col[j], 0), (int32_t)(K - 1));
       spv[e] = a.sp_val[j];
     }
   };
-  if constexpr (SPX) sp_rows(blockIdx.x);
+  // (SPX = 2) the x row's 16-byte pieces 8 (tid + 512 g) .. + 7, loaded first
+  constexpr int kWG = 4;  // pieces per thread: up to 4 x 4096 columns
+  u32x4_t wx[kWG];
+  if constexpr (SPX == 2) {
+    const uint16_t* x0 = reinterpret_cast<const uint16_t*>(a.x);
+#pragma unroll
+    for (int g = 0; g < kWG; ++g) {
+      const int64_t e0 = 4096 * g + 8 * (int64_t)tid;
+      wx[g] = *reinterpret_cast<const u32x4_t*>(x0 + (e0 < K ? e0 : 0));
+    }
+  }
+  if constexpr (SPX != 0) sp_rows(blockIdx.x);
 
   // Small x: one coalesced copy into LDS per workgroup (rows at stride K + 8),
   // loaded first, so that waiting for it does not wait for the code stream.
@@ -437,6 +455,76 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
     if (++lc == nitem) { lc = 0; ltile += gridDim.x; }
   }
 
+  if constexpr (SPX == 2) {
+    // Transform of the x row in blocks of P = 2^lp columns, float32 at sW
+    // (unscaled), part 1: piece g of thread tid covers columns 8 (tid + 512 g) ..
+    // + 7, so a wave holds 512 consecutive columns; column bits 0-2 are combined
+    // in registers and bits 3-8 across the wave's lanes.  No barrier: it runs
+    // while the first chunks are in flight, and the prologue's barrier ends it.
+    const int lp = a.sp_wht_lp;
+#pragma unroll
+    for (int g = 0; g < kWG; ++g) {
+      const int64_t e0 = 4096 * g + 8 * (int64_t)tid;
+      if (4096 * g >= K) break;  // uniform
+      float v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = bf16_bits_to_f32((wx[g][j >> 1] >> (16 * (j & 1))) & 0xFFFFu);
+#pragma unroll
+      for (int st = 1; st < 8; st <<= 1)
+        if ((1 << lp) > st) {
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            if (!(j & st)) {
+              const float u = v[j], w = v[j + st];
+              v[j] = u + w;
+              v[j + st] = u - w;
+            }
+        }
+      // lane bits 0-1: DPP quad permutations; 2-3: swizzles (xor within 32
+      // lanes); 4-5: half swaps, which hand every lane both operands (a = the
+      // lower lane's value, b = the upper's) so that the pair becomes (a + b, a - b)
+#pragma unroll
+      for (int sb = 0; sb < 4; ++sb)
+        if (lp > 3 + sb) {
+          const bool up = (lane >> sb) & 1;
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const int vi = __float_as_int(v[j]);
+            int oi;
+            if (sb == 0) oi = __builtin_amdgcn_mov_dpp(vi, 0xB1, 0xF, 0xF, false);
+            else if (sb == 1) oi = __builtin_amdgcn_mov_dpp(vi, 0x4E, 0xF, 0xF, false);
+            else if (sb == 2) oi = __builtin_amdgcn_ds_swizzle(vi, (4 << 10) | 0x1F);
+            else oi = __builtin_amdgcn_ds_swizzle(vi, (8 << 10) | 0x1F);
+            const float o = __int_as_float(oi);
+            v[j] = up ? o - v[j] : v[j] + o;
+          }
+        }
+      if (lp > 7) {
+        const bool up = (lane >> 4) & 1;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[j]), __float_as_uint(v[j]), false, false);
+          const float lo = __uint_as_float(sw[0]), hi = __uint_as_float(sw[1]);
+          v[j] = up ? lo - hi : lo + hi;
+        }
+      }
+      if (lp > 8) {
+        const bool up = (lane >> 5) & 1;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[j]), __float_as_uint(v[j]), false, false);
+          const float lo = __uint_as_float(sw[0]), hi = __uint_as_float(sw[1]);
+          v[j] = up ? lo - hi : lo + hi;
+        }
+      }
+      if (e0 < K) {
+        lds_wr128(P.sW + (uint32_t)e0 * 4u, u32x4_t{__float_as_uint(v[0]), __float_as_uint(v[1]),
+                                                  __float_as_uint(v[2]), __float_as_uint(v[3])});
+        lds_wr128(P.sW + (uint32_t)e0 * 4u + 16u, u32x4_t{__float_as_uint(v[4]), __float_as_uint(v[5]),
+                                                        __float_as_uint(v[6]), __float_as_uint(v[7])});
+      }
+    }
+  }
   build_table_kernarg<BITS>(tbl, lv, tid);
   if constexpr (XLDS) {
     if (tid < 8) lds_wr128(P.sZ + 16u * tid, zero);
@@ -457,7 +545,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
       if (q < tcount) sTP[q] = tp[i];
     }
   }
-  if constexpr (SPX) sp_entries();
+  if constexpr (SPX != 0) sp_entries();
   // fused adapter product: lane's 8 elements k0 .. k0 + 7 of every A row j < 16
   // (rows past r and elements past the wave's range read as zero), issued after
   // the table and x are in LDS (issuing them holds the wave for a while)
@@ -472,7 +560,40 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
                                                ars, buf_off(tkv && j < r, (uint32_t)((j * K + tk0) * 2)), 0, 0));
   }
   __syncthreads();
-
+  if constexpr (SPX == 2) {
+    // part 2: column bits 9 and up, in LDS rounds of up to 3 bits (each ends
+    // with a barrier, the last one before any epilogue reads the transform)
+    const int lp = a.sp_wht_lp;
+    for (int b = 9; b < lp; b += 3) {
+      const int nbit = min(3, lp - b);
+      const int R = 1 << nbit;
+      const int64_t h = int64_t(1) << b;
+      for (int64_t t = tid; t < (K >> nbit); t += kThreads) {
+        const int64_t c0 = ((t >> b) << (b + nbit)) | (t & (h - 1));
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (j < R) v[j] = __uint_as_float(lds_rd32(P.sW + (uint32_t)(c0 + j * h) * 4u));
+#pragma unroll
+        for (int st = 1; st < 8; st <<= 1)
+          if (st < R) {
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+              if (j < R && !(j & st)) {
+                const float u = v[j], w = v[j + st];
+                v[j] = u + w;
+                v[j + st] = u - w;
+              }
+          }
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          if (j < R)
+            *reinterpret_cast<__attribute__((address_space(3))) float*>((uintptr_t)(P.sW + (uint32_t)(c0 + j * h) * 4u)) =
+                v[j];
+      }
+      __syncthreads();
+    }
+  }
   // sT[i] = sum over parts of src[part][i], in part order, staged through sRed
   auto stage_t = [&](const float* src, int nparts) {
     const int per = mr > 0 ? max(1, (kWaves * 256) / mr) : 1;
@@ -699,6 +820,12 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
   // Reduce the K slices of a finished tile and write its outputs.  All 512
   // threads run the epilogue (threads past the outputs repeat one and store
   // out of range), so the stores are issued on every path.
+  // row o's side-channel term (SPX = 2: times 1 / P, exact)
+  auto sp_sum = [&](int o) {
+    float t = sRed[256 + o];
+    if constexpr (SPX == 2) t *= 1.0f / (float)(1 << a.sp_wht_lp);
+    return t;
+  };
   auto finish_tile = [&](int64_t tl) {
     if constexpr (DOT) {
 #pragma unroll
@@ -707,22 +834,28 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
         if (lane % G::PR == 0) sRed[wave * 16 + (i * 64 + lane) / G::PR] = v;
         accd[i] = 0.0f;
       }
-      if constexpr (SPX) {
-        // side-channel sum of tile row tid (float32, outliers in CSR order) into sRed slot kWaves * 16 + tid
+      if constexpr (SPX != 0) {
+        // side-channel sum of tile row o = tid >> 5: lane i adds its entries
+        // i + 32 e in e order (then i + 256 + 32 k), the 32 lanes are summed by
+        // a fixed butterfly, and lane 0 writes sRed slot 256 + o
         if (tl != blockIdx.x) {
           sp_rows(tl);
           sp_entries();
         }
-        if (tid < 16) {
-          auto xv = [&](int32_t c) { return bf16_bits_to_f32(lds_rd16(P.sX + (uint32_t)c * 2u)); };
-          float sum = 0.0f;
+        auto src = [&](int32_t c) {
+          if constexpr (SPX == 1) return bf16_bits_to_f32(lds_rd16(P.sX + (uint32_t)c * 2u));
+          else return __uint_as_float(lds_rd32(P.sW + (uint32_t)c * 4u));
+        };
+        const int64_t li = tid & 31;
+        float sum = 0.0f;
 #pragma unroll
-          for (int e = 0; e < 4; ++e)
-            if (sp0 + e < sp1) sum = fmaf(spv[e], xv(spc[e]), sum);
-          for (int64_t j = sp0 + 4; j < sp1; ++j)
-            sum = fmaf(a.sp_val[j], xv(min<int32_t>(max<int32_t>(a.sp_col[j], 0), (int32_t)(K - 1))), sum);
-          sRed[kWaves * 16 + tid] = sum;
-        }
+        for (int e = 0; e < kSpE; ++e)
+          if (sp0 + li + 32 * e < sp1) sum = fmaf(spv[e], src(spc[e]), sum);
+        for (int64_t j = sp0 + li + 32 * kSpE; j < sp1; j += 32)
+          sum = fmaf(a.sp_val[j], src(min<int32_t>(max<int32_t>(a.sp_col[j], 0), (int32_t)(K - 1))), sum);
+#pragma unroll
+        for (int o = 1; o < 32; o <<= 1) sum += __shfl_xor(sum, o, 64);
+        if (li == 0) sRed[256 + (tid >> 5)] = sum;
       }
       __syncthreads();
       if constexpr (TF) {
@@ -741,7 +874,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
         for (int w = 0; w < kWaves; ++w) s += sRed[w * 16 + o];
         const int64_t nn = tl * 16 + o;
         float out = fmaf(a.scale, lo, s);
-        if constexpr (SPX) out += sRed[kWaves * 16 + o];
+        if constexpr (SPX != 0) out += sp_sum(o);
         if (a.addend && tid < 256 && j == 0 && nn < N) out += a.addend[nn];
         const uint32_t yo = buf_off(tid < 256 && j == 0 && nn < N, (uint32_t)(nn * ES));
         if constexpr (YDT == DT_F32) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(out), yr, yo, 0, 0);
@@ -752,7 +885,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
 #pragma unroll
         for (int w = 0; w < kWaves; ++w) s += sRed[w * 16 + o];
         const int64_t nn = tl * 16 + o;
-        if constexpr (SPX) s += sRed[kWaves * 16 + o];
+        if constexpr (SPX != 0) s += sp_sum(o);
         epilogue(0, o, nn, tid < 16 && nn < N, s);
       }
     } else {
@@ -835,7 +968,7 @@ int device_cus() {
   return cus;
 }
 
-template <int BITS, int YDT, bool XLDS, bool ADP, int D, bool DOT = false, bool TF = false, bool SPX = false>
+template <int BITS, int YDT, bool XLDS, bool ADP, int D, bool DOT = false, bool TF = false, int SPX = 0>
 hipError_t launch_k(const Params& P, int64_t grid, size_t shmem, const Levels& lv, hipStream_t s) {
   auto kern = k_gemv<BITS, YDT, XLDS, ADP, D, DOT, TF, SPX>;
   static bool attr = false;
@@ -864,6 +997,7 @@ struct Plan {
   bool deep = false;  // a wave's chunk stream is longer than 2 (ring depth 4)
   bool dot = false;   // single-row path
   bool tf = false;    // fused adapter product
+  bool spw = false;   // room for the transform of the x row (Walsh-Hadamard side channel)
 };
 
 template <int BITS>
@@ -934,6 +1068,11 @@ Plan plan_gemv(const LinearArgs& a) {
     pl.dot = dot;
     pl.tf = tf && P.tmode == T_FUSED;
     pl.lds = lds + (xlds ? xbytes : 0);
+    if (a.sp_row_ptr && a.sp_wht_lp >= 0 && dot) {
+      P.sW = (uint32_t)r16(pl.lds);
+      pl.spw = P.sW + (size_t)a.K * 4 <= kLdsMax;
+      if (pl.spw) pl.lds = P.sW + (size_t)a.K * 4;
+    }
     return pl;
   }
   pl.ok = false;
@@ -952,9 +1091,13 @@ hipError_t launch_gemv_b(const LinearArgs& a, const Levels& lv, hipStream_t s) {
     // the side channel is summed in the kernel only on the single-row path with a short stream
     if constexpr (BITS != 3) {
       if (pl.dot && !pl.deep && a.sp_nnz > 0) {
-        if (pl.tf) return launch_k<BITS, YDT, true, true, 2, true, true, true>(P, grid, lds, lv, s);
-        if (adp) return launch_k<BITS, YDT, true, true, 2, true, false, true>(P, grid, lds, lv, s);
-        return launch_k<BITS, YDT, true, false, 2, true, false, true>(P, grid, lds, lv, s);
+        if (a.sp_wht_lp >= 0) {
+          if (!pl.spw || adp) return hipErrorInvalidValue;
+          return launch_k<BITS, YDT, true, false, 2, true, false, 2>(P, grid, lds, lv, s);
+        }
+        if (pl.tf) return launch_k<BITS, YDT, true, true, 2, true, true, 1>(P, grid, lds, lv, s);
+        if (adp) return launch_k<BITS, YDT, true, true, 2, true, false, 1>(P, grid, lds, lv, s);
+        return launch_k<BITS, YDT, true, false, 2, true, false, 1>(P, grid, lds, lv, s);
       }
     }
     return hipErrorInvalidValue;
@@ -1010,7 +1153,7 @@ bool gemv_fuses_sparse(const LinearArgs& a) {
     case 4: pl = plan_gemv<4>(a); break;
     default: pl = plan_gemv<8>(a); break;
   }
-  return pl.ok && pl.dot && !pl.deep;
+  return pl.ok && pl.dot && !pl.deep && (a.sp_wht_lp < 0 || (pl.spw && a.r <= 0));
 }
 
 hipError_t launch_gemv(const LinearArgs& a, const Levels& lv, hipStream_t s) {

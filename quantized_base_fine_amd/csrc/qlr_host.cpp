@@ -235,7 +235,7 @@ qlr::LinearArgs make_args(const LinearCheck& c, float scale, char* ws, int split
 // The sparse side channel, when given, is summed inside the decode kernel (the
 // caller has checked sparse_fused); addend is the alternative, a precomputed term.
 qlr_status run_linear(const LinearCheck& c, float scale, char* ws, qlr_path path, hipStream_t s,
-                      const float* addend = nullptr, const qlr_sparse* sp = nullptr) {
+                      const float* addend = nullptr, const qlr_sparse* sp = nullptr, int wht_lp = -1) {
   if (c.M == 0) return QLR_OK;
   hipError_t e = hipSuccess;
   const int splits = qlr::lora_t_splits(c.M, c.w->cols, (int)c.xdt, (int)c.abdt);
@@ -246,6 +246,7 @@ qlr_status run_linear(const LinearCheck& c, float scale, char* ws, qlr_path path
     a.sp_col = sp->col;
     a.sp_val = sp->val;
     a.sp_nnz = sp->nnz;
+    a.sp_wht_lp = wht_lp;
   }
   if (c.r > 0 && !(path == QLR_PATH_GEMV && qlr::gemv_fuses_adapter(a))) {
     e = qlr::launch_lora_t(c.x, (int)c.xdt, c.M, c.w->cols, c.A, (int)c.abdt, c.r,
@@ -805,9 +806,19 @@ qlr_status qlr_linear_fwd_wha(const void* x, qlr_dtype xdt, int64_t M, const qlr
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   float* C = reinterpret_cast<float*>(ws);
   const float* addend = nullptr;
+  int lp = 0;
+  while ((1 << lp) < hblock) ++lp;
+  if (F->nnz > 0 && path == QLR_PATH_GEMV) {
+    // a single x row on the decode kernel: the transform and the coefficients are summed inside it
+    qlr::LinearArgs probe = make_args(c, 0.0f, nullptr, 1);
+    probe.sp_row_ptr = F->row_ptr;
+    probe.sp_col = F->col;
+    probe.sp_val = F->val;
+    probe.sp_nnz = F->nnz;
+    probe.sp_wht_lp = lp;
+    if (qlr::gemv_fuses_sparse(probe)) return run_linear(c, 0.0f, nullptr, path, s, nullptr, F, lp);
+  }
   if (F->nnz > 0) {
-    int lp = 0;
-    while ((1 << lp) < hblock) ++lp;
     const hipError_t e = qlr::launch_wha_addend(x, (int)xdt, M, K, w->rows, lp, F->row_ptr, F->col, F->val, F->nnz,
                                                 C, s);
     if (e != hipSuccess) return hip_fail(e, "adapter transform launch");

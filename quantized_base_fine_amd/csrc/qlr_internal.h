@@ -72,6 +72,9 @@ struct LinearArgs {
   const int32_t* sp_col = nullptr;
   const float* sp_val = nullptr;
   int64_t sp_nnz = 0;
+  // >= 0: the side channel multiplies the Walsh-Hadamard transform of x over
+  // blocks of 2^sp_wht_lp columns, scaled by 2^-sp_wht_lp, instead of x
+  int sp_wht_lp = -1;
 };
 
 // float32 path: any dtypes, any M.
