@@ -9,7 +9,7 @@
 // float32 column records (MR values of one column together), transforms them
 // in place within blocks of P columns, and then walks the coefficients of a
 // range of F's rows: G lanes per row, each taking every G-th coefficient in
-// rounds of 4 (all loads of a round in flight together), summed over the G
+// rounds of 8 (all loads of a round in flight together), summed over the G
 // lanes in a fixed butterfly order.
 #include <algorithm>
 
@@ -68,9 +68,12 @@ __device__ __forceinline__ void rec_store(float* z, int64_t c, const Rec<MR>& r)
 }
 
 // blockIdx.x: x rows [MR bx, MR bx + MR); blockIdx.y: F rows [nchunk by, ...).
-// Each thread walks RB rows per pass, G lanes per row.
-template <int XDT, int MR, int G, int RB>
-__global__ __launch_bounds__(256) void k_wha_addend(const void* __restrict__ x, int64_t M, int64_t K, int64_t N,
+// TB threads; G lanes per F row, lane g taking the row's coefficients
+// g + G u (u < 8) of each round, so a round covers 8 G consecutive ones; each
+// lane walks RB rows per pass, and the next pass's row offsets are loaded
+// while the current pass's coefficients are in flight.
+template <int XDT, int MR, int G, int RB, int TB>
+__global__ __launch_bounds__(TB) void k_wha_addend(const void* __restrict__ x, int64_t M, int64_t K, int64_t N,
                                                     int lp, const int32_t* __restrict__ row_ptr,
                                                     const int32_t* __restrict__ col, const float* __restrict__ val,
                                                     int64_t nnz, float* __restrict__ C, int64_t nchunk) {
@@ -80,7 +83,7 @@ __global__ __launch_bounds__(256) void k_wha_addend(const void* __restrict__ x, 
   const int64_t m0 = (int64_t)blockIdx.x * MR;
 
   // 1. stage: chunk q = columns 8 q .. 8 q + 7 of each of the MR rows (16-byte loads)
-  for (int64_t q = tid; q < K / 8; q += 256) {
+  for (int64_t q = tid; q < K / 8; q += TB) {
     float v[MR][8];
 #pragma unroll
     for (int mm = 0; mm < MR; ++mm) {
@@ -117,7 +120,7 @@ __global__ __launch_bounds__(256) void k_wha_addend(const void* __restrict__ x, 
     const int R = 1 << nbit;
     const int64_t h = int64_t(1) << b;
     const int64_t tasks = K >> nbit;
-    for (int64_t t = tid; t < tasks; t += 256) {
+    for (int64_t t = tid; t < tasks; t += TB) {
       const int64_t c0 = ((t >> b) << (b + nbit)) | (t & (h - 1));
       Rec<MR> r[8];
 #pragma unroll
@@ -149,34 +152,40 @@ __global__ __launch_bounds__(256) void k_wha_addend(const void* __restrict__ x, 
   // 3. the sparse product over the transformed rows
   const float inv_p = 1.0f / (float)(int64_t(1) << lp);  // exact: a power of two
   const int g = tid % G;
-  constexpr int kRowsPass = (256 / G) * RB;
+  constexpr int kE = 8;                       // coefficients per lane per round
+  constexpr int kRowsPass = (TB / G) * RB;
   const int64_t nb = (int64_t)blockIdx.y * nchunk, ne = min(N, nb + nchunk);
-  for (int64_t base = nb; base < ne; base += kRowsPass) {
-    int64_t p0[RB], p1[RB];
+  // row offsets of a pass, clamped into range: a malformed CSR gives wrong sums, never a stray access
+  auto offsets = [&](int64_t base, int64_t (&q0)[RB], int64_t (&q1)[RB]) {
 #pragma unroll
     for (int u = 0; u < RB; ++u) {
-      const int64_t n = base + tid / G + (256 / G) * u;
+      const int64_t n = base + tid / G + (TB / G) * u;
       const int64_t nc = n < ne ? n : ne - 1;
-      // offsets and columns clamped into range: a malformed CSR gives wrong sums, never a stray access
-      p0[u] = n < ne ? max<int64_t>(row_ptr[nc], 0) : 0;
-      p1[u] = n < ne ? min<int64_t>(row_ptr[nc + 1], nnz) : 0;
+      q0[u] = n < ne ? min<int64_t>(max<int64_t>(row_ptr[nc], 0), nnz) : 0;
+      q1[u] = n < ne ? max<int64_t>(q0[u], min<int64_t>(row_ptr[nc + 1], nnz)) : 0;
     }
+  };
+  int64_t p0[RB], p1[RB];
+  offsets(nb, p0, p1);
+  for (int64_t base = nb; base < ne; base += kRowsPass) {
+    int64_t n0[RB], n1[RB];
+    offsets(base + kRowsPass, n0, n1);  // the next pass's (past ne: empty)
     float acc[RB][MR];
 #pragma unroll
     for (int u = 0; u < RB; ++u)
 #pragma unroll
       for (int mm = 0; mm < MR; ++mm) acc[u][mm] = 0.0f;
-    for (int64_t e0 = 0;; e0 += 4 * G) {
+    for (int64_t e0 = 0;; e0 += kE * G) {
       bool more = false;
 #pragma unroll
       for (int u = 0; u < RB; ++u) more |= p0[u] + e0 + g < p1[u];
       if (!more) break;
-      int32_t cc[RB][4];
-      float vv[RB][4];
+      int32_t cc[RB][kE];
+      float vv[RB][kE];
 #pragma unroll
       for (int u = 0; u < RB; ++u)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
+        for (int e = 0; e < kE; ++e) {
           const int64_t j = p0[u] + e0 + g + (int64_t)G * e;
           const int64_t jc = j < nnz ? j : nnz - 1;
           cc[u][e] = min<int32_t>(max<int32_t>(col[jc], 0), (int32_t)(K - 1));
@@ -185,7 +194,7 @@ __global__ __launch_bounds__(256) void k_wha_addend(const void* __restrict__ x, 
 #pragma unroll
       for (int u = 0; u < RB; ++u)
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
+        for (int e = 0; e < kE; ++e) {
           if (p0[u] + e0 + g + (int64_t)G * e < p1[u]) {
             const Rec<MR> r = rec_load<MR>(z, cc[u][e]);
 #pragma unroll
@@ -202,33 +211,39 @@ __global__ __launch_bounds__(256) void k_wha_addend(const void* __restrict__ x, 
         for (int mm = 0; mm < MR; ++mm) acc[u][mm] += __shfl_xor(acc[u][mm], o, 64);
 #pragma unroll
     for (int u = 0; u < RB; ++u) {
-      const int64_t n = base + tid / G + (256 / G) * u;
+      const int64_t n = base + tid / G + (TB / G) * u;
       if (g == 0 && n < ne) {
 #pragma unroll
         for (int mm = 0; mm < MR; ++mm)
           if (m0 + mm < M) C[(m0 + mm) * N + n] = acc[u][mm] * inv_p;
       }
     }
+#pragma unroll
+    for (int u = 0; u < RB; ++u) {
+      p0[u] = n0[u];
+      p1[u] = n1[u];
+    }
   }
 }
 
-template <int XDT, int MR, int G, int RB>
+template <int XDT, int MR, int G, int RB, int TB>
 hipError_t wha_t(const void* x, int64_t M, int64_t K, int64_t N, int lp, const int32_t* row_ptr, const int32_t* col,
                  const float* val, int64_t nnz, float* C, hipStream_t s) {
   const int64_t xblocks = (M + MR - 1) / MR;
-  constexpr int64_t kRowsPass = (256 / G) * RB;
+  constexpr int64_t kRowsPass = (TB / G) * RB;
+  // enough workgroups to fill the chip (each stages and transforms its x rows once)
   const int64_t nch = std::max<int64_t>(1, std::min<int64_t>((N + kRowsPass - 1) / kRowsPass,
-                                                             (1024 + xblocks - 1) / xblocks));
+                                                             (256 + xblocks - 1) / xblocks));
   const int64_t nchunk = (N + nch - 1) / nch;
   const size_t shmem = (size_t)MR * K * 4;
   static bool attr = false;
   if (!attr) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_wha_addend<XDT, MR, G, RB>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_wha_addend<XDT, MR, G, RB, TB>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)kWhaLds);
     if (e != hipSuccess) return e;
     attr = true;
   }
-  hipLaunchKernelGGL((k_wha_addend<XDT, MR, G, RB>), dim3((unsigned)xblocks, (unsigned)nch), dim3(256), shmem, s, x,
+  hipLaunchKernelGGL((k_wha_addend<XDT, MR, G, RB, TB>), dim3((unsigned)xblocks, (unsigned)nch), dim3(TB), shmem, s, x,
                      M, K, N, lp, row_ptr, col, val, nnz, C, nchunk);
   return hipGetLastError();
 }
@@ -236,10 +251,10 @@ hipError_t wha_t(const void* x, int64_t M, int64_t K, int64_t N, int lp, const i
 template <int XDT>
 hipError_t wha_x(const void* x, int64_t M, int64_t K, int64_t N, int lp, const int32_t* row_ptr, const int32_t* col,
                  const float* val, int64_t nnz, float* C, hipStream_t s) {
-  if (M >= 8 && 8 * K * 4 <= kWhaLds) return wha_t<XDT, 8, 4, 2>(x, M, K, N, lp, row_ptr, col, val, nnz, C, s);
-  if (M >= 4 && 4 * K * 4 <= kWhaLds) return wha_t<XDT, 4, 4, 2>(x, M, K, N, lp, row_ptr, col, val, nnz, C, s);
-  if (M >= 2 && 2 * K * 4 <= kWhaLds) return wha_t<XDT, 2, 8, 2>(x, M, K, N, lp, row_ptr, col, val, nnz, C, s);
-  return wha_t<XDT, 1, 8, 2>(x, M, K, N, lp, row_ptr, col, val, nnz, C, s);
+  if (M >= 8 && 8 * K * 4 <= kWhaLds) return wha_t<XDT, 8, 4, 1, 1024>(x, M, K, N, lp, row_ptr, col, val, nnz, C, s);
+  if (M >= 4 && 4 * K * 4 <= kWhaLds) return wha_t<XDT, 4, 4, 1, 1024>(x, M, K, N, lp, row_ptr, col, val, nnz, C, s);
+  if (M >= 2 && 2 * K * 4 <= kWhaLds) return wha_t<XDT, 2, 4, 1, 1024>(x, M, K, N, lp, row_ptr, col, val, nnz, C, s);
+  return wha_t<XDT, 1, 4, 1, 1024>(x, M, K, N, lp, row_ptr, col, val, nnz, C, s);
 }
 
 }  // namespace
