@@ -144,7 +144,7 @@ def traffic_from_profile(kernel_key: str):
 # built from (the stored figure is dropped when any of them changes).
 _CSRC = "quantized_base_fine_amd/csrc/"
 TRAFFIC_KERNELS = {
-    "decode": ("k_gemv<4, 2, true, false, 2, true, false>",
+    "decode": ("k_gemv<4, 2, true, false, 2, true, false, 0>",
                [_CSRC + f for f in ("qlr_gemv.hip", "qlr_lut.h", "qlr_device.h", "qlr_internal.h")]),
     "prefill": ("k_gemm<4, 2, false, false>",
                 [_CSRC + f for f in ("qlr_gemm.hip", "qlr_lut.h", "qlr_device.h", "qlr_internal.h")]),
@@ -309,6 +309,9 @@ def main():
     ap.add_argument("--no-mixed", action="store_true", help="skip the mixed-stack phase")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="first run one elementwise copy of 256 MiB (counter calibration)")
+    ap.add_argument("--counter-phases", action="store_true",
+                    help="time only the fp16-adapter and base phases (one launch per layer of each roofline "
+                         "kernel) and print their per-call times: for the counter runs")
     ap.add_argument("--eager", action="store_true",
                     help="no HIP graphs (every launch visible to per-dispatch counter collection)")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -435,6 +438,8 @@ def main():
 
     PHASES = ("prefill", "prefill_base", "decode", "decode_base", "backward", "backward_base", "dba_decode",
               "dba_prefill", "ol_decode", "ol_prefill", "wha_decode", "wha_prefill")
+    if args.counter_phases:
+        PHASES = PHASES[:6]
     mixed = None
     if not args.no_mixed:
         mixed, mixed_flops, mixed_n = build_mixed(torch, qlr, workloads, dev)
@@ -444,7 +449,8 @@ def main():
     # The decode phases (short, launch-bound calls) also run as HIP graphs of the
     # R prepared calls; every replay is checked against the eager outputs first.
     graphs = {}
-    for ph in (() if args.eager else ("decode", "decode_base", "dba_decode", "ol_decode", "wha_decode")):
+    for ph in (() if args.eager else tuple(p for p in ("decode", "decode_base", "dba_decode", "ol_decode", "wha_decode")
+                                            if p in PHASES)):
         for L in layers:
             L[ph]()
         torch.cuda.synchronize()
@@ -519,6 +525,9 @@ def main():
             phase_ms["mixed"] += marks[2 + len(PHASES)].elapsed_time(marks[3 + len(PHASES)])
     S = args.steps
     mean = {p: 1e3 * phase_ms[p] / (S * R) for p in PHASES}  # average launch duration, us
+    if args.counter_phases:
+        print(json.dumps({"call_us": {p: round(v, 3) for p, v in mean.items()}}))
+        return
     dec_gbs = S * R * decode_bytes() / (phase_ms["decode"] / 1e3) / 1e9
     pre_tfs = S * R * prefill_flops() / (phase_ms["prefill"] / 1e3) / 1e12
     q_gbs = S * R * quantize_bytes() / (phase_ms["quantize"] / 1e3) / 1e9
