@@ -342,11 +342,9 @@ __global__ __launch_bounds__(256) void k_ol_rowptr(int64_t rows, int64_t cols, i
 // blockIdx.x: MR rows of x, staged in LDS transposed (sx[c][mm], MR values of
 // one column contiguous, so one 16-byte read serves 8 bf16 rows); MR = 0 reads
 // one x row from global memory (rows too long for LDS).  blockIdx.y: a range of
-// weight rows; each thread takes 8 rows at a time and walks their outliers in
-// rounds of 4 per row, every load of a round issued before any is used
-// (unconditional, clamped loads).
-template <int XDT, int MR>
-__global__ __launch_bounds__(256) void k_sparse_addend(const void* __restrict__ x, int64_t M, int64_t K, int64_t N,
+// weight rows, 1024 threads each taking one row per pass (see the loop).
+template <int XDT, int MR, int TB>
+__global__ __launch_bounds__(TB) void k_sparse_addend(const void* __restrict__ x, int64_t M, int64_t K, int64_t N,
                                                        const int32_t* __restrict__ row_ptr,
                                                        const int32_t* __restrict__ col,
                                                        const float* __restrict__ val, int64_t nnz,
@@ -366,7 +364,7 @@ __global__ __launch_bounds__(256) void k_sparse_addend(const void* __restrict__ 
   auto sl = [](int64_t c) -> int64_t { return (c & ~int64_t(7)) | ((c & 7) ^ ((c >> 3) & 7)); };
   if constexpr (MR > 0) {
     // chunk q of the x rows: EPC consecutive columns of each of the MR rows
-    for (int64_t q = tid; q < K / EPC; q += 256) {
+    for (int64_t q = tid; q < K / EPC; q += TB) {
       XT v[MR][EPC];
 #pragma unroll
       for (int mm = 0; mm < MR; ++mm) {
@@ -417,60 +415,52 @@ __global__ __launch_bounds__(256) void k_sparse_addend(const void* __restrict__ 
     }
   };
   const int64_t nb = (int64_t)blockIdx.y * nchunk, ne = min(N, nb + nchunk);
-  constexpr int RB = 8;  // weight rows per thread per batch
-  for (int64_t base = nb; base < ne; base += RB * 256) {
-    int64_t p0[RB], p1[RB];
+  // one weight row per thread and pass; its outliers in rounds of 8 (every load
+  // of a round in flight together); the next pass's offsets are loaded while the
+  // current pass's outliers are in flight.  Offsets and columns are clamped into
+  // range: a malformed CSR gives wrong sums, never a stray access.
+  constexpr int kE = 8;
+  auto offsets = [&](int64_t base, int64_t& q0, int64_t& q1) {
+    const int64_t n = base + tid;
+    const int64_t nc = n < ne ? n : ne - 1;
+    q0 = n < ne ? min<int64_t>(max<int64_t>(row_ptr[nc], 0), nnz) : 0;
+    q1 = n < ne ? max<int64_t>(q0, min<int64_t>(row_ptr[nc + 1], nnz)) : 0;
+  };
+  int64_t p0, p1;
+  offsets(nb, p0, p1);
+  for (int64_t base = nb; base < ne; base += TB) {
+    int64_t n0, n1;
+    offsets(base + TB, n0, n1);
+    float acc[R];
 #pragma unroll
-    for (int u = 0; u < RB; ++u) {
-      const int64_t n = base + tid + 256 * u;
-      const int64_t nc = n < ne ? n : ne - 1;
-      // offsets and columns are clamped into range: a malformed CSR gives wrong sums, never a stray access
-      p0[u] = n < ne ? max<int64_t>(row_ptr[nc], 0) : 0;
-      p1[u] = n < ne ? min<int64_t>(row_ptr[nc + 1], nnz) : 0;
-    }
-    float acc[RB][R];
+    for (int mm = 0; mm < R; ++mm) acc[mm] = 0.0f;
+    for (int64_t e0 = p0; e0 < p1; e0 += kE) {
+      int32_t cc[kE];
+      float vv[kE];
 #pragma unroll
-    for (int u = 0; u < RB; ++u)
+      for (int e = 0; e < kE; ++e) {
+        const int64_t jc = e0 + e < nnz ? e0 + e : nnz - 1;
+        cc[e] = min<int32_t>(max<int32_t>(col[jc], 0), (int32_t)(K - 1));
+        vv[e] = val[jc];
+      }
 #pragma unroll
-      for (int mm = 0; mm < R; ++mm) acc[u][mm] = 0.0f;
-    // rounds of 4 outliers per row: every row's loads of a round are in flight together
-    for (int64_t e0 = 0;; e0 += 4) {
-      bool more = false;
+      for (int e = 0; e < kE; ++e) {
+        if (e0 + e < p1) {
+          float xv[R];
+          xcol(cc[e], xv);
 #pragma unroll
-      for (int u = 0; u < RB; ++u) more |= p0[u] + e0 < p1[u];
-      if (!more) break;
-      int32_t cc[RB][4];
-      float vv[RB][4];
-#pragma unroll
-      for (int u = 0; u < RB; ++u)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const int64_t j = p0[u] + e0 + e;
-          const int64_t jc = j < nnz ? j : nnz - 1;
-          cc[u][e] = min<int32_t>(max<int32_t>(col[jc], 0), (int32_t)(K - 1));
-          vv[u][e] = val[jc];
+          for (int mm = 0; mm < R; ++mm) acc[mm] = fmaf(vv[e], xv[mm], acc[mm]);
         }
-#pragma unroll
-      for (int u = 0; u < RB; ++u)
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          if (p0[u] + e0 + e < p1[u]) {
-            float xv[R];
-            xcol(cc[u][e], xv);
-#pragma unroll
-            for (int mm = 0; mm < R; ++mm) acc[u][mm] = fmaf(vv[u][e], xv[mm], acc[u][mm]);
-          }
-        }
-    }
-#pragma unroll
-    for (int u = 0; u < RB; ++u) {
-      const int64_t n = base + tid + 256 * u;
-      if (n < ne) {
-#pragma unroll
-        for (int mm = 0; mm < R; ++mm)
-          if (m0 + mm < M) C[(m0 + mm) * N + n] = acc[u][mm];
       }
     }
+    const int64_t n = base + tid;
+    if (n < ne) {
+#pragma unroll
+      for (int mm = 0; mm < R; ++mm)
+        if (m0 + mm < M) C[(m0 + mm) * N + n] = acc[mm];
+    }
+    p0 = n0;
+    p1 = n1;
   }
 }
 
@@ -478,19 +468,21 @@ template <int XDT, int MR>
 hipError_t sparse_addend_t(const void* x, int64_t M, int64_t K, int64_t N, const int32_t* row_ptr,
                            const int32_t* col, const float* val, int64_t nnz, float* C, hipStream_t s) {
   constexpr int R = MR > 0 ? MR : 1;
+  constexpr int TB = 1024;
   const int64_t xblocks = (M + R - 1) / R;
-  const int64_t nch = std::max<int64_t>(1, std::min<int64_t>((N + 255) / 256, (512 + xblocks - 1) / xblocks));
+  // enough workgroups to fill the chip (each stages its x rows once)
+  const int64_t nch = std::max<int64_t>(1, std::min<int64_t>((N + TB - 1) / TB, (256 + xblocks - 1) / xblocks));
   const int64_t nchunk = (N + nch - 1) / nch;
   const size_t es = XDT == DT_F32 ? 4 : 2;
   const size_t shmem = MR > 0 ? (size_t)MR * K * es : 0;
   static bool attr = false;
   if (!attr) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_sparse_addend<XDT, MR>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_sparse_addend<XDT, MR, TB>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, kSparseLds);
     if (e != hipSuccess) return e;
     attr = true;
   }
-  hipLaunchKernelGGL((k_sparse_addend<XDT, MR>), dim3((unsigned)xblocks, (unsigned)nch), dim3(256), shmem, s, x, M,
+  hipLaunchKernelGGL((k_sparse_addend<XDT, MR, TB>), dim3((unsigned)xblocks, (unsigned)nch), dim3(TB), shmem, s, x, M,
                      K, N, row_ptr, col, val, nnz, C, nchunk);
   return hipGetLastError();
 }
