@@ -57,9 +57,18 @@ def transform_matrix(K: int, P: int) -> np.ndarray:
 
 
 def wht_rows(x, xdtype: str, P: int) -> np.ndarray:
-    """z = x blockdiag(H_P) / P (float64), i.e. x H^-T with H^-1 = H / P."""
+    """z = x blockdiag(H_P) / P (float64), i.e. x H^-T with H^-1 = H / P.
+
+    Written per block (block b of z is block b of x times H_P): the same product
+    as with the full block-diagonal matrix, without forming it for wide K."""
     x64 = widen(x, xdtype).astype(np.float64)
-    return x64 @ transform_matrix(x64.shape[1], P) / P
+    M, K = x64.shape
+    _check_block(K, P)
+    Hp = hadamard(P)
+    z = np.empty_like(x64)
+    for b in range(K // P):
+        z[:, b * P:(b + 1) * P] = x64[:, b * P:(b + 1) * P] @ Hp
+    return z / P
 
 
 def delta_w(csr, N: int, K: int, P: int) -> np.ndarray:

@@ -235,3 +235,12 @@ def test_fwd_graph_replays_match_eager():
         torch.cuda.synchronize()
         assert torch.equal(call.y, ref), i
         _ = (x.float() * 2).sum().item()
+
+
+@pytest.mark.parametrize("path,M", [("gemv", 1), ("gemv", 5), ("gemm", 40), ("f32", 3)])
+def test_fwd_wide_rows(path, M):
+    """K = 11008 (the 7B-class down projection's width), 1 % outliers."""
+    lin, k = _layer(256, 11008, M, 16, seed=120 + M)
+    qw, sp = _gpu_split(lin.W, lin.wdtype, lin.bits, k)
+    q, csr = ool.quantize_with_outliers(lin.W, lin.wdtype, lin.bits, lin.N, lin.K, k)
+    _check_fwd(_run(lin, qw, sp, "f32", PATHS[path]), lin, q, csr)

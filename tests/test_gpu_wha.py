@@ -144,3 +144,20 @@ def test_wha_graph_replays_match_eager():
         torch.cuda.synchronize()
         assert torch.equal(call.y, ref), i
         _ = (x.float() * 2).sum().item()
+
+
+@pytest.mark.parametrize("path,M", [("gemv", 1), ("gemv", 5), ("gemm", 40), ("f32", 3)])
+def test_wha_wide_blocked(path, M):
+    """K = 11008 = 2^8 x 43 with blocks of 256 (three x pieces per thread on the decode kernel)."""
+    lin = _layer(256, 11008, M, seed=90 + M)
+    qw, csr, F = _prep(lin, per_row=64, floor=8, seed=9)
+    _check(_run(lin, qw, F, 256, "f32", PATHS[path]), lin, _wdeq(lin), csr, 256)
+
+
+@pytest.mark.parametrize("K,M", [(8192, 1), (8192, 40), (16384, 1)])
+def test_wha_wide_full_transform(K, M):
+    """One full transform over K = 8192 (two LDS rounds for bits 9-12 on the decode kernel) and
+    K = 16384 (no room for the transform beside the decode kernel's tables: the separate kernel)."""
+    lin = _layer(192, K, M, seed=100 + M + K // 1024)
+    qw, csr, F = _prep(lin, per_row=48, floor=8, seed=10)
+    _check(_run(lin, qw, F, K, "f32"), lin, _wdeq(lin), csr, K)

@@ -116,3 +116,13 @@ def test_coefficient_generator_budget_floor_and_rows():
     for n in range(N):
         seg = col[row_ptr[n]:row_ptr[n + 1]]
         assert np.all(np.diff(seg) > 0) and seg.min() >= 0 and seg.max() < K
+
+
+def test_rows_transform_per_block_equals_the_block_diagonal_matrix():
+    """wht_rows forms each block separately; the full block-diagonal product gives the same values."""
+    rng = np.random.default_rng(11)
+    x = rng.standard_normal((3, 192)).astype(np.float32)
+    for P in (1, 8, 64):
+        z = wha.wht_rows(x, "f32", P)
+        ref = x.astype(np.float64) @ wha.transform_matrix(192, P) / P
+        assert np.allclose(z, ref, rtol=1e-14, atol=1e-15)
