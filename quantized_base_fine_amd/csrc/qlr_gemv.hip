@@ -280,11 +280,12 @@ __device__ __forceinline__ float dot_piece(const u32x4_t& pc, const u32x4_t* xv,
 // every workgroup also computes t = x A^T itself, from A rows read after the
 // code stream has been issued (L2-resident after the first workgroup of each
 // XCD), instead of reading the partial sums of a separate kernel.
-template <int BITS, int YDT, bool XLDS, bool ADP, int D, bool DOT, bool TF, int SPX>
+template <int BITS, int YDT, bool XLDS, bool ADP, int D, bool DOT, bool TF, int SPX, bool DBA>
 __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
   static_assert(!DOT || (XLDS && BITS != 3), "the single-row path reads x from LDS and 16-byte pieces of whole codes");
   static_assert(!TF || (DOT && ADP), "the fused adapter product belongs to the single-row path");
   static_assert(SPX == 0 || DOT, "the fused side channel belongs to the single-row path");
+  static_assert(!DBA || TF, "the double-binary branch is fused through the adapter product");
   // per-wave LDS staging buffer: codes and scales, or scales only (single-row path)
   constexpr uint32_t kStageW = DOT ? 16 * CH * 4 : ChunkGeo<BITS>::kStage;
   using G = ChunkGeo<BITS>;
@@ -368,7 +369,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
     // the tile's B rows (16 x r bf16, contiguous): piece wave * 64 + lane
     if constexpr (ADP) {
       const int pc = wave * 64 + lane;
-      const bool bv = (TF || P.bpre) && tv && c == nitem - 1 && pc < 2 * r;
+      const bool bv = !DBA && (TF || P.bpre) && tv && c == nitem - 1 && pc < 2 * r;
       const __amdgpu_buffer_rsrc_t brs = rsrc(a.B, N * r * 2);
       ch.bp = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
                                               brs, buf_off(bv, row0 * (uint32_t)(2 * r) + (uint32_t)pc * 16u), 0, 0));
@@ -549,10 +550,23 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
   // fused adapter product: lane's 8 elements k0 .. k0 + 7 of every A row j < 16
   // (rows past r and elements past the wave's range read as zero), issued after
   // the table and x are in LDS (issuing them holds the wave for a while)
-  u32x4_t afr[TF ? kFuseR : 1];
+  u32x4_t afr[TF && !DBA ? kFuseR : 1];
   const int64_t tk0 = kb0 * 64 + 8 * lane;
   const bool tkv = tk0 < kb1 * 64;
-  if constexpr (TF) {
+  // (DBA) the double-binary branch in place of A: gamma at the lane's 8 columns
+  // (fp16) and, per row j of B2, the 8 sign bits of those columns
+  u32x4_t dg = {0u, 0u, 0u, 0u};
+  uint32_t dbits[DBA ? kFuseR : 1];
+  if constexpr (DBA) {
+    const int64_t kc = tkv ? tk0 : 0;
+    dg = *reinterpret_cast<const u32x4_t*>(a.dba_gamma + kc);
+    const int64_t w2 = (K + 31) / 32;
+#pragma unroll
+    for (int j = 0; j < kFuseR; ++j) {
+      const uint32_t wd = a.dba_b2[(int64_t)(j < r ? j : 0) * w2 + (kc >> 5)];
+      dbits[j] = (wd >> (kc & 31)) & 0xFFu;
+    }
+  } else if constexpr (TF) {
     const __amdgpu_buffer_rsrc_t ars = rsrc(a.A, (int64_t)r * K * 2);
 #pragma unroll
     for (int j = 0; j < kFuseR; ++j)
@@ -730,12 +744,29 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
     if constexpr (TF) {
       const u32x4_t xv = lds_rd128(P.sX + (uint32_t)(tkv ? tk0 * 2 : 0));
       float v[kFuseR];
+      if constexpr (DBA) {
+        // t'_j over the lane's columns: sum of +-gamma_k x_k by the sign bits of B2 row j
+        // (gamma_k x_k is exact in float32: 11 by 8 significant bits)
+        float gx[8];
 #pragma unroll
-      for (int j = 0; j < kFuseR; ++j) {
-        float sj = 0.0f;
+        for (int e = 0; e < 8; ++e)
+          gx[e] = f16_bits_to_f32((dg[e >> 1] >> (16 * (e & 1))) & 0xFFFFu) *
+                  bf16_bits_to_f32((xv[e >> 1] >> (16 * (e & 1))) & 0xFFFFu);
 #pragma unroll
-        for (int q = 0; q < 4; ++q) sj = dot2(afr[j][q], xv[q], sj);
-        v[j] = tkv ? sj : 0.0f;
+        for (int j = 0; j < kFuseR; ++j) {
+          float sj = 0.0f;
+#pragma unroll
+          for (int e = 0; e < 8; ++e) sj += ((dbits[j] >> e) & 1u) ? gx[e] : -gx[e];
+          v[j] = tkv && j < r ? sj : 0.0f;
+        }
+      } else {
+#pragma unroll
+        for (int j = 0; j < kFuseR; ++j) {
+          float sj = 0.0f;
+#pragma unroll
+          for (int q = 0; q < 4; ++q) sj = dot2(afr[j][q], xv[q], sj);
+          v[j] = tkv ? sj : 0.0f;
+        }
       }
       // exchange distances 32 and 16: swaps of lane halves (lanes without the
       // distance bit keep value i, the others value i + n/2, each summed with
@@ -867,7 +898,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
 #pragma unroll
         for (int w = 0; w < kWaves; ++w)
           tj += *reinterpret_cast<const __attribute__((address_space(3))) float*>((uintptr_t)(P.sTP + 4u * (w * kFuseR + j)));
-        const float bj = j < r ? bf16_bits_to_f32(lds_rd16(P.sB + (uint32_t)((o * r + j) * 2))) : 0.0f;
+        float bj;
+        if constexpr (DBA) {
+          // alpha_n beta_j times the sign of B1[n][j] (R <= 16: one word per row)
+          const int64_t n = min(tl * 16 + o, N - 1);
+          const uint32_t w1 = a.dba_b1[n];
+          const float ab = f16_bits_to_f32(a.dba_alpha[n]) * f16_bits_to_f32(a.dba_beta[j < r ? j : 0]);
+          bj = j < r ? (((w1 >> j) & 1u) ? ab : -ab) : 0.0f;
+        } else {
+          bj = j < r ? bf16_bits_to_f32(lds_rd16(P.sB + (uint32_t)((o * r + j) * 2))) : 0.0f;
+        }
         const float lo = group_sum<16>(tj * bj);
         float s = 0.0f;
 #pragma unroll
@@ -924,7 +964,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
       if (cc == nitem - 1) {
         if constexpr (ADP) {
           const int pc = wave * 64 + lane;
-          if ((TF || P.bpre) && pc < 2 * r) lds_wr128(P.sB + (uint32_t)pc * 16u, ring[s].bp);
+          if (!DBA && (TF || P.bpre) && pc < 2 * r) lds_wr128(P.sB + (uint32_t)pc * 16u, ring[s].bp);
         }
         if constexpr (TF) {
           if (ctile == blockIdx.x) compute_t();
@@ -968,9 +1008,10 @@ int device_cus() {
   return cus;
 }
 
-template <int BITS, int YDT, bool XLDS, bool ADP, int D, bool DOT = false, bool TF = false, int SPX = 0>
+template <int BITS, int YDT, bool XLDS, bool ADP, int D, bool DOT = false, bool TF = false, int SPX = 0,
+          bool DBA = false>
 hipError_t launch_k(const Params& P, int64_t grid, size_t shmem, const Levels& lv, hipStream_t s) {
-  auto kern = k_gemv<BITS, YDT, XLDS, ADP, D, DOT, TF, SPX>;
+  auto kern = k_gemv<BITS, YDT, XLDS, ADP, D, DOT, TF, SPX, DBA>;
   static bool attr = false;
   if (!attr) {
     // the kernel addresses LDS from 0: it must not have static LDS
@@ -1021,8 +1062,9 @@ Plan plan_gemv(const LinearArgs& a) {
   auto r16 = [](size_t b) { return (b + 15) & ~(size_t)15; };
   for (int attempt = 0; attempt < 2; ++attempt) {
     const bool dot = attempt == 0 && BITS != 3 && a.M == 1 && (size_t)a.K * 2 <= kXLdsMax;
-    const bool tf = dot && r > 0 && r <= kFuseR && nb <= 8 * kWaves && !pl.deep && a.A != nullptr &&
-                    (reinterpret_cast<uintptr_t>(a.A) & 15) == 0;
+    const bool dbaf = a.dba_b2 != nullptr;  // the double-binary branch through the fused product
+    const bool tf = dot && r > 0 && r <= kFuseR && nb <= 8 * kWaves && !pl.deep &&
+                    (dbaf || (a.A != nullptr && (reinterpret_cast<uintptr_t>(a.A) & 15) == 0));
     const size_t stage = dot ? 16 * CH * 4 : ChunkGeo<BITS>::kStage;
     size_t lds = PairTable<BITS>::kBytes + (size_t)kWaves * 2 * stage + (size_t)kWaves * 256 * sizeof(float);
     // adapter product: fused, partials prefetched when they fit the registers, else summed by a loop
@@ -1060,7 +1102,7 @@ Plan plan_gemv(const LinearArgs& a) {
     const size_t xbytes = (size_t)a.M * (size_t)(a.K + 8) * 2 + 512;
     const bool xlds = (size_t)a.M * (size_t)a.K * 2 <= kXLdsMax && lds + 128 + xbytes <= kLdsMax;
     if (dot && !xlds) continue;  // the single-row path needs x in LDS
-    if (tf && (P.tmode != T_FUSED || !P.bpre)) continue;
+    if (tf && (P.tmode != T_FUSED || (!P.bpre && !dbaf))) continue;
     P.sZ = (uint32_t)lds;
     lds += 128;
     P.sX = (uint32_t)lds;
@@ -1087,6 +1129,12 @@ hipError_t launch_gemv_b(const LinearArgs& a, const Levels& lv, hipStream_t s) {
   const int64_t grid = pl.grid;
   const size_t lds = pl.lds;
   const bool adp = a.r > 0;
+  if (a.dba_b2) {
+    if constexpr (BITS != 3) {
+      if (pl.tf) return launch_k<BITS, YDT, true, true, 2, true, true, 0, true>(P, grid, lds, lv, s);
+    }
+    return hipErrorInvalidValue;
+  }
   if (a.sp_row_ptr) {
     // the side channel is summed in the kernel only on the single-row path with a short stream
     if constexpr (BITS != 3) {
@@ -1143,6 +1191,17 @@ bool gemv_fuses_adapter(const LinearArgs& a) {
     case 4: return plan_gemv<4>(a).tf;
     default: return plan_gemv<8>(a).tf;
   }
+}
+
+bool gemv_fuses_dba(const LinearArgs& a) {
+  if (a.M != 1 || a.bits == 3 || !a.dba_b2 || a.r <= 0 || a.r > kFuseR) return false;
+  Plan pl;
+  switch (a.bits) {
+    case 2: pl = plan_gemv<2>(a); break;
+    case 4: pl = plan_gemv<4>(a); break;
+    default: pl = plan_gemv<8>(a); break;
+  }
+  return pl.ok && pl.tf;
 }
 
 bool gemv_fuses_sparse(const LinearArgs& a) {

@@ -669,6 +669,23 @@ qlr_status qlr_linear_fwd_dba(const void* x, qlr_dtype xdt, int64_t M, const qlr
   if (M == 0) return QLR_OK;
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* wsp = reinterpret_cast<char*>(ws);
+  if (path == QLR_PATH_GEMV && ell == 1 && R <= 16) {
+    // a single x row on the decode kernel: both stages of the branch inside it (scale 1, rank R)
+    qlr::LinearArgs f = make_args(c, 1.0f, nullptr, 1);
+    f.r = R;
+    f.A = nullptr;
+    f.B = nullptr;
+    f.dba_b1 = ad->b1;
+    f.dba_b2 = ad->b2;
+    f.dba_alpha = ad->alpha;
+    f.dba_beta = ad->beta;
+    f.dba_gamma = ad->gamma;
+    if (qlr::gemv_fuses_dba(f)) {
+      const hipError_t e = qlr::launch_gemv(f, levels_arg(w->bits), s);
+      if (e != hipSuccess) return hip_fail(e, "linear launch");
+      return QLR_OK;
+    }
+  }
   const qlr::DbaArgs d{R, ell, ad->b1, ad->b2, ad->alpha, ad->beta, ad->gamma};
   float* t2 = reinterpret_cast<float*>(wsp + lay.t2);
   uint16_t* beff = reinterpret_cast<uint16_t*>(wsp + lay.beff);

@@ -75,6 +75,13 @@ struct LinearArgs {
   // >= 0: the side channel multiplies the Walsh-Hadamard transform of x over
   // blocks of 2^sp_wht_lp columns, scaled by 2^-sp_wht_lp, instead of x
   int sp_wht_lp = -1;
+  // optional double-binary branch (l = 1, r = its rank <= 16) summed inside the
+  // single-row decode kernel in place of A and B (see gemv_fuses_dba)
+  const uint32_t* dba_b1 = nullptr;
+  const uint32_t* dba_b2 = nullptr;
+  const uint16_t* dba_alpha = nullptr;
+  const uint16_t* dba_beta = nullptr;
+  const uint16_t* dba_gamma = nullptr;
 };
 
 // float32 path: any dtypes, any M.
@@ -88,6 +95,9 @@ bool gemv_fuses_adapter(const LinearArgs& a);
 // True when launch_gemv can add a CSR side channel (a.sp_*) itself for this
 // call: the single-row path with a short chunk stream.
 bool gemv_fuses_sparse(const LinearArgs& a);
+// True when launch_gemv can form the double-binary branch itself (a.dba_*, one
+// envelope term, a.r = its rank <= 16, a single x row).
+bool gemv_fuses_dba(const LinearArgs& a);
 // bf16 tiled GEMM path.
 hipError_t launch_gemm(const LinearArgs& a, const Levels& lv, hipStream_t s);
 // Up to gemm_group_max() independent linears of one code width, one M and one
