@@ -19,7 +19,8 @@ namespace qlr {
 
 namespace {
 
-constexpr int64_t kWhaLds = 128 * 1024;
+constexpr int64_t kWhaLds = 128 * 1024;     // the staged x records at most
+constexpr int64_t kWhaLdsAll = 160 * 1024;  // records, the row order and the class counters
 
 // LDS slot of column c's record: its low 3 bits XORed with bits 3..5, so the 8
 // consecutive records a thread stages, and its neighbours', spread over the banks
@@ -154,20 +155,49 @@ __global__ __launch_bounds__(TB) void k_wha_addend(const void* __restrict__ x, i
   const int g = tid % G;
   constexpr int kE = 8;                       // coefficients per lane per round
   constexpr int kRowsPass = (TB / G) * RB;
-  const int64_t nb = (int64_t)blockIdx.y * nchunk, ne = min(N, nb + nchunk);
-  // row offsets of a pass, clamped into range: a malformed CSR gives wrong sums, never a stray access
+  const int64_t nb = (int64_t)blockIdx.y * nchunk, ne = min(N, nb + nchunk), nrows = ne - nb;
+  if (nrows <= 0) return;  // uniform
+  // Rows are taken in order of their round count (a counting sort into perm,
+  // after the records), so that a pass's rows need about as many rounds each
+  // and no pass waits on one long row.  The order within a count class comes
+  // from LDS atomics; it decides only which rows share a pass, not any sum.
+  constexpr int kCls = 16;
+  __shared__ uint32_t cls_n[kCls], cls_at[kCls];
+  int32_t* perm = reinterpret_cast<int32_t*>(z + (size_t)MR * K);
+  auto row_len = [&](int64_t q) {
+    const int64_t a0 = min<int64_t>(max<int64_t>(row_ptr[nb + q], 0), nnz);
+    return max<int64_t>(a0, min<int64_t>(row_ptr[nb + q + 1], nnz)) - a0;
+  };
+  auto cls_of = [&](int64_t len) { return (int)min<int64_t>(kCls - 1, (len + kE * G - 1) / (kE * G)); };
+  if (tid < kCls) cls_n[tid] = 0;
+  __syncthreads();
+  for (int64_t q = tid; q < nrows; q += TB) atomicAdd(&cls_n[cls_of(row_len(q))], 1u);
+  __syncthreads();
+  if (tid == 0) {
+    uint32_t acc = 0;
+    for (int c = 0; c < kCls; ++c) {
+      cls_at[c] = acc;
+      acc += cls_n[c];
+    }
+  }
+  __syncthreads();
+  for (int64_t q = tid; q < nrows; q += TB) perm[atomicAdd(&cls_at[cls_of(row_len(q))], 1u)] = (int32_t)q;
+  __syncthreads();
+  // row offsets of a pass (position i of perm), clamped into range: a malformed
+  // CSR gives wrong sums, never a stray access
+  auto row_at = [&](int64_t i) { return nb + perm[i < nrows ? i : nrows - 1]; };
   auto offsets = [&](int64_t base, int64_t (&q0)[RB], int64_t (&q1)[RB]) {
 #pragma unroll
     for (int u = 0; u < RB; ++u) {
-      const int64_t n = base + tid / G + (TB / G) * u;
-      const int64_t nc = n < ne ? n : ne - 1;
-      q0[u] = n < ne ? min<int64_t>(max<int64_t>(row_ptr[nc], 0), nnz) : 0;
-      q1[u] = n < ne ? max<int64_t>(q0[u], min<int64_t>(row_ptr[nc + 1], nnz)) : 0;
+      const int64_t i = base + tid / G + (TB / G) * u;
+      const int64_t nc = row_at(i);
+      q0[u] = i < nrows ? min<int64_t>(max<int64_t>(row_ptr[nc], 0), nnz) : 0;
+      q1[u] = i < nrows ? max<int64_t>(q0[u], min<int64_t>(row_ptr[nc + 1], nnz)) : 0;
     }
   };
   int64_t p0[RB], p1[RB];
-  offsets(nb, p0, p1);
-  for (int64_t base = nb; base < ne; base += kRowsPass) {
+  offsets(0, p0, p1);
+  for (int64_t base = 0; base < nrows; base += kRowsPass) {
     int64_t n0[RB], n1[RB];
     offsets(base + kRowsPass, n0, n1);  // the next pass's (past ne: empty)
     float acc[RB][MR];
@@ -211,8 +241,9 @@ __global__ __launch_bounds__(TB) void k_wha_addend(const void* __restrict__ x, i
         for (int mm = 0; mm < MR; ++mm) acc[u][mm] += __shfl_xor(acc[u][mm], o, 64);
 #pragma unroll
     for (int u = 0; u < RB; ++u) {
-      const int64_t n = base + tid / G + (TB / G) * u;
-      if (g == 0 && n < ne) {
+      const int64_t i = base + tid / G + (TB / G) * u;
+      if (g == 0 && i < nrows) {
+        const int64_t n = row_at(i);
 #pragma unroll
         for (int mm = 0; mm < MR; ++mm)
           if (m0 + mm < M) C[(m0 + mm) * N + n] = acc[u][mm] * inv_p;
@@ -231,15 +262,18 @@ hipError_t wha_t(const void* x, int64_t M, int64_t K, int64_t N, int lp, const i
                  const float* val, int64_t nnz, float* C, hipStream_t s) {
   const int64_t xblocks = (M + MR - 1) / MR;
   constexpr int64_t kRowsPass = (TB / G) * RB;
-  // enough workgroups to fill the chip (each stages and transforms its x rows once)
-  const int64_t nch = std::max<int64_t>(1, std::min<int64_t>((N + kRowsPass - 1) / kRowsPass,
-                                                             (256 + xblocks - 1) / xblocks));
+  // enough workgroups to fill the chip (each stages and transforms its x rows
+  // once), and row ranges short enough for their order (int32 each) beside the records
+  const int64_t rec = (int64_t)MR * K * 4;
+  const int64_t max_rows = (kWhaLdsAll - 256 - rec) / 4;
+  int64_t nch = std::max<int64_t>(1, std::min<int64_t>((N + kRowsPass - 1) / kRowsPass, (256 + xblocks - 1) / xblocks));
+  nch = std::max<int64_t>(nch, (N + max_rows - 1) / max_rows);
   const int64_t nchunk = (N + nch - 1) / nch;
-  const size_t shmem = (size_t)MR * K * 4;
+  const size_t shmem = (size_t)rec + (size_t)nchunk * 4;
   static bool attr = false;
   if (!attr) {
     const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_wha_addend<XDT, MR, G, RB, TB>),
-                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kWhaLds);
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)(kWhaLdsAll - 256));
     if (e != hipSuccess) return e;
     attr = true;
   }
