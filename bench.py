@@ -270,6 +270,51 @@ def build_mixed(torch, qlr, workloads, dev):
     return qlr.MixedCall(entries, out_dtype=torch.bfloat16), flops, len(entries)
 
 
+def single_call_latency(torch, layer, stream, reps: int = 25):
+    """One call at a time (synchronized before and after, HIP events around it): the
+    latency a lone call sees, median and min over reps, us."""
+    res = {}
+    for ph in ("decode", "decode_base", "prefill", "prefill_base"):
+        call = layer[ph]
+        for _ in range(3):
+            call()
+        torch.cuda.synchronize()
+        ts = []
+        for _ in range(reps):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            call()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            ts.append(1e3 * e0.elapsed_time(e1))
+        ts.sort()
+        res[ph] = {"median_us": round(ts[len(ts) // 2], 3), "min_us": round(ts[0], 3)}
+    return res
+
+
+def device_copy(torch, dev, stream, decode_gbs, reps: int = 10):
+    """A 1 GiB device-to-device copy (read + write counted), the bandwidth a plain
+    streaming kernel reaches here; the decode figure is set against it."""
+    n = 1 << 30
+    src = torch.empty(n, dtype=torch.uint8, device=dev)
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        dst.copy_(src)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) / 1e3)
+    ts.sort()
+    gbs = 2 * n / ts[len(ts) // 2] / 1e9
+    del src, dst
+    return {"bytes": 2 * n, "gbs": round(gbs, 1), "decode_vs_copy": round(decode_gbs / gbs, 4)}
+
+
 def cpu_baseline(budget_s: float = 12.0):
     """The oracle (numpy float64) on the host cores, on a bounded sample."""
     import numpy as np
@@ -639,6 +684,8 @@ def main():
             "roofline": {"bound": "mfma", "achieved": round(mixed_tfs, 1), "peak": BF16_PEAK_TFLOPS,
                          "unit": "TFLOP/s", "frac": round(mixed_tfs / BF16_PEAK_TFLOPS, 4)},
         }
+    out["single_call"] = single_call_latency(torch, layers[0], stream)
+    out["device_copy"] = device_copy(torch, dev, stream, out["value"])
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline()
     print(json.dumps(out))
