@@ -144,7 +144,7 @@ def traffic_from_profile(kernel_key: str):
 # built from (the stored figure is dropped when any of them changes).
 _CSRC = "quantized_base_fine_amd/csrc/"
 TRAFFIC_KERNELS = {
-    "decode": ("k_gemv<4, 2, true, false, 2, true, false, 0>",
+    "decode": ("k_gemv<4, 2, true, false, 2, true, false, 0, false>",
                [_CSRC + f for f in ("qlr_gemv.hip", "qlr_lut.h", "qlr_device.h", "qlr_internal.h")]),
     "prefill": ("k_gemm<4, 2, false, false>",
                 [_CSRC + f for f in ("qlr_gemm.hip", "qlr_lut.h", "qlr_device.h", "qlr_internal.h")]),
