@@ -8,9 +8,9 @@
 // every output before rounding.  A workgroup stages MR rows of x in LDS as
 // float32 column records (MR values of one column together), transforms them
 // in place within blocks of P columns, and then walks the coefficients of a
-// range of F's rows: G lanes per row, each taking every G-th coefficient in
-// rounds of 8 (all loads of a round in flight together), summed over the G
-// lanes in a fixed butterfly order.
+// range of F's rows: G lanes per row, each taking 8 of every 8 G coefficients
+// per round (all loads of a round in flight together), summed over the G lanes
+// in a fixed butterfly order.
 #include <algorithm>
 
 #include "qlr_internal.h"
@@ -69,11 +69,14 @@ __device__ __forceinline__ void rec_store(float* z, int64_t c, const Rec<MR>& r)
 }
 
 // blockIdx.x: x rows [MR bx, MR bx + MR); blockIdx.y: F rows [nchunk by, ...).
-// TB threads; G lanes per F row, lane g taking the row's coefficients
-// g + G u (u < 8) of each round, so a round covers 8 G consecutive ones; each
-// lane walks RB rows per pass, and the next pass's row offsets are loaded
-// while the current pass's coefficients are in flight.
-template <int XDT, int MR, int G, int RB, int TB>
+// TB threads; G lanes per F row, and a round covers 8 G consecutive
+// coefficients of the row.  VL: lane g takes 4 g + {0..3} and 4 (g + G) +
+// {0..3}, two 16-byte loads each of col and val, so the G lanes of a row read
+// 16 G contiguous bytes per load (needs 4 <= nnz < 2^29); otherwise lane g
+// takes g + G u (u < 8), one 4-byte load each.  Each lane walks RB rows per
+// pass, and the next pass's row offsets are loaded while the current pass's
+// coefficients are in flight.
+template <int XDT, int MR, int G, int RB, int TB, bool VL>
 __global__ __launch_bounds__(TB) void k_wha_addend(const void* __restrict__ x, int64_t M, int64_t K, int64_t N,
                                                     int lp, const int32_t* __restrict__ row_ptr,
                                                     const int32_t* __restrict__ col, const float* __restrict__ val,
@@ -191,15 +194,71 @@ __global__ __launch_bounds__(TB) void k_wha_addend(const void* __restrict__ x, i
     for (int u = 0; u < RB; ++u) {
       const int64_t i = base + tid / G + (TB / G) * u;
       const int64_t nc = row_at(i);
-      q0[u] = i < nrows ? min<int64_t>(max<int64_t>(row_ptr[nc], 0), nnz) : 0;
-      q1[u] = i < nrows ? max<int64_t>(q0[u], min<int64_t>(row_ptr[nc + 1], nnz)) : 0;
+      // both loads unconditional (nc is in range) and their values used
+      // unconditionally: a load behind a branch would make the compiler wait
+      // for every load in flight.  Past the range the pass gets [lo, lo).
+      const int64_t a0 = row_ptr[nc], a1 = row_ptr[nc + 1];
+      const int64_t lo = a0 < 0 ? 0 : (a0 > nnz ? nnz : a0);
+      const int64_t hi = a1 < lo ? lo : (a1 > nnz ? nnz : a1);
+      q0[u] = lo;
+      q1[u] = i < nrows ? hi : lo;
     }
   };
-  int64_t p0[RB], p1[RB];
+  // VL: col and val as buffer resources (loads past the end read zero)
+  const int nbytes = VL ? (int)(nnz * 4) : 0;
+  const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(col), (short)0, nbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(val), (short)0, nbytes, 0x00020000);
+  // One round of a lane: its kE coefficients of each of its RB rows from offset
+  // e0 of rows [q, qe), and which of them exist (bit u kE + e).
+  struct Round {
+    int32_t cc[RB][kE];
+    float vv[RB][kE];
+    uint32_t ok;
+  };
+  auto first = [&](int64_t q, int64_t e0) { return VL ? q + e0 + 4 * g : q + e0 + g; };
+  auto load_round = [&](const int64_t (&q)[RB], const int64_t (&qe)[RB], int64_t e0, Round& R) {
+    R.ok = 0;
+#pragma unroll
+    for (int u = 0; u < RB; ++u) {
+      if constexpr (VL) {
+        // a load that would run past nnz starts at nnz - 4 instead; its element
+        // t then sits at js + t, and those before j belong to another lane
+#pragma unroll
+        for (int hh = 0; hh < kE / 4; ++hh) {
+          const int64_t j = q[u] + e0 + 4 * (g + G * hh);
+          const int64_t js = j < nnz - 4 ? j : nnz - 4;
+          const u32x4_t lc = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(crs, (int)(js * 4), 0, 0));
+          const u32x4_t lv = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(vrs, (int)(js * 4), 0, 0));
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            R.cc[u][4 * hh + t] = min<int32_t>(max<int32_t>((int32_t)lc[t], 0), (int32_t)(K - 1));
+            R.vv[u][4 * hh + t] = __uint_as_float(lv[t]);
+            R.ok |= (js + t >= j && js + t < qe[u]) ? 1u << (u * kE + 4 * hh + t) : 0u;
+          }
+        }
+      } else {
+#pragma unroll
+        for (int e = 0; e < kE; ++e) {
+          const int64_t j = q[u] + e0 + g + (int64_t)G * e;
+          const int64_t jc = j < nnz ? j : nnz - 1;
+          R.cc[u][e] = min<int32_t>(max<int32_t>(col[jc], 0), (int32_t)(K - 1));
+          R.vv[u][e] = val[jc];
+          R.ok |= j < qe[u] ? 1u << (u * kE + e) : 0u;
+        }
+      }
+    }
+  };
+  // Offsets run two passes ahead and coefficients one round ahead: while a
+  // round is summed, the lane's next round of the pass is in flight, or after
+  // its last round the first round of the next pass.
+  int64_t p0[RB], p1[RB], n0[RB], n1[RB];
   offsets(0, p0, p1);
+  offsets(kRowsPass, n0, n1);
+  Round cur;
+  load_round(p0, p1, 0, cur);
   for (int64_t base = 0; base < nrows; base += kRowsPass) {
-    int64_t n0[RB], n1[RB];
-    offsets(base + kRowsPass, n0, n1);  // the next pass's (past ne: empty)
+    int64_t f0[RB], f1[RB];
+    offsets(base + 2 * kRowsPass, f0, f1);  // past ne: empty
     float acc[RB][MR];
 #pragma unroll
     for (int u = 0; u < RB; ++u)
@@ -208,29 +267,27 @@ __global__ __launch_bounds__(TB) void k_wha_addend(const void* __restrict__ x, i
     for (int64_t e0 = 0;; e0 += kE * G) {
       bool more = false;
 #pragma unroll
-      for (int u = 0; u < RB; ++u) more |= p0[u] + e0 + g < p1[u];
-      if (!more) break;
-      int32_t cc[RB][kE];
-      float vv[RB][kE];
+      for (int u = 0; u < RB; ++u) more |= first(p0[u], e0 + kE * G) < p1[u];
+      int64_t lq[RB], lqe[RB];
+#pragma unroll
+      for (int u = 0; u < RB; ++u) {
+        lq[u] = more ? p0[u] : n0[u];
+        lqe[u] = more ? p1[u] : n1[u];
+      }
+      Round nxt;
+      load_round(lq, lqe, more ? e0 + kE * G : 0, nxt);
 #pragma unroll
       for (int u = 0; u < RB; ++u)
 #pragma unroll
         for (int e = 0; e < kE; ++e) {
-          const int64_t j = p0[u] + e0 + g + (int64_t)G * e;
-          const int64_t jc = j < nnz ? j : nnz - 1;
-          cc[u][e] = min<int32_t>(max<int32_t>(col[jc], 0), (int32_t)(K - 1));
-          vv[u][e] = val[jc];
-        }
+          if (cur.ok >> (u * kE + e) & 1u) {
+            const Rec<MR> r = rec_load<MR>(z, cur.cc[u][e]);
 #pragma unroll
-      for (int u = 0; u < RB; ++u)
-#pragma unroll
-        for (int e = 0; e < kE; ++e) {
-          if (p0[u] + e0 + g + (int64_t)G * e < p1[u]) {
-            const Rec<MR> r = rec_load<MR>(z, cc[u][e]);
-#pragma unroll
-            for (int mm = 0; mm < MR; ++mm) acc[u][mm] = fmaf(vv[u][e], r.v[mm], acc[u][mm]);
+            for (int mm = 0; mm < MR; ++mm) acc[u][mm] = fmaf(cur.vv[u][e], r.v[mm], acc[u][mm]);
           }
         }
+      cur = nxt;
+      if (!more) break;
     }
     // sum over the row's G lanes (adjacent lanes of one wave), fixed order
 #pragma unroll
@@ -253,11 +310,13 @@ __global__ __launch_bounds__(TB) void k_wha_addend(const void* __restrict__ x, i
     for (int u = 0; u < RB; ++u) {
       p0[u] = n0[u];
       p1[u] = n1[u];
+      n0[u] = f0[u];
+      n1[u] = f1[u];
     }
   }
 }
 
-template <int XDT, int MR, int G, int RB, int TB>
+template <int XDT, int MR, int G, int RB, int TB, bool VL>
 hipError_t wha_t(const void* x, int64_t M, int64_t K, int64_t N, int lp, const int32_t* row_ptr, const int32_t* col,
                  const float* val, int64_t nnz, float* C, hipStream_t s) {
   const int64_t xblocks = (M + MR - 1) / MR;
@@ -272,23 +331,23 @@ hipError_t wha_t(const void* x, int64_t M, int64_t K, int64_t N, int lp, const i
   const size_t shmem = (size_t)rec + (size_t)nchunk * 4;
   static bool attr = false;
   if (!attr) {
-    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_wha_addend<XDT, MR, G, RB, TB>),
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_wha_addend<XDT, MR, G, RB, TB, VL>),
                                              hipFuncAttributeMaxDynamicSharedMemorySize, (int)(kWhaLdsAll - 256));
     if (e != hipSuccess) return e;
     attr = true;
   }
-  hipLaunchKernelGGL((k_wha_addend<XDT, MR, G, RB, TB>), dim3((unsigned)xblocks, (unsigned)nch), dim3(TB), shmem, s, x,
+  hipLaunchKernelGGL((k_wha_addend<XDT, MR, G, RB, TB, VL>), dim3((unsigned)xblocks, (unsigned)nch), dim3(TB), shmem, s, x,
                      M, K, N, lp, row_ptr, col, val, nnz, C, nchunk);
   return hipGetLastError();
 }
 
-template <int XDT>
+template <int XDT, bool VL>
 hipError_t wha_x(const void* x, int64_t M, int64_t K, int64_t N, int lp, const int32_t* row_ptr, const int32_t* col,
                  const float* val, int64_t nnz, float* C, hipStream_t s) {
-  if (M >= 8 && 8 * K * 4 <= kWhaLds) return wha_t<XDT, 8, 4, 1, 1024>(x, M, K, N, lp, row_ptr, col, val, nnz, C, s);
-  if (M >= 4 && 4 * K * 4 <= kWhaLds) return wha_t<XDT, 4, 4, 1, 1024>(x, M, K, N, lp, row_ptr, col, val, nnz, C, s);
-  if (M >= 2 && 2 * K * 4 <= kWhaLds) return wha_t<XDT, 2, 4, 1, 1024>(x, M, K, N, lp, row_ptr, col, val, nnz, C, s);
-  return wha_t<XDT, 1, 4, 1, 1024>(x, M, K, N, lp, row_ptr, col, val, nnz, C, s);
+  if (M >= 8 && 8 * K * 4 <= kWhaLds) return wha_t<XDT, 8, 4, 1, 1024, VL>(x, M, K, N, lp, row_ptr, col, val, nnz, C, s);
+  if (M >= 4 && 4 * K * 4 <= kWhaLds) return wha_t<XDT, 4, 4, 1, 1024, VL>(x, M, K, N, lp, row_ptr, col, val, nnz, C, s);
+  if (M >= 2 && 2 * K * 4 <= kWhaLds) return wha_t<XDT, 2, 4, 1, 1024, VL>(x, M, K, N, lp, row_ptr, col, val, nnz, C, s);
+  return wha_t<XDT, 1, 4, 1, 1024, VL>(x, M, K, N, lp, row_ptr, col, val, nnz, C, s);
 }
 
 }  // namespace
@@ -299,8 +358,13 @@ hipError_t launch_wha_addend(const void* x, int xdt, int64_t M, int64_t K, int64
                              const int32_t* col, const float* val, int64_t nnz, float* C, hipStream_t s) {
   if (M == 0 || N == 0) return hipSuccess;
   if (K > wha_max_cols() || K % 8 != 0) return hipErrorInvalidValue;
-  if (xdt == DT_F32) return wha_x<DT_F32>(x, M, K, N, lp, row_ptr, col, val, nnz, C, s);
-  return wha_x<DT_BF16>(x, M, K, N, lp, row_ptr, col, val, nnz, C, s);
+  // 16-byte coefficient loads address col and val with 32-bit byte offsets
+  const bool vl = nnz >= 4 && nnz < (int64_t(1) << 29);
+  if (xdt == DT_F32)
+    return vl ? wha_x<DT_F32, true>(x, M, K, N, lp, row_ptr, col, val, nnz, C, s)
+              : wha_x<DT_F32, false>(x, M, K, N, lp, row_ptr, col, val, nnz, C, s);
+  return vl ? wha_x<DT_BF16, true>(x, M, K, N, lp, row_ptr, col, val, nnz, C, s)
+            : wha_x<DT_BF16, false>(x, M, K, N, lp, row_ptr, col, val, nnz, C, s);
 }
 
 }  // namespace qlr

@@ -161,3 +161,21 @@ def test_wha_wide_full_transform(K, M):
     lin = _layer(192, K, M, seed=100 + M + K // 1024)
     qw, csr, F = _prep(lin, per_row=48, floor=8, seed=10)
     _check(_run(lin, qw, F, K, "f32"), lin, _wdeq(lin), csr, K)
+
+
+@pytest.mark.parametrize("nnz", [1, 3, 4, 5, 37])
+def test_wha_few_coefficients(nnz):
+    """A handful of coefficients in the last rows: fewer than 4 (one 4-byte load each), exactly 4 and just
+    above (16-byte loads clamped to the array's end, elements before the lane's own skipped)."""
+    lin = _layer(96, 256, 24, seed=70 + nnz)
+    qw = qlr.quantize(dev(lin.W, lin.wdtype), lin.bits)
+    rng = np.random.default_rng(700 + nnz)
+    rows = np.sort(rng.choice(np.arange(90, 96), size=nnz))
+    row_ptr = np.searchsorted(rows, np.arange(97)).astype(np.int32)
+    col = rng.integers(0, 256, nnz).astype(np.int32)
+    val = rng.standard_normal(nnz).astype(np.float32)
+    csr = (row_ptr, col, val)
+    F = qlr.sparse_from_csr(96, 256, *csr, "cuda")
+    wd = _wdeq(lin)
+    for path in ("gemm", "f32"):
+        _check(_run(lin, qw, F, 64, "f32", PATHS[path]), lin, wd, csr, 64)
