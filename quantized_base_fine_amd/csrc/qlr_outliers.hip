@@ -415,43 +415,88 @@ __global__ __launch_bounds__(TB) void k_sparse_addend(const void* __restrict__ x
     }
   };
   const int64_t nb = (int64_t)blockIdx.y * nchunk, ne = min(N, nb + nchunk);
-  // one weight row per thread and pass; its outliers in rounds of 8 (every load
-  // of a round in flight together); the next pass's offsets are loaded while the
-  // current pass's outliers are in flight.  Offsets and columns are clamped into
-  // range: a malformed CSR gives wrong sums, never a stray access.
+  // One weight row per thread and pass, its outliers in rounds of 8.  Offsets
+  // run two passes ahead and outliers one round ahead: while a round is summed,
+  // the thread's next round, or after its last round the first round of its
+  // next pass, is in flight.  Offsets and columns are clamped into range: a
+  // malformed CSR gives wrong sums, never a stray access.
   constexpr int kE = 8;
   auto offsets = [&](int64_t base, int64_t& q0, int64_t& q1) {
     const int64_t n = base + tid;
     const int64_t nc = n < ne ? n : ne - 1;
-    q0 = n < ne ? min<int64_t>(max<int64_t>(row_ptr[nc], 0), nnz) : 0;
-    q1 = n < ne ? max<int64_t>(q0, min<int64_t>(row_ptr[nc + 1], nnz)) : 0;
+    // both loads unconditional and their values used unconditionally (a load
+    // behind a branch would make the compiler wait for every load in flight);
+    // past the range the pass gets [lo, lo)
+    const int64_t a0 = row_ptr[nc], a1 = row_ptr[nc + 1];
+    const int64_t lo = a0 < 0 ? 0 : (a0 > nnz ? nnz : a0);
+    const int64_t hi = a1 < lo ? lo : (a1 > nnz ? nnz : a1);
+    q0 = lo;
+    q1 = n < ne ? hi : lo;
   };
-  int64_t p0, p1;
+  // VL (4 <= nnz < 2^29): two 16-byte loads each of col and val per round; a
+  // load that would run past nnz starts at nnz - 4, its element t then at js + t
+  const bool vl = nnz >= 4 && nnz < (int64_t(1) << 29);
+  const int nbytes = vl ? (int)(nnz * 4) : 0;
+  const __amdgpu_buffer_rsrc_t crs = __builtin_amdgcn_make_buffer_rsrc(const_cast<int32_t*>(col), (short)0, nbytes, 0x00020000);
+  const __amdgpu_buffer_rsrc_t vrs = __builtin_amdgcn_make_buffer_rsrc(const_cast<float*>(val), (short)0, nbytes, 0x00020000);
+  struct Round {
+    int32_t cc[kE];
+    float vv[kE];
+    uint32_t ok;  // bit e: coefficient e exists
+  };
+  auto load_round = [&](int64_t q, int64_t qe, int64_t e0, Round& R) {
+    R.ok = 0;
+    if (vl) {  // uniform
+#pragma unroll
+      for (int hh = 0; hh < kE / 4; ++hh) {
+        const int64_t j = q + e0 + 4 * hh;
+        const int64_t js = j < nnz - 4 ? j : nnz - 4;
+        const u32x4_t lc = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(crs, (int)(js * 4), 0, 0));
+        const u32x4_t lv = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(vrs, (int)(js * 4), 0, 0));
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          R.cc[4 * hh + t] = min<int32_t>(max<int32_t>((int32_t)lc[t], 0), (int32_t)(K - 1));
+          R.vv[4 * hh + t] = __uint_as_float(lv[t]);
+          R.ok |= (js + t >= j && js + t < qe) ? 1u << (4 * hh + t) : 0u;
+        }
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < kE; ++e) {
+        const int64_t j = q + e0 + e;
+        const int64_t jc = j < nnz ? j : (nnz > 0 ? nnz - 1 : 0);
+        R.cc[e] = nnz > 0 ? min<int32_t>(max<int32_t>(col[jc], 0), (int32_t)(K - 1)) : 0;
+        R.vv[e] = nnz > 0 ? val[jc] : 0.0f;
+        R.ok |= j < qe ? 1u << e : 0u;
+      }
+    }
+  };
+  int64_t p0, p1, n0, n1;
   offsets(nb, p0, p1);
+  offsets(nb + TB, n0, n1);
+  Round cur;
+  load_round(p0, p1, 0, cur);
   for (int64_t base = nb; base < ne; base += TB) {
-    int64_t n0, n1;
-    offsets(base + TB, n0, n1);
+    int64_t f0, f1;
+    offsets(base + 2 * TB, f0, f1);
     float acc[R];
 #pragma unroll
     for (int mm = 0; mm < R; ++mm) acc[mm] = 0.0f;
-    for (int64_t e0 = p0; e0 < p1; e0 += kE) {
-      int32_t cc[kE];
-      float vv[kE];
+    for (int64_t e0 = 0;; e0 += kE) {
+      const bool more = p0 + e0 + kE < p1;
+      Round nxt;
+      load_round(more ? p0 : n0, more ? p1 : n1, more ? e0 + kE : 0, nxt);
 #pragma unroll
       for (int e = 0; e < kE; ++e) {
-        const int64_t jc = e0 + e < nnz ? e0 + e : nnz - 1;
-        cc[e] = min<int32_t>(max<int32_t>(col[jc], 0), (int32_t)(K - 1));
-        vv[e] = val[jc];
-      }
-#pragma unroll
-      for (int e = 0; e < kE; ++e) {
-        if (e0 + e < p1) {
+        if (cur.ok >> e & 1u) {
           float xv[R];
-          xcol(cc[e], xv);
+          xcol(cur.cc[e], xv);
 #pragma unroll
-          for (int mm = 0; mm < R; ++mm) acc[mm] = fmaf(vv[e], xv[mm], acc[mm]);
+          for (int mm = 0; mm < R; ++mm) acc[mm] = fmaf(cur.vv[e], xv[mm], acc[mm]);
         }
       }
+      cur = nxt;
+      if (!more) break;
     }
     const int64_t n = base + tid;
     if (n < ne) {
@@ -461,6 +506,8 @@ __global__ __launch_bounds__(TB) void k_sparse_addend(const void* __restrict__ x
     }
     p0 = n0;
     p1 = n1;
+    n0 = f0;
+    n1 = f1;
   }
 }
 

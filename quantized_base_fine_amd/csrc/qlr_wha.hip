@@ -240,9 +240,9 @@ __global__ __launch_bounds__(TB) void k_wha_addend(const void* __restrict__ x, i
 #pragma unroll
         for (int e = 0; e < kE; ++e) {
           const int64_t j = q[u] + e0 + g + (int64_t)G * e;
-          const int64_t jc = j < nnz ? j : nnz - 1;
-          R.cc[u][e] = min<int32_t>(max<int32_t>(col[jc], 0), (int32_t)(K - 1));
-          R.vv[u][e] = val[jc];
+          const int64_t jc = j < nnz ? j : (nnz > 0 ? nnz - 1 : 0);
+          R.cc[u][e] = nnz > 0 ? min<int32_t>(max<int32_t>(col[jc], 0), (int32_t)(K - 1)) : 0;
+          R.vv[u][e] = nnz > 0 ? val[jc] : 0.0f;
           R.ok |= j < qe[u] ? 1u << (u * kE + e) : 0u;
         }
       }
