@@ -23,6 +23,47 @@ __global__ void k_fill_u32(uint32_t* p, uint32_t v, int64_t n) {
   if (i < n) p[i] = v;
 }
 
+// 8 consecutive elements from e0 (all in range): the raw 16 or 32 bytes, then
+// their widening to float32 (apart, so that every load can be issued first)
+template <int DT>
+struct Raw8 {
+  uint4 u[DT == DT_F32 ? 2 : 1];
+};
+
+template <int DT>
+__device__ __forceinline__ Raw8<DT> load8_raw(const void* W, int64_t e0) {
+  Raw8<DT> r;
+  if constexpr (DT == DT_F32) {
+    const uint4* p = reinterpret_cast<const uint4*>(reinterpret_cast<const float*>(W) + e0);
+    r.u[0] = p[0];
+    r.u[1] = p[1];
+  } else {
+    r.u[0] = *reinterpret_cast<const uint4*>(reinterpret_cast<const uint16_t*>(W) + e0);
+  }
+  return r;
+}
+
+template <int DT>
+__device__ __forceinline__ void widen8(const Raw8<DT>& r, float (&w)[8]) {
+  if constexpr (DT == DT_F32) {
+    const uint32_t d[8] = {r.u[0].x, r.u[0].y, r.u[0].z, r.u[0].w, r.u[1].x, r.u[1].y, r.u[1].z, r.u[1].w};
+#pragma unroll
+    for (int i = 0; i < 8; ++i) w[i] = __uint_as_float(d[i]);
+  } else {
+    const uint32_t d[4] = {r.u[0].x, r.u[0].y, r.u[0].z, r.u[0].w};
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      if constexpr (DT == DT_F16) {
+        w[2 * i] = f16_bits_to_f32((uint16_t)(d[i] & 0xFFFFu));
+        w[2 * i + 1] = f16_bits_to_f32((uint16_t)(d[i] >> 16));
+      } else {
+        w[2 * i] = bf16_bits_to_f32(d[i] & 0xFFFFu);
+        w[2 * i + 1] = bf16_bits_to_f32(d[i] >> 16);
+      }
+    }
+  }
+}
+
 template <int DT>
 __device__ __forceinline__ void load8(const void* W, int64_t e0, int64_t numel, float (&w)[8],
                                       int& present) {
@@ -93,19 +134,9 @@ __global__ __launch_bounds__(kThreads) void k_quantize(const void* __restrict__ 
 
   bool bad = false;
   const int q = tid & 7;  // lane within the block
-#pragma unroll 1
-  for (int pass = 0; pass < 256 / kBlocksPerPass; ++pass) {
-    const int jj = pass * kBlocksPerPass + (tid >> 3);
+  // block jj's absmax and codes from the lane's 8 elements w (present of them real)
+  auto encode = [&](int jj, const float (&w)[8], int present) {
     const int64_t j = blk0 + jj;
-    const int64_t e0 = j * 64 + q * 8;
-    float w[8];
-    int present = 0;
-    if (jj < nblk_here) {
-      load8<DT>(W, e0, numel, w, present);
-    } else {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) w[i] = 0.0f;
-    }
     float m = 0.0f;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
@@ -130,6 +161,34 @@ __global__ __launch_bounds__(kThreads) void k_quantize(const void* __restrict__ 
       packed |= (uint64_t)c << (BITS * i);
     }
     if (jj < nblk_here) store_codes<BITS>(codes + j * (8 * BITS) + q * BITS, packed);
+  };
+  if (blk0 * 64 + 256 * 64 <= numel) {
+    // a whole group (uniform): the loads of all passes in flight together
+    Raw8<DT> raw[256 / kBlocksPerPass];
+#pragma unroll
+    for (int pass = 0; pass < 256 / kBlocksPerPass; ++pass)
+      raw[pass] = load8_raw<DT>(W, (blk0 + pass * kBlocksPerPass + (tid >> 3)) * 64 + q * 8);
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int pass = 0; pass < 256 / kBlocksPerPass; ++pass) {
+      float w[8];
+      widen8<DT>(raw[pass], w);
+      encode(pass * kBlocksPerPass + (tid >> 3), w, 8);
+    }
+  } else {
+#pragma unroll 1
+    for (int pass = 0; pass < 256 / kBlocksPerPass; ++pass) {
+      const int jj = pass * kBlocksPerPass + (tid >> 3);
+      float w[8];
+      int present = 0;
+      if (jj < nblk_here) {
+        load8<DT>(W, (blk0 + jj) * 64 + q * 8, numel, w, present);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) w[i] = 0.0f;
+      }
+      encode(jj, w, present);
+    }
   }
   __syncthreads();
 
