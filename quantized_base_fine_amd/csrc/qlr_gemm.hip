@@ -326,14 +326,19 @@ __global__ __launch_bounds__(512, 1) void k_gemm(GemmParams P, Levels lv) {
     const uint16_t* xs_base = reinterpret_cast<const uint16_t*>(a.x) + P.m_begin * KC;
     const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
         const_cast<uint16_t*>(xs_base), (short)0, (int)((P.m_end - P.m_begin) * KC * 2), 0x00020000);
-    // staging load j (0..7): tile row 64 pw + 8 j + t (t = lane / 8), 16-byte chunk lane % 8
+    // load j (0..7) of wave pw: tile rows 64 pw + 8 j + t (t = lane / 8)
     const uint32_t t8 = (uint32_t)(lane >> 3);
-    const uint32_t xg0 = (uint32_t)(((m0 - P.m_begin) + 64 * pw + t8) * KC + 8 * (lane & 7)) * 2u;
     const uint32_t xg_row8 = (uint32_t)(8 * KC * 2);
-    uint32_t xst[2];  // LDS slot of row 64 pw + 8 j + t: swizzle depends on j only through j & 1
+    // x goes to LDS by direct loads: load j of a wave fills rows 64 pw + 8 j ..
+    // + 7 (1 KB, lane L at byte 16 L: row 64 pw + 8 j + L / 8, slot L % 8), so
+    // lane L reads the global chunk that the swizzle puts at its slot; the
+    // swizzle depends on j only through j & 1
+    uint32_t xgd[2];
 #pragma unroll
     for (int p = 0; p < 2; ++p)
-      xst[p] = kXOff + (uint32_t)((64 * pw + t8) * 128) + ((((uint32_t)lane & 7u) ^ swz(t8 + 8u * p)) << 4);
+      xgd[p] = (uint32_t)(((m0 - P.m_begin) + 64 * pw + t8) * KC + 8 * (((uint32_t)lane & 7u) ^ swz(t8 + 8u * p))) * 2u;
+    typedef __attribute__((address_space(3))) char lds_char;
+    lds_char* const xlds = (lds_char*)smem + kXOff + pw * 8192;
     // Forward: weight row n0 + rr (rr = pt / 2), codes [32 dh, 32 dh + 32) of
     // block kb.  TR: weight row 64 kb + rr (rr = pt / 4), codes [32 dh, 32 dh +
     // 32) of block column n0 / 64 + bq.
@@ -361,18 +366,14 @@ __global__ __launch_bounds__(512, 1) void k_gemm(GemmParams P, Levels lv) {
     }
     const uint32_t tp = kTOff + (BITS == 8 ? 4u * (lane & 15) : 8u * fr);
 
-    struct XS { u32x4_t v[8]; };
     struct CS { Codes32<BITS> c; uint32_t q8; float sc; };
-    auto load_xj = [&](XS& st, int64_t kb, int j) {
-      st.v[j] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(xr, xg0 + j * xg_row8, (int)(kb * 128), 0));
-    };
-    auto load_x = [&](XS& st, int64_t kb) {
+    // block kb's x rows into buffer buf (in flight until a vmcnt wait)
+    auto load_x_lds = [&](int64_t kb, int buf) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j) load_xj(st, kb, j);
-    };
-    auto store_x = [&](const XS& st, int buf) {
-#pragma unroll
-      for (int j = 0; j < 8; ++j) lds_store_u32x4(xst[j & 1] + buf * kXTile + 1024u * j, st.v[j]);
+      for (int j = 0; j < 8; ++j)
+        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (void __attribute__((address_space(3)))*)(
+                                                         xlds + buf * kXTile + 1024 * j),
+                                                 16, xgd[j & 1] + j * xg_row8, (int)(kb * 128), 0, 0);
     };
     auto load_c = [&](CS& st, int64_t kb) {
       const int64_t blk = wblk + kb * wstep;
@@ -423,16 +424,12 @@ __global__ __launch_bounds__(512, 1) void k_gemm(GemmParams P, Levels lv) {
     // Block k+2 is written while the consumers multiply block k.  x(j) and
     // codes(j) live in register set j % 3 and are loaded two blocks before they
     // are written (a set is free again once its block is in LDS).
-    XS x0, x1, x2;
     CS c0, c1, c2;
-    load_x(x0, 0);
+    load_x_lds(0, 0);
     load_c(c0, 0);
-    load_x(x1, min<int64_t>(1, kbl));
+    if (!(ADP && nb == 1)) load_x_lds(min<int64_t>(1, kbl), 1);
     load_c(c1, min<int64_t>(1, kbl));
     load_c(c2, min<int64_t>(2, kbl));
-    load_x(x2, min<int64_t>(2, kbl));
-    store_x(x0, 0);
-    load_x(x0, min<int64_t>(3, kbl));
     dequant_store(c0, 0);
     load_c(c0, min<int64_t>(3, kbl));
     // ADP: adapter block j >= nb (a = j - nb, adapter columns [32 a, 32 a + 32))
@@ -528,40 +525,33 @@ __global__ __launch_bounds__(512, 1) void k_gemm(GemmParams P, Levels lv) {
     if (ADP && nb == 1) {
       adapter_write(1);
     } else {
-      store_x(x1, 1);
       dequant_store(c1, 1);
     }
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // x of blocks 0 and 1 in LDS
     __syncthreads();
-    // Step k: load x(k+4) into set (k+1) % 3 and codes(k+4) into set (k+1) % 3;
-    // write x(k+2) and the dequantized block k+2 into buffer (k+2) % 3.  The
-    // step runs in pinned chunks, each a few loads plus the arithmetic of one
-    // code word, so the wave keeps computing while the load queue drains.
-    auto pstep = [&](XS& xl, const XS& xw, CS& cl, const CS& cw, int64_t k, int bw) {
+    // Step k: x(k+2) by direct loads into buffer (k+2) % 3 (freed by the last
+    // barrier), codes(k+4) into set (k+1) % 3, and the dequantized block k+2
+    // into buffer (k+2) % 3.  Before the step's barrier the wave waits for all
+    // but its 8 newest loads: x(k+1), issued a step earlier, is then in LDS
+    // for the consumers' next block.  The step runs in pinned chunks, each a
+    // code word's arithmetic, so the wave keeps computing while loads drain.
+    auto pstep = [&](CS& cl, const CS& cw, int64_t k, int bw) {
+      __builtin_amdgcn_sched_barrier(0);
+      load_x_lds(min(k + 2, kbl), bw);
       __builtin_amdgcn_sched_barrier(0);
       load_c(cl, min(k + 4, kbl));
       const DQ d = dq_begin(cw);
       uint32_t o[16];
       dq_part(d, std::integral_constant<int, 0>{}, o);
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int j = 0; j < 3; ++j) load_xj(xl, min(k + 4, kbl), j);
-#pragma unroll
-      for (int j = 0; j < 3; ++j) lds_store_u32x4(xst[j & 1] + bw * kXTile + 1024u * j, xw.v[j]);
       dq_part(d, std::integral_constant<int, 1>{}, o);
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int j = 3; j < 6; ++j) load_xj(xl, min(k + 4, kbl), j);
-#pragma unroll
-      for (int j = 3; j < 6; ++j) lds_store_u32x4(xst[j & 1] + bw * kXTile + 1024u * j, xw.v[j]);
       dq_part(d, std::integral_constant<int, 2>{}, o);
       __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int j = 6; j < 8; ++j) load_xj(xl, min(k + 4, kbl), j);
-#pragma unroll
-      for (int j = 6; j < 8; ++j) lds_store_u32x4(xst[j & 1] + bw * kXTile + 1024u * j, xw.v[j]);
       dq_part(d, std::integral_constant<int, 3>{}, o);
       store_w(o, bw);
       __builtin_amdgcn_sched_barrier(0);
+      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
       __syncthreads();
       __builtin_amdgcn_sched_barrier(0);
     };
@@ -571,12 +561,14 @@ __global__ __launch_bounds__(512, 1) void k_gemm(GemmParams P, Levels lv) {
     const int64_t nr3 = nreg - nreg % 3;
     int64_t kb = 0;
     for (; kb < nr3; kb += 3) {
-      pstep(x1, x2, c1, c2, kb, 2);
-      pstep(x2, x0, c2, c0, kb + 1, 0);
-      pstep(x0, x1, c0, c1, kb + 2, 1);
+      pstep(c1, c2, kb, 2);
+      pstep(c2, c0, kb + 1, 0);
+      pstep(c0, c1, kb + 2, 1);
     }
-    if (kb < nreg) pstep(x1, x2, c1, c2, kb, 2);
-    if (kb + 1 < nreg) pstep(x2, x0, c2, c0, kb + 1, 0);
+    if (kb < nreg) pstep(c1, c2, kb, 2);
+    if (kb + 1 < nreg) pstep(c2, c0, kb + 1, 0);
+    // every direct load in LDS before the adapter steps and the epilogue reuse it
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
     if constexpr (ADP) {
       // steps nreg .. nbt - 1 write the adapter blocks (j = k + 2 >= nb)
       for (int64_t k = nreg; k < nbt; ++k) {
