@@ -326,3 +326,29 @@ def test_decode_graph_replays_match_eager():
         torch.cuda.synchronize()
         assert torch.equal(y, eager), i
         _ = (x.float() * 2).sum().item()  # unrelated eager work between replays
+
+
+def test_linear_rows_past_32bit_offsets():
+    """M = 262,400 rows of K = 4096 (x above 2 GiB): the GEMM runs as two row ranges (261,888 rows, then 512),
+    each addressed with 32-bit buffer offsets from its own base.  x repeats one 512-row block, so every row's
+    reference is that block's; rows on both sides of the split and at the ends are checked."""
+    import types
+    base = _small_linear(256, 4096, 512, 4, 16, seed=40)
+    qw = _gpu_quant(base.W, "f16", 4)
+    rows = list(range(256))
+    wd = oracle_rows_dequant(base.W, "f16", 4, rows)
+    M = 262400
+    xs = dev(base.x, "bf16")
+    x = xs.repeat((M + 511) // 512, 1)[:M].contiguous()
+    A, B = dev(base.A, "bf16"), dev(base.B, "bf16")
+    print(f"linear M={M} K=4096 N=256 r=16 (two row ranges)", flush=True)
+    y = qlr.linear(x, qw, A, B, base.scale, out_dtype=torch.float32)
+    torch.cuda.synchronize()
+    ms = [0, 1, 261887, 261888, 261889, 262143, 262144, M - 1] + \
+        np.random.default_rng(40).choice(M, size=8, replace=False).tolist()
+    got = f32_of(y[torch.tensor(ms, device=y.device)])
+    ref = types.SimpleNamespace(x=base.x[[m % 512 for m in ms]], xdtype="bf16", A=base.A, B=base.B,
+                                abdtype="bf16", scale=base.scale)
+    check_linear(got, ref, wd, rows, "f32")
+    del x, y
+    torch.cuda.empty_cache()
