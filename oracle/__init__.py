@@ -18,7 +18,8 @@ Pages (titles as printed):
   * "LoRDBA" (gist.science summary): the unmerged "adapter mode", in which the
     frozen quantized base and the adapter branch stay separate terms.
   * "AutoQRA" (gist.science summary), section 3.1: one (bits, rank) pair per
-    layer; section 1: the quantized backbone is frozen and adapters are trained
+    layer (a mixed stack is a list of independent ``quantize`` + ``linear``
+    entries, each with its own bits and rank); section 1: the quantized backbone is frozen and adapters are trained
     (the backward in ``linear``).
   * "LoRDBA" section 2: the double-binary adapter branch (``dba``).
   * "QFT" (gist.science summary), section 2.2: the hybrid outlier split
@@ -34,7 +35,7 @@ from .codebook import normal_quantile, quantile_codebook
 from .quant import (widen, block_absmax, nearest_codes, pack_codes, unpack_codes,
                     double_quantize, dequantize_scales, dequantize, quantize,
                     qweight_sizes, QuantizedWeight)
-from .linear import (lora_t, linear, linear_tolerance, mixed, linear_backward,
+from .linear import (lora_t, linear, linear_tolerance, linear_backward,
                      linear_backward_tolerance, adapter_grads, adapter_grads_tolerance)
 from . import dba, outliers, wha
 
@@ -42,6 +43,6 @@ __all__ = [
     "normal_quantile", "quantile_codebook", "widen", "block_absmax", "nearest_codes",
     "pack_codes", "unpack_codes", "double_quantize", "dequantize_scales", "dequantize",
     "quantize", "qweight_sizes", "QuantizedWeight", "lora_t", "linear",
-    "linear_tolerance", "mixed", "linear_backward", "linear_backward_tolerance", "adapter_grads",
+    "linear_tolerance", "linear_backward", "linear_backward_tolerance", "adapter_grads",
     "adapter_grads_tolerance", "dba", "outliers", "wha",
 ]

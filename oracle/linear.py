@@ -47,11 +47,6 @@ def linear_tolerance(x, xdtype, wdeq32):
     return np.abs(_f64(x, xdtype)) @ np.abs(wdeq32.astype(np.float64)).T
 
 
-def mixed(entries):
-    """Independent linears: ``entries`` is a list of kwargs for ``linear``."""
-    return [linear(**e) for e in entries]
-
-
 def linear_backward(dy, dydtype, x, xdtype, wdeq32, A=None, B=None, abdtype="f32", scale=0.0):
     """Gradients of the forward above for an upstream gradient dy (M x N), float64.
 

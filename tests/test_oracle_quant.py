@@ -249,3 +249,42 @@ def test_bf16_widening():
     bits16 = np.array([0x3F80, 0xBF80, 0x0000, 0x8000, 0x4049], dtype=np.uint16)
     f = oracle.widen(bits16, "bf16")
     assert f.tolist()[:4] == [1.0, -1.0, 0.0, -0.0] and abs(f[4] - 3.140625) == 0
+
+
+def _round_f32_signed(q: Fraction) -> float:
+    """Round any rational to float32 (nearest, ties even): round-to-nearest is symmetric in sign."""
+    if q < 0:
+        return -_round_f32_fraction(-q)
+    return _round_f32_fraction(q)
+
+
+@pytest.mark.parametrize("bits", BITS)
+def test_dequantize_two_roundings(bits):
+    """Dequantization is fl32(L[c] * fl32(m * s)): two float32 roundings in that order (QLoRA page,
+    "2. Double Quantization": the block constant is dequantized first, then scales the level).
+
+    Steps with 24 significant bits make m * s inexact, so a single rounding fl32(L * m * s) differs on
+    some elements; the reference is built from exact rationals, independently of numpy's float32.
+    """
+    rng = np.random.default_rng(300 + bits)
+    L = oracle.quantile_codebook(bits)
+    nblk = 256 * 2
+    step = np.array([np.float32((int(rng.integers(1 << 23, 1 << 24)) | 1) * 2.0 ** -30) for _ in range(2)],
+                    dtype=np.float32)
+    q8 = rng.integers(0, 256, size=nblk).astype(np.uint8)
+    codes = rng.integers(0, 1 << bits, size=(nblk, 64)).astype(np.uint8)
+    packed = Q.pack_codes(codes, bits)
+    got_a = Q.dequantize_scales(q8, step)
+    got_w = oracle.dequantize(packed, q8, step, bits, nblk * 64).reshape(nblk, 64)
+    differs = 0
+    for j in range(nblk):
+        s = Fraction(float(step[j // 256]))
+        a1 = _round_f32_fraction(int(q8[j]) * s)
+        assert float(got_a[j]) == a1, j
+        for e in range(0, 64, 5 if bits == 8 else 3):
+            lv = Fraction(float(L[codes[j, e]]))
+            two = _round_f32_signed(lv * Fraction(a1))
+            one = _round_f32_signed(lv * int(q8[j]) * s)
+            assert float(got_w[j, e]) == two, (j, e)
+            differs += two != one
+    assert differs > 0  # the sample tells the two orders apart
