@@ -7,6 +7,7 @@ one shared library is linked next to this file.
 from __future__ import annotations
 
 import concurrent.futures as cf
+import hashlib
 import os
 import shutil
 import subprocess
@@ -37,6 +38,35 @@ COMMON = [
 ]
 
 
+def source_files():
+    """Every file the library is built from (kernels, host code, headers), in a fixed order."""
+    files = [os.path.join(CSRC, f) for f in sorted(os.listdir(CSRC)) if f.endswith((".hip", ".cpp", ".h"))]
+    return files + [os.path.join(ROOT, "include", "qlr.h")]
+
+
+def source_hash() -> str:
+    """sha256 over the library's sources (names and contents); built into the library."""
+    h = hashlib.sha256()
+    for path in source_files():
+        h.update(os.path.relpath(path, ROOT).encode() + b"\0")
+        with open(path, "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()
+
+
+def _stamp() -> str:
+    """A translation unit that exports the source hash as a data symbol."""
+    path = os.path.join(BUILD, "qlr_stamp.cpp")
+    text = f'extern "C" __attribute__((visibility("default"))) const char qlr_source_sha256[65] = "{source_hash()}";\n'
+    with open(path, "w") as f:
+        f.write(text)
+    obj = path + ".o"
+    res = subprocess.run([hipcc(), "-O2", "-fPIC", "-c", path, "-o", obj], capture_output=True, text=True)
+    if res.returncode != 0:
+        raise RuntimeError(f"hipcc failed for the source stamp:\n{res.stderr}")
+    return obj
+
+
 def _compile(src: str) -> str:
     obj = os.path.join(BUILD, src + ".o")
     cmd = [hipcc(), *COMMON, "-c", os.path.join(CSRC, src), "-o", obj]
@@ -53,6 +83,7 @@ def build(verbose: bool = False) -> str:
     workers = min(len(SOURCES), max(1, min(8, os.cpu_count() or 1)))
     with cf.ThreadPoolExecutor(max_workers=workers) as ex:
         objs = list(ex.map(_compile, SOURCES))
+    objs.append(_stamp())
     tmp = LIB + ".tmp"
     cmd = [hipcc(), "--offload-arch=gfx950", "-shared", "-fPIC", "-o", tmp, *objs]
     res = subprocess.run(cmd, capture_output=True, text=True)

@@ -113,16 +113,27 @@ _lock = threading.Lock()
 
 
 def lib():
-    """Load libqlr.so (building it first only if it does not exist)."""
+    """Load libqlr.so (building it first only if it does not exist).
+
+    A library built from other sources than the ones in the tree is refused: the
+    build stamps it with a hash of its sources, checked here against the tree.
+    """
     global _lib
     if _lib is not None:
         return _lib
     with _lock:
         if _lib is None:
+            from .build import build, source_hash
             if not os.path.exists(LIB_PATH):
-                from .build import build
                 build()
             handle = C.CDLL(LIB_PATH)
+            try:
+                built = (C.c_char * 65).in_dll(handle, "qlr_source_sha256").value.decode()
+            except ValueError:
+                built = ""
+            if built != source_hash():
+                raise RuntimeError(f"{LIB_PATH} was built from other sources than the ones in the tree; "
+                                   "rebuild it (python -m quantized_base_fine_amd.build)")
             for name, (res, args) in EXPORTS.items():
                 fn = getattr(handle, name)
                 fn.restype = res
