@@ -236,9 +236,17 @@ qlr_status qlr_dequantize(const qlr_qweight* w, void* out, qlr_dtype odt, void* 
  * x (device) M x K in xdt (f32 or bf16); A (device) r x K and B (device) N x r
  * in abdt (f32 or bf16), both NULL when r == 0; y (device) M x N in ydt
  * (f32 or bf16).  Requires cols % 64 == 0 (whole blocks per row).  M may be 0
- * (nothing is launched).  Each y element is within
- * 1e-3 * sum_k |x[m,k] w'[n,k]| + 1e-5 of the exact result (plus half a bf16
- * ulp when ydt is bf16).  ws (device) >= qlr_workspace_bytes(QLR_OP_LINEAR,
+ * (nothing is launched).  Error bound per y element, S = sum_k |x[m,k] w'[n,k]|
+ * (plus half a bf16 ulp of the result when ydt is bf16), on any input:
+ *   - QLR_PATH_F32 and QLR_PATH_GEMV: 1e-3 * S + 1e-5.  The decode kernels
+ *     carry each codebook level as two bf16 halves (about 16 significant bits)
+ *     and the float32 kernels in float32; sums are float32.
+ *   - QLR_PATH_GEMM: 5e-3 * S + 1e-5.  The prefill kernel rounds each
+ *     dequantized weight once to bf16 (relative error up to 2^-8) for the bf16
+ *     matrix cores.  When those rounding errors do not all share a sign, as
+ *     for zero-mean x or weights, the error stays far inside 1e-3 * S; a caller
+ *     that needs 1e-3 * S on every input at M > 16 forces QLR_PATH_F32.
+ * ws (device) >= qlr_workspace_bytes(QLR_OP_LINEAR,
  * M, N, K, r) (scratch for x A^T; any contents).
  * Asynchronous, allocation-free, no host synchronisation.
  * Errors: QLR_ERR_NULL, QLR_ERR_SHAPE, QLR_ERR_DTYPE, QLR_ERR_BITS,
@@ -356,7 +364,9 @@ qlr_status qlr_linear_fwd_dba(const void* x, qlr_dtype xdt, int64_t M, const qlr
  * sums of exactly widened inputs.  Per element, each result is within
  * 1e-3 * S + 1e-5 of the exact value, S the sum of the absolute values of the
  * terms that define it (with |u| and |t| likewise bounded by sums of absolute
- * products), plus half a bf16 ulp for a bf16 dx.  ws (device) >=
+ * products), plus half a bf16 ulp for a bf16 dx; on the MFMA family dx is
+ * within 5e-3 * S + 1e-5 (the weight enters rounded to bf16, as on the
+ * prefill GEMM of qlr_linear_fwd).  ws (device) >=
  * qlr_workspace_bytes(QLR_OP_LINEAR_BWD, M, rows, cols, r).  Asynchronous,
  * allocation-free; the results do not depend on timing.
  * Errors: QLR_ERR_NULL, QLR_ERR_SHAPE, QLR_ERR_DTYPE, QLR_ERR_BITS,
@@ -370,7 +380,8 @@ qlr_status qlr_linear_bwd(const void* dy, qlr_dtype dydt, const void* x, qlr_dty
 
 /*
  * Force the kernel family used by qlr_linear_fwd and qlr_linear_fwd_mixed on
- * the calling thread (for tests and measurement).  QLR_PATH_AUTO restores the
+ * the calling thread (for tests, measurement, and callers that need a
+ * family's error bound; see qlr_linear_fwd).  QLR_PATH_AUTO restores the
  * default choice: F32 for float32 x or float32 adapters, GEMV for M <= 16,
  * GEMM otherwise.  Host only.  Errors: QLR_ERR_PATH for an unknown value.
  */

@@ -26,14 +26,18 @@
 //
 // Layout on the 16x16x32 bf16 MFMA (A = x rows, B = unscaled levels):
 //   lane l: x row / weight row (l & 15), lane group g = l >> 4 owns the 16
-//   consecutive elements [16g, 16g+16) of each 64-element block; the first
-//   MFMA takes elements [16g, 16g+8), the second [16g+8, 16g+16).  Both MFMAs
-//   of a block stay inside that block, so the block's dequantized absmax
+//   consecutive elements [16g, 16g+16) of each 64-element block; one MFMA pair
+//   takes elements [16g, 16g+8), another [16g+8, 16g+16).  All MFMAs of a
+//   block stay inside that block, so the block's dequantized absmax
 //   multiplies the 16x16 product afterwards (one FMA per output and block)
 //   instead of every weight.
-// Levels are looked up in a lane-private LDS table indexed by the packed code
-// bits of two neighbouring weights (entry e of lane L at byte e*256 + 4L), so
-// 64 lanes never collide on a bank; one table read yields a bf16 pair.
+// Levels are looked up in an LDS table indexed by the packed code bits of two
+// neighbouring weights, with a copy per lane position so that lanes never
+// collide on a bank (qlr_lut.h).  Each level enters as two bf16 halves, hi and
+// lo, multiplied with x separately (two packed dot products, or two MFMAs):
+// a level rounded to bf16 alone is off by up to 2^-8 of its value, and with x
+// and the weights of one sign those errors add up to more than the layer's
+// 1e-3 bound; hi + lo carries the float32 level to about 2^-16.
 #include <algorithm>
 #include <type_traits>
 
@@ -168,11 +172,12 @@ __device__ __forceinline__ Raw<BITS> raw_from_lds(uint32_t row_addr, int u, int 
   return r;
 }
 
-// The lane-private pair table, built straight from the by-value levels: wave
-// w writes entries [w E/8, (w+1) E/8) of every lane's copy, so an entry's level
-// indices are uniform across the wave; for 3- and 4-bit codes the low level
-// index runs over all levels within a wave and is a compile-time index (one
-// batched scalar load), the high one takes E/8/NL values per wave.
+// The level table (layout in qlr_lut.h), built straight from the by-value
+// levels: wave w writes entries [w E/8, (w+1) E/8) of every copy, so an entry's
+// level indices are uniform across the wave; for 3- and 4-bit codes the low
+// level index runs over all levels within a wave and is a compile-time index
+// (one batched scalar load), the high one takes E/8/NL values per wave.  For
+// paired widths lane L writes word L >> 5 (hi pair or lo pair) of copy L % 32.
 template <int BITS>
 __device__ __forceinline__ void build_table_kernarg(uint32_t* tbl, const Levels& lv, int tid) {
   constexpr int NL = 1 << BITS;
@@ -180,21 +185,30 @@ __device__ __forceinline__ void build_table_kernarg(uint32_t* tbl, const Levels&
   constexpr int EPW = E / kWaves;
   const int lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  uint32_t* t = tbl + (w * EPW) * 64 + lane;
+  const bool lo_half = lane >= 32;
+  uint32_t* t = tbl + (w * EPW) * 64 + (BITS == 8 ? lane : 2 * (lane & 31) + (lane >> 5));
+  auto word = [&](float a, float b) {
+    const uint32_t h = level_hi(a) | (level_hi(b) << 16);
+    const uint32_t l = level_lo(a) | (level_lo(b) << 16);
+    return lo_half ? l : h;
+  };
   if constexpr (BITS == 8) {
 #pragma unroll
-    for (int i = 0; i < EPW; ++i) t[i * 64] = f32_to_bf16_bits(lv.v[w * EPW + i]);
+    for (int i = 0; i < EPW; ++i) {
+      const float v = lv.v[w * EPW + i];
+      t[i * 64] = level_hi(v) | (level_lo(v) << 16);
+    }
   } else if constexpr (EPW >= NL) {
     float lo[NL];
 #pragma unroll
     for (int j = 0; j < NL; ++j) lo[j] = lv.v[j];
 #pragma unroll
-    for (int i = 0; i < EPW; ++i) t[i * 64] = pack_bf16x2(lo[i & (NL - 1)], lv.v[w * (EPW / NL) + (i >> BITS)]);
+    for (int i = 0; i < EPW; ++i) t[i * 64] = word(lo[i & (NL - 1)], lv.v[w * (EPW / NL) + (i >> BITS)]);
   } else {
 #pragma unroll
     for (int i = 0; i < EPW; ++i) {
       const int e = w * EPW + i;
-      t[i * 64] = pack_bf16x2(lv.v[e & (NL - 1)], lv.v[e >> BITS]);
+      t[i * 64] = word(lv.v[e & (NL - 1)], lv.v[e >> BITS]);
     }
   }
 }
@@ -223,44 +237,45 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
 }
 
 // Single-row products: sum over the 128 / BITS codes of one 16-byte piece of
-// level(code) * x, with the levels looked up as bf16 pairs in the lane-private
+// level(code) * x, with the levels looked up as bf16 hi/lo halves in the
 // table (at LDS address 0) and multiplied with the matching x pairs (xv holds
 // the piece's x values in order, 8 per 16-byte vector).  Two accumulation
-// chains, added at the end.
+// chains for the hi halves and two for the lo halves, added at the end.
 template <int BITS>
-__device__ __forceinline__ float dot_piece(const u32x4_t& pc, const u32x4_t* xv, uint32_t lane4) {
-  float s0 = 0.0f, s1 = 0.0f;
+__device__ __forceinline__ float dot_piece(const u32x4_t& pc, const u32x4_t* xv, uint32_t tl) {
+  float s0 = 0.0f, s1 = 0.0f, t0 = 0.0f, t1 = 0.0f;
+  auto acc = [&](u32x2v_t e, uint32_t xp, bool odd) {
+    if (odd) {
+      s1 = dot2(e.x, xp, s1);
+      t1 = dot2(e.y, xp, t1);
+    } else {
+      s0 = dot2(e.x, xp, s0);
+      t0 = dot2(e.y, xp, t0);
+    }
+  };
   if constexpr (BITS == 4) {
 #pragma unroll
     for (int w = 0; w < 4; ++w)
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
-        const uint32_t lvp = lds_word(__builtin_amdgcn_perm(pc[w], lane4, 0x0C0C0000u | ((uint32_t)(4 + b) << 8)));
-        if (b & 1) s1 = dot2(lvp, xv[w][b], s1);
-        else s0 = dot2(lvp, xv[w][b], s0);
-      }
+      for (int b = 0; b < 4; ++b)
+        acc(lds_entry(__builtin_amdgcn_perm(pc[w], tl, 0x0C0C0000u | ((uint32_t)(4 + b) << 8))), xv[w][b], b & 1);
   } else if constexpr (BITS == 2) {
 #pragma unroll
     for (int w = 0; w < 4; ++w)
 #pragma unroll
-      for (int n = 0; n < 8; ++n) {
-        const uint32_t lvp = lds_word((((pc[w] >> (4 * n)) & 15u) << 8) | lane4);
-        if (n & 1) s1 = dot2(lvp, xv[2 * w + (n >> 2)][n & 3], s1);
-        else s0 = dot2(lvp, xv[2 * w + (n >> 2)][n & 3], s0);
-      }
+      for (int n = 0; n < 8; ++n)
+        acc(lds_entry((((pc[w] >> (4 * n)) & 15u) << 8) | tl), xv[2 * w + (n >> 2)][n & 3], n & 1);
   } else {
 #pragma unroll
     for (int w = 0; w < 4; ++w)
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const uint32_t lo = lds_word((((pc[w] >> (16 * j)) & 255u) << 8) | lane4);
-        const uint32_t hi = lds_word((((pc[w] >> (16 * j + 8)) & 255u) << 8) | lane4);
-        const uint32_t xp = xv[w >> 1][2 * (w & 1) + j];
-        if (j) s1 = dot2(lo | (hi << 16), xp, s1);
-        else s0 = dot2(lo | (hi << 16), xp, s0);
+        const uint32_t e0 = lds_word((((pc[w] >> (16 * j)) & 255u) << 8) | tl);
+        const uint32_t e1 = lds_word((((pc[w] >> (16 * j + 8)) & 255u) << 8) | tl);
+        acc(split8(e0, e1), xv[w >> 1][2 * (w & 1) + j], j);
       }
   }
-  return s0 + s1;
+  return (s0 + s1) + (t0 + t1);
 }
 
 // ADP: the call has an adapter branch (r > 0); calls without one run a separate
@@ -306,7 +321,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
   const int tid = threadIdx.x;
   const int lane = tid & 63, wave = tid >> 6;
   const int nl = lane & 15, g = lane >> 4;
-  const uint32_t lane4 = (uint32_t)lane * 4u;
+  const uint32_t tlane = table_lane<BITS>(lane);
   const int64_t kb0 = nb * wave / kWaves, kb1 = nb * (wave + 1) / kWaves;
   const int nchunk = (int)((kb1 - kb0 + CH - 1) / CH);
   const int nitem = nchunk > 0 ? nchunk : 1;  // items (chunks) per tile for this wave
@@ -666,7 +681,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
       for (int i = 0; i < G::NP; ++i) {
         const int row = (i * 64 + lane) / G::PR;
         const float ap = __uint_as_float(lds_rd32(sscale + (uint32_t)(row * CH + u) * 4));
-        const float sp = dot_piece<BITS>(__builtin_bit_cast(u32x4_t, ch.piece[i]), xv, lane4);
+        const float sp = dot_piece<BITS>(__builtin_bit_cast(u32x4_t, ch.piece[i]), xv, tlane);
         accd[i] = fmaf(ap, bval ? sp : 0.0f, accd[i]);
       }
     }
@@ -705,11 +720,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
         x0 = xvalid ? ch.x[u][0] : zero;
         x1 = xvalid ? ch.x[u][1] : zero;
       }
-      u32x4_t b0, b1;
-      decode16<BITS>(raw_from_lds<BITS>(rowad, u, g), lane4, b0, b1);
+      u32x4_t b0h, b0l, b1h, b1l;
+      decode16<BITS>(raw_from_lds<BITS>(rowad, u, g), tlane, b0h, b0l, b1h, b1l);
       f32x4_t d = {0.f, 0.f, 0.f, 0.f};
-      d = mfma16x16x32(as_bf16x8(x0), as_bf16x8(b0), d);
-      return mfma16x16x32(as_bf16x8(x1), as_bf16x8(b1), d);
+      d = mfma16x16x32(as_bf16x8(x0), as_bf16x8(b0h), d);
+      d = mfma16x16x32(as_bf16x8(x1), as_bf16x8(b1h), d);
+      d = mfma16x16x32(as_bf16x8(x0), as_bf16x8(b0l), d);
+      return mfma16x16x32(as_bf16x8(x1), as_bf16x8(b1l), d);
     };
     auto accumulate = [&](int u, const f32x4_t& d) {
       const float ap = __uint_as_float(aps[u]);

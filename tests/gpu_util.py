@@ -74,19 +74,24 @@ def oracle_rows_dequant(W, wdtype, bits, rows):
     return out
 
 
-def check_linear(y_gpu, lin, wdeq_rows, rows, ydt="f32", ms=None):
-    """Per-element bound |y - y_ref| <= 1e-3 * S + 1e-5 (+ half a bf16 ulp for bf16 y).
+# Rounding a float32 value y to bf16 moves it by at most half a bf16 ulp, which is at most 2^-8 |y|.
+BF16_HALF_ULP_REL = 2.0 ** -8
 
-    ``wdeq_rows``: oracle-dequantized rows ``rows`` of W'; ``ms``: x rows to check.
+
+def check_linear(y_gpu, lin, wdeq_rows, rows, ydt="f32", ms=None, rel=1e-3):
+    """Per-element bound |y - y_ref| <= rel * S + 1e-5 (+ half a bf16 ulp for bf16 y).
+
+    ``wdeq_rows``: oracle-dequantized rows ``rows`` of W'; ``ms``: x rows to check;
+    ``rel``: 1e-3 (the layer's bound), or the bf16-weight GEMM family's wider one.
     Returns the worst ratio error / bound.
     """
     x = lin.x if ms is None else lin.x[ms]
     A, B = lin.A, (None if lin.B is None else lin.B[rows])
     yref = oracle.linear(x, lin.xdtype, wdeq_rows, A, B, lin.abdtype, lin.scale)
     S = oracle.linear_tolerance(x, lin.xdtype, wdeq_rows)
-    bound = 1e-3 * S + 1e-5
+    bound = rel * S + 1e-5
     if ydt == "bf16":
-        bound = bound + np.abs(yref) * 2.0 ** -9
+        bound = bound + np.abs(yref) * BF16_HALF_ULP_REL
     got = y_gpu if ms is None else y_gpu[ms]
     got = got[:, rows].astype(np.float64)
     err = np.abs(got - yref)
@@ -123,7 +128,7 @@ def check_backward(got, lin, dy, wdeq, ks=None, dxdt="f32"):
         ratios.append(ratio)
 
     if dx is not None:
-        one(dx[:, cols], ref[0], S[0], 2.0 ** -9 if dxdt == "bf16" else 0.0)
+        one(dx[:, cols], ref[0], S[0], BF16_HALF_ULP_REL if dxdt == "bf16" else 0.0)
     if lin.r > 0:
         one(dA[:, cols], ref[1], S[1])
         if ks is None:

@@ -42,7 +42,7 @@ def _check(y, lin, ad, wd, ydt="f32", ms=None):
     args = (ad.alpha.astype(np.float64), ad.beta.astype(np.float64), ad.gamma.astype(np.float64), ad.b1, ad.b2)
     ref = odba.linear_dba(x, lin.xdtype, wd, *args)
     S = odba.linear_dba_tolerance(x, lin.xdtype, wd, *args)
-    bound = 1e-3 * S + 1e-5 + (np.abs(ref) * 2.0 ** -9 if ydt == "bf16" else 0.0)
+    bound = 1e-3 * S + 1e-5 + (np.abs(ref) * 2.0 ** -8 if ydt == "bf16" else 0.0)
     got = (y if ms is None else y[ms]).astype(np.float64)
     err = np.abs(got - ref)
     assert np.all(np.isfinite(got))

@@ -49,7 +49,7 @@ def _check(y, lin, wd, csr, P, ydt="f32", x=None):
     x = lin.x if x is None else x
     ref = owha.linear_wht(x, lin.xdtype, wd, csr, P)
     S = owha.linear_wht_tolerance(x, lin.xdtype, wd, csr, P)
-    bound = 1e-3 * S + 1e-5 + (np.abs(ref) * 2.0 ** -9 if ydt == "bf16" else 0.0)
+    bound = 1e-3 * S + 1e-5 + (np.abs(ref) * 2.0 ** -8 if ydt == "bf16" else 0.0)
     err = np.abs(y.astype(np.float64) - ref)
     assert np.all(np.isfinite(y))
     assert np.all(err <= bound), f"max err/bound {float(np.max(err / bound)):.3f}"
