@@ -247,6 +247,108 @@ def decode_by_bits(torch, qlr, W, x1, A0, B0, scale, dev, reps=5):
 
 
 
+def time_sequence(torch, calls, stream, graph: bool, reps: int = 5):
+    """Median over reps of the time of the calls back to back (a HIP graph of them when
+    `graph`, checked against the eager outputs first), per call, in us."""
+    for c in calls:
+        c()
+    torch.cuda.synchronize()
+    run = None
+    if graph:
+        ref = [c.y.clone() for c in calls]
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=stream):
+            for c in calls:
+                c()
+        for c in calls:
+            c.y.zero_()
+        g.replay()
+        torch.cuda.synchronize()
+        assert all(torch.equal(c.y, r0) for c, r0 in zip(calls, ref)), "graph replay differs from eager"
+        run = g.replay
+    else:
+        def run():
+            for c in calls:
+                c()
+    run()
+    torch.cuda.synchronize()
+    ts = []
+    for _ in range(reps):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        run()
+        e1.record(stream)
+        torch.cuda.synchronize()
+        ts.append(e0.elapsed_time(e1) * 1e3 / len(calls))
+    ts.sort()
+    return ts[len(ts) // 2]
+
+
+# The other single-linear workloads: 7B MLP projections (r64) and a 65B-class MLP projection (r64).
+CONFIGS = {
+    "mlp_up_11008x4096": ("up", (1, 16), 2048),
+    "mlp_down_4096x11008": ("down", (1, 16), 2048),
+    "big65_22016x8192": ("big65", (1,), 4096),
+}
+
+
+def bench_configs(torch, qlr, workloads, dev, stream, only=None, graph=True):
+    """Decode and prefill of each workload in CONFIGS over R distinct copies of its quantized
+    weight (R sized so the copies exceed twice the 256 MB last-level cache), with and without
+    the adapter: per-call time, effective GB/s (decode) or TFLOP/s (prefill) and the roofline
+    fraction of the adapter-free call (one GEMV / GEMM kernel)."""
+    import numpy as np
+
+    def to_dev(a, dt):
+        if dt == "bf16":
+            return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+        return torch.from_numpy(np.ascontiguousarray(a)).to(dev)
+
+    out = {}
+    for name, (which, m_dec, m_pre) in CONFIGS.items():
+        if only and name != only:
+            continue
+        lin = workloads.big65(1) if which == "big65" else workloads.mlp(which, 1)
+        N, K, r = lin.N, lin.K, lin.r
+        W = to_dev(lin.W, "f16")
+        A, B = to_dev(lin.A, "bf16"), to_dev(lin.B, "bf16")
+        cb, qb, kb = qlr.qweight_sizes(N, K, BITS)
+        R = (2 * MALL_BYTES) // (cb + qb + kb) + 1
+        qws = torch.empty(qlr.workspace_bytes(qlr.OP_QUANTIZE), dtype=torch.uint8, device=dev)
+        layers = [qlr.quantize(W, BITS, ws=qws) for _ in range(R)]
+        del W
+        rec = {"N": N, "K": K, "bits": BITS, "rank": r, "layers": R}
+        for M in tuple(m_dec) + (m_pre,):
+            gen = torch.Generator(device=dev)
+            gen.manual_seed(1000 + M)
+            x = torch.randn((M, K), generator=gen, device=dev).to(torch.bfloat16)
+            y = torch.empty((M, N), dtype=torch.bfloat16, device=dev)
+            ws = torch.empty(max(qlr.workspace_bytes(qlr.OP_LINEAR, M, N, K, r), 16), dtype=torch.uint8, device=dev)
+            decode = M <= 16
+            for tag, adp in (("adapter", True), ("base", False)):
+                calls = [qlr.LinearCall(x, q, A, B, lin.scale, out=y, ws=ws) if adp else qlr.LinearCall(x, q, out=y)
+                         for q in layers]
+                us = time_sequence(torch, calls, stream, graph=graph and decode)
+                rr = r if adp else 0
+                key = f"M{M}_{tag}"
+                if decode:
+                    nbytes = decode_bytes(M=M, N=N, K=K, r=rr)
+                    gbs = nbytes / (us * 1e-6) / 1e9
+                    rec[key] = {"us_per_call": round(us, 3), "gbs": round(gbs, 1), "bytes_per_call": nbytes,
+                                "frac": round(gbs / HBM_PEAK_GBS, 4)}
+                else:
+                    fl = prefill_flops(M=M, N=N, K=K, r=rr)
+                    tfs = fl / (us * 1e-6) / 1e12
+                    rec[key] = {"us_per_call": round(us, 3), "tflops": round(tfs, 1), "flops_per_call": fl,
+                                "frac": round(tfs / BF16_PEAK_TFLOPS, 4)}
+                del calls
+            del x, y, ws
+        del layers
+        torch.cuda.empty_cache()
+        out[name] = rec
+    return out
+
+
 def build_mixed(torch, qlr, workloads, dev):
     """The mixed stack at full size: 32 layers x 7 independent linears with per-linear
     (bits, rank) drawn by the stack's seed, M = 512.  Weights, x and adapters are drawn
@@ -359,6 +461,9 @@ def main():
                          "kernel) and print their per-call times: for the counter runs")
     ap.add_argument("--eager", action="store_true",
                     help="no HIP graphs (every launch visible to per-dispatch counter collection)")
+    ap.add_argument("--no-configs", action="store_true", help="skip the MLP and 65B workloads")
+    ap.add_argument("--config-only", choices=sorted(CONFIGS),
+                    help="time only this workload (decode and prefill; eager when --eager) and exit")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="no GPU: write profiles/traffic.json from two rocprofv3 --pmc runs")
     args = ap.parse_args()
@@ -381,6 +486,16 @@ def main():
     # One stream of our own carries every call; prepared calls bind to it and the
     # graphs are captured on it.
     torch.cuda.set_stream(torch.cuda.Stream(dev))
+    if args.config_only:
+        if args.copy_calibration:
+            src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+            torch.add(src, 0.0, out=torch.empty_like(src))
+            torch.cuda.synchronize()
+            del src
+        res = bench_configs(torch, qlr, workloads, dev, torch.cuda.current_stream(dev), only=args.config_only,
+                            graph=not args.eager)
+        print(json.dumps(res))
+        return
     cb, qb, kb = qlr.qweight_sizes(N_, K_, BITS)
     R = args.layers or (2 * MALL_BYTES) // (cb + qb + kb) + 1
 
@@ -673,6 +788,8 @@ def main():
     }
     if not args.eager:
         out["decode_by_bits"] = decode_by_bits(torch, qlr, W, x1, A0, B0, lin1.scale, dev)
+    if not args.no_configs and not args.eager:
+        out["configs"] = bench_configs(torch, qlr, workloads, dev, stream)
     if mixed is not None:
         mixed_ms = phase_ms["mixed"] / S
         mixed_tfs = mixed_flops / (mixed_ms * 1e-3) / 1e12

@@ -91,8 +91,10 @@ struct Chunk {
 // Largest x (bytes) staged once per workgroup in LDS instead of being read per
 // chunk in the MFMA layout (which repeats every x row 16 times per wave).
 constexpr size_t kXLdsMax = 32 * 1024;
-// Adapter partial sums (float32) prefetched into registers, per thread.
-constexpr int kTPre = 4;
+// Adapter partial sums (float32) prefetched into registers, per thread: all of
+// them, as the adapter-product split count guarantees (kTPartsMax).
+constexpr int kTPre = kTPartsMax / kThreads;
+static_assert(kTPre * kThreads == kTPartsMax, "prefetch covers every partial sum");
 
 // How the epilogue gets the adapter product t = x A^T: from the split partial
 // sums of the adapter-product kernel (T_GLOBAL, T_LOOP, T_PREFETCH), or
@@ -936,6 +938,27 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
         const uint32_t yo = buf_off(tid < 256 && j == 0 && nn < N, (uint32_t)(nn * ES));
         if constexpr (YDT == DT_F32) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(out), yr, yo, 0, 0);
         else __builtin_amdgcn_raw_buffer_store_b16((uint16_t)f32_to_bf16_bits(out), yr, yo, 0, 0);
+      } else if (ADP && P.bpre && P.tmode != T_GLOBAL) {
+        // output o = tid / 32 by a half-wave: lane q sums t_j B[o][j] over
+        // j = q, q + 32, ..., the 32 lanes are added by a fixed butterfly, and
+        // lane 0 adds the row sum and stores
+        const int o = tid >> 5, q = tid & 31;
+        float s = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) s += sRed[w * 16 + o];
+        if constexpr (SPX != 0) s += sp_sum(o);
+        float lo = 0.0f;
+        for (int j = q; j < r; j += 32)
+          lo = fmaf(sT[j], bf16_bits_to_f32(lds_rd16(P.sB + (uint32_t)((o * r + j) * 2))), lo);
+#pragma unroll
+        for (int d = 1; d < 32; d <<= 1) lo += __shfl_xor(lo, d, 64);
+        const int64_t nn = tl * 16 + o;
+        const bool ov = q == 0 && nn < N;
+        float out = fmaf(a.scale, lo, s);
+        if (a.addend && ov) out += a.addend[nn];
+        const uint32_t yo = buf_off(ov, (uint32_t)(nn * ES));
+        if constexpr (YDT == DT_F32) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(out), yr, yo, 0, 0);
+        else __builtin_amdgcn_raw_buffer_store_b16((uint16_t)f32_to_bf16_bits(out), yr, yo, 0, 0);
       } else {
         const int o = tid & 15;
         float s = 0.0f;
@@ -950,14 +973,46 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
       for (int v = 0; v < 4; ++v) sRed[wave * 256 + lane * 4 + v] = acc[v];
       acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
       __syncthreads();
-      const int o = tid & 255;
-      float s = 0.0f;
+      if (ADP && P.bpre && P.tmode != T_GLOBAL && (r & 7) == 0) {
+        // output o = tid / 2 by two neighbouring lanes, each summing every other
+        // group of 8 ranks (16-byte LDS reads of t and B), added by one exchange
+        const int o = tid >> 1, hh = tid & 1;
+        float s = 0.0f;
 #pragma unroll
-      for (int w = 0; w < kWaves; ++w) s += sRed[w * 256 + o];
-      const int l = o >> 2, v = o & 3;
-      const int m = 4 * (l >> 4) + v;  // MFMA output row (x row)
-      const int64_t nn = tl * 16 + (l & 15);
-      epilogue(m, l & 15, nn, tid < 256 && m < M && nn < N, s);
+        for (int w = 0; w < kWaves; ++w) s += sRed[w * 256 + o];
+        const int l = o >> 2, v = o & 3;
+        const int m = 4 * (l >> 4) + v;  // MFMA output row (x row)
+        const int l15 = l & 15;
+        const int64_t nn = tl * 16 + l15;
+        const int mc = m < M ? m : M - 1;
+        const uint32_t trow = P.sT + (uint32_t)(mc * r * 4), brow = P.sB + (uint32_t)(l15 * r * 2);
+        float lo = 0.0f;
+        for (int j = 8 * hh; j < r; j += 16) {
+          const u32x4_t t0 = lds_rd128(trow + 4u * j), t1 = lds_rd128(trow + 4u * j + 16u);
+          const u32x4_t bb = lds_rd128(brow + 2u * j);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            lo = fmaf(__uint_as_float(q < 2 ? t0[2 * q] : t1[2 * q - 4]), bf16_bits_to_f32(bb[q] & 0xFFFFu), lo);
+            lo = fmaf(__uint_as_float(q < 2 ? t0[2 * q + 1] : t1[2 * q - 3]), bf16_bits_to_f32(bb[q] >> 16), lo);
+          }
+        }
+        lo += __shfl_xor(lo, 1, 64);
+        const bool ov = hh == 0 && m < M && nn < N;
+        float out = fmaf(a.scale, lo, s);
+        if (a.addend && ov) out += a.addend[(int64_t)m * N + nn];
+        const uint32_t yo = buf_off(ov, (uint32_t)(((int64_t)m * N + nn) * ES));
+        if constexpr (YDT == DT_F32) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(out), yr, yo, 0, 0);
+        else __builtin_amdgcn_raw_buffer_store_b16((uint16_t)f32_to_bf16_bits(out), yr, yo, 0, 0);
+      } else {
+        const int o = tid & 255;
+        float s = 0.0f;
+#pragma unroll
+        for (int w = 0; w < kWaves; ++w) s += sRed[w * 256 + o];
+        const int l = o >> 2, v = o & 3;
+        const int m = 4 * (l >> 4) + v;  // MFMA output row (x row)
+        const int64_t nn = tl * 16 + (l & 15);
+        epilogue(m, l & 15, nn, tid < 256 && m < M && nn < N, s);
+      }
     }
     // the next tile reuses sRed and the B tile; after the workgroup's last tile
     // nothing is reused

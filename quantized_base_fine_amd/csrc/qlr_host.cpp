@@ -117,7 +117,7 @@ qlr_status check_qweight(const qlr_qweight* w) {
 // only on M and K (the bf16 count bounds the others).
 size_t linear_ws_bytes(int64_t M, int64_t K, int32_t r) {
   if (M <= 0 || r <= 0) return 0;
-  const size_t parts = (size_t)qlr::lora_t_splits(M, K, qlr::DT_BF16, qlr::DT_BF16);
+  const size_t parts = (size_t)qlr::lora_t_splits(M, K, r, qlr::DT_BF16, qlr::DT_BF16);
   return ((parts * (size_t)M * (size_t)r * sizeof(float)) + 255) & ~(size_t)255;
 }
 
@@ -133,8 +133,8 @@ BwdLayout bwd_layout(int64_t M, int64_t N, int64_t K, int32_t r) {
   if (r <= 0) return L;
   auto up = [](size_t b) { return (b + 255) & ~(size_t)255; };
   const size_t mr = (size_t)std::max<int64_t>(M, 0) * (size_t)r * sizeof(float);
-  const size_t st = M > 0 ? (size_t)qlr::lora_t_splits(M, K, qlr::DT_BF16, qlr::DT_BF16) : 0;
-  const size_t su = M > 0 ? (size_t)qlr::lora_t_splits(M, N, qlr::DT_BF16, qlr::DT_BF16) : 0;
+  const size_t st = M > 0 ? (size_t)qlr::lora_t_splits(M, K, r, qlr::DT_BF16, qlr::DT_BF16) : 0;
+  const size_t su = M > 0 ? (size_t)qlr::lora_t_splits(M, N, r, qlr::DT_BF16, qlr::DT_BF16) : 0;
   L.t = 0;
   L.u = L.t + up(st * mr);
   L.bt = L.u + up(su * mr);
@@ -238,7 +238,7 @@ qlr_status run_linear(const LinearCheck& c, float scale, char* ws, qlr_path path
                       const float* addend = nullptr, const qlr_sparse* sp = nullptr, int wht_lp = -1) {
   if (c.M == 0) return QLR_OK;
   hipError_t e = hipSuccess;
-  const int splits = qlr::lora_t_splits(c.M, c.w->cols, (int)c.xdt, (int)c.abdt);
+  const int splits = qlr::lora_t_splits(c.M, c.w->cols, c.r, (int)c.xdt, (int)c.abdt);
   qlr::LinearArgs a = make_args(c, scale, ws, splits);
   a.addend = addend;
   if (sp) {
@@ -484,7 +484,7 @@ qlr_status qlr_linear_fwd_mixed(const qlr_layer* layers, int32_t n, int64_t M, q
     char* wl = need_l > 0 ? wsp : nullptr;
     wsp += need_l;
     if (path == QLR_PATH_GEMM && M > 0) {
-      const int splits = qlr::lora_t_splits(M, L.w->cols, (int)xdt, (int)abdt);
+      const int splits = qlr::lora_t_splits(M, L.w->cols, L.r, (int)xdt, (int)abdt);
       if (L.r > 0) {
         if (M > 16 && xdt == QLR_BF16 && abdt == QLR_BF16) {
           tgroup.push_back(qlr::LoraTItem{L.x, L.A, reinterpret_cast<float*>(wl), L.w->cols, L.r, false});
@@ -593,8 +593,8 @@ qlr_status qlr_linear_bwd(const void* dy, qlr_dtype dydt, const void* x, qlr_dty
   char* wsp = reinterpret_cast<char*>(ws);
   float* tws = r > 0 ? reinterpret_cast<float*>(wsp + lay.t) : nullptr;
   float* uws = r > 0 ? reinterpret_cast<float*>(wsp + lay.u) : nullptr;
-  const int st_t = M > 0 ? qlr::lora_t_splits(M, K, (int)xdt, (int)abdt) : 1;
-  const int st_u = M > 0 ? qlr::lora_t_splits(M, N, (int)dydt, (int)abdt) : 1;
+  const int st_t = M > 0 ? qlr::lora_t_splits(M, K, r, (int)xdt, (int)abdt) : 1;
+  const int st_u = M > 0 ? qlr::lora_t_splits(M, N, r, (int)dydt, (int)abdt) : 1;
   hipError_t e = hipSuccess;
   if (r > 0 && M > 0) {
     if (M > 16 && xdt == QLR_BF16 && abdt == QLR_BF16 && N % 64 == 0 && r % 8 == 0) {
@@ -781,7 +781,7 @@ qlr_status qlr_linear_fwd_outliers(const void* x, qlr_dtype xdt, int64_t M, cons
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* wsp = reinterpret_cast<char*>(ws);
   // a single x row on the decode kernel: the side channel is summed inside it
-  const qlr::LinearArgs probe = make_args(c, scale, wsp, qlr::lora_t_splits(M, w->cols, (int)xdt, (int)abdt));
+  const qlr::LinearArgs probe = make_args(c, scale, wsp, qlr::lora_t_splits(M, w->cols, c.r, (int)xdt, (int)abdt));
   if (sp->nnz > 0 && path == QLR_PATH_GEMV && qlr::gemv_fuses_sparse(probe))
     return run_linear(c, scale, wsp, path, s, nullptr, sp);
   float* C = reinterpret_cast<float*>(wsp + linear_ws_bytes(M, w->cols, r));

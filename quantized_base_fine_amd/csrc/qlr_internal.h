@@ -22,12 +22,14 @@ hipError_t launch_dequantize(const uint8_t* codes, const uint8_t* q8, const floa
                              int64_t numel, int bits, const Levels& lv, void* out, int odt,
                              hipStream_t s);
 
-// Number of K-splits of the adapter product t = x A^T for M rows and K columns:
-// the product is written as `splits` partial sums p[s][M][r] (float32) that the
-// consumers add in split order.  K need not be a multiple of 64 (the backward's
-// u = dy B contracts over the weight's rows); such products run one split on
-// the float32 kernel.
-int lora_t_splits(int64_t M, int64_t K, int xdt, int abdt);
+// Number of K-splits of the adapter product t = x A^T for M rows, K columns and
+// rank r: the product is written as `splits` partial sums p[s][M][r] (float32)
+// that the consumers add in split order; splits * M * r <= kTPartsMax (the
+// decode kernel prefetches them all at once).  K need not be a multiple of 64
+// (the backward's u = dy B contracts over the weight's rows); such products run
+// one split on the float32 kernel.
+constexpr int kTPartsMax = 4096;
+int lora_t_splits(int64_t M, int64_t K, int r, int xdt, int abdt);
 
 // p[s][m][j] = sum over split s's K range of x[m,k] A[j,k]  (float32 partials).
 hipError_t launch_lora_t(const void* x, int xdt, int64_t M, int64_t K, const void* A, int abdt,

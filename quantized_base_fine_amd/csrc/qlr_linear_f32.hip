@@ -166,55 +166,54 @@ __global__ __launch_bounds__(256) void k_lora_t_tile(TGroup G) {
   if (m < M && j < r) t[m * r + j] = sum;
 }
 
-// bf16 x and A, M <= 16, through 16x16x32 bf16 MFMA with float32 accumulation.
-// blockIdx.x: 16-row tile of x; blockIdx.y: group of 64 adapter rows;
-// blockIdx.z: K split.  The 4 waves share the split's 32-wide K steps and are
-// reduced through LDS; the split's partial sum goes to p[z][m][j].
-__global__ __launch_bounds__(256) void k_lora_t_mfma(const uint16_t* __restrict__ x, int64_t M,
-                                                     int64_t K, const uint16_t* __restrict__ A,
-                                                     int r, float* __restrict__ p) {
-  __shared__ float sRed[4][4][256];
+// bf16 x and A, M <= 16 (one 16-row MFMA tile): K-split partial sums
+// p[s][m][j] of t = x A^T.  Workgroup (16 adapter rows j0 .. j0 + 15, split s)
+// of 16 waves: wave w takes the 32-column steps c0 + w, c0 + w + 16, ... of the
+// split, issues the loads of up to kLtSteps of them before any product (the
+// split count keeps a split within one such round for the decode shapes), and
+// multiplies on 16x16x32 bf16 MFMA (x rows as the A operand, adapter rows as
+// B).  The 16 waves' sums are added through LDS in wave order.
+constexpr int kLtWaves = 16, kLtSteps = 8;
+__global__ __launch_bounds__(kLtWaves * 64) void k_lora_t_small(const uint16_t* __restrict__ x, int64_t M,
+                                                               int64_t K, const uint16_t* __restrict__ A, int r,
+                                                               float* __restrict__ p) {
+  __shared__ float red[kLtWaves][256];
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = lane & 15, g = lane >> 4;
-  const int64_t m0 = (int64_t)blockIdx.x * 16;
-  const int j0 = blockIdx.y * 64;
-  const int S = gridDim.z, sidx = blockIdx.z;
-  const bool xv = m0 + row < M;
-  const uint16_t* xp = x + (xv ? (m0 + row) : 0) * K + g * 8;
-  const uint16_t* ap[4];
-  bool av[4];
-#pragma unroll
-  for (int jt = 0; jt < 4; ++jt) {
-    const int j = j0 + jt * 16 + row;
-    av[jt] = j < r;
-    ap[jt] = A + (int64_t)(av[jt] ? j : 0) * K + g * 8;
-  }
+  const int j0 = blockIdx.x * 16;
+  const int S = gridDim.y, sidx = blockIdx.y;
+  const bool xv = row < M, av = j0 + row < r;
+  const uint16_t* xp = x + (int64_t)(xv ? row : 0) * K + g * 8;
+  const uint16_t* ap = A + (int64_t)(av ? j0 + row : 0) * K + g * 8;
   const int64_t nsteps = K / 32;
   const int64_t c0 = nsteps * sidx / S, c1 = nsteps * (sidx + 1) / S;
-  f32x4_t acc[4] = {};
+  f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
   const u32x4_t zero = {0u, 0u, 0u, 0u};
-#pragma unroll 4
-  for (int64_t st = c0 + wave; st < c1; st += 4) {
-    const int64_t k = st * 32;
-    const u32x4_t xa = xv ? *reinterpret_cast<const u32x4_t*>(xp + k) : zero;
+  for (int64_t base = c0 + wave; base < c1; base += kLtWaves * kLtSteps) {
+    u32x4_t xa[kLtSteps], ab[kLtSteps];
 #pragma unroll
-    for (int jt = 0; jt < 4; ++jt) {
-      const u32x4_t ab = av[jt] ? *reinterpret_cast<const u32x4_t*>(ap[jt] + k) : zero;
-      acc[jt] = mfma16x16x32(as_bf16x8(xa), as_bf16x8(ab), acc[jt]);
+    for (int i = 0; i < kLtSteps; ++i) {
+      const int64_t st = base + (int64_t)i * kLtWaves;
+      const bool sv = st < c1;
+      const int64_t k = (sv ? st : c0) * 32;
+      xa[i] = (xv && sv) ? *reinterpret_cast<const u32x4_t*>(xp + k) : zero;
+      ab[i] = (av && sv) ? *reinterpret_cast<const u32x4_t*>(ap + k) : zero;
     }
+#pragma unroll
+    for (int i = 0; i < kLtSteps; ++i) acc = mfma16x16x32(as_bf16x8(xa[i]), as_bf16x8(ab[i]), acc);
   }
 #pragma unroll
-  for (int jt = 0; jt < 4; ++jt)
-#pragma unroll
-    for (int v = 0; v < 4; ++v) sRed[wave][jt][lane * 4 + v] = acc[jt][v];
+  for (int v = 0; v < 4; ++v) red[wave][lane * 4 + v] = acc[v];
   __syncthreads();
-  for (int idx = threadIdx.x; idx < 4 * 256; idx += 256) {
-    const int jt = idx >> 8, e = idx & 255;
-    const float s = (sRed[0][jt][e] + sRed[1][jt][e]) + (sRed[2][jt][e] + sRed[3][jt][e]);
+  if (threadIdx.x < 256) {
+    const int e = threadIdx.x;
+    float sum = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kLtWaves; ++w) sum += red[w][e];
     const int l = e >> 2, v = e & 3;
-    const int64_t m = m0 + 4 * (l >> 4) + v;  // MFMA output row
-    const int j = j0 + jt * 16 + (l & 15);     // MFMA output column
-    if (m < M && j < r) p[((int64_t)sidx * M + m) * r + j] = s;
+    const int m = 4 * (l >> 4) + v;  // MFMA output row (x row)
+    const int j = j0 + (l & 15);     // MFMA output column (adapter row)
+    if (m < M && j < r) p[((int64_t)sidx * M + m) * r + j] = sum;
   }
 }
 
@@ -292,11 +291,13 @@ hipError_t launch_f32_b1(const LinearArgs& a, const Levels& lv, hipStream_t s) {
 
 }  // namespace
 
-int lora_t_splits(int64_t M, int64_t K, int xdt, int abdt) {
+int lora_t_splits(int64_t M, int64_t K, int r, int xdt, int abdt) {
   if (!(xdt == DT_BF16 && abdt == DT_BF16) || M > 16 || K % 64 != 0) return 1;
-  const int64_t steps = K / 32, mtiles = (M + 15) / 16;
-  int64_t s = std::min<int64_t>(steps / 4, (256 + mtiles - 1) / mtiles);
-  s = std::min<int64_t>(s, 64);
+  // enough splits to spread A over the chip, few enough that a decode
+  // workgroup prefetches all partial sums in one round (kTPartsMax floats)
+  const int64_t steps = K / 32;
+  int64_t s = std::min<int64_t>(steps / 4, 64);
+  s = std::min<int64_t>(s, std::max<int64_t>(1, kTPartsMax / (M * std::max(r, 1))));
   return (int)std::max<int64_t>(s, 1);
 }
 
@@ -310,8 +311,9 @@ hipError_t launch_lora_t(const void* x, int xdt, int64_t M, int64_t K, const voi
     return launch_lora_t_group(&it, 1, M, s);
   }
   if (mfma) {
-    dim3 grid((unsigned)((M + 15) / 16), (unsigned)((r + 63) / 64), (unsigned)splits);
-    hipLaunchKernelGGL(k_lora_t_mfma, grid, dim3(256), 0, s, reinterpret_cast<const uint16_t*>(x), M,
+    if (M > 16 || splits < 1 || splits > 65535) return hipErrorInvalidValue;
+    dim3 grid((unsigned)((r + 15) / 16), (unsigned)splits);
+    hipLaunchKernelGGL(k_lora_t_small, grid, dim3(kLtWaves * 64), 0, s, reinterpret_cast<const uint16_t*>(x), M,
                        K, reinterpret_cast<const uint16_t*>(A), r, t);
     return hipGetLastError();
   }

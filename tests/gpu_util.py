@@ -58,6 +58,12 @@ def oracle_rows_dequant(W, wdtype, bits, rows):
     """float32 dequantized rows (len(rows), K) computed by the oracle alone."""
     N, K = W.shape
     qg = oracle_groups(W, wdtype, bits, groups_covering(K, rows, W.size))
+    return rows_from_groups(qg, K, bits, rows)
+
+
+def rows_from_groups(qg, K, bits, rows):
+    """float32 dequantized weight rows from the oracle's per-group quantization ``qg``
+    ({group: QuantizedWeight}) of the groups covering them."""
     per = BLOCK * GROUP
     out = np.empty((len(rows), K), dtype=np.float32)
     for i, n in enumerate(rows):

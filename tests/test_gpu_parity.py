@@ -122,17 +122,6 @@ def test_quantize_attn_full():
     assert np.array_equal(got.view(np.uint32), refd.view(np.uint32))
 
 
-@pytest.mark.parametrize("which", ["up", "down", "big65"])
-def test_quantize_large_sampled_groups(which):
-    """MLP and 65B-class weights: sampled double-quantization groups, bit-exact."""
-    lin = workloads.big65(1) if which == "big65" else workloads.mlp(which, 1)
-    qw = _gpu_quant(lin.W, "f16", 4)
-    ngroups = qw.absmax_c.numel()
-    rng = np.random.default_rng(5)
-    groups = sorted(set([0, ngroups - 1] + rng.choice(ngroups, size=24, replace=False).tolist()))
-    _assert_qweight_equal(qw, None, oracle_groups(lin.W, "f16", 4, groups))
-
-
 # ---------------------------------------------------------------- linear forward
 
 def _run_linear(lin, qw, ydt="f32", path=qlr.PATH_AUTO):
@@ -211,6 +200,7 @@ def test_linear_mlp_sampled(which):
     for M in (1, 16, 2048):
         lin = workloads.mlp(which, M, W=base.W)
         check_linear(_run_linear(lin, qw, "bf16"), lin, wd, rows, "bf16")
+        check_linear(_run_linear(lin, qw, "f32"), lin, wd, rows, "f32")
 
 
 def test_linear_big65_sampled():
@@ -224,6 +214,7 @@ def test_linear_big65_sampled():
         lin = workloads.big65(M, W=base.W)
         ms = sorted(set([0, M - 1] + rng.choice(M, size=min(M, 40), replace=False).tolist()))
         check_linear(_run_linear(lin, qw, "bf16"), lin, wd, rows, "bf16", ms=ms)
+        check_linear(_run_linear(lin, qw, "f32"), lin, wd, rows, "f32", ms=ms)
 
 
 def test_linear_edge_cases():

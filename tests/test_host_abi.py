@@ -56,6 +56,9 @@ def test_workspace_sizes():
     assert qlr.workspace_bytes(qlr.OP_LINEAR, 2048, 4096, 4096, 16) == 2048 * 16 * 4  # M > 16: one K pass
     assert qlr.workspace_bytes(qlr.OP_LINEAR, 1, 4096, 4096, 16) == 32 * 16 * 4
     assert qlr.workspace_bytes(qlr.OP_LINEAR, 3, 10, 64, 5) == 256
+    # splits x M x r <= 4096 (a decode workgroup prefetches every partial sum at once)
+    assert qlr.workspace_bytes(qlr.OP_LINEAR, 16, 4096, 11008, 64) == 4 * 16 * 64 * 4
+    assert qlr.workspace_bytes(qlr.OP_LINEAR, 1, 22016, 8192, 64) == 64 * 64 * 4
 
 
 def _status(fn, *args):

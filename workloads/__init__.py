@@ -260,3 +260,33 @@ def mixed_linear(i: int, M: int = 512, seed: int = 0, plan=None,
         N, K = shape_override
     return make_linear(f"mixed_{i}", 4, N, K, M, sigma=0.02, wdtype="f16", bits=bits, r=r,
                        alpha=16.0, abdtype="bf16", xdtype="bf16", sub=1000 + i, seed=seed)
+
+
+# ---------------------------------------------------------------- inputs drawn on the GPU
+
+def device_normal(shape, sigma: float, dtype, device, cfg: int, *ids: int, seed: int = 0):
+    """N(0, sigma^2) drawn on the GPU by torch's seeded generator, in float32, scaled by sigma in
+    float32 and cast to ``dtype`` (a torch dtype).  For inputs too large to draw on the host in
+    reasonable time (the full mixed stack): the seed is a function of (seed, cfg, *ids) only, so a
+    draw is reproducible; it is a different sample than ``normal`` draws for the same ids."""
+    import torch
+    state = np.random.SeedSequence([seed, cfg, *ids]).generate_state(2, dtype=np.uint32)
+    gen = torch.Generator(device=device)
+    gen.manual_seed(int(state[0]) << 32 | int(state[1]))
+    z = torch.randn(shape, generator=gen, device=device, dtype=torch.float32)
+    return (z * np.float32(sigma)).to(dtype)
+
+
+def device_mixed_linear(i: int, M: int, device, plan=None, seed: int = 0):
+    """Linear number ``i`` of the mixed stack with its inputs drawn on the GPU (``device_normal``):
+    returns (N, K, bits, r, alpha, W fp16, x bf16, A bf16, B bf16) with the distributions of
+    ``mixed_linear`` (W N(0, 0.02^2), A N(0, 1/K), B N(0, 0.01^2), x N(0, 1), alpha 16)."""
+    import torch
+    plan = plan or mixed_plan(seed)
+    N, K, bits, r = plan[i]
+    sub = 1000 + i
+    W = device_normal((N, K), 0.02, torch.float16, device, 4, T_W, sub, seed=seed)
+    x = device_normal((M, K), 1.0, torch.bfloat16, device, 4, T_X, sub, M, seed=seed)
+    A = device_normal((r, K), float(np.sqrt(1.0 / K)), torch.bfloat16, device, 4, T_A, sub, seed=seed)
+    B = device_normal((N, r), 0.01, torch.bfloat16, device, 4, T_B, sub, seed=seed)
+    return N, K, bits, r, 16.0, W, x, A, B
