@@ -258,6 +258,25 @@ qlr_status qlr_linear_fwd(const void* x, qlr_dtype xdt, int64_t M, const qlr_qwe
                           void* y, qlr_dtype ydt, void* ws, size_t ws_bytes, void* stream);
 
 /*
+ * For callers that cannot allocate device memory or pass a workspace (code
+ * under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc): qlr_linear_fwd without the workspace arguments, same arguments
+ * otherwise, same kernels and results.  Its scratch (the adapter product's
+ * float32 partial sums) is a file-scope device array of
+ * QLR_STATIC_SCRATCH_BYTES on each GPU the library runs on, held until the
+ * process ends; the call allocates nothing.  A call whose
+ * qlr_workspace_bytes(QLR_OP_LINEAR, M, rows, cols, r) exceeds that size fails
+ * with QLR_ERR_WORKSPACE (nothing launched).  Every call on one GPU shares that
+ * GPU's array and leaves its contents behind: calls that overlap in time on one
+ * GPU (different streams or host threads) race and give wrong results.  The
+ * kernels need no initial contents.  Asynchronous.  Errors: as qlr_linear_fwd.
+ */
+#define QLR_STATIC_SCRATCH_BYTES (8u << 20)
+qlr_status qlr_linear_fwd_static(const void* x, qlr_dtype xdt, int64_t M, const qlr_qweight* w,
+                                 const void* A, const void* B, qlr_dtype abdt, int32_t r, float scale,
+                                 void* y, qlr_dtype ydt, void* stream);
+
+/*
  * Mixed stack (AutoQRA page, section 3.1: each layer has its own bit width
  * and rank).  `layers` (host array of n entries) are independent linears, all
  * with the same M and dtypes, each computed as qlr_linear_fwd would.  No y

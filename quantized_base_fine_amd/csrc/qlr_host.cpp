@@ -290,6 +290,54 @@ qlr_status quantize_common(const void* W, qlr_dtype wdt, int64_t rows, int64_t c
 
 }  // namespace
 
+// ---------------------------------------------------------------- allocation-free forward scratch
+//
+// The scratch of qlr_linear_fwd_static (the adapter product's float32 partial
+// sums): one array per GPU, allocated with the code object when the library is
+// first used on that GPU and held until the process ends.  Host code never uses
+// the array's name as an address: the device address comes from
+// hipGetSymbolAddress, once per device with that device current, and is kept
+// per device.
+static __device__ __align__(256) unsigned char scratch[QLR_STATIC_SCRATCH_BYTES];
+
+namespace {
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the device that owns `stream`.
+qlr_status scratch_for_stream(hipStream_t stream, void** out) {
+  int cur = 0;
+  hipError_t e = hipGetDevice(&cur);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  int dev = cur;
+  if (stream != nullptr) {
+    hipDevice_t d = 0;
+    e = hipStreamGetDevice(stream, &d);
+    if (e != hipSuccess) return hip_fail(e, "hipStreamGetDevice");
+    dev = (int)d;
+  }
+  if (dev < 0 || dev >= kMaxDevices) return fail(QLR_ERR_HIP, "device %d out of range", dev);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    if (dev != cur && (e = hipSetDevice(dev)) != hipSuccess) return hip_fail(e, "hipSetDevice");
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (dev != cur) {
+      const hipError_t e2 = hipSetDevice(cur);
+      if (e == hipSuccess && e2 != hipSuccess) return hip_fail(e2, "hipSetDevice");
+    }
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (p == nullptr) return fail(QLR_ERR_HIP, "hipGetSymbolAddress(scratch) gave a null address");
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return QLR_OK;
+}
+
+}  // namespace
+
 extern "C" {
 
 int qlr_version(void) { return 100; }
@@ -427,6 +475,29 @@ qlr_status qlr_linear_fwd(const void* x, qlr_dtype xdt, int64_t M, const qlr_qwe
   st = pick_path(M, xdt, abdt, r, &path);
   if (st != QLR_OK) return st;
   return run_linear(c, scale, reinterpret_cast<char*>(ws), path, reinterpret_cast<hipStream_t>(stream));
+}
+
+qlr_status qlr_linear_fwd_static(const void* x, qlr_dtype xdt, int64_t M, const qlr_qweight* w, const void* A,
+                                 const void* B, qlr_dtype abdt, int32_t r, float scale, void* y, qlr_dtype ydt,
+                                 void* stream) {
+  const LinearCheck c{x, xdt, M, w, A, B, abdt, r, y, ydt};
+  qlr_status st = check_linear(c);
+  if (st != QLR_OK) return st;
+  const size_t need = linear_ws_bytes(M, w->cols, r);
+  if (need > (size_t)QLR_STATIC_SCRATCH_BYTES)
+    return fail(QLR_ERR_WORKSPACE, "the call needs %zu bytes of scratch; the static area holds %zu (use qlr_linear_fwd)",
+                need, (size_t)QLR_STATIC_SCRATCH_BYTES);
+  qlr_path path;
+  st = pick_path(M, xdt, abdt, r, &path);
+  if (st != QLR_OK) return st;
+  if (M == 0) return QLR_OK;
+  hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  void* ws = nullptr;
+  if (need > 0) {
+    st = scratch_for_stream(s, &ws);
+    if (st != QLR_OK) return st;
+  }
+  return run_linear(c, scale, reinterpret_cast<char*>(ws), path, s);
 }
 
 qlr_status qlr_linear_fwd_mixed(const qlr_layer* layers, int32_t n, int64_t M, qlr_dtype xdt, qlr_dtype abdt,

@@ -88,6 +88,9 @@ EXPORTS = {
     "qlr_linear_fwd": (C.c_int, [C.c_void_p, C.c_int, C.c_int64, C.POINTER(CQWeight),
                                  C.c_void_p, C.c_void_p, C.c_int, C.c_int32, C.c_float,
                                  C.c_void_p, C.c_int, C.c_void_p, C.c_size_t, C.c_void_p]),
+    "qlr_linear_fwd_static": (C.c_int, [C.c_void_p, C.c_int, C.c_int64, C.POINTER(CQWeight),
+                                        C.c_void_p, C.c_void_p, C.c_int, C.c_int32, C.c_float,
+                                        C.c_void_p, C.c_int, C.c_void_p]),
     "qlr_linear_fwd_mixed": (C.c_int, [C.POINTER(CLayer), C.c_int32, C.c_int64, C.c_int, C.c_int,
                                        C.c_int, C.c_void_p, C.c_size_t, C.c_void_p]),
     "qlr_linear_bwd": (C.c_int, [C.c_void_p, C.c_int, C.c_void_p, C.c_int, C.c_int64,
@@ -280,6 +283,29 @@ def linear(x, qw: QWeight, A=None, B=None, scale: float = 0.0, out_dtype=None, o
     check(lib().qlr_linear_fwd(x.data_ptr(), _dt(x), M, C.byref(cw), _ptr(A), _ptr(B), abdt, r,
                                float(scale), y.data_ptr(), _dt(y), _ptr(ws),
                                0 if ws is None else ws.numel(), _stream(x.device)))
+    return y
+
+
+STATIC_SCRATCH_BYTES = 8 << 20
+
+
+def linear_static(x, qw: QWeight, A=None, B=None, scale: float = 0.0, out_dtype=None, out=None):
+    """``linear`` through qlr_linear_fwd_static: no workspace (the library's static per-GPU
+    scratch of STATIC_SCRATCH_BYTES), nothing allocated by the library.  ``out`` avoids
+    the output allocation too."""
+    torch = _torch()
+    _require_cuda(x, A, B)
+    M = x.shape[0]
+    r = 0 if A is None else A.shape[0]
+    if x.shape[1] != qw.cols:
+        raise ValueError("x columns must equal the weight's cols")
+    if r > 0 and (A.shape != (r, qw.cols) or B.shape != (qw.rows, r) or A.dtype != B.dtype):
+        raise ValueError("A must be (r, K) and B (N, r) with one dtype")
+    y = out if out is not None else torch.empty((M, qw.rows), dtype=out_dtype or x.dtype, device=x.device)
+    abdt = _dt(A) if r > 0 else QLR_BF16
+    cw = qw.c_struct()
+    check(lib().qlr_linear_fwd_static(x.data_ptr(), _dt(x), M, C.byref(cw), _ptr(A), _ptr(B), abdt, r,
+                                      float(scale), y.data_ptr(), _dt(y), _stream(x.device)))
     return y
 
 

@@ -298,3 +298,17 @@ def test_wha_validation_and_workspace():
     # workspace: the M x N float32 branch term
     assert qlr.workspace_bytes(qlr.OP_LINEAR_WHA, 2048, 4096, 4096) == 2048 * 4096 * 4
     assert qlr.workspace_bytes(qlr.OP_LINEAR_WHA, 1, 4096, 4096) == 4096 * 4
+
+
+def test_static_forward_rejects_oversized_calls():
+    """qlr_linear_fwd_static refuses, before touching a device, a call whose scratch exceeds its static
+    area (the pointers are never dereferenced: the size check comes first)."""
+    lib = qlr.lib()
+    fake = 1 << 20  # a 16-byte aligned non-null address
+    cw = qlr.CQWeight(qlr.FORMAT_VERSION, 4, qlr.BLOCK, qlr.GROUP, 4096, 4096, fake, fake, fake)
+    M, r = 20000, 128
+    assert qlr.workspace_bytes(qlr.OP_LINEAR, M, 4096, 4096, r) > qlr.STATIC_SCRATCH_BYTES
+    st = lib.qlr_linear_fwd_static(fake, qlr.QLR_BF16, M, C.byref(cw), fake, fake, qlr.QLR_BF16, r, 0.125, fake,
+                                   qlr.QLR_BF16, None)
+    assert qlr.STATUS[st] == "QLR_ERR_WORKSPACE"
+    assert b"static area" in lib.qlr_last_error()
