@@ -247,6 +247,37 @@ def decode_by_bits(torch, qlr, W, x1, A0, B0, scale, dev, reps=5):
 
 
 
+class _YCall:
+    """A prepared mixed call seen as one call with one output tensor (its outputs concatenated
+    for the graph-replay check)."""
+
+    def __init__(self, mc):
+        self.mc = mc
+        self.y = None
+
+    def __call__(self):
+        ys = self.mc()
+        if self.y is None:
+            self.y = _Cat(ys)
+        return ys
+
+
+class _Cat:
+    def __init__(self, ys):
+        self.ys = ys
+
+    def clone(self):
+        return [y.clone() for y in self.ys]
+
+    def zero_(self):
+        for y in self.ys:
+            y.zero_()
+
+    def equal(self, ref):
+        import torch
+        return all(torch.equal(a, b) for a, b in zip(self.ys, ref))
+
+
 def time_sequence(torch, calls, stream, graph: bool, reps: int = 5):
     """Median over reps of the time of the calls back to back (a HIP graph of them when
     `graph`, checked against the eager outputs first), per call, in us."""
@@ -264,7 +295,8 @@ def time_sequence(torch, calls, stream, graph: bool, reps: int = 5):
             c.y.zero_()
         g.replay()
         torch.cuda.synchronize()
-        assert all(torch.equal(c.y, r0) for c, r0 in zip(calls, ref)), "graph replay differs from eager"
+        assert all((c.y.equal(r0) if isinstance(c.y, _Cat) else torch.equal(c.y, r0))
+                   for c, r0 in zip(calls, ref)), "graph replay differs from eager"
         run = g.replay
     else:
         def run():
@@ -351,25 +383,23 @@ def bench_configs(torch, qlr, workloads, dev, stream, only=None, graph=True):
 
 def build_mixed(torch, qlr, workloads, dev):
     """The mixed stack at full size: 32 layers x 7 independent linears with per-linear
-    (bits, rank) drawn by the stack's seed, M = 512.  Weights, x and adapters are drawn
-    on the GPU from a seeded generator with the same distributions as the parity
-    workloads (W N(0, 0.02^2) fp16, A N(0, 1/K), B N(0, 0.01^2) bf16, x N(0, 1) bf16) and
-    quantized once.  Returns the prepared call and its algorithmic flops."""
-    import math
-    gen = torch.Generator(device=dev)
-    gen.manual_seed(4)
+    (bits, rank) drawn by the stack's seed, M = 512, inputs drawn on the GPU by the seeded
+    generator the full-size parity test uses (W N(0, 0.02^2) fp16, A N(0, 1/K),
+    B N(0, 0.01^2) bf16, x N(0, 1) bf16), quantized once.  Returns the prepared M = 512
+    call, its flops, the prepared decode call (the same layers at M = 1: each x's first
+    row) and its algorithmic bytes."""
     qws = torch.empty(qlr.workspace_bytes(qlr.OP_QUANTIZE), dtype=torch.uint8, device=dev)
-    entries, flops = [], 0
-    for N, K, b, r in workloads.mixed_plan():
-        W = (torch.randn((N, K), generator=gen, device=dev) * 0.02).to(torch.float16)
+    plan = workloads.mixed_plan()
+    entries, flops, dbytes = [], 0, 0
+    for i, (N, K, b, r) in enumerate(plan):
+        N, K, b, r, alpha, W, x, A, B = workloads.device_mixed_linear(i, MIXED_M, dev, plan)
         qw = qlr.quantize(W, b, ws=qws)
         del W
-        x = torch.randn((MIXED_M, K), generator=gen, device=dev).to(torch.bfloat16)
-        A = (torch.randn((r, K), generator=gen, device=dev) / math.sqrt(K)).to(torch.bfloat16)
-        B = (torch.randn((N, r), generator=gen, device=dev) * 0.01).to(torch.bfloat16)
-        entries.append(dict(x=x, qw=qw, A=A, B=B, scale=16.0 / r))
+        entries.append(dict(x=x, qw=qw, A=A, B=B, scale=alpha / r))
         flops += 2 * MIXED_M * N * K + 2 * MIXED_M * r * (K + N)
-    return qlr.MixedCall(entries, out_dtype=torch.bfloat16), flops, len(entries)
+        dbytes += decode_bytes(M=1, N=N, K=K, b=b, r=r)
+    dec = qlr.MixedCall([dict(e, x=e["x"][:1]) for e in entries], out_dtype=torch.bfloat16)
+    return qlr.MixedCall(entries, out_dtype=torch.bfloat16), flops, len(entries), dec, dbytes
 
 
 def single_call_latency(torch, layer, stream, reps: int = 25):
@@ -462,6 +492,8 @@ def main():
     ap.add_argument("--eager", action="store_true",
                     help="no HIP graphs (every launch visible to per-dispatch counter collection)")
     ap.add_argument("--no-configs", action="store_true", help="skip the MLP and 65B workloads")
+    ap.add_argument("--mixed-only", action="store_true",
+                    help="time only the mixed stack (M = 512 eagerly, then M = 1 as a graph unless --eager) and exit")
     ap.add_argument("--config-only", choices=sorted(CONFIGS),
                     help="time only this workload (decode and prefill; eager when --eager) and exit")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
@@ -486,6 +518,19 @@ def main():
     # One stream of our own carries every call; prepared calls bind to it and the
     # graphs are captured on it.
     torch.cuda.set_stream(torch.cuda.Stream(dev))
+    if args.mixed_only:
+        st = torch.cuda.current_stream(dev)
+        mc, fl, n, dec, dbytes = build_mixed(torch, qlr, workloads, dev)
+        res = {"linears": n}
+        for name, call, graph in (("M512", mc, False), ("M1", dec, not args.eager)):
+            us = time_sequence(torch, [_YCall(call)], st, graph=graph, reps=3)
+            res[name] = {"us_per_call": round(us, 2)}
+            if name == "M512":
+                res[name]["tflops"] = round(fl / (us * 1e-6) / 1e12, 1)
+            else:
+                res[name]["gbs"] = round(dbytes / (us * 1e-6) / 1e9, 1)
+        print(json.dumps(res))
+        return
     if args.config_only:
         if args.copy_calibration:
             src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
@@ -602,7 +647,7 @@ def main():
         PHASES = PHASES[:6]
     mixed = None
     if not args.no_mixed:
-        mixed, mixed_flops, mixed_n = build_mixed(torch, qlr, workloads, dev)
+        mixed, mixed_flops, mixed_n, mixed_dec, mixed_dec_bytes = build_mixed(torch, qlr, workloads, dev)
         mixed()
         torch.cuda.synchronize()
 
@@ -790,6 +835,15 @@ def main():
         out["decode_by_bits"] = decode_by_bits(torch, qlr, W, x1, A0, B0, lin1.scale, dev)
     if not args.no_configs and not args.eager:
         out["configs"] = bench_configs(torch, qlr, workloads, dev, stream)
+    if mixed is not None and not args.eager:
+        # the stack at decode size: one mixed call per replay of a HIP graph, checked against eager first
+        dec_us = time_sequence(torch, [_YCall(mixed_dec)], stream, graph=True)
+        out["mixed_decode"] = {
+            "workload": "the mixed stack at M=1 (each linear's first x row), one qlr_linear_fwd_mixed call",
+            "bytes_per_call": mixed_dec_bytes, "us_per_call": round(dec_us, 2),
+            "gbs": round(mixed_dec_bytes / (dec_us * 1e-6) / 1e9, 1),
+            "frac": round(mixed_dec_bytes / (dec_us * 1e-6) / 1e9 / HBM_PEAK_GBS, 4),
+        }
     if mixed is not None:
         mixed_ms = phase_ms["mixed"] / S
         mixed_tfs = mixed_flops / (mixed_ms * 1e-3) / 1e12

@@ -321,7 +321,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
   float* sT = reinterpret_cast<float*>(reinterpret_cast<char*>(smem) + P.sT);
 
   const int tid = threadIdx.x;
-  const int lane = tid & 63, wave = tid >> 6;
+  // (the wave index is uniform within a wave: saying so keeps the chunk loops scalar)
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nl = lane & 15, g = lane >> 4;
   const uint32_t tlane = table_lane<BITS>(lane);
   const int64_t kb0 = nb * wave / kWaves, kb1 = nb * (wave + 1) / kWaves;
@@ -342,40 +343,54 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
   // scale-loading lane: (row lane / 4, block lane % 4) of a chunk
   const int srow = lane >> 2, sblk = lane & 3;
 
-  // Offsets are formed in 32 bits (every valid one is below 2^31; invalid ones
-  // are replaced by kOOB).
+  // Byte offsets of this lane's loads at chunk 0 of tile blockIdx.x, formed
+  // once; chunk c of a tile adds c * CH blocks, each later tile of the
+  // workgroup gridDim.x * 16 rows (32-bit adds only).  Rows past N, and the
+  // tiles past the last that the ring loads ahead, lie past the end of the
+  // buffer resources and read zero, or (offsets wrapping past 2^32) bytes of
+  // other rows: either way only sums that are never stored see them, so the
+  // loads need no bounds test.  Blocks past the wave's K range are read and not
+  // added.
   const uint32_t nb32 = (uint32_t)nb;
-  auto load_chunk = [&](int64_t tile, int c, Ch& ch) {
-    const bool tv = tile < P.ntiles;
-    const int64_t kbs = kb0 + (int64_t)c * CH;
-    const uint32_t row0 = (uint32_t)tile * 16u, kbs32 = (uint32_t)kbs;
+  const uint32_t kb032 = (uint32_t)kb0;
+  const uint32_t rowb = nb32 * (8u * BITS);  // code bytes per weight row
+  const uint32_t row_first = (uint32_t)blockIdx.x * 16u;
+  uint32_t coff0[G::NP];
+#pragma unroll
+  for (int i = 0; i < G::NP; ++i) {
+    const int p = i * 64 + lane;
+    coff0[i] = (row_first + (uint32_t)(p / G::PR)) * rowb + kb032 * (8u * BITS) + (uint32_t)((p % G::PR) * G::PB);
+  }
+  const uint32_t qoff0 = (row_first + (uint32_t)srow) * nb32 + kb032 + (uint32_t)sblk;
+  const uint32_t tstep_c = (uint32_t)gridDim.x * 16u * rowb, tstep_q = (uint32_t)gridDim.x * 16u * nb32;
+  // load cursor: its tile, chunk, and the tile's offset from tile blockIdx.x
+  int64_t ltile = blockIdx.x;
+  int lc = 0;
+  uint32_t lct = 0, lqt = 0;
+  auto load_chunk = [&](Ch& ch) {
+    const int c = lc;
+    const uint32_t cb = (uint32_t)c * (uint32_t)CH;
     // code pieces: piece p -> row p / PR, byte (p % PR) * PB of the chunk row
 #pragma unroll
     for (int i = 0; i < G::NP; ++i) {
-      const int p = i * 64 + lane;
-      const int row = p / G::PR, col = p % G::PR;
-      // (the pin keeps the multiply-add in 32 bits: a fused 64-bit form reads
-      // a register pair whose unused high half may be a load in flight)
-      uint32_t blkb = ((row0 + (uint32_t)row) * nb32 + kbs32) * (8u * BITS);
-      asm volatile("" : "+v"(blkb));
-      const uint32_t off = blkb + (uint32_t)(col * G::PB);
-      const uint32_t o32 = buf_off(tv && tile * 16 + row < N, off);
+      uint32_t off = coff0[i] + lct + cb * (8u * BITS);
+      asm volatile("" : "+v"(off));
       if constexpr (G::PB == 16) {
-        ch.piece[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(cr, o32, 0, 0));
+        ch.piece[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(cr, off, 0, 0));
       } else {
-        ch.piece[i] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(cr, o32, 0, 0));
+        ch.piece[i] = __builtin_bit_cast(u32x2_t, __builtin_amdgcn_raw_buffer_load_b64(cr, off, 0, 0));
       }
     }
     // absmax code and group constant of (row srow, block kbs + sblk)
     {
-      const int64_t n = tile * 16 + srow, kb = kbs + sblk;
-      const uint32_t blk = (row0 + (uint32_t)srow) * nb32 + kbs32 + (uint32_t)sblk;
-      const bool sv = tv && n < N && kb < nb;
-      ch.q8 = __builtin_amdgcn_raw_buffer_load_b8(qr, buf_off(sv, blk), 0, 0);
-      ch.sc = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(sr, buf_off(sv, (blk >> 8) * 4u), 0, 0));
+      uint32_t blk = qoff0 + lqt + cb;
+      asm volatile("" : "+v"(blk));
+      ch.q8 = __builtin_amdgcn_raw_buffer_load_b8(qr, blk, 0, 0);
+      ch.sc = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(sr, (blk >> 8) << 2, 0, 0));
     }
     // x fragments of the chunk's blocks (clamped into the row; unused past kb1)
     if constexpr (!XLDS) {
+      const int64_t kbs = kb0 + (int64_t)c * CH;
 #pragma unroll
       for (int u = 0; u < CH; ++u) {
         const int64_t kb = min(kbs + u, nb - 1);
@@ -386,10 +401,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
     // the tile's B rows (16 x r bf16, contiguous): piece wave * 64 + lane
     if constexpr (ADP) {
       const int pc = wave * 64 + lane;
-      const bool bv = !DBA && (TF || P.bpre) && tv && c == nitem - 1 && pc < 2 * r;
+      const bool bv = !DBA && (TF || P.bpre) && ltile < P.ntiles && c == nitem - 1 && pc < 2 * r;
       const __amdgpu_buffer_rsrc_t brs = rsrc(a.B, N * r * 2);
       ch.bp = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                              brs, buf_off(bv, row0 * (uint32_t)(2 * r) + (uint32_t)pc * 16u), 0, 0));
+                                              brs, buf_off(bv, (uint32_t)ltile * (uint32_t)(32 * r) + (uint32_t)pc * 16u),
+                                              0, 0));
+    }
+    if (++lc == nitem) {
+      lc = 0;
+      ltile += gridDim.x;
+      lct += tstep_c;
+      lqt += tstep_q;
     }
   };
 
@@ -465,13 +487,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
 
   // the first D chunks of this wave's stream (tiles blockIdx.x, + gridDim.x, ...)
   Ch ring[D];
-  int64_t ltile = blockIdx.x;
-  int lc = 0;
 #pragma unroll
-  for (int s = 0; s < D; ++s) {
-    load_chunk(ltile, lc, ring[s]);
-    if (++lc == nitem) { lc = 0; ltile += gridDim.x; }
-  }
+  for (int s = 0; s < D; ++s) load_chunk(ring[s]);
 
   if constexpr (SPX == 2) {
     // Transform of the x row in blocks of P = 2^lp columns, float32 at sW
@@ -1058,8 +1075,301 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
 #pragma unroll
       for (int s = 0; s < D; ++s) {
         consume(s, j0 + s);
-        load_chunk(ltile, lc, ring[s]);
-        if (++lc == nitem) { lc = 0; ltile += gridDim.x; }
+        load_chunk(ring[s]);
+      }
+    }
+  }
+}
+
+// Geometry of the grouped single-row kernel: 16-byte pieces of whole codes, and
+// for 3-bit codes 12-byte pieces (32 codes; a 24-byte block is two of them,
+// 4-byte aligned), 8 lanes per 96-byte chunk row.
+typedef uint32_t u32x3_t __attribute__((ext_vector_type(3)));
+template <int BITS>
+struct DotGeo {
+  static constexpr int kRowBytes = CH * 8 * BITS;
+  static constexpr int PB = (BITS == 3) ? 12 : 16;
+  static constexpr int PR = kRowBytes / PB;       // pieces per chunk row
+  static constexpr int NP = (16 * PR + 63) / 64;  // pieces per lane
+  static constexpr int CP = PB * 8 / BITS;        // codes per piece
+  typedef typename std::conditional<BITS == 3, u32x3_t, u32x4_t>::type Piece;
+};
+template <int BITS>
+struct DChunk {
+  typename DotGeo<BITS>::Piece piece[DotGeo<BITS>::NP];
+  uint32_t q8;
+  float sc;
+  u32x4_t bp;
+};
+
+// dot_piece for a 12-byte piece of 32 3-bit codes: pair p (codes 2p, 2p + 1)
+// is the 6-bit field at bits [6p, 6p + 6), an index of the 64-entry table; the
+// fields of pairs 5 and 10 straddle a word boundary (funnel shift).
+__device__ __forceinline__ float dot_piece3(const u32x3_t& pc, const u32x4_t* xv, uint32_t tl) {
+  float s0 = 0.0f, s1 = 0.0f, t0 = 0.0f, t1 = 0.0f;
+#pragma unroll
+  for (int p = 0; p < 16; ++p) {
+    const int bit = 6 * p, w = bit >> 5, sh = bit & 31;
+    uint32_t e;
+    if (sh <= 26) e = (pc[w] >> sh) & 63u;
+    else e = __builtin_amdgcn_alignbit(pc[w + 1], pc[w], (uint32_t)sh) & 63u;
+    const u32x2v_t en = lds_entry((e << 8) | tl);
+    const uint32_t xp = xv[p >> 2][p & 3];
+    if (p & 1) {
+      s1 = dot2(en.x, xp, s1);
+      t1 = dot2(en.y, xp, t1);
+    } else {
+      s0 = dot2(en.x, xp, s0);
+      t0 = dot2(en.y, xp, t0);
+    }
+  }
+  return (s0 + s1) + (t0 + t1);
+}
+
+// ---------------------------------------------------------------- grouped single-row decode
+//
+// Up to kGvGroupMax independent linears of one code width at M = 1 in one
+// launch (a mixed stack's decode; AutoQRA page, section 3.1: each layer has its
+// own bits and rank).  The work units are the layers' 16-row tiles, each costing
+// its layer's blocks per row; workgroup b takes the contiguous run of units
+// whose start cost lies in [b C / G, (b + 1) C / G) (C the group's total), so
+// the workgroups stream about the same number of bytes and each crosses only a
+// few layer boundaries.  Within a layer it is the single-row path of k_gemv:
+// when a workgroup enters a layer it issues that layer's first chunks, then
+// stages the x row (and the adapter product, summed over its splits) in LDS;
+// the 8 waves split K, each keeps a ring of D chunks in flight (never past its
+// run: loads beyond it read nothing), and every tile ends with the cross-wave
+// reduction and the epilogue (adapter term spread over the threads).
+constexpr int kGvGroupMax = 16;
+struct GvLayer {
+  const uint16_t* x;     // 1 x K bf16
+  const uint8_t* codes;
+  const uint8_t* q8;
+  const float* cst;
+  const float* t;        // t_splits x r float32 partial sums of x A^T (r > 0)
+  const uint16_t* B;     // N x r bf16
+  void* y;               // 1 x N
+  int32_t N, nb, r, t_splits;
+  float scale;
+  int32_t ntiles;
+  int64_t cost0;         // units before this layer: sum of ntiles x nb
+};
+struct GvParams {
+  int32_t nl;
+  int64_t total;
+  uint32_t sT, sTP, sB, sX;  // LDS byte addresses: summed t, its partials, the tile's B rows, the x row
+  GvLayer L[kGvGroupMax];
+};
+
+template <int BITS, int YDT, bool ADP, int D>
+__global__ __launch_bounds__(kThreads, 1) void k_gemv_group(GvParams P, Levels lv) {
+  using G = DotGeo<BITS>;
+  using Ch = DChunk<BITS>;
+  constexpr uint32_t kStageW = 16 * CH * 4;
+  constexpr int ES = (YDT == DT_F32) ? 4 : 2;
+  constexpr int CP = G::CP;      // codes per piece
+  constexpr int PPB = 64 / CP;   // pieces per block
+  extern __shared__ uint32_t smem[];
+  const int tid = threadIdx.x;
+  // (the wave index is uniform within a wave: saying so keeps the chunk loops scalar)
+  const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const uint32_t tlane = table_lane<BITS>(lane);
+  const uint32_t stage0 = (uint32_t)PairTable<BITS>::kBytes;
+  float* sRed = reinterpret_cast<float*>(reinterpret_cast<char*>(smem) + stage0 + kWaves * 2 * kStageW);
+  const float* sT = reinterpret_cast<const float*>(reinterpret_cast<const char*>(smem) + P.sT);
+  const uint32_t wstage = stage0 + (uint32_t)wave * 2 * kStageW;
+  const int srow = lane >> 2, sblk = lane & 3;
+  build_table_kernarg<BITS>(smem, lv, tid);  // complete at the first segment's barrier
+  const int64_t c_begin = P.total * blockIdx.x / gridDim.x, c_end = P.total * (blockIdx.x + 1) / gridDim.x;
+  for (int l = 0; l < P.nl; ++l) {
+    const GvLayer& L = P.L[l];
+    const int64_t nb = L.nb, lo = c_begin - L.cost0, hi = c_end - L.cost0;
+    if (hi <= 0 || lo >= (int64_t)L.ntiles * nb) continue;
+    // the units u of this layer whose start cost u nb lies in [lo, hi)
+    const int32_t t0 = (int32_t)(lo <= 0 ? 0 : (lo + nb - 1) / nb);
+    const int32_t t1 = (int32_t)min<int64_t>(L.ntiles, (hi + nb - 1) / nb);
+    if (t0 >= t1) continue;
+    const int64_t N = L.N, K = nb * 64;
+    const int r = ADP ? L.r : 0;
+    const int64_t kb0 = nb * wave / kWaves, kb1 = nb * (wave + 1) / kWaves;
+    const int nchunk = (int)((kb1 - kb0 + CH - 1) / CH);
+    const int nitem = nchunk > 0 ? nchunk : 1;
+    const int64_t total = (int64_t)(t1 - t0) * nitem;
+    const __amdgpu_buffer_rsrc_t cr = rsrc(L.codes, N * nb * 8 * BITS);
+    const __amdgpu_buffer_rsrc_t qr = rsrc(L.q8, N * nb);
+    const __amdgpu_buffer_rsrc_t sr = rsrc(L.cst, ((N * nb + 255) >> 8) * 4);
+    const __amdgpu_buffer_rsrc_t brs = rsrc(L.B, ADP ? N * r * 2 : 0);
+    const __amdgpu_buffer_rsrc_t yr = rsrc(L.y, N * ES);
+    const uint32_t nb32 = (uint32_t)nb, kb032 = (uint32_t)kb0;
+    const uint32_t rowb = nb32 * (8u * BITS);
+    uint32_t coff0[G::NP];
+#pragma unroll
+    for (int i = 0; i < G::NP; ++i) {
+      const int p = i * 64 + lane;
+      coff0[i] = ((uint32_t)t0 * 16u + (uint32_t)(p / G::PR)) * rowb + kb032 * (8u * BITS) +
+                 (uint32_t)((p % G::PR) * G::PB);
+    }
+    const uint32_t qoff0 = ((uint32_t)t0 * 16u + (uint32_t)srow) * nb32 + kb032 + (uint32_t)sblk;
+    int32_t ltile = t0;
+    int lc = 0;
+    uint32_t lct = 0, lqt = 0;
+    // chunk lc of tile ltile (nothing read once the cursor is past the run)
+    auto load_chunk = [&](Ch& ch) __attribute__((always_inline)) {
+      const bool in = ltile < t1;
+      const uint32_t cb = (uint32_t)lc * (uint32_t)CH;
+#pragma unroll
+      for (int i = 0; i < G::NP; ++i) {
+        const uint32_t off = buf_off(in, coff0[i] + lct + cb * (8u * BITS));
+        if constexpr (BITS == 3) ch.piece[i] = __builtin_bit_cast(u32x3_t, __builtin_amdgcn_raw_buffer_load_b96(cr, off, 0, 0));
+        else ch.piece[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(cr, off, 0, 0));
+      }
+      const uint32_t blk = qoff0 + lqt + cb;
+      ch.q8 = __builtin_amdgcn_raw_buffer_load_b8(qr, buf_off(in, blk), 0, 0);
+      ch.sc = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(sr, buf_off(in, (blk >> 8) << 2), 0, 0));
+      if constexpr (ADP) {
+        const int pc = wave * 64 + lane;
+        const bool bv = in && lc == nitem - 1 && pc < 2 * r;
+        ch.bp = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                                brs, buf_off(bv, (uint32_t)ltile * (uint32_t)(32 * r) + (uint32_t)pc * 16u),
+                                                0, 0));
+      }
+      if (++lc == nitem) {
+        lc = 0;
+        ++ltile;
+        lct += 16u * rowb;
+        lqt += 16u * nb32;
+      }
+    };
+    // the previous segment's tiles are done with x, t and B in LDS (and, the first time, the table is written)
+    __syncthreads();
+    Ch ring[D];
+#pragma unroll
+    for (int q = 0; q < D; ++q) load_chunk(ring[q]);
+    {
+      // the x row (K <= 16384: at most 4 pieces per thread) and the adapter partials (at most 8 per
+      // thread), every load issued before any is used
+      constexpr int kXP = (int)(kXLdsMax / 16 / kThreads), kTP = kTPartsMax / kThreads;
+      const uint16_t* xg = L.x;
+      const int64_t xpieces = K / 8;
+      u32x4_t xs[kXP];
+#pragma unroll
+      for (int i = 0; i < kXP; ++i) {
+        const int64_t q = tid + (int64_t)i * kThreads;
+        if (i * kThreads < xpieces) xs[i] = *reinterpret_cast<const u32x4_t*>(xg + (q < xpieces ? q : 0) * 8);
+      }
+      float tpv[kTP];
+      const int tc = ADP ? L.t_splits * r : 0;
+      if constexpr (ADP) {
+#pragma unroll
+        for (int i = 0; i < kTP; ++i) {
+          const int q = tid + i * kThreads;
+          tpv[i] = q < tc ? L.t[q] : 0.0f;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < kXP; ++i) {
+        const int64_t q = tid + (int64_t)i * kThreads;
+        if (q < xpieces) lds_wr128(P.sX + (uint32_t)q * 16u, xs[i]);
+      }
+      if constexpr (ADP) {
+        float* sTPw = reinterpret_cast<float*>(reinterpret_cast<char*>(smem) + P.sTP);
+#pragma unroll
+        for (int i = 0; i < kTP; ++i) {
+          const int q = tid + i * kThreads;
+          if (q < tc) sTPw[q] = tpv[i];
+        }
+      }
+    }
+    __syncthreads();
+    if constexpr (ADP) {
+      // t_j = its partials summed in split order (read by the first tile's epilogue, after a barrier)
+      float* sTw = reinterpret_cast<float*>(reinterpret_cast<char*>(smem) + P.sT);
+      const float* sTPr = reinterpret_cast<const float*>(reinterpret_cast<const char*>(smem) + P.sTP);
+      for (int j = tid; j < r; j += kThreads) {
+        float acc = 0.0f;
+        for (int q = 0; q < L.t_splits; ++q) acc += sTPr[q * r + j];
+        sTw[j] = acc;
+      }
+    }
+    float accd[G::NP];
+#pragma unroll
+    for (int i = 0; i < G::NP; ++i) accd[i] = 0.0f;
+    auto compute_dot = [&](const Ch& ch, int32_t tl, int c, int buf) __attribute__((always_inline)) {
+      const uint32_t sscale = wstage + (uint32_t)buf * kStageW;
+      {
+        const bool nvalid = (int64_t)tl * 16 + srow < N;
+        const float ap = nvalid ? (float)ch.q8 * ch.sc : 0.0f;
+        *reinterpret_cast<__attribute__((address_space(3))) float*>((uintptr_t)(sscale + (uint32_t)(srow * CH + sblk) * 4)) = ap;
+      }
+      const int64_t kbs = kb0 + (int64_t)c * CH;
+      const int col = lane % G::PR;
+      const int u = col / PPB;
+      const bool bval = kbs + u < kb1;  // blocks past the wave's range are read but not added
+      const uint32_t xa = P.sX + (uint32_t)((kbs * 64 + col * CP) * 2);
+      u32x4_t xv[CP / 8];
+#pragma unroll
+      for (int q = 0; q < CP / 8; ++q) xv[q] = lds_rd128(xa + 16u * q);
+#pragma unroll
+      for (int i = 0; i < G::NP; ++i) {
+        const int row = (i * 64 + lane) / G::PR;
+        const float ap = __uint_as_float(lds_rd32(sscale + (uint32_t)(row * CH + u) * 4));
+        float sp;
+        if constexpr (BITS == 3) sp = dot_piece3(ch.piece[i], xv, tlane);
+        else sp = dot_piece<BITS>(ch.piece[i], xv, tlane);
+        accd[i] = fmaf(ap, bval ? sp : 0.0f, accd[i]);
+      }
+    };
+    auto finish_tile = [&](int32_t tl) __attribute__((always_inline)) {
+#pragma unroll
+      for (int i = 0; i < G::NP; ++i) {
+        const float v = group_sum<G::PR>(accd[i]);
+        if (lane % G::PR == 0) sRed[wave * 16 + (i * 64 + lane) / G::PR] = v;
+        accd[i] = 0.0f;
+      }
+      __syncthreads();
+      // output o = tid / 32 by a half-wave (adapter ranks q, q + 32, ... per lane, then a butterfly)
+      const int o = tid >> 5, q = tid & 31;
+      float sum = 0.0f;
+#pragma unroll
+      for (int w = 0; w < kWaves; ++w) sum += sRed[w * 16 + o];
+      float lo2 = 0.0f;
+      if constexpr (ADP) {
+        for (int j = q; j < r; j += 32)
+          lo2 = fmaf(sT[j], bf16_bits_to_f32(lds_rd16(P.sB + (uint32_t)((o * r + j) * 2))), lo2);
+#pragma unroll
+        for (int d = 1; d < 32; d <<= 1) lo2 += __shfl_xor(lo2, d, 64);
+      }
+      const int64_t nn = (int64_t)tl * 16 + o;
+      const float out = fmaf(L.scale, lo2, sum);
+      const uint32_t yo = buf_off(q == 0 && nn < N, (uint32_t)nn * (uint32_t)ES);
+      if constexpr (YDT == DT_F32) __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(out), yr, yo, 0, 0);
+      else __builtin_amdgcn_raw_buffer_store_b16((uint16_t)f32_to_bf16_bits(out), yr, yo, 0, 0);
+      __syncthreads();  // sRed and the B tile are reused by the next tile
+    };
+    int32_t ctile = t0;
+    int cc = 0, buf = 0;
+    // (the counters advance by value selects: a store to a selected counter would keep both in memory)
+    auto consume = [&](int q, int64_t j) __attribute__((always_inline)) {
+      if (j < total) {
+        if (nchunk > 0) compute_dot(ring[q], ctile, cc, buf);
+        buf ^= 1;
+        const bool last = cc == nitem - 1;
+        if (last) {
+          if constexpr (ADP) {
+            const int pc = wave * 64 + lane;
+            if (pc < 2 * r) lds_wr128(P.sB + (uint32_t)pc * 16u, ring[q].bp);
+          }
+          finish_tile(ctile);
+        }
+        cc = last ? 0 : cc + 1;
+        ctile += last ? 1 : 0;
+      }
+    };
+    for (int64_t j0 = 0; j0 < total; j0 += D) {
+#pragma unroll
+      for (int q = 0; q < D; ++q) {
+        consume(q, j0 + q);
+        load_chunk(ring[q]);
       }
     }
   }
@@ -1285,6 +1595,115 @@ bool gemv_fuses_sparse(const LinearArgs& a) {
     default: pl = plan_gemv<8>(a); break;
   }
   return pl.ok && pl.dot && !pl.deep && (a.sp_wht_lp < 0 || (pl.spw && a.r <= 0));
+}
+
+namespace {
+
+template <int BITS, int YDT, bool ADP, int D>
+hipError_t launch_gv_group_k(const GvParams& P, int64_t grid, size_t shmem, const Levels& lv, hipStream_t s) {
+  auto kern = k_gemv_group<BITS, YDT, ADP, D>;
+  static bool attr = false;
+  if (!attr) {
+    hipFuncAttributes fa;
+    hipError_t e = hipFuncGetAttributes(&fa, reinterpret_cast<const void*>(kern));
+    if (e != hipSuccess) return e;
+    if (fa.sharedSizeBytes != 0) return hipErrorInvalidKernelFile;
+    e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern), hipFuncAttributeMaxDynamicSharedMemorySize,
+                            (int)kLdsMax);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  hipLaunchKernelGGL(kern, dim3((unsigned)grid), dim3(kThreads), shmem, s, P, lv);
+  return hipGetLastError();
+}
+
+template <int BITS>
+hipError_t launch_gv_group_b(const GvParams& P, int64_t grid, size_t shmem, bool adp, bool deep, int ydt,
+                             const Levels& lv, hipStream_t s) {
+  if (ydt == DT_F32) {
+    if (adp) return deep ? launch_gv_group_k<BITS, DT_F32, true, 4>(P, grid, shmem, lv, s)
+                         : launch_gv_group_k<BITS, DT_F32, true, 2>(P, grid, shmem, lv, s);
+    return deep ? launch_gv_group_k<BITS, DT_F32, false, 4>(P, grid, shmem, lv, s)
+                : launch_gv_group_k<BITS, DT_F32, false, 2>(P, grid, shmem, lv, s);
+  }
+  if (adp) return deep ? launch_gv_group_k<BITS, DT_BF16, true, 4>(P, grid, shmem, lv, s)
+                       : launch_gv_group_k<BITS, DT_BF16, true, 2>(P, grid, shmem, lv, s);
+  return deep ? launch_gv_group_k<BITS, DT_BF16, false, 4>(P, grid, shmem, lv, s)
+              : launch_gv_group_k<BITS, DT_BF16, false, 2>(P, grid, shmem, lv, s);
+}
+
+}  // namespace
+
+int gemv_group_max() { return kGvGroupMax; }
+
+bool gemv_groupable(const LinearArgs& a) {
+  const int64_t r = a.r > 0 ? a.r : 0;
+  return a.M == 1 && a.xdt == DT_BF16 && a.K % 64 == 0 && a.K * 2 <= (int64_t)kXLdsMax &&
+         r <= 256 && (r == 0 || (a.abdt == DT_BF16 && a.t != nullptr && (int64_t)a.t_splits * r <= kTPartsMax &&
+                                 (reinterpret_cast<uintptr_t>(a.B) & 15) == 0)) &&
+         a.N * (a.K / 64) * 8 * a.bits < (int64_t(1) << 31) && a.N * r * 2 < (int64_t(1) << 31) &&
+         (reinterpret_cast<uintptr_t>(a.x) & 15) == 0 && a.addend == nullptr && a.sp_row_ptr == nullptr &&
+         a.dba_b2 == nullptr;
+}
+
+hipError_t launch_gemv_group(const LinearArgs* ls, int n, const Levels& lv, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  if (n > kGvGroupMax) return hipErrorInvalidValue;
+  GvParams P;
+  P.nl = n;
+  int64_t cost = 0, maxK = 0;
+  int maxr = 0;
+  bool adp = false;
+  for (int i = 0; i < n; ++i) {
+    const LinearArgs& a = ls[i];
+    if (!gemv_groupable(a) || a.bits != ls[0].bits || a.ydt != ls[0].ydt) return hipErrorInvalidValue;
+    GvLayer& L = P.L[i];
+    L.x = reinterpret_cast<const uint16_t*>(a.x);
+    L.codes = a.codes;
+    L.q8 = a.q8;
+    L.cst = a.cst;
+    L.t = a.t;
+    L.B = reinterpret_cast<const uint16_t*>(a.B);
+    L.y = a.y;
+    L.N = (int32_t)a.N;
+    L.nb = (int32_t)(a.K / 64);
+    L.r = a.r > 0 ? a.r : 0;
+    L.t_splits = a.t_splits;
+    L.scale = a.scale;
+    L.ntiles = (int32_t)((a.N + 15) / 16);
+    L.cost0 = cost;
+    cost += (int64_t)L.ntiles * L.nb;
+    maxK = std::max<int64_t>(maxK, a.K);
+    maxr = std::max(maxr, L.r);
+    adp = adp || L.r > 0;
+  }
+  P.total = cost;
+  if (cost == 0) return hipSuccess;
+  auto r16 = [](size_t b) { return (b + 15) & ~(size_t)15; };
+  const int bits = ls[0].bits;
+  size_t lds = bits == 2 ? PairTable<2>::kBytes : bits == 3 ? PairTable<3>::kBytes : bits == 4 ? PairTable<4>::kBytes
+                                                                                           : PairTable<8>::kBytes;
+  lds += (size_t)kWaves * 2 * (16 * CH * 4) + (size_t)kWaves * 256 * sizeof(float);
+  P.sT = (uint32_t)lds;
+  lds += r16((size_t)maxr * 4);
+  P.sTP = (uint32_t)lds;
+  if (adp) lds += (size_t)kTPartsMax * 4;
+  P.sB = (uint32_t)lds;
+  lds += r16((size_t)32 * maxr);
+  P.sX = (uint32_t)lds;
+  lds += (size_t)maxK * 2 + 512;  // the row reads up to 256 elements past its end, for blocks it does not add
+  if (lds > kLdsMax) return hipErrorInvalidValue;
+  int64_t tiles = 0;
+  for (int i = 0; i < n; ++i) tiles += P.L[i].ntiles;
+  const int64_t grid = std::min<int64_t>(device_cus(), tiles);
+  // ring depth 4 unless a wave's share of its workgroup's run (cost / grid blocks over 8 waves) is at most 2 chunks
+  const bool deep = cost / grid / (8 * CH) > 2;
+  switch (ls[0].bits) {
+    case 2: return launch_gv_group_b<2>(P, grid, lds, adp, deep, ls[0].ydt, lv, s);
+    case 3: return launch_gv_group_b<3>(P, grid, lds, adp, deep, ls[0].ydt, lv, s);
+    case 4: return launch_gv_group_b<4>(P, grid, lds, adp, deep, ls[0].ydt, lv, s);
+    default: return launch_gv_group_b<8>(P, grid, lds, adp, deep, ls[0].ydt, lv, s);
+  }
 }
 
 hipError_t launch_gemv(const LinearArgs& a, const Levels& lv, hipStream_t s) {

@@ -542,9 +542,12 @@ qlr_status qlr_linear_fwd_mixed(const qlr_layer* layers, int32_t n, int64_t M, q
   hipStream_t s = reinterpret_cast<hipStream_t>(stream);
   char* wsp = reinterpret_cast<char*>(ws);
   // GEMM-path layers run as grouped launches (one code width and adapter flag
-  // per group, in layer order), after their adapter products; the others one by one
+  // per group, in layer order), after their adapter products; at M = 1 the
+  // single-row decode layers run as grouped launches too (one code width per
+  // group), after their adapter products in grouped launches; the others one by one
   std::vector<qlr::LinearArgs> groups[2][4];
-  std::vector<qlr::LoraTItem> tgroup;
+  std::vector<qlr::LinearArgs> dgroups[4];
+  std::vector<qlr::LoraTItem> tgroup, tsmall;
   auto widx = [](int bits) { return bits == 2 ? 0 : bits == 3 ? 1 : bits == 4 ? 2 : 3; };
   for (int32_t i = 0; i < n; ++i) {
     const qlr_layer& L = layers[i];
@@ -554,6 +557,15 @@ qlr_status qlr_linear_fwd_mixed(const qlr_layer* layers, int32_t n, int64_t M, q
     const size_t need_l = linear_ws_bytes(M, L.w->cols, L.r);
     char* wl = need_l > 0 ? wsp : nullptr;
     wsp += need_l;
+    if (path == QLR_PATH_GEMV && M == 1) {
+      const int splits = qlr::lora_t_splits(M, L.w->cols, L.r, (int)xdt, (int)abdt);
+      const qlr::LinearArgs a = make_args(c, L.scale, wl, splits);
+      if (qlr::gemv_groupable(a)) {
+        if (L.r > 0) tsmall.push_back(qlr::LoraTItem{L.x, L.A, reinterpret_cast<float*>(wl), L.w->cols, L.r, false});
+        dgroups[widx(L.w->bits)].push_back(a);
+        continue;
+      }
+    }
     if (path == QLR_PATH_GEMM && M > 0) {
       const int splits = qlr::lora_t_splits(M, L.w->cols, L.r, (int)xdt, (int)abdt);
       if (L.r > 0) {
@@ -570,6 +582,20 @@ qlr_status qlr_linear_fwd_mixed(const qlr_layer* layers, int32_t n, int64_t M, q
     }
     qlr_status st = run_linear(c, L.scale, wl, path, s);
     if (st != QLR_OK) return st;
+  }
+  // adapter products of the grouped decode layers, then their decode kernels
+  for (size_t b = 0; b < tsmall.size(); b += qlr::lora_t_small_group_max()) {
+    const int cnt = (int)std::min<size_t>(qlr::lora_t_small_group_max(), tsmall.size() - b);
+    const hipError_t e = qlr::launch_lora_t_small_group(tsmall.data() + b, cnt, M, s);
+    if (e != hipSuccess) return hip_fail(e, "grouped adapter product launch");
+  }
+  for (int w = 0; w < 4; ++w) {
+    std::vector<qlr::LinearArgs>& g = dgroups[w];
+    for (size_t b = 0; b < g.size(); b += qlr::gemv_group_max()) {
+      const int cnt = (int)std::min<size_t>(qlr::gemv_group_max(), g.size() - b);
+      const hipError_t e = qlr::launch_gemv_group(g.data() + b, cnt, levels_arg(g[b].bits), s);
+      if (e != hipSuccess) return hip_fail(e, "grouped decode launch");
+    }
   }
   // adapter products of the grouped layers, then their GEMMs
   for (size_t b = 0; b < tgroup.size(); b += qlr::lora_t_group_max()) {

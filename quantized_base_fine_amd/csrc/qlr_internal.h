@@ -47,6 +47,11 @@ struct LoraTItem {
 };
 int lora_t_group_max();
 hipError_t launch_lora_t_group(const LoraTItem* items, int n, int64_t M, hipStream_t s);
+// The same for M <= 16 (bf16, K % 64 == 0, not bt): each item written as
+// lora_t_splits(M, K, r) partial sums, as launch_lora_t would; up to
+// lora_t_small_group_max() items per launch.
+int lora_t_small_group_max();
+hipError_t launch_lora_t_small_group(const LoraTItem* items, int n, int64_t M, hipStream_t s);
 
 struct LinearArgs {
   const void* x;
@@ -100,6 +105,13 @@ bool gemv_fuses_sparse(const LinearArgs& a);
 // True when launch_gemv can form the double-binary branch itself (a.dba_*, one
 // envelope term, a.r = its rank <= 16, a single x row).
 bool gemv_fuses_dba(const LinearArgs& a);
+// Grouped single-row decode: up to gemv_group_max() linears of one code width
+// and output dtype at M = 1 in one launch (a mixed stack's decode), each
+// accepted by gemv_groupable (bits 2/4/8, bf16, x in LDS, adapter partials in t
+// from the small-M adapter product, no side channel or addend).
+int gemv_group_max();
+bool gemv_groupable(const LinearArgs& a);
+hipError_t launch_gemv_group(const LinearArgs* ls, int n, const Levels& lv, hipStream_t s);
 // bf16 tiled GEMM path.
 hipError_t launch_gemm(const LinearArgs& a, const Levels& lv, hipStream_t s);
 // Up to gemm_group_max() independent linears of one code width, one M and one

@@ -174,14 +174,11 @@ __global__ __launch_bounds__(256) void k_lora_t_tile(TGroup G) {
 // multiplies on 16x16x32 bf16 MFMA (x rows as the A operand, adapter rows as
 // B).  The 16 waves' sums are added through LDS in wave order.
 constexpr int kLtWaves = 16, kLtSteps = 8;
-__global__ __launch_bounds__(kLtWaves * 64) void k_lora_t_small(const uint16_t* __restrict__ x, int64_t M,
-                                                               int64_t K, const uint16_t* __restrict__ A, int r,
-                                                               float* __restrict__ p) {
-  __shared__ float red[kLtWaves][256];
+__device__ __forceinline__ void lora_t_small_body(const uint16_t* __restrict__ x, int64_t M, int64_t K,
+                                                  const uint16_t* __restrict__ A, int r, float* __restrict__ p,
+                                                  int j0, int S, int sidx, float (*red)[256]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int row = lane & 15, g = lane >> 4;
-  const int j0 = blockIdx.x * 16;
-  const int S = gridDim.y, sidx = blockIdx.y;
   const bool xv = row < M, av = j0 + row < r;
   const uint16_t* xp = x + (int64_t)(xv ? row : 0) * K + g * 8;
   const uint16_t* ap = A + (int64_t)(av ? j0 + row : 0) * K + g * 8;
@@ -215,6 +212,38 @@ __global__ __launch_bounds__(kLtWaves * 64) void k_lora_t_small(const uint16_t* 
     const int j = j0 + (l & 15);     // MFMA output column (adapter row)
     if (m < M && j < r) p[((int64_t)sidx * M + m) * r + j] = sum;
   }
+}
+
+__global__ __launch_bounds__(kLtWaves * 64) void k_lora_t_small(const uint16_t* __restrict__ x, int64_t M,
+                                                               int64_t K, const uint16_t* __restrict__ A, int r,
+                                                               float* __restrict__ p) {
+  __shared__ float red[kLtWaves][256];
+  lora_t_small_body(x, M, K, A, r, p, blockIdx.x * 16, gridDim.y, blockIdx.y, red);
+}
+
+// Several products of one M <= 16 in one launch (a mixed stack's decode):
+// workgroup w belongs to the item whose range [wg0, wg0 + jtiles x splits)
+// holds it, and takes (16 adapter rows, split) of that item as k_lora_t_small.
+constexpr int kLtsGroupMax = 32;
+struct LtsItem {
+  const uint16_t* x;
+  const uint16_t* A;
+  float* t;
+  int64_t K;
+  int32_t r, splits, jtiles, wg0;
+};
+struct LtsGroup {
+  int64_t M;
+  int32_t n;
+  LtsItem L[kLtsGroupMax];
+};
+__global__ __launch_bounds__(kLtWaves * 64) void k_lora_t_small_group(LtsGroup G) {
+  __shared__ float red[kLtWaves][256];
+  int li = 0;
+  while (li + 1 < G.n && (int32_t)blockIdx.x >= G.L[li + 1].wg0) ++li;
+  const LtsItem& it = G.L[li];
+  const int local = (int)blockIdx.x - it.wg0;
+  lora_t_small_body(it.x, G.M, it.K, it.A, it.r, it.t, (local % it.jtiles) * 16, it.splits, local / it.jtiles, red);
 }
 
 // ---------------------------------------------------------------- float32 forward
@@ -340,6 +369,35 @@ hipError_t launch_linear_f32(const LinearArgs& a, const Levels& lv, hipStream_t 
 }
 
 int lora_t_group_max() { return kTGroupMax; }
+
+int lora_t_small_group_max() { return kLtsGroupMax; }
+
+hipError_t launch_lora_t_small_group(const LoraTItem* items, int n, int64_t M, hipStream_t s) {
+  if (n <= 0 || M <= 0) return hipSuccess;
+  if (n > kLtsGroupMax || M > 16) return hipErrorInvalidValue;
+  LtsGroup G;
+  G.M = M;
+  G.n = 0;
+  int32_t wg = 0;
+  for (int i = 0; i < n; ++i) {
+    const LoraTItem& it = items[i];
+    if (it.r <= 0) continue;
+    if (it.bt || it.K % 64 != 0) return hipErrorInvalidValue;
+    LtsItem& L = G.L[G.n++];
+    L.x = reinterpret_cast<const uint16_t*>(it.x);
+    L.A = reinterpret_cast<const uint16_t*>(it.A);
+    L.t = it.t;
+    L.K = it.K;
+    L.r = it.r;
+    L.splits = lora_t_splits(M, it.K, it.r, DT_BF16, DT_BF16);
+    L.jtiles = (it.r + 15) / 16;
+    L.wg0 = wg;
+    wg += L.jtiles * L.splits;
+  }
+  if (G.n == 0) return hipSuccess;
+  hipLaunchKernelGGL(k_lora_t_small_group, dim3((unsigned)wg), dim3(kLtWaves * 64), 0, s, G);
+  return hipGetLastError();
+}
 
 hipError_t launch_lora_t_group(const LoraTItem* items, int n, int64_t M, hipStream_t s) {
   if (n <= 0 || M <= 0) return hipSuccess;

@@ -238,9 +238,11 @@ def test_linear_edge_cases():
 # ---------------------------------------------------------------- mixed stack
 
 def test_mixed_small():
-    """Per-layer (bits, rank) drawn as for the mixed stack, shrunk shapes, M = 48 and M = 8."""
+    """Per-layer (bits, rank) drawn as for the mixed stack, shrunk shapes, M = 48, 8 and 1 (at M = 1 the
+    2-, 4- and 8-bit layers run as grouped decode launches: blocks per row 6 and 7, so waves hold 0 or 1
+    blocks; ragged rows)."""
     plan = workloads.mixed_plan()
-    for M in (48, 8):
+    for M in (48, 8, 1):
         lins = [workloads.mixed_linear(i, M=M, plan=plan, shape_override=(200 + 16 * (i % 3), 384 + 64 * (i % 2)))
                 for i in range(10)]
         entries, qws = [], []
