@@ -582,12 +582,24 @@ __global__ __launch_bounds__(512, 1) void k_gemm(GemmParams P, Levels lv) {
   } else {
     // =================== consumers: MFMA on 128 x 64 of the tile ===================
     const int mh = wave & 1, nh = wave >> 1;
-    // fragment of step s (0..3): row fr (+32 i or +32 c), chunk 2 s + h
+    // fragment of step s (0..3): row fr (+32 i or +32 c), chunk 2 s + h.  One LDS
+    // base address per step and operand (a second one for the third x buffer,
+    // whose offset would pass 64 KB), pinned so that the compiler cannot see
+    // their low bits: then every fragment read is base + a constant that fits the
+    // instruction's 16-bit offset, instead of a precomputed address register each.
     uint32_t fo[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) fo[s] = (uint32_t)(fr * 128) + ((((uint32_t)(2 * s + h)) ^ swz((uint32_t)fr & 15u)) << 4);
     const uint32_t xrow0 = (uint32_t)(128 * mh * 128);
     const uint32_t wrow0 = (uint32_t)(64 * nh * 128);
+    uint32_t xb[4], xb2[4], wb[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      xb[s] = kXOff + xrow0 + fo[s];
+      xb2[s] = xb[s] + 2 * kXTile;
+      wb[s] = kWOff + wrow0 + fo[s];
+      asm volatile("" : "+v"(xb[s]), "+v"(xb2[s]), "+v"(wb[s]));
+    }
     // TR: transpose-read address of 16-lane group g, lane sp, for column tile c
     // (rows 8 h + sp / 4 of the 16-row slice, four columns from 16 (g & 1) + 4 (sp & 3)).
     uint32_t tbo[2];
@@ -609,10 +621,13 @@ __global__ __launch_bounds__(512, 1) void k_gemm(GemmParams P, Levels lv) {
         for (int v = 0; v < 16; ++v) acc[i][c][v] = 0.0f;
 
     __syncthreads();  // producers: blocks 0 and 1 written
-    u32x4_t fa[2][4], fb[2][2];
+    // fragments of three MFMA steps in registers: step g (of 12 in the 3-block
+    // unrolled loop) uses slot g % 3 while the reads of step g + 2 are in flight
+    u32x4_t fa[3][4], fb[3][2];
     auto read_frags = [&](int buf, int s, int slot) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) fa[slot][i] = lds_u32x4(kXOff + buf * kXTile + xrow0 + fo[s] + 4096u * i);
+      for (int i = 0; i < 4; ++i)
+        fa[slot][i] = lds_u32x4(buf == 2 ? xb2[s] + 4096u * i : xb[s] + (uint32_t)buf * kXTile + 4096u * i);
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         if constexpr (TR) {
@@ -622,7 +637,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm(GemmParams P, Levels lv) {
           fb[slot][c] = u32x4_t{__builtin_bit_cast(uint2, lo).x, __builtin_bit_cast(uint2, lo).y,
                                 __builtin_bit_cast(uint2, hi).x, __builtin_bit_cast(uint2, hi).y};
         } else {
-          fb[slot][c] = lds_u32x4(kWOff + buf * kWTile + wrow0 + fo[s] + 4096u * c);
+          fb[slot][c] = lds_u32x4(wb[s] + (uint32_t)buf * kWTile + 4096u * c);
         }
       }
     };
@@ -633,16 +648,20 @@ __global__ __launch_bounds__(512, 1) void k_gemm(GemmParams P, Levels lv) {
         for (int c = 0; c < 2; ++c) acc[i][c] = mfma32x32x16(as_bf16x8(fa[slot][i]), as_bf16x8(fb[slot][c]), acc[i][c]);
     };
     read_frags(0, 0, 0);
-    // block k: four MFMA steps, each first reading the next step's fragments
-    // (after step 3: step 0 of block k+1, buffer bn, written one block earlier)
-    auto cstep = [&](int bc, int bn) {
+    read_frags(0, 1, 1);
+    // block k at position J of the unrolled loop: four MFMA steps, each first
+    // reading the fragments two steps ahead (steps 2 and 3 of block k, then
+    // steps 0 and 1 of block k+1, buffer bn, written one block earlier)
+    auto cstep = [&](auto jpos, int bc, int bn) {
+      constexpr int J = decltype(jpos)::value;
 #pragma unroll
       for (int s = 0; s < 4; ++s) {
+        const int g = 4 * J + s;
         __builtin_amdgcn_sched_barrier(0);
-        if (s < 3) read_frags(bc, s + 1, (s + 1) & 1);
-        else read_frags(bn, 0, 0);
+        if (s < 2) read_frags(bc, s + 2, (g + 2) % 3);
+        else read_frags(bn, s - 2, (g + 2) % 3);
         __builtin_amdgcn_sched_barrier(0);
-        mfmas(s & 1);
+        mfmas(g % 3);
       }
       __builtin_amdgcn_sched_barrier(0);
       __syncthreads();
@@ -652,12 +671,12 @@ __global__ __launch_bounds__(512, 1) void k_gemm(GemmParams P, Levels lv) {
     const int64_t nb3 = nbt - nbt % 3;
     int64_t kb = 0;
     for (; kb < nb3; kb += 3) {
-      cstep(0, 1);
-      cstep(1, 2);
-      cstep(2, 0);
+      cstep(std::integral_constant<int, 0>{}, 0, 1);
+      cstep(std::integral_constant<int, 1>{}, 1, 2);
+      cstep(std::integral_constant<int, 2>{}, 2, 0);
     }
-    if (kb < nbt) cstep(0, 1);
-    if (kb + 1 < nbt) cstep(1, 2);
+    if (kb < nbt) cstep(std::integral_constant<int, 0>{}, 0, 1);
+    if (kb + 1 < nbt) cstep(std::integral_constant<int, 1>{}, 1, 2);
 
     __syncthreads();  // every wave is past its last tile read: the staging area is free
 
