@@ -238,9 +238,14 @@ qlr_status qlr_dequantize(const qlr_qweight* w, void* out, qlr_dtype odt, void* 
  * (f32 or bf16).  Requires cols % 64 == 0 (whole blocks per row).  M may be 0
  * (nothing is launched).  Error bound per y element, S = sum_k |x[m,k] w'[n,k]|
  * (plus half a bf16 ulp of the result when ydt is bf16), on any input:
- *   - QLR_PATH_F32 and QLR_PATH_GEMV: 1e-3 * S + 1e-5.  The decode kernels
- *     carry each codebook level as two bf16 halves (about 16 significant bits)
- *     and the float32 kernels in float32; sums are float32.
+ *   - QLR_PATH_F32 and QLR_PATH_GEMV: 1e-3 * S + 1e-5.  The single-row
+ *     decode kernels (M = 1 with 2-, 4- or 8-bit codes, and every width in
+ *     qlr_linear_fwd_mixed) take each codebook level as one fp16 number
+ *     (within 2^-11 of it) times x as fp16 numbers scaled by a power of two
+ *     per 64-column block, exact whenever the block's values fit (otherwise
+ *     that part of the row is summed in float32); the other decode kernels
+ *     carry each level as two bf16 halves (about 16 significant bits); the
+ *     float32 kernels work in float32; sums are float32.
  *   - QLR_PATH_GEMM: 5e-3 * S + 1e-5.  The prefill kernel rounds each
  *     dequantized weight once to bf16 (relative error up to 2^-8) for the bf16
  *     matrix cores.  When those rounding errors do not all share a sign, as

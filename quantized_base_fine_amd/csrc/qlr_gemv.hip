@@ -33,11 +33,14 @@
 //   instead of every weight.
 // Levels are looked up in an LDS table indexed by the packed code bits of two
 // neighbouring weights, with a copy per lane position so that lanes never
-// collide on a bank (qlr_lut.h).  Each level enters as two bf16 halves, hi and
-// lo, multiplied with x separately (two packed dot products, or two MFMAs):
-// a level rounded to bf16 alone is off by up to 2^-8 of its value, and with x
-// and the weights of one sign those errors add up to more than the layer's
-// 1e-3 bound; hi + lo carries the float32 level to about 2^-16.
+// collide on a bank (qlr_lut.h).  A level rounded to bf16 alone is off by up
+// to 2^-8 of its value, and with x and the weights of one sign those errors
+// add up to more than the layer's 1e-3 bound.  So on the MFMA path each level
+// enters as two bf16 halves, hi and lo (two MFMAs), which carry the float32
+// level to about 2^-16; the single-row path takes it as one fp16 number
+// (within 2^-11) and x as fp16 numbers with an exact power-of-two scale per
+// block, one packed fp16 dot product per level pair (half the lookups and the
+// products of two halves).
 #include <algorithm>
 #include <type_traits>
 
@@ -95,6 +98,10 @@ constexpr size_t kXLdsMax = 32 * 1024;
 // them, as the adapter-product split count guarantees (kTPartsMax).
 constexpr int kTPre = kTPartsMax / kThreads;
 static_assert(kTPre * kThreads == kTPartsMax, "prefetch covers every partial sum");
+// the single-row path's fp16 table takes the place of the MFMA path's hi/lo table
+static_assert(LevelTableH<2>::kBytes == PairTable<2>::kBytes && LevelTableH<3>::kBytes == PairTable<3>::kBytes &&
+                  LevelTableH<4>::kBytes == PairTable<4>::kBytes && LevelTableH<8>::kBytes == PairTable<8>::kBytes,
+              "one LDS layout for both tables");
 
 // How the epilogue gets the adapter product t = x A^T: from the split partial
 // sums of the adapter-product kernel (T_GLOBAL, T_LOOP, T_PREFETCH), or
@@ -114,6 +121,8 @@ struct Params {
   uint32_t sTP;
   uint32_t sB;
   uint32_t sX;
+  uint32_t sXh;  // single-row path: the x row as fp16 numbers x 2^s_b
+  uint32_t sXs;  // and its per-block exponents s_b (int32, kXsBad: not exact)
   uint32_t sZ;   // 128 zero bytes (x fragments of rows past M)
   uint32_t sW;   // float32 transform of the x row (Walsh-Hadamard side channel)
 };
@@ -215,6 +224,33 @@ __device__ __forceinline__ void build_table_kernarg(uint32_t* tbl, const Levels&
   }
 }
 
+// The fp16 level table of the single-row path (layout in qlr_lut.h), from the
+// by-value levels: wave w writes entries [w E/8, (w+1) E/8), one 256-byte entry
+// (64 copies of one word) per store instruction, so an entry's level indices
+// are uniform across the wave (batched scalar loads).  For 2-bit codes (16
+// entries) waves 0 and 1 write them all.
+template <int BITS>
+__device__ __forceinline__ void build_table_h(uint32_t* tbl, const Levels& lv, int tid) {
+  constexpr int NL = 1 << BITS;
+  constexpr int E = LevelTableH<BITS>::kEntries;
+  constexpr int EPW = (E / kWaves > 0) ? E / kWaves : 1;
+  const int lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  if (w * EPW >= E) return;
+  uint32_t* t = tbl + (w * EPW) * 64 + lane;
+  auto h16 = [](float v) { return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)v); };
+#pragma unroll
+  for (int i = 0; i < EPW; ++i) {
+    const int e = w * EPW + i;
+    if constexpr (BITS == 8) {
+      const uint32_t hv = h16(lv.v[e]);
+      t[i * 64] = hv | (hv << 16);
+    } else {
+      t[i * 64] = h16(lv.v[e & (NL - 1)]) | (h16(lv.v[e >> BITS]) << 16);
+    }
+  }
+}
+
 // Sum over aligned groups of G consecutive lanes (G = 2, 4, 8 or 16), every
 // lane of a group getting the group's sum, by row-local data-parallel moves:
 // neighbour pairs, then quads, then the mirrored half of an 8-lane group, then
@@ -238,55 +274,142 @@ __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
 }
 
-// Single-row products: sum over the 128 / BITS codes of one 16-byte piece of
-// level(code) * x, with the levels looked up as bf16 hi/lo halves in the
-// table (at LDS address 0) and multiplied with the matching x pairs (xv holds
-// the piece's x values in order, 8 per 16-byte vector).  Two accumulation
-// chains for the hi halves and two for the lo halves, added at the end.
-template <int BITS>
-__device__ __forceinline__ float dot_piece(const u32x4_t& pc, const u32x4_t* xv, uint32_t tl) {
-  float s0 = 0.0f, s1 = 0.0f, t0 = 0.0f, t1 = 0.0f;
-  auto acc = [&](u32x2v_t e, uint32_t xp, bool odd) {
-    if (odd) {
-      s1 = dot2(e.x, xp, s1);
-      t1 = dot2(e.y, xp, t1);
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ float dot2h(uint32_t a, uint32_t b, float c) {
+  return __builtin_amdgcn_fdot2(__builtin_bit_cast(f16x2_t, a), __builtin_bit_cast(f16x2_t, b), c, false);
+}
+
+// Single-row products: sum over the codes of one piece (16 bytes of 2-, 4- or
+// 8-bit codes) of level(code) * x, the levels looked up in the fp16 table (at
+// LDS address 0) and paired with the matching x pairs (xv holds the piece's x
+// values in order, 8 per 16-byte vector).  H: x is the fp16 row (scaled), one
+// packed fp16 dot product per pair; otherwise x is the bf16 row and each pair
+// takes two float32 multiply-adds (fp16 level and bf16 x are both exact in
+// float32).  Two accumulation chains, added at the end.
+template <bool H>
+struct PairAcc {
+  float s0 = 0.0f, s1 = 0.0f;
+  // e: the two fp16 levels, xp: the two x values (both lower element in the low half)
+  __device__ __forceinline__ void add(uint32_t e, uint32_t xp, bool odd) {
+    float& s = odd ? s1 : s0;
+    if constexpr (H) {
+      s = dot2h(e, xp, s);
     } else {
-      s0 = dot2(e.x, xp, s0);
-      t0 = dot2(e.y, xp, t0);
+      s = fmaf(f16_bits_to_f32((uint16_t)(e & 0xFFFFu)), bf16_bits_to_f32(xp & 0xFFFFu), s);
+      s = fmaf(f16_bits_to_f32((uint16_t)(e >> 16)), bf16_bits_to_f32(xp >> 16), s);
     }
-  };
+  }
+  __device__ __forceinline__ float sum() const { return s0 + s1; }
+};
+// LDS address of entry (byte b of w) for the lane: one byte permute puts the
+// byte into bits 8..15 over the lane's copy offset.
+__device__ __forceinline__ uint32_t entry_addr(uint32_t w, uint32_t tl, int b) {
+  return __builtin_amdgcn_perm(w, tl, 0x0C0C0000u | ((uint32_t)(4 + b) << 8));
+}
+template <int BITS, bool H>
+__device__ __forceinline__ float dot_piece(const u32x4_t& pc, const u32x4_t* xv, uint32_t tl) {
+  PairAcc<H> acc;
   if constexpr (BITS == 4) {
+    // byte b of word w = pair 4w + b
 #pragma unroll
     for (int w = 0; w < 4; ++w)
 #pragma unroll
-      for (int b = 0; b < 4; ++b)
-        acc(lds_entry(__builtin_amdgcn_perm(pc[w], tl, 0x0C0C0000u | ((uint32_t)(4 + b) << 8))), xv[w][b], b & 1);
+      for (int b = 0; b < 4; ++b) acc.add(lds_word(entry_addr(pc[w], tl, b)), xv[w][b], b & 1);
   } else if constexpr (BITS == 2) {
+    // nibble n of word w = pair 8w + n; the even nibbles spread into bytes by one
+    // mask, the odd ones by a shift and the mask
 #pragma unroll
-    for (int w = 0; w < 4; ++w)
+    for (int w = 0; w < 4; ++w) {
+      const uint32_t ev = pc[w] & 0x0F0F0F0Fu, od = (pc[w] >> 4) & 0x0F0F0F0Fu;
 #pragma unroll
       for (int n = 0; n < 8; ++n)
-        acc(lds_entry((((pc[w] >> (4 * n)) & 15u) << 8) | tl), xv[2 * w + (n >> 2)][n & 3], n & 1);
+        acc.add(lds_word(entry_addr((n & 1) ? od : ev, tl, n >> 1)), xv[2 * w + (n >> 2)][n & 3], n & 1);
+    }
   } else {
+    // byte b of word w = code 4w + b; codes 2p and 2p + 1 make x pair p
 #pragma unroll
     for (int w = 0; w < 4; ++w)
 #pragma unroll
       for (int j = 0; j < 2; ++j) {
-        const uint32_t e0 = lds_word((((pc[w] >> (16 * j)) & 255u) << 8) | tl);
-        const uint32_t e1 = lds_word((((pc[w] >> (16 * j + 8)) & 255u) << 8) | tl);
-        acc(split8(e0, e1), xv[w >> 1][2 * (w & 1) + j], j);
+        const uint32_t e0 = lds_word(entry_addr(pc[w], tl, 2 * j));
+        const uint32_t e1 = lds_word(entry_addr(pc[w], tl, 2 * j + 1));
+        acc.add(__builtin_amdgcn_perm(e1, e0, 0x05040100u), xv[w >> 1][2 * (w & 1) + j], j);
       }
   }
-  return (s0 + s1) + (t0 + t1);
+  return acc.sum();
+}
+
+// x as scaled fp16 numbers, per 64-column block b of the row: x 2^s_b, with s_b
+// the power of two that puts the block's largest |x| in [2^14, 2^15).  A block
+// is exact when each of its values is then a normal fp16 number or zero, so
+// that every product with an fp16 level is exact in float32; a block holding
+// Inf or NaN, or whose largest |x| is below 2^-126, is not.  The 8 pieces of a
+// block sit in 8 neighbouring lanes (the staging order), which reduce its
+// largest |x| and its exactness among themselves.  kXsBad marks a block that
+// is not exact in the scale array.
+constexpr int kXsBad = 0x7FFFFFFF;
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_u32(uint32_t v) {
+  return __builtin_amdgcn_update_dpp(0u, v, CTRL, 0xF, 0xF, false);
+}
+__device__ __forceinline__ uint32_t group_max8(uint32_t v) {
+  v = max(v, dpp_u32<0xB1>(v));   // lane ^ 1
+  v = max(v, dpp_u32<0x4E>(v));   // lane ^ 2
+  return max(v, dpp_u32<0x141>(v));  // 7 - lane within 8
+}
+__device__ __forceinline__ uint32_t group_min8(uint32_t v) {
+  v = min(v, dpp_u32<0xB1>(v));
+  v = min(v, dpp_u32<0x4E>(v));
+  return min(v, dpp_u32<0x141>(v));
+}
+// h: the piece's 8 values as fp16 x 2^s_b; returns s_b, or kXsBad.  On the bf16
+// bits: a value 1.m x 2^(E - 127) (exponent field E, 7-bit m) becomes 1.m x
+// 2^(E - 127 + s), whose fp16 exponent field is E - 112 + s, so the fp16 bits
+// without the sign are ((E << 7 | m) + (s - 112) 128) << 3; it is a normal fp16
+// number when that field is at least 1, i.e. when E << 7 | m >= max(1, 113 - s)
+// 128 (subnormal bf16 values, E = 0, never pass).  The field is at most 29 for
+// the block's largest value, so the sums stay below 2^12 per 16-bit half.
+__device__ __forceinline__ int x_piece_f16(const u32x4_t& xb, u32x4_t& h) {
+  typedef uint16_t u16x2_t __attribute__((ext_vector_type(2)));
+  u16x2_t mx = {0, 0}, mn = {0xFFFF, 0xFFFF};  // largest |x| bits; smallest |x| bits - 1 (0 wraps to 0xFFFF)
+  u16x2_t a[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    a[j] = __builtin_bit_cast(u16x2_t, xb[j] & 0x7FFF7FFFu);
+    mx = __builtin_elementwise_max(mx, a[j]);
+    mn = __builtin_elementwise_min(mn, a[j] - (u16x2_t){1, 1});
+  }
+  const uint32_t m = group_max8(max((uint32_t)mx.x, (uint32_t)mx.y));
+  const uint32_t lo = group_min8(min((uint32_t)mn.x, (uint32_t)mn.y));
+  // |x| bits >= 0x7F80: Inf or NaN; below 0x0080 (and not 0): a subnormal largest |x|
+  const bool scalable = m < 0x7F80u && (m == 0u || m >= 0x0080u);
+  const int s = m == 0u ? 0 : 141 - (int)(m >> 7);
+  const uint32_t tmin = (uint32_t)max(1, 113 - s) * 128u;
+  const bool ok = scalable && (lo == 0xFFFFu || lo + 1u >= tmin);
+  const uint16_t bias = (uint16_t)((s - 112) * 128);
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    u16x2_t v = (a[j] + (u16x2_t){bias, bias}) << (u16x2_t){3, 3};
+    v = v * __builtin_elementwise_min(a[j], (u16x2_t){1, 1});  // zeros stay zero
+    h[j] = __builtin_bit_cast(uint32_t, v) | (xb[j] & 0x80008000u);
+  }
+  return ok ? s : kXsBad;
+}
+// Whether every block [b0, b1) of the row (at most 64) is exact, uniformly over the wave.
+__device__ __forceinline__ bool x_blocks_exact(uint32_t sxs, int64_t b0, int64_t b1, int lane) {
+  const int64_t b = b0 + lane;
+  const int v = b < b1 ? (int)lds_rd32(sxs + (uint32_t)b * 4u) : 0;
+  return __builtin_amdgcn_ballot_w64(v == kXsBad) == 0;
 }
 
 // ADP: the call has an adapter branch (r > 0); calls without one run a separate
 // instantiation, which also gives it its own kernel name.
 // DOT (a single x row, 2-, 4- or 8-bit codes): the codes are used straight from
 // the registers they were loaded into, each lane taking 16-byte pieces of
-// rows; level pairs are looked up and multiplied with x pairs by packed bf16
-// dot products, and the row sums are reduced across the lanes of a row and the
-// waves at the end of a tile.  Otherwise the codes are staged through LDS into
+// rows; level pairs are looked up and multiplied with x pairs by packed fp16
+// dot products (a wave whose x blocks are not all exact in fp16 takes float32
+// products of the same levels with the bf16 row), and the row sums are
+// reduced across the lanes of a row and the waves at the end of a tile.  Otherwise the codes are staged through LDS into
 // the 16x16x32 MFMA layout (x rows as the A operand).
 //
 // Every global access of the chunk stream is issued unconditionally (out-of-
@@ -324,7 +447,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
   // (the wave index is uniform within a wave: saying so keeps the chunk loops scalar)
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int nl = lane & 15, g = lane >> 4;
-  const uint32_t tlane = table_lane<BITS>(lane);
+  const uint32_t tlane = DOT ? table_lane_h(lane) : table_lane<BITS>(lane);
   const int64_t kb0 = nb * wave / kWaves, kb1 = nb * (wave + 1) / kWaves;
   const int nchunk = (int)((kb1 - kb0 + CH - 1) / CH);
   const int nitem = nchunk > 0 ? nchunk : 1;  // items (chunks) per tile for this wave
@@ -560,13 +683,25 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
       }
     }
   }
-  build_table_kernarg<BITS>(tbl, lv, tid);
+  if constexpr (DOT) build_table_h<BITS>(tbl, lv, tid);
+  else build_table_kernarg<BITS>(tbl, lv, tid);
   if constexpr (XLDS) {
     if (tid < 8) lds_wr128(P.sZ + 16u * tid, zero);
 #pragma unroll
     for (int i = 0; i < kXPer; ++i) {
       const int64_t q = tid + (int64_t)i * kThreads;
-      if (q < xpieces) {
+      if constexpr (DOT) {
+        // (single row) also the fp16 form, and block q / 8's exponent from its first lane
+        if ((int64_t)i * kThreads < xpieces) {
+          u32x4_t xh;
+          const int sb = x_piece_f16(q < xpieces ? xst[i] : zero, xh);
+          if (q < xpieces) {
+            lds_wr128(P.sX + (uint32_t)q * 16u, xst[i]);
+            lds_wr128(P.sXh + (uint32_t)q * 16u, xh);
+            if ((q & 7) == 0) *reinterpret_cast<__attribute__((address_space(3))) int*>((uintptr_t)(P.sXs + (uint32_t)(q >> 3) * 4u)) = sb;
+          }
+        }
+      } else if (q < xpieces) {
         const int64_t m = q / (K / 8), c8 = q % (K / 8);
         lds_wr128(P.sX + (uint32_t)((m * (K + 8) + c8 * 8) * 2), xst[i]);
       }
@@ -671,6 +806,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
     }
   }
 
+  // (single-row path) the wave multiplies the fp16 x row when all its blocks are
+  // exact (hx), else the bf16 row
+  bool hx = false;
+  if constexpr (DOT) hx = x_blocks_exact(P.sXs, kb0, kb1, lane);
+
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
   float accd[G::NP];  // single-row path: one row sum per piece
 #pragma unroll
@@ -692,17 +832,28 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
       const int col = lane % G::PR;
       const int u = col / PPB;
       const bool bval = kbs + u < kb1;  // blocks past the wave's range are read but not added
-      const uint32_t xa = P.sX + (uint32_t)((kbs * 64 + col * CP) * 2);
+      const uint32_t xa = (hx ? P.sXh : P.sX) + (uint32_t)((kbs * 64 + col * CP) * 2);
       u32x4_t xv[CP / 8];
   #pragma unroll
       for (int q = 0; q < CP / 8; ++q) xv[q] = lds_rd128(xa + 16u * q);
+      // the pieces' block scales and the lane's block exponent (blocks past the row read the
+      // array's padding, never added), read before the products so their latency is hidden
+      float ap[G::NP];
   #pragma unroll
-      for (int i = 0; i < G::NP; ++i) {
-        const int row = (i * 64 + lane) / G::PR;
-        const float ap = __uint_as_float(lds_rd32(sscale + (uint32_t)(row * CH + u) * 4));
-        const float sp = dot_piece<BITS>(__builtin_bit_cast(u32x4_t, ch.piece[i]), xv, tlane);
-        accd[i] = fmaf(ap, bval ? sp : 0.0f, accd[i]);
+      for (int i = 0; i < G::NP; ++i)
+        ap[i] = __uint_as_float(lds_rd32(sscale + (uint32_t)(((i * 64 + lane) / G::PR) * CH + u) * 4));
+      const int sb = (int)lds_rd32(P.sXs + (uint32_t)(kbs + u) * 4u);
+      float sp[G::NP];
+      if (hx) {
+  #pragma unroll
+        for (int i = 0; i < G::NP; ++i)
+          sp[i] = ldexpf(dot_piece<BITS, true>(__builtin_bit_cast(u32x4_t, ch.piece[i]), xv, tlane), -sb);
+      } else {
+  #pragma unroll
+        for (int i = 0; i < G::NP; ++i) sp[i] = dot_piece<BITS, false>(__builtin_bit_cast(u32x4_t, ch.piece[i]), xv, tlane);
       }
+  #pragma unroll
+      for (int i = 0; i < G::NP; ++i) accd[i] = fmaf(ap[i], bval ? sp[i] : 0.0f, accd[i]);
     }
   };
 
@@ -1105,25 +1256,18 @@ struct DChunk {
 // dot_piece for a 12-byte piece of 32 3-bit codes: pair p (codes 2p, 2p + 1)
 // is the 6-bit field at bits [6p, 6p + 6), an index of the 64-entry table; the
 // fields of pairs 5 and 10 straddle a word boundary (funnel shift).
+template <bool H>
 __device__ __forceinline__ float dot_piece3(const u32x3_t& pc, const u32x4_t* xv, uint32_t tl) {
-  float s0 = 0.0f, s1 = 0.0f, t0 = 0.0f, t1 = 0.0f;
+  PairAcc<H> acc;
 #pragma unroll
   for (int p = 0; p < 16; ++p) {
     const int bit = 6 * p, w = bit >> 5, sh = bit & 31;
     uint32_t e;
     if (sh <= 26) e = (pc[w] >> sh) & 63u;
     else e = __builtin_amdgcn_alignbit(pc[w + 1], pc[w], (uint32_t)sh) & 63u;
-    const u32x2v_t en = lds_entry((e << 8) | tl);
-    const uint32_t xp = xv[p >> 2][p & 3];
-    if (p & 1) {
-      s1 = dot2(en.x, xp, s1);
-      t1 = dot2(en.y, xp, t1);
-    } else {
-      s0 = dot2(en.x, xp, s0);
-      t0 = dot2(en.y, xp, t0);
-    }
+    acc.add(lds_word((e << 8) | tl), xv[p >> 2][p & 3], p & 1);
   }
-  return (s0 + s1) + (t0 + t1);
+  return acc.sum();
 }
 
 // ---------------------------------------------------------------- grouped single-row decode
@@ -1158,6 +1302,7 @@ struct GvParams {
   int32_t nl;
   int64_t total;
   uint32_t sT, sTP, sB, sX;  // LDS byte addresses: summed t, its partials, the tile's B rows, the x row
+  uint32_t sXh, sXs;         // the x row as fp16 numbers x 2^s_b, and the block exponents s_b
   GvLayer L[kGvGroupMax];
 };
 
@@ -1173,13 +1318,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv_group(GvParams P, Levels l
   const int tid = threadIdx.x;
   // (the wave index is uniform within a wave: saying so keeps the chunk loops scalar)
   const int lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const uint32_t tlane = table_lane<BITS>(lane);
-  const uint32_t stage0 = (uint32_t)PairTable<BITS>::kBytes;
+  const uint32_t tlane = table_lane_h(lane);
+  const uint32_t stage0 = (uint32_t)LevelTableH<BITS>::kBytes;
   float* sRed = reinterpret_cast<float*>(reinterpret_cast<char*>(smem) + stage0 + kWaves * 2 * kStageW);
   const float* sT = reinterpret_cast<const float*>(reinterpret_cast<const char*>(smem) + P.sT);
   const uint32_t wstage = stage0 + (uint32_t)wave * 2 * kStageW;
   const int srow = lane >> 2, sblk = lane & 3;
-  build_table_kernarg<BITS>(smem, lv, tid);  // complete at the first segment's barrier
+  build_table_h<BITS>(smem, lv, tid);  // complete at the first segment's barrier
   const int64_t c_begin = P.total * blockIdx.x / gridDim.x, c_end = P.total * (blockIdx.x + 1) / gridDim.x;
   for (int l = 0; l < P.nl; ++l) {
     const GvLayer& L = P.L[l];
@@ -1269,7 +1414,15 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv_group(GvParams P, Levels l
 #pragma unroll
       for (int i = 0; i < kXP; ++i) {
         const int64_t q = tid + (int64_t)i * kThreads;
-        if (q < xpieces) lds_wr128(P.sX + (uint32_t)q * 16u, xs[i]);
+        if (i * kThreads < xpieces) {
+          u32x4_t xh;
+          const int sb = x_piece_f16(q < xpieces ? xs[i] : u32x4_t{0u, 0u, 0u, 0u}, xh);
+          if (q < xpieces) {
+            lds_wr128(P.sX + (uint32_t)q * 16u, xs[i]);
+            lds_wr128(P.sXh + (uint32_t)q * 16u, xh);
+            if ((q & 7) == 0) *reinterpret_cast<__attribute__((address_space(3))) int*>((uintptr_t)(P.sXs + (uint32_t)(q >> 3) * 4u)) = sb;
+          }
+        }
       }
       if constexpr (ADP) {
         float* sTPw = reinterpret_cast<float*>(reinterpret_cast<char*>(smem) + P.sTP);
@@ -1291,6 +1444,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv_group(GvParams P, Levels l
         sTw[j] = acc;
       }
     }
+    // the wave multiplies the fp16 x row when all its blocks are exact (hx), else the bf16 row
+    const bool hx = x_blocks_exact(P.sXs, kb0, kb1, lane);
     float accd[G::NP];
 #pragma unroll
     for (int i = 0; i < G::NP; ++i) accd[i] = 0.0f;
@@ -1305,19 +1460,35 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv_group(GvParams P, Levels l
       const int col = lane % G::PR;
       const int u = col / PPB;
       const bool bval = kbs + u < kb1;  // blocks past the wave's range are read but not added
-      const uint32_t xa = P.sX + (uint32_t)((kbs * 64 + col * CP) * 2);
+      const uint32_t xa = (hx ? P.sXh : P.sX) + (uint32_t)((kbs * 64 + col * CP) * 2);
       u32x4_t xv[CP / 8];
 #pragma unroll
       for (int q = 0; q < CP / 8; ++q) xv[q] = lds_rd128(xa + 16u * q);
+      // the pieces' block scales and the lane's block exponent (blocks past the row read the
+      // array's padding, never added), read before the products so their latency is hidden
+      float ap[G::NP];
 #pragma unroll
-      for (int i = 0; i < G::NP; ++i) {
-        const int row = (i * 64 + lane) / G::PR;
-        const float ap = __uint_as_float(lds_rd32(sscale + (uint32_t)(row * CH + u) * 4));
-        float sp;
-        if constexpr (BITS == 3) sp = dot_piece3(ch.piece[i], xv, tlane);
-        else sp = dot_piece<BITS>(ch.piece[i], xv, tlane);
-        accd[i] = fmaf(ap, bval ? sp : 0.0f, accd[i]);
+      for (int i = 0; i < G::NP; ++i)
+        ap[i] = __uint_as_float(lds_rd32(sscale + (uint32_t)(((i * 64 + lane) / G::PR) * CH + u) * 4));
+      const int sb = (int)lds_rd32(P.sXs + (uint32_t)(kbs + u) * 4u);
+      float sp[G::NP];
+      if (hx) {
+#pragma unroll
+        for (int i = 0; i < G::NP; ++i) {
+          float v;
+          if constexpr (BITS == 3) v = dot_piece3<true>(ch.piece[i], xv, tlane);
+          else v = dot_piece<BITS, true>(ch.piece[i], xv, tlane);
+          sp[i] = ldexpf(v, -sb);
+        }
+      } else {
+#pragma unroll
+        for (int i = 0; i < G::NP; ++i) {
+          if constexpr (BITS == 3) sp[i] = dot_piece3<false>(ch.piece[i], xv, tlane);
+          else sp[i] = dot_piece<BITS, false>(ch.piece[i], xv, tlane);
+        }
       }
+#pragma unroll
+      for (int i = 0; i < G::NP; ++i) accd[i] = fmaf(ap[i], bval ? sp[i] : 0.0f, accd[i]);
     };
     auto finish_tile = [&](int32_t tl) __attribute__((always_inline)) {
 #pragma unroll
@@ -1449,6 +1620,15 @@ Plan plan_gemv(const LinearArgs& a) {
                     (dbaf || (a.A != nullptr && (reinterpret_cast<uintptr_t>(a.A) & 15) == 0));
     const size_t stage = dot ? 16 * CH * 4 : ChunkGeo<BITS>::kStage;
     size_t lds = PairTable<BITS>::kBytes + (size_t)kWaves * 2 * stage + (size_t)kWaves * 256 * sizeof(float);
+    // single-row path: the x row as fp16 numbers (read up to 256 elements past its end, like the bf16
+    // row) and its block exponents (read up to CH blocks past the row)
+    P.sXh = P.sXs = 0;
+    if (dot) {
+      P.sXh = (uint32_t)lds;
+      lds += (size_t)(a.K + 8) * 2 + 512;
+      P.sXs = (uint32_t)lds;
+      lds += r16((size_t)(nb + 8) * 4);
+    }
     // adapter product: fused, partials prefetched when they fit the registers, else summed by a loop
     const size_t mr = (size_t)a.M * (size_t)r;
     const size_t tparts = (size_t)a.t_splits * mr;
@@ -1636,9 +1816,13 @@ hipError_t launch_gv_group_b(const GvParams& P, int64_t grid, size_t shmem, bool
 
 int gemv_group_max() { return kGvGroupMax; }
 
+// Longest row of the grouped kernel: the bf16 and fp16 rows, the level table and
+// the largest adapter staging (r = 256) then fill at most 152 KB of LDS.
+constexpr int64_t kGvMaxK = 12288;
+
 bool gemv_groupable(const LinearArgs& a) {
   const int64_t r = a.r > 0 ? a.r : 0;
-  return a.M == 1 && a.xdt == DT_BF16 && a.K % 64 == 0 && a.K * 2 <= (int64_t)kXLdsMax &&
+  return a.M == 1 && a.xdt == DT_BF16 && a.K % 64 == 0 && a.K <= kGvMaxK &&
          r <= 256 && (r == 0 || (a.abdt == DT_BF16 && a.t != nullptr && (int64_t)a.t_splits * r <= kTPartsMax &&
                                  (reinterpret_cast<uintptr_t>(a.B) & 15) == 0)) &&
          a.N * (a.K / 64) * 8 * a.bits < (int64_t(1) << 31) && a.N * r * 2 < (int64_t(1) << 31) &&
@@ -1692,6 +1876,10 @@ hipError_t launch_gemv_group(const LinearArgs* ls, int n, const Levels& lv, hipS
   lds += r16((size_t)32 * maxr);
   P.sX = (uint32_t)lds;
   lds += (size_t)maxK * 2 + 512;  // the row reads up to 256 elements past its end, for blocks it does not add
+  P.sXh = (uint32_t)lds;          // the same as fp16 numbers
+  lds += (size_t)maxK * 2 + 512;
+  P.sXs = (uint32_t)lds;          // block exponents (read up to CH blocks past the row)
+  lds += r16((size_t)(maxK / 64 + 8) * 4);
   if (lds > kLdsMax) return hipErrorInvalidValue;
   int64_t tiles = 0;
   for (int i = 0; i < n; ++i) tiles += P.L[i].ntiles;

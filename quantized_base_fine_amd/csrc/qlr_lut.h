@@ -1,6 +1,7 @@
-// Level lookup of the decode kernels: a table in LDS of bf16 levels, each level
-// carried as two bf16 halves, hi = bf16(L) and lo = bf16(L - hi).  Together they
-// hold L to about 16 significant bits, so a product with a bf16 x (exact in
+// Level lookup of the decode kernels' MFMA path (several x rows, or 3-bit codes
+// on their own at M = 1): a table in LDS of bf16 levels, each level carried as
+// two bf16 halves, hi = bf16(L) and lo = bf16(L - hi).  Together they hold L
+// to about 16 significant bits, so a product with a bf16 x (exact in
 // float32 either way) is within 2^-16 of the exact one relative to |x L|; hi
 // alone can be off by up to 2^-8, which is more than the layer's 1e-3 budget
 // when every term of a sum has the same sign.
@@ -96,6 +97,25 @@ __device__ __forceinline__ void decode16(const Raw<BITS>& r, uint32_t tl, u32x4_
     }
   }
 }
+
+// Level table of the single-row decode path: each level as one fp16 number
+// (11 significant bits, so within 2^-11 of the level relative to it; every
+// level of the 2-, 3-, 4- and 8-bit codebooks is a normal fp16 number), and
+// the x row converted to fp16 with an exact power-of-two scale, so one packed
+// fp16 dot product gives two exact level x products.
+//   * 2-, 3- and 4-bit codes: entry e = the packed bits of two neighbouring
+//     codes (the lower code in the low bits), one word: the two fp16 levels,
+//     the lower code's in the low half.
+//   * 8-bit codes: entry e = one code, its fp16 level in the low half.
+// Copy L = lane of entry e sits at byte e*256 + 4L: no two lanes of a wave ever
+// read the same bank.  Like PairTable it sits at LDS address 0, and a lookup
+// address is (entry << 8) | table_lane_h(lane).
+template <int BITS>
+struct LevelTableH {
+  static constexpr int kEntries = (BITS == 8) ? 256 : (1 << (2 * BITS));
+  static constexpr int kBytes = kEntries * 256;
+};
+__device__ __forceinline__ uint32_t table_lane_h(int lane) { return 4u * (uint32_t)lane; }
 
 // float32 level pairs for the prefill dequantizer: entry e (e = two packed
 // codes, or one 8-bit code) of copy c at byte e*256 + 8c, c = lane % 32, so a
