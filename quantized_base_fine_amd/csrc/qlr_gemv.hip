@@ -74,17 +74,18 @@ struct ChunkGeo {
 
 // One chunk of a wave's stream held in registers between its loads and its
 // staging: raw code pieces, the (row, block) absmax code and group constant of
-// this lane, the x fragments of the chunk's blocks (when x is not in LDS) and,
-// for the adapter, one 16-byte piece of the tile's B rows (loaded with the
-// last chunk of a tile only; every other chunk reads it out of range, as zero).
+// this lane and the x fragments of the chunk's blocks (when x is not in LDS).
 template <int BITS, bool XLDS>
 struct Chunk {
   typename ChunkGeo<BITS>::Piece piece[ChunkGeo<BITS>::NP];
   uint32_t q8;
   float sc;
   u32x4_t x[XLDS ? 1 : CH][2];  // x fragments (unused when x is staged in LDS)
-  u32x4_t bp;
 };
+// 16-byte pieces of B rows each thread of the decode kernel loads up front:
+// all the B rows of a workgroup's tiles (2 r pieces per tile) when they number
+// at most kBPre * 512.
+constexpr int kBPre = 2;
 
 // Chunks a wave keeps in flight (the ring depth D): 4 for long streams, 2 when
 // a wave's whole stream is at most 2 chunks or x rides with the chunks.  Every
@@ -116,7 +117,7 @@ struct Params {
                  // into LDS after the first barrier; T_PREFETCH: partials loaded
                  // with the first chunks, summed into LDS; T_FUSED: x A^T
                  // computed in the kernel (per-wave sums at sTP)
-  int bpre;      // B rows of each tile ride with the tile's last chunk into LDS
+  int bpre;      // the B rows of all of a workgroup's tiles are loaded into LDS up front
   uint32_t sT;   // LDS byte addresses: summed t (M x r), raw partials, B tile, x
   uint32_t sTP;
   uint32_t sB;
@@ -521,15 +522,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
         ch.x[u][1] = *reinterpret_cast<const u32x4_t*>(xg + kb * 64 + 8);
       }
     }
-    // the tile's B rows (16 x r bf16, contiguous): piece wave * 64 + lane
-    if constexpr (ADP) {
-      const int pc = wave * 64 + lane;
-      const bool bv = !DBA && (TF || P.bpre) && ltile < P.ntiles && c == nitem - 1 && pc < 2 * r;
-      const __amdgpu_buffer_rsrc_t brs = rsrc(a.B, N * r * 2);
-      ch.bp = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                              brs, buf_off(bv, (uint32_t)ltile * (uint32_t)(32 * r) + (uint32_t)pc * 16u),
-                                              0, 0));
-    }
     if (++lc == nitem) {
       lc = 0;
       ltile += gridDim.x;
@@ -594,6 +586,23 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
         const int64_t qc = q < xpieces ? q : 0;
         xst[i] = *reinterpret_cast<const u32x4_t*>(x + qc * 8);
       }
+    }
+  }
+  // (adapter) the B rows of this workgroup's tiles, 16 x r bf16 each (tile g of
+  // the workgroup, blockIdx.x + g gridDim.x, at sB + 32 r g): piece p = tid +
+  // 512 i, issued after x and before the chunk stream, written to LDS before
+  // the first barrier
+  const int64_t ntl = (P.ntiles - blockIdx.x + gridDim.x - 1) / gridDim.x;  // tiles of this workgroup
+  const int bpieces = (ADP && !DBA && (TF || P.bpre)) ? (int)ntl * 2 * r : 0;
+  u32x4_t bpv[ADP ? kBPre : 1];
+  if constexpr (ADP) {
+    const __amdgpu_buffer_rsrc_t brs = rsrc(a.B, N * r * 2);
+#pragma unroll
+    for (int i = 0; i < kBPre; ++i) {
+      const int p = tid + i * kThreads;
+      const int gt = p / (2 * max(r, 1)), pc = p - gt * 2 * r;
+      const uint32_t off = ((uint32_t)blockIdx.x + (uint32_t)gt * gridDim.x) * (uint32_t)(32 * r) + (uint32_t)pc * 16u;
+      bpv[i] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(brs, buf_off(p < bpieces, off), 0, 0));
     }
   }
   // adapter partials, when prefetched: element tid + 512 i of the splits x M x r array
@@ -705,6 +714,13 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
         const int64_t m = q / (K / 8), c8 = q % (K / 8);
         lds_wr128(P.sX + (uint32_t)((m * (K + 8) + c8 * 8) * 2), xst[i]);
       }
+    }
+  }
+  if constexpr (ADP) {
+#pragma unroll
+    for (int i = 0; i < kBPre; ++i) {
+      const int p = tid + i * kThreads;
+      if (p < bpieces) lds_wr128(P.sB + (uint32_t)p * 16u, bpv[i]);
     }
   }
   if constexpr (ADP && !TF) {
@@ -978,6 +994,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
     }
   };
 
+  uint32_t sBt = P.sB;  // LDS B rows of the tile being finished
   // Output (m, row nn = tile row l15) = s + scale * sum_j t[m][j] B[nn][j], stored
   // when ov (else out of range).
   auto epilogue = [&](int m, int l15, int64_t nn, bool ov, float s) {
@@ -989,7 +1006,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
       const bool bpre = TF || P.bpre;
       const bool tlds = TF || P.tmode != T_GLOBAL;
       if (bpre) {
-        const uint32_t brow = P.sB + (uint32_t)(l15 * r * 2);
+        const uint32_t brow = sBt + (uint32_t)(l15 * r * 2);
         if (tlds && (r & 7) == 0) {
           // 8 ranks per step from 16-byte LDS reads (t rows and B rows are
           // 16-byte aligned when r is a multiple of 8), same order of sums
@@ -1093,7 +1110,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
           const float ab = f16_bits_to_f32(a.dba_alpha[n]) * f16_bits_to_f32(a.dba_beta[j < r ? j : 0]);
           bj = j < r ? (((w1 >> j) & 1u) ? ab : -ab) : 0.0f;
         } else {
-          bj = j < r ? bf16_bits_to_f32(lds_rd16(P.sB + (uint32_t)((o * r + j) * 2))) : 0.0f;
+          bj = j < r ? bf16_bits_to_f32(lds_rd16(sBt + (uint32_t)((o * r + j) * 2))) : 0.0f;
         }
         const float lo = group_sum<16>(tj * bj);
         float s = 0.0f;
@@ -1117,7 +1134,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
         if constexpr (SPX != 0) s += sp_sum(o);
         float lo = 0.0f;
         for (int j = q; j < r; j += 32)
-          lo = fmaf(sT[j], bf16_bits_to_f32(lds_rd16(P.sB + (uint32_t)((o * r + j) * 2))), lo);
+          lo = fmaf(sT[j], bf16_bits_to_f32(lds_rd16(sBt + (uint32_t)((o * r + j) * 2))), lo);
 #pragma unroll
         for (int d = 1; d < 32; d <<= 1) lo += __shfl_xor(lo, d, 64);
         const int64_t nn = tl * 16 + o;
@@ -1153,7 +1170,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
         const int l15 = l & 15;
         const int64_t nn = tl * 16 + l15;
         const int mc = m < M ? m : M - 1;
-        const uint32_t trow = P.sT + (uint32_t)(mc * r * 4), brow = P.sB + (uint32_t)(l15 * r * 2);
+        const uint32_t trow = P.sT + (uint32_t)(mc * r * 4), brow = sBt + (uint32_t)(l15 * r * 2);
         float lo = 0.0f;
         for (int j = 8 * hh; j < r; j += 16) {
           const u32x4_t t0 = lds_rd128(trow + 4u * j), t1 = lds_rd128(trow + 4u * j + 16u);
@@ -1182,8 +1199,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
         epilogue(m, l & 15, nn, tid < 256 && m < M && nn < N, s);
       }
     }
-    // the next tile reuses sRed and the B tile; after the workgroup's last tile
-    // nothing is reused
+    sBt += (uint32_t)(32 * r);  // the next tile's B rows
+    // the next tile reuses sRed; after the workgroup's last tile nothing is reused
     if (tl + gridDim.x < P.ntiles) __syncthreads();
   };
 
@@ -1202,10 +1219,6 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
       }
       buf ^= 1;
       if (cc == nitem - 1) {
-        if constexpr (ADP) {
-          const int pc = wave * 64 + lane;
-          if (!DBA && (TF || P.bpre) && pc < 2 * r) lds_wr128(P.sB + (uint32_t)pc * 16u, ring[s].bp);
-        }
         if constexpr (TF) {
           if (ctile == blockIdx.x) compute_t();
         }
@@ -1651,11 +1664,14 @@ Plan plan_gemv(const LinearArgs& a) {
         P.tmode = T_LOOP;
         lds += r16(mr * 4);
       }
-      // B rows of a tile: 2r 16-byte pieces over the 512 threads, from a 16-byte aligned B
-      if (2 * r <= kThreads && (reinterpret_cast<uintptr_t>(a.B) & 15) == 0 && lds + r16(32 * r) <= kLdsMax) {
+      // the B rows of every tile of a workgroup (2 r 16-byte pieces per tile, at most
+      // kBPre per thread), from a 16-byte aligned B
+      const int64_t tpw = (P.ntiles + pl.grid - 1) / pl.grid;
+      if (tpw * 2 * r <= (int64_t)kBPre * kThreads && (reinterpret_cast<uintptr_t>(a.B) & 15) == 0 &&
+          lds + r16((size_t)(32 * r * tpw)) <= kLdsMax) {
         P.bpre = 1;
         P.sB = (uint32_t)lds;
-        lds += r16(32 * r);
+        lds += r16((size_t)(32 * r * tpw));
       }
     }
     // x staged in LDS (rows at stride K + 8 bf16) when small enough (+512 bytes:

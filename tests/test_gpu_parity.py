@@ -157,6 +157,21 @@ def test_linear_paths_small(bits, path, M, r):
         check_linear(y, lin, wd, rows, ydt)
 
 
+@pytest.mark.parametrize("bits", [4, 3])
+@pytest.mark.parametrize("r", [80, 128])
+@pytest.mark.parametrize("M", [1, 8])
+def test_decode_adapter_many_tiles(bits, r, M):
+    """20487 rows (1281 tiles of 16: 5 or 6 per workgroup on a 256-CU grid): the B rows of all of a
+    workgroup's tiles go to LDS up front when they are at most 1024 16-byte pieces (r 80: 960), else the
+    epilogue reads them from global memory (r 128: 1536); both against the oracle, every output."""
+    lin = _small_linear(20487, 256, M, bits, r, seed=11 + r + M)
+    qw = _gpu_quant(lin.W, "f16", bits)
+    rows = list(range(lin.N))
+    wd = oracle_rows_dequant(lin.W, "f16", bits, rows)
+    for ydt in ("f32", "bf16"):
+        check_linear(_run_linear(lin, qw, ydt, qlr.PATH_GEMV), lin, wd, rows, ydt)
+
+
 @pytest.mark.parametrize("path,M", [("gemv", 1), ("gemv", 7), ("gemm", 130), ("f32", 7)])
 def test_linear_long_k_tail(path, M):
     """K = 11008 (172 blocks: DQ groups straddle rows, waves get partial chunks), N = 100, every path."""
