@@ -30,9 +30,10 @@ __global__ __launch_bounds__(256) void k_lora_t_valu(const void* __restrict__ x,
   if (lane == 0) t[m * r + j] = acc;
 }
 
-// bf16 x and A, M > 16: t[m][j] in one pass (no K split).  blockIdx.x: 16-row
-// tile of x; blockIdx.y: 16 adapter rows.  The 4 waves split K in 64-element
-// blocks.  A wave loads its x and A pieces coalesced (16-byte pieces, 8 lanes
+// bf16 x and A, M > 16: t[m][j] in one pass (no K split).  A workgroup takes
+// a tile of mt x rows (16, or 8 when 16-row tiles would leave CUs idle: the
+// MFMA's other 8 rows then read zero) and 16 adapter rows.  Its 8 waves split
+// K in 64-element blocks.  A wave loads its x and A pieces coalesced (16-byte pieces, 8 lanes
 // per 128-byte row segment, through buffer resources: rows past M or r and
 // blocks past the wave's range read zero, so every load is unconditional),
 // keeps the next block in flight in registers, stages the current one in its
@@ -59,7 +60,10 @@ __device__ __forceinline__ uint32_t t_off(bool ok, uint32_t off) {
 }
 // One launch covers up to kTGroupMax independent products of one M (a mixed
 // stack's adapters in groups; a single product is a group of one).  Tiles are
-// numbered layer by layer, x-row tiles outer, adapter-row tiles inner.
+// numbered layer by layer, x-row tiles outer, adapter-row tiles inner, and
+// dealt to the XCDs in contiguous ranges (workgroup b runs on XCD b % 8 and
+// takes tile (b % 8) per_xcd + b / 8), so the adapter-row tiles of one x-row
+// tile share an XCD and its L2 reads those x rows from HBM once.
 constexpr int kTGroupMax = 16;
 struct TLayer {
   const uint16_t* x;
@@ -69,28 +73,34 @@ struct TLayer {
   int32_t r, jtiles, bt;
   int64_t tile0;
 };
+constexpr int kTtWaves = 8;
 struct TGroup {
   int64_t M;
+  int32_t mt;       // x rows per tile (16 or 8)
+  int64_t ntiles;   // tiles of all layers
+  int64_t per_xcd;  // tiles per XCD: the grid is 8 per_xcd workgroups
   int32_t nl;
   TLayer L[kTGroupMax];
 };
-__global__ __launch_bounds__(256) void k_lora_t_tile(TGroup G) {
-  __shared__ __attribute__((aligned(16))) char lds[4 * kTSlice];
-  __shared__ float red[4][256];
+__global__ __launch_bounds__(kTtWaves * 64) void k_lora_t_tile(TGroup G) {
+  __shared__ __attribute__((aligned(16))) char lds[kTtWaves * kTSlice];
+  __shared__ float red[kTtWaves][256];
+  const int64_t tile = (int64_t)(blockIdx.x & 7) * G.per_xcd + (blockIdx.x >> 3);
+  if (tile >= G.ntiles) return;  // whole workgroup, before any barrier
   int li = 0;
-  while (li + 1 < G.nl && (int64_t)blockIdx.x >= G.L[li + 1].tile0) ++li;
+  while (li + 1 < G.nl && tile >= G.L[li + 1].tile0) ++li;
   const TLayer& Ly = G.L[li];
   const uint16_t* __restrict__ x = Ly.x;
   const uint16_t* __restrict__ A = Ly.A;
   float* __restrict__ t = Ly.t;
   const int64_t M = G.M, K = Ly.K;
   const int r = Ly.r;
-  const int64_t lt = (int64_t)blockIdx.x - Ly.tile0;
+  const int64_t lt = tile - Ly.tile0;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int64_t m0 = (lt / Ly.jtiles) * 16, j0 = (lt % Ly.jtiles) * 16;
+  const int64_t m0 = (lt / Ly.jtiles) * G.mt, j0 = (lt % Ly.jtiles) * 16;
   const int64_t nb = K / 64;
-  const int64_t kb0 = nb * wave / 4, kb1 = nb * (wave + 1) / 4;
-  const int64_t mrows = std::min<int64_t>(16, M - m0), jrows = std::min<int64_t>(16, (int64_t)r - j0);
+  const int64_t kb0 = nb * wave / kTtWaves, kb1 = nb * (wave + 1) / kTtWaves;
+  const int64_t mrows = std::min<int64_t>(G.mt, M - m0), jrows = std::min<int64_t>(16, (int64_t)r - j0);
   const __amdgpu_buffer_rsrc_t xr = __builtin_amdgcn_make_buffer_rsrc(
       const_cast<uint16_t*>(x + m0 * K), (short)0, (int)(mrows * K * 2), 0x00020000);
   // bt: the adapter operand is given as K x r (the backward's B, for u = dy B);
@@ -159,11 +169,16 @@ __global__ __launch_bounds__(256) void k_lora_t_tile(TGroup G) {
   for (int v = 0; v < 4; ++v) red[wave][lane * 4 + v] = acc[v];
   __syncthreads();
   const int e = threadIdx.x;
-  const float sum = (red[0][e] + red[1][e]) + (red[2][e] + red[3][e]);
-  const int l = e >> 2, v = e & 3;
-  const int64_t m = m0 + 4 * (l >> 4) + v;  // MFMA output row
-  const int64_t j = j0 + (l & 15);          // MFMA output column
-  if (m < M && j < r) t[m * r + j] = sum;
+  if (e < 256) {
+    float sum = 0.0f;
+#pragma unroll
+    for (int w = 0; w < kTtWaves; ++w) sum += red[w][e];  // wave order
+    const int l = e >> 2, v = e & 3;
+    const int mi = 4 * (l >> 4) + v;        // MFMA output row
+    const int64_t m = m0 + mi;
+    const int64_t j = j0 + (l & 15);        // MFMA output column
+    if (mi < G.mt && m < M && j < r) t[m * r + j] = sum;
+  }
 }
 
 // bf16 x and A, M <= 16 (one 16-row MFMA tile): K-split partial sums
@@ -405,8 +420,13 @@ hipError_t launch_lora_t_group(const LoraTItem* items, int n, int64_t M, hipStre
   TGroup G;
   G.M = M;
   G.nl = 0;
+  int64_t jt = 0;
+  for (int i = 0; i < n; ++i)
+    if (items[i].r > 0) jt += (items[i].r + 15) / 16;
+  // 8-row tiles when 16-row ones would give fewer workgroups than CUs
+  G.mt = ((M + 15) / 16) * jt < 256 ? 8 : 16;
   int64_t t0 = 0;
-  const int64_t mtiles = (M + 15) / 16;
+  const int64_t mtiles = (M + G.mt - 1) / G.mt;
   for (int i = 0; i < n; ++i) {
     const LoraTItem& it = items[i];
     if (it.r <= 0) continue;
@@ -425,7 +445,9 @@ hipError_t launch_lora_t_group(const LoraTItem* items, int n, int64_t M, hipStre
     t0 += mtiles * L.jtiles;
   }
   if (G.nl == 0) return hipSuccess;
-  hipLaunchKernelGGL(k_lora_t_tile, dim3((unsigned)t0), dim3(256), 0, s, G);
+  G.ntiles = t0;
+  G.per_xcd = (t0 + 7) / 8;
+  hipLaunchKernelGGL(k_lora_t_tile, dim3((unsigned)(8 * G.per_xcd)), dim3(kTtWaves * 64), 0, s, G);
   return hipGetLastError();
 }
 
