@@ -210,6 +210,11 @@ __device__ __forceinline__ void dequant_pairs(const Codes32<BITS>& c, float ap, 
 __device__ __forceinline__ uint32_t swz(uint32_t r) {
   return (r ^ ((r >> 2) & 1u) ^ ((r >> 3) & 1u)) & 7u;
 }
+// Physical 16-byte chunk of logical chunk c (0..15) of row R of the transposed
+// GEMM's weight tile: c ^ (0, 6, 10, 12)[R mod 4] ^ bit 3 of c.
+__device__ __forceinline__ uint32_t tr_chunk(uint32_t c, uint32_t R) {
+  return c ^ ((0xCA60u >> (4u * (R & 3u))) & 15u) ^ ((c >> 3) & 1u);
+}
 
 // Level table in LDS for widths other than 4 (built once per workgroup).
 template <int BITS>
@@ -265,10 +270,15 @@ struct GemmParams {
 // columns.  The x operand is dy (M x N), the output dx (M x K), the adapter
 // operand A (r x K).  Per 64-row step the producers dequantize a 64 x 128
 // slice of W' (two blocks of each of 64 rows; four lanes read a row's codes
-// together) into a row-major LDS tile whose 16-byte chunks are XOR-swizzled by
-// 5 (row mod 4).  The consumers read the B fragments (8 consecutive rows of one
-// column per lane) with the LDS transpose read, two 4-row reads per fragment;
-// 4 consecutive rows then fall in 4 distinct 64-byte windows of the banks.
+// together) into a row-major LDS tile of 256-byte rows whose 16-byte chunks are
+// XOR-swizzled (tr_chunk).  The consumers read the B fragments (8 consecutive
+// rows of one column per lane) with the LDS transpose read, two 4-row reads per
+// fragment.  The swizzle keeps both access streams free of bank conflicts
+// whether the LDS serves 128 or 256 bytes per cycle: the producers' 16-byte
+// stores (8 lanes = 2 rows x 4 chunks c, c + 4, c + 8, c + 12 per cycle, or 16
+// lanes = 4 rows), and the transposed 8-byte reads (16 lanes = 4 rows x 2
+// chunks x 2 halves per cycle, or 32 lanes).  Chunks c and c + 8 of a row share
+// a 128-byte bank window, which the XOR with bit 3 of c pulls apart.
 template <int BITS, int YDT, bool ADP, bool TR>
 __global__ __launch_bounds__(512, 1) void k_gemm(GemmParams P, Levels lv) {
   extern __shared__ uint32_t smem[];
@@ -360,7 +370,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm(GemmParams P, Levels lv) {
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       if constexpr (TR)
-        wst[q] = kWOff + (uint32_t)(rr * 256) + ((((uint32_t)(8 * bq + 4 * dh + q)) ^ (5u * ((uint32_t)rr & 3u))) << 4);
+        wst[q] = kWOff + (uint32_t)(rr * 256) + (tr_chunk((uint32_t)(8 * bq + 4 * dh + q), (uint32_t)rr) << 4);
       else
         wst[q] = kWOff + (uint32_t)(rr * 128) + ((((uint32_t)(4 * dh + q)) ^ swz((uint32_t)rr & 15u)) << 4);
     }
@@ -608,7 +618,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm(GemmParams P, Levels lv) {
 #pragma unroll
       for (int c = 0; c < 2; ++c) {
         const uint32_t chunk = 8u * nh + 4u * c + 2u * (g & 1u) + ((sp >> 1) & 1u);
-        tbo[c] = (8u * h + (sp >> 2)) * 256u + ((chunk ^ (5u * (sp >> 2))) << 4) + 8u * (sp & 1u);
+        tbo[c] = (8u * h + (sp >> 2)) * 256u + (tr_chunk(chunk, sp >> 2) << 4) + 8u * (sp & 1u);
       }
     }
 
