@@ -317,8 +317,13 @@ qlr_status qlr_quantize_outliers(const void* W, qlr_dtype wdt, int64_t rows, int
  * with row_ptr nondecreasing from 0 to nnz and columns in [0, cols) (a
  * malformed one gives wrong values; the kernels clamp every index they read).
  * The sparse term is formed in float32 (outliers in CSR order) and added to
- * each output before rounding.  Arguments otherwise as qlr_linear_fwd; the
- * error bound's S also sums |x[m, col] val| over the row's outliers.
+ * each output before rounding, except on the prefill GEMM family with 2- or
+ * 4-bit codes: there each 128-row tile of the weight whose entries fit the
+ * kernel's spare LDS (about 2000 with 4-bit codes, 1500 with 2-bit) adds them
+ * to its dequantized bf16 weights, rounding each changed weight to bf16 again
+ * (within that family's bound), and only the other tiles take the float32 term.
+ * Arguments otherwise as qlr_linear_fwd; the error bound's S also sums
+ * |x[m, col] val| over the row's outliers.
  * ws >= qlr_workspace_bytes(QLR_OP_LINEAR_OUTLIERS, M, rows, cols, r).
  * Asynchronous, allocation-free.
  */

@@ -72,6 +72,15 @@ struct GemmTable {
 template <int BITS>
 constexpr uint32_t gemm_lds_bytes() { return kTOff + GemmTable<BITS>::kBytes; }
 static_assert(gemm_lds_bytes<3>() <= 160 * 1024 && gemm_lds_bytes<8>() <= 160 * 1024, "LDS budget");
+// Outlier side channel of the forward (2- and 4-bit codes, whose level tables
+// leave LDS free): after the tiles and the table, the tile's row offsets
+// (kGemmTileRows + 1 int32, 528 bytes with padding), then its columns and values.
+constexpr uint32_t kLdsAll = 160 * 1024;
+template <int BITS>
+constexpr uint32_t gemm_sp_off() { return (gemm_lds_bytes<BITS>() + 15u) & ~15u; }
+template <int BITS>
+constexpr int gemm_sp_cap() { return (BITS == 2 || BITS == 4) ? (int)((kLdsAll - gemm_sp_off<BITS>() - 528) / 8) : 0; }
+static_assert(BN == kGemmTileRows, "the side channel's tile rows are the GEMM's");
 
 // Raw codes of one thread for one block: the 32 codes [32h, 32h+32) of a weight row.
 template <int BITS>
@@ -247,7 +256,11 @@ struct GemmLayer {
   const float* t;   // splits x M x r partial sums of x A^T (r > 0)
   const void* B;    // N x r
   void* y;
-  const float* addend;  // M x N float32 or null (forward only)
+  const float* addend;  // M x N float32 or null (forward only; with the side channel: its other tiles)
+  const int32_t* sp_rp;  // forward: CSR side channel added to the weight tiles that hold it (or null)
+  const int32_t* sp_col;
+  const float* sp_val;
+  int64_t sp_nnz;
   int64_t N, K;
   int32_t r, t_splits;
   float scale;
@@ -279,7 +292,7 @@ struct GemmParams {
 // lanes = 4 rows), and the transposed 8-byte reads (16 lanes = 4 rows x 2
 // chunks x 2 halves per cycle, or 32 lanes).  Chunks c and c + 8 of a row share
 // a 128-byte bank window, which the XOR with bit 3 of c pulls apart.
-template <int BITS, int YDT, bool ADP, bool TR>
+template <int BITS, int YDT, bool ADP, bool TR, bool SPF>
 __global__ __launch_bounds__(512, 1) void k_gemm(GemmParams P, Levels lv) {
   extern __shared__ uint32_t smem[];
   // XCD-aware tile order: workgroup b runs on XCD b % 8
@@ -327,6 +340,28 @@ __global__ __launch_bounds__(512, 1) void k_gemm(GemmParams P, Levels lv) {
     build_gemm_table<BITS>(sL, tid);
   }
   __syncthreads();
+
+  // Outlier side channel (forward, SPF instantiations only): when the entries of the tile's weight rows
+  // n0 .. n0 + 127 fit in LDS, the consumers stage them while the producers'
+  // first loads are in flight, and each producer thread adds its row's entries
+  // to the bf16 weights it has just dequantized (then rounded again to bf16);
+  // otherwise the tile adds the float32 addend, which holds its rows.  The
+  // offsets are clamped exactly as the addend kernel clamps them, so both agree
+  // on which tiles are whose.
+  constexpr int kSpCap = (TR || !SPF) ? 0 : gemm_sp_cap<BITS>();
+  constexpr uint32_t kSpRo = gemm_sp_off<BITS>(), kSpCol = kSpRo + 528u, kSpVal = kSpCol + 4u * (uint32_t)kSpCap;
+  bool spf = false;
+  int64_t sp_e0 = 0, sp_cnt = 0;
+  if (kSpCap > 0 && Lr.sp_rp != nullptr) {
+    const int64_t nnz = Lr.sp_nnz;
+    const int64_t e0 = min<int64_t>(max<int64_t>(Lr.sp_rp[n0], 0), nnz);
+    const int64_t e1 = max<int64_t>(e0, min<int64_t>(Lr.sp_rp[min(n0 + BN, N)], nnz));
+    sp_e0 = e0;
+    sp_cnt = e1 - e0;
+    spf = sp_cnt <= kSpCap;
+  }
+  typedef __attribute__((address_space(3))) int lds_int_t;
+  auto lds_i32 = [](uint32_t addr) { return *reinterpret_cast<const lds_int_t*>((uintptr_t)addr); };
 
   if (wave >= 4) {
     // =================== producers: x staging and dequantization ===================
@@ -421,7 +456,41 @@ __global__ __launch_bounds__(512, 1) void k_gemm(GemmParams P, Levels lv) {
       for (int q = 0; q < 4; ++q)
         lds_store_u32x4(wst[q] + buf * kWTile, u32x4_t{o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]});
     };
-    auto dequant_store = [&](const CS& cs, int buf) {
+    // (side channel) the thread's cursor over its row's entries: index of the
+    // next one, the end, and the next two entries' columns (INT_MAX past the end)
+    // and values in registers, so the test of a block never waits for LDS
+    int sp_e = 0, sp_end = 0, sp_nc = INT_MAX, sp_nc2 = INT_MAX;
+    float sp_nv = 0.0f, sp_nv2 = 0.0f;
+    auto sp_load = [&](int e, int& c, float& v) {
+      const uint32_t ec = (uint32_t)min(e, kSpCap - 1);  // read in range; past the end the entry is dropped
+      const int cc = lds_i32(kSpCol + 4u * ec);
+      v = lds_f32(kSpVal + 4u * ec);
+      c = e < sp_end ? cc : INT_MAX;
+    };
+    // after block kbk's weights are in buffer buf: add the entries of columns
+    // [64 kbk + 32 dh, + 32) to them, one packed bf16 LDS atomic add each (the
+    // residual rounded to bf16, the sum rounded to nearest even)
+    auto sp_patch = [&](int64_t kbk, int buf) {
+      if constexpr (kSpCap > 0) {
+        const int lo = (int)(64 * kbk) + 32 * dh, hi = lo + 32;
+        while (sp_nc < hi) {
+          if (sp_nc >= lo) {
+            const uint32_t idx = (uint32_t)(sp_nc - lo);
+            const uint32_t ad = kWOff + (uint32_t)buf * kWTile + (uint32_t)(rr * 128) +
+                                (((4u * (uint32_t)dh + (idx >> 3)) ^ swz((uint32_t)rr & 15u)) << 4) + 4u * ((idx & 7u) >> 1);
+            const __bf16 hv = (__bf16)sp_nv, zv = (__bf16)0.0f;
+            const bf16x2_t add = (idx & 1u) ? bf16x2_t{zv, hv} : bf16x2_t{hv, zv};
+            __builtin_amdgcn_ds_atomic_fadd_v2bf16(
+                reinterpret_cast<__attribute__((address_space(3))) bf16x2_t*>((uintptr_t)ad), add);
+          }
+          ++sp_e;
+          sp_nc = sp_nc2;
+          sp_nv = sp_nv2;
+          sp_load(sp_e + 1, sp_nc2, sp_nv2);
+        }
+      }
+    };
+    auto dequant_store = [&](const CS& cs, int buf, int64_t kbk) {
       const DQ d = dq_begin(cs);
       uint32_t o[16];
       dq_part(d, std::integral_constant<int, 0>{}, o);
@@ -429,6 +498,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm(GemmParams P, Levels lv) {
       dq_part(d, std::integral_constant<int, 2>{}, o);
       dq_part(d, std::integral_constant<int, 3>{}, o);
       store_w(o, buf);
+      sp_patch(kbk, buf);
     };
 
     // Block k+2 is written while the consumers multiply block k.  x(j) and
@@ -440,7 +510,14 @@ __global__ __launch_bounds__(512, 1) void k_gemm(GemmParams P, Levels lv) {
     if (!(ADP && nb == 1)) load_x_lds(min<int64_t>(1, kbl), 1);
     load_c(c1, min<int64_t>(1, kbl));
     load_c(c2, min<int64_t>(2, kbl));
-    dequant_store(c0, 0);
+    if (spf) {
+      __syncthreads();  // the consumers have staged the tile's side channel
+      sp_e = lds_i32(kSpRo + 4u * (uint32_t)rr);
+      sp_end = lds_i32(kSpRo + 4u * (uint32_t)(rr + 1));
+      sp_load(sp_e, sp_nc, sp_nv);
+      sp_load(sp_e + 1, sp_nc2, sp_nv2);
+    }
+    dequant_store(c0, 0, 0);
     load_c(c0, min<int64_t>(3, kbl));
     // ADP: adapter block j >= nb (a = j - nb, adapter columns [32 a, 32 a + 32))
     // into buffer j % 3.  x side (thread = tile row): [hi(s t) | lo(s t)], t the
@@ -535,7 +612,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm(GemmParams P, Levels lv) {
     if (ADP && nb == 1) {
       adapter_write(1);
     } else {
-      dequant_store(c1, 1);
+      dequant_store(c1, 1, min<int64_t>(1, kbl));
     }
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // x of blocks 0 and 1 in LDS
     __syncthreads();
@@ -560,6 +637,8 @@ __global__ __launch_bounds__(512, 1) void k_gemm(GemmParams P, Levels lv) {
       __builtin_amdgcn_sched_barrier(0);
       dq_part(d, std::integral_constant<int, 3>{}, o);
       store_w(o, bw);
+      __builtin_amdgcn_sched_barrier(0);
+      sp_patch(min(k + 2, kbl), bw);
       __builtin_amdgcn_sched_barrier(0);
       asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
       __syncthreads();
@@ -630,6 +709,21 @@ __global__ __launch_bounds__(512, 1) void k_gemm(GemmParams P, Levels lv) {
 #pragma unroll
         for (int v = 0; v < 16; ++v) acc[i][c][v] = 0.0f;
 
+    if (spf) {
+      // the tile's row offsets (relative to its first entry, clamped into [0, count];
+      // rows past N get count) and entries (columns clamped into the row), for the producers
+      typedef __attribute__((address_space(3))) float lds_float_t;
+      for (int i = tid; i <= BN; i += 256) {
+        const int64_t v = min<int64_t>(max<int64_t>(Lr.sp_rp[min(n0 + i, N)], sp_e0), sp_e0 + sp_cnt) - sp_e0;
+        *reinterpret_cast<lds_int_t*>((uintptr_t)(kSpRo + 4u * (uint32_t)i)) = (int)v;
+      }
+      for (int64_t j = tid; j < sp_cnt; j += 256) {
+        *reinterpret_cast<lds_int_t*>((uintptr_t)(kSpCol + 4u * (uint32_t)j)) =
+            min<int32_t>(max<int32_t>(Lr.sp_col[sp_e0 + j], 0), (int32_t)(K - 1));
+        *reinterpret_cast<lds_float_t*>((uintptr_t)(kSpVal + 4u * (uint32_t)j)) = Lr.sp_val[sp_e0 + j];
+      }
+      __syncthreads();  // matches the producers' side-channel barrier
+    }
     __syncthreads();  // producers: blocks 0 and 1 written
     // fragments of three MFMA steps in registers: step g (of 12 in the 3-block
     // unrolled loop) uses slot g % 3 while the reads of step g + 2 are in flight
@@ -696,7 +790,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm(GemmParams P, Levels lv) {
     constexpr uint32_t RS = 128 * ES + 16;  // padded row stride (bytes)
     // with an addend (forward only) the tile is staged in float32 whatever the
     // output type: the addend is added, and the sum rounded, by the store pass
-    const bool stage32 = !TR && a.addend != nullptr;
+    const bool stage32 = !TR && a.addend != nullptr && !spf;
     if (stage32) {
       constexpr uint32_t RS4 = 128 * 4 + 16;
 #pragma unroll
@@ -728,7 +822,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm(GemmParams P, Levels lv) {
     __syncthreads();  // staging written
   }
   // ---- coalesced global stores of the staged tile by all 512 threads
-  if (!TR && a.addend != nullptr) {
+  if (!TR && a.addend != nullptr && !spf) {
     // float32 staging: 16-byte chunk idx = tid + 512 q holds columns 4 (idx % 32) ..
     // + 3 of row idx / 32; all 16 addend chunks of a thread are loaded first
     // (clamped addresses, 16-byte loads when the rows are 16-byte aligned)
@@ -813,10 +907,11 @@ int64_t gemm_max_rows(int64_t K) {
   return std::max<int64_t>(BM, ((int64_t(1) << 31) - 1) / row_bytes / BM * BM);
 }
 
-template <int BITS, int YDT, bool ADP, bool TR>
+template <int BITS, int YDT, bool ADP, bool TR, bool SPF = false>
 hipError_t launch_gemm_t(const LinearArgs* ls, int n, const Levels& lv, hipStream_t s) {
-  const size_t shmem = gemm_lds_bytes<BITS>();
-  auto kern = k_gemm<BITS, YDT, ADP, TR>;
+  // SPF (the outlier side channel added to the weight tiles): its staging takes the rest of LDS
+  const size_t shmem = SPF ? kLdsAll : gemm_lds_bytes<BITS>();
+  auto kern = k_gemm<BITS, YDT, ADP, TR, SPF>;
   static bool attr = false;
   if (!attr) {
     // the kernel addresses LDS from 0: it must not have static LDS
@@ -825,7 +920,7 @@ hipError_t launch_gemm_t(const LinearArgs* ls, int n, const Levels& lv, hipStrea
     if (e != hipSuccess) return e;
     if (fa.sharedSizeBytes != 0) return hipErrorInvalidKernelFile;
     e = hipFuncSetAttribute(reinterpret_cast<const void*>(kern),
-                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)shmem);
+                            hipFuncAttributeMaxDynamicSharedMemorySize, (int)kLdsAll);
     if (e != hipSuccess) return e;
     attr = true;
   }
@@ -857,6 +952,10 @@ hipError_t launch_gemm_t(const LinearArgs* ls, int n, const Levels& lv, hipStrea
       L.B = a.B;
       L.y = a.y;
       L.addend = a.addend;
+      L.sp_rp = SPF ? a.sp_row_ptr : nullptr;
+      L.sp_col = a.sp_col;
+      L.sp_val = a.sp_val;
+      L.sp_nnz = a.sp_nnz;
       L.N = a.N;
       L.K = a.K;
       L.r = a.r;
@@ -879,6 +978,17 @@ template <int BITS, bool TR>
 hipError_t launch_gemm_b(const LinearArgs* ls, int n, const Levels& lv, hipStream_t s) {
   bool adp = false;
   for (int i = 0; i < n; ++i) adp = adp || ls[i].r > 0;
+  if constexpr (!TR && (BITS == 2 || BITS == 4)) {
+    // one linear whose outlier side channel goes into its weight tiles
+    if (n == 1 && ls[0].sp_gemm && ls[0].sp_row_ptr != nullptr) {
+      if (adp) {
+        if (ls[0].ydt == DT_F32) return launch_gemm_t<BITS, DT_F32, true, false, true>(ls, n, lv, s);
+        return launch_gemm_t<BITS, DT_BF16, true, false, true>(ls, n, lv, s);
+      }
+      if (ls[0].ydt == DT_F32) return launch_gemm_t<BITS, DT_F32, false, false, true>(ls, n, lv, s);
+      return launch_gemm_t<BITS, DT_BF16, false, false, true>(ls, n, lv, s);
+    }
+  }
   if (adp) {
     if (ls[0].ydt == DT_F32) return launch_gemm_t<BITS, DT_F32, true, TR>(ls, n, lv, s);
     return launch_gemm_t<BITS, DT_BF16, true, TR>(ls, n, lv, s);
@@ -896,6 +1006,14 @@ hipError_t launch_gemm(const LinearArgs& a, const Levels& lv, hipStream_t s) {
 int gemm_group_max() { return kGroupMax; }
 
 int64_t gemm_max_rows_of(int64_t KC) { return gemm_max_rows(KC); }
+
+int64_t gemm_sparse_cap(int bits) {
+  switch (bits) {
+    case 2: return gemm_sp_cap<2>();
+    case 4: return gemm_sp_cap<4>();
+    default: return 0;
+  }
+}
 
 hipError_t launch_gemm_group(const LinearArgs* ls, int n, const Levels& lv, hipStream_t s) {
   if (n <= 0) return hipSuccess;

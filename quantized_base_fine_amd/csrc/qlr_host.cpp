@@ -247,6 +247,7 @@ qlr_status run_linear(const LinearCheck& c, float scale, char* ws, qlr_path path
     a.sp_val = sp->val;
     a.sp_nnz = sp->nnz;
     a.sp_wht_lp = wht_lp;
+    a.sp_gemm = path == QLR_PATH_GEMM && wht_lp < 0;
   }
   if (c.r > 0 && !(path == QLR_PATH_GEMV && qlr::gemv_fuses_adapter(a))) {
     e = qlr::launch_lora_t(c.x, (int)c.xdt, c.M, c.w->cols, c.A, (int)c.abdt, c.r,
@@ -883,13 +884,16 @@ qlr_status qlr_linear_fwd_outliers(const void* x, qlr_dtype xdt, int64_t M, cons
     return run_linear(c, scale, wsp, path, s, nullptr, sp);
   float* C = reinterpret_cast<float*>(wsp + linear_ws_bytes(M, w->cols, r));
   const float* addend = nullptr;
+  // the prefill GEMM adds a 128-row tile's entries to its weights itself when they
+  // fit (gemm_sparse_cap); the float32 addend then holds only the other tiles' rows
+  const bool gemm_sp = path == QLR_PATH_GEMM && qlr::gemm_sparse_cap(w->bits) > 0;
   if (sp->nnz > 0) {
     const hipError_t e = qlr::launch_sparse_addend(x, (int)xdt, M, w->cols, w->rows, sp->row_ptr, sp->col, sp->val,
-                                                   sp->nnz, C, s);
+                                                   sp->nnz, C, s, gemm_sp ? qlr::gemm_sparse_cap(w->bits) : -1);
     if (e != hipSuccess) return hip_fail(e, "sparse term launch");
     addend = C;
   }
-  return run_linear(c, scale, wsp, path, s, addend);
+  return run_linear(c, scale, wsp, path, s, addend, gemm_sp && sp->nnz > 0 ? sp : nullptr);
 }
 
 qlr_status qlr_linear_fwd_wha(const void* x, qlr_dtype xdt, int64_t M, const qlr_qweight* w, const qlr_sparse* F,

@@ -82,6 +82,11 @@ struct LinearArgs {
   // >= 0: the side channel multiplies the Walsh-Hadamard transform of x over
   // blocks of 2^sp_wht_lp columns, scaled by 2^-sp_wht_lp, instead of x
   int sp_wht_lp = -1;
+  // prefill GEMM (forward): the CSR side channel's entries are added to the
+  // dequantized weights of every 128-row tile whose entries number at most
+  // gemm_sparse_cap(bits); the other tiles add `addend`, which then holds
+  // their rows (launch_sparse_addend with that cap)
+  bool sp_gemm = false;
   // optional double-binary branch (l = 1, r = its rank <= 16) summed inside the
   // single-row decode kernel in place of A and B (see gemv_fuses_dba)
   const uint32_t* dba_b1 = nullptr;
@@ -114,6 +119,10 @@ bool gemv_groupable(const LinearArgs& a);
 hipError_t launch_gemv_group(const LinearArgs* ls, int n, const Levels& lv, hipStream_t s);
 // bf16 tiled GEMM path.
 hipError_t launch_gemm(const LinearArgs& a, const Levels& lv, hipStream_t s);
+// Weight rows per tile of the prefill GEMM, and the most side-channel entries a
+// tile adds to its weights itself (0: none; widths whose level table fills LDS).
+constexpr int64_t kGemmTileRows = 128;
+int64_t gemm_sparse_cap(int bits);
 // Up to gemm_group_max() independent linears of one code width, one M and one
 // output dtype in one launch (mixed stacks); lv holds that width's levels.
 int gemm_group_max();
@@ -147,9 +156,12 @@ hipError_t launch_outlier_split(const void* W, int wdt, int64_t numel, int64_t k
 hipError_t launch_outlier_finish(int64_t rows, int64_t cols, int64_t k, int bits, const Levels& lv,
                                  const uint8_t* codes, const uint8_t* q8, const float* cst, const int32_t* oidx,
                                  const float* oval, int32_t* row_ptr, int32_t* col, float* val, hipStream_t s);
-// C (M x N float32) = x S^T for S in CSR (N rows, K columns).
+// C (M x N float32) = x S^T for S in CSR (N rows, K columns).  cap >= 0: only
+// the rows of aligned kGemmTileRows-row groups holding more than cap entries
+// are computed (the others are left as they are).
 hipError_t launch_sparse_addend(const void* x, int xdt, int64_t M, int64_t K, int64_t N, const int32_t* row_ptr,
-                                const int32_t* col, const float* val, int64_t nnz, float* C, hipStream_t s);
+                                const int32_t* col, const float* val, int64_t nnz, float* C, hipStream_t s,
+                                int64_t cap = -1);
 
 // C (M x N float32) = z F^T, z = x blockdiag(H_P) / P (P = 2^lp), F in CSR (N rows, K columns);
 // K % 8 == 0 and K <= wha_max_cols(); nnz >= 1.

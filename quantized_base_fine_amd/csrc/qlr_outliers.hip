@@ -348,8 +348,23 @@ __global__ __launch_bounds__(TB) void k_sparse_addend(const void* __restrict__ x
                                                        const int32_t* __restrict__ row_ptr,
                                                        const int32_t* __restrict__ col,
                                                        const float* __restrict__ val, int64_t nnz,
-                                                       float* __restrict__ C, int64_t nchunk) {
+                                                       float* __restrict__ C, int64_t nchunk, int64_t cap) {
   using XT = std::conditional_t<XDT == DT_F32, float, uint16_t>;
+  // cap >= 0: rows of kGemmTileRows-row groups with at most cap entries are the
+  // prefill GEMM's own (it adds them to its weights) and are skipped; a
+  // workgroup whose range holds none of the other rows ends here.  The clamps
+  // are the GEMM's.
+  const int64_t nb = (int64_t)blockIdx.y * nchunk, ne = min(N, nb + nchunk);
+  auto group_count = [&](int64_t g) {
+    const int64_t e0 = min<int64_t>(max<int64_t>(row_ptr[min(g * kGemmTileRows, N)], 0), nnz);
+    return max<int64_t>(e0, min<int64_t>(row_ptr[min((g + 1) * kGemmTileRows, N)], nnz)) - e0;
+  };
+  if (cap >= 0) {
+    const int64_t g0 = nb / kGemmTileRows, g1 = ne > nb ? (ne - 1) / kGemmTileRows + 1 : g0;
+    bool any = false;
+    for (int64_t g = g0 + threadIdx.x; g < g1; g += TB) any = any || group_count(g) > cap;
+    if (!__syncthreads_or(any)) return;  // uniform
+  }
   constexpr int R = MR > 0 ? MR : 1;
   constexpr int EPC = 16 / (int)sizeof(XT);  // elements per 16-byte chunk of an x row
   extern __shared__ uint4 smem_u4[];
@@ -414,24 +429,24 @@ __global__ __launch_bounds__(TB) void k_sparse_addend(const void* __restrict__ x
       }
     }
   };
-  const int64_t nb = (int64_t)blockIdx.y * nchunk, ne = min(N, nb + nchunk);
   // One weight row per thread and pass, its outliers in rounds of 8.  Offsets
   // run two passes ahead and outliers one round ahead: while a round is summed,
   // the thread's next round, or after its last round the first round of its
   // next pass, is in flight.  Offsets and columns are clamped into range: a
   // malformed CSR gives wrong sums, never a stray access.
   constexpr int kE = 8;
-  auto offsets = [&](int64_t base, int64_t& q0, int64_t& q1) {
+  auto offsets = [&](int64_t base, int64_t& q0, int64_t& q1, bool& keep) {
     const int64_t n = base + tid;
     const int64_t nc = n < ne ? n : ne - 1;
     // both loads unconditional and their values used unconditionally (a load
     // behind a branch would make the compiler wait for every load in flight);
-    // past the range the pass gets [lo, lo)
+    // past the range, and for the GEMM's own rows, the pass gets [lo, lo)
     const int64_t a0 = row_ptr[nc], a1 = row_ptr[nc + 1];
     const int64_t lo = a0 < 0 ? 0 : (a0 > nnz ? nnz : a0);
     const int64_t hi = a1 < lo ? lo : (a1 > nnz ? nnz : a1);
+    keep = n < ne && (cap < 0 || group_count(nc / kGemmTileRows) > cap);
     q0 = lo;
-    q1 = n < ne ? hi : lo;
+    q1 = keep ? hi : lo;
   };
   // VL (4 <= nnz < 2^29): two 16-byte loads each of col and val per round; a
   // load that would run past nnz starts at nnz - 4, its element t then at js + t
@@ -472,13 +487,15 @@ __global__ __launch_bounds__(TB) void k_sparse_addend(const void* __restrict__ x
     }
   };
   int64_t p0, p1, n0, n1;
-  offsets(nb, p0, p1);
-  offsets(nb + TB, n0, n1);
+  bool pk, nk;  // the pass's row is stored
+  offsets(nb, p0, p1, pk);
+  offsets(nb + TB, n0, n1, nk);
   Round cur;
   load_round(p0, p1, 0, cur);
   for (int64_t base = nb; base < ne; base += TB) {
     int64_t f0, f1;
-    offsets(base + 2 * TB, f0, f1);
+    bool fk;
+    offsets(base + 2 * TB, f0, f1, fk);
     float acc[R];
 #pragma unroll
     for (int mm = 0; mm < R; ++mm) acc[mm] = 0.0f;
@@ -499,20 +516,22 @@ __global__ __launch_bounds__(TB) void k_sparse_addend(const void* __restrict__ x
       if (!more) break;
     }
     const int64_t n = base + tid;
-    if (n < ne) {
+    if (pk) {
 #pragma unroll
       for (int mm = 0; mm < R; ++mm)
         if (m0 + mm < M) C[(m0 + mm) * N + n] = acc[mm];
     }
     p0 = n0;
     p1 = n1;
+    pk = nk;
     n0 = f0;
     n1 = f1;
+    nk = fk;
   }
 }
 
 template <int XDT, int MR>
-hipError_t sparse_addend_t(const void* x, int64_t M, int64_t K, int64_t N, const int32_t* row_ptr,
+hipError_t sparse_addend_t(int64_t cap, const void* x, int64_t M, int64_t K, int64_t N, const int32_t* row_ptr,
                            const int32_t* col, const float* val, int64_t nnz, float* C, hipStream_t s) {
   constexpr int R = MR > 0 ? MR : 1;
   constexpr int TB = 1024;
@@ -530,19 +549,19 @@ hipError_t sparse_addend_t(const void* x, int64_t M, int64_t K, int64_t N, const
     attr = true;
   }
   hipLaunchKernelGGL((k_sparse_addend<XDT, MR, TB>), dim3((unsigned)xblocks, (unsigned)nch), dim3(TB), shmem, s, x, M,
-                     K, N, row_ptr, col, val, nnz, C, nchunk);
+                     K, N, row_ptr, col, val, nnz, C, nchunk, cap);
   return hipGetLastError();
 }
 
 template <int XDT>
-hipError_t sparse_addend_x(const void* x, int64_t M, int64_t K, int64_t N, const int32_t* row_ptr,
+hipError_t sparse_addend_x(int64_t cap, const void* x, int64_t M, int64_t K, int64_t N, const int32_t* row_ptr,
                            const int32_t* col, const float* val, int64_t nnz, float* C, hipStream_t s) {
   const int64_t row = K * (XDT == DT_F32 ? 4 : 2);  // LDS bytes of one staged x row
-  if (M > 4 && 8 * row <= kSparseLds) return sparse_addend_t<XDT, 8>(x, M, K, N, row_ptr, col, val, nnz, C, s);
-  if (M > 2 && 4 * row <= kSparseLds) return sparse_addend_t<XDT, 4>(x, M, K, N, row_ptr, col, val, nnz, C, s);
-  if (M > 1 && 2 * row <= kSparseLds) return sparse_addend_t<XDT, 2>(x, M, K, N, row_ptr, col, val, nnz, C, s);
-  if (row <= kSparseLds) return sparse_addend_t<XDT, 1>(x, M, K, N, row_ptr, col, val, nnz, C, s);
-  return sparse_addend_t<XDT, 0>(x, M, K, N, row_ptr, col, val, nnz, C, s);
+  if (M > 4 && 8 * row <= kSparseLds) return sparse_addend_t<XDT, 8>(cap, x, M, K, N, row_ptr, col, val, nnz, C, s);
+  if (M > 2 && 4 * row <= kSparseLds) return sparse_addend_t<XDT, 4>(cap, x, M, K, N, row_ptr, col, val, nnz, C, s);
+  if (M > 1 && 2 * row <= kSparseLds) return sparse_addend_t<XDT, 2>(cap, x, M, K, N, row_ptr, col, val, nnz, C, s);
+  if (row <= kSparseLds) return sparse_addend_t<XDT, 1>(cap, x, M, K, N, row_ptr, col, val, nnz, C, s);
+  return sparse_addend_t<XDT, 0>(cap, x, M, K, N, row_ptr, col, val, nnz, C, s);
 }
 
 template <int WDT>
@@ -613,10 +632,11 @@ hipError_t launch_outlier_split(const void* W, int wdt, int64_t numel, int64_t k
 }
 
 hipError_t launch_sparse_addend(const void* x, int xdt, int64_t M, int64_t K, int64_t N, const int32_t* row_ptr,
-                                const int32_t* col, const float* val, int64_t nnz, float* C, hipStream_t s) {
+                                const int32_t* col, const float* val, int64_t nnz, float* C, hipStream_t s,
+                                int64_t cap) {
   if (M == 0 || N == 0) return hipSuccess;
-  if (xdt == DT_F32) return sparse_addend_x<DT_F32>(x, M, K, N, row_ptr, col, val, nnz, C, s);
-  return sparse_addend_x<DT_BF16>(x, M, K, N, row_ptr, col, val, nnz, C, s);
+  if (xdt == DT_F32) return sparse_addend_x<DT_F32>(cap, x, M, K, N, row_ptr, col, val, nnz, C, s);
+  return sparse_addend_x<DT_BF16>(cap, x, M, K, N, row_ptr, col, val, nnz, C, s);
 }
 
 hipError_t launch_outlier_finish(int64_t rows, int64_t cols, int64_t k, int bits, const Levels& lv,
