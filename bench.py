@@ -146,9 +146,9 @@ _CSRC = "quantized_base_fine_amd/csrc/"
 TRAFFIC_KERNELS = {
     "decode": ("k_gemv<4, 2, true, false, 2, true, false, 0, false>",
                [_CSRC + f for f in ("qlr_gemv.hip", "qlr_lut.h", "qlr_device.h", "qlr_internal.h")]),
-    "prefill": ("k_gemm<4, 2, false, false>",
+    "prefill": ("k_gemm<4, 2, false, false, false>",
                 [_CSRC + f for f in ("qlr_gemm.hip", "qlr_lut.h", "qlr_device.h", "qlr_internal.h")]),
-    "backward": ("k_gemm<4, 2, false, true>",
+    "backward": ("k_gemm<4, 2, false, true, false>",
                  [_CSRC + f for f in ("qlr_gemm.hip", "qlr_lut.h", "qlr_device.h", "qlr_internal.h")]),
 }
 COPY_BYTES = 256 << 20  # the calibration copy reads and writes this many bytes
