@@ -338,16 +338,26 @@ qlr_status qlr_linear_fwd_outliers(const void* x, qlr_dtype xdt, int64_t M, cons
  * hblock columns (a power of two dividing cols; hblock = cols is one full
  * transform), so H^-1 = H / hblock, and F the sparse coefficient matrix
  * (rows x cols CSR in the qlr_sparse format: row_ptr, col = transform index,
- * val = the coefficient values c in float32).  Computed as z F^T with
+ * val = the coefficient values c in float32; repeated columns of a row add).
+ * On the decode and float32 families it is computed as z F^T with
  * z = x blockdiag(H) / hblock: each x row is transformed by butterflies
  * (additions and subtractions, float32), scaled exactly by 1 / hblock, then
  * multiplied by F (float32), and the result is added to each output before
- * rounding.  No low-rank adapter in this call (the branch replaces it).
+ * rounding.  On the prefill GEMM family (bf16 x, M > 16, rows * cols * 2 <
+ * 2^31) the branch is merged into a bf16 copy of the weight in the workspace
+ * instead: each row of F is transformed the same way (float32), scaled by
+ * 1 / hblock, added to the row's dequantized weights w' and rounded once to
+ * bf16, and the GEMM multiplies that copy (the stored weight and F are not
+ * changed).  No low-rank adapter in this call (the branch replaces it).
  *   x: M x cols, bf16 or f32 (bf16 on the decode and prefill kernels); cols <= 32768.
- *   ws >= qlr_workspace_bytes(QLR_OP_LINEAR_WHA, M, rows, cols, 0) (M x rows float32).
- * Tolerance as qlr_linear_fwd, with S extended by sum_j |c_j| (sum of |x| over
- * j's block) / hblock.  Asynchronous, allocation-free.  Errors: as
- * qlr_linear_fwd, plus QLR_ERR_SHAPE for hblock, cols or a mismatching F.
+ *   ws >= qlr_workspace_bytes(QLR_OP_LINEAR_WHA, M, rows, cols, 0): M x rows
+ *   float32, or where the prefill GEMM runs (M > 16 or that path forced, on
+ *   the calling thread) the larger of that and rows x cols bf16.
+ * Tolerance as qlr_linear_fwd for the family that runs (on the GEMM family
+ * its bf16 weights are W' + F H / hblock), with S extended by sum_j |c_j|
+ * (sum of |x| over j's block) / hblock.  Asynchronous, allocation-free.
+ * Errors: as qlr_linear_fwd, plus QLR_ERR_SHAPE for hblock, cols or a
+ * mismatching F.
  */
 qlr_status qlr_linear_fwd_wha(const void* x, qlr_dtype xdt, int64_t M, const qlr_qweight* w, const qlr_sparse* F,
                               int32_t hblock, void* y, qlr_dtype ydt, void* ws, size_t ws_bytes, void* stream);

@@ -39,6 +39,11 @@
 // remapped so that each XCD walks a contiguous, row-major range of tiles, which
 // keeps one 256-row slab of x hot in that XCD's L2.
 //
+// Dense weights (BITS = 16: the weight given as bf16 values, the Walsh-Hadamard
+// branch merged into it).  The producers load the weight tile by direct loads
+// as they load x, with no dequantization; tiles are taken column-major, since
+// 16-bit weights re-read by every XCD would cost more than x re-read by every XCD.
+//
 // Adapter.  t = x A^T (float32, from the adapter-product kernel) enters as
 // extra K blocks after the last weight block, 32 adapter columns each: the x
 // side holds [hi(s t) | lo(s t)] with hi = bf16(s t) and lo = bf16(s t - hi)
@@ -68,6 +73,11 @@ constexpr uint32_t kXOff = 0, kWOff = 3 * kXTile, kTOff = kWOff + 3 * kWTile;
 template <int BITS>
 struct GemmTable {
   static constexpr uint32_t kBytes = (BITS == 4) ? 0 : (BITS == 8) ? 256 * 16 * 4 : PairTableF32<BITS>::kBytes;
+};
+// BITS = 16: the weight is given as dense bf16 values (no codes, no table)
+template <>
+struct GemmTable<16> {
+  static constexpr uint32_t kBytes = 0;
 };
 template <int BITS>
 constexpr uint32_t gemm_lds_bytes() { return kTOff + GemmTable<BITS>::kBytes; }
@@ -294,6 +304,7 @@ struct GemmParams {
 // a 128-byte bank window, which the XOR with bit 3 of c pulls apart.
 template <int BITS, int YDT, bool ADP, bool TR, bool SPF>
 __global__ __launch_bounds__(512, 1) void k_gemm(GemmParams P, Levels lv) {
+  static_assert(BITS != 16 || (!ADP && !TR && !SPF), "dense weights: forward without adapter or side channel");
   extern __shared__ uint32_t smem[];
   // XCD-aware tile order: workgroup b runs on XCD b % 8
   const int64_t xcd = blockIdx.x & 7, local = blockIdx.x >> 3;
@@ -325,7 +336,10 @@ __global__ __launch_bounds__(512, 1) void k_gemm(GemmParams P, Levels lv) {
   const int64_t nbt = nb + (ADP ? (a.r + 31) / 32 : 0);
   const int64_t M = P.m_end;
   const int64_t lt = tile - Lr.tile0;
-  const int64_t mt = lt / Lr.ntiles, nt = lt % Lr.ntiles;
+  // layer tiles row-major (one XCD keeps one x slab in its L2); with dense
+  // weights column-major (one XCD reads its range of bf16 weight rows once)
+  const int64_t mt = BITS == 16 ? lt % P.mtiles : lt / Lr.ntiles;
+  const int64_t nt = BITS == 16 ? lt / P.mtiles : lt % Lr.ntiles;
   const int64_t m0 = P.m_begin + mt * BM, n0 = nt * BN;
 
   const int tid = threadIdx.x;
@@ -333,7 +347,7 @@ __global__ __launch_bounds__(512, 1) void k_gemm(GemmParams P, Levels lv) {
   const int fr = lane & 31, h = lane >> 5;
   const int64_t kbl = nb - 1;
 
-  if constexpr (BITS != 4) {
+  if constexpr (BITS != 4 && BITS != 16) {
     float* sL = reinterpret_cast<float*>(smem) + kXOff / 4;
     stage_levels<1 << BITS>(lv, sL);
     __syncthreads();
@@ -384,290 +398,332 @@ __global__ __launch_bounds__(512, 1) void k_gemm(GemmParams P, Levels lv) {
       xgd[p] = (uint32_t)(((m0 - P.m_begin) + 64 * pw + t8) * KC + 8 * (((uint32_t)lane & 7u) ^ swz(t8 + 8u * p))) * 2u;
     typedef __attribute__((address_space(3))) char lds_char;
     lds_char* const xlds = (lds_char*)smem + kXOff + pw * 8192;
-    // Forward: weight row n0 + rr (rr = pt / 2), codes [32 dh, 32 dh + 32) of
-    // block kb.  TR: weight row 64 kb + rr (rr = pt / 4), codes [32 dh, 32 dh +
-    // 32) of block column n0 / 64 + bq.
-    const int rr = TR ? (pt >> 2) : (pt >> 1), dh = pt & 1, bq = TR ? ((pt >> 1) & 1) : 0;
-    bool wv;
-    int64_t wblk, wstep;
-    if constexpr (TR) {
-      const int64_t nbK = K >> 6, wcol = (n0 >> 6) + bq;
-      wv = wcol < nbK;
-      wblk = (int64_t)rr * nbK + (wv ? wcol : nbK - 1);
-      wstep = 64 * nbK;
-    } else {
-      const int64_t wn = n0 + rr;
-      wv = wn < N;
-      wblk = (wv ? wn : N - 1) * nb;
-      wstep = 1;
-    }
-    uint32_t wst[4];  // LDS slot of the thread's chunk q of row rr
+    if constexpr (BITS == 16) {
+      // Dense bf16 weight (a.codes: N x K row-major, N K 2 < 2^31 bytes): the
+      // weight tile goes to LDS by direct loads exactly as x does.  Load j (0..3)
+      // of wave pw fills tile rows 32 pw + 8 j .. + 7, lane L reading the chunk
+      // that the swizzle puts at its slot; rows past N read zero.  Step k issues
+      // block k+2 (x and weight: 12 loads per wave) and waits for block k+1.
+      const __amdgpu_buffer_rsrc_t wr = __builtin_amdgcn_make_buffer_rsrc(
+          const_cast<uint8_t*>(a.codes), (short)0, (int)(N * K * 2), 0x00020000);
+      uint32_t wgd[2];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      if constexpr (TR)
-        wst[q] = kWOff + (uint32_t)(rr * 256) + (tr_chunk((uint32_t)(8 * bq + 4 * dh + q), (uint32_t)rr) << 4);
-      else
-        wst[q] = kWOff + (uint32_t)(rr * 128) + ((((uint32_t)(4 * dh + q)) ^ swz((uint32_t)rr & 15u)) << 4);
-    }
-    const uint32_t tp = kTOff + (BITS == 8 ? 4u * (lane & 15) : 8u * fr);
-
-    struct CS { Codes32<BITS> c; uint32_t q8; float sc; };
-    // block kb's x rows into buffer buf (in flight until a vmcnt wait)
-    auto load_x_lds = [&](int64_t kb, int buf) {
+      for (int p = 0; p < 2; ++p)
+        wgd[p] = (uint32_t)((n0 + 32 * pw + t8) * K + 8 * (((uint32_t)lane & 7u) ^ swz(t8 + 8u * p))) * 2u;
+      const uint32_t wg_row8 = (uint32_t)(8 * K * 2);
+      lds_char* const wlds = (lds_char*)smem + kWOff + pw * 4096;
+      auto load_xw = [&](int64_t kb, int buf) {
 #pragma unroll
-      for (int j = 0; j < 8; ++j)
-        __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (void __attribute__((address_space(3)))*)(
-                                                         xlds + buf * kXTile + 1024 * j),
-                                                 16, xgd[j & 1] + j * xg_row8, (int)(kb * 128), 0, 0);
-    };
-    auto load_c = [&](CS& st, int64_t kb) {
-      const int64_t blk = wblk + kb * wstep;
-      st.c = load_codes32<BITS>(a.codes + blk * (8 * BITS) + dh * (4 * BITS));
-      st.q8 = a.q8[blk];
-      st.sc = a.cst[blk >> 8];
-    };
-    // Dequantization of block kb's codes (pinned first: an empty register-only
-    // asm makes them opaque, so instruction selection cannot start their
-    // arithmetic right after the load, which would wait for codes in flight).
-    struct DQ { Codes32<BITS> c; float ap; Lut4 t; };
-    auto dq_begin = [&](const CS& cs) {
-      DQ d;
-      d.c = cs.c;
-      uint32_t q8 = cs.q8;
-      float sc = cs.sc;
+        for (int j = 0; j < 8; ++j)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (void __attribute__((address_space(3)))*)(
+                                                           xlds + buf * kXTile + 1024 * j),
+                                                   16, xgd[j & 1] + j * xg_row8, (int)(kb * 128), 0, 0);
 #pragma unroll
-      for (int i = 0; i < BITS; ++i) asm volatile("" : "+v"(d.c.w[i]));
-      asm volatile("" : "+v"(q8), "+v"(sc));
-      d.ap = wv ? (float)q8 * sc : 0.0f;
-      if constexpr (BITS == 4) d.t = make_lut4(lv, d.ap);
-      return d;
-    };
-    // pairs [4 i, 4 i + 4) of the 16 output pairs (for 4-bit: code word i); the
-    // results are pinned so that they are computed here, not next to the stores
-    auto dq_part = [&](const DQ& d, auto part, uint32_t (&o)[16]) {
-      constexpr int I = decltype(part)::value;
-      if constexpr (BITS == 4) lut4_word(d.c.w[I], d.t, o + 4 * I);
-      else dequant_pairs<BITS, 4 * I, 4 * I + 4>(d.c, d.ap, tp, o);
-#pragma unroll
-      for (int j = 4 * I; j < 4 * I + 4; ++j) asm volatile("" : "+v"(o[j]));
-    };
-    auto store_w = [&](const uint32_t (&o)[16], int buf) {
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        lds_store_u32x4(wst[q] + buf * kWTile, u32x4_t{o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]});
-    };
-    // (side channel) the thread's cursor over its row's entries: index of the
-    // next one, the end, and the next two entries' columns (INT_MAX past the end)
-    // and values in registers, so the test of a block never waits for LDS
-    int sp_e = 0, sp_end = 0, sp_nc = INT_MAX, sp_nc2 = INT_MAX;
-    float sp_nv = 0.0f, sp_nv2 = 0.0f;
-    auto sp_load = [&](int e, int& c, float& v) {
-      const uint32_t ec = (uint32_t)min(e, kSpCap - 1);  // read in range; past the end the entry is dropped
-      const int cc = lds_i32(kSpCol + 4u * ec);
-      v = lds_f32(kSpVal + 4u * ec);
-      c = e < sp_end ? cc : INT_MAX;
-    };
-    // after block kbk's weights are in buffer buf: add the entries of columns
-    // [64 kbk + 32 dh, + 32) to them, one packed bf16 LDS atomic add each (the
-    // residual rounded to bf16, the sum rounded to nearest even)
-    auto sp_patch = [&](int64_t kbk, int buf) {
-      if constexpr (kSpCap > 0) {
-        const int lo = (int)(64 * kbk) + 32 * dh, hi = lo + 32;
-        while (sp_nc < hi) {
-          if (sp_nc >= lo) {
-            const uint32_t idx = (uint32_t)(sp_nc - lo);
-            const uint32_t ad = kWOff + (uint32_t)buf * kWTile + (uint32_t)(rr * 128) +
-                                (((4u * (uint32_t)dh + (idx >> 3)) ^ swz((uint32_t)rr & 15u)) << 4) + 4u * ((idx & 7u) >> 1);
-            const __bf16 hv = (__bf16)sp_nv, zv = (__bf16)0.0f;
-            const bf16x2_t add = (idx & 1u) ? bf16x2_t{zv, hv} : bf16x2_t{hv, zv};
-            __builtin_amdgcn_ds_atomic_fadd_v2bf16(
-                reinterpret_cast<__attribute__((address_space(3))) bf16x2_t*>((uintptr_t)ad), add);
-          }
-          ++sp_e;
-          sp_nc = sp_nc2;
-          sp_nv = sp_nv2;
-          sp_load(sp_e + 1, sp_nc2, sp_nv2);
-        }
+        for (int j = 0; j < 4; ++j)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(wr, (void __attribute__((address_space(3)))*)(
+                                                           wlds + buf * kWTile + 1024 * j),
+                                                   16, wgd[j & 1] + j * wg_row8, (int)(kb * 128), 0, 0);
+      };
+      load_xw(0, 0);
+      load_xw(min<int64_t>(1, kbl), 1);
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // blocks 0 and 1 in LDS
+      __syncthreads();
+      // one step (and barrier) per consumer block; the last two load unused copies
+      for (int64_t k = 0; k < nb; ++k) {
+        __builtin_amdgcn_sched_barrier(0);
+        load_xw(min(k + 2, kbl), (int)((k + 2) % 3));
+        asm volatile("s_waitcnt vmcnt(12)" ::: "memory");
+        __syncthreads();
       }
-    };
-    auto dequant_store = [&](const CS& cs, int buf, int64_t kbk) {
-      const DQ d = dq_begin(cs);
-      uint32_t o[16];
-      dq_part(d, std::integral_constant<int, 0>{}, o);
-      dq_part(d, std::integral_constant<int, 1>{}, o);
-      dq_part(d, std::integral_constant<int, 2>{}, o);
-      dq_part(d, std::integral_constant<int, 3>{}, o);
-      store_w(o, buf);
-      sp_patch(kbk, buf);
-    };
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      __syncthreads();
+      __syncthreads();
+    } else {
+      // Forward: weight row n0 + rr (rr = pt / 2), codes [32 dh, 32 dh + 32) of
+      // block kb.  TR: weight row 64 kb + rr (rr = pt / 4), codes [32 dh, 32 dh +
+      // 32) of block column n0 / 64 + bq.
+      const int rr = TR ? (pt >> 2) : (pt >> 1), dh = pt & 1, bq = TR ? ((pt >> 1) & 1) : 0;
+      bool wv;
+      int64_t wblk, wstep;
+      if constexpr (TR) {
+        const int64_t nbK = K >> 6, wcol = (n0 >> 6) + bq;
+        wv = wcol < nbK;
+        wblk = (int64_t)rr * nbK + (wv ? wcol : nbK - 1);
+        wstep = 64 * nbK;
+      } else {
+        const int64_t wn = n0 + rr;
+        wv = wn < N;
+        wblk = (wv ? wn : N - 1) * nb;
+        wstep = 1;
+      }
+      uint32_t wst[4];  // LDS slot of the thread's chunk q of row rr
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if constexpr (TR)
+          wst[q] = kWOff + (uint32_t)(rr * 256) + (tr_chunk((uint32_t)(8 * bq + 4 * dh + q), (uint32_t)rr) << 4);
+        else
+          wst[q] = kWOff + (uint32_t)(rr * 128) + ((((uint32_t)(4 * dh + q)) ^ swz((uint32_t)rr & 15u)) << 4);
+      }
+      const uint32_t tp = kTOff + (BITS == 8 ? 4u * (lane & 15) : 8u * fr);
 
-    // Block k+2 is written while the consumers multiply block k.  x(j) and
-    // codes(j) live in register set j % 3 and are loaded two blocks before they
-    // are written (a set is free again once its block is in LDS).
-    CS c0, c1, c2;
-    load_x_lds(0, 0);
-    load_c(c0, 0);
-    if (!(ADP && nb == 1)) load_x_lds(min<int64_t>(1, kbl), 1);
-    load_c(c1, min<int64_t>(1, kbl));
-    load_c(c2, min<int64_t>(2, kbl));
-    if (spf) {
-      __syncthreads();  // the consumers have staged the tile's side channel
-      sp_e = lds_i32(kSpRo + 4u * (uint32_t)rr);
-      sp_end = lds_i32(kSpRo + 4u * (uint32_t)(rr + 1));
-      sp_load(sp_e, sp_nc, sp_nv);
-      sp_load(sp_e + 1, sp_nc2, sp_nv2);
-    }
-    dequant_store(c0, 0, 0);
-    load_c(c0, min<int64_t>(3, kbl));
-    // ADP: adapter block j >= nb (a = j - nb, adapter columns [32 a, 32 a + 32))
-    // into buffer j % 3.  x side (thread = tile row): [hi(s t) | lo(s t)], t the
-    // float32 adapter product of that row, split into bf16 hi = bf16(s t) and
-    // lo = bf16(s t - hi).  Weight side: forward, row n of the tile holds
-    // [B[n][32 a ..] | the same]; TR, rows 0..31 and 32..63 both hold A[32 a + row % 32]
-    // over the tile's columns.  Runs in steps where the producers would otherwise
-    // idle; its operands are mostly L2-resident (shared by the tile's neighbours).
-    auto adapter_write = [&](int64_t j) {
-      if constexpr (ADP) {
-        const int aa = (int)(j - nb), r = a.r;
-        const uint32_t bw = (uint32_t)(j % 3);
-        const uint16_t* Bl = reinterpret_cast<const uint16_t*>(a.B);
-        const u32x4_t zero4 = {0u, 0u, 0u, 0u};
-        u32x4_t wv[4];
-        if constexpr (TR) {
-          const int jj = 32 * aa + (rr & 31);
-          const uint16_t* ap = Bl + (int64_t)min(jj, r - 1) * K;
+      struct CS { Codes32<BITS> c; uint32_t q8; float sc; };
+      // block kb's x rows into buffer buf (in flight until a vmcnt wait)
+      auto load_x_lds = [&](int64_t kb, int buf) {
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int64_t c = n0 + 64 * bq + 32 * dh + 8 * q;
-            const u32x4_t v = *reinterpret_cast<const u32x4_t*>(ap + min(c, K - 8));
-            wv[q] = (jj < r && c < K) ? v : zero4;
+        for (int j = 0; j < 8; ++j)
+          __builtin_amdgcn_raw_ptr_buffer_load_lds(xr, (void __attribute__((address_space(3)))*)(
+                                                           xlds + buf * kXTile + 1024 * j),
+                                                   16, xgd[j & 1] + j * xg_row8, (int)(kb * 128), 0, 0);
+      };
+      auto load_c = [&](CS& st, int64_t kb) {
+        const int64_t blk = wblk + kb * wstep;
+        st.c = load_codes32<BITS>(a.codes + blk * (8 * BITS) + dh * (4 * BITS));
+        st.q8 = a.q8[blk];
+        st.sc = a.cst[blk >> 8];
+      };
+      // Dequantization of block kb's codes (pinned first: an empty register-only
+      // asm makes them opaque, so instruction selection cannot start their
+      // arithmetic right after the load, which would wait for codes in flight).
+      struct DQ { Codes32<BITS> c; float ap; Lut4 t; };
+      auto dq_begin = [&](const CS& cs) {
+        DQ d;
+        d.c = cs.c;
+        uint32_t q8 = cs.q8;
+        float sc = cs.sc;
+#pragma unroll
+        for (int i = 0; i < BITS; ++i) asm volatile("" : "+v"(d.c.w[i]));
+        asm volatile("" : "+v"(q8), "+v"(sc));
+        d.ap = wv ? (float)q8 * sc : 0.0f;
+        if constexpr (BITS == 4) d.t = make_lut4(lv, d.ap);
+        return d;
+      };
+      // pairs [4 i, 4 i + 4) of the 16 output pairs (for 4-bit: code word i); the
+      // results are pinned so that they are computed here, not next to the stores
+      auto dq_part = [&](const DQ& d, auto part, uint32_t (&o)[16]) {
+        constexpr int I = decltype(part)::value;
+        if constexpr (BITS == 4) lut4_word(d.c.w[I], d.t, o + 4 * I);
+        else dequant_pairs<BITS, 4 * I, 4 * I + 4>(d.c, d.ap, tp, o);
+#pragma unroll
+        for (int j = 4 * I; j < 4 * I + 4; ++j) asm volatile("" : "+v"(o[j]));
+      };
+      auto store_w = [&](const uint32_t (&o)[16], int buf) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          lds_store_u32x4(wst[q] + buf * kWTile, u32x4_t{o[4 * q], o[4 * q + 1], o[4 * q + 2], o[4 * q + 3]});
+      };
+      // (side channel) the thread's cursor over its row's entries: index of the
+      // next one, the end, and the next two entries' columns (INT_MAX past the end)
+      // and values in registers, so the test of a block never waits for LDS
+      int sp_e = 0, sp_end = 0, sp_nc = INT_MAX, sp_nc2 = INT_MAX;
+      float sp_nv = 0.0f, sp_nv2 = 0.0f;
+      auto sp_load = [&](int e, int& c, float& v) {
+        const uint32_t ec = (uint32_t)min(e, kSpCap - 1);  // read in range; past the end the entry is dropped
+        const int cc = lds_i32(kSpCol + 4u * ec);
+        v = lds_f32(kSpVal + 4u * ec);
+        c = e < sp_end ? cc : INT_MAX;
+      };
+      // after block kbk's weights are in buffer buf: add the entries of columns
+      // [64 kbk + 32 dh, + 32) to them, one packed bf16 LDS atomic add each (the
+      // residual rounded to bf16, the sum rounded to nearest even)
+      auto sp_patch = [&](int64_t kbk, int buf) {
+        if constexpr (kSpCap > 0) {
+          const int lo = (int)(64 * kbk) + 32 * dh, hi = lo + 32;
+          while (sp_nc < hi) {
+            if (sp_nc >= lo) {
+              const uint32_t idx = (uint32_t)(sp_nc - lo);
+              const uint32_t ad = kWOff + (uint32_t)buf * kWTile + (uint32_t)(rr * 128) +
+                                  (((4u * (uint32_t)dh + (idx >> 3)) ^ swz((uint32_t)rr & 15u)) << 4) + 4u * ((idx & 7u) >> 1);
+              const __bf16 hv = (__bf16)sp_nv, zv = (__bf16)0.0f;
+              const bf16x2_t add = (idx & 1u) ? bf16x2_t{zv, hv} : bf16x2_t{hv, zv};
+              __builtin_amdgcn_ds_atomic_fadd_v2bf16(
+                  reinterpret_cast<__attribute__((address_space(3))) bf16x2_t*>((uintptr_t)ad), add);
+            }
+            ++sp_e;
+            sp_nc = sp_nc2;
+            sp_nv = sp_nv2;
+            sp_load(sp_e + 1, sp_nc2, sp_nv2);
           }
-        } else {
-          const int64_t n = n0 + rr;
-          const bool nv = n < N;
-          const uint16_t* bp = Bl + (nv ? n : N - 1) * (int64_t)r;
+        }
+      };
+      auto dequant_store = [&](const CS& cs, int buf, int64_t kbk) {
+        const DQ d = dq_begin(cs);
+        uint32_t o[16];
+        dq_part(d, std::integral_constant<int, 0>{}, o);
+        dq_part(d, std::integral_constant<int, 1>{}, o);
+        dq_part(d, std::integral_constant<int, 2>{}, o);
+        dq_part(d, std::integral_constant<int, 3>{}, o);
+        store_w(o, buf);
+        sp_patch(kbk, buf);
+      };
+
+      // Block k+2 is written while the consumers multiply block k.  x(j) and
+      // codes(j) live in register set j % 3 and are loaded two blocks before they
+      // are written (a set is free again once its block is in LDS).
+      CS c0, c1, c2;
+      load_x_lds(0, 0);
+      load_c(c0, 0);
+      if (!(ADP && nb == 1)) load_x_lds(min<int64_t>(1, kbl), 1);
+      load_c(c1, min<int64_t>(1, kbl));
+      load_c(c2, min<int64_t>(2, kbl));
+      if (spf) {
+        __syncthreads();  // the consumers have staged the tile's side channel
+        sp_e = lds_i32(kSpRo + 4u * (uint32_t)rr);
+        sp_end = lds_i32(kSpRo + 4u * (uint32_t)(rr + 1));
+        sp_load(sp_e, sp_nc, sp_nv);
+        sp_load(sp_e + 1, sp_nc2, sp_nv2);
+      }
+      dequant_store(c0, 0, 0);
+      load_c(c0, min<int64_t>(3, kbl));
+      // ADP: adapter block j >= nb (a = j - nb, adapter columns [32 a, 32 a + 32))
+      // into buffer j % 3.  x side (thread = tile row): [hi(s t) | lo(s t)], t the
+      // float32 adapter product of that row, split into bf16 hi = bf16(s t) and
+      // lo = bf16(s t - hi).  Weight side: forward, row n of the tile holds
+      // [B[n][32 a ..] | the same]; TR, rows 0..31 and 32..63 both hold A[32 a + row % 32]
+      // over the tile's columns.  Runs in steps where the producers would otherwise
+      // idle; its operands are mostly L2-resident (shared by the tile's neighbours).
+      auto adapter_write = [&](int64_t j) {
+        if constexpr (ADP) {
+          const int aa = (int)(j - nb), r = a.r;
+          const uint32_t bw = (uint32_t)(j % 3);
+          const uint16_t* Bl = reinterpret_cast<const uint16_t*>(a.B);
+          const u32x4_t zero4 = {0u, 0u, 0u, 0u};
+          u32x4_t wv[4];
+          if constexpr (TR) {
+            const int jj = 32 * aa + (rr & 31);
+            const uint16_t* ap = Bl + (int64_t)min(jj, r - 1) * K;
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const int jq = 32 * aa + 8 * q;
-            if (r % 8 == 0) {
-              const u32x4_t v = *reinterpret_cast<const u32x4_t*>(bp + min(jq, r - 8));
-              wv[q] = (nv && jq < r) ? v : zero4;
-            } else {
+            for (int q = 0; q < 4; ++q) {
+              const int64_t c = n0 + 64 * bq + 32 * dh + 8 * q;
+              const u32x4_t v = *reinterpret_cast<const u32x4_t*>(ap + min(c, K - 8));
+              wv[q] = (jj < r && c < K) ? v : zero4;
+            }
+          } else {
+            const int64_t n = n0 + rr;
+            const bool nv = n < N;
+            const uint16_t* bp = Bl + (nv ? n : N - 1) * (int64_t)r;
 #pragma unroll
-              for (int e2 = 0; e2 < 4; ++e2) {
-                const uint32_t lo = (nv && jq + 2 * e2 < r) ? bp[jq + 2 * e2] : 0u;
-                const uint32_t hi = (nv && jq + 2 * e2 + 1 < r) ? bp[jq + 2 * e2 + 1] : 0u;
-                wv[q][e2] = lo | (hi << 16);
+            for (int q = 0; q < 4; ++q) {
+              const int jq = 32 * aa + 8 * q;
+              if (r % 8 == 0) {
+                const u32x4_t v = *reinterpret_cast<const u32x4_t*>(bp + min(jq, r - 8));
+                wv[q] = (nv && jq < r) ? v : zero4;
+              } else {
+#pragma unroll
+                for (int e2 = 0; e2 < 4; ++e2) {
+                  const uint32_t lo = (nv && jq + 2 * e2 < r) ? bp[jq + 2 * e2] : 0u;
+                  const uint32_t hi = (nv && jq + 2 * e2 + 1 < r) ? bp[jq + 2 * e2 + 1] : 0u;
+                  wv[q][e2] = lo | (hi << 16);
+                }
               }
             }
           }
-        }
-        // x side: row pt of the tile
-        const int64_t m = m0 + pt;
-        const bool mv = m < M;
-        float tv[32];
+          // x side: row pt of the tile
+          const int64_t m = m0 + pt;
+          const bool mv = m < M;
+          float tv[32];
 #pragma unroll
-        for (int i = 0; i < 32; ++i) tv[i] = 0.0f;
-        if (r % 4 == 0) {
-          // per split, all eight 16-byte loads in flight at once (clamped
-          // addresses, zeroed at use); splits added in order
-          for (int sp = 0; sp < a.t_splits; ++sp) {
-            const float* tq = a.t + ((int64_t)sp * a.M + (mv ? m : M - 1)) * r;
-            f32x4_t v[8];
+          for (int i = 0; i < 32; ++i) tv[i] = 0.0f;
+          if (r % 4 == 0) {
+            // per split, all eight 16-byte loads in flight at once (clamped
+            // addresses, zeroed at use); splits added in order
+            for (int sp = 0; sp < a.t_splits; ++sp) {
+              const float* tq = a.t + ((int64_t)sp * a.M + (mv ? m : M - 1)) * r;
+              f32x4_t v[8];
 #pragma unroll
-            for (int q4 = 0; q4 < 8; ++q4) v[q4] = *reinterpret_cast<const f32x4_t*>(tq + min(32 * aa + 4 * q4, r - 4));
+              for (int q4 = 0; q4 < 8; ++q4) v[q4] = *reinterpret_cast<const f32x4_t*>(tq + min(32 * aa + 4 * q4, r - 4));
 #pragma unroll
-            for (int q4 = 0; q4 < 8; ++q4)
+              for (int q4 = 0; q4 < 8; ++q4)
 #pragma unroll
-              for (int e = 0; e < 4; ++e) tv[4 * q4 + e] += (32 * aa + 4 * q4 < r) ? v[q4][e] : 0.0f;
+                for (int e = 0; e < 4; ++e) tv[4 * q4 + e] += (32 * aa + 4 * q4 < r) ? v[q4][e] : 0.0f;
+            }
+          } else {
+            for (int sp = 0; sp < a.t_splits; ++sp) {
+              const float* tq = a.t + ((int64_t)sp * a.M + (mv ? m : M - 1)) * r;
+#pragma unroll
+              for (int i = 0; i < 32; ++i)
+                if (32 * aa + i < r) tv[i] += tq[32 * aa + i];
+            }
           }
-        } else {
-          for (int sp = 0; sp < a.t_splits; ++sp) {
-            const float* tq = a.t + ((int64_t)sp * a.M + (mv ? m : M - 1)) * r;
+          const uint32_t xrow = kXOff + bw * kXTile + (uint32_t)pt * 128u;
 #pragma unroll
-            for (int i = 0; i < 32; ++i)
-              if (32 * aa + i < r) tv[i] += tq[32 * aa + i];
+          for (int c = 0; c < 4; ++c) {
+            u32x4_t hv, lv;
+#pragma unroll
+            for (int e2 = 0; e2 < 4; ++e2) {
+              const float u0 = mv ? a.scale * tv[8 * c + 2 * e2] : 0.0f;
+              const float u1 = mv ? a.scale * tv[8 * c + 2 * e2 + 1] : 0.0f;
+              const uint32_t hb0 = f32_to_bf16_bits(u0), hb1 = f32_to_bf16_bits(u1);
+              hv[e2] = hb0 | (hb1 << 16);
+              lv[e2] = pack_bf16x2(u0 - bf16_bits_to_f32(hb0), u1 - bf16_bits_to_f32(hb1));
+            }
+            lds_store_u32x4(xrow + ((((uint32_t)c) ^ swz((uint32_t)pt & 15u)) << 4), hv);
+            lds_store_u32x4(xrow + ((((uint32_t)(4 + c)) ^ swz((uint32_t)pt & 15u)) << 4), lv);
           }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) lds_store_u32x4(wst[q] + bw * kWTile, wv[q]);
         }
-        const uint32_t xrow = kXOff + bw * kXTile + (uint32_t)pt * 128u;
-#pragma unroll
-        for (int c = 0; c < 4; ++c) {
-          u32x4_t hv, lv;
-#pragma unroll
-          for (int e2 = 0; e2 < 4; ++e2) {
-            const float u0 = mv ? a.scale * tv[8 * c + 2 * e2] : 0.0f;
-            const float u1 = mv ? a.scale * tv[8 * c + 2 * e2 + 1] : 0.0f;
-            const uint32_t hb0 = f32_to_bf16_bits(u0), hb1 = f32_to_bf16_bits(u1);
-            hv[e2] = hb0 | (hb1 << 16);
-            lv[e2] = pack_bf16x2(u0 - bf16_bits_to_f32(hb0), u1 - bf16_bits_to_f32(hb1));
-          }
-          lds_store_u32x4(xrow + ((((uint32_t)c) ^ swz((uint32_t)pt & 15u)) << 4), hv);
-          lds_store_u32x4(xrow + ((((uint32_t)(4 + c)) ^ swz((uint32_t)pt & 15u)) << 4), lv);
-        }
-#pragma unroll
-        for (int q = 0; q < 4; ++q) lds_store_u32x4(wst[q] + bw * kWTile, wv[q]);
-      }
-    };
+      };
 
-    if (ADP && nb == 1) {
-      adapter_write(1);
-    } else {
-      dequant_store(c1, 1, min<int64_t>(1, kbl));
-    }
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // x of blocks 0 and 1 in LDS
-    __syncthreads();
-    // Step k: x(k+2) by direct loads into buffer (k+2) % 3 (freed by the last
-    // barrier), codes(k+4) into set (k+1) % 3, and the dequantized block k+2
-    // into buffer (k+2) % 3.  Before the step's barrier the wave waits for all
-    // but its 8 newest loads: x(k+1), issued a step earlier, is then in LDS
-    // for the consumers' next block.  The step runs in pinned chunks, each a
-    // code word's arithmetic, so the wave keeps computing while loads drain.
-    auto pstep = [&](CS& cl, const CS& cw, int64_t k, int bw) {
-      __builtin_amdgcn_sched_barrier(0);
-      load_x_lds(min(k + 2, kbl), bw);
-      __builtin_amdgcn_sched_barrier(0);
-      load_c(cl, min(k + 4, kbl));
-      const DQ d = dq_begin(cw);
-      uint32_t o[16];
-      dq_part(d, std::integral_constant<int, 0>{}, o);
-      __builtin_amdgcn_sched_barrier(0);
-      dq_part(d, std::integral_constant<int, 1>{}, o);
-      __builtin_amdgcn_sched_barrier(0);
-      dq_part(d, std::integral_constant<int, 2>{}, o);
-      __builtin_amdgcn_sched_barrier(0);
-      dq_part(d, std::integral_constant<int, 3>{}, o);
-      store_w(o, bw);
-      __builtin_amdgcn_sched_barrier(0);
-      sp_patch(min(k + 2, kbl), bw);
-      __builtin_amdgcn_sched_barrier(0);
-      asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
-      __syncthreads();
-      __builtin_amdgcn_sched_barrier(0);
-    };
-    // regular steps write blocks 2 .. nb - 1 (without an adapter, two more steps
-    // write unused copies: every step ends with the barrier of one consumer block)
-    const int64_t nreg = ADP ? (nb > 2 ? nb - 2 : 0) : nb;
-    const int64_t nr3 = nreg - nreg % 3;
-    int64_t kb = 0;
-    for (; kb < nr3; kb += 3) {
-      pstep(c1, c2, kb, 2);
-      pstep(c2, c0, kb + 1, 0);
-      pstep(c0, c1, kb + 2, 1);
-    }
-    if (kb < nreg) pstep(c1, c2, kb, 2);
-    if (kb + 1 < nreg) pstep(c2, c0, kb + 1, 0);
-    // every direct load in LDS before the adapter steps and the epilogue reuse it
-    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-    if constexpr (ADP) {
-      // steps nreg .. nbt - 1 write the adapter blocks (j = k + 2 >= nb)
-      for (int64_t k = nreg; k < nbt; ++k) {
-        if (k + 2 < nbt) adapter_write(k + 2);
-        __syncthreads();
+      if (ADP && nb == 1) {
+        adapter_write(1);
+      } else {
+        dequant_store(c1, 1, min<int64_t>(1, kbl));
       }
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // x of blocks 0 and 1 in LDS
+      __syncthreads();
+      // Step k: x(k+2) by direct loads into buffer (k+2) % 3 (freed by the last
+      // barrier), codes(k+4) into set (k+1) % 3, and the dequantized block k+2
+      // into buffer (k+2) % 3.  Before the step's barrier the wave waits for all
+      // but its 8 newest loads: x(k+1), issued a step earlier, is then in LDS
+      // for the consumers' next block.  The step runs in pinned chunks, each a
+      // code word's arithmetic, so the wave keeps computing while loads drain.
+      auto pstep = [&](CS& cl, const CS& cw, int64_t k, int bw) {
+        __builtin_amdgcn_sched_barrier(0);
+        load_x_lds(min(k + 2, kbl), bw);
+        __builtin_amdgcn_sched_barrier(0);
+        load_c(cl, min(k + 4, kbl));
+        const DQ d = dq_begin(cw);
+        uint32_t o[16];
+        dq_part(d, std::integral_constant<int, 0>{}, o);
+        __builtin_amdgcn_sched_barrier(0);
+        dq_part(d, std::integral_constant<int, 1>{}, o);
+        __builtin_amdgcn_sched_barrier(0);
+        dq_part(d, std::integral_constant<int, 2>{}, o);
+        __builtin_amdgcn_sched_barrier(0);
+        dq_part(d, std::integral_constant<int, 3>{}, o);
+        store_w(o, bw);
+        __builtin_amdgcn_sched_barrier(0);
+        sp_patch(min(k + 2, kbl), bw);
+        __builtin_amdgcn_sched_barrier(0);
+        asm volatile("s_waitcnt vmcnt(8)" ::: "memory");
+        __syncthreads();
+        __builtin_amdgcn_sched_barrier(0);
+      };
+      // regular steps write blocks 2 .. nb - 1 (without an adapter, two more steps
+      // write unused copies: every step ends with the barrier of one consumer block)
+      const int64_t nreg = ADP ? (nb > 2 ? nb - 2 : 0) : nb;
+      const int64_t nr3 = nreg - nreg % 3;
+      int64_t kb = 0;
+      for (; kb < nr3; kb += 3) {
+        pstep(c1, c2, kb, 2);
+        pstep(c2, c0, kb + 1, 0);
+        pstep(c0, c1, kb + 2, 1);
+      }
+      if (kb < nreg) pstep(c1, c2, kb, 2);
+      if (kb + 1 < nreg) pstep(c2, c0, kb + 1, 0);
+      // every direct load in LDS before the adapter steps and the epilogue reuse it
+      asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+      if constexpr (ADP) {
+        // steps nreg .. nbt - 1 write the adapter blocks (j = k + 2 >= nb)
+        for (int64_t k = nreg; k < nbt; ++k) {
+          if (k + 2 < nbt) adapter_write(k + 2);
+          __syncthreads();
+        }
+      }
+      // the consumers' two epilogue barriers: tiles free, then the output staged
+      __syncthreads();
+      __syncthreads();
     }
-    // the consumers' two epilogue barriers: tiles free, then the output staged
-    __syncthreads();
-    __syncthreads();
   } else {
     // =================== consumers: MFMA on 128 x 64 of the tile ===================
     const int mh = wave & 1, nh = wave >> 1;
@@ -1001,6 +1057,14 @@ hipError_t launch_gemm_b(const LinearArgs* ls, int n, const Levels& lv, hipStrea
 
 hipError_t launch_gemm(const LinearArgs& a, const Levels& lv, hipStream_t s) {
   return launch_gemm_group(&a, 1, lv, s);
+}
+
+hipError_t launch_gemm_dense(const LinearArgs& a, hipStream_t s) {
+  if (a.r != 0 || a.N <= 0 || a.K % 64 != 0 || a.N * a.K * 2 > INT_MAX || a.sp_row_ptr != nullptr)
+    return hipErrorInvalidValue;
+  static const Levels none{};
+  if (a.ydt == DT_F32) return launch_gemm_t<16, DT_F32, false, false>(&a, 1, none, s);
+  return launch_gemm_t<16, DT_BF16, false, false>(&a, 1, none, s);
 }
 
 int gemm_group_max() { return kGroupMax; }

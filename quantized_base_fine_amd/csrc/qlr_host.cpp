@@ -161,6 +161,10 @@ DbaLayout dba_layout(int64_t M, int64_t N, int64_t K, int R, int ell, int xdt) {
 }
 
 // choose the kernel family for a linear call
+// The Walsh-Hadamard branch is merged into the weight on the prefill GEMM when
+// the bf16 copy fits the dense-weight GEMM's 32-bit offsets.
+bool wha_merges(int64_t N, int64_t K) { return N > 0 && K > 0 && N <= (int64_t)0x7FFFFFFF / 2 / K; }
+
 qlr_status pick_path(int64_t M, qlr_dtype xdt, qlr_dtype abdt, int32_t r, qlr_path* out) {
   const bool bf16_ok = xdt == QLR_BF16 && (r == 0 || abdt == QLR_BF16);
   qlr_path p = t_path;
@@ -403,7 +407,11 @@ qlr_status qlr_workspace_bytes(qlr_op op, int64_t M, int64_t N, int64_t K, int32
   }
   if (op == QLR_OP_LINEAR_WHA) {
     if (M < 0 || N < 0 || K < 0) return fail(QLR_ERR_SHAPE, "negative size");
-    *bytes = ((size_t)M * (size_t)N * 4 + 255) & ~(size_t)255;
+    // the float32 addend (M x N), or on the prefill GEMM the merged bf16 weight (N x K)
+    size_t b = ((size_t)M * (size_t)N * 4 + 255) & ~(size_t)255;
+    const bool gemm = t_path == QLR_PATH_GEMM || (t_path == QLR_PATH_AUTO && M > 16);
+    if (M > 0 && gemm && wha_merges(N, K)) b = std::max(b, ((size_t)N * (size_t)K * 2 + 255) & ~(size_t)255);
+    *bytes = b;
     return QLR_OK;
   }
   if (op == QLR_OP_LINEAR_DBA) {
@@ -935,6 +943,19 @@ qlr_status qlr_linear_fwd_wha(const void* x, qlr_dtype xdt, int64_t M, const qlr
     probe.sp_nnz = F->nnz;
     probe.sp_wht_lp = lp;
     if (qlr::gemv_fuses_sparse(probe)) return run_linear(c, 0.0f, nullptr, path, s, nullptr, F, lp);
+  }
+  if (F->nnz > 0 && path == QLR_PATH_GEMM && wha_merges(w->rows, K)) {
+    // prefill: the branch merged into a bf16 copy of the weight, then the dense-weight GEMM
+    uint16_t* Wd = reinterpret_cast<uint16_t*>(ws);
+    hipError_t e = qlr::launch_wha_merge(reinterpret_cast<const uint8_t*>(w->codes), w->absmax_q8, w->absmax_c,
+                                         w->bits, levels_arg(w->bits), w->rows, K, lp, F->row_ptr, F->col, F->val,
+                                         F->nnz, Wd, s);
+    if (e != hipSuccess) return hip_fail(e, "adapter merge launch");
+    qlr::LinearArgs a = make_args(c, 0.0f, nullptr, 1);
+    a.codes = reinterpret_cast<const uint8_t*>(Wd);
+    e = qlr::launch_gemm_dense(a, s);
+    if (e != hipSuccess) return hip_fail(e, "linear launch");
+    return QLR_OK;
   }
   if (F->nnz > 0) {
     const hipError_t e = qlr::launch_wha_addend(x, (int)xdt, M, K, w->rows, lp, F->row_ptr, F->col, F->val, F->nnz,

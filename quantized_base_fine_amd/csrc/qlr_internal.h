@@ -168,6 +168,15 @@ hipError_t launch_sparse_addend(const void* x, int xdt, int64_t M, int64_t K, in
 hipError_t launch_wha_addend(const void* x, int xdt, int64_t M, int64_t K, int64_t N, int lp, const int32_t* row_ptr,
                              const int32_t* col, const float* val, int64_t nnz, float* C, hipStream_t s);
 int64_t wha_max_cols();
+// The branch merged into the weight for the prefill GEMM: Wd (N x K bf16) =
+// bf16(W' + F blockdiag(H_P) / P), P = 2^lp, F in CSR (N rows, K columns);
+// K % 64 == 0 and K <= wha_max_cols().
+hipError_t launch_wha_merge(const uint8_t* codes, const uint8_t* q8, const float* cst, int bits, const Levels& lv,
+                            int64_t N, int64_t K, int lp, const int32_t* row_ptr, const int32_t* col, const float* val,
+                            int64_t nnz, uint16_t* out, hipStream_t s);
+// Prefill GEMM on a dense bf16 weight held in a.codes (N x K row-major,
+// N K 2 <= INT_MAX bytes): y = x Wd^T (+ a.addend); no adapter.
+hipError_t launch_gemm_dense(const LinearArgs& a, hipStream_t s);
 
 // ---- backward (adapter training)
 // Input gradient dx = dy W' + scale u A on the transposed bf16 GEMM: a.x = dy

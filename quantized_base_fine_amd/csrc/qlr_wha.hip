@@ -11,6 +11,12 @@
 // range of F's rows: G lanes per row, each taking 8 of every 8 G coefficients
 // per round (all loads of a round in flight together), summed over the G lanes
 // in a fixed butterfly order.
+//
+// For the prefill GEMM a second kernel forms instead the weight with the branch
+// merged into it, Wd = bf16(W' + F blockdiag(H_P) / P) (bf16, N x K), which the
+// dense-weight GEMM multiplies: row n of F H / P is the transform of F's row n
+// (its coefficients scattered into a zero row), so the branch costs one pass
+// over the weight instead of a gather per x row and coefficient.
 #include <algorithm>
 
 #include "qlr_internal.h"
@@ -350,9 +356,235 @@ hipError_t wha_x(const void* x, int64_t M, int64_t K, int64_t N, int lp, const i
   return wha_t<XDT, 1, 4, 1, 1024, VL>(x, M, K, N, lp, row_ptr, col, val, nnz, C, s);
 }
 
+// ---- the merged weight of the prefill path
+//
+// One workgroup of 256 threads per weight row n.  Its float32 row of F
+// (coefficients added into a zeroed LDS row, columns clamped into the row) is
+// transformed in place within blocks of P = 2^lp columns.  The butterfly
+// stages of different column bits commute, so the bits from 10 up (blocks
+// longer than 1024) go first, in LDS passes of up to four stages (each thread
+// holds the 16 values of one group in registers); then, for each 4096 columns,
+// thread t takes columns 16 t .. 16 t + 15: bits 0-3 are combined in its
+// registers and bits 4-9 across the wave's lanes (DPP quad permutations for
+// lane bits 0-1, swizzles for 2-3, half swaps for 4-5).  The thread then
+// dequantizes its 16 weights, w' = fl32(L[c] fl32(m s)) as dequantization
+// defines it, adds its transform values scaled by 2^-lp (exact) and stores
+// bf16(w' + d) rounded to nearest even.  LDS slot of column i: bits 0..3 XORed
+// with bits 6..9 and bits 4..5 with bits 8..9, so that the 64 lanes of every
+// pass's 4-byte reads and writes, and of the threads' 16-column reads, hit 64
+// distinct banks.  The first 4096 columns' codes and scales are loaded before
+// the transform.
+__device__ __forceinline__ uint32_t mslot(uint32_t i) { return i ^ ((i >> 6) & 15u) ^ (((i >> 8) & 3u) << 4); }
+
+template <int B>
+__device__ __forceinline__ void merge_pass(float* row, uint32_t K, int sh) {
+  constexpr int E = 1 << B;
+  const uint32_t ng = K >> B;
+  for (uint32_t gi = threadIdx.x; gi < ng; gi += 256) {
+    const uint32_t base = ((gi >> sh) << (sh + B)) | (gi & ((1u << sh) - 1u));
+    float v[E];
+#pragma unroll
+    for (int i = 0; i < E; ++i) v[i] = row[mslot(base + ((uint32_t)i << sh))];
+#pragma unroll
+    for (int st = 1; st < E; st <<= 1)
+#pragma unroll
+      for (int i = 0; i < E; ++i)
+        if ((i & st) == 0) {
+          const float a = v[i], c = v[i + st];
+          v[i] = a + c;
+          v[i + st] = a - c;
+        }
+#pragma unroll
+    for (int i = 0; i < E; ++i) row[mslot(base + ((uint32_t)i << sh))] = v[i];
+  }
+}
+
+// 16 codes of BITS bits (LSB first) starting at element 16 q of the flat codes
+template <int BITS>
+__device__ __forceinline__ void merge_codes16(const uint8_t* codes, int64_t q, uint32_t (&w)[(BITS + 1) / 2]) {
+  const uint8_t* p = codes + q * (2 * BITS);
+  if constexpr (BITS == 2) {
+    w[0] = *reinterpret_cast<const uint32_t*>(p);
+  } else if constexpr (BITS == 4) {
+    const uint2 u = *reinterpret_cast<const uint2*>(p);
+    w[0] = u.x;
+    w[1] = u.y;
+  } else if constexpr (BITS == 8) {
+    const uint4 u = *reinterpret_cast<const uint4*>(p);
+    w[0] = u.x;
+    w[1] = u.y;
+    w[2] = u.z;
+    w[3] = u.w;
+  } else {  // 6 bytes at a 2-byte boundary
+    const uint16_t* h = reinterpret_cast<const uint16_t*>(p);
+    w[0] = (uint32_t)h[0] | ((uint32_t)h[1] << 16);
+    w[1] = h[2];
+  }
+}
+template <int BITS>
+__device__ __forceinline__ uint32_t code_at(const uint32_t (&w)[(BITS + 1) / 2], int i) {
+  if constexpr (BITS == 3) {
+    const uint64_t v = (uint64_t)w[0] | ((uint64_t)w[1] << 32);
+    return (uint32_t)(v >> (3 * i)) & 7u;
+  } else {
+    return (w[(BITS * i) >> 5] >> ((BITS * i) & 31)) & ((1u << BITS) - 1u);
+  }
+}
+
+template <int BITS>
+__global__ __launch_bounds__(256) void k_wha_merge(const uint8_t* __restrict__ codes, const uint8_t* __restrict__ q8,
+                                                   const float* __restrict__ cst, Levels lv, int64_t K, int lp,
+                                                   const int32_t* __restrict__ row_ptr, const int32_t* __restrict__ col,
+                                                   const float* __restrict__ val, int64_t nnz, uint16_t* __restrict__ out) {
+  constexpr int NL = 1 << BITS, CW = (BITS + 1) / 2;
+  extern __shared__ float msm[];
+  float* sL = msm;
+  float* row = msm + NL;
+  const int64_t n = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const uint32_t Ku = (uint32_t)K;
+  const int64_t e0 = n * K;  // first flat element of the row
+  // the first 4096 columns' codes and block scale (clamped reads; used only in range)
+  uint32_t cw[CW];
+  float ap0;
+  {
+    const int64_t c = e0 + min(16u * (uint32_t)tid, Ku - 16u);
+    merge_codes16<BITS>(codes, c >> 4, cw);
+    ap0 = (float)q8[c >> 6] * cst[c >> 14];
+  }
+  const int64_t c0 = min<int64_t>(max<int64_t>(row_ptr[n], 0), nnz);
+  const int64_t c1 = max<int64_t>(c0, min<int64_t>(row_ptr[n + 1], nnz));
+  stage_levels<NL>(lv, sL);
+  for (uint32_t i = 4 * tid; i < Ku; i += 1024) *reinterpret_cast<float4*>(row + i) = make_float4(0.f, 0.f, 0.f, 0.f);
+  __syncthreads();
+  for (int64_t e = c0 + tid; e < c1; e += 256) {
+    const uint32_t c = (uint32_t)min<int64_t>(max<int64_t>(col[e], 0), K - 1);
+    atomicAdd(row + mslot(c), val[e]);  // (repeated columns of a row add up)
+  }
+  __syncthreads();
+  for (int sh = 10; sh < lp; sh += 4) {
+    switch (min(4, lp - sh)) {
+      case 1: merge_pass<1>(row, Ku, sh); break;
+      case 2: merge_pass<2>(row, Ku, sh); break;
+      case 3: merge_pass<3>(row, Ku, sh); break;
+      default: merge_pass<4>(row, Ku, sh); break;
+    }
+    __syncthreads();
+  }
+  const float inv_p = __builtin_bit_cast(float, (uint32_t)(127 - lp) << 23);  // 2^-lp
+  for (uint32_t s0 = 0; s0 < Ku; s0 += 4096) {  // uniform: every lane takes part in the lane exchanges
+    const uint32_t cb = s0 + 16u * (uint32_t)tid;
+    const bool on = cb < Ku;
+    float v[16];
+#pragma unroll
+    for (int j = 0; j < 16; ++j) v[j] = on ? row[mslot(cb + (uint32_t)j)] : 0.0f;
+#pragma unroll
+    for (int st = 1; st < 16; st <<= 1)
+      if ((1 << lp) > st) {
+#pragma unroll
+        for (int j = 0; j < 16; ++j)
+          if (!(j & st)) {
+            const float a = v[j], b = v[j + st];
+            v[j] = a + b;
+            v[j + st] = a - b;
+          }
+      }
+    // lane bit sb pairs lane l (value a if bit sb of l is 0) with l ^ 2^sb
+    // (value b): the pair becomes (a + b, a - b)
+#pragma unroll
+    for (int sb = 0; sb < 4; ++sb)
+      if (lp > 4 + sb) {
+        const bool up = (lane >> sb) & 1;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) {
+          const int vi = __float_as_int(v[j]);
+          int oi;
+          if (sb == 0) oi = __builtin_amdgcn_mov_dpp(vi, 0xB1, 0xF, 0xF, false);       // lane ^ 1
+          else if (sb == 1) oi = __builtin_amdgcn_mov_dpp(vi, 0x4E, 0xF, 0xF, false);  // lane ^ 2
+          else if (sb == 2) oi = __builtin_amdgcn_ds_swizzle(vi, (4 << 10) | 0x1F);    // lane ^ 4
+          else oi = __builtin_amdgcn_ds_swizzle(vi, (8 << 10) | 0x1F);                 // lane ^ 8
+          const float o = __int_as_float(oi);
+          v[j] = up ? o - v[j] : v[j] + o;
+        }
+      }
+    // lane bits 4 and 5: the half swaps hand both lanes of a pair (a, b)
+    if (lp > 8) {
+      const bool up = (lane >> 4) & 1;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const auto sw = __builtin_amdgcn_permlane16_swap(__float_as_uint(v[j]), __float_as_uint(v[j]), false, false);
+        const float a = __uint_as_float(sw[0]), b = __uint_as_float(sw[1]);
+        v[j] = up ? a - b : a + b;
+      }
+    }
+    if (lp > 9) {
+      const bool up = (lane >> 5) & 1;
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const auto sw = __builtin_amdgcn_permlane32_swap(__float_as_uint(v[j]), __float_as_uint(v[j]), false, false);
+        const float a = __uint_as_float(sw[0]), b = __uint_as_float(sw[1]);
+        v[j] = up ? a - b : a + b;
+      }
+    }
+    if (on) {
+      uint32_t w[CW];
+      float ap;
+      if (s0 == 0) {
+#pragma unroll
+        for (int i = 0; i < CW; ++i) w[i] = cw[i];
+        ap = ap0;
+      } else {
+        const int64_t c = e0 + cb;
+        merge_codes16<BITS>(codes, c >> 4, w);
+        ap = (float)q8[c >> 6] * cst[c >> 14];
+      }
+      uint32_t o[8];
+#pragma unroll
+      for (int i = 0; i < 16; i += 2) {
+        const float w0 = __fmul_rn(sL[code_at<BITS>(w, i)], ap) + v[i] * inv_p;
+        const float w1 = __fmul_rn(sL[code_at<BITS>(w, i + 1)], ap) + v[i + 1] * inv_p;
+        o[i / 2] = pack_bf16x2(w0, w1);
+      }
+      uint4* dst = reinterpret_cast<uint4*>(out + e0 + cb);
+      dst[0] = make_uint4(o[0], o[1], o[2], o[3]);
+      dst[1] = make_uint4(o[4], o[5], o[6], o[7]);
+    }
+  }
+}
+
+template <int BITS>
+hipError_t wha_merge_b(const uint8_t* codes, const uint8_t* q8, const float* cst, const Levels& lv, int64_t N,
+                       int64_t K, int lp, const int32_t* row_ptr, const int32_t* col, const float* val, int64_t nnz,
+                       uint16_t* out, hipStream_t s) {
+  const size_t shmem = (size_t)((1 << BITS) + K) * 4;
+  static bool attr = false;
+  if (!attr) {
+    const hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(k_wha_merge<BITS>),
+                                             hipFuncAttributeMaxDynamicSharedMemorySize, (int)kWhaLdsAll);
+    if (e != hipSuccess) return e;
+    attr = true;
+  }
+  hipLaunchKernelGGL((k_wha_merge<BITS>), dim3((unsigned)N), dim3(256), shmem, s, codes, q8, cst, lv, K, lp,
+                     row_ptr, col, val, nnz, out);
+  return hipGetLastError();
+}
+
 }  // namespace
 
 int64_t wha_max_cols() { return kWhaLds / 4; }
+
+hipError_t launch_wha_merge(const uint8_t* codes, const uint8_t* q8, const float* cst, int bits, const Levels& lv,
+                            int64_t N, int64_t K, int lp, const int32_t* row_ptr, const int32_t* col, const float* val,
+                            int64_t nnz, uint16_t* out, hipStream_t s) {
+  if (N == 0) return hipSuccess;
+  if (K > wha_max_cols() || K % 64 != 0 || lp < 0 || (int64_t(1) << lp) > K) return hipErrorInvalidValue;
+  switch (bits) {
+    case 2: return wha_merge_b<2>(codes, q8, cst, lv, N, K, lp, row_ptr, col, val, nnz, out, s);
+    case 3: return wha_merge_b<3>(codes, q8, cst, lv, N, K, lp, row_ptr, col, val, nnz, out, s);
+    case 4: return wha_merge_b<4>(codes, q8, cst, lv, N, K, lp, row_ptr, col, val, nnz, out, s);
+    default: return wha_merge_b<8>(codes, q8, cst, lv, N, K, lp, row_ptr, col, val, nnz, out, s);
+  }
+}
 
 hipError_t launch_wha_addend(const void* x, int xdt, int64_t M, int64_t K, int64_t N, int lp, const int32_t* row_ptr,
                              const int32_t* col, const float* val, int64_t nnz, float* C, hipStream_t s) {
