@@ -147,6 +147,12 @@ typedef struct {
   int32_t* row_ptr; /* device, rows + 1 */
   int32_t* col;     /* device, nnz */
   float* val;       /* device, nnz */
+  /* host: the largest number of entries in a group of 128 rows starting at a
+   * multiple of 128 (rows 128 g .. 128 g + 127), as qlr_quantize_outliers sets
+   * it.  A caller that fills the CSR itself sets -1 (not known) or the exact
+   * figure; any value outside 1 .. nnz counts as not known.  Lets the prefill
+   * forward skip work it would otherwise do to find this out on the device. */
+  int64_t max_group_nnz;
 } qlr_sparse;
 
 /* Library version (major*10000 + minor*100 + patch). */
@@ -300,8 +306,9 @@ qlr_status qlr_linear_fwd_mixed(const qlr_layer* layers, int32_t n, int64_t M, q
  * exact widening; ties to the lower flat index) are set to 0 and the result is
  * quantized as qlr_quantize does (out); sp receives, for each of them in
  * row-major order, its column and the float32 residual fl32(w - w'), w' the
- * dense part's dequantized value there, and sp->row_ptr the CSR row offsets.
- * The caller sets sp->rows, sp->cols, sp->nnz = k and provides its buffers.
+ * dense part's dequantized value there, and sp->row_ptr the CSR row offsets;
+ * sp->max_group_nnz is set on the host.  The caller sets sp->rows, sp->cols,
+ * sp->nnz = k and provides its buffers.
  * rows * cols < 2^31, 0 <= k <= rows * cols.  ws (device) >=
  * qlr_workspace_bytes(QLR_OP_QUANTIZE_OUTLIERS, k, rows, cols, 0).
  * BLOCKING (reads the non-finite flags).  Errors: as qlr_quantize, plus
@@ -321,8 +328,9 @@ qlr_status qlr_quantize_outliers(const void* W, qlr_dtype wdt, int64_t rows, int
  * 4-bit codes: there each 128-row tile of the weight whose entries fit the
  * kernel's spare LDS (about 2000 with 4-bit codes, 1500 with 2-bit) adds them
  * to its dequantized bf16 weights, rounding each changed weight to bf16 again
- * (within that family's bound), and only the other tiles take the float32 term.
- * Arguments otherwise as qlr_linear_fwd; the error bound's S also sums
+ * (within that family's bound), and only the other tiles take the float32 term
+ * (its kernel is not launched when sp->max_group_nnz says that every tile's
+ * entries fit).  Arguments otherwise as qlr_linear_fwd; the error bound's S also sums
  * |x[m, col] val| over the row's outliers.
  * ws >= qlr_workspace_bytes(QLR_OP_LINEAR_OUTLIERS, M, rows, cols, r).
  * Asynchronous, allocation-free.

@@ -855,12 +855,17 @@ qlr_status qlr_quantize_outliers(const void* W, qlr_dtype wdt, int64_t rows, int
   e = qlr::launch_outlier_finish(rows, cols, k, bits, lv, reinterpret_cast<const uint8_t*>(out->codes),
                                  out->absmax_q8, out->absmax_c, oidx, oval, sp->row_ptr, sp->col, sp->val, s);
   if (e != hipSuccess) return hip_fail(e, "outlier finish launch");
-  uint32_t flags[2] = {0, 0};
-  e = hipMemcpyAsync(&flags[0], qflag, 4, hipMemcpyDeviceToHost, s);
-  if (e == hipSuccess && sflag) e = hipMemcpyAsync(&flags[1], sflag, 4, hipMemcpyDeviceToHost, s);
+  // the largest entry count of a 128-row group, read back with the flags
+  uint32_t* gmax = qflag + 1;
+  e = qlr::launch_group_max(rows, k, sp->row_ptr, gmax, s);
+  if (e != hipSuccess) return hip_fail(e, "group count launch");
+  uint32_t flags[3] = {0, 0, 0};
+  e = hipMemcpyAsync(&flags[0], qflag, 8, hipMemcpyDeviceToHost, s);
+  if (e == hipSuccess && sflag) e = hipMemcpyAsync(&flags[2], sflag, 4, hipMemcpyDeviceToHost, s);
   if (e == hipSuccess) e = hipStreamSynchronize(s);
   if (e != hipSuccess) return hip_fail(e, "flag read");
-  if (flags[0] || flags[1]) return fail(QLR_ERR_NONFINITE, "W holds NaN or Inf");
+  if (flags[0] || flags[2]) return fail(QLR_ERR_NONFINITE, "W holds NaN or Inf");
+  sp->max_group_nnz = (int64_t)flags[1];
   return QLR_OK;
 }
 
@@ -895,7 +900,11 @@ qlr_status qlr_linear_fwd_outliers(const void* x, qlr_dtype xdt, int64_t M, cons
   // the prefill GEMM adds a 128-row tile's entries to its weights itself when they
   // fit (gemm_sparse_cap); the float32 addend then holds only the other tiles' rows
   const bool gemm_sp = path == QLR_PATH_GEMM && qlr::gemm_sparse_cap(w->bits) > 0;
-  if (sp->nnz > 0) {
+  // when the split has said that every group's entries fit, no tile needs the addend
+  // (a figure outside 1 .. nnz cannot be exact for nnz > 0: it counts as not known)
+  const bool all_fit = gemm_sp && sp->max_group_nnz >= 1 && sp->max_group_nnz <= sp->nnz &&
+                       sp->max_group_nnz <= qlr::gemm_sparse_cap(w->bits);
+  if (sp->nnz > 0 && !all_fit) {
     const hipError_t e = qlr::launch_sparse_addend(x, (int)xdt, M, w->cols, w->rows, sp->row_ptr, sp->col, sp->val,
                                                    sp->nnz, C, s, gemm_sp ? qlr::gemm_sparse_cap(w->bits) : -1);
     if (e != hipSuccess) return hip_fail(e, "sparse term launch");

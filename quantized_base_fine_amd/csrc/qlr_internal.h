@@ -156,6 +156,9 @@ hipError_t launch_outlier_split(const void* W, int wdt, int64_t numel, int64_t k
 hipError_t launch_outlier_finish(int64_t rows, int64_t cols, int64_t k, int bits, const Levels& lv,
                                  const uint8_t* codes, const uint8_t* q8, const float* cst, const int32_t* oidx,
                                  const float* oval, int32_t* row_ptr, int32_t* col, float* val, hipStream_t s);
+// *out = the largest entry count over the row groups [128 g, 128 g + 128) of a CSR
+// with `rows` rows and k entries (one workgroup).
+hipError_t launch_group_max(int64_t rows, int64_t k, const int32_t* row_ptr, uint32_t* out, hipStream_t s);
 // C (M x N float32) = x S^T for S in CSR (N rows, K columns).  cap >= 0: only
 // the rows of aligned kGemmTileRows-row groups holding more than cap entries
 // are computed (the others are left as they are).

@@ -322,6 +322,31 @@ __global__ __launch_bounds__(256) void k_ol_finish(int64_t k, int64_t cols, cons
 }
 
 // row_ptr[r] = number of outliers with flat index < r * cols (binary search over the ascending indices)
+// Largest entry count over the row groups [128 g, 128 g + 128) of a CSR, by
+// one workgroup: a strided max per thread, then over the wave's lanes and the
+// waves (row offsets clamped into [0, k], as the forward kernels read them).
+__global__ __launch_bounds__(1024) void k_ol_group_max(int64_t rows, int64_t k, const int32_t* __restrict__ row_ptr,
+                                                       uint32_t* __restrict__ out) {
+  __shared__ uint32_t red[16];
+  const int64_t groups = (rows + 127) / 128;
+  auto off = [&](int64_t r) { return min<int64_t>(max<int64_t>(row_ptr[r], 0), k); };
+  uint32_t m = 0;
+  for (int64_t g = threadIdx.x; g < groups; g += 1024) {
+    const int64_t a = off(128 * g), b = off(min<int64_t>(rows, 128 * (g + 1)));
+    m = max(m, (uint32_t)max<int64_t>(b - a, 0));
+  }
+#pragma unroll
+  for (int o = 32; o >= 1; o >>= 1) m = max(m, (uint32_t)__shfl_xor((int)m, o, 64));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = m;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    uint32_t r = 0;
+#pragma unroll
+    for (int w = 0; w < 16; ++w) r = max(r, red[w]);
+    *out = r;
+  }
+}
+
 __global__ __launch_bounds__(256) void k_ol_rowptr(int64_t rows, int64_t cols, int64_t k,
                                                    const int32_t* __restrict__ oidx, int32_t* __restrict__ row_ptr) {
   const int64_t r = (int64_t)blockIdx.x * 256 + threadIdx.x;
@@ -652,6 +677,11 @@ hipError_t launch_outlier_finish(int64_t rows, int64_t cols, int64_t k, int bits
     case 4: return ol_finish_b<4>(k, cols, oidx, oval, codes, q8, cst, lv, col, val, s);
     default: return ol_finish_b<8>(k, cols, oidx, oval, codes, q8, cst, lv, col, val, s);
   }
+}
+
+hipError_t launch_group_max(int64_t rows, int64_t k, const int32_t* row_ptr, uint32_t* out, hipStream_t s) {
+  hipLaunchKernelGGL(k_ol_group_max, dim3(1), dim3(1024), 0, s, rows, k, row_ptr, out);
+  return hipGetLastError();
 }
 
 }  // namespace qlr

@@ -65,7 +65,7 @@ class CDba(C.Structure):
 class CSparse(C.Structure):
     _fields_ = [
         ("rows", C.c_int64), ("cols", C.c_int64), ("nnz", C.c_int64), ("row_ptr", C.c_void_p),
-        ("col", C.c_void_p), ("val", C.c_void_p),
+        ("col", C.c_void_p), ("val", C.c_void_p), ("max_group_nnz", C.c_int64),
     ]
 
 
@@ -492,10 +492,13 @@ class Sparse:
     row_ptr: "object"
     col: "object"
     val: "object"
+    # largest entry count of a group of 128 rows starting at a multiple of 128 (set by
+    # quantize_outliers), -1 when not known
+    max_group_nnz: int = -1
 
     def c_struct(self) -> CSparse:
         return CSparse(self.rows, self.cols, self.nnz, self.row_ptr.data_ptr(), self.col.data_ptr(),
-                       self.val.data_ptr())
+                       self.val.data_ptr(), self.max_group_nnz)
 
     @staticmethod
     def empty(rows: int, cols: int, nnz: int, device) -> "Sparse":
@@ -520,6 +523,7 @@ def quantize_outliers(W, bits: int, k: int, out: Optional[QWeight] = None, spars
     cw, cs = qw.c_struct(), sp.c_struct()
     check(lib().qlr_quantize_outliers(W.data_ptr(), _dt(W), rows, cols, bits, BLOCK, k, C.byref(cw), C.byref(cs),
                                       ws.data_ptr(), ws.numel(), _stream(W.device)))
+    sp.max_group_nnz = int(cs.max_group_nnz)
     return qw, sp
 
 

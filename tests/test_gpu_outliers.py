@@ -47,7 +47,15 @@ def _check_split(W, wdtype, bits, k, qw, sp):
     assert np.array_equal(sp.row_ptr.cpu().numpy(), row_ptr), "row offsets differ"
     assert np.array_equal(sp.col.cpu().numpy()[:k], col), "columns differ"
     assert np.array_equal(sp.val.cpu().numpy()[:k].view(np.uint32), val.view(np.uint32)), "residuals differ"
+    assert sp.max_group_nnz == _max_group_nnz(row_ptr), "largest 128-row group count differs"
     return q, (row_ptr, col, val)
+
+
+def _max_group_nnz(row_ptr):
+    """The largest entry count of the row groups [128 g, 128 g + 128) of a CSR (host)."""
+    rows = len(row_ptr) - 1
+    edges = np.append(np.arange(0, rows, 128), rows)
+    return int(np.max(np.diff(row_ptr[edges]))) if rows > 0 else 0
 
 
 def _ties(seed, rows, cols, dtype):
@@ -283,3 +291,42 @@ def test_fwd_gemm_tiles_fused_and_not(bits):
     q = oracle.quantize(lin.W.reshape(-1), "f16", bits)
     for ydt in ("f32", "bf16"):
         _check_fwd(_run(lin, qw, sp, ydt, qlr.PATH_GEMM), lin, q, csr, ydt, rel=GEMM_REL)
+
+
+@pytest.mark.parametrize("counts", [[400, 300, 0], [3000, 400, 0]])
+def test_fwd_gemm_group_count_skips_addend(counts):
+    """Prefill GEMM with 4-bit codes, 384 x 576, M = 300, r 16: with sp.max_group_nnz exact the addend
+    kernel is skipped when every 128-row tile's entries fit (400 here) and launched when one does not
+    (3000); both agree bit for bit with the same call with the count unknown (-1, the addend kernel
+    always launched), and with the oracle."""
+    N, K, M = 384, 576, 300
+    lin = workloads.make_linear("ogrp", 420 + counts[0], N, K, M, sigma=0.02, wdtype="f16", bits=4, r=16,
+                                alpha=16.0, abdtype="bf16", xdtype="bf16")
+    csr = _csr_per_tile(N, K, counts, seed=counts[0])
+    qw = qlr.quantize(dev(lin.W, "f16"), 4)
+    q = oracle.quantize(lin.W.reshape(-1), "f16", 4)
+    sp = qlr.sparse_from_csr(N, K, *csr, "cuda")
+    assert sp.max_group_nnz == -1
+    y_unknown = _run(lin, qw, sp, "f32", qlr.PATH_GEMM)
+    sp.max_group_nnz = _max_group_nnz(csr[0])
+    assert sp.max_group_nnz == max(counts)
+    y_known = _run(lin, qw, sp, "f32", qlr.PATH_GEMM)
+    assert np.array_equal(y_known.view(np.uint32), y_unknown.view(np.uint32))
+    _check_fwd(y_known, lin, q, csr, rel=GEMM_REL)
+
+
+def test_split_group_count_on_the_attn_split():
+    """The split of the 4096 x 4096 attention weight (k = 16,777): its group count is exact, fits the
+    GEMM's tiles (so the prefill forward launches no addend kernel), and the forward agrees bit for bit
+    with the same call with the count unknown."""
+    base = workloads.attn(1)
+    k = int(round(0.001 * base.W.size))
+    qw, sp = _gpu_split(base.W, "f16", 4, k)
+    row_ptr = sp.row_ptr.cpu().numpy()
+    assert sp.max_group_nnz == _max_group_nnz(row_ptr)
+    assert 0 < sp.max_group_nnz <= 1982
+    lin = workloads.attn(300, W=base.W)
+    y_known = _run(lin, qw, sp, "bf16", qlr.PATH_GEMM)
+    sp.max_group_nnz = -1
+    y_unknown = _run(lin, qw, sp, "bf16", qlr.PATH_GEMM)
+    assert np.array_equal(y_known.view(np.uint32), y_unknown.view(np.uint32))
