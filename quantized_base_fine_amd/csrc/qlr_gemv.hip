@@ -421,16 +421,22 @@ __device__ __forceinline__ bool x_blocks_exact(uint32_t sxs, int64_t b0, int64_t
 // every workgroup also computes t = x A^T itself, from A rows read after the
 // code stream has been issued (L2-resident after the first workgroup of each
 // XCD), instead of reading the partial sums of a separate kernel.
-template <int BITS, int YDT, bool XLDS, bool ADP, int D, bool DOT, bool TF, int SPX, bool DBA>
+// XR (MFMA path, x read from global memory, exactly two chunks per wave and
+// tile, 40..64 blocks per row): the wave's x fragments (its 8 blocks of the 16
+// x rows in the MFMA layout, 64 registers) are loaded once, before the chunk
+// stream, instead of riding with every chunk: a chunk's loads are then its
+// code pieces and scales only, and x is read once per workgroup, not per tile.
+template <int BITS, int YDT, bool XLDS, bool ADP, int D, bool DOT, bool TF, int SPX, bool DBA, bool XR>
 __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
   static_assert(!DOT || (XLDS && BITS != 3), "the single-row path reads x from LDS and 16-byte pieces of whole codes");
   static_assert(!TF || (DOT && ADP), "the fused adapter product belongs to the single-row path");
   static_assert(SPX == 0 || DOT, "the fused side channel belongs to the single-row path");
   static_assert(!DBA || TF, "the double-binary branch is fused through the adapter product");
+  static_assert(!XR || (!XLDS && !DOT && (D == 2 || D == 4)), "x in registers: MFMA path, x from global memory");
   // per-wave LDS staging buffer: codes and scales, or scales only (single-row path)
   constexpr uint32_t kStageW = DOT ? 16 * CH * 4 : ChunkGeo<BITS>::kStage;
   using G = ChunkGeo<BITS>;
-  using Ch = Chunk<BITS, XLDS>;
+  using Ch = Chunk<BITS, XLDS || XR>;
   constexpr int ES = (YDT == DT_F32) ? 4 : 2;
   extern __shared__ uint32_t smem[];
   const LinearArgs& a = P.a;
@@ -513,7 +519,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
       ch.sc = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(sr, (blk >> 8) << 2, 0, 0));
     }
     // x fragments of the chunk's blocks (clamped into the row; unused past kb1)
-    if constexpr (!XLDS) {
+    if constexpr (!XLDS && !XR) {
       const int64_t kbs = kb0 + (int64_t)c * CH;
 #pragma unroll
       for (int u = 0; u < CH; ++u) {
@@ -614,6 +620,18 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
     for (int i = 0; i < kTPre; ++i) {
       const int q = tid + i * kThreads;
       tp[i] = __uint_as_float(__builtin_amdgcn_raw_buffer_load_b32(trs, buf_off(q < tcount, (uint32_t)q * 4u), 0, 0));
+    }
+  }
+
+  // (XR) the x fragments of the wave's blocks kb0 .. kb0 + 7 (clamped into the
+  // row; those past kb1 are never added), before the chunk stream
+  u32x4_t xr[XR ? 2 * CH : 1][2];
+  if constexpr (XR) {
+#pragma unroll
+    for (int u = 0; u < 2 * CH; ++u) {
+      const int64_t kb = min(kb0 + u, nb - 1);
+      xr[u][0] = *reinterpret_cast<const u32x4_t*>(xg + kb * 64);
+      xr[u][1] = *reinterpret_cast<const u32x4_t*>(xg + kb * 64 + 8);
     }
   }
 
@@ -875,7 +893,8 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
 
   // Stage a chunk's codes and scales in this wave's LDS buffer `buf` (only this
   // wave reads them, and a wave's LDS instructions run in order), then compute.
-  auto compute = [&](const Ch& ch, int64_t tl, int c, int buf) {
+  // (XR: `slot` is the ring slot, whose chunk index within its tile is slot % 2)
+  auto compute = [&](const Ch& ch, int64_t tl, int c, int buf, int slot) {
     const uint32_t sb = wstage + (uint32_t)buf * G::kStage;
 #pragma unroll
     for (int i = 0; i < G::NP; ++i) {
@@ -902,6 +921,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
         const uint32_t xa = xlane + (uint32_t)(kbs + u) * xstep;
         x0 = lds_rd128(xa);
         x1 = lds_rd128(xa + 16);
+      } else if constexpr (XR) {
+        x0 = xvalid ? xr[(slot & 1) * CH + u][0] : zero;
+        x1 = xvalid ? xr[(slot & 1) * CH + u][1] : zero;
       } else {
         x0 = xvalid ? ch.x[u][0] : zero;
         x1 = xvalid ? ch.x[u][1] : zero;
@@ -1215,7 +1237,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
     if (j < total) {
       if (nchunk > 0) {
         if constexpr (DOT) compute_dot(ring[s], ctile, cc, buf);
-        else compute(ring[s], ctile, cc, buf);
+        else compute(ring[s], ctile, cc, buf, s);
       }
       buf ^= 1;
       if (cc == nitem - 1) {
@@ -1575,9 +1597,9 @@ int device_cus() {
 }
 
 template <int BITS, int YDT, bool XLDS, bool ADP, int D, bool DOT = false, bool TF = false, int SPX = 0,
-          bool DBA = false>
+          bool DBA = false, bool XR = false>
 hipError_t launch_k(const Params& P, int64_t grid, size_t shmem, const Levels& lv, hipStream_t s) {
-  auto kern = k_gemv<BITS, YDT, XLDS, ADP, D, DOT, TF, SPX, DBA>;
+  auto kern = k_gemv<BITS, YDT, XLDS, ADP, D, DOT, TF, SPX, DBA, XR>;
   static bool attr = false;
   if (!attr) {
     // the kernel addresses LDS from 0: it must not have static LDS
@@ -1604,6 +1626,7 @@ struct Plan {
   bool deep = false;  // a wave's chunk stream is longer than 2 (ring depth 4)
   bool dot = false;   // single-row path
   bool tf = false;    // fused adapter product
+  bool xr = false;    // MFMA path: each wave's x fragments in registers (two chunks per wave and tile)
   bool spw = false;   // room for the transform of the x row (Walsh-Hadamard side channel)
 };
 
@@ -1686,6 +1709,8 @@ Plan plan_gemv(const LinearArgs& a) {
     P.sX = (uint32_t)lds;
     pl.xlds = xlds;
     pl.dot = dot;
+    // every wave's K range is 5..8 blocks (two chunks): 40 <= nb <= 64
+    pl.xr = !xlds && !dot && nb >= 5 * kWaves && nb <= 2 * CH * kWaves;
     pl.tf = tf && P.tmode == T_FUSED;
     pl.lds = lds + (xlds ? xbytes : 0);
     if (a.sp_row_ptr && a.sp_wht_lp >= 0 && dot) {
@@ -1744,11 +1769,19 @@ hipError_t launch_gemv_b(const LinearArgs& a, const Levels& lv, hipStream_t s) {
       if (pl.deep) return launch_k<BITS, YDT, true, true, 4>(P, grid, lds, lv, s);
       return launch_k<BITS, YDT, true, true, 2>(P, grid, lds, lv, s);
     }
+    if (pl.xr) {
+      if (pl.deep) return launch_k<BITS, YDT, false, true, 4, false, false, 0, false, true>(P, grid, lds, lv, s);
+      return launch_k<BITS, YDT, false, true, 2, false, false, 0, false, true>(P, grid, lds, lv, s);
+    }
     return launch_k<BITS, YDT, false, true, 2>(P, grid, lds, lv, s);
   }
   if (pl.xlds) {
     if (pl.deep) return launch_k<BITS, YDT, true, false, 4>(P, grid, lds, lv, s);
     return launch_k<BITS, YDT, true, false, 2>(P, grid, lds, lv, s);
+  }
+  if (pl.xr) {
+    if (pl.deep) return launch_k<BITS, YDT, false, false, 4, false, false, 0, false, true>(P, grid, lds, lv, s);
+    return launch_k<BITS, YDT, false, false, 2, false, false, 0, false, true>(P, grid, lds, lv, s);
   }
   return launch_k<BITS, YDT, false, false, 2>(P, grid, lds, lv, s);
 }
