@@ -161,10 +161,11 @@ def test_linear_paths_small(bits, path, M, r):
 @pytest.mark.parametrize("K", [2496, 2560, 3200, 4096])
 @pytest.mark.parametrize("M,r", [(2, 0), (16, 16), (5, 64)])
 def test_decode_mfma_x_in_registers(bits, K, M, r):
-    """The MFMA decode path with each wave's x fragments loaded once into registers (40..64 blocks per
-    row: every wave's K range is two chunks; K = 2496 has 39 blocks and keeps x riding with the chunks):
-    ragged N (1049 rows: 66 tiles, several per workgroup on small grids), every code width, with and
-    without the adapter; every output against the oracle, float32 and bf16 y."""
+    """The MFMA decode path around its x-in-registers case (x over the 32 KB that is staged in LDS and
+    40..64 blocks per row, every wave's K range two chunks: M = 16 at K >= 2560 and M = 5 at K = 4096;
+    K = 2496 has 39 blocks and keeps x riding with the chunks; M = 2 and the narrower M = 5 rows stage x
+    in LDS): ragged N (1049 rows: 66 tiles), every code width, with and without the adapter; every output
+    against the oracle, float32 and bf16 y."""
     lin = _small_linear(1049, K, M, bits, r, seed=K + M + r + bits)
     qw = _gpu_quant(lin.W, "f16", bits)
     rows = list(range(lin.N))
@@ -175,7 +176,7 @@ def test_decode_mfma_x_in_registers(bits, K, M, r):
 
 @pytest.mark.parametrize("K", [2560, 4096])
 def test_decode_3bit_single_row_mfma(K):
-    """3-bit codes at M = 1 take the MFMA path (x in registers at these widths): every output."""
+    """3-bit codes at M = 1 take the MFMA path (x staged in LDS): every output."""
     lin = _small_linear(777, K, 1, 3, 16, seed=K // 64)
     qw = _gpu_quant(lin.W, "f16", 3)
     rows = list(range(lin.N))
