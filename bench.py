@@ -154,10 +154,11 @@ TRAFFIC_KERNELS = {
 COPY_BYTES = 256 << 20  # the calibration copy reads and writes this many bytes
 
 
-def traffic_from_counters(fetch_dir: str, write_dir: str):
-    """profiles/traffic.json from two rocprofv3 --pmc runs (FETCH_SIZE, WRITE_SIZE in KiB
-    per dispatch) of `bench.py --eager --copy-calibration`: the mean per launch of each
-    kernel, scaled by what the counter reads for the calibration copy of known size."""
+def traffic_from_counters(fetch_dir: str, write_dir: str, out_path: str = ""):
+    """profiles/traffic.json (or out_path) from two rocprofv3 --pmc runs (FETCH_SIZE,
+    WRITE_SIZE in KiB per dispatch) of `bench.py --eager --copy-calibration`: the mean per
+    launch of each kernel, scaled by what the counter reads for the calibration copy of
+    known size.  Every kernel of TRAFFIC_KERNELS must appear in both runs."""
     import csv
     import glob
     import hashlib
@@ -186,7 +187,7 @@ def traffic_from_counters(fetch_dir: str, write_dir: str):
         fv = [v for k, vs in fetch.items() if kname in k for v in vs]
         wv = [v for k, vs in write.items() if kname in k for v in vs]
         if not fv or not wv:
-            continue
+            raise SystemExit(f"no counter rows for {kname} (kernel renamed? update TRAFFIC_KERNELS)")
         h = hashlib.sha256()
         for src in sources:
             with open(os.path.join(ROOT, src), "rb") as f:
@@ -197,7 +198,7 @@ def traffic_from_counters(fetch_dir: str, write_dir: str):
                     "calibration": {"copy_fetch_kib": cf, "copy_write_kib": cw,
                                     "fetch_scale": round(scale_f, 4), "write_scale": round(scale_w, 4)},
                     "bytes_per_launch": int(round(fk * 1024 * scale_f + wk * 1024 * scale_w))}
-    with open(os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
+    with open(out_path or os.path.join(ROOT, "profiles", "traffic.json"), "w") as f:
         json.dump(out, f, indent=1)
     print(json.dumps(out, indent=1))
 
