@@ -270,6 +270,31 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
+// x rows for the MFMA path are loaded with each quad of lanes in one 64-byte
+// segment (lane l: 16 bytes of row l / 4, piece l % 4 of the block's first
+// half in h0 and of its second half in h1; a piece is 8 columns), the rate the
+// address unit sustains; the 16x16x32 A fragments want lane 16 g + n to hold
+// pieces 2 g (f0) and 2 g + 1 (f1) of row n.  Quad moves gather the even
+// pieces of a row into one register and the odd ones into another (lane
+// 4 n + q holding pieces (0, 4, 2, 6)[q] and (1, 5, 3, 7)[q]), and one lane
+// permute per word moves them into place.
+__device__ __forceinline__ void x_frag(const u32x4_t& h0, const u32x4_t& h1, int lane, u32x4_t& f0, u32x4_t& f1) {
+  const bool odd = (lane & 1) != 0;
+  const int g = lane >> 4;
+  const int src = (4 * (lane & 15) + (((g & 1) << 1) | (g >> 1))) << 2;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    // the quad moves run on every lane (their sources are the lane's neighbours),
+    // then plain selects
+    const uint32_t m1 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)h1[j], 0xA0, 0xF, 0xF, false);
+    const uint32_t m0 = (uint32_t)__builtin_amdgcn_update_dpp(0, (int)h0[j], 0xF5, 0xF, 0xF, false);
+    const uint32_t e = odd ? m1 : h0[j];
+    const uint32_t o = odd ? h1[j] : m0;
+    f0[j] = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)e);
+    f1[j] = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)o);
+  }
+}
+
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 __device__ __forceinline__ float dot2(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a), __builtin_bit_cast(bf16x2_t, b), c, false);
@@ -465,7 +490,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
   const bool xvalid = nl < M;
   const uint32_t xlane = xvalid ? P.sX + (uint32_t)(nl * (K + 8) * 2 + 32 * g) : P.sZ + 32u * g;
   const uint32_t xstep = xvalid ? 128u : 0u;
-  const uint16_t* xg = reinterpret_cast<const uint16_t*>(a.x) + (int64_t)(xvalid ? nl : M - 1) * K + 16 * g;
+  // coalesced x pieces of row lane / 4 (clamped into x), moved into the
+  // fragment layout by x_frag where they are used
+  const uint16_t* xg = reinterpret_cast<const uint16_t*>(a.x) + (int64_t)min(lane >> 2, M - 1) * K + 8 * (lane & 3);
   const __amdgpu_buffer_rsrc_t cr = rsrc(a.codes, N * nb * 8 * BITS);
   const __amdgpu_buffer_rsrc_t qr = rsrc(a.q8, N * nb);
   const __amdgpu_buffer_rsrc_t sr = rsrc(a.cst, ((N * nb + 255) >> 8) * 4);
@@ -525,7 +552,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
       for (int u = 0; u < CH; ++u) {
         const int64_t kb = min(kbs + u, nb - 1);
         ch.x[u][0] = *reinterpret_cast<const u32x4_t*>(xg + kb * 64);
-        ch.x[u][1] = *reinterpret_cast<const u32x4_t*>(xg + kb * 64 + 8);
+        ch.x[u][1] = *reinterpret_cast<const u32x4_t*>(xg + kb * 64 + 32);
       }
     }
     if (++lc == nitem) {
@@ -631,7 +658,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
     for (int u = 0; u < 2 * CH; ++u) {
       const int64_t kb = min(kb0 + u, nb - 1);
       xr[u][0] = *reinterpret_cast<const u32x4_t*>(xg + kb * 64);
-      xr[u][1] = *reinterpret_cast<const u32x4_t*>(xg + kb * 64 + 8);
+      xr[u][1] = *reinterpret_cast<const u32x4_t*>(xg + kb * 64 + 32);
     }
   }
 
@@ -925,8 +952,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
         x0 = xvalid ? xr[(slot & 1) * CH + u][0] : zero;
         x1 = xvalid ? xr[(slot & 1) * CH + u][1] : zero;
       } else {
-        x0 = xvalid ? ch.x[u][0] : zero;
-        x1 = xvalid ? ch.x[u][1] : zero;
+        x_frag(ch.x[u][0], ch.x[u][1], lane, x0, x1);
+        x0 = xvalid ? x0 : zero;
+        x1 = xvalid ? x1 : zero;
       }
       u32x4_t b0h, b0l, b1h, b1l;
       decode16<BITS>(raw_from_lds<BITS>(rowad, u, g), tlane, b0h, b0l, b1h, b1l);
@@ -1252,6 +1280,17 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemv(Params P, Levels lv) {
       }
     }
   };
+  if constexpr (XR) {
+    // the x fragments into the MFMA layout, once (their loads were issued
+    // before the ring's, so the first chunk's wait covers them)
+#pragma unroll
+    for (int u = 0; u < 2 * CH; ++u) {
+      u32x4_t f0, f1;
+      x_frag(xr[u][0], xr[u][1], lane, f0, f1);
+      xr[u][0] = f0;
+      xr[u][1] = f1;
+    }
+  }
   if constexpr (TF) {
     // the whole stream is in the ring (at most D chunks): straight-line, no refills
 #pragma unroll
