@@ -187,16 +187,20 @@ __global__ __launch_bounds__(kTtWaves * 64) void k_lora_t_tile(TGroup G) {
 // split, issues the loads of up to kLtSteps of them before any product (the
 // split count keeps a split within one such round for the decode shapes), and
 // multiplies on 16x16x32 bf16 MFMA (x rows as the A operand, adapter rows as
-// B).  The 16 waves' sums are added through LDS in wave order.
+// B).  A step's loads give each quad of lanes one row's 64 bytes (lane l: row
+// l / 4, 8 columns from 8 (l % 4)), the rate the address unit sustains, and a
+// lane permute per word puts row n's piece g in lane 16 g + n, the fragment
+// layout.  The 16 waves' sums are added through LDS in wave order.
 constexpr int kLtWaves = 16, kLtSteps = 8;
 __device__ __forceinline__ void lora_t_small_body(const uint16_t* __restrict__ x, int64_t M, int64_t K,
                                                   const uint16_t* __restrict__ A, int r, float* __restrict__ p,
                                                   int j0, int S, int sidx, float (*red)[256]) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  const int row = lane & 15, g = lane >> 4;
+  const int row = lane >> 2, g = lane & 3;  // the lane's loads
   const bool xv = row < M, av = j0 + row < r;
   const uint16_t* xp = x + (int64_t)(xv ? row : 0) * K + g * 8;
   const uint16_t* ap = A + (int64_t)(av ? j0 + row : 0) * K + g * 8;
+  const int src = (4 * (lane & 15) + (lane >> 4)) << 2;  // lane 16 g + n <- lane 4 n + g
   const int64_t nsteps = K / 32;
   const int64_t c0 = nsteps * sidx / S, c1 = nsteps * (sidx + 1) / S;
   f32x4_t acc = {0.f, 0.f, 0.f, 0.f};
@@ -212,7 +216,16 @@ __device__ __forceinline__ void lora_t_small_body(const uint16_t* __restrict__ x
       ab[i] = (av && sv) ? *reinterpret_cast<const u32x4_t*>(ap + k) : zero;
     }
 #pragma unroll
-    for (int i = 0; i < kLtSteps; ++i) acc = mfma16x16x32(as_bf16x8(xa[i]), as_bf16x8(ab[i]), acc);
+    for (int i = 0; i < kLtSteps; ++i) {
+      if (base + (int64_t)i * kLtWaves >= c1) break;  // uniform: the split's last steps
+      u32x4_t xf, af;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        xf[j] = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)xa[i][j]);
+        af[j] = (uint32_t)__builtin_amdgcn_ds_bpermute(src, (int)ab[i][j]);
+      }
+      acc = mfma16x16x32(as_bf16x8(xf), as_bf16x8(af), acc);
+    }
   }
 #pragma unroll
   for (int v = 0; v < 4; ++v) red[wave][lane * 4 + v] = acc[v];
