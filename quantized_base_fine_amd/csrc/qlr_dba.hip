@@ -50,9 +50,10 @@ __device__ __forceinline__ void dba_beff_item(const DbaArgs& d, int64_t N, uint1
 // in LDS (once, shared by all its rows and adapter rows); its 16 waves then
 // take every 16th 32-wide K step, all of a wave's steps loaded before any is
 // multiplied (kDbaSteps at a time), and are added through LDS.  Per step a
-// lane reads 8 elements of its x row (A operand) and 8 hi and 8 lo halves of
-// gamma, flips the sign bits where B2[j][k] is -1 (B operand) and multiplies
-// both halves into one accumulator.
+// lane takes 8 elements of its x row (A operand; loaded coalesced and moved
+// into place by a lane permute) and 8 hi and 8 lo halves of gamma, flips the
+// sign bits where B2[j][k] is -1 (B operand) and multiplies both halves into
+// one accumulator.
 constexpr int kDbaWaves = 16, kDbaSteps = 4;
 struct DbaGrid {
   int64_t mtiles, tblocks;
@@ -77,7 +78,12 @@ __global__ __launch_bounds__(1024) void k_dba_prep(DbaArgs d, DbaGrid gd, const 
   const int64_t m0 = mt * 16;
   const int S = gd.splits;
   const bool xv = m0 + row < M;
-  const uint16_t* xp = x + (xv ? m0 + row : 0) * K + 8 * g;
+  // x loads: each quad of lanes one row's 64 bytes of a step (lane l: row l / 4,
+  // 8 columns from 8 (l % 4)); a lane permute per word moves row n's piece g to
+  // lane 16 g + n, the fragment layout
+  const int xrow = lane >> 2;
+  const uint16_t* xp = x + (m0 + xrow < M ? m0 + xrow : 0) * K + 8 * (lane & 3);
+  const int xsrc = (4 * row + g) << 2;
   const int j = j0 + row;
   const bool jv = j < d.R;
   const int64_t w2 = (K + 31) / 32;
@@ -130,7 +136,10 @@ __global__ __launch_bounds__(1024) void k_dba_prep(DbaArgs d, DbaGrid gd, const 
         bh[e2] = jv ? (gh[e2] ^ f) : 0u;
         bl[e2] = jv ? (gl[e2] ^ f) : 0u;
       }
-      const u32x4_t xq = sv ? xa[q] : zero;
+      u32x4_t xf;
+#pragma unroll
+      for (int e2 = 0; e2 < 4; ++e2) xf[e2] = (uint32_t)__builtin_amdgcn_ds_bpermute(xsrc, (int)xa[q][e2]);
+      const u32x4_t xq = sv ? xf : zero;
       acc = mfma16x16x32(as_bf16x8(xq), as_bf16x8(bh), acc);
       acc = mfma16x16x32(as_bf16x8(xq), as_bf16x8(bl), acc);
     }
