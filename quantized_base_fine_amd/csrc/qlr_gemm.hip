@@ -428,7 +428,9 @@ __global__ __launch_bounds__(512, 1) void k_gemm(GemmParams P, Levels lv) {
       load_xw(min<int64_t>(1, kbl), 1);
       asm volatile("s_waitcnt vmcnt(0)" ::: "memory");  // blocks 0 and 1 in LDS
       __syncthreads();
-      // one step (and barrier) per consumer block; the last two load unused copies
+      // one step (and barrier) per consumer block; the last two load unused copies.
+      // The barrier's fence waits for all of the step's direct loads: the
+      // consumers read the first fragments of block k+2 before the next barrier.
       for (int64_t k = 0; k < nb; ++k) {
         __builtin_amdgcn_sched_barrier(0);
         load_xw(min(k + 2, kbl), (int)((k + 2) % 3));
@@ -673,10 +675,16 @@ __global__ __launch_bounds__(512, 1) void k_gemm(GemmParams P, Levels lv) {
       __syncthreads();
       // Step k: x(k+2) by direct loads into buffer (k+2) % 3 (freed by the last
       // barrier), codes(k+4) into set (k+1) % 3, and the dequantized block k+2
-      // into buffer (k+2) % 3.  Before the step's barrier the wave waits for all
-      // but its 8 newest loads: x(k+1), issued a step earlier, is then in LDS
-      // for the consumers' next block.  The step runs in pinned chunks, each a
-      // code word's arithmetic, so the wave keeps computing while loads drain.
+      // into buffer (k+2) % 3.  x(k+2) must be in LDS at the step's barrier:
+      // after it the consumers finish block k+1 and, two MFMA steps ahead,
+      // already read the first fragments of block k+2.  The fence of
+      // __syncthreads() waits for that (for every direct load into LDS in
+      // flight; only the step's newest code loads stay outstanding), the
+      // explicit wait before it for everything older than the step's 8 newest
+      // loads.  So every step holds one round trip of its x loads; issuing x a
+      // step earlier would take a fourth buffer.  The step runs in pinned
+      // chunks, each a code word's arithmetic, so the wave keeps computing
+      // while loads drain.
       auto pstep = [&](CS& cl, const CS& cw, int64_t k, int bw) {
         __builtin_amdgcn_sched_barrier(0);
         load_x_lds(min(k + 2, kbl), bw);
